@@ -1,0 +1,160 @@
+/*
+ * ssm_scan.h -- C ABI of the MI355X (gfx950) state-mediated selective SSM kernel.
+ *
+ * The operation (one independent recurrence per (batch, head) slice):
+ *
+ *   h_t = A_t h_{t-1} + gamma_t B_t X_t + beta_t B_{t-1} X_{t-1}
+ *   y_t = C_t^T h_t + D_h X_t
+ *
+ * Sources: "When a Diagonal State Is Not Enough" (sungsoo.github.io), Part 01
+ * (h_t = A_t h_{t-1} + B_t u_t, y_t = C_t h_t + D_t u_t) and Part 03 (selective
+ * recurrence; Theorem 24: with time-shared token-local maps the state-mediated
+ * kernel is unnormalized scalar-mode linear attention under a multiplicative
+ * mask; Theorem 8: commuting transitions diagonalizable over the reals give real
+ * scalar modes, complex eigenvalues give rotating pairs); Parts 03 and 08.3
+ * (SSD-MIMO: R values written and O rows read per step, decay shared within a
+ * head; HybridMamba: per-coordinate real rows, rotating pairs, two-endpoint
+ * writes); arXiv abstract on mlinfo.pages.dev (same architectures, fused GPU
+ * kernels timed forward + backward at SSM-core scope).
+ *
+ * Transition A_t (block diagonal, N = n_real + 2 n_pairs rows):
+ *   real row n:  a_t[n] = exp(-Delta_t * A_{h,n})   (head mode: A_{h,n} = A_h)
+ *   pair k (rows n_real+2k, n_real+2k+1):
+ *                rho_t = exp(-Delta_t * A_{h, n_real+k}),  theta_t = Delta_t * omega_{h,k},
+ *                block = rho_t [[cos theta, -sin theta], [sin theta, cos theta]]
+ *   Delta_t = softplus(dt_t) if SSM_F_DT_SOFTPLUS, else dt_t.
+ *   Without SSM_F_TWO_ENDPOINT: beta = 0, gamma = 1.  h_{-1} = 0, B_{-1} X_{-1} = 0.
+ *
+ * Layouts: row-major, last index fastest; g = h / (nheads / ngroups).
+ *   x   [batch][seqlen][nheads][rank_in][headdim]       (io dtype)
+ *   B   [batch][seqlen][ngroups][rank_in][dstate]       (io dtype)
+ *   C   [batch][seqlen][ngroups][rank_out][dstate]      (io dtype)
+ *   y, dy [batch][seqlen][nheads][rank_out][headdim]    (io dtype)
+ *   dt, beta, gamma, ddt, dbeta, dgamma [batch][seqlen][nheads]   (fp32)
+ *   A   head mode [nheads]; coordinate mode [nheads][n_real + n_pairs] (fp32)
+ *   omega [nheads][n_pairs], D [nheads]                           (fp32)
+ *   dA, domega, dD: same shapes as A, omega, D (fp32)
+ *   dx, dB, dC: same shapes and dtype as x, B, C.
+ *
+ * Ownership and behaviour:
+ *   - Every pointer is a caller-owned DEVICE pointer, 16-byte aligned.  The
+ *     library never allocates, frees or synchronizes; all work is enqueued on
+ *     `stream` (a hipStream_t, NULL = default stream) and is asynchronous.
+ *   - Validation happens before any launch; an error returns a negative status
+ *     and enqueues nothing.  A failed launch returns SSM_ERR_HIP.
+ *   - Outputs (including parameter gradients) are overwritten, never
+ *     accumulated, and are bitwise reproducible run to run.
+ *   - Optional pointers may be NULL: omega iff n_pairs == 0; beta and gamma iff
+ *     SSM_F_TWO_ENDPOINT is clear; D iff SSM_F_HAS_D is clear (D requires
+ *     rank_out == rank_in).  In the backward, a NULL gradient output is not
+ *     computed; dx, dB, dC, ddt must be non-NULL.
+ *   - `saved` (fp32, ssm_saved_bytes(desc) bytes) receives the chunk-boundary
+ *     states from the forward when non-NULL; ssm_scan_bwd requires the buffer a
+ *     forward with the same descriptor and inputs filled.
+ *   - `ws` is device scratch of at least ssm_workspace_bytes(desc, dir) bytes
+ *     (may be NULL when that is 0).  Calls that share a workspace on one
+ *     stream are ordered; concurrent calls need separate workspaces.
+ *   - The library is thread-safe and keeps no per-call state.
+ */
+#ifndef SSM_SCAN_H
+#define SSM_SCAN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SSM_ABI_VERSION 1
+
+typedef enum {
+  SSM_OK = 0,
+  SSM_ERR_NULL = -1,        /* a required pointer is NULL (or a forbidden one is set) */
+  SSM_ERR_SHAPE = -2,       /* inconsistent sizes */
+  SSM_ERR_DTYPE = -3,       /* unknown io dtype */
+  SSM_ERR_ALIGN = -4,       /* pointer not 16-byte aligned */
+  SSM_ERR_UNSUPPORTED = -5, /* valid but not implemented for this shape / mode */
+  SSM_ERR_WORKSPACE = -6,   /* workspace smaller than ssm_workspace_bytes() */
+  SSM_ERR_HIP = -7          /* a HIP launch failed */
+} ssm_status;
+
+typedef enum { SSM_F32 = 0, SSM_BF16 = 1 } ssm_dtype;
+
+typedef enum {
+  SSM_DECAY_HEAD = 0,  /* one rate per head (Mamba-2-style SSD); n_pairs must be 0 */
+  SSM_DECAY_COORD = 1  /* one rate per real row and per pair (HybridMamba rows) */
+} ssm_decay_mode;
+
+enum {
+  SSM_F_DT_SOFTPLUS = 1u,  /* Delta = softplus(dt) inside the kernel */
+  SSM_F_TWO_ENDPOINT = 2u, /* write beta_t B_{t-1} X_{t-1} + gamma_t B_t X_t */
+  SSM_F_HAS_D = 4u         /* add the feedthrough D_h X_t (rank_out == rank_in) */
+};
+
+typedef struct {
+  int32_t batch, seqlen, nheads, ngroups;
+  int32_t headdim;  /* P */
+  int32_t dstate;   /* N = n_real + 2 n_pairs */
+  int32_t rank_in;  /* R: values written per step */
+  int32_t rank_out; /* O: rows read per step */
+  int32_t n_real, n_pairs;
+  int32_t chunk;    /* tokens per chunk; 0 = library's choice */
+  int32_t io_dtype;   /* ssm_dtype: storage of x, B, C, y, dy, dx, dB, dC */
+  int32_t decay_mode; /* ssm_decay_mode */
+  uint32_t flags;     /* SSM_F_* */
+} ssm_desc;
+
+typedef struct {
+  const void *x, *B, *C;
+  const float *dt, *A, *omega, *beta, *gamma, *D;
+  void *y;
+  float *saved; /* optional: chunk-boundary states for the backward */
+} ssm_fwd_args;
+
+typedef struct {
+  const void *x, *B, *C, *dy;
+  const float *dt, *A, *omega, *beta, *gamma, *D;
+  const float *saved; /* filled by ssm_scan_fwd with the same inputs */
+  void *dx, *dB, *dC;
+  float *ddt, *dA, *domega, *dbeta, *dgamma, *dD;
+} ssm_bwd_args;
+
+/* Library ABI version (SSM_ABI_VERSION of the build). */
+int ssm_abi_version(void);
+
+/* Human-readable text for a status code (static storage). */
+const char *ssm_status_string(int status);
+
+/* Validate a descriptor without launching anything; returns SSM_OK or an error. */
+int ssm_check_desc(const ssm_desc *desc);
+
+/* Chunk length the library uses for this descriptor (after validation), or a
+   negative status. */
+int ssm_chunk_tokens(const ssm_desc *desc);
+
+/* Bytes of the `saved` buffer (fp32 chunk-boundary states); 0 on an invalid descriptor. */
+size_t ssm_saved_bytes(const ssm_desc *desc);
+
+/* Device scratch needed by ssm_scan_fwd (for_backward = 0) or ssm_scan_bwd
+   (for_backward = 1); 0 on an invalid descriptor. */
+size_t ssm_workspace_bytes(const ssm_desc *desc, int for_backward);
+
+/* Forward chunked scan: writes y (and `saved` when non-NULL).
+   Steps of the method run on the GPU: chunk-local cumulative decay (wave
+   prefix), rotation folding and two-endpoint write prologue, masked
+   intra-chunk products on MFMA, chunk state and inter-chunk state passing kept
+   in registers, readout + feedthrough + store. */
+int ssm_scan_fwd(const ssm_desc *desc, const ssm_fwd_args *args, void *ws, size_t ws_bytes,
+                 void *stream);
+
+/* Fused reverse-mode pass: dx, dB, dC, ddt and the requested parameter
+   gradients (dA, domega, dbeta, dgamma, dD), given dy and the forward's
+   `saved` states. */
+int ssm_scan_bwd(const ssm_desc *desc, const ssm_bwd_args *args, void *ws, size_t ws_bytes,
+                 void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SSM_SCAN_H */

@@ -1,0 +1,184 @@
+// ssm_api.cpp -- the exported C ABI (include/ssm_scan.h): descriptor validation,
+// plan selection (kernel variant, chunk length, P-blocks), launches.
+#include <hip/hip_runtime.h>
+
+#include <cstdlib>
+#include <cstring>
+
+#include "ssm_kernels.hpp"
+#include "ssm_scan.h"
+
+namespace {
+
+using ssm::BwdKey;
+using ssm::FwdKey;
+
+struct Plan {
+  bool coord_kernel;  // per-row kernel (per-row rates, pairs or two-endpoint writes)
+  bool head_rates;    // per-row kernel fed one rate per head
+  int R, KR, QT, nchunks;
+  bool bf16;
+};
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int env_int(const char* name, int dflt) {
+  const char* v = std::getenv(name);
+  return (v && *v) ? std::atoi(v) : dflt;
+}
+
+// Shape rules of the operation itself (independent of what is implemented).
+int check_operation(const ssm_desc* d) {
+  if (!d) return SSM_ERR_NULL;
+  if (d->io_dtype != SSM_F32 && d->io_dtype != SSM_BF16) return SSM_ERR_DTYPE;
+  if (d->batch < 0 || d->seqlen < 0 || d->nheads <= 0 || d->ngroups <= 0 || d->headdim <= 0 ||
+      d->dstate <= 0 || d->rank_in <= 0 || d->rank_out <= 0 || d->n_real < 0 ||
+      d->n_pairs < 0 || d->chunk < 0)
+    return SSM_ERR_SHAPE;
+  if (d->nheads % d->ngroups) return SSM_ERR_SHAPE;
+  if (d->n_real + 2 * d->n_pairs != d->dstate) return SSM_ERR_SHAPE;
+  if (d->decay_mode != SSM_DECAY_HEAD && d->decay_mode != SSM_DECAY_COORD) return SSM_ERR_SHAPE;
+  if (d->decay_mode == SSM_DECAY_HEAD && d->n_pairs != 0) return SSM_ERR_SHAPE;
+  if (d->flags & ~(SSM_F_DT_SOFTPLUS | SSM_F_TWO_ENDPOINT | SSM_F_HAS_D)) return SSM_ERR_SHAPE;
+  if ((d->flags & SSM_F_HAS_D) && d->rank_in != d->rank_out) return SSM_ERR_SHAPE;
+  return SSM_OK;
+}
+
+int make_plan(const ssm_desc* d, Plan* pl) {
+  int rc = check_operation(d);
+  if (rc) return rc;
+  if (d->rank_out != d->rank_in) return SSM_ERR_UNSUPPORTED;
+  if (d->headdim % 16) return SSM_ERR_UNSUPPORTED;
+  if (d->n_pairs > 0 && (d->n_real % 2)) return SSM_ERR_UNSUPPORTED;
+  const bool te = (d->flags & SSM_F_TWO_ENDPOINT) != 0;
+  pl->bf16 = d->io_dtype == SSM_BF16;
+  pl->coord_kernel = d->decay_mode == SSM_DECAY_COORD || te || d->n_pairs > 0;
+  pl->head_rates = d->decay_mode == SSM_DECAY_HEAD;
+  pl->R = d->rank_in;
+  pl->KR = te ? 2 * d->rank_in : d->rank_in;
+  int qt = d->chunk;
+  if (qt == 0) {
+    if (!pl->coord_kernel) qt = 64 / d->rank_in;
+    else qt = (16 * pl->KR >= 32) ? 16 : 32 / pl->KR;
+    if (qt < 1) qt = 1;
+  }
+  pl->QT = qt;
+  pl->nchunks = (d->seqlen + qt - 1) / qt;
+  // a forward variant with some P-block must exist for this shape
+  for (int pb : {64, 32, 16}) {
+    FwdKey k{pl->bf16, d->dstate, pb, pl->R, pl->KR, pl->QT, pl->coord_kernel};
+    if (d->headdim % pb == 0 && ssm::fwd_variant_exists(k)) return SSM_OK;
+  }
+  return SSM_ERR_UNSUPPORTED;
+}
+
+int choose_pb(const ssm_desc* d, const Plan& pl) {
+  const int forced = env_int("SSM_FWD_PB", 0);
+  const long slices = (long)d->batch * d->nheads;
+  int best = 0;
+  for (int pb : {64, 32, 16}) {
+    FwdKey k{pl.bf16, d->dstate, pb, pl.R, pl.KR, pl.QT, pl.coord_kernel};
+    if (d->headdim % pb || !ssm::fwd_variant_exists(k)) continue;
+    if (forced) {
+      if (pb == forced) return pb;
+      continue;
+    }
+    best = pb;  // smallest available so far
+    if (slices * (d->headdim / pb) >= 512) return pb;
+  }
+  return best;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ssm_abi_version(void) { return SSM_ABI_VERSION; }
+
+const char* ssm_status_string(int s) {
+  switch (s) {
+    case SSM_OK: return "ok";
+    case SSM_ERR_NULL: return "required pointer is NULL (or an unused one is set)";
+    case SSM_ERR_SHAPE: return "inconsistent sizes or flags";
+    case SSM_ERR_DTYPE: return "unknown io dtype";
+    case SSM_ERR_ALIGN: return "pointer not 16-byte aligned";
+    case SSM_ERR_UNSUPPORTED: return "shape or mode not implemented by this library";
+    case SSM_ERR_WORKSPACE: return "workspace too small";
+    case SSM_ERR_HIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+int ssm_check_desc(const ssm_desc* d) {
+  Plan pl;
+  return make_plan(d, &pl);
+}
+
+int ssm_chunk_tokens(const ssm_desc* d) {
+  Plan pl;
+  const int rc = make_plan(d, &pl);
+  return rc ? rc : pl.QT;
+}
+
+size_t ssm_saved_bytes(const ssm_desc* d) {
+  Plan pl;
+  if (make_plan(d, &pl)) return 0;
+  return (size_t)d->batch * d->nheads * (pl.nchunks + 1) * d->dstate * d->headdim * sizeof(float);
+}
+
+size_t ssm_workspace_bytes(const ssm_desc* d, int for_backward) {
+  Plan pl;
+  if (make_plan(d, &pl)) return 0;
+  (void)for_backward;
+  return 0;
+}
+
+int ssm_scan_fwd(const ssm_desc* d, const ssm_fwd_args* a, void* ws, size_t ws_bytes,
+                 void* stream) {
+  Plan pl;
+  int rc = make_plan(d, &pl);
+  if (rc) return rc;
+  if (!a) return SSM_ERR_NULL;
+  (void)ws;
+  (void)ws_bytes;
+  // an empty problem touches no memory (empty tensors may have NULL pointers)
+  if (d->batch == 0 || d->seqlen == 0) return SSM_OK;
+  const bool te = (d->flags & SSM_F_TWO_ENDPOINT) != 0;
+  const bool hasD = (d->flags & SSM_F_HAS_D) != 0;
+  if (!a->x || !a->B || !a->C || !a->dt || !a->A || !a->y) return SSM_ERR_NULL;
+  if ((d->n_pairs > 0) != (a->omega != nullptr)) return SSM_ERR_NULL;
+  if (te != (a->beta != nullptr) || te != (a->gamma != nullptr)) return SSM_ERR_NULL;
+  if (hasD != (a->D != nullptr)) return SSM_ERR_NULL;
+  for (const void* q : {a->x, a->B, a->C, (const void*)a->y})
+    if (!aligned(q, 16)) return SSM_ERR_ALIGN;
+  for (const void* q : {(const void*)a->dt, (const void*)a->A, (const void*)a->omega,
+                        (const void*)a->beta, (const void*)a->gamma, (const void*)a->D,
+                        (const void*)a->saved})
+    if (q && !aligned(q, 4)) return SSM_ERR_ALIGN;
+
+  const int pb = choose_pb(d, pl);
+  FwdKey key{pl.bf16, d->dstate, pb, pl.R, pl.KR, pl.QT, pl.coord_kernel};
+  ssm::FwdParams p{};
+  p.x = a->x; p.B = a->B; p.C = a->C; p.dt = a->dt; p.A = a->A; p.omega = a->omega;
+  p.beta = a->beta; p.gamma = a->gamma; p.D = a->D; p.y = a->y; p.saved = a->saved;
+  p.batch = d->batch; p.L = d->seqlen; p.H = d->nheads; p.G = d->ngroups; p.P = d->headdim;
+  p.n_real = d->n_real; p.n_pairs = d->n_pairs; p.nchunks = pl.nchunks;
+  p.npblk = d->headdim / pb;
+  p.softplus = (d->flags & SSM_F_DT_SOFTPLUS) ? 1 : 0;
+  p.has_D = hasD ? 1 : 0;
+  p.head_rates = pl.head_rates ? 1 : 0;
+  const hipError_t e = ssm::launch_fwd(key, p, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+}
+
+int ssm_scan_bwd(const ssm_desc* d, const ssm_bwd_args* a, void* ws, size_t ws_bytes,
+                 void* stream) {
+  Plan pl;
+  int rc = make_plan(d, &pl);
+  if (rc) return rc;
+  if (!a) return SSM_ERR_NULL;
+  (void)ws; (void)ws_bytes; (void)stream;
+  return SSM_ERR_UNSUPPORTED;
+}
+
+}  // extern "C"

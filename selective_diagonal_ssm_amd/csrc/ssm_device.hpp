@@ -1,0 +1,179 @@
+// ssm_device.hpp -- gfx950 device helpers shared by the forward and reverse kernels:
+// element storage (bf16 bits or fp32), 16x16 MFMA tiles, wave-wide prefix sums.
+//
+// MFMA tile conventions (v_mfma_f32_16x16x32_bf16 and its fp32 counterpart):
+//   A fragment (16 x 32): lane l holds A[l & 15][8 * (l >> 4) + i], i = 0..7
+//   B fragment (32 x 16): lane l holds B[8 * (l >> 4) + i][l & 15], i = 0..7
+//   D tile     (16 x 16): lane l holds D[4 * (l >> 4) + i][l & 15], i = 0..3
+// An operand stored row-major with the contraction index contiguous therefore
+// loads as one 16-byte LDS read per lane (bf16).  The fp32 path keeps the same
+// fragment layout (8 floats per lane) and issues eight 16x16x4 fp32 MFMAs, so the
+// two element types share every kernel.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ssm {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------- element storage
+template <bool BF16> struct Elem;
+template <> struct Elem<true> {
+  using T = uint16_t;
+  static constexpr int kVec = 8;  // elements per 16-byte vector
+};
+template <> struct Elem<false> {
+  using T = float;
+  static constexpr int kVec = 4;
+};
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t v) {
+  return __uint_as_float(static_cast<uint32_t>(v) << 16);
+}
+
+// round to nearest even; NaN stays NaN
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+__device__ __forceinline__ float to_f32(uint16_t v) { return bf16_to_f32(v); }
+__device__ __forceinline__ float to_f32(float v) { return v; }
+
+template <typename T> __device__ __forceinline__ T from_f32(float f);
+template <> __device__ __forceinline__ uint16_t from_f32<uint16_t>(float f) { return f32_to_bf16(f); }
+template <> __device__ __forceinline__ float from_f32<float>(float f) { return f; }
+
+// 16-byte vector of elements in registers
+struct Vec16 {
+  uint4 raw;
+};
+
+template <bool BF16>
+__device__ __forceinline__ void unpack(const uint4& r, float* v) {
+  if constexpr (BF16) {
+    const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __uint_as_float(w[i] << 16);
+      v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  } else {
+    v[0] = __uint_as_float(r.x);
+    v[1] = __uint_as_float(r.y);
+    v[2] = __uint_as_float(r.z);
+    v[3] = __uint_as_float(r.w);
+  }
+}
+
+template <bool BF16>
+__device__ __forceinline__ uint4 pack(const float* v) {
+  uint4 r;
+  if constexpr (BF16) {
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      w[i] = static_cast<uint32_t>(f32_to_bf16(v[2 * i])) |
+             (static_cast<uint32_t>(f32_to_bf16(v[2 * i + 1])) << 16);
+    r.x = w[0]; r.y = w[1]; r.z = w[2]; r.w = w[3];
+  } else {
+    r.x = __float_as_uint(v[0]);
+    r.y = __float_as_uint(v[1]);
+    r.z = __float_as_uint(v[2]);
+    r.w = __float_as_uint(v[3]);
+  }
+  return r;
+}
+
+// the raw stored elements of a 16-byte vector
+template <bool BF16>
+__device__ __forceinline__ void unpack_raw(const uint4& r, typename Elem<BF16>::T* e) {
+  if constexpr (BF16) {
+    const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      e[2 * i] = static_cast<uint16_t>(w[i] & 0xffffu);
+      e[2 * i + 1] = static_cast<uint16_t>(w[i] >> 16);
+    }
+  } else {
+    e[0] = __uint_as_float(r.x);
+    e[1] = __uint_as_float(r.y);
+    e[2] = __uint_as_float(r.z);
+    e[3] = __uint_as_float(r.w);
+  }
+}
+
+// ---------------------------------------------------------------- MFMA fragments
+template <bool BF16> struct Frag;
+template <> struct Frag<true> { bf16x8 v; };
+template <> struct Frag<false> { float v[8]; };
+
+// 8 consecutive elements starting at p (16-byte aligned for bf16, 32 for fp32)
+template <bool BF16>
+__device__ __forceinline__ Frag<BF16> load_frag(const typename Elem<BF16>::T* p) {
+  Frag<BF16> f;
+  if constexpr (BF16) {
+    f.v = *reinterpret_cast<const bf16x8*>(p);
+  } else {
+    const float4 a = *reinterpret_cast<const float4*>(p);
+    const float4 b = *reinterpret_cast<const float4*>(p + 4);
+    f.v[0] = a.x; f.v[1] = a.y; f.v[2] = a.z; f.v[3] = a.w;
+    f.v[4] = b.x; f.v[5] = b.y; f.v[6] = b.z; f.v[7] = b.w;
+  }
+  return f;
+}
+
+// acc += A(16x32) * B(32x16)
+template <bool BF16>
+__device__ __forceinline__ void mma(f32x4& acc, const Frag<BF16>& a, const Frag<BF16>& b) {
+  if constexpr (BF16) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, b.v, acc, 0, 0, 0);
+  } else {
+    // lane l supplies k = 8*(l>>4) + i to instruction i, seen by the 16x16x4
+    // instruction as its k = l >> 4; the eight instructions cover all 32 k.
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[i], b.v[i], acc, 0, 0, 0);
+  }
+}
+
+// ---------------------------------------------------------------- wave primitives
+__device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
+
+// inclusive prefix sum across the 64 lanes of a wave
+__device__ __forceinline__ float wave_prefix_sum(float v) {
+  const int lane = lane_id();
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const float o = __shfl_up(v, off, kWave);
+    if (lane >= off) v += o;
+  }
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
+  return v;
+}
+
+__device__ __forceinline__ float softplus_f32(float v) {
+  return v > 20.f ? v : log1pf(expf(v));
+}
+
+__device__ __forceinline__ float sigmoid_f32(float v) { return 1.f / (1.f + expf(-v)); }
+
+// Workgroup -> work item mapping that keeps consecutive logical ids on one XCD
+// (the dispatcher places workgroup i on XCD i % 8), so the P-blocks of one slice
+// share that XCD's L2 for their common B and C reads.
+__device__ __forceinline__ int xcd_logical_id(int wg, int nwg) {
+  if (nwg % 8) return wg;
+  return (wg % 8) * (nwg / 8) + wg / 8;
+}
+
+}  // namespace ssm

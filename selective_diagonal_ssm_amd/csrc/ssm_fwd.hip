@@ -1,0 +1,504 @@
+// ssm_fwd.hip -- forward chunked scan of the state-mediated selective SSM kernel
+// for gfx950 (MI355X).
+//
+// One workgroup (4 waves) owns one (batch, head) slice and one block of PB value
+// columns, and walks the sequence chunk by chunk with the N x PB state held in
+// MFMA accumulator registers (fp32).  Per chunk of QT tokens:
+//
+//  a1  chunk-local cumulative step CD_t = sum_{r<=t} Delta_r by a wave prefix sum
+//      (Delta = softplus(dt) when flagged); the log-decay of row n is
+//      L_t[n] = -A_n CD_t and the pair angle Theta_t[k] = omega_k CD_t.
+//  a2  write prologue: rotation folding C~_t = R(-Theta_t) C_t, K~_s = R(-Theta_s) K_s
+//      (exact because a pair's rotation commutes with its scalar decay), and the
+//      two-endpoint write as rank-2R keys per token: K_s = [gamma_s B_s | beta_s B_{s-1}]
+//      with values [X_s ; X_{s-1}] (one halo token per chunk).
+//  a3  intra-chunk masked product Y = (Q K^T o M) V on bf16 MFMA (fp32 accumulate).
+//      Head decay: M_ts = exp(L_t - L_s) [s <= t] applied per element in fp32.
+//      Per-row decay: the decay is folded into the operands around the chunk
+//      midpoint, q_t = C~_t e^{L_t - L_end/2}, k_s = K~_s e^{L_end/2 - L_s}, so that no
+//      factor exceeds e^{|L_end|/2}; the mask is then the causal indicator.
+//  a4/a5  chunk state and state passing: S <- Lambda o S + (K~ o e^{L_end - L_s})^T V,
+//      then the chunk-total rotation of the pairs; S never leaves the registers
+//      (a bf16 copy in LDS feeds the next chunk's readout).
+//  a6  readout C~_t e^{L_t} S_in + Y + D X_t, stored as the io dtype.
+//
+// Sources: "When a Diagonal State Is Not Enough" (sungsoo.github.io), Part 01 and
+// Part 03 (recurrence; Theorem 24 masked linear attention form; Theorem 8 rotating
+// pairs), Parts 03 / 08.3 (SSD-MIMO rank-R writes, HybridMamba rows and
+// two-endpoint writes).
+#include "ssm_device.hpp"
+#include "ssm_kernels.hpp"
+
+namespace ssm {
+
+template <bool BF16, int N, int PB, int R, int KR, int QT, bool COORD>
+struct FwdShape {
+  using T = typename Elem<BF16>::T;
+  static constexpr int VEC = Elem<BF16>::kVec;
+  static constexpr int PAD = 16 / static_cast<int>(sizeof(T));
+  static constexpr int NC = N < 32 ? 32 : N;  // contraction width over n (zero padded)
+  static constexpr int QO = QT * R;
+  static constexpr int QK = QT * KR;
+  static constexpr bool TE = KR > R;
+  static constexpr int TEH = TE ? 1 : 0;
+  static constexpr int NS = NC + PAD;  // row stride of n-contiguous buffers
+  static constexpr int KS = QK + PAD;  // row stride of key-contiguous buffers
+  static constexpr int BROWS = (QT + TEH) * R;
+  static constexpr int NTH = 256;
+  static constexpr int NVEC_N = N / VEC;
+  static constexpr int NVEC_P = PB / VEC;
+  static constexpr int C_VECS = QO * NVEC_N;
+  static constexpr int B_VECS = BROWS * NVEC_N;
+  static constexpr int X_VECS = BROWS * NVEC_P;
+  static constexpr int C_PER = (C_VECS + NTH - 1) / NTH;
+  static constexpr int B_PER = (B_VECS + NTH - 1) / NTH;
+  static constexpr int X_PER = (X_VECS + NTH - 1) / NTH;
+  static constexpr int TQ = QO / 16, TK = QK / 16, TP = PB / 16, TN = N / 16;
+  static constexpr int ST_TILES = TN * TP;
+  static constexpr int ST_PER_WAVE = (ST_TILES + 3) / 4;
+  static_assert(QO % 16 == 0 && QK % 32 == 0, "chunk rows must fill MFMA tiles");
+  static_assert(N % 16 == 0 && PB % 16 == 0 && QT <= 64, "unsupported tile shape");
+  static_assert(KR == R || KR == 2 * R, "keys per token are R or 2R");
+};
+
+template <bool BF16, int N, int PB, int R, int KR, int QT, bool COORD>
+__global__ __launch_bounds__(256) void ssm_fwd_kernel(FwdParams p) {
+  using S = FwdShape<BF16, N, PB, R, KR, QT, COORD>;
+  using T = typename S::T;
+  constexpr int NS = S::NS, KS = S::KS, VEC = S::VEC;
+
+  __shared__ __align__(16) T sQ[S::QO * NS];
+  __shared__ __align__(16) T sQe[COORD ? S::QO * NS : 8];
+  __shared__ __align__(16) T sK[S::QK * NS];
+  __shared__ __align__(16) T sKeT[N * KS];
+  __shared__ __align__(16) T sVT[PB * KS];
+  __shared__ __align__(16) T sS[S::QO * KS];
+  __shared__ __align__(16) T sST[PB * NS];
+  __shared__ float sCD[64], sEL[64], sW[64], sBeta[64], sGamma[64];
+  __shared__ float sRate[N], sOmega[N / 2 + 1];
+  __shared__ float sMisc[4];
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int lid = xcd_logical_id(blockIdx.x, gridDim.x);
+  const int slice = lid / p.npblk, pblk = lid % p.npblk;
+  const int b = slice / p.H, h = slice % p.H;
+  const int g = h / (p.H / p.G);
+  const int p0 = pblk * PB;
+  const int L = p.L, H = p.H, G = p.G, P = p.P;
+  const int nreal = p.n_real;
+
+  if (COORD) {
+    const int na = p.n_real + p.n_pairs;
+    for (int n = tid; n < N; n += S::NTH) {
+      float r;
+      if (p.head_rates) r = p.A[h];  // one rate per head
+      else if (n < nreal) r = p.A[(size_t)h * na + n];
+      else r = p.A[(size_t)h * na + nreal + ((n - nreal) >> 1)];
+      sRate[n] = r;
+    }
+    for (int k = tid; k < p.n_pairs; k += S::NTH) sOmega[k] = p.omega[(size_t)h * p.n_pairs + k];
+  }
+  // zero the state copy and the contraction padding columns
+  for (int i = tid; i < PB * NS; i += S::NTH) sST[i] = T(0);
+  if (S::NC > N) {
+    for (int i = tid; i < S::QO * (S::NC - N); i += S::NTH) {
+      const int r = i / (S::NC - N), c = N + i % (S::NC - N);
+      sQ[r * NS + c] = T(0);
+      if (COORD) sQe[r * NS + c] = T(0);
+    }
+    for (int i = tid; i < S::QK * (S::NC - N); i += S::NTH) {
+      const int r = i / (S::NC - N), c = N + i % (S::NC - N);
+      sK[r * NS + c] = T(0);
+    }
+  }
+  const float Ah = COORD ? 0.f : p.A[h];
+  const float Dh = p.has_D ? p.D[h] : 0.f;
+
+  const T* xg = static_cast<const T*>(p.x);
+  const T* Bg = static_cast<const T*>(p.B);
+  const T* Cg = static_cast<const T*>(p.C);
+  T* yg = static_cast<T*>(p.y);
+
+  f32x4 st[S::ST_PER_WAVE];
+#pragma unroll
+  for (int k = 0; k < S::ST_PER_WAVE; ++k) st[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  uint4 rc[S::C_PER], rb[S::B_PER], rx[S::X_PER];
+  float rdt = 0.f, rbe = 0.f, rga = 0.f;
+  const uint4 zero4 = make_uint4(0, 0, 0, 0);
+
+  auto load_chunk = [&](int c) {
+    const int t0 = c * QT;
+#pragma unroll
+    for (int k = 0; k < S::C_PER; ++k) {
+      const int v = tid + S::NTH * k;
+      uint4 val = zero4;
+      if (v < S::C_VECS) {
+        const int row = v / S::NVEC_N, nv = v % S::NVEC_N;
+        const int t = t0 + row / R, o = row % R;
+        if (t < L)
+          val = *reinterpret_cast<const uint4*>(
+              Cg + ((((size_t)b * L + t) * G + g) * R + o) * N + nv * VEC);
+      }
+      rc[k] = val;
+    }
+#pragma unroll
+    for (int k = 0; k < S::B_PER; ++k) {
+      const int v = tid + S::NTH * k;
+      uint4 val = zero4;
+      if (v < S::B_VECS) {
+        const int row = v / S::NVEC_N, nv = v % S::NVEC_N;
+        const int t = t0 + row / R - S::TEH, r = row % R;
+        if (t >= 0 && t < L)
+          val = *reinterpret_cast<const uint4*>(
+              Bg + ((((size_t)b * L + t) * G + g) * R + r) * N + nv * VEC);
+      }
+      rb[k] = val;
+    }
+#pragma unroll
+    for (int k = 0; k < S::X_PER; ++k) {
+      const int v = tid + S::NTH * k;
+      uint4 val = zero4;
+      if (v < S::X_VECS) {
+        const int row = v / S::NVEC_P, pv = v % S::NVEC_P;
+        const int t = t0 + row / R - S::TEH, r = row % R;
+        if (t >= 0 && t < L)
+          val = *reinterpret_cast<const uint4*>(
+              xg + ((((size_t)b * L + t) * H + h) * R + r) * P + p0 + pv * VEC);
+      }
+      rx[k] = val;
+    }
+    if (wave == 0) {
+      const int t = t0 + lane;
+      const bool ok = lane < QT && t < L;
+      const size_t idx = ((size_t)b * L + t) * H + h;
+      rdt = ok ? p.dt[idx] : 0.f;
+      if (S::TE) {
+        rbe = ok ? p.beta[idx] : 0.f;
+        rga = ok ? p.gamma[idx] : 0.f;
+      }
+    }
+  };
+
+  // fold a rotation by -Theta into consecutive (even, odd) pair rows of a vector
+  auto unrotate = [&](float* v, int n0, float cd) {
+#pragma unroll
+    for (int i = 0; i < VEC; i += 2) {
+      const int n = n0 + i;
+      if (n >= nreal) {
+        const float th = sOmega[(n - nreal) >> 1] * cd;
+        float sn, cs;
+        sincosf(th, &sn, &cs);
+        const float a = v[i], bb = v[i + 1];
+        v[i] = cs * a + sn * bb;
+        v[i + 1] = -sn * a + cs * bb;
+      }
+    }
+  };
+
+  const int nch = p.nchunks;
+  const size_t sl_saved = (size_t)slice * (nch + 1);
+  if (p.saved) {
+    // slot 0: the zero initial state
+    for (int i = tid; i < N * PB; i += S::NTH) {
+      const int n = i / PB, pl = i % PB;
+      p.saved[(sl_saved * N + n) * P + p0 + pl] = 0.f;
+    }
+  }
+
+  load_chunk(0);
+  for (int c = 0; c < nch; ++c) {
+    const int t0 = c * QT;
+    __syncthreads();
+    // ---- a1: chunk-local cumulative step (wave prefix sum)
+    if (wave == 0) {
+      float dl = 0.f;
+      if (lane < QT && t0 + lane < L) dl = p.softplus ? softplus_f32(rdt) : rdt;
+      const float cd = wave_prefix_sum(dl);
+      const float cdend = __shfl(cd, QT - 1, kWave);
+      if (lane < QT) {
+        sCD[lane] = cd;
+        if (!COORD) {
+          sEL[lane] = __expf(-Ah * cd);
+          sW[lane] = __expf(-Ah * (cdend - cd));
+        }
+        if (S::TE) {
+          sBeta[lane] = rbe;
+          sGamma[lane] = rga;
+        }
+      }
+      if (lane == 0) {
+        sMisc[0] = cdend;
+        sMisc[1] = COORD ? 0.f : __expf(-Ah * cdend);
+      }
+    }
+    __syncthreads();
+    const float cdend = sMisc[0];
+
+    // ---- a2: operands (queries, keys, values) into LDS
+#pragma unroll
+    for (int k = 0; k < S::C_PER; ++k) {
+      const int v = tid + S::NTH * k;
+      if (v < S::C_VECS) {
+        const int row = v / S::NVEC_N, nv = v % S::NVEC_N;
+        const int n0 = nv * VEC;
+        if (COORD) {
+          float vals[VEC], q[VEC], qe[VEC];
+          unpack<BF16>(rc[k], vals);
+          const float cd = sCD[row / R];
+          unrotate(vals, n0, cd);
+#pragma unroll
+          for (int i = 0; i < VEC; ++i) {
+            const float ar = sRate[n0 + i];
+            q[i] = vals[i] * __expf(-ar * (cd - 0.5f * cdend));
+            qe[i] = vals[i] * __expf(-ar * cd);
+          }
+          *reinterpret_cast<uint4*>(sQ + row * NS + n0) = pack<BF16>(q);
+          *reinterpret_cast<uint4*>(sQe + row * NS + n0) = pack<BF16>(qe);
+        } else {
+          *reinterpret_cast<uint4*>(sQ + row * NS + n0) = rc[k];
+        }
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < S::B_PER; ++k) {
+      const int v = tid + S::NTH * k;
+      if (v < S::B_VECS) {
+        const int row = v / S::NVEC_N, nv = v % S::NVEC_N;
+        const int n0 = nv * VEC;
+        const int sl = row / R - S::TEH, r = row % R;
+        float vals[VEC];
+        unpack<BF16>(rb[k], vals);
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          // e = 0: gamma_s B_s written at s = sl; e = 1: beta_{s+1} B_s written at s+1
+          if (e == 1 && !S::TE) break;
+          const int tau = sl + e;
+          if (tau < 0 || tau >= QT || (e == 0 && sl < 0)) continue;
+          const int j = tau * KR + (e ? R : 0) + r;
+          const float w = S::TE ? (e ? sBeta[tau] : sGamma[tau]) : 1.f;
+          float u[VEC], kk[VEC], ke[VEC];
+#pragma unroll
+          for (int i = 0; i < VEC; ++i) u[i] = vals[i] * w;
+          if (COORD) {
+            const float cd = sCD[tau];
+            unrotate(u, n0, cd);
+#pragma unroll
+            for (int i = 0; i < VEC; ++i) {
+              const float ar = sRate[n0 + i];
+              kk[i] = u[i] * __expf(-ar * (0.5f * cdend - cd));
+              ke[i] = u[i] * __expf(-ar * (cdend - cd));
+            }
+          } else {
+            const float ws = sW[tau];
+#pragma unroll
+            for (int i = 0; i < VEC; ++i) {
+              kk[i] = u[i];
+              ke[i] = u[i] * ws;
+            }
+          }
+          *reinterpret_cast<uint4*>(sK + j * NS + n0) = pack<BF16>(kk);
+#pragma unroll
+          for (int i = 0; i < VEC; ++i) sKeT[(n0 + i) * KS + j] = from_f32<T>(ke[i]);
+        }
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < S::X_PER; ++k) {
+      const int v = tid + S::NTH * k;
+      if (v < S::X_VECS) {
+        const int row = v / S::NVEC_P, pv = v % S::NVEC_P;
+        const int sl = row / R - S::TEH, r = row % R;
+        T e[VEC];
+        unpack_raw<BF16>(rx[k], e);
+        if (sl >= 0) {
+          const int j = sl * KR + r;
+#pragma unroll
+          for (int i = 0; i < VEC; ++i) sVT[(pv * VEC + i) * KS + j] = e[i];
+        }
+        if (S::TE && sl + 1 < QT) {
+          const int j = (sl + 1) * KR + R + r;
+#pragma unroll
+          for (int i = 0; i < VEC; ++i) sVT[(pv * VEC + i) * KS + j] = e[i];
+        }
+      }
+    }
+    if (c + 1 < nch) load_chunk(c + 1);
+    __syncthreads();
+
+    // ---- a3: masked intra-chunk scores
+    for (int tile = wave; tile < S::TQ * S::TK; tile += 4) {
+      const int ti = tile / S::TK, tj = tile % S::TK;
+      const int tmax = (16 * ti + 15) / R;
+      const int smin = (16 * tj) / KR;
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      if (smin <= tmax) {
+#pragma unroll
+        for (int kk = 0; kk < S::NC / 32; ++kk) {
+          const auto a = load_frag<BF16>(sQ + (16 * ti + (lane & 15)) * NS + kk * 32 + 8 * (lane >> 4));
+          const auto bq = load_frag<BF16>(sK + (16 * tj + (lane & 15)) * NS + kk * 32 + 8 * (lane >> 4));
+          mma<BF16>(acc, a, bq);
+        }
+      }
+      const int col = 16 * tj + (lane & 15);
+      const int s = col / KR;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = 16 * ti + 4 * (lane >> 4) + i;
+        const int t = row / R;
+        float val = 0.f;
+        if (s <= t) {
+          val = acc[i];
+          if (!COORD) val *= __expf(-Ah * (sCD[t] - sCD[s]));
+        }
+        sS[row * KS + col] = from_f32<T>(val);
+      }
+    }
+    __syncthreads();
+
+    // ---- a6: readout of the incoming state + intra-chunk output + feedthrough
+    for (int tile = wave; tile < S::TQ * S::TP; tile += 4) {
+      const int ti = tile / S::TP, tp = tile % S::TP;
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      const T* qsrc = COORD ? sQe : sQ;
+#pragma unroll
+      for (int kk = 0; kk < S::NC / 32; ++kk) {
+        const auto a = load_frag<BF16>(qsrc + (16 * ti + (lane & 15)) * NS + kk * 32 + 8 * (lane >> 4));
+        const auto bs = load_frag<BF16>(sST + (16 * tp + (lane & 15)) * NS + kk * 32 + 8 * (lane >> 4));
+        mma<BF16>(acc, a, bs);
+      }
+      if (!COORD) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i] *= sEL[(16 * ti + 4 * (lane >> 4) + i) / R];
+      }
+      const int tmax = (16 * ti + 15) / R;
+      const int kend = ((tmax + 1) * KR + 31) / 32;
+      for (int kk = 0; kk < kend; ++kk) {
+        const auto a = load_frag<BF16>(sS + (16 * ti + (lane & 15)) * KS + kk * 32 + 8 * (lane >> 4));
+        const auto bv = load_frag<BF16>(sVT + (16 * tp + (lane & 15)) * KS + kk * 32 + 8 * (lane >> 4));
+        mma<BF16>(acc, a, bv);
+      }
+      const int pl = 16 * tp + (lane & 15);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = 16 * ti + 4 * (lane >> 4) + i;
+        const int t = row / R, o = row % R;
+        const int tg = t0 + t;
+        float val = acc[i];
+        if (p.has_D) val += Dh * to_f32(sVT[pl * KS + t * KR + o]);
+        if (tg < L) yg[((((size_t)b * L + tg) * H + h) * R + o) * P + p0 + pl] = from_f32<T>(val);
+      }
+    }
+
+    // ---- a4/a5: chunk state and state passing (registers)
+#pragma unroll
+    for (int k = 0; k < S::ST_PER_WAVE; ++k) {
+      const int tile = wave + 4 * k;
+      if (tile < S::ST_TILES) {
+        const int tn = tile / S::TP, tp = tile % S::TP;
+        f32x4 acc = st[k];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int n = 16 * tn + 4 * (lane >> 4) + i;
+          acc[i] *= COORD ? __expf(-sRate[n] * cdend) : sMisc[1];
+        }
+#pragma unroll
+        for (int kk = 0; kk < S::QK / 32; ++kk) {
+          const auto a = load_frag<BF16>(sKeT + (16 * tn + (lane & 15)) * KS + kk * 32 + 8 * (lane >> 4));
+          const auto bv = load_frag<BF16>(sVT + (16 * tp + (lane & 15)) * KS + kk * 32 + 8 * (lane >> 4));
+          mma<BF16>(acc, a, bv);
+        }
+        if (COORD) {
+#pragma unroll
+          for (int i = 0; i < 4; i += 2) {
+            const int n = 16 * tn + 4 * (lane >> 4) + i;
+            if (n >= nreal) {
+              const float th = sOmega[(n - nreal) >> 1] * cdend;
+              float sn, cs;
+              sincosf(th, &sn, &cs);
+              const float a0 = acc[i], a1 = acc[i + 1];
+              acc[i] = cs * a0 - sn * a1;
+              acc[i + 1] = sn * a0 + cs * a1;
+            }
+          }
+        }
+        st[k] = acc;
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < S::ST_PER_WAVE; ++k) {
+      const int tile = wave + 4 * k;
+      if (tile < S::ST_TILES) {
+        const int tn = tile / S::TP, tp = tile % S::TP;
+        const int pl = 16 * tp + (lane & 15);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int n = 16 * tn + 4 * (lane >> 4) + i;
+          sST[pl * NS + n] = from_f32<T>(st[k][i]);
+          if (p.saved) p.saved[((sl_saved + c + 1) * N + n) * P + p0 + pl] = st[k][i];
+        }
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------ dispatch
+#define SSM_FWD_VARIANTS(X)                 \
+  /* fp32 io */                             \
+  X(false, 16, 16, 1, 1, 64, false)         \
+  X(false, 32, 16, 1, 1, 64, false)         \
+  X(false, 32, 16, 2, 2, 32, false)         \
+  X(false, 16, 16, 1, 2, 16, true)          \
+  X(false, 32, 16, 1, 2, 16, true)          \
+  X(false, 32, 16, 2, 4, 16, true)          \
+  X(false, 32, 16, 1, 1, 32, true)          \
+  X(false, 32, 16, 2, 2, 16, true)          \
+  /* bf16 io, head decay */                 \
+  X(true, 32, 16, 1, 1, 64, false)          \
+  X(true, 64, 16, 1, 1, 64, false)          \
+  X(true, 64, 16, 1, 1, 32, false)          \
+  X(true, 128, 16, 1, 1, 64, false)         \
+  X(true, 128, 32, 1, 1, 64, false)         \
+  X(true, 128, 64, 1, 1, 64, false)         \
+  X(true, 64, 16, 2, 2, 32, false)          \
+  X(true, 64, 16, 4, 4, 16, false)          \
+  X(true, 64, 32, 4, 4, 16, false)          \
+  X(true, 64, 16, 4, 4, 8, false)           \
+  /* bf16 io, per-row decay / pairs / two-endpoint */ \
+  X(true, 32, 16, 1, 2, 16, true)           \
+  X(true, 64, 16, 1, 2, 16, true)           \
+  X(true, 64, 16, 2, 4, 16, true)           \
+  X(true, 64, 16, 2, 4, 8, true)            \
+  X(true, 64, 32, 2, 4, 16, true)           \
+  X(true, 64, 16, 1, 1, 32, true)           \
+  X(true, 64, 16, 2, 2, 16, true)           \
+  X(true, 64, 16, 4, 4, 16, true)           \
+  X(true, 64, 16, 4, 8, 8, true)
+
+bool fwd_variant_exists(const FwdKey& k) {
+#define SSM_FWD_MATCH(BF, NN, PBB, RR, KRR, QTT, CO)                                         \
+  if (k.bf16 == BF && k.N == NN && k.PB == PBB && k.R == RR && k.KR == KRR && k.QT == QTT && \
+      k.coord == CO)                                                                         \
+    return true;
+  SSM_FWD_VARIANTS(SSM_FWD_MATCH)
+#undef SSM_FWD_MATCH
+  return false;
+}
+
+hipError_t launch_fwd(const FwdKey& k, const FwdParams& p, hipStream_t stream) {
+  const int nwg = p.batch * p.H * p.npblk;
+  if (nwg == 0 || p.nchunks == 0) return hipSuccess;
+#define SSM_FWD_LAUNCH(BF, NN, PBB, RR, KRR, QTT, CO)                                        \
+  if (k.bf16 == BF && k.N == NN && k.PB == PBB && k.R == RR && k.KR == KRR && k.QT == QTT && \
+      k.coord == CO) {                                                                       \
+    hipLaunchKernelGGL((ssm_fwd_kernel<BF, NN, PBB, RR, KRR, QTT, CO>), dim3(nwg), dim3(256), \
+                       0, stream, p);                                                        \
+    return hipGetLastError();                                                                \
+  }
+  SSM_FWD_VARIANTS(SSM_FWD_LAUNCH)
+#undef SSM_FWD_LAUNCH
+  return hipErrorInvalidValue;
+}
+
+}  // namespace ssm

@@ -1,0 +1,74 @@
+// ssm_kernels.hpp -- launch parameters and host-side launch entry points of the
+// HIP kernels (internal to libssmscan; the public boundary is include/ssm_scan.h).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ssm {
+
+struct FwdParams {
+  const void* x;
+  const void* B;
+  const void* C;
+  const float* dt;
+  const float* A;
+  const float* omega;
+  const float* beta;
+  const float* gamma;
+  const float* D;
+  void* y;
+  float* saved;  // [batch][nheads][nchunks + 1][N][P] fp32, or null
+  int batch, L, H, G, P, n_real, n_pairs, nchunks, npblk;
+  int softplus, has_D;
+  int head_rates;  // A holds one rate per head even though the per-row kernel runs
+};
+
+struct BwdParams {
+  const void* x;
+  const void* B;
+  const void* C;
+  const void* dy;
+  const float* dt;
+  const float* A;
+  const float* omega;
+  const float* beta;
+  const float* gamma;
+  const float* D;
+  const float* saved;
+  void* dx;
+  void* dB;
+  void* dC;
+  float* ddt;
+  float* dbeta;
+  float* dgamma;
+  float* part;     // per-(slice, segment) parameter-gradient partials (workspace)
+  float* gseg;     // segment-boundary adjoint states (workspace)
+  float* dA;
+  float* domega;
+  float* dD;
+  int batch, L, H, G, P, n_real, n_pairs, nchunks, nseg, chunks_per_seg;
+  int softplus, has_D, npart;
+  int head_rates;
+};
+
+// Kernel variant key: io dtype, state size, P-block, rank, keys per token, tokens
+// per chunk, decay mode.
+struct FwdKey {
+  bool bf16;
+  int N, PB, R, KR, QT;
+  bool coord;
+};
+
+// Returns hipSuccess, or hipErrorInvalidValue when no variant matches.
+hipError_t launch_fwd(const FwdKey& key, const FwdParams& p, hipStream_t stream);
+bool fwd_variant_exists(const FwdKey& key);
+
+struct BwdKey {
+  bool bf16;
+  int N, P, R, KR, QT;
+  bool coord;
+};
+hipError_t launch_bwd(const BwdKey& key, const BwdParams& p, hipStream_t stream);
+bool bwd_variant_exists(const BwdKey& key);
+
+}  // namespace ssm

@@ -1,0 +1,66 @@
+"""torch-facing wrapper: allocate outputs / saved states / workspace and call the C ABI.
+
+Only allocation and argument marshalling happen here.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import _lib
+
+
+def _dtype(io_dtype: str):
+    return torch.bfloat16 if io_dtype == "bf16" else torch.float32
+
+
+def forward(desc_dict: dict, io_dtype: str, x, B, C, dt, A, omega=None, beta=None, gamma=None,
+            D=None, save_for_backward: bool = False, chunk: int = 0, stream=None):
+    """Run the forward scan.  Returns (y, saved) where saved is None unless
+    ``save_for_backward``."""
+    desc = _lib.make_desc(desc_dict, io_dtype, chunk)
+    d = desc_dict
+    y = torch.empty((d["batch"], d["seqlen"], d["nheads"], d["rank_out"], d["headdim"]),
+                    dtype=_dtype(io_dtype), device=x.device)
+    saved = None
+    if save_for_backward:
+        nbytes = _lib.saved_bytes(desc)
+        saved = torch.empty(max(nbytes // 4, 1), dtype=torch.float32, device=x.device)
+    wsb = _lib.workspace_bytes(desc, False)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=x.device) if wsb else None
+    _lib.scan_fwd(desc, x, B, C, dt, A, y, omega=omega, beta=beta, gamma=gamma, D=D, saved=saved,
+                  ws=ws, stream=stream)
+    return y, saved
+
+
+def backward(desc_dict: dict, io_dtype: str, x, B, C, dy, dt, A, saved, omega=None, beta=None,
+             gamma=None, D=None, chunk: int = 0, stream=None, want=("dA", "domega", "dbeta",
+                                                                     "dgamma", "dD")):
+    """Run the fused reverse pass.  Returns a dict of gradient tensors."""
+    desc = _lib.make_desc(desc_dict, io_dtype, chunk)
+    d = desc_dict
+    dev = x.device
+    f32 = torch.float32
+    g = {
+        "dx": torch.empty_like(x),
+        "dB": torch.empty_like(B),
+        "dC": torch.empty_like(C),
+        "ddt": torch.empty_like(dt),
+    }
+    if "dA" in want:
+        g["dA"] = torch.empty_like(A)
+    if "domega" in want and d["n_pairs"] > 0:
+        g["domega"] = torch.empty((d["nheads"], d["n_pairs"]), dtype=f32, device=dev)
+    if d["two_endpoint"]:
+        if "dbeta" in want:
+            g["dbeta"] = torch.empty_like(dt)
+        if "dgamma" in want:
+            g["dgamma"] = torch.empty_like(dt)
+    if d["has_D"] and "dD" in want:
+        g["dD"] = torch.empty((d["nheads"],), dtype=f32, device=dev)
+    wsb = _lib.workspace_bytes(desc, True)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev) if wsb else None
+    _lib.scan_bwd(desc, x, B, C, dy, dt, A, saved, g["dx"], g["dB"], g["dC"], g["ddt"],
+                  omega=omega, beta=beta, gamma=gamma, D=D, dA=g.get("dA"),
+                  domega=g.get("domega"), dbeta=g.get("dbeta"), dgamma=g.get("dgamma"),
+                  dD=g.get("dD"), ws=ws, stream=stream)
+    return g

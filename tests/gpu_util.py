@@ -1,0 +1,40 @@
+"""Helpers shared by the GPU parity tests: run the HIP path on a problem from
+workloads.py and compare with the oracle by relative L2 (fp64)."""
+import numpy as np
+import torch
+
+import selective_diagonal_ssm_amd as ssm
+import workloads
+
+BF16_TOL = 1e-2   # bf16 path: rel-L2 per tensor
+F32_TOL = 1e-4    # fp32 path
+
+
+def rel_l2(a, ref):
+    a = np.asarray(a, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    den = np.linalg.norm(ref.ravel())
+    num = np.linalg.norm((a - ref).ravel())
+    return num / den if den > 0 else num
+
+
+def tol(prob):
+    return BF16_TOL if prob["dtype"] == "bf16" else F32_TOL
+
+
+def run_fwd(prob, chunk=0, save=False):
+    t = workloads.to_device(prob)
+    y, saved = ssm.forward(prob["desc"], prob["dtype"], t["x"], t["B"], t["C"], t["dt"], t["A"],
+                           omega=t.get("omega"), beta=t.get("beta"), gamma=t.get("gamma"),
+                           D=t.get("D"), save_for_backward=save, chunk=chunk)
+    torch.cuda.synchronize()
+    return y.float().cpu().numpy().astype(np.float64), saved, t
+
+
+def run_bwd(prob, chunk=0):
+    y, saved, t = run_fwd(prob, chunk=chunk, save=True)
+    g = ssm.backward(prob["desc"], prob["dtype"], t["x"], t["B"], t["C"], t["dy"], t["dt"],
+                     t["A"], saved, omega=t.get("omega"), beta=t.get("beta"),
+                     gamma=t.get("gamma"), D=t.get("D"), chunk=chunk)
+    torch.cuda.synchronize()
+    return y, {k: v.float().cpu().numpy().astype(np.float64) for k, v in g.items()}

@@ -1,0 +1,98 @@
+"""CPU checks of the C-ABI library: it loads, exports every symbol the header
+declares, and rejects bad descriptors / pointers before any GPU call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import selective_diagonal_ssm_amd as ssm
+from selective_diagonal_ssm_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    src = open(os.path.join(ROOT, "include", "ssm_scan.h")).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(ssm_\w+)\s*\(", src, re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(_lib.LIB_PATH)
+    names = header_functions()
+    assert set(names) == set(_lib.EXPORTS), names
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_abi_version_and_status_strings():
+    lib = ssm.load()
+    assert lib.ssm_abi_version() == 1
+    for s in range(0, -8, -1):
+        assert lib.ssm_status_string(s)
+
+
+def base_desc(**kw):
+    d = dict(batch=2, seqlen=100, nheads=4, ngroups=4, headdim=64, dstate=64, rank_in=1,
+             rank_out=1, n_real=64, n_pairs=0, decay_mode="head", dt_softplus=True,
+             two_endpoint=False, has_D=True)
+    d.update(kw)
+    return d
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(), 0),
+    (dict(nheads=3, ngroups=2), -2),            # groups must divide heads
+    (dict(n_real=60), -2),                      # n_real + 2 n_pairs != dstate
+    (dict(decay_mode="head", n_real=32, n_pairs=16), -2),  # pairs need per-row mode
+    (dict(rank_in=2, rank_out=1), -2),          # D needs O == R
+    (dict(rank_in=2, rank_out=1, has_D=False), -5),  # O != R not implemented on GPU
+    (dict(headdim=24), -5),
+    (dict(dstate=48, n_real=48), -5),
+    (dict(decay_mode="coord", n_real=31, n_pairs=16, dstate=63), -5),
+    (dict(seqlen=-1), -2),
+])
+def test_descriptor_validation(kw, status):
+    d = _lib.make_desc(base_desc(**kw), "bf16")
+    assert ssm.check_desc(d) == status
+
+
+def test_bad_dtype_and_flags():
+    d = _lib.make_desc(base_desc(), "bf16")
+    d.io_dtype = 7
+    assert ssm.check_desc(d) == -3
+    d = _lib.make_desc(base_desc(), "bf16")
+    d.flags = 64
+    assert ssm.check_desc(d) == -2
+
+
+def test_chunk_and_saved_bytes():
+    d = _lib.make_desc(base_desc(), "bf16")
+    assert ssm.chunk_tokens(d) == 64
+    nch = (100 + 63) // 64
+    assert ssm.saved_bytes(d) == 2 * 4 * (nch + 1) * 64 * 64 * 4
+    dh = _lib.make_desc(base_desc(decay_mode="coord", n_real=32, n_pairs=16, rank_in=2,
+                                  rank_out=2, two_endpoint=True), "bf16")
+    assert ssm.chunk_tokens(dh) == 16
+
+
+def test_null_pointers_rejected_before_launch():
+    lib = ssm.load()
+    d = _lib.make_desc(base_desc(), "bf16")
+    args = _lib.SsmFwdArgs()
+    assert lib.ssm_scan_fwd(ctypes.byref(d), ctypes.byref(args), None, 0, None) == -1
+    assert lib.ssm_scan_fwd(ctypes.byref(d), None, None, 0, None) == -1
+    assert lib.ssm_scan_fwd(None, ctypes.byref(args), None, 0, None) == -1
+    # misaligned pointers (never dereferenced: validation fails first)
+    fake = [0x1000 * (i + 1) for i in range(11)]
+    args = _lib.SsmFwdArgs(*fake)
+    args.omega = None
+    args.beta = None
+    args.gamma = None
+    args.saved = None
+    args.x = 0x1002
+    assert lib.ssm_scan_fwd(ctypes.byref(d), ctypes.byref(args), None, 0, None) == -4
+    # D given without the flag
+    d2 = _lib.make_desc(base_desc(has_D=False), "bf16")
+    args.x = 0x1000
+    assert lib.ssm_scan_fwd(ctypes.byref(d2), ctypes.byref(args), None, 0, None) == -1

@@ -1,0 +1,138 @@
+"""GPU parity of the forward scan against the fp64 oracle (relative L2 per tensor).
+
+Tolerances: 1e-4 for the fp32 path, 1e-2 for the bf16 path.  Small shapes use
+ragged lengths (not a multiple of the chunk) and several chunks; full-size
+workloads are checked on sampled (batch, head) slices, which the oracle
+computes independently of the rest.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from gpu_util import rel_l2, run_fwd, tol
+
+pytestmark = pytest.mark.gpu
+
+
+SMALL_CASES = {
+    # fp32 path: the same kernels as bf16 with fp32 operands, checked at 1e-4
+    "f32_siso_full": ("siso_f32", {}),
+    "f32_siso_ragged": ("siso_f32", dict(batch=2, seqlen=200, nheads=3, ngroups=3)),
+    "f32_head_n32": ("ssd_siso", dict(dtype="f32", dstate=32, n_real=32, headdim=16, batch=2,
+                                      nheads=2, ngroups=2, seqlen=150)),
+    "f32_head_r2": ("ssd_mimo", dict(dtype="f32", dstate=32, n_real=32, headdim=16, rank_in=2,
+                                     rank_out=2, batch=2, nheads=2, ngroups=2, seqlen=100)),
+    "f32_hybrid_r2": ("hybrid", dict(dtype="f32", dstate=32, n_real=16, n_pairs=8, headdim=16,
+                                     batch=2, nheads=2, ngroups=2, seqlen=77)),
+    "f32_hybrid_r1": ("hybrid", dict(dtype="f32", dstate=32, n_real=16, n_pairs=8, headdim=16,
+                                     rank_in=1, rank_out=1, batch=2, nheads=2, ngroups=2,
+                                     seqlen=70)),
+    "f32_hybrid_n16": ("hybrid", dict(dtype="f32", dstate=16, n_real=8, n_pairs=4, headdim=16,
+                                      rank_in=1, rank_out=1, batch=1, nheads=2, ngroups=2,
+                                      seqlen=90)),
+    "f32_coord_plain_r1": ("hybrid", dict(dtype="f32", two_endpoint=False, dstate=32,
+                                          n_real=16, n_pairs=8, headdim=16, rank_in=1,
+                                          rank_out=1, batch=2, nheads=2, ngroups=2,
+                                          seqlen=75)),
+    "f32_coord_plain_r2": ("hybrid", dict(dtype="f32", two_endpoint=False, dstate=32,
+                                          n_real=16, n_pairs=8, headdim=16, batch=2, nheads=2,
+                                          ngroups=2, seqlen=61)),
+    # bf16 path
+    "bf16_ssd_siso": ("ssd_siso", dict(batch=2, seqlen=300, nheads=3, ngroups=3)),
+    "bf16_ssd_siso_n64": ("ssd_siso", dict(batch=2, seqlen=130, nheads=2, ngroups=2, dstate=64,
+                                           n_real=64)),
+    "bf16_ssd_mimo": ("ssd_mimo", dict(batch=2, seqlen=200, nheads=2, ngroups=2)),
+    "bf16_hybrid": ("hybrid", dict(batch=2, seqlen=150, nheads=2, ngroups=2)),
+    "bf16_hybrid_r1": ("hybrid_r1", dict(batch=2, seqlen=150, nheads=2, ngroups=2)),
+    "bf16_groups": ("ssd_siso", dict(batch=1, seqlen=100, nheads=4, ngroups=2, dstate=64,
+                                     n_real=64)),
+    "bf16_len1": ("ssd_siso", dict(batch=2, seqlen=1, nheads=2, ngroups=2, dstate=64,
+                                   n_real=64)),
+    "bf16_len_chunk": ("ssd_siso", dict(batch=1, seqlen=64, nheads=2, ngroups=2, dstate=64,
+                                        n_real=64)),
+    "bf16_len_chunk1": ("hybrid", dict(batch=1, seqlen=17, nheads=2, ngroups=2)),
+}
+
+
+@pytest.mark.parametrize("case", sorted(SMALL_CASES))
+def test_fwd_small_matches_oracle(case):
+    name, kw = SMALL_CASES[case]
+    prob = workloads.make_problem(workloads.spec(name, **kw), seed=0)
+    print(f"[fwd] case={case} desc={prob['desc']}", flush=True)
+    y, _, _ = run_fwd(prob)
+    ref, _ = oracle.fwd(prob)
+    err = rel_l2(y, ref)
+    print(f"[fwd] case={case} rel_l2={err:.3e}", flush=True)
+    assert err <= tol(prob), err
+
+
+FULL = ["ssd_siso", "ssd_mimo", "hybrid", "hybrid_r1"]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_fwd_full_size_sampled_slices(name):
+    prob = workloads.make_problem(name, seed=0)
+    d = prob["desc"]
+    print(f"[fwd-full] {name} desc={d}", flush=True)
+    y, _, _ = run_fwd(prob)
+    rng = np.random.default_rng(1)
+    slices = [(int(rng.integers(d["batch"])), int(rng.integers(d["nheads"]))) for _ in range(6)]
+    slices += [(0, 0), (d["batch"] - 1, d["nheads"] - 1)]
+    ref, _ = oracle.fwd(prob, slices=slices)
+    for b, h in slices:
+        err = rel_l2(y[b, :, h], ref[b, :, h])
+        print(f"[fwd-full] {name} slice=({b},{h}) rel_l2={err:.3e}", flush=True)
+        assert err <= tol(prob), (b, h, err)
+    assert np.isfinite(y).all()
+
+
+def test_fwd_deterministic():
+    prob = workloads.make_problem(workloads.spec("hybrid", batch=2, seqlen=500, nheads=4,
+                                                 ngroups=4), seed=3)
+    y1, _, _ = run_fwd(prob)
+    y2, _, _ = run_fwd(prob)
+    assert np.array_equal(y1, y2)
+
+
+@pytest.mark.parametrize("name,kw,chunks", [
+    ("ssd_siso", dict(batch=2, seqlen=300, nheads=2, ngroups=2, dstate=64, n_real=64), (32, 64)),
+    ("ssd_mimo", dict(batch=2, seqlen=200, nheads=2, ngroups=2), (8, 16)),
+    ("hybrid", dict(batch=2, seqlen=150, nheads=2, ngroups=2), (8, 16)),
+])
+def test_fwd_chunk_size_invariance(name, kw, chunks):
+    prob = workloads.make_problem(workloads.spec(name, **kw), seed=5)
+    ref, _ = oracle.fwd(prob)
+    ys = []
+    for q in chunks:
+        y, _, _ = run_fwd(prob, chunk=q)
+        err = rel_l2(y, ref)
+        print(f"[chunk] {name} chunk={q} rel_l2={err:.3e}", flush=True)
+        assert err <= tol(prob)
+        ys.append(y)
+    assert rel_l2(ys[0], ys[1]) <= tol(prob)
+
+
+def test_fwd_siso_recovery_cross_kernel():
+    # head decay routed through the per-row kernel (two-endpoint flag with
+    # beta = 0, gamma = 1) reproduces the head-decay SSD kernel: the exact SISO
+    # special case of the HybridMamba construction.
+    prob = workloads.make_problem(workloads.spec("ssd_siso", batch=2, seqlen=130, nheads=2,
+                                                 ngroups=2, dstate=64, n_real=64), seed=7)
+    y_head, _, _ = run_fwd(prob)
+    te = dict(prob)
+    te["desc"] = dict(prob["desc"], two_endpoint=True)
+    te["beta"] = np.zeros_like(prob["dt"])
+    te["gamma"] = np.ones_like(prob["dt"])
+    y_coord, _, _ = run_fwd(te)
+    ref, _ = oracle.fwd(prob)
+    assert rel_l2(y_head, ref) <= 1e-2 and rel_l2(y_coord, ref) <= 1e-2
+    assert rel_l2(y_coord, y_head) <= 1e-2
+
+
+def test_fwd_empty_is_noop():
+    prob = workloads.make_problem(workloads.spec("ssd_siso", batch=1, seqlen=0, nheads=2,
+                                                 ngroups=2, dstate=64, n_real=64), seed=0)
+    y, _, _ = run_fwd(prob)
+    assert y.size == 0

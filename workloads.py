@@ -125,3 +125,20 @@ def make_problem(spec_or_name, seed: int = 0, with_dy: bool | None = None) -> di
     prob = dict(desc={k: s[k] for k in DESC_KEYS}, dtype=s["dtype"], chunk=s.get("chunk", 0),
                 x=x, B=B, C=C, dt=dt, A=A, omega=omega, beta=beta, gamma=gamma, D=D, dy=dy)
     return prob
+
+
+def to_device(prob: dict, device="cuda"):
+    """Copy a problem's arrays to torch tensors on `device` (x, B, C, dy in the
+    io dtype; the rest fp32)."""
+    import torch
+
+    io = torch.bfloat16 if prob["dtype"] == "bf16" else torch.float32
+    out = {}
+    for k in ("x", "B", "C", "dy"):
+        if prob.get(k) is not None:
+            out[k] = torch.from_numpy(prob[k]).to(device=device).to(io).contiguous()
+    for k in ("dt", "A", "omega", "beta", "gamma", "D"):
+        v = prob.get(k)
+        if v is not None and (k != "omega" or v.size):
+            out[k] = torch.from_numpy(np.ascontiguousarray(v)).to(device=device).contiguous()
+    return out
