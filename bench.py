@@ -1,0 +1,230 @@
+#!/usr/bin/env python3
+"""Throughput of the state-mediated selective SSM scan on one MI355X.
+
+One step = the whole hot path over one batch of synthetic input: the forward
+chunked scan (writing the chunk-boundary states the reverse pass needs) and the
+fused reverse-mode pass.  The default workload is the Mamba-2-style SSD SISO
+problem (batch 8, L 2048, 24 heads, P 64, N 128, bf16, chunk 64), seeded
+synthetic inputs already resident in HBM.
+
+Prints ONE JSON line: metric, value (Mtokens/s; a token is one (batch, position)
+across all heads), ms_per_step, the roofline of the dominant kernel (timed live
+with HIP events on the stream the kernels run on), and the fp64 CPU oracle timed
+on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import workloads  # noqa: E402
+
+METRIC = "SSM-core fwd/bwd Mtokens/s (bf16) and % of HBM/MFMA roofline on 1 MI355X"
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+
+
+def algorithmic_bytes(desc: dict, io_bytes: int, direction: str) -> int:
+    """Compulsory HBM bytes of one launch: every input read once, every output
+    written once (per-head parameters and chunk states excluded)."""
+    b, L, H, G = desc["batch"], desc["seqlen"], desc["nheads"], desc["ngroups"]
+    P, N, R, O = desc["headdim"], desc["dstate"], desc["rank_in"], desc["rank_out"]
+    te = 1 if desc["two_endpoint"] else 0
+    tok = b * L
+    if direction == "fwd":
+        per_h = (R * P + O * P) * io_bytes + 4 + 8 * te            # x, y, dt, beta, gamma
+        per_g = (R * N + O * N) * io_bytes                          # B, C
+    else:
+        per_h = (2 * R * P + O * P) * io_bytes + 8 + 16 * te        # x, dx, dy, dt, ddt (+beta/gamma, grads)
+        per_g = 2 * (R * N + O * N) * io_bytes                      # B, C, dB, dC
+    return tok * (H * per_h + G * per_g)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in ("ssm_fwd.hip", "ssm_bwd.hip", "ssm_device.hpp"):
+        p = os.path.join(ROOT, "selective_diagonal_ssm_amd", "csrc", f)
+        if os.path.exists(p):
+            h.update(open(p, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from committed rocprofv3 counter summaries, only if
+    they were taken on the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("kernel_hash") != kernel_source_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(prob: dict, mode: str, target_s: float = 15.0):
+    import oracle
+
+    oracle.build(force=False)
+    d = prob["desc"]
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or len(os.sched_getaffinity(0))
+    os.environ["OMP_NUM_THREADS"] = str(threads)
+    all_slices = [(b, h) for b in range(d["batch"]) for h in range(d["nheads"])]
+
+    def run(sl):
+        t0 = time.perf_counter()
+        oracle.fwd(prob, slices=sl)
+        if mode == "fwdbwd":
+            oracle.bwd(prob, prob["dy"], slices=sl)
+        return time.perf_counter() - t0
+
+    k = min(len(all_slices), threads)
+    t_cal = run(all_slices[:k])
+    k2 = int(min(len(all_slices), max(k, k * target_s / max(t_cal, 1e-3))))
+    k2 = max(threads, (k2 // threads) * threads) if k2 >= threads else k2
+    k2 = min(k2, len(all_slices))
+    sample = all_slices[:k2]
+    t = run(sample)
+    tokens = k2 * d["seqlen"] / d["nheads"]  # (batch, position) tokens across all heads
+    return {"value": tokens / t / 1e6, "unit": "Mtokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{k2} of {len(all_slices)} (batch, head) slices, full length "
+                      f"{d['seqlen']}, {'forward + reverse' if mode == 'fwdbwd' else 'forward'}"
+                      f", fp64, {t:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="ssd_siso", choices=sorted(workloads.WORKLOADS))
+    ap.add_argument("--mode", default="fwdbwd", choices=["fwd", "fwdbwd"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(every (batch, head) slice is independent; see the sharding notes).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import selective_diagonal_ssm_amd as ssm
+
+    prob = workloads.make_problem(args.workload, seed=0,
+                                  with_dy=(args.mode == "fwdbwd"))
+    d = prob["desc"]
+    io = prob["dtype"]
+    t = workloads.to_device(prob)
+    chunk = prob.get("chunk", 0)
+    desc = ssm.make_desc(d, io, chunk)
+    dev = t["x"].device
+    y = torch.empty((d["batch"], d["seqlen"], d["nheads"], d["rank_out"], d["headdim"]),
+                    dtype=t["x"].dtype, device=dev)
+    saved = None
+    grads = {}
+    if args.mode == "fwdbwd":
+        saved = torch.empty(ssm.saved_bytes(desc) // 4, dtype=torch.float32, device=dev)
+        grads = {"dx": torch.empty_like(t["x"]), "dB": torch.empty_like(t["B"]),
+                 "dC": torch.empty_like(t["C"]), "ddt": torch.empty_like(t["dt"]),
+                 "dA": torch.empty_like(t["A"])}
+        if d["n_pairs"]:
+            grads["domega"] = torch.empty_like(t["omega"])
+        if d["two_endpoint"]:
+            grads["dbeta"] = torch.empty_like(t["dt"])
+            grads["dgamma"] = torch.empty_like(t["dt"])
+        if d["has_D"]:
+            grads["dD"] = torch.empty_like(t["D"])
+    ws_f = ssm.workspace_bytes(desc, False)
+    ws_b = ssm.workspace_bytes(desc, True) if args.mode == "fwdbwd" else 0
+    ws = torch.empty(max(ws_f, ws_b, 1), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def fwd():
+        ssm.scan_fwd(desc, t["x"], t["B"], t["C"], t["dt"], t["A"], y, omega=t.get("omega"),
+                     beta=t.get("beta"), gamma=t.get("gamma"), D=t.get("D"), saved=saved, ws=ws,
+                     stream=stream)
+
+    def bwd():
+        ssm.scan_bwd(desc, t["x"], t["B"], t["C"], t["dy"], t["dt"], t["A"], saved, grads["dx"],
+                     grads["dB"], grads["dC"], grads["ddt"], omega=t.get("omega"),
+                     beta=t.get("beta"), gamma=t.get("gamma"), D=t.get("D"), dA=grads.get("dA"),
+                     domega=grads.get("domega"), dbeta=grads.get("dbeta"),
+                     dgamma=grads.get("dgamma"), dD=grads.get("dD"), ws=ws, stream=stream)
+
+    for _ in range(args.warmup):
+        fwd()
+        if args.mode == "fwdbwd":
+            bwd()
+    torch.cuda.synchronize()
+
+    # events on the stream the kernels are enqueued on (torch's current stream)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    start.record(stream)
+    for k in range(args.steps):
+        ev[k][0].record(stream)
+        fwd()
+        ev[k][1].record(stream)
+        if args.mode == "fwdbwd":
+            bwd()
+        ev[k][2].record(stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = start.elapsed_time(end)
+    fwd_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    bwd_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev])) if args.mode == "fwdbwd" else 0.0
+    ms_per_step = total_ms / args.steps
+    tokens = d["batch"] * d["seqlen"]
+    value = tokens / (ms_per_step * 1e-3) / 1e6
+
+    io_bytes = 2 if io == "bf16" else 4
+    kern = "bwd" if bwd_ms > fwd_ms else "fwd"
+    kms = bwd_ms if kern == "bwd" else fwd_ms
+    abytes = algorithmic_bytes(d, io_bytes, kern)
+    achieved = abytes / (kms * 1e-3) / 1e9
+    traffic = measured_traffic(kern, args.workload)
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "kernel": f"ssm_{kern}", "algorithmic_bytes_per_launch": abytes,
+                "avg_launch_ms": round(kms, 4)}
+    fwd_bytes = algorithmic_bytes(d, io_bytes, "fwd")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(prob, args.mode)
+
+    out = {
+        "metric": METRIC, "value": round(value, 3), "unit": "Mtokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if io == "bf16" else "f32", "data": "synthetic",
+        "config": {"workload": args.workload, "batch": d["batch"], "seq_len": d["seqlen"],
+                   "nheads": d["nheads"], "headdim": d["headdim"], "dstate": d["dstate"],
+                   "rank": d["rank_in"], "decay": d["decay_mode"], "n_pairs": d["n_pairs"],
+                   "two_endpoint": d["two_endpoint"], "chunk": ssm.chunk_tokens(desc),
+                   "step": "forward + reverse" if args.mode == "fwdbwd" else "forward"},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "breakdown": {"fwd_ms": round(fwd_ms, 4), "bwd_ms": round(bwd_ms, 4),
+                      "fwd_mtok_s": round(tokens / (fwd_ms * 1e-3) / 1e6, 3),
+                      "fwd_hbm_frac": round(fwd_bytes / (fwd_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                      "wall_s": round(wall, 3)},
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

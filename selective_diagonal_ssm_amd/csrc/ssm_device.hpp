@@ -129,6 +129,37 @@ __device__ __forceinline__ Frag<BF16> load_frag(const typename Elem<BF16>::T* p)
   return f;
 }
 
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+// Fragment whose contraction index runs along the ROWS of a row-major buffer:
+// lane l receives buf[8 * (l >> 4) + i][l & 15] (i = 0..7) of the 32 x 16 block at
+// `base` (row stride `ld` elements).  Serves as a B operand stored [k][n] or an A
+// operand stored transposed [k][m].  bf16 uses the gfx950 LDS transpose read
+// (ds_read_b64_tr_b16): inside each 16-lane group, lanes 4r..4r+3 supply the four
+// 4-element pieces of row r of a 4 x 16 block and lane i receives its column i.
+template <bool BF16>
+__device__ __forceinline__ Frag<BF16> load_frag_tr(const typename Elem<BF16>::T* base, int ld) {
+  const int l = threadIdx.x & 63;
+  Frag<BF16> f;
+  if constexpr (BF16) {
+    const int row = 8 * (l >> 4) + ((l >> 2) & 3);
+    const int col = 4 * (l & 3);
+    typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+    const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_i16x4*)(base + row * ld + col));
+    const i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_i16x4*)(base + (row + 4) * ld + col));
+    typedef short i16x8 __attribute__((ext_vector_type(8)));
+    const i16x8 c = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+    f.v = __builtin_bit_cast(bf16x8, c);
+  } else {
+    const int col = l & 15, row0 = 8 * (l >> 4);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) f.v[i] = base[(row0 + i) * ld + col];
+  }
+  return f;
+}
+
 // acc += A(16x32) * B(32x16)
 template <bool BF16>
 __device__ __forceinline__ void mma(f32x4& acc, const Frag<BF16>& a, const Frag<BF16>& b) {

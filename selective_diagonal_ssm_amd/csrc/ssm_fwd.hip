@@ -42,7 +42,8 @@ struct FwdShape {
   static constexpr bool TE = KR > R;
   static constexpr int TEH = TE ? 1 : 0;
   static constexpr int NS = NC + PAD;  // row stride of n-contiguous buffers
-  static constexpr int KS = QK + PAD;  // row stride of key-contiguous buffers
+  static constexpr int KS = QK + PAD;  // row stride of key-contiguous buffers (scores)
+  static constexpr int VS = PB + PAD;  // row stride of value buffers
   static constexpr int BROWS = (QT + TEH) * R;
   static constexpr int NTH = 256;
   static constexpr int NVEC_N = N / VEC;
@@ -65,16 +66,17 @@ template <bool BF16, int N, int PB, int R, int KR, int QT, bool COORD>
 __global__ __launch_bounds__(256) void ssm_fwd_kernel(FwdParams p) {
   using S = FwdShape<BF16, N, PB, R, KR, QT, COORD>;
   using T = typename S::T;
-  constexpr int NS = S::NS, KS = S::KS, VEC = S::VEC;
+  constexpr int NS = S::NS, KS = S::KS, VS = S::VS, VEC = S::VEC;
 
   __shared__ __align__(16) T sQ[S::QO * NS];
   __shared__ __align__(16) T sQe[COORD ? S::QO * NS : 8];
   __shared__ __align__(16) T sK[S::QK * NS];
-  __shared__ __align__(16) T sKeT[N * KS];
-  __shared__ __align__(16) T sVT[PB * KS];
+  __shared__ __align__(16) T sKe[COORD ? S::QK * NS : 8];  // keys scaled to the chunk end
+  __shared__ __align__(16) T sV[S::QK * S::VS];            // values, natural [key row][p]
+  __shared__ __align__(16) T sVw[COORD ? 8 : S::QK * S::VS];  // values scaled to the chunk end
   __shared__ __align__(16) T sS[S::QO * KS];
   __shared__ __align__(16) T sST[PB * NS];
-  __shared__ float sCD[64], sEL[64], sW[64], sBeta[64], sGamma[64];
+  __shared__ float sCD[64], sEL[64];
   __shared__ float sRate[N], sOmega[N / 2 + 1];
   __shared__ float sMisc[4];
 
@@ -168,7 +170,7 @@ __global__ __launch_bounds__(256) void ssm_fwd_kernel(FwdParams p) {
       }
       rx[k] = val;
     }
-    if (wave == 0) {
+    {
       const int t = t0 + lane;
       const bool ok = lane < QT && t < L;
       const size_t idx = ((size_t)b * L + t) * H + h;
@@ -210,42 +212,35 @@ __global__ __launch_bounds__(256) void ssm_fwd_kernel(FwdParams p) {
   for (int c = 0; c < nch; ++c) {
     const int t0 = c * QT;
     __syncthreads();
-    // ---- a1: chunk-local cumulative step (wave prefix sum)
+    // ---- a1: chunk-local cumulative step (wave prefix sum; every wave holds it,
+    // lane = token, so the operand prologue needs no extra barrier)
+    float dl = 0.f;
+    if (lane < QT && t0 + lane < L) dl = p.softplus ? softplus_f32(rdt) : rdt;
+    const float cd_l = wave_prefix_sum(dl);
+    const float cdend = __shfl(cd_l, QT - 1, kWave);
+    const float w_l = COORD ? 0.f : __expf(-Ah * (cdend - cd_l));
+    const float be_l = rbe, ga_l = rga;
     if (wave == 0) {
-      float dl = 0.f;
-      if (lane < QT && t0 + lane < L) dl = p.softplus ? softplus_f32(rdt) : rdt;
-      const float cd = wave_prefix_sum(dl);
-      const float cdend = __shfl(cd, QT - 1, kWave);
       if (lane < QT) {
-        sCD[lane] = cd;
-        if (!COORD) {
-          sEL[lane] = __expf(-Ah * cd);
-          sW[lane] = __expf(-Ah * (cdend - cd));
-        }
-        if (S::TE) {
-          sBeta[lane] = rbe;
-          sGamma[lane] = rga;
-        }
+        sCD[lane] = cd_l;
+        if (!COORD) sEL[lane] = __expf(-Ah * cd_l);
       }
-      if (lane == 0) {
-        sMisc[0] = cdend;
-        sMisc[1] = COORD ? 0.f : __expf(-Ah * cdend);
-      }
+      if (lane == 0) sMisc[1] = COORD ? 0.f : __expf(-Ah * cdend);
     }
-    __syncthreads();
-    const float cdend = sMisc[0];
 
     // ---- a2: operands (queries, keys, values) into LDS
 #pragma unroll
     for (int k = 0; k < S::C_PER; ++k) {
       const int v = tid + S::NTH * k;
+      const int crow = (v < S::C_VECS ? v : 0) / S::NVEC_N;
+      const float cd_c = COORD ? __shfl(cd_l, crow / R, kWave) : 0.f;
       if (v < S::C_VECS) {
         const int row = v / S::NVEC_N, nv = v % S::NVEC_N;
         const int n0 = nv * VEC;
         if (COORD) {
           float vals[VEC], q[VEC], qe[VEC];
           unpack<BF16>(rc[k], vals);
-          const float cd = sCD[row / R];
+          const float cd = cd_c;
           unrotate(vals, n0, cd);
 #pragma unroll
           for (int i = 0; i < VEC; ++i) {
@@ -263,6 +258,12 @@ __global__ __launch_bounds__(256) void ssm_fwd_kernel(FwdParams p) {
 #pragma unroll
     for (int k = 0; k < S::B_PER; ++k) {
       const int v = tid + S::NTH * k;
+      const int brow = (v < S::B_VECS ? v : 0) / S::NVEC_N;
+      const int bsl = brow / R - S::TEH;
+      const int tau0 = bsl < 0 ? 0 : bsl, tau1 = bsl + 1 < QT ? bsl + 1 : QT - 1;
+      const float cdt[2] = {__shfl(cd_l, tau0, kWave), __shfl(cd_l, tau1, kWave)};
+      const float gbt[2] = {S::TE ? __shfl(ga_l, tau0, kWave) : 1.f,
+                            S::TE ? __shfl(be_l, tau1, kWave) : 0.f};
       if (v < S::B_VECS) {
         const int row = v / S::NVEC_N, nv = v % S::NVEC_N;
         const int n0 = nv * VEC;
@@ -276,12 +277,12 @@ __global__ __launch_bounds__(256) void ssm_fwd_kernel(FwdParams p) {
           const int tau = sl + e;
           if (tau < 0 || tau >= QT || (e == 0 && sl < 0)) continue;
           const int j = tau * KR + (e ? R : 0) + r;
-          const float w = S::TE ? (e ? sBeta[tau] : sGamma[tau]) : 1.f;
+          const float w = gbt[e];
           float u[VEC], kk[VEC], ke[VEC];
 #pragma unroll
           for (int i = 0; i < VEC; ++i) u[i] = vals[i] * w;
           if (COORD) {
-            const float cd = sCD[tau];
+            const float cd = cdt[e];
             unrotate(u, n0, cd);
 #pragma unroll
             for (int i = 0; i < VEC; ++i) {
@@ -290,36 +291,43 @@ __global__ __launch_bounds__(256) void ssm_fwd_kernel(FwdParams p) {
               ke[i] = u[i] * __expf(-ar * (cdend - cd));
             }
           } else {
-            const float ws = sW[tau];
 #pragma unroll
             for (int i = 0; i < VEC; ++i) {
               kk[i] = u[i];
-              ke[i] = u[i] * ws;
+              ke[i] = 0.f;
             }
           }
           *reinterpret_cast<uint4*>(sK + j * NS + n0) = pack<BF16>(kk);
-#pragma unroll
-          for (int i = 0; i < VEC; ++i) sKeT[(n0 + i) * KS + j] = from_f32<T>(ke[i]);
+          if (COORD) *reinterpret_cast<uint4*>(sKe + j * NS + n0) = pack<BF16>(ke);
         }
       }
     }
 #pragma unroll
     for (int k = 0; k < S::X_PER; ++k) {
       const int v = tid + S::NTH * k;
+      const int xrow = (v < S::X_VECS ? v : 0) / S::NVEC_P;
+      const int xsl = xrow / R - S::TEH;
+      const int xt0 = xsl < 0 ? 0 : xsl, xt1 = xsl + 1 < QT ? xsl + 1 : QT - 1;
+      const float xw[2] = {COORD ? 0.f : __shfl(w_l, xt0, kWave),
+                           COORD ? 0.f : __shfl(w_l, xt1, kWave)};
       if (v < S::X_VECS) {
         const int row = v / S::NVEC_P, pv = v % S::NVEC_P;
         const int sl = row / R - S::TEH, r = row % R;
-        T e[VEC];
-        unpack_raw<BF16>(rx[k], e);
-        if (sl >= 0) {
-          const int j = sl * KR + r;
 #pragma unroll
-          for (int i = 0; i < VEC; ++i) sVT[(pv * VEC + i) * KS + j] = e[i];
-        }
-        if (S::TE && sl + 1 < QT) {
-          const int j = (sl + 1) * KR + R + r;
+        for (int e = 0; e < 2; ++e) {
+          if (e == 1 && !S::TE) break;
+          const int tau = sl + e;
+          if (tau < 0 || tau >= QT || (e == 0 && sl < 0)) continue;
+          const int j = tau * KR + (e ? R : 0) + r;
+          *reinterpret_cast<uint4*>(sV + j * VS + pv * VEC) = rx[k];
+          if (!COORD) {
+            float xv[VEC];
+            unpack<BF16>(rx[k], xv);
+            const float ws = xw[e];
 #pragma unroll
-          for (int i = 0; i < VEC; ++i) sVT[(pv * VEC + i) * KS + j] = e[i];
+            for (int i = 0; i < VEC; ++i) xv[i] *= ws;
+            *reinterpret_cast<uint4*>(sVw + j * VS + pv * VEC) = pack<BF16>(xv);
+          }
         }
       }
     }
@@ -375,7 +383,7 @@ __global__ __launch_bounds__(256) void ssm_fwd_kernel(FwdParams p) {
       const int kend = ((tmax + 1) * KR + 31) / 32;
       for (int kk = 0; kk < kend; ++kk) {
         const auto a = load_frag<BF16>(sS + (16 * ti + (lane & 15)) * KS + kk * 32 + 8 * (lane >> 4));
-        const auto bv = load_frag<BF16>(sVT + (16 * tp + (lane & 15)) * KS + kk * 32 + 8 * (lane >> 4));
+        const auto bv = load_frag_tr<BF16>(sV + (kk * 32) * VS + 16 * tp, VS);
         mma<BF16>(acc, a, bv);
       }
       const int pl = 16 * tp + (lane & 15);
@@ -385,7 +393,7 @@ __global__ __launch_bounds__(256) void ssm_fwd_kernel(FwdParams p) {
         const int t = row / R, o = row % R;
         const int tg = t0 + t;
         float val = acc[i];
-        if (p.has_D) val += Dh * to_f32(sVT[pl * KS + t * KR + o]);
+        if (p.has_D) val += Dh * to_f32(sV[(t * KR + o) * VS + pl]);
         if (tg < L) yg[((((size_t)b * L + tg) * H + h) * R + o) * P + p0 + pl] = from_f32<T>(val);
       }
     }
@@ -404,8 +412,8 @@ __global__ __launch_bounds__(256) void ssm_fwd_kernel(FwdParams p) {
         }
 #pragma unroll
         for (int kk = 0; kk < S::QK / 32; ++kk) {
-          const auto a = load_frag<BF16>(sKeT + (16 * tn + (lane & 15)) * KS + kk * 32 + 8 * (lane >> 4));
-          const auto bv = load_frag<BF16>(sVT + (16 * tp + (lane & 15)) * KS + kk * 32 + 8 * (lane >> 4));
+          const auto a = load_frag_tr<BF16>((COORD ? sKe : sK) + (kk * 32) * NS + 16 * tn, NS);
+          const auto bv = load_frag_tr<BF16>((COORD ? sV : sVw) + (kk * 32) * VS + 16 * tp, VS);
           mma<BF16>(acc, a, bv);
         }
         if (COORD) {
