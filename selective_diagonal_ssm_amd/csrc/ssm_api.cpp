@@ -126,11 +126,22 @@ size_t ssm_saved_bytes(const ssm_desc* d) {
   return (size_t)d->batch * d->nheads * (pl.nchunks + 1) * d->dstate * d->headdim * sizeof(float);
 }
 
+static int npart_of(const ssm_desc* d, const Plan& pl) {
+  const int na = (pl.coord_kernel && !pl.head_rates) ? d->n_real + d->n_pairs : 1;
+  return na + d->n_pairs + 1;
+}
+
+static size_t bwd_gseg_bytes(const ssm_desc* d, const Plan& pl) {
+  return (size_t)d->batch * d->nheads * pl.nchunks * d->dstate * d->headdim * sizeof(float);
+}
+
 size_t ssm_workspace_bytes(const ssm_desc* d, int for_backward) {
   Plan pl;
   if (make_plan(d, &pl)) return 0;
-  (void)for_backward;
-  return 0;
+  if (!for_backward) return 0;
+  const size_t g = (bwd_gseg_bytes(d, pl) + 255) / 256 * 256;
+  const size_t part = (size_t)d->batch * d->nheads * pl.nchunks * npart_of(d, pl) * sizeof(float);
+  return g + part;
 }
 
 int ssm_scan_fwd(const ssm_desc* d, const ssm_fwd_args* a, void* ws, size_t ws_bytes,
@@ -177,8 +188,50 @@ int ssm_scan_bwd(const ssm_desc* d, const ssm_bwd_args* a, void* ws, size_t ws_b
   int rc = make_plan(d, &pl);
   if (rc) return rc;
   if (!a) return SSM_ERR_NULL;
-  (void)ws; (void)ws_bytes; (void)stream;
-  return SSM_ERR_UNSUPPORTED;
+  // head groups shared by several heads would need a cross-head sum of dB / dC
+  if (d->ngroups != d->nheads) return SSM_ERR_UNSUPPORTED;
+  BwdKey key{pl.bf16, d->dstate, d->headdim, pl.R, pl.KR, pl.QT, pl.coord_kernel};
+  if (!ssm::bwd_variant_exists(key)) return SSM_ERR_UNSUPPORTED;
+  if (d->batch == 0 || d->seqlen == 0) return SSM_OK;
+  const bool te = (d->flags & SSM_F_TWO_ENDPOINT) != 0;
+  const bool hasD = (d->flags & SSM_F_HAS_D) != 0;
+  if (!a->x || !a->B || !a->C || !a->dy || !a->dt || !a->A || !a->saved || !a->dx || !a->dB ||
+      !a->dC || !a->ddt)
+    return SSM_ERR_NULL;
+  if ((d->n_pairs > 0) != (a->omega != nullptr)) return SSM_ERR_NULL;
+  if (te != (a->beta != nullptr) || te != (a->gamma != nullptr)) return SSM_ERR_NULL;
+  if (hasD != (a->D != nullptr)) return SSM_ERR_NULL;
+  if (!te && (a->dbeta || a->dgamma)) return SSM_ERR_NULL;
+  if (d->n_pairs == 0 && a->domega) return SSM_ERR_NULL;
+  if (!hasD && a->dD) return SSM_ERR_NULL;
+  for (const void* q : {a->x, a->B, a->C, a->dy, (const void*)a->dx, (const void*)a->dB,
+                        (const void*)a->dC, (const void*)a->saved, (const void*)ws})
+    if (q && !aligned(q, 16)) return SSM_ERR_ALIGN;
+  for (const void* q : {(const void*)a->dt, (const void*)a->A, (const void*)a->omega,
+                        (const void*)a->beta, (const void*)a->gamma, (const void*)a->D,
+                        (const void*)a->ddt, (const void*)a->dA, (const void*)a->domega,
+                        (const void*)a->dbeta, (const void*)a->dgamma, (const void*)a->dD})
+    if (q && !aligned(q, 4)) return SSM_ERR_ALIGN;
+  const size_t need = ssm_workspace_bytes(d, 1);
+  if (!ws || ws_bytes < need) return SSM_ERR_WORKSPACE;
+
+  ssm::BwdParams p{};
+  p.x = a->x; p.B = a->B; p.C = a->C; p.dy = a->dy; p.dt = a->dt; p.A = a->A;
+  p.omega = a->omega; p.beta = a->beta; p.gamma = a->gamma; p.D = a->D; p.saved = a->saved;
+  p.dx = a->dx; p.dB = a->dB; p.dC = a->dC; p.ddt = a->ddt; p.dbeta = a->dbeta;
+  p.dgamma = a->dgamma; p.dA = a->dA; p.domega = a->domega; p.dD = a->dD;
+  p.gseg = static_cast<float*>(ws);
+  p.part = reinterpret_cast<float*>(static_cast<char*>(ws) +
+                                    (bwd_gseg_bytes(d, pl) + 255) / 256 * 256);
+  p.batch = d->batch; p.L = d->seqlen; p.H = d->nheads; p.G = d->ngroups; p.P = d->headdim;
+  p.n_real = d->n_real; p.n_pairs = d->n_pairs; p.nchunks = pl.nchunks;
+  p.nseg = 1; p.chunks_per_seg = pl.nchunks;
+  p.softplus = (d->flags & SSM_F_DT_SOFTPLUS) ? 1 : 0;
+  p.has_D = hasD ? 1 : 0;
+  p.npart = npart_of(d, pl);
+  p.head_rates = pl.head_rates ? 1 : 0;
+  const hipError_t e = ssm::launch_bwd(key, p, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
 }
 
 }  // extern "C"

@@ -1,8 +1,1075 @@
-// ssm_bwd.hip -- fused reverse-mode pass (placeholder until the kernels land).
+// ssm_bwd.hip -- reverse-mode pass of the state-mediated selective SSM kernel (gfx950).
+//
+// The adjoint of  h_t = A_t h_{t-1} + W_t,  y_t = C_t^T h_t + D X_t  is
+//   g_t = C_t dy_t + A_{t+1}^T g_{t+1}    (g_t = dL/dh_t),
+// and every gradient of a chunk depends only on the state entering it (saved by
+// the forward) and on g at the first token of the next chunk.  Three kernels:
+//
+//  ssm_bwd_adjoint  (reverse sweep, one workgroup per (slice, P-block)): the chunk
+//      boundary adjoints Gpre[c] = g_{t0(c)} from
+//        Gpre[c] = sum_{t in c} Phi_{t,t0}^T C_t dy_t + Phi_{t0',t0}^T Gpre[c+1],
+//      Phi_{t,t0} = A_t ... A_{t0+1}; chunk-local folding as in the forward.
+//  ssm_bwd_chunk    (one workgroup per (slice, chunk), fully parallel): dX, dB, dC,
+//      dDelta, dbeta, dgamma and per-chunk parameter partials from the chunked
+//      adjoint (transposed masked products on MFMA):
+//        dV  = (S o M)^T dY + Ke G~,   dK~ = (Z o M)^T Q + e^{L_end-L_s} (G~ V^T),
+//        dC~ = (Z o M) K + e^{L_t} dY S_in^T,   Z = dY V^T,
+//      with G~ the folded adjoint of the chunk's final state.  The step gradient
+//      uses the exact telescoping identity
+//        d(log-decay)_r = sum_{t >= r} [C~_t . dC~_t - K~_t . dK~_t] (+ final-state term)
+//      (row sum minus column sum of Z o S o M for the intra-chunk part), and the
+//      pair angles the matching C~^T J dC~ + K~^T J dK~ terms (J = 90-degree
+//      rotation).  Operands that carry fp32 state (S_in, G~) are split into bf16
+//      hi + lo parts so the cancelling sums keep fp32-level accuracy.
+//  ssm_bwd_params   deterministic fixed-order sum of the per-chunk partials of
+//      dA, domega, dD.
+//
+// Sources: "When a Diagonal State Is Not Enough" (sungsoo.github.io), Part 01 and
+// Part 03 (recurrence, Theorem 24 masked-attention form, Theorem 8 pairs), Part 04
+// (verification compares outputs, input gradients and parameter gradients).
 #include "ssm_device.hpp"
 #include "ssm_kernels.hpp"
 
 namespace ssm {
-bool bwd_variant_exists(const BwdKey&) { return false; }
-hipError_t launch_bwd(const BwdKey&, const BwdParams&, hipStream_t) { return hipErrorInvalidValue; }
+
+// ============================================================== boundary adjoints
+template <bool BF16, int N, int PB, int R, int QT, bool COORD>
+struct AdjShape {
+  using T = typename Elem<BF16>::T;
+  static constexpr int VEC = Elem<BF16>::kVec;
+  static constexpr int PAD = 16 / static_cast<int>(sizeof(T));
+  static constexpr int QO = QT * R;
+  static constexpr int QOC = (QO + 31) / 32 * 32;  // contraction rows, zero padded
+  static constexpr int NS = N + PAD;
+  static constexpr int VS = PB + PAD;
+  static constexpr int NTH = 256;
+  static constexpr int C_VECS = QO * (N / VEC);
+  static constexpr int Y_VECS = QO * (PB / VEC);
+  static constexpr int C_PER = (C_VECS + NTH - 1) / NTH;
+  static constexpr int Y_PER = (Y_VECS + NTH - 1) / NTH;
+  static constexpr int TN = N / 16, TP = PB / 16;
+  static constexpr int ST_TILES = TN * TP;
+  static constexpr int ST_PER_WAVE = (ST_TILES + 3) / 4;
+};
+
+template <bool BF16, int N, int PB, int R, int QT, bool COORD>
+__global__ __launch_bounds__(256) void ssm_bwd_adjoint(BwdParams p) {
+  using S = AdjShape<BF16, N, PB, R, QT, COORD>;
+  using T = typename S::T;
+  constexpr int NS = S::NS, VS = S::VS, VEC = S::VEC;
+  __shared__ __align__(16) T sQ[S::QOC * NS];  // folded, decayed C rows
+  __shared__ __align__(16) T sY[S::QOC * VS];  // dy rows (head mode: decayed)
+  __shared__ float sRate[N], sOmega[N / 2 + 1];
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int npblk = p.P / PB;
+  const int lid = xcd_logical_id(blockIdx.x, gridDim.x);
+  const int slice = lid / npblk, pblk = lid % npblk;
+  const int b = slice / p.H, h = slice % p.H, g = h / (p.H / p.G);
+  const int p0 = pblk * PB;
+  const int L = p.L, H = p.H, G = p.G, P = p.P, nreal = p.n_real;
+
+  if (COORD) {
+    const int na = p.n_real + p.n_pairs;
+    for (int n = tid; n < N; n += S::NTH) {
+      float r;
+      if (p.head_rates) r = p.A[h];
+      else if (n < nreal) r = p.A[(size_t)h * na + n];
+      else r = p.A[(size_t)h * na + nreal + ((n - nreal) >> 1)];
+      sRate[n] = r;
+    }
+    for (int k = tid; k < p.n_pairs; k += S::NTH) sOmega[k] = p.omega[(size_t)h * p.n_pairs + k];
+  }
+  for (int i = tid; i < (S::QOC - S::QO) * NS; i += S::NTH) sQ[S::QO * NS + i] = T(0);
+  for (int i = tid; i < (S::QOC - S::QO) * VS; i += S::NTH) sY[S::QO * VS + i] = T(0);
+  const float Ah = COORD ? 0.f : p.A[h];
+  const T* Cg = static_cast<const T*>(p.C);
+  const T* dyg = static_cast<const T*>(p.dy);
+
+  f32x4 st[S::ST_PER_WAVE];
+#pragma unroll
+  for (int k = 0; k < S::ST_PER_WAVE; ++k) st[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int nch = p.nchunks;
+  for (int c = nch - 1; c >= 0; --c) {
+    const int t0 = c * QT;
+    const int tn = t0 + QT;  // first token of the next chunk
+    __syncthreads();
+    // step of this chunk's tokens (lane = token) and of the next chunk's first token
+    float dl = 0.f;
+    if (lane < QT && t0 + lane < L) {
+      const float raw = p.dt[((size_t)b * L + t0 + lane) * H + h];
+      dl = p.softplus ? softplus_f32(raw) : raw;
+    }
+    float dnext = 0.f;
+    if (tn < L) {
+      const float raw = p.dt[((size_t)b * L + tn) * H + h];
+      dnext = p.softplus ? softplus_f32(raw) : raw;
+    }
+    const float cd = wave_prefix_sum(dl);
+    const float cdx = cd - __shfl(dl, 0, kWave);      // sum over (t0, t]
+    const float cdx_end = __shfl(cdx, QT - 1, kWave) + dnext;  // sum over (t0, t0']
+
+    // carried adjoint: Gpre[c+1] -> Phi_{t0',t0}^T Gpre[c+1]
+#pragma unroll
+    for (int k = 0; k < S::ST_PER_WAVE; ++k) {
+      const int tile = wave + 4 * k;
+      if (tile < S::ST_TILES) {
+        const int tnn = tile / S::TP;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int n = 16 * tnn + 4 * (lane >> 4) + i;
+          st[k][i] *= COORD ? __expf(-sRate[n] * cdx_end) : __expf(-Ah * cdx_end);
+        }
+        if (COORD) {
+#pragma unroll
+          for (int i = 0; i < 4; i += 2) {
+            const int n = 16 * tnn + 4 * (lane >> 4) + i;
+            if (n >= nreal) {
+              float sn, cs;
+              sincosf(sOmega[(n - nreal) >> 1] * cdx_end, &sn, &cs);
+              const float a0 = st[k][i], a1 = st[k][i + 1];
+              st[k][i] = cs * a0 + sn * a1;  // R(-theta)
+              st[k][i + 1] = -sn * a0 + cs * a1;
+            }
+          }
+        }
+      }
+    }
+    // operands: rows (t, o) of  e^{L'_t} R(-Theta'_t) C_t  and  dy_t
+#pragma unroll
+    for (int k = 0; k < S::C_PER; ++k) {
+      const int v = tid + S::NTH * k;
+      const int row = (v < S::C_VECS ? v : 0) / (N / VEC);
+      const float cdr = __shfl(cdx, row / R, kWave);
+      if (v < S::C_VECS) {
+        const int nv = v % (N / VEC), n0 = nv * VEC;
+        const int t = t0 + row / R, o = row % R;
+        uint4 raw = make_uint4(0, 0, 0, 0);
+        if (t < L)
+          raw = *reinterpret_cast<const uint4*>(Cg + ((((size_t)b * L + t) * G + g) * R + o) * N + n0);
+        if (COORD) {
+          float vals[VEC];
+          unpack<BF16>(raw, vals);
+#pragma unroll
+          for (int i = 0; i < VEC; i += 2) {
+            const int n = n0 + i;
+            if (n >= nreal) {
+              float sn, cs;
+              sincosf(sOmega[(n - nreal) >> 1] * cdr, &sn, &cs);
+              const float a = vals[i], bb = vals[i + 1];
+              vals[i] = cs * a + sn * bb;
+              vals[i + 1] = -sn * a + cs * bb;
+            }
+          }
+#pragma unroll
+          for (int i = 0; i < VEC; ++i) vals[i] *= __expf(-sRate[n0 + i] * cdr);
+          raw = pack<BF16>(vals);
+        }
+        *reinterpret_cast<uint4*>(sQ + row * NS + n0) = raw;
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < S::Y_PER; ++k) {
+      const int v = tid + S::NTH * k;
+      const int row = (v < S::Y_VECS ? v : 0) / (PB / VEC);
+      const float wr = COORD ? 1.f : __expf(-Ah * __shfl(cdx, row / R, kWave));
+      if (v < S::Y_VECS) {
+        const int pv = v % (PB / VEC);
+        const int t = t0 + row / R, o = row % R;
+        uint4 raw = make_uint4(0, 0, 0, 0);
+        if (t < L)
+          raw = *reinterpret_cast<const uint4*>(dyg + ((((size_t)b * L + t) * H + h) * R + o) * P + p0 + pv * VEC);
+        if (!COORD) {
+          float vals[VEC];
+          unpack<BF16>(raw, vals);
+#pragma unroll
+          for (int i = 0; i < VEC; ++i) vals[i] *= wr;
+          raw = pack<BF16>(vals);
+        }
+        *reinterpret_cast<uint4*>(sY + row * VS + pv * VEC) = raw;
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < S::ST_PER_WAVE; ++k) {
+      const int tile = wave + 4 * k;
+      if (tile < S::ST_TILES) {
+        const int tnn = tile / S::TP, tp = tile % S::TP;
+        f32x4 acc = st[k];
+#pragma unroll
+        for (int kk = 0; kk < S::QOC / 32; ++kk) {
+          const auto a = load_frag_tr<BF16>(sQ + (kk * 32) * NS + 16 * tnn, NS);
+          const auto bq = load_frag_tr<BF16>(sY + (kk * 32) * VS + 16 * tp, VS);
+          mma<BF16>(acc, a, bq);
+        }
+        st[k] = acc;
+        const int pl = 16 * tp + (lane & 15);
+        float* dst = p.gseg + ((size_t)slice * nch + c) * N * P;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int n = 16 * tnn + 4 * (lane >> 4) + i;
+          dst[(size_t)n * P + p0 + pl] = acc[i];
+        }
+      }
+    }
+  }
+}
+
+// ============================================================== chunk gradients
+template <bool BF16, int N, int P, int R, int KR, int QT, bool COORD>
+struct BwdShape {
+  using T = typename Elem<BF16>::T;
+  static constexpr int VEC = Elem<BF16>::kVec;
+  static constexpr int PAD = 16 / static_cast<int>(sizeof(T));
+  static constexpr int NC = N < 32 ? 32 : N;
+  static constexpr int PC = P < 32 ? 32 : P;
+  static constexpr int QO = QT * R;
+  static constexpr int QOC = (QO + 31) / 32 * 32;
+  static constexpr int QK = QT * KR;
+  static constexpr bool TE = KR > R;
+  static constexpr int TEH = TE ? 1 : 0;
+  static constexpr int NS = NC + PAD;   // [row][n] buffers
+  static constexpr int PS = PC + PAD;   // [row][p] buffers
+  static constexpr int KS = QK + PAD;   // [row][key] buffers
+  static constexpr int BROWS = (QT + TEH) * R;
+  static constexpr int NTH = 256;
+  static constexpr int C_VECS = QO * (N / VEC);
+  static constexpr int B_VECS = BROWS * (N / VEC);
+  static constexpr int X_VECS = BROWS * (P / VEC);
+  static constexpr int Y_VECS = QO * (P / VEC);
+  static constexpr int TQ = QO / 16, TK = QK / 16, TN = N / 16, TP = P / 16;
+  static_assert(QO % 16 == 0 && QK % 32 == 0, "chunk rows must fill MFMA tiles");
+  static_assert(N % 16 == 0 && P % 16 == 0 && QT <= 64, "unsupported tile shape");
+};
+
+template <bool BF16, int N, int P, int R, int KR, int QT, bool COORD>
+__global__ __launch_bounds__(256) void ssm_bwd_chunk(BwdParams p) {
+  using S = BwdShape<BF16, N, P, R, KR, QT, COORD>;
+  using T = typename S::T;
+  constexpr int NS = S::NS, PS = S::PS, KS = S::KS, VEC = S::VEC;
+  constexpr int QO = S::QO, QK = S::QK;
+
+  __shared__ __align__(16) T sQ[S::QOC * NS];   // q rows (t, o)
+  __shared__ __align__(16) T sK[QK * NS];        // k rows j
+  __shared__ __align__(16) T sKe[COORD ? QK * NS : 8];
+  __shared__ __align__(16) T sV[QK * PS];        // value rows j
+  __shared__ __align__(16) T sY[S::QOC * PS];   // dy rows (t, o)
+  __shared__ __align__(16) T sSM[S::QOC * KS];  // (S o M) rows (t, o)
+  __shared__ __align__(16) T sZM[S::QOC * KS];  // (Z o M) rows (t, o)
+  __shared__ __align__(16) T sGh[S::NC * PS];   // folded adjoint G~ (hi / lo)
+  __shared__ __align__(16) T sGl[S::NC * PS];
+  __shared__ __align__(16) T sSh[N * PS];        // incoming state (hi / lo)
+  __shared__ __align__(16) T sSl[N * PS];
+  __shared__ float sRate[N], sOmega[N / 2 + 1];
+  __shared__ float sE[N], sEth[N / 2 + 1];       // final-state terms per row / pair
+  __shared__ float sEK[4][N], sEKth[4][N / 2 + 1];  // per-wave inter source sums per row / pair
+  __shared__ float sTok[4][64];                  // per-wave per-token dcd contributions (per-row mode)
+  __shared__ float sTT[4][64], sSrc[4][64];      // head: target / source inter terms per token
+  __shared__ float sRS[4][64], sCS[4][64];       // head: row / column sums of Z o S o M
+  __shared__ float sDg[4][64], sDb[4][64];       // per-wave dgamma / dbeta sums
+  __shared__ float sPA[4][N], sPW[4][N / 2 + 1]; // per-wave parameter partials
+  __shared__ float sDX[S::TE ? 2 * (QT + 1) * R * P : 1];  // two-endpoint dX assembly
+  __shared__ float sDB[S::TE ? 2 * (QT + 1) * R * N : 1];  // two-endpoint dB assembly
+  __shared__ float sTailX[S::TE ? R * P : 1], sTailB[S::TE ? R * N : 1];
+  __shared__ float sMisc[8];
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int nch = p.nchunks;
+  const int slice = blockIdx.x / nch, c = blockIdx.x % nch;
+  const int b = slice / p.H, h = slice % p.H, g = h / (p.H / p.G);
+  const int L = p.L, H = p.H, G = p.G, nreal = p.n_real, npairs = p.n_pairs;
+  const int t0 = c * QT, tn = t0 + QT;
+  const bool has_next = tn < L;
+
+  const T* xg = static_cast<const T*>(p.x);
+  const T* Bg = static_cast<const T*>(p.B);
+  const T* Cg = static_cast<const T*>(p.C);
+  const T* dyg = static_cast<const T*>(p.dy);
+  T* dxg = static_cast<T*>(p.dx);
+  T* dBg = static_cast<T*>(p.dB);
+  T* dCg = static_cast<T*>(p.dC);
+
+  if (COORD) {
+    const int na = nreal + npairs;
+    for (int n = tid; n < N; n += S::NTH) {
+      float r;
+      if (p.head_rates) r = p.A[h];
+      else if (n < nreal) r = p.A[(size_t)h * na + n];
+      else r = p.A[(size_t)h * na + nreal + ((n - nreal) >> 1)];
+      sRate[n] = r;
+    }
+    for (int k = tid; k < npairs; k += S::NTH) sOmega[k] = p.omega[(size_t)h * npairs + k];
+  }
+  for (int i = tid; i < 4 * 64; i += S::NTH) {
+    (&sTok[0][0])[i] = 0.f; (&sRS[0][0])[i] = 0.f; (&sCS[0][0])[i] = 0.f;
+    (&sDg[0][0])[i] = 0.f; (&sDb[0][0])[i] = 0.f; (&sTT[0][0])[i] = 0.f; (&sSrc[0][0])[i] = 0.f;
+  }
+  for (int i = tid; i < (S::NC - N) * PS; i += S::NTH) { sGh[N * PS + i] = T(0); sGl[N * PS + i] = T(0); }
+  for (int i = tid; i < 4 * N; i += S::NTH) { (&sEK[0][0])[i] = 0.f; (&sPA[0][0])[i] = 0.f; }
+  for (int i = tid; i < 4 * (N / 2 + 1); i += S::NTH) { (&sEKth[0][0])[i] = 0.f; (&sPW[0][0])[i] = 0.f; }
+  // zero padding rows / columns
+  for (int i = tid; i < (S::QOC - QO) * NS; i += S::NTH) sQ[QO * NS + i] = T(0);
+  for (int i = tid; i < (S::QOC - QO) * PS; i += S::NTH) sY[QO * PS + i] = T(0);
+  for (int i = tid; i < (S::QOC - QO) * KS; i += S::NTH) { sSM[QO * KS + i] = T(0); sZM[QO * KS + i] = T(0); }
+  if (S::NC > N) {
+    for (int i = tid; i < S::QOC * (S::NC - N); i += S::NTH) sQ[(i / (S::NC - N)) * NS + N + i % (S::NC - N)] = T(0);
+    for (int i = tid; i < QK * (S::NC - N); i += S::NTH) {
+      sK[(i / (S::NC - N)) * NS + N + i % (S::NC - N)] = T(0);
+      if (COORD) sKe[(i / (S::NC - N)) * NS + N + i % (S::NC - N)] = T(0);
+    }
+  }
+  if (S::PC > P) {
+    for (int i = tid; i < QK * (S::PC - P); i += S::NTH) sV[(i / (S::PC - P)) * PS + P + i % (S::PC - P)] = T(0);
+    for (int i = tid; i < S::QOC * (S::PC - P); i += S::NTH) sY[(i / (S::PC - P)) * PS + P + i % (S::PC - P)] = T(0);
+    for (int i = tid; i < N * (S::PC - P); i += S::NTH) {
+      const int r = i / (S::PC - P), cc = P + i % (S::PC - P);
+      sGh[r * PS + cc] = T(0); sGl[r * PS + cc] = T(0); sSh[r * PS + cc] = T(0); sSl[r * PS + cc] = T(0);
+    }
+  }
+  const float Ah = COORD ? 0.f : p.A[h];
+  const float Dh = p.has_D ? p.D[h] : 0.f;
+
+  // ---------------------------------------------------------------- scalars
+  float raw_l = 0.f, dl = 0.f, be_l = 0.f, ga_l = 1.f;
+  if (lane < QT && t0 + lane < L) {
+    const size_t idx = ((size_t)b * L + t0 + lane) * H + h;
+    raw_l = p.dt[idx];
+    dl = p.softplus ? softplus_f32(raw_l) : raw_l;
+    if (S::TE) { be_l = p.beta[idx]; ga_l = p.gamma[idx]; }
+  } else if (S::TE) {
+    ga_l = 0.f;
+  }
+  float dnext = 0.f, bnext = 0.f;
+  if (has_next) {
+    const size_t idx = ((size_t)b * L + tn) * H + h;
+    const float raw = p.dt[idx];
+    dnext = p.softplus ? softplus_f32(raw) : raw;
+    if (S::TE) bnext = p.beta[idx];
+  }
+  const float cd_l = wave_prefix_sum(dl);
+  const float cdend = __shfl(cd_l, QT - 1, kWave);
+  const float w_l = COORD ? 0.f : __expf(-Ah * (cdend - cd_l));   // e^{L_end - L_t}
+  const float el_l = COORD ? 0.f : __expf(-Ah * cd_l);            // e^{L_t}
+
+  // ---------------------------------------------------------------- staging
+  // queries (t, o)
+  for (int v0 = 0; v0 < S::C_VECS; v0 += S::NTH) {
+    const int v = v0 + tid;
+    const int vv = v < S::C_VECS ? v : 0;
+    const int row = vv / (N / VEC), n0 = (vv % (N / VEC)) * VEC;
+    const int tl = row / R, o = row % R, t = t0 + tl;
+    const float cd = __shfl(cd_l, tl, kWave);
+    if (v >= S::C_VECS) continue;
+    uint4 raw = make_uint4(0, 0, 0, 0);
+    if (t < L) raw = *reinterpret_cast<const uint4*>(Cg + ((((size_t)b * L + t) * G + g) * R + o) * N + n0);
+    if (COORD) {
+      float vals[VEC];
+      unpack<BF16>(raw, vals);
+#pragma unroll
+      for (int i = 0; i < VEC; i += 2) {
+        const int n = n0 + i;
+        if (n >= nreal) {
+          float sn, cs;
+          sincosf(sOmega[(n - nreal) >> 1] * cd, &sn, &cs);
+          const float a = vals[i], bb = vals[i + 1];
+          vals[i] = cs * a + sn * bb;
+          vals[i + 1] = -sn * a + cs * bb;
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) vals[i] *= __expf(-sRate[n0 + i] * (cd - 0.5f * cdend));
+      raw = pack<BF16>(vals);
+    }
+    *reinterpret_cast<uint4*>(sQ + row * NS + n0) = raw;
+  }
+  // keys j: gamma_s B_s at (s, r) and beta_s B_{s-1} at (s, R + r)
+  for (int v0 = 0; v0 < S::B_VECS; v0 += S::NTH) {
+    const int v = v0 + tid;
+    const int vv = v < S::B_VECS ? v : 0;
+    const int row = vv / (N / VEC), n0 = (vv % (N / VEC)) * VEC;
+    const int sl = row / R - S::TEH, r = row % R, t = t0 + sl;
+    const int ta = sl < 0 ? 0 : sl, tb = sl + 1 < QT ? sl + 1 : QT - 1;
+    const float cdv[2] = {__shfl(cd_l, ta, kWave), __shfl(cd_l, tb, kWave)};
+    const float wv[2] = {S::TE ? __shfl(ga_l, ta, kWave) : 1.f, S::TE ? __shfl(be_l, tb, kWave) : 0.f};
+    if (v >= S::B_VECS) continue;
+    uint4 raw = make_uint4(0, 0, 0, 0);
+    if (t >= 0 && t < L) raw = *reinterpret_cast<const uint4*>(Bg + ((((size_t)b * L + t) * G + g) * R + r) * N + n0);
+    float vals[VEC];
+    unpack<BF16>(raw, vals);
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      if (e == 1 && !S::TE) break;
+      const int tau = sl + e;
+      if (tau < 0 || tau >= QT || (e == 0 && sl < 0)) continue;
+      const int j = tau * KR + (e ? R : 0) + r;
+      float u[VEC], kk[VEC], ke[VEC];
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) u[i] = vals[i] * wv[e];
+      if (COORD) {
+#pragma unroll
+        for (int i = 0; i < VEC; i += 2) {
+          const int n = n0 + i;
+          if (n >= nreal) {
+            float sn, cs;
+            sincosf(sOmega[(n - nreal) >> 1] * cdv[e], &sn, &cs);
+            const float a = u[i], bb = u[i + 1];
+            u[i] = cs * a + sn * bb;
+            u[i + 1] = -sn * a + cs * bb;
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) {
+          kk[i] = u[i] * __expf(-sRate[n0 + i] * (0.5f * cdend - cdv[e]));
+          ke[i] = u[i] * __expf(-sRate[n0 + i] * (cdend - cdv[e]));
+        }
+        *reinterpret_cast<uint4*>(sKe + j * NS + n0) = pack<BF16>(ke);
+      } else {
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) kk[i] = u[i];
+      }
+      *reinterpret_cast<uint4*>(sK + j * NS + n0) = pack<BF16>(kk);
+    }
+  }
+  // values j and dy rows
+  float dDp = 0.f;
+  for (int v = tid; v < S::X_VECS; v += S::NTH) {
+    const int row = v / (P / VEC), p0 = (v % (P / VEC)) * VEC;
+    const int sl = row / R - S::TEH, r = row % R, t = t0 + sl;
+    uint4 raw = make_uint4(0, 0, 0, 0);
+    if (t >= 0 && t < L) raw = *reinterpret_cast<const uint4*>(xg + ((((size_t)b * L + t) * H + h) * R + r) * P + p0);
+    if (sl >= 0) *reinterpret_cast<uint4*>(sV + (sl * KR + r) * PS + p0) = raw;
+    if (S::TE && sl + 1 < QT) *reinterpret_cast<uint4*>(sV + ((sl + 1) * KR + R + r) * PS + p0) = raw;
+  }
+  for (int v = tid; v < S::Y_VECS; v += S::NTH) {
+    const int row = v / (P / VEC), p0 = (v % (P / VEC)) * VEC;
+    const int tl = row / R, o = row % R, t = t0 + tl;
+    uint4 raw = make_uint4(0, 0, 0, 0);
+    if (t < L) raw = *reinterpret_cast<const uint4*>(dyg + ((((size_t)b * L + t) * H + h) * R + o) * P + p0);
+    *reinterpret_cast<uint4*>(sY + row * PS + p0) = raw;
+  }
+  // incoming state S_in and folded adjoint G~ = e^{-A Dnext} R(-omega (cd_end + Dnext)) g'
+  // (split into bf16 hi + lo), final-state terms per row / pair
+  {
+    const float* Sg = p.saved + ((size_t)slice * (nch + 1) + c) * N * P;
+    const float* Gg = p.gseg + ((size_t)slice * nch + (c + 1)) * N * P;
+    const bool gvalid = has_next && (c + 1 < nch);
+    const float lend_h = COORD ? 0.f : __expf(-Ah * cdend);
+    const float gdec_h = COORD ? 0.f : __expf(-Ah * dnext);
+    constexpr int PV = P / 4;  // fp32 vectors per row
+    for (int v = tid; v < (N / 2) * PV; v += S::NTH) {
+      const int rp = v / PV, pc = v % PV;
+      const int n = 2 * rp, q0 = pc * 4;
+      float sa[4], sb[4], ga[4], gb[4];
+      {
+        const float4 a = *reinterpret_cast<const float4*>(Sg + (size_t)n * P + q0);
+        const float4 bb = *reinterpret_cast<const float4*>(Sg + (size_t)(n + 1) * P + q0);
+        sa[0] = a.x; sa[1] = a.y; sa[2] = a.z; sa[3] = a.w;
+        sb[0] = bb.x; sb[1] = bb.y; sb[2] = bb.z; sb[3] = bb.w;
+      }
+      if (gvalid) {
+        const float4 a = *reinterpret_cast<const float4*>(Gg + (size_t)n * P + q0);
+        const float4 bb = *reinterpret_cast<const float4*>(Gg + (size_t)(n + 1) * P + q0);
+        ga[0] = a.x; ga[1] = a.y; ga[2] = a.z; ga[3] = a.w;
+        gb[0] = bb.x; gb[1] = bb.y; gb[2] = bb.z; gb[3] = bb.w;
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ga[i] = gb[i] = 0.f;
+      }
+      float fa, fb, lea, leb;
+      if (COORD) {
+        fa = __expf(-sRate[n] * dnext); fb = __expf(-sRate[n + 1] * dnext);
+        lea = __expf(-sRate[n] * cdend); leb = __expf(-sRate[n + 1] * cdend);
+      } else {
+        fa = fb = gdec_h; lea = leb = lend_h;
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) { ga[i] *= fa; gb[i] *= fb; }
+      const bool pair = COORD && n >= nreal;
+      if (pair) {
+        float sn, cs;
+        sincosf(sOmega[(n - nreal) >> 1] * (cdend + dnext), &sn, &cs);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float a0 = ga[i], a1 = gb[i];
+          ga[i] = cs * a0 + sn * a1;
+          gb[i] = -sn * a0 + cs * a1;
+        }
+      }
+      float ea = 0.f, eb = 0.f, eth = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        ea += ga[i] * sa[i];
+        eb += gb[i] * sb[i];
+        eth += -ga[i] * sb[i] + gb[i] * sa[i];  // <G~, J S>
+      }
+      ea *= lea; eb *= leb; eth *= lea;
+      // reduce over the PV p-vectors of this row pair (consecutive lanes)
+#pragma unroll
+      for (int off = 1; off < PV; off <<= 1) {
+        ea += __shfl_xor(ea, off, kWave);
+        eb += __shfl_xor(eb, off, kWave);
+        eth += __shfl_xor(eth, off, kWave);
+      }
+      if (pc == 0) {
+        sE[n] = ea; sE[n + 1] = eb;
+        if (pair) sEth[(n - nreal) >> 1] = eth;
+      }
+      // bf16 hi / lo copies
+      float hi[4], lo[4];
+      auto split = [&](const float* x, T* dh, T* dlo) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          hi[i] = to_f32(from_f32<T>(x[i]));
+          lo[i] = x[i] - hi[i];
+          dh[i] = from_f32<T>(hi[i]);
+          dlo[i] = from_f32<T>(lo[i]);
+        }
+      };
+      split(sa, sSh + n * PS + q0, sSl + n * PS + q0);
+      split(sb, sSh + (n + 1) * PS + q0, sSl + (n + 1) * PS + q0);
+      split(ga, sGh + n * PS + q0, sGl + n * PS + q0);
+      split(gb, sGh + (n + 1) * PS + q0, sGl + (n + 1) * PS + q0);
+    }
+    // two-endpoint tails of the last token: beta_{t0'} B_{t1}^T g' and g' X_{t1}^T
+    if (S::TE) {
+      const int t1 = t0 + QT - 1;
+      for (int i = tid; i < R * P; i += S::NTH) {
+        const int r = i / P, pp = i % P;
+        float acc = 0.f;
+        if (gvalid) {
+          for (int n = 0; n < N; ++n)
+            acc += to_f32(Bg[((((size_t)b * L + t1) * G + g) * R + r) * N + n]) * Gg[(size_t)n * P + pp];
+        }
+        sTailX[i] = bnext * acc;
+      }
+      for (int i = tid; i < R * N; i += S::NTH) {
+        const int r = i / N, n = i % N;
+        float acc = 0.f;
+        if (gvalid) {
+          for (int pp = 0; pp < P; ++pp)
+            acc += Gg[(size_t)n * P + pp] * to_f32(xg[((((size_t)b * L + t1) * H + h) * R + r) * P + pp]);
+        }
+        sTailB[i] = bnext * acc;
+      }
+    }
+  }
+  __syncthreads();
+  if (p.has_D) {
+    for (int i = tid; i < QO * P; i += S::NTH) {
+      const int row = i / P, pp = i % P, tl = row / R, o = row % R;
+      dDp += to_f32(sY[row * PS + pp]) * to_f32(sV[(tl * KR + o) * PS + pp]);
+    }
+  }
+  dDp = wave_sum(dDp);
+  if (lane == 0) sMisc[wave] = dDp;
+
+  // ---------------------------------------------------------------- scores
+  for (int tile = wave; tile < S::TQ * S::TK; tile += 4) {
+    const int ti = tile / S::TK, tj = tile % S::TK;
+    const int tmax = (16 * ti + 15) / R, smin = (16 * tj) / KR;
+    f32x4 sc = {0.f, 0.f, 0.f, 0.f}, z = {0.f, 0.f, 0.f, 0.f};
+    if (smin <= tmax) {
+#pragma unroll
+      for (int kk = 0; kk < S::NC / 32; ++kk) {
+        const auto a = load_frag<BF16>(sQ + (16 * ti + (lane & 15)) * NS + kk * 32 + 8 * (lane >> 4));
+        const auto bq = load_frag<BF16>(sK + (16 * tj + (lane & 15)) * NS + kk * 32 + 8 * (lane >> 4));
+        mma<BF16>(sc, a, bq);
+      }
+#pragma unroll
+      for (int kk = 0; kk < S::PC / 32; ++kk) {
+        const auto a = load_frag<BF16>(sY + (16 * ti + (lane & 15)) * PS + kk * 32 + 8 * (lane >> 4));
+        const auto bv = load_frag<BF16>(sV + (16 * tj + (lane & 15)) * PS + kk * 32 + 8 * (lane >> 4));
+        mma<BF16>(z, a, bv);
+      }
+    }
+    const int col = 16 * tj + (lane & 15), s = col / KR;
+    const float cds = __shfl(cd_l, s, kWave);
+    float csum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = 16 * ti + 4 * (lane >> 4) + i, t = row / R;
+      const float cdt = __shfl(cd_l, t, kWave);
+      float m = 0.f;
+      if (s <= t) m = COORD ? 1.f : __expf(-Ah * (cdt - cds));
+      sSM[row * KS + col] = from_f32<T>(sc[i] * m);
+      sZM[row * KS + col] = from_f32<T>(z[i] * m);
+      if (!COORD) {
+        float wv = z[i] * sc[i] * m;
+        // row sum over the 16 columns of this tile
+        float rs = wv;
+#pragma unroll
+        for (int off = 1; off < 16; off <<= 1) rs += __shfl_xor(rs, off, kWave);
+        if ((lane & 15) == 0) sRS[wave][t] += rs;
+        csum += wv;
+      }
+    }
+    if (!COORD) {
+      csum += __shfl_xor(csum, 16, kWave);
+      csum += __shfl_xor(csum, 32, kWave);
+#pragma unroll
+      for (int off = 1; off < KR; off <<= 1) csum += __shfl_xor(csum, off, kWave);
+      if (lane < 16 && (lane % KR) == 0) sCS[wave][s] += csum;
+    }
+  }
+  __syncthreads();
+
+  // ---------------------------------------------------------------- dV -> dX
+  for (int tile = wave; tile < S::TK * S::TP; tile += 4) {
+    const int tj = tile / S::TP, tp = tile % S::TP;
+    f32x4 ai = {0.f, 0.f, 0.f, 0.f}, ae = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < S::QOC / 32; ++kk) {
+      const auto a = load_frag_tr<BF16>(sSM + (kk * 32) * KS + 16 * tj, KS);
+      const auto bq = load_frag_tr<BF16>(sY + (kk * 32) * PS + 16 * tp, PS);
+      mma<BF16>(ai, a, bq);
+    }
+#pragma unroll
+    for (int kk = 0; kk < S::NC / 32; ++kk) {
+      const auto a = load_frag<BF16>((COORD ? sKe : sK) + (16 * tj + (lane & 15)) * NS + kk * 32 + 8 * (lane >> 4));
+      if (kk * 32 < N) {
+        const auto bh = load_frag_tr<BF16>(sGh + (kk * 32) * PS + 16 * tp, PS);
+        const auto bl = load_frag_tr<BF16>(sGl + (kk * 32) * PS + 16 * tp, PS);
+        mma<BF16>(ae, a, bh);
+        mma<BF16>(ae, a, bl);
+      }
+    }
+    const int pp = 16 * tp + (lane & 15);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int j = 16 * tj + 4 * (lane >> 4) + i;
+      const int s = j / KR, kr = j % KR;
+      const float wj = COORD ? 1.f : __shfl(w_l, s, kWave);
+      const float dv = ai[i] + wj * ae[i];
+      if (!S::TE) {
+        const int t = t0 + s;
+        const float val = dv + (p.has_D ? Dh * to_f32(sY[(s * R + kr) * PS + pp]) : 0.f);
+        if (t < L) dxg[((((size_t)b * L + t) * H + h) * R + kr) * P + pp] = from_f32<T>(val);
+      } else if (kr < R) {
+        sDX[((s + 1) * R + kr) * P + pp] = dv;                       // gamma row -> X_s
+      } else if (s >= 1) {
+        sDX[(QT + 1) * R * P + (s * R + kr - R) * P + pp] = dv;      // beta row -> X_{s-1}
+      }
+    }
+  }
+
+  // ---------------------------------------------------------------- dK~ -> dB, dbeta, dgamma
+  for (int tile = wave; tile < S::TN * S::TK; tile += 4) {
+    const int tnn = tile / S::TK, tj = tile % S::TK;
+    f32x4 ai = {0.f, 0.f, 0.f, 0.f}, ae = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < S::QOC / 32; ++kk) {
+      const auto a = load_frag_tr<BF16>(sQ + (kk * 32) * NS + 16 * tnn, NS);
+      const auto bz = load_frag_tr<BF16>(sZM + (kk * 32) * KS + 16 * tj, KS);
+      mma<BF16>(ai, a, bz);
+    }
+#pragma unroll
+    for (int kk = 0; kk < S::PC / 32; ++kk) {
+      const auto bv = load_frag<BF16>(sV + (16 * tj + (lane & 15)) * PS + kk * 32 + 8 * (lane >> 4));
+      const auto ah = load_frag<BF16>(sGh + (16 * tnn + (lane & 15)) * PS + kk * 32 + 8 * (lane >> 4));
+      const auto al = load_frag<BF16>(sGl + (16 * tnn + (lane & 15)) * PS + kk * 32 + 8 * (lane >> 4));
+      mma<BF16>(ae, ah, bv);
+      mma<BF16>(ae, al, bv);
+    }
+    const int j = 16 * tj + (lane & 15), s = j / KR, kr = j % KR;
+    const float cds = __shfl(cd_l, s, kWave);
+    const float wj = COORD ? 1.f : __shfl(w_l, s, kWave);
+    const float gam = S::TE ? __shfl(ga_l, s, kWave) : 1.f;
+    const float bet = S::TE ? __shfl(be_l, s, kWave) : 0.f;
+    const bool brow = S::TE && kr >= R;
+    const int rr = brow ? kr - R : kr;
+    const int tb = t0 + (brow ? s - 1 : s);  // token whose B row this key carries
+    float tokacc = 0.f, dgb = 0.f;
+    float dk[4], kv[4], rpa[4], rek[4], rpw[2] = {0.f, 0.f}, rekt[2] = {0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int n = 16 * tnn + 4 * (lane >> 4) + i;
+      kv[i] = to_f32(sK[j * NS + n]);
+      rpa[i] = 0.f; rek[i] = 0.f;
+      if (COORD) {
+        const float er = __expf(-sRate[n] * 0.5f * cdend);  // e^{r_n}
+        const float ck = ai[i] + er * ae[i];
+        dk[i] = __expf(-sRate[n] * (0.5f * cdend - cds)) * ck;  // e^{r - L_s} ck  (dK~)
+        // source terms: -k o cK  (rows); the inter part also feeds the final-state term
+        const float dr = -kv[i] * ck;
+        tokacc += -sRate[n] * dr;
+        rpa[i] = -cds * dr;
+        rek[i] = kv[i] * er * ae[i];
+      } else {
+        dk[i] = ai[i] + wj * ae[i];
+        tokacc += kv[i] * wj * ae[i];  // K~ o dK~ (inter part)
+      }
+    }
+    if (COORD) {
+#pragma unroll
+      for (int i = 0; i < 4; i += 2) {
+        const int n = 16 * tnn + 4 * (lane >> 4) + i;
+        if (n >= nreal) {
+          const int kp = (n - nreal) >> 1;
+          const float er = __expf(-sRate[n] * 0.5f * cdend);
+          const float ca = ai[i] + er * ae[i], cb = ai[i + 1] + er * ae[i + 1];
+          // K~^T J dK~ in scaled form: -k_a cK_b + k_b cK_a
+          const float dth = -kv[i] * cb + kv[i + 1] * ca;
+          tokacc += sOmega[kp] * dth;
+          rpw[i >> 1] = cds * dth;
+          rekt[i >> 1] = -(-kv[i] * er * ae[i + 1] + kv[i + 1] * er * ae[i]);
+          // unfold the rotation of the key: u = R(+Theta_s) dK~
+          float sn, cs;
+          sincosf(sOmega[kp] * cds, &sn, &cs);
+          const float a0 = dk[i], a1 = dk[i + 1];
+          dk[i] = cs * a0 - sn * a1;
+          dk[i + 1] = sn * a0 + cs * a1;
+        }
+      }
+    }
+    // gradient w.r.t. the stored B row and the endpoint weights
+    const bool own = !(brow && s == 0) && tb < L;  // the halo row's B belongs to the previous chunk
+    float braw[4];
+    {
+      const int tbc = tb < 0 ? 0 : tb;
+      const int n0 = 16 * tnn + 4 * (lane >> 4);
+      const T* src = Bg + ((((size_t)b * L + tbc) * G + g) * R + rr) * N + n0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) braw[i] = (tb >= 0 && tb < L) ? to_f32(src[i]) : 0.f;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dgb += dk[i] * braw[i];
+    const float wgt = brow ? bet : gam;
+    if (!S::TE) {
+      if (own) {
+        const int n0 = 16 * tnn + 4 * (lane >> 4);
+        T* dst = dBg + ((((size_t)b * L + tb) * G + g) * R + rr) * N + n0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dst[i] = from_f32<T>(dk[i]);
+      }
+    } else {
+      const int n0 = 16 * tnn + 4 * (lane >> 4);
+      if (!brow) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sDB[((s + 1) * R + rr) * N + n0 + i] = wgt * dk[i];
+      } else if (s >= 1) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sDB[(QT + 1) * R * N + (s * R + rr) * N + n0 + i] = wgt * dk[i];
+      }
+    }
+    if (COORD) {
+      // per-row sums over the 16 key columns of this tile
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int off = 1; off < 16; off <<= 1) {
+          rpa[i] += __shfl_xor(rpa[i], off, kWave);
+          rek[i] += __shfl_xor(rek[i], off, kWave);
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+#pragma unroll
+        for (int off = 1; off < 16; off <<= 1) {
+          rpw[q] += __shfl_xor(rpw[q], off, kWave);
+          rekt[q] += __shfl_xor(rekt[q], off, kWave);
+        }
+      }
+      if ((lane & 15) == 0) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int n = 16 * tnn + 4 * (lane >> 4) + i;
+          sPA[wave][n] += rpa[i];
+          sEK[wave][n] += rek[i];
+          if ((i & 1) == 0 && n >= nreal) {
+            sPW[wave][(n - nreal) >> 1] += rpw[i >> 1];
+            sEKth[wave][(n - nreal) >> 1] += rekt[i >> 1];
+          }
+        }
+      }
+    }
+    // per-key sums over the 4 row groups, then over the keys of one token
+    tokacc += __shfl_xor(tokacc, 16, kWave);
+    tokacc += __shfl_xor(tokacc, 32, kWave);
+    dgb += __shfl_xor(dgb, 16, kWave);
+    dgb += __shfl_xor(dgb, 32, kWave);
+#pragma unroll
+    for (int off = 1; off < R; off <<= 1) dgb += __shfl_xor(dgb, off, kWave);
+#pragma unroll
+    for (int off = 1; off < KR; off <<= 1) tokacc += __shfl_xor(tokacc, off, kWave);
+    if (lane < 16) {
+      if ((lane % KR) == 0) {
+        if (COORD) sTok[wave][s] += tokacc;  // weighted source contribution
+        else sSrc[wave][s] += tokacc;        // K~ o dK~ (inter), unweighted
+      }
+      if (S::TE && (lane % R) == 0) {
+        if (brow) sDb[wave][s] += dgb;
+        else sDg[wave][s] += dgb;
+      }
+    }
+  }
+
+  // ---------------------------------------------------------------- dC~ -> dC
+  for (int tile = wave; tile < S::TN * S::TQ; tile += 4) {
+    const int tnn = tile / S::TQ, tq = tile % S::TQ;
+    f32x4 ai = {0.f, 0.f, 0.f, 0.f}, ae = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < QK / 32; ++kk) {
+      const auto a = load_frag_tr<BF16>(sK + (kk * 32) * NS + 16 * tnn, NS);
+      const auto bz = load_frag<BF16>(sZM + (16 * tq + (lane & 15)) * KS + kk * 32 + 8 * (lane >> 4));
+      mma<BF16>(ai, a, bz);
+    }
+#pragma unroll
+    for (int kk = 0; kk < S::PC / 32; ++kk) {
+      const auto by = load_frag<BF16>(sY + (16 * tq + (lane & 15)) * PS + kk * 32 + 8 * (lane >> 4));
+      const auto ah = load_frag<BF16>(sSh + (16 * tnn + (lane & 15)) * PS + kk * 32 + 8 * (lane >> 4));
+      const auto al = load_frag<BF16>(sSl + (16 * tnn + (lane & 15)) * PS + kk * 32 + 8 * (lane >> 4));
+      mma<BF16>(ae, ah, by);
+      mma<BF16>(ae, al, by);
+    }
+    const int row = 16 * tq + (lane & 15), t = row / R, o = row % R, tg = t0 + t;
+    const float cdt = __shfl(cd_l, t, kWave);
+    const float elt = COORD ? 0.f : __shfl(el_l, t, kWave);
+    float tokacc = 0.f, dc[4], qv[4], rpa[4], rpw[2] = {0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int n = 16 * tnn + 4 * (lane >> 4) + i;
+      qv[i] = to_f32(sQ[row * NS + n]);
+      rpa[i] = 0.f;
+      if (COORD) {
+        const float er = __expf(-sRate[n] * 0.5f * cdend);
+        const float cc = ai[i] + er * ae[i];
+        dc[i] = __expf(-sRate[n] * (cdt - 0.5f * cdend)) * cc;
+        const float dr = qv[i] * cc;
+        tokacc += -sRate[n] * dr;
+        rpa[i] = -cdt * dr;
+      } else {
+        dc[i] = ai[i] + elt * ae[i];
+        tokacc += qv[i] * elt * ae[i];  // C~ o dC~ (inter part)
+      }
+    }
+    if (COORD) {
+#pragma unroll
+      for (int i = 0; i < 4; i += 2) {
+        const int n = 16 * tnn + 4 * (lane >> 4) + i;
+        if (n >= nreal) {
+          const int kp = (n - nreal) >> 1;
+          const float er = __expf(-sRate[n] * 0.5f * cdend);
+          const float ca = ai[i] + er * ae[i], cb = ai[i + 1] + er * ae[i + 1];
+          const float dth = -qv[i] * cb + qv[i + 1] * ca;  // C~^T J dC~ (scaled form)
+          tokacc += sOmega[kp] * dth;
+          rpw[i >> 1] = cdt * dth;
+          float sn, cs;
+          sincosf(sOmega[kp] * cdt, &sn, &cs);
+          const float a0 = dc[i], a1 = dc[i + 1];
+          dc[i] = cs * a0 - sn * a1;
+          dc[i + 1] = sn * a0 + cs * a1;
+        }
+      }
+    }
+    if (tg < L) {
+      const int n0 = 16 * tnn + 4 * (lane >> 4);
+      T* dst = dCg + ((((size_t)b * L + tg) * G + g) * R + o) * N + n0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dst[i] = from_f32<T>(dc[i]);
+    }
+    if (COORD) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int off = 1; off < 16; off <<= 1) rpa[i] += __shfl_xor(rpa[i], off, kWave);
+      }
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+#pragma unroll
+        for (int off = 1; off < 16; off <<= 1) rpw[q] += __shfl_xor(rpw[q], off, kWave);
+      }
+      if ((lane & 15) == 0) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int n = 16 * tnn + 4 * (lane >> 4) + i;
+          sPA[wave][n] += rpa[i];
+          if ((i & 1) == 0 && n >= nreal) sPW[wave][(n - nreal) >> 1] += rpw[i >> 1];
+        }
+      }
+    }
+    tokacc += __shfl_xor(tokacc, 16, kWave);
+    tokacc += __shfl_xor(tokacc, 32, kWave);
+#pragma unroll
+    for (int off = 1; off < R; off <<= 1) tokacc += __shfl_xor(tokacc, off, kWave);
+    if (lane < 16 && (lane % R) == 0) {
+      if (COORD) sTok[wave][t] += tokacc;
+      else sTT[wave][t] += tokacc;
+    }
+  }
+  __syncthreads();
+
+  // ---------------------------------------------------------------- two-endpoint assembly
+  if (S::TE) {
+    for (int i = tid; i < QT * R * P; i += S::NTH) {
+      const int s = i / (R * P), rem = i % (R * P), r = rem / P, pp = rem % P;
+      const int t = t0 + s;
+      float v = sDX[((s + 1) * R + r) * P + pp];
+      if (s + 1 < QT) v += sDX[(QT + 1) * R * P + ((s + 1) * R + r) * P + pp];
+      else v += sTailX[r * P + pp];
+      if (p.has_D) v += Dh * to_f32(sY[(s * R + r) * PS + pp]);
+      if (t < L) dxg[((((size_t)b * L + t) * H + h) * R + r) * P + pp] = from_f32<T>(v);
+    }
+    for (int i = tid; i < QT * R * N; i += S::NTH) {
+      const int s = i / (R * N), rem = i % (R * N), r = rem / N, n = rem % N;
+      const int t = t0 + s;
+      float v = sDB[((s + 1) * R + r) * N + n];
+      if (s + 1 < QT) v += sDB[(QT + 1) * R * N + ((s + 1) * R + r) * N + n];
+      else v += sTailB[r * N + n];
+      if (t < L) dBg[((((size_t)b * L + t) * G + g) * R + r) * N + n] = from_f32<T>(v);
+    }
+  }
+
+  // ---------------------------------------------------------------- step gradient
+  // per-token d(loss)/d(L_t) contributions; the final-state term sits on the last
+  // position of the chunk; dDelta_r = sum_{t >= r} dcd_t (reverse cumsum).
+  if (wave == 0) {
+    float tok = 0.f, dunw = 0.f;  // weighted dcd_t, and (head) the unweighted D_t
+    float srcsum = 0.f, e = 0.f;
+    if (COORD) {
+      if (lane < QT) tok = sTok[0][lane] + sTok[1][lane] + sTok[2][lane] + sTok[3][lane];
+      float eterm = 0.f;
+      for (int n = lane; n < N; n += kWave) {
+        const float en = sE[n] + sEK[0][n] + sEK[1][n] + sEK[2][n] + sEK[3][n];
+        eterm += -sRate[n] * en;
+      }
+      for (int k = lane; k < npairs; k += kWave) {
+        const float et = sEth[k] + sEKth[0][k] + sEKth[1][k] + sEKth[2][k] + sEKth[3][k];
+        eterm += sOmega[k] * et;
+      }
+      eterm = wave_sum(eterm);
+      if (lane == QT - 1) tok += eterm;
+    } else {
+      float src = 0.f;
+      if (lane < QT) {
+        const float rs = sRS[0][lane] + sRS[1][lane] + sRS[2][lane] + sRS[3][lane];
+        const float cs = sCS[0][lane] + sCS[1][lane] + sCS[2][lane] + sCS[3][lane];
+        const float tt = sTT[0][lane] + sTT[1][lane] + sTT[2][lane] + sTT[3][lane];
+        src = sSrc[0][lane] + sSrc[1][lane] + sSrc[2][lane] + sSrc[3][lane];
+        dunw = rs - cs + tt - src;
+      }
+      srcsum = wave_sum(src);
+      for (int n = lane; n < N; n += kWave) e += sE[n];
+      e = wave_sum(e);
+      if (lane == QT - 1) dunw += e + srcsum;
+      tok = -Ah * dunw;
+    }
+    const float tot = wave_sum(tok);
+    const float pre = wave_prefix_sum(tok);
+    const float rev = tot - pre + tok;
+    const int t = t0 + lane;
+    if (lane < QT && t < L) {
+      const size_t idx = ((size_t)b * L + t) * H + h;
+      p.ddt[idx] = p.softplus ? rev * sigmoid_f32(raw_l) : rev;
+      if (S::TE) {
+        if (p.dgamma) p.dgamma[idx] = sDg[0][lane] + sDg[1][lane] + sDg[2][lane] + sDg[3][lane];
+        if (p.dbeta) p.dbeta[idx] = sDb[0][lane] + sDb[1][lane] + sDb[2][lane] + sDb[3][lane];
+      }
+    }
+    if (!COORD && p.part) {
+      // dA_h partial = sum_t (-cd_t) D_t
+      const float v = wave_sum(lane < QT ? -cd_l * dunw : 0.f);
+      if (lane == 0) p.part[((size_t)slice * nch + c) * p.npart] = v;
+    }
+  }
+  // parameter partials of this chunk (per-row mode)
+  if (p.part) {
+    float* dst = p.part + ((size_t)slice * nch + c) * p.npart;
+    const int na = (COORD && !p.head_rates) ? nreal + npairs : 1;
+    if (COORD) {
+      __syncthreads();
+      for (int n = tid; n < N; n += S::NTH) {
+        const float en = sE[n] + sEK[0][n] + sEK[1][n] + sEK[2][n] + sEK[3][n];
+        sEK[0][n] = sPA[0][n] + sPA[1][n] + sPA[2][n] + sPA[3][n] + (-cdend) * en;
+      }
+      __syncthreads();
+      if (p.head_rates) {
+        if (wave == 0) {
+          float v = 0.f;
+          for (int n = lane; n < N; n += kWave) v += sEK[0][n];
+          v = wave_sum(v);
+          if (lane == 0) dst[0] = v;
+        }
+      } else {
+        for (int n = tid; n < nreal; n += S::NTH) dst[n] = sEK[0][n];
+        for (int k = tid; k < npairs; k += S::NTH) {
+          const int n = nreal + 2 * k;
+          dst[nreal + k] = sEK[0][n] + sEK[0][n + 1];
+          const float et = sEth[k] + sEKth[0][k] + sEKth[1][k] + sEKth[2][k] + sEKth[3][k];
+          dst[na + k] = sPW[0][k] + sPW[1][k] + sPW[2][k] + sPW[3][k] + cdend * et;
+        }
+      }
+    }
+    if (tid == 0) dst[na + npairs] = sMisc[0] + sMisc[1] + sMisc[2] + sMisc[3];
+  }
+}
+
+// ============================================================== parameter sums
+__global__ void ssm_bwd_params(BwdParams p, int nA) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  const int per_head = p.npart;
+  if (i >= p.H * per_head) return;
+  const int h = i / per_head, k = i % per_head;
+  float acc = 0.f;
+  for (int b = 0; b < p.batch; ++b) {
+    const float* src = p.part + ((size_t)(b * p.H + h) * p.nchunks) * per_head + k;
+    for (int c = 0; c < p.nchunks; ++c) acc += src[(size_t)c * per_head];
+  }
+  if (k < nA) {
+    if (p.dA) p.dA[(size_t)h * nA + k] = acc;
+  } else if (k < nA + p.n_pairs) {
+    if (p.domega) p.domega[(size_t)h * p.n_pairs + (k - nA)] = acc;
+  } else {
+    if (p.dD) p.dD[h] = acc;
+  }
+}
+
+// ------------------------------------------------------------------ dispatch
+// (io bf16?, N, P, R, keys per token, tokens per chunk, per-row decay)
+#define SSM_BWD_VARIANTS(X)            \
+  X(false, 16, 16, 1, 1, 64, false)    \
+  X(false, 32, 16, 1, 1, 64, false)    \
+  X(false, 32, 16, 2, 2, 32, false)    \
+  X(false, 16, 16, 1, 2, 16, true)     \
+  X(false, 32, 16, 1, 2, 16, true)     \
+  X(false, 32, 16, 2, 4, 16, true)     \
+  X(false, 32, 16, 1, 1, 32, true)     \
+  X(false, 32, 16, 2, 2, 16, true)     \
+  X(true, 64, 64, 1, 1, 64, false)     \
+  X(true, 128, 64, 1, 1, 64, false)    \
+  X(true, 64, 64, 4, 4, 16, false)     \
+  X(true, 64, 64, 1, 2, 16, true)      \
+  X(true, 64, 64, 2, 4, 16, true)
+
+bool bwd_variant_exists(const BwdKey& k) {
+#define SSM_BWD_MATCH(BF, NN, PP, RR, KRR, QTT, CO)                                          \
+  if (k.bf16 == BF && k.N == NN && k.P == PP && k.R == RR && k.KR == KRR && k.QT == QTT &&   \
+      k.coord == CO)                                                                         \
+    return true;
+  SSM_BWD_VARIANTS(SSM_BWD_MATCH)
+#undef SSM_BWD_MATCH
+  return false;
+}
+
+hipError_t launch_bwd(const BwdKey& k, const BwdParams& p, hipStream_t stream) {
+  const int slices = p.batch * p.H;
+  if (slices == 0 || p.nchunks == 0) return hipSuccess;
+  const int nA = k.coord && !p.head_rates ? p.n_real + p.n_pairs : 1;
+#define SSM_BWD_LAUNCH(BF, NN, PP, RR, KRR, QTT, CO)                                          \
+  if (k.bf16 == BF && k.N == NN && k.P == PP && k.R == RR && k.KR == KRR && k.QT == QTT &&    \
+      k.coord == CO) {                                                                        \
+    constexpr int PB = 16;                                                                    \
+    hipLaunchKernelGGL((ssm_bwd_adjoint<BF, NN, PB, RR, QTT, CO>), dim3(slices * (PP / PB)),  \
+                       dim3(256), 0, stream, p);                                              \
+    hipLaunchKernelGGL((ssm_bwd_chunk<BF, NN, PP, RR, KRR, QTT, CO>),                          \
+                       dim3(slices * p.nchunks), dim3(256), 0, stream, p);                    \
+    hipLaunchKernelGGL(ssm_bwd_params, dim3((p.H * p.npart + 255) / 256), dim3(256), 0,      \
+                       stream, p, nA);                                                        \
+    return hipGetLastError();                                                                 \
+  }
+  SSM_BWD_VARIANTS(SSM_BWD_LAUNCH)
+#undef SSM_BWD_LAUNCH
+  return hipErrorInvalidValue;
+}
+
 }  // namespace ssm
