@@ -107,7 +107,21 @@ def main():
     ap.add_argument("--workload", default="ssd_siso", choices=sorted(workloads.WORKLOADS))
     ap.add_argument("--mode", default="fwdbwd", choices=["fwd", "fwdbwd"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (for HBM counter scaling)")
     args = ap.parse_args()
+
+    if args.copy_calibration:
+        import torch
+
+        n = args.copy_calibration * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": n * 4, "copy_bytes_written": n * 4, "launches": 3}))
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
@@ -148,17 +162,18 @@ def main():
     ws = torch.empty(max(ws_f, ws_b, 1), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
 
-    def fwd():
+    def fwd(events=None):
         ssm.scan_fwd(desc, t["x"], t["B"], t["C"], t["dt"], t["A"], y, omega=t.get("omega"),
                      beta=t.get("beta"), gamma=t.get("gamma"), D=t.get("D"), saved=saved, ws=ws,
-                     stream=stream)
+                     stream=stream, events=events)
 
-    def bwd():
+    def bwd(events=None):
         ssm.scan_bwd(desc, t["x"], t["B"], t["C"], t["dy"], t["dt"], t["A"], saved, grads["dx"],
                      grads["dB"], grads["dC"], grads["ddt"], omega=t.get("omega"),
                      beta=t.get("beta"), gamma=t.get("gamma"), D=t.get("D"), dA=grads.get("dA"),
                      domega=grads.get("domega"), dbeta=grads.get("dbeta"),
-                     dgamma=grads.get("dgamma"), dD=grads.get("dD"), ws=ws, stream=stream)
+                     dgamma=grads.get("dgamma"), dD=grads.get("dD"), ws=ws, stream=stream,
+                     events=events)
 
     for _ in range(args.warmup):
         fwd()
@@ -166,39 +181,54 @@ def main():
             bwd()
     torch.cuda.synchronize()
 
-    # events on the stream the kernels are enqueued on (torch's current stream)
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
+    # HIP events recorded by the library on the stream the kernels run on, around
+    # each kernel (forward: 1 kernel; reverse pass: 3 kernels)
+    mk = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    evf = [[mk() for _ in range(2)] for _ in range(args.steps)]
+    evb = [[mk() for _ in range(4)] for _ in range(args.steps)]
+    for e in [e for row in evf + evb for e in row]:
+        e.record(stream)  # materialize the handles
+    start, end = mk(), mk()
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     start.record(stream)
     for k in range(args.steps):
-        ev[k][0].record(stream)
-        fwd()
-        ev[k][1].record(stream)
+        fwd(evf[k])
         if args.mode == "fwdbwd":
-            bwd()
-        ev[k][2].record(stream)
+            bwd(evb[k])
     end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     total_ms = start.elapsed_time(end)
-    fwd_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
-    bwd_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev])) if args.mode == "fwdbwd" else 0.0
+
+    def avg(rows, i, j):
+        return float(np.mean([r[i].elapsed_time(r[j]) for r in rows]))
+
+    kern_ms = {"ssm_fwd_kernel": avg(evf, 0, 1)}
+    if args.mode == "fwdbwd":
+        kern_ms["ssm_bwd_adjoint"] = avg(evb, 0, 1)
+        kern_ms["ssm_bwd_chunk"] = avg(evb, 1, 2)
+        kern_ms["ssm_bwd_params"] = avg(evb, 2, 3)
+    fwd_ms = kern_ms["ssm_fwd_kernel"]
+    bwd_ms = sum(v for k, v in kern_ms.items() if k.startswith("ssm_bwd"))
     ms_per_step = total_ms / args.steps
     tokens = d["batch"] * d["seqlen"]
     value = tokens / (ms_per_step * 1e-3) / 1e6
 
     io_bytes = 2 if io == "bf16" else 4
-    kern = "bwd" if bwd_ms > fwd_ms else "fwd"
-    kms = bwd_ms if kern == "bwd" else fwd_ms
-    abytes = algorithmic_bytes(d, io_bytes, kern)
+    # the dominant kernel; the compulsory bytes of a direction are carried by its
+    # main kernel (the reverse pass's chunk-gradient kernel reads every input and
+    # writes every gradient; its boundary-adjoint and parameter kernels are overhead)
+    kern = max(kern_ms, key=kern_ms.get)
+    kms = kern_ms[kern]
+    direction = "fwd" if kern == "ssm_fwd_kernel" else "bwd"
+    abytes = algorithmic_bytes(d, io_bytes, direction) if kern in ("ssm_fwd_kernel",
+                                                                   "ssm_bwd_chunk") else 0
     achieved = abytes / (kms * 1e-3) / 1e9
     traffic = measured_traffic(kern, args.workload)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "kernel": f"ssm_{kern}", "algorithmic_bytes_per_launch": abytes,
+                "kernel": kern, "algorithmic_bytes_per_launch": abytes,
                 "avg_launch_ms": round(kms, 4)}
     fwd_bytes = algorithmic_bytes(d, io_bytes, "fwd")
 
@@ -218,7 +248,8 @@ def main():
                    "step": "forward + reverse" if args.mode == "fwdbwd" else "forward"},
         "roofline": roofline,
         "cpu_baseline": cpu,
-        "breakdown": {"fwd_ms": round(fwd_ms, 4), "bwd_ms": round(bwd_ms, 4),
+        "breakdown": {"kernel_ms": {k: round(v, 4) for k, v in kern_ms.items()},
+                      "fwd_ms": round(fwd_ms, 4), "bwd_ms": round(bwd_ms, 4),
                       "fwd_mtok_s": round(tokens / (fwd_ms * 1e-3) / 1e6, 3),
                       "fwd_hbm_frac": round(fwd_bytes / (fwd_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                       "wall_s": round(wall, 3)},

@@ -110,6 +110,8 @@ typedef struct {
   const float *dt, *A, *omega, *beta, *gamma, *D;
   void *y;
   float *saved; /* optional: chunk-boundary states for the backward */
+  void *const *events; /* optional: 2 hipEvent_t recorded on `stream` before and after
+                          the kernel (per-kernel timing); NULL = none */
 } ssm_fwd_args;
 
 typedef struct {
@@ -118,6 +120,9 @@ typedef struct {
   const float *saved; /* filled by ssm_scan_fwd with the same inputs */
   void *dx, *dB, *dC;
   float *ddt, *dA, *domega, *dbeta, *dgamma, *dD;
+  void *const *events; /* optional: 4 hipEvent_t recorded on `stream` around the three
+                          kernels of the pass (boundary adjoints, chunk gradients,
+                          parameter sums); NULL = none */
 } ssm_bwd_args;
 
 /* Library ABI version (SSM_ABI_VERSION of the build). */

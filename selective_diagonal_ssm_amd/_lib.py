@@ -39,13 +39,13 @@ _vp = ctypes.c_void_p
 
 class SsmFwdArgs(ctypes.Structure):
     _fields_ = [(n, _vp) for n in ("x", "B", "C", "dt", "A", "omega", "beta", "gamma", "D", "y",
-                                   "saved")]
+                                   "saved", "events")]
 
 
 class SsmBwdArgs(ctypes.Structure):
     _fields_ = [(n, _vp) for n in ("x", "B", "C", "dy", "dt", "A", "omega", "beta", "gamma", "D",
                                    "saved", "dx", "dB", "dC", "ddt", "dA", "domega", "dbeta",
-                                   "dgamma", "dD")]
+                                   "dgamma", "dD", "events")]
 
 
 class SsmError(RuntimeError):
@@ -119,11 +119,22 @@ def workspace_bytes(desc: SsmDesc, for_backward: bool) -> int:
     return load().ssm_workspace_bytes(ctypes.byref(desc), int(for_backward))
 
 
+def _events(events):
+    """ctypes array of hipEvent_t handles from torch.cuda.Event objects (recorded once
+    beforehand so that the handles exist), or None."""
+    if not events:
+        return None, None
+    arr = (ctypes.c_void_p * len(events))(*[ctypes.c_void_p(e.cuda_event) for e in events])
+    return ctypes.cast(arr, ctypes.c_void_p), arr
+
+
 def scan_fwd(desc: SsmDesc, x, B, C, dt, A, y, omega=None, beta=None, gamma=None, D=None,
-             saved=None, ws=None, stream=None) -> None:
-    """Enqueue the forward scan; all tensors are caller-allocated device tensors."""
+             saved=None, ws=None, stream=None, events=None) -> None:
+    """Enqueue the forward scan; all tensors are caller-allocated device tensors.
+    `events`: optional 2 torch.cuda.Event recorded around the kernel."""
+    ev, _keep = _events(events)
     args = SsmFwdArgs(_ptr(x), _ptr(B), _ptr(C), _ptr(dt), _ptr(A), _ptr(omega), _ptr(beta),
-                      _ptr(gamma), _ptr(D), _ptr(y), _ptr(saved))
+                      _ptr(gamma), _ptr(D), _ptr(y), _ptr(saved), ev)
     ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
     rc = load().ssm_scan_fwd(ctypes.byref(desc), ctypes.byref(args), _ptr(ws), ws_bytes,
                              _stream(stream))
@@ -133,12 +144,14 @@ def scan_fwd(desc: SsmDesc, x, B, C, dt, A, y, omega=None, beta=None, gamma=None
 
 def scan_bwd(desc: SsmDesc, x, B, C, dy, dt, A, saved, dx, dB, dC, ddt, omega=None, beta=None,
              gamma=None, D=None, dA=None, domega=None, dbeta=None, dgamma=None, dD=None, ws=None,
-             stream=None) -> None:
-    """Enqueue the fused reverse pass; all tensors are caller-allocated device tensors."""
+             stream=None, events=None) -> None:
+    """Enqueue the fused reverse pass; all tensors are caller-allocated device tensors.
+    `events`: optional 4 torch.cuda.Event recorded around the pass's three kernels."""
+    ev, _keep = _events(events)
     args = SsmBwdArgs(_ptr(x), _ptr(B), _ptr(C), _ptr(dy), _ptr(dt), _ptr(A), _ptr(omega),
                       _ptr(beta), _ptr(gamma), _ptr(D), _ptr(saved), _ptr(dx), _ptr(dB),
                       _ptr(dC), _ptr(ddt), _ptr(dA), _ptr(domega), _ptr(dbeta), _ptr(dgamma),
-                      _ptr(dD))
+                      _ptr(dD), ev)
     ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
     rc = load().ssm_scan_bwd(ctypes.byref(desc), ctypes.byref(args), _ptr(ws), ws_bytes,
                              _stream(stream))

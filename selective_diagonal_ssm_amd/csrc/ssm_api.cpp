@@ -64,27 +64,50 @@ int make_plan(const ssm_desc* d, Plan* pl) {
   }
   pl->QT = qt;
   pl->nchunks = (d->seqlen + qt - 1) / qt;
-  // a forward variant with some P-block must exist for this shape
-  for (int pb : {64, 32, 16}) {
-    FwdKey k{pl->bf16, d->dstate, pb, pl->R, pl->KR, pl->QT, pl->coord_kernel};
-    if (d->headdim % pb == 0 && ssm::fwd_variant_exists(k)) return SSM_OK;
-  }
+  // a forward variant must exist for this shape
+  for (int pb : {64, 32, 16})
+    for (int nt : {1024, 512, 256}) {
+      FwdKey k{pl->bf16, d->dstate, pb, pl->R, pl->KR, pl->QT, pl->coord_kernel, nt};
+      if (d->headdim % pb == 0 && ssm::fwd_variant_exists(k)) return SSM_OK;
+    }
   return SSM_ERR_UNSUPPORTED;
 }
 
-int choose_pb(const ssm_desc* d, const Plan& pl) {
-  const int forced = env_int("SSM_FWD_PB", 0);
+// Forward variant: P-block width and workgroup size.  Preference: the widest
+// workgroup that exists, with the P-block chosen so that (batch x heads x
+// P-blocks) workgroups cover the machine without needless P-splitting (a split
+// recomputes the chunk scores once per block).  SSM_FWD_PB / SSM_FWD_THREADS
+// force a choice among the instantiated variants (experiments).
+FwdKey choose_fwd(const ssm_desc* d, const Plan& pl) {
+  const int force_pb = env_int("SSM_FWD_PB", 0);
+  const int force_nt = env_int("SSM_FWD_THREADS", 0);
   const long slices = (long)d->batch * d->nheads;
-  int best = 0;
+  FwdKey best{pl.bf16, d->dstate, 0, pl.R, pl.KR, pl.QT, pl.coord_kernel, 0};
+  long best_score = -1;
   for (int pb : {64, 32, 16}) {
-    FwdKey k{pl.bf16, d->dstate, pb, pl.R, pl.KR, pl.QT, pl.coord_kernel};
-    if (d->headdim % pb || !ssm::fwd_variant_exists(k)) continue;
-    if (forced) {
-      if (pb == forced) return pb;
-      continue;
+    if (d->headdim % pb) continue;
+    if (force_pb && pb != force_pb) continue;
+    for (int nt : {1024, 512, 256}) {
+      if (force_nt && nt != force_nt) continue;
+      FwdKey k{pl.bf16, d->dstate, pb, pl.R, pl.KR, pl.QT, pl.coord_kernel, nt};
+      if (!ssm::fwd_variant_exists(k)) continue;
+      // score: enough workgroups to occupy the 256 compute units (at least
+      // ~0.75 of them), then the widest P-block, then the widest workgroup
+      const long wgs = slices * (d->headdim / pb);
+      const long score = (wgs >= 192 ? 1000000L : wgs * 1000L) + pb * 100L + nt / 16;
+      if (score > best_score) {
+        best_score = score;
+        best = k;
+      }
     }
-    best = pb;  // smallest available so far
-    if (slices * (d->headdim / pb) >= 512) return pb;
+  }
+  if (best_score < 0) {
+    // forced combination not instantiated: fall back to any existing variant
+    for (int pb : {64, 32, 16})
+      for (int nt : {1024, 512, 256}) {
+        FwdKey k{pl.bf16, d->dstate, pb, pl.R, pl.KR, pl.QT, pl.coord_kernel, nt};
+        if (d->headdim % pb == 0 && ssm::fwd_variant_exists(k)) return k;
+      }
   }
   return best;
 }
@@ -167,8 +190,9 @@ int ssm_scan_fwd(const ssm_desc* d, const ssm_fwd_args* a, void* ws, size_t ws_b
                         (const void*)a->saved})
     if (q && !aligned(q, 4)) return SSM_ERR_ALIGN;
 
-  const int pb = choose_pb(d, pl);
-  FwdKey key{pl.bf16, d->dstate, pb, pl.R, pl.KR, pl.QT, pl.coord_kernel};
+  const FwdKey key = choose_fwd(d, pl);
+  if (key.PB <= 0 || d->headdim % key.PB) return SSM_ERR_UNSUPPORTED;
+  const int pb = key.PB;
   ssm::FwdParams p{};
   p.x = a->x; p.B = a->B; p.C = a->C; p.dt = a->dt; p.A = a->A; p.omega = a->omega;
   p.beta = a->beta; p.gamma = a->gamma; p.D = a->D; p.y = a->y; p.saved = a->saved;
@@ -178,7 +202,7 @@ int ssm_scan_fwd(const ssm_desc* d, const ssm_fwd_args* a, void* ws, size_t ws_b
   p.softplus = (d->flags & SSM_F_DT_SOFTPLUS) ? 1 : 0;
   p.has_D = hasD ? 1 : 0;
   p.head_rates = pl.head_rates ? 1 : 0;
-  const hipError_t e = ssm::launch_fwd(key, p, static_cast<hipStream_t>(stream));
+  const hipError_t e = ssm::launch_fwd(key, p, static_cast<hipStream_t>(stream), a->events);
   return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
 }
 
@@ -230,7 +254,7 @@ int ssm_scan_bwd(const ssm_desc* d, const ssm_bwd_args* a, void* ws, size_t ws_b
   p.has_D = hasD ? 1 : 0;
   p.npart = npart_of(d, pl);
   p.head_rates = pl.head_rates ? 1 : 0;
-  const hipError_t e = ssm::launch_bwd(key, p, static_cast<hipStream_t>(stream));
+  const hipError_t e = ssm::launch_bwd(key, p, static_cast<hipStream_t>(stream), a->events);
   return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
 }
 

@@ -33,7 +33,7 @@
 namespace ssm {
 
 // ============================================================== boundary adjoints
-template <bool BF16, int N, int PB, int R, int QT, bool COORD>
+template <bool BF16, int N, int PB, int R, int QT, bool COORD, int NTHREADS>
 struct AdjShape {
   using T = typename Elem<BF16>::T;
   static constexpr int VEC = Elem<BF16>::kVec;
@@ -42,19 +42,21 @@ struct AdjShape {
   static constexpr int QOC = (QO + 31) / 32 * 32;  // contraction rows, zero padded
   static constexpr int NS = N + PAD;
   static constexpr int VS = PB + PAD;
-  static constexpr int NTH = 256;
+  static constexpr int NTH = NTHREADS;
+  static constexpr int NW = NTHREADS / 64;
   static constexpr int C_VECS = QO * (N / VEC);
   static constexpr int Y_VECS = QO * (PB / VEC);
   static constexpr int C_PER = (C_VECS + NTH - 1) / NTH;
   static constexpr int Y_PER = (Y_VECS + NTH - 1) / NTH;
   static constexpr int TN = N / 16, TP = PB / 16;
   static constexpr int ST_TILES = TN * TP;
-  static constexpr int ST_PER_WAVE = (ST_TILES + 3) / 4;
+  static constexpr int ST_PER_WAVE = (ST_TILES + NW - 1) / NW;
 };
 
-template <bool BF16, int N, int PB, int R, int QT, bool COORD>
-__global__ __launch_bounds__(256) void ssm_bwd_adjoint(BwdParams p) {
-  using S = AdjShape<BF16, N, PB, R, QT, COORD>;
+template <bool BF16, int N, int PB, int R, int QT, bool COORD, int NTHREADS>
+__global__ __launch_bounds__(NTHREADS) void ssm_bwd_adjoint(BwdParams p) {
+  using S = AdjShape<BF16, N, PB, R, QT, COORD, NTHREADS>;
+  constexpr int NW = S::NW;
   using T = typename S::T;
   constexpr int NS = S::NS, VS = S::VS, VEC = S::VEC;
   __shared__ __align__(16) T sQ[S::QOC * NS];  // folded, decayed C rows
@@ -113,7 +115,7 @@ __global__ __launch_bounds__(256) void ssm_bwd_adjoint(BwdParams p) {
     // carried adjoint: Gpre[c+1] -> Phi_{t0',t0}^T Gpre[c+1]
 #pragma unroll
     for (int k = 0; k < S::ST_PER_WAVE; ++k) {
-      const int tile = wave + 4 * k;
+      const int tile = wave + NW * k;
       if (tile < S::ST_TILES) {
         const int tnn = tile / S::TP;
 #pragma unroll
@@ -193,7 +195,7 @@ __global__ __launch_bounds__(256) void ssm_bwd_adjoint(BwdParams p) {
     __syncthreads();
 #pragma unroll
     for (int k = 0; k < S::ST_PER_WAVE; ++k) {
-      const int tile = wave + 4 * k;
+      const int tile = wave + NW * k;
       if (tile < S::ST_TILES) {
         const int tnn = tile / S::TP, tp = tile % S::TP;
         f32x4 acc = st[k];
@@ -217,7 +219,23 @@ __global__ __launch_bounds__(256) void ssm_bwd_adjoint(BwdParams p) {
 }
 
 // ============================================================== chunk gradients
-template <bool BF16, int N, int P, int R, int KR, int QT, bool COORD>
+// fixed-order sum of per-wave slots
+template <int NW, typename A>
+__device__ __forceinline__ float wsum(const A& arr, int i) {
+  float v = 0.f;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) v += arr[w][i];
+  return v;
+}
+template <int NW>
+__device__ __forceinline__ float wsum1(const float* arr) {
+  float v = 0.f;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) v += arr[w];
+  return v;
+}
+
+template <bool BF16, int N, int P, int R, int KR, int QT, bool COORD, int NTHREADS>
 struct BwdShape {
   using T = typename Elem<BF16>::T;
   static constexpr int VEC = Elem<BF16>::kVec;
@@ -233,7 +251,8 @@ struct BwdShape {
   static constexpr int PS = PC + PAD;   // [row][p] buffers
   static constexpr int KS = QK + PAD;   // [row][key] buffers
   static constexpr int BROWS = (QT + TEH) * R;
-  static constexpr int NTH = 256;
+  static constexpr int NTH = NTHREADS;
+  static constexpr int NW = NTHREADS / 64;
   static constexpr int C_VECS = QO * (N / VEC);
   static constexpr int B_VECS = BROWS * (N / VEC);
   static constexpr int X_VECS = BROWS * (P / VEC);
@@ -243,9 +262,10 @@ struct BwdShape {
   static_assert(N % 16 == 0 && P % 16 == 0 && QT <= 64, "unsupported tile shape");
 };
 
-template <bool BF16, int N, int P, int R, int KR, int QT, bool COORD>
-__global__ __launch_bounds__(256) void ssm_bwd_chunk(BwdParams p) {
-  using S = BwdShape<BF16, N, P, R, KR, QT, COORD>;
+template <bool BF16, int N, int P, int R, int KR, int QT, bool COORD, int NTHREADS>
+__global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
+  using S = BwdShape<BF16, N, P, R, KR, QT, COORD, NTHREADS>;
+  constexpr int NW = S::NW;
   using T = typename S::T;
   constexpr int NS = S::NS, PS = S::PS, KS = S::KS, VEC = S::VEC;
   constexpr int QO = S::QO, QK = S::QK;
@@ -263,16 +283,18 @@ __global__ __launch_bounds__(256) void ssm_bwd_chunk(BwdParams p) {
   __shared__ __align__(16) T sSl[N * PS];
   __shared__ float sRate[N], sOmega[N / 2 + 1];
   __shared__ float sE[N], sEth[N / 2 + 1];       // final-state terms per row / pair
-  __shared__ float sEK[4][N], sEKth[4][N / 2 + 1];  // per-wave inter source sums per row / pair
-  __shared__ float sTok[4][64];                  // per-wave per-token dcd contributions (per-row mode)
-  __shared__ float sTT[4][64], sSrc[4][64];      // head: target / source inter terms per token
-  __shared__ float sRS[4][64], sCS[4][64];       // head: row / column sums of Z o S o M
-  __shared__ float sDg[4][64], sDb[4][64];       // per-wave dgamma / dbeta sums
-  __shared__ float sPA[4][N], sPW[4][N / 2 + 1]; // per-wave parameter partials
+  constexpr int WC = COORD ? NW : 1, WH = COORD ? 1 : NW, WT = S::TE ? NW : 1;
+  constexpr int NCO = COORD ? N : 1, PCO = COORD ? N / 2 + 1 : 1;
+  __shared__ float sEK[WC][NCO], sEKth[WC][PCO];  // per-wave inter source sums per row / pair
+  __shared__ float sPA[WC][NCO], sPW[WC][PCO];    // per-wave parameter partials
+  __shared__ float sTok[WC][64];                  // per-wave weighted per-token terms (per-row mode)
+  __shared__ float sTT[WH][64], sSrc[WH][64];     // head: target / source inter terms per token
+  __shared__ float sRS[WH][64], sCS[WH][64];      // head: row / column sums of Z o S o M
+  __shared__ float sDg[WT][64], sDb[WT][64];      // per-wave dgamma / dbeta sums
   __shared__ float sDX[S::TE ? 2 * (QT + 1) * R * P : 1];  // two-endpoint dX assembly
   __shared__ float sDB[S::TE ? 2 * (QT + 1) * R * N : 1];  // two-endpoint dB assembly
   __shared__ float sTailX[S::TE ? R * P : 1], sTailB[S::TE ? R * N : 1];
-  __shared__ float sMisc[8];
+  __shared__ float sMisc[NW];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int nch = p.nchunks;
@@ -301,13 +323,14 @@ __global__ __launch_bounds__(256) void ssm_bwd_chunk(BwdParams p) {
     }
     for (int k = tid; k < npairs; k += S::NTH) sOmega[k] = p.omega[(size_t)h * npairs + k];
   }
-  for (int i = tid; i < 4 * 64; i += S::NTH) {
-    (&sTok[0][0])[i] = 0.f; (&sRS[0][0])[i] = 0.f; (&sCS[0][0])[i] = 0.f;
-    (&sDg[0][0])[i] = 0.f; (&sDb[0][0])[i] = 0.f; (&sTT[0][0])[i] = 0.f; (&sSrc[0][0])[i] = 0.f;
+  for (int i = tid; i < WC * 64; i += S::NTH) (&sTok[0][0])[i] = 0.f;
+  for (int i = tid; i < WH * 64; i += S::NTH) {
+    (&sTT[0][0])[i] = 0.f; (&sSrc[0][0])[i] = 0.f; (&sRS[0][0])[i] = 0.f; (&sCS[0][0])[i] = 0.f;
   }
+  for (int i = tid; i < WT * 64; i += S::NTH) { (&sDg[0][0])[i] = 0.f; (&sDb[0][0])[i] = 0.f; }
+  for (int i = tid; i < WC * NCO; i += S::NTH) { (&sEK[0][0])[i] = 0.f; (&sPA[0][0])[i] = 0.f; }
+  for (int i = tid; i < WC * PCO; i += S::NTH) { (&sEKth[0][0])[i] = 0.f; (&sPW[0][0])[i] = 0.f; }
   for (int i = tid; i < (S::NC - N) * PS; i += S::NTH) { sGh[N * PS + i] = T(0); sGl[N * PS + i] = T(0); }
-  for (int i = tid; i < 4 * N; i += S::NTH) { (&sEK[0][0])[i] = 0.f; (&sPA[0][0])[i] = 0.f; }
-  for (int i = tid; i < 4 * (N / 2 + 1); i += S::NTH) { (&sEKth[0][0])[i] = 0.f; (&sPW[0][0])[i] = 0.f; }
   // zero padding rows / columns
   for (int i = tid; i < (S::QOC - QO) * NS; i += S::NTH) sQ[QO * NS + i] = T(0);
   for (int i = tid; i < (S::QOC - QO) * PS; i += S::NTH) sY[QO * PS + i] = T(0);
@@ -565,7 +588,7 @@ __global__ __launch_bounds__(256) void ssm_bwd_chunk(BwdParams p) {
   if (lane == 0) sMisc[wave] = dDp;
 
   // ---------------------------------------------------------------- scores
-  for (int tile = wave; tile < S::TQ * S::TK; tile += 4) {
+  for (int tile = wave; tile < S::TQ * S::TK; tile += NW) {
     const int ti = tile / S::TK, tj = tile % S::TK;
     const int tmax = (16 * ti + 15) / R, smin = (16 * tj) / KR;
     f32x4 sc = {0.f, 0.f, 0.f, 0.f}, z = {0.f, 0.f, 0.f, 0.f};
@@ -615,7 +638,7 @@ __global__ __launch_bounds__(256) void ssm_bwd_chunk(BwdParams p) {
   __syncthreads();
 
   // ---------------------------------------------------------------- dV -> dX
-  for (int tile = wave; tile < S::TK * S::TP; tile += 4) {
+  for (int tile = wave; tile < S::TK * S::TP; tile += NW) {
     const int tj = tile / S::TP, tp = tile % S::TP;
     f32x4 ai = {0.f, 0.f, 0.f, 0.f}, ae = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -654,7 +677,7 @@ __global__ __launch_bounds__(256) void ssm_bwd_chunk(BwdParams p) {
   }
 
   // ---------------------------------------------------------------- dK~ -> dB, dbeta, dgamma
-  for (int tile = wave; tile < S::TN * S::TK; tile += 4) {
+  for (int tile = wave; tile < S::TN * S::TK; tile += NW) {
     const int tnn = tile / S::TK, tj = tile % S::TK;
     f32x4 ai = {0.f, 0.f, 0.f, 0.f}, ae = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -805,7 +828,7 @@ __global__ __launch_bounds__(256) void ssm_bwd_chunk(BwdParams p) {
   }
 
   // ---------------------------------------------------------------- dC~ -> dC
-  for (int tile = wave; tile < S::TN * S::TQ; tile += 4) {
+  for (int tile = wave; tile < S::TN * S::TQ; tile += NW) {
     const int tnn = tile / S::TQ, tq = tile % S::TQ;
     f32x4 ai = {0.f, 0.f, 0.f, 0.f}, ae = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -927,14 +950,14 @@ __global__ __launch_bounds__(256) void ssm_bwd_chunk(BwdParams p) {
     float tok = 0.f, dunw = 0.f;  // weighted dcd_t, and (head) the unweighted D_t
     float srcsum = 0.f, e = 0.f;
     if (COORD) {
-      if (lane < QT) tok = sTok[0][lane] + sTok[1][lane] + sTok[2][lane] + sTok[3][lane];
+      if (lane < QT) tok = wsum<WC>(sTok, lane);
       float eterm = 0.f;
       for (int n = lane; n < N; n += kWave) {
-        const float en = sE[n] + sEK[0][n] + sEK[1][n] + sEK[2][n] + sEK[3][n];
+        const float en = sE[n] + wsum<WC>(sEK, n);
         eterm += -sRate[n] * en;
       }
       for (int k = lane; k < npairs; k += kWave) {
-        const float et = sEth[k] + sEKth[0][k] + sEKth[1][k] + sEKth[2][k] + sEKth[3][k];
+        const float et = sEth[k] + wsum<WC>(sEKth, k);
         eterm += sOmega[k] * et;
       }
       eterm = wave_sum(eterm);
@@ -942,10 +965,10 @@ __global__ __launch_bounds__(256) void ssm_bwd_chunk(BwdParams p) {
     } else {
       float src = 0.f;
       if (lane < QT) {
-        const float rs = sRS[0][lane] + sRS[1][lane] + sRS[2][lane] + sRS[3][lane];
-        const float cs = sCS[0][lane] + sCS[1][lane] + sCS[2][lane] + sCS[3][lane];
-        const float tt = sTT[0][lane] + sTT[1][lane] + sTT[2][lane] + sTT[3][lane];
-        src = sSrc[0][lane] + sSrc[1][lane] + sSrc[2][lane] + sSrc[3][lane];
+        const float rs = wsum<WH>(sRS, lane);
+        const float cs = wsum<WH>(sCS, lane);
+        const float tt = wsum<WH>(sTT, lane);
+        src = wsum<WH>(sSrc, lane);
         dunw = rs - cs + tt - src;
       }
       srcsum = wave_sum(src);
@@ -962,8 +985,8 @@ __global__ __launch_bounds__(256) void ssm_bwd_chunk(BwdParams p) {
       const size_t idx = ((size_t)b * L + t) * H + h;
       p.ddt[idx] = p.softplus ? rev * sigmoid_f32(raw_l) : rev;
       if (S::TE) {
-        if (p.dgamma) p.dgamma[idx] = sDg[0][lane] + sDg[1][lane] + sDg[2][lane] + sDg[3][lane];
-        if (p.dbeta) p.dbeta[idx] = sDb[0][lane] + sDb[1][lane] + sDb[2][lane] + sDb[3][lane];
+        if (p.dgamma) p.dgamma[idx] = wsum<WT>(sDg, lane);
+        if (p.dbeta) p.dbeta[idx] = wsum<WT>(sDb, lane);
       }
     }
     if (!COORD && p.part) {
@@ -979,8 +1002,8 @@ __global__ __launch_bounds__(256) void ssm_bwd_chunk(BwdParams p) {
     if (COORD) {
       __syncthreads();
       for (int n = tid; n < N; n += S::NTH) {
-        const float en = sE[n] + sEK[0][n] + sEK[1][n] + sEK[2][n] + sEK[3][n];
-        sEK[0][n] = sPA[0][n] + sPA[1][n] + sPA[2][n] + sPA[3][n] + (-cdend) * en;
+        const float en = sE[n] + wsum<WC>(sEK, n);
+        sEK[0][n] = wsum<WC>(sPA, n) + (-cdend) * en;
       }
       __syncthreads();
       if (p.head_rates) {
@@ -995,12 +1018,12 @@ __global__ __launch_bounds__(256) void ssm_bwd_chunk(BwdParams p) {
         for (int k = tid; k < npairs; k += S::NTH) {
           const int n = nreal + 2 * k;
           dst[nreal + k] = sEK[0][n] + sEK[0][n + 1];
-          const float et = sEth[k] + sEKth[0][k] + sEKth[1][k] + sEKth[2][k] + sEKth[3][k];
-          dst[na + k] = sPW[0][k] + sPW[1][k] + sPW[2][k] + sPW[3][k] + cdend * et;
+          const float et = sEth[k] + wsum<WC>(sEKth, k);
+          dst[na + k] = wsum<WC>(sPW, k) + cdend * et;
         }
       }
     }
-    if (tid == 0) dst[na + npairs] = sMisc[0] + sMisc[1] + sMisc[2] + sMisc[3];
+    if (tid == 0) dst[na + npairs] = wsum1<NW>(sMisc);
   }
 }
 
@@ -1051,20 +1074,36 @@ bool bwd_variant_exists(const BwdKey& k) {
   return false;
 }
 
-hipError_t launch_bwd(const BwdKey& k, const BwdParams& p, hipStream_t stream) {
+#ifndef ADJ_NT
+#define ADJ_NT 1024
+#endif
+#ifndef CHUNK_NT
+#define CHUNK_NT 512
+#endif
+#define ADJ_PB(PP) (PP)
+
+hipError_t launch_bwd(const BwdKey& k, const BwdParams& p, hipStream_t stream,
+                      void* const* events) {
   const int slices = p.batch * p.H;
   if (slices == 0 || p.nchunks == 0) return hipSuccess;
+  auto mark = [&](int i) {
+    if (events && events[i]) hipEventRecord(static_cast<hipEvent_t>(events[i]), stream);
+  };
   const int nA = k.coord && !p.head_rates ? p.n_real + p.n_pairs : 1;
 #define SSM_BWD_LAUNCH(BF, NN, PP, RR, KRR, QTT, CO)                                          \
   if (k.bf16 == BF && k.N == NN && k.P == PP && k.R == RR && k.KR == KRR && k.QT == QTT &&    \
       k.coord == CO) {                                                                        \
-    constexpr int PB = 16;                                                                    \
-    hipLaunchKernelGGL((ssm_bwd_adjoint<BF, NN, PB, RR, QTT, CO>), dim3(slices * (PP / PB)),  \
-                       dim3(256), 0, stream, p);                                              \
-    hipLaunchKernelGGL((ssm_bwd_chunk<BF, NN, PP, RR, KRR, QTT, CO>),                          \
-                       dim3(slices * p.nchunks), dim3(256), 0, stream, p);                    \
+    constexpr int PB = ADJ_PB(PP);                                                            \
+    mark(0);                                                                                  \
+    hipLaunchKernelGGL((ssm_bwd_adjoint<BF, NN, PB, RR, QTT, CO, ADJ_NT>),                     \
+                       dim3(slices * (PP / PB)), dim3(ADJ_NT), 0, stream, p);                 \
+    mark(1);                                                                                  \
+    hipLaunchKernelGGL((ssm_bwd_chunk<BF, NN, PP, RR, KRR, QTT, CO, CHUNK_NT>),                \
+                       dim3(slices * p.nchunks), dim3(CHUNK_NT), 0, stream, p);               \
+    mark(2);                                                                                  \
     hipLaunchKernelGGL(ssm_bwd_params, dim3((p.H * p.npart + 255) / 256), dim3(256), 0,      \
                        stream, p, nA);                                                        \
+    mark(3);                                                                                  \
     return hipGetLastError();                                                                 \
   }
   SSM_BWD_VARIANTS(SSM_BWD_LAUNCH)

@@ -31,7 +31,7 @@
 
 namespace ssm {
 
-template <bool BF16, int N, int PB, int R, int KR, int QT, bool COORD>
+template <bool BF16, int N, int PB, int R, int KR, int QT, bool COORD, int NTHREADS>
 struct FwdShape {
   using T = typename Elem<BF16>::T;
   static constexpr int VEC = Elem<BF16>::kVec;
@@ -45,7 +45,8 @@ struct FwdShape {
   static constexpr int KS = QK + PAD;  // row stride of key-contiguous buffers (scores)
   static constexpr int VS = PB + PAD;  // row stride of value buffers
   static constexpr int BROWS = (QT + TEH) * R;
-  static constexpr int NTH = 256;
+  static constexpr int NTH = NTHREADS;
+  static constexpr int NW = NTHREADS / 64;  // waves per workgroup
   static constexpr int NVEC_N = N / VEC;
   static constexpr int NVEC_P = PB / VEC;
   static constexpr int C_VECS = QO * NVEC_N;
@@ -56,15 +57,16 @@ struct FwdShape {
   static constexpr int X_PER = (X_VECS + NTH - 1) / NTH;
   static constexpr int TQ = QO / 16, TK = QK / 16, TP = PB / 16, TN = N / 16;
   static constexpr int ST_TILES = TN * TP;
-  static constexpr int ST_PER_WAVE = (ST_TILES + 3) / 4;
+  static constexpr int ST_PER_WAVE = (ST_TILES + NW - 1) / NW;
   static_assert(QO % 16 == 0 && QK % 32 == 0, "chunk rows must fill MFMA tiles");
   static_assert(N % 16 == 0 && PB % 16 == 0 && QT <= 64, "unsupported tile shape");
   static_assert(KR == R || KR == 2 * R, "keys per token are R or 2R");
 };
 
-template <bool BF16, int N, int PB, int R, int KR, int QT, bool COORD>
-__global__ __launch_bounds__(256) void ssm_fwd_kernel(FwdParams p) {
-  using S = FwdShape<BF16, N, PB, R, KR, QT, COORD>;
+template <bool BF16, int N, int PB, int R, int KR, int QT, bool COORD, int NTHREADS>
+__global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
+  using S = FwdShape<BF16, N, PB, R, KR, QT, COORD, NTHREADS>;
+  constexpr int NW = S::NW;
   using T = typename S::T;
   constexpr int NS = S::NS, KS = S::KS, VS = S::VS, VEC = S::VEC;
 
@@ -335,7 +337,7 @@ __global__ __launch_bounds__(256) void ssm_fwd_kernel(FwdParams p) {
     __syncthreads();
 
     // ---- a3: masked intra-chunk scores
-    for (int tile = wave; tile < S::TQ * S::TK; tile += 4) {
+    for (int tile = wave; tile < S::TQ * S::TK; tile += NW) {
       const int ti = tile / S::TK, tj = tile % S::TK;
       const int tmax = (16 * ti + 15) / R;
       const int smin = (16 * tj) / KR;
@@ -365,7 +367,7 @@ __global__ __launch_bounds__(256) void ssm_fwd_kernel(FwdParams p) {
     __syncthreads();
 
     // ---- a6: readout of the incoming state + intra-chunk output + feedthrough
-    for (int tile = wave; tile < S::TQ * S::TP; tile += 4) {
+    for (int tile = wave; tile < S::TQ * S::TP; tile += NW) {
       const int ti = tile / S::TP, tp = tile % S::TP;
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
       const T* qsrc = COORD ? sQe : sQ;
@@ -401,7 +403,7 @@ __global__ __launch_bounds__(256) void ssm_fwd_kernel(FwdParams p) {
     // ---- a4/a5: chunk state and state passing (registers)
 #pragma unroll
     for (int k = 0; k < S::ST_PER_WAVE; ++k) {
-      const int tile = wave + 4 * k;
+      const int tile = wave + NW * k;
       if (tile < S::ST_TILES) {
         const int tn = tile / S::TP, tp = tile % S::TP;
         f32x4 acc = st[k];
@@ -436,7 +438,7 @@ __global__ __launch_bounds__(256) void ssm_fwd_kernel(FwdParams p) {
     __syncthreads();
 #pragma unroll
     for (int k = 0; k < S::ST_PER_WAVE; ++k) {
-      const int tile = wave + 4 * k;
+      const int tile = wave + NW * k;
       if (tile < S::ST_TILES) {
         const int tn = tile / S::TP, tp = tile % S::TP;
         const int pl = 16 * tp + (lane & 15);
@@ -452,56 +454,79 @@ __global__ __launch_bounds__(256) void ssm_fwd_kernel(FwdParams p) {
 }
 
 // ------------------------------------------------------------------ dispatch
+// (io bf16?, N, P-block, R, keys per token, tokens per chunk, per-row decay, threads)
 #define SSM_FWD_VARIANTS(X)                 \
   /* fp32 io */                             \
-  X(false, 16, 16, 1, 1, 64, false)         \
-  X(false, 32, 16, 1, 1, 64, false)         \
-  X(false, 32, 16, 2, 2, 32, false)         \
-  X(false, 16, 16, 1, 2, 16, true)          \
-  X(false, 32, 16, 1, 2, 16, true)          \
-  X(false, 32, 16, 2, 4, 16, true)          \
-  X(false, 32, 16, 1, 1, 32, true)          \
-  X(false, 32, 16, 2, 2, 16, true)          \
+  X(false, 16, 16, 1, 1, 64, false, 256)         \
+  X(false, 32, 16, 1, 1, 64, false, 256)         \
+  X(false, 32, 16, 2, 2, 32, false, 256)         \
+  X(false, 16, 16, 1, 2, 16, true, 256)          \
+  X(false, 32, 16, 1, 2, 16, true, 256)          \
+  X(false, 32, 16, 2, 4, 16, true, 256)          \
+  X(false, 32, 16, 1, 1, 32, true, 256)          \
+  X(false, 32, 16, 2, 2, 16, true, 256)          \
   /* bf16 io, head decay */                 \
-  X(true, 32, 16, 1, 1, 64, false)          \
-  X(true, 64, 16, 1, 1, 64, false)          \
-  X(true, 64, 16, 1, 1, 32, false)          \
-  X(true, 128, 16, 1, 1, 64, false)         \
-  X(true, 128, 32, 1, 1, 64, false)         \
-  X(true, 128, 64, 1, 1, 64, false)         \
-  X(true, 64, 16, 2, 2, 32, false)          \
-  X(true, 64, 16, 4, 4, 16, false)          \
-  X(true, 64, 32, 4, 4, 16, false)          \
-  X(true, 64, 16, 4, 4, 8, false)           \
+  X(true, 32, 16, 1, 1, 64, false, 256)          \
+  X(true, 64, 16, 1, 1, 64, false, 256)          \
+  X(true, 64, 16, 1, 1, 32, false, 256)          \
+  X(true, 128, 16, 1, 1, 64, false, 256)         \
+  X(true, 128, 32, 1, 1, 64, false, 256)         \
+  X(true, 128, 64, 1, 1, 64, false, 256)         \
+  X(true, 128, 16, 1, 1, 64, false, 512)    \
+  X(true, 128, 32, 1, 1, 64, false, 512)    \
+  X(true, 128, 64, 1, 1, 64, false, 512)    \
+  X(true, 128, 64, 1, 1, 64, false, 1024)   \
+  X(true, 128, 32, 1, 1, 64, false, 1024)   \
+  X(true, 64, 16, 2, 2, 32, false, 256)          \
+  X(true, 64, 16, 4, 4, 16, false, 256)          \
+  X(true, 64, 32, 4, 4, 16, false, 256)          \
+  X(true, 64, 16, 4, 4, 8, false, 256)           \
   /* bf16 io, per-row decay / pairs / two-endpoint */ \
-  X(true, 32, 16, 1, 2, 16, true)           \
-  X(true, 64, 16, 1, 2, 16, true)           \
-  X(true, 64, 16, 2, 4, 16, true)           \
-  X(true, 64, 16, 2, 4, 8, true)            \
-  X(true, 64, 32, 2, 4, 16, true)           \
-  X(true, 64, 16, 1, 1, 32, true)           \
-  X(true, 64, 16, 2, 2, 16, true)           \
-  X(true, 64, 16, 4, 4, 16, true)           \
-  X(true, 64, 16, 4, 8, 8, true)
+  X(true, 32, 16, 1, 2, 16, true, 256)           \
+  X(true, 64, 16, 1, 2, 16, true, 256)           \
+  X(true, 64, 16, 2, 4, 16, true, 256)           \
+  X(true, 64, 16, 2, 4, 8, true, 256)            \
+  X(true, 64, 32, 2, 4, 16, true, 256)           \
+  X(true, 64, 16, 1, 1, 32, true, 256)           \
+  X(true, 64, 16, 2, 2, 16, true, 256)           \
+  X(true, 64, 16, 4, 4, 16, true, 256)           \
+  X(true, 64, 16, 4, 8, 8, true, 256)      \
+  X(true, 64, 64, 1, 1, 64, false, 1024)   \
+  X(true, 64, 64, 4, 4, 16, false, 1024)   \
+  X(true, 64, 32, 4, 4, 16, false, 1024)   \
+  X(true, 64, 16, 4, 4, 16, false, 1024)   \
+  X(true, 64, 64, 2, 4, 16, true, 1024)    \
+  X(true, 64, 32, 2, 4, 16, true, 1024)    \
+  X(true, 64, 16, 2, 4, 16, true, 1024)    \
+  X(true, 64, 16, 2, 4, 16, true, 512)     \
+  X(true, 64, 64, 1, 2, 16, true, 1024)    \
+  X(true, 64, 32, 1, 2, 16, true, 1024)    \
+  X(true, 64, 16, 1, 2, 16, true, 1024)
 
 bool fwd_variant_exists(const FwdKey& k) {
-#define SSM_FWD_MATCH(BF, NN, PBB, RR, KRR, QTT, CO)                                         \
+#define SSM_FWD_MATCH(BF, NN, PBB, RR, KRR, QTT, CO, NT)                                     \
   if (k.bf16 == BF && k.N == NN && k.PB == PBB && k.R == RR && k.KR == KRR && k.QT == QTT && \
-      k.coord == CO)                                                                         \
+      k.coord == CO && k.nthreads == NT)                                                     \
     return true;
   SSM_FWD_VARIANTS(SSM_FWD_MATCH)
 #undef SSM_FWD_MATCH
   return false;
 }
 
-hipError_t launch_fwd(const FwdKey& k, const FwdParams& p, hipStream_t stream) {
+hipError_t launch_fwd(const FwdKey& k, const FwdParams& p, hipStream_t stream,
+                      void* const* events) {
   const int nwg = p.batch * p.H * p.npblk;
   if (nwg == 0 || p.nchunks == 0) return hipSuccess;
-#define SSM_FWD_LAUNCH(BF, NN, PBB, RR, KRR, QTT, CO)                                        \
+  auto mark = [&](int i) {
+    if (events && events[i]) hipEventRecord(static_cast<hipEvent_t>(events[i]), stream);
+  };
+#define SSM_FWD_LAUNCH(BF, NN, PBB, RR, KRR, QTT, CO, NT)                                    \
   if (k.bf16 == BF && k.N == NN && k.PB == PBB && k.R == RR && k.KR == KRR && k.QT == QTT && \
-      k.coord == CO) {                                                                       \
-    hipLaunchKernelGGL((ssm_fwd_kernel<BF, NN, PBB, RR, KRR, QTT, CO>), dim3(nwg), dim3(256), \
-                       0, stream, p);                                                        \
+      k.coord == CO && k.nthreads == NT) {                                                   \
+    mark(0);                                                                                 \
+    hipLaunchKernelGGL((ssm_fwd_kernel<BF, NN, PBB, RR, KRR, QTT, CO, NT>), dim3(nwg),        \
+                       dim3(NT), 0, stream, p);                                              \
+    mark(1);                                                                                 \
     return hipGetLastError();                                                                \
   }
   SSM_FWD_VARIANTS(SSM_FWD_LAUNCH)

@@ -57,10 +57,12 @@ struct FwdKey {
   bool bf16;
   int N, PB, R, KR, QT;
   bool coord;
+  int nthreads;
 };
 
 // Returns hipSuccess, or hipErrorInvalidValue when no variant matches.
-hipError_t launch_fwd(const FwdKey& key, const FwdParams& p, hipStream_t stream);
+hipError_t launch_fwd(const FwdKey& key, const FwdParams& p, hipStream_t stream,
+                      void* const* events);
 bool fwd_variant_exists(const FwdKey& key);
 
 struct BwdKey {
@@ -68,7 +70,8 @@ struct BwdKey {
   int N, P, R, KR, QT;
   bool coord;
 };
-hipError_t launch_bwd(const BwdKey& key, const BwdParams& p, hipStream_t stream);
+hipError_t launch_bwd(const BwdKey& key, const BwdParams& p, hipStream_t stream,
+                      void* const* events);
 bool bwd_variant_exists(const BwdKey& key);
 
 }  // namespace ssm
