@@ -50,6 +50,10 @@ int make_plan(const ssm_desc* d, Plan* pl) {
   if (d->rank_out != d->rank_in) return SSM_ERR_UNSUPPORTED;
   if (d->headdim % 16) return SSM_ERR_UNSUPPORTED;
   if (d->n_pairs > 0 && (d->n_real % 2)) return SSM_ERR_UNSUPPORTED;
+  // kernels index inside a tensor with 32-bit offsets
+  const double elems = (double)d->batch * d->seqlen * d->nheads * d->rank_in *
+                       (d->headdim > d->dstate ? d->headdim : d->dstate);
+  if (elems >= 2147483648.0) return SSM_ERR_UNSUPPORTED;
   const bool te = (d->flags & SSM_F_TWO_ENDPOINT) != 0;
   pl->bf16 = d->io_dtype == SSM_BF16;
   pl->coord_kernel = d->decay_mode == SSM_DECAY_COORD || te || d->n_pairs > 0;

@@ -35,12 +35,17 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t v) {
   return __uint_as_float(static_cast<uint32_t>(v) << 16);
 }
 
-// round to nearest even; NaN stays NaN
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// round to nearest even (gfx950 v_cvt_pk_bf16_f32); NaN stays NaN
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return static_cast<uint16_t>(u >> 16);
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
+}
+
+// two floats -> packed bf16 pair (low half = a)
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  const bf16x2 v = {static_cast<__bf16>(a), static_cast<__bf16>(b)};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 __device__ __forceinline__ float to_f32(uint16_t v) { return bf16_to_f32(v); }
@@ -49,11 +54,6 @@ __device__ __forceinline__ float to_f32(float v) { return v; }
 template <typename T> __device__ __forceinline__ T from_f32(float f);
 template <> __device__ __forceinline__ uint16_t from_f32<uint16_t>(float f) { return f32_to_bf16(f); }
 template <> __device__ __forceinline__ float from_f32<float>(float f) { return f; }
-
-// 16-byte vector of elements in registers
-struct Vec16 {
-  uint4 raw;
-};
 
 template <bool BF16>
 __device__ __forceinline__ void unpack(const uint4& r, float* v) {
@@ -76,12 +76,10 @@ template <bool BF16>
 __device__ __forceinline__ uint4 pack(const float* v) {
   uint4 r;
   if constexpr (BF16) {
-    uint32_t w[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      w[i] = static_cast<uint32_t>(f32_to_bf16(v[2 * i])) |
-             (static_cast<uint32_t>(f32_to_bf16(v[2 * i + 1])) << 16);
-    r.x = w[0]; r.y = w[1]; r.z = w[2]; r.w = w[3];
+    r.x = pack_bf16x2(v[0], v[1]);
+    r.y = pack_bf16x2(v[2], v[3]);
+    r.z = pack_bf16x2(v[4], v[5]);
+    r.w = pack_bf16x2(v[6], v[7]);
   } else {
     r.x = __float_as_uint(v[0]);
     r.y = __float_as_uint(v[1]);

@@ -66,21 +66,22 @@ struct FwdShape {
 template <bool BF16, int N, int PB, int R, int KR, int QT, bool COORD, int NTHREADS>
 __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
   using S = FwdShape<BF16, N, PB, R, KR, QT, COORD, NTHREADS>;
-  constexpr int NW = S::NW;
   using T = typename S::T;
+  constexpr int NW = S::NW;
   constexpr int NS = S::NS, KS = S::KS, VS = S::VS, VEC = S::VEC;
+  constexpr int QSZ = S::QO * NS, KSZ = S::QK * NS, VSZ = S::QK * S::VS;
 
-  __shared__ __align__(16) T sQ[S::QO * NS];
-  __shared__ __align__(16) T sQe[COORD ? S::QO * NS : 8];
-  __shared__ __align__(16) T sK[S::QK * NS];
-  __shared__ __align__(16) T sKe[COORD ? S::QK * NS : 8];  // keys scaled to the chunk end
-  __shared__ __align__(16) T sV[S::QK * S::VS];            // values, natural [key row][p]
-  __shared__ __align__(16) T sVw[COORD ? 8 : S::QK * S::VS];  // values scaled to the chunk end
-  __shared__ __align__(16) T sS[S::QO * KS];
-  __shared__ __align__(16) T sST[PB * NS];
-  __shared__ float sCD[64], sEL[64];
+  // double-buffered chunk operands: chunk c is consumed while chunk c+1 is staged
+  __shared__ __align__(16) T sQ[2 * QSZ];                     // queries (folded; per-row: scaled)
+  __shared__ __align__(16) T sQe[COORD ? 2 * QSZ : 8];        // per-row: queries scaled by e^{L_t}
+  __shared__ __align__(16) T sK[2 * KSZ];                     // keys
+  __shared__ __align__(16) T sKe[COORD ? 2 * KSZ : 8];        // per-row: keys scaled to the chunk end
+  __shared__ __align__(16) T sV[2 * VSZ];                     // values, natural [key row][p]
+  __shared__ __align__(16) T sVw[COORD ? 8 : 2 * VSZ];        // head: values scaled to the chunk end
+  __shared__ __align__(16) T sS[S::QO * KS];                  // masked scores of the current chunk
+  __shared__ __align__(16) T sST[PB * NS];                    // state entering the current chunk (bf16)
+  __shared__ float sCD[2][64], sEL[2][64], sMisc[2][4];
   __shared__ float sRate[N], sOmega[N / 2 + 1];
-  __shared__ float sMisc[4];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int lid = xcd_logical_id(blockIdx.x, gridDim.x);
@@ -102,15 +103,15 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
     }
     for (int k = tid; k < p.n_pairs; k += S::NTH) sOmega[k] = p.omega[(size_t)h * p.n_pairs + k];
   }
-  // zero the state copy and the contraction padding columns
+  // zero the state copy and the contraction padding columns of both buffers
   for (int i = tid; i < PB * NS; i += S::NTH) sST[i] = T(0);
   if (S::NC > N) {
-    for (int i = tid; i < S::QO * (S::NC - N); i += S::NTH) {
+    for (int i = tid; i < 2 * S::QO * (S::NC - N); i += S::NTH) {
       const int r = i / (S::NC - N), c = N + i % (S::NC - N);
       sQ[r * NS + c] = T(0);
       if (COORD) sQe[r * NS + c] = T(0);
     }
-    for (int i = tid; i < S::QK * (S::NC - N); i += S::NTH) {
+    for (int i = tid; i < 2 * S::QK * (S::NC - N); i += S::NTH) {
       const int r = i / (S::NC - N), c = N + i % (S::NC - N);
       sK[r * NS + c] = T(0);
     }
@@ -118,10 +119,16 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
   const float Ah = COORD ? 0.f : p.A[h];
   const float Dh = p.has_D ? p.D[h] : 0.f;
 
-  const T* xg = static_cast<const T*>(p.x);
-  const T* Bg = static_cast<const T*>(p.B);
-  const T* Cg = static_cast<const T*>(p.C);
-  T* yg = static_cast<T*>(p.y);
+  // slice bases (64-bit once); offsets inside a slice fit in 32 bits (the host
+  // rejects tensors of 2^31 or more elements)
+  const T* xg = static_cast<const T*>(p.x) + ((size_t)b * L * H + h) * R * P + p0;
+  const T* Bg = static_cast<const T*>(p.B) + ((size_t)b * L * G + g) * R * N;
+  const T* Cg = static_cast<const T*>(p.C) + ((size_t)b * L * G + g) * R * N;
+  T* yg = static_cast<T*>(p.y) + ((size_t)b * L * H + h) * R * P + p0;
+  const float* dtg = p.dt + (size_t)b * L * H + h;
+  const float* beg = S::TE ? p.beta + (size_t)b * L * H + h : nullptr;
+  const float* gag = S::TE ? p.gamma + (size_t)b * L * H + h : nullptr;
+  const int tsG = G * R * N, tsH = H * R * P;  // per-token strides
 
   f32x4 st[S::ST_PER_WAVE];
 #pragma unroll
@@ -140,9 +147,7 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
       if (v < S::C_VECS) {
         const int row = v / S::NVEC_N, nv = v % S::NVEC_N;
         const int t = t0 + row / R, o = row % R;
-        if (t < L)
-          val = *reinterpret_cast<const uint4*>(
-              Cg + ((((size_t)b * L + t) * G + g) * R + o) * N + nv * VEC);
+        if (t < L) val = *reinterpret_cast<const uint4*>(Cg + t * tsG + o * N + nv * VEC);
       }
       rc[k] = val;
     }
@@ -153,9 +158,7 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
       if (v < S::B_VECS) {
         const int row = v / S::NVEC_N, nv = v % S::NVEC_N;
         const int t = t0 + row / R - S::TEH, r = row % R;
-        if (t >= 0 && t < L)
-          val = *reinterpret_cast<const uint4*>(
-              Bg + ((((size_t)b * L + t) * G + g) * R + r) * N + nv * VEC);
+        if (t >= 0 && t < L) val = *reinterpret_cast<const uint4*>(Bg + t * tsG + r * N + nv * VEC);
       }
       rb[k] = val;
     }
@@ -166,20 +169,17 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
       if (v < S::X_VECS) {
         const int row = v / S::NVEC_P, pv = v % S::NVEC_P;
         const int t = t0 + row / R - S::TEH, r = row % R;
-        if (t >= 0 && t < L)
-          val = *reinterpret_cast<const uint4*>(
-              xg + ((((size_t)b * L + t) * H + h) * R + r) * P + p0 + pv * VEC);
+        if (t >= 0 && t < L) val = *reinterpret_cast<const uint4*>(xg + t * tsH + r * P + pv * VEC);
       }
       rx[k] = val;
     }
     {
       const int t = t0 + lane;
       const bool ok = lane < QT && t < L;
-      const size_t idx = ((size_t)b * L + t) * H + h;
-      rdt = ok ? p.dt[idx] : 0.f;
+      rdt = ok ? dtg[t * H] : 0.f;
       if (S::TE) {
-        rbe = ok ? p.beta[idx] : 0.f;
-        rga = ok ? p.gamma[idx] : 0.f;
+        rbe = ok ? beg[t * H] : 0.f;
+        rga = ok ? gag[t * H] : 0.f;
       }
     }
   };
@@ -200,22 +200,10 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
     }
   };
 
-  const int nch = p.nchunks;
-  const size_t sl_saved = (size_t)slice * (nch + 1);
-  if (p.saved) {
-    // slot 0: the zero initial state
-    for (int i = tid; i < N * PB; i += S::NTH) {
-      const int n = i / PB, pl = i % PB;
-      p.saved[(sl_saved * N + n) * P + p0 + pl] = 0.f;
-    }
-  }
-
-  load_chunk(0);
-  for (int c = 0; c < nch; ++c) {
+  // ---- a1 + a2: prefix of the step (every wave, lane = token) and the operands of
+  // the chunk held in registers, written into buffer `bi`
+  auto stage = [&](int c, int bi) {
     const int t0 = c * QT;
-    __syncthreads();
-    // ---- a1: chunk-local cumulative step (wave prefix sum; every wave holds it,
-    // lane = token, so the operand prologue needs no extra barrier)
     float dl = 0.f;
     if (lane < QT && t0 + lane < L) dl = p.softplus ? softplus_f32(rdt) : rdt;
     const float cd_l = wave_prefix_sum(dl);
@@ -224,13 +212,20 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
     const float be_l = rbe, ga_l = rga;
     if (wave == 0) {
       if (lane < QT) {
-        sCD[lane] = cd_l;
-        if (!COORD) sEL[lane] = __expf(-Ah * cd_l);
+        sCD[bi][lane] = cd_l;
+        if (!COORD) sEL[bi][lane] = __expf(-Ah * cd_l);
       }
-      if (lane == 0) sMisc[1] = COORD ? 0.f : __expf(-Ah * cdend);
+      if (lane == 0) {
+        sMisc[bi][0] = cdend;
+        sMisc[bi][1] = COORD ? 0.f : __expf(-Ah * cdend);
+      }
     }
-
-    // ---- a2: operands (queries, keys, values) into LDS
+    T* q = sQ + bi * QSZ;
+    T* qe = sQe + (COORD ? bi * QSZ : 0);
+    T* kb = sK + bi * KSZ;
+    T* keb = sKe + (COORD ? bi * KSZ : 0);
+    T* vb = sV + bi * VSZ;
+    T* vwb = sVw + (COORD ? 0 : bi * VSZ);
 #pragma unroll
     for (int k = 0; k < S::C_PER; ++k) {
       const int v = tid + S::NTH * k;
@@ -240,20 +235,19 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
         const int row = v / S::NVEC_N, nv = v % S::NVEC_N;
         const int n0 = nv * VEC;
         if (COORD) {
-          float vals[VEC], q[VEC], qe[VEC];
+          float vals[VEC], qq[VEC], qqe[VEC];
           unpack<BF16>(rc[k], vals);
-          const float cd = cd_c;
-          unrotate(vals, n0, cd);
+          unrotate(vals, n0, cd_c);
 #pragma unroll
           for (int i = 0; i < VEC; ++i) {
             const float ar = sRate[n0 + i];
-            q[i] = vals[i] * __expf(-ar * (cd - 0.5f * cdend));
-            qe[i] = vals[i] * __expf(-ar * cd);
+            qq[i] = vals[i] * __expf(-ar * (cd_c - 0.5f * cdend));
+            qqe[i] = vals[i] * __expf(-ar * cd_c);
           }
-          *reinterpret_cast<uint4*>(sQ + row * NS + n0) = pack<BF16>(q);
-          *reinterpret_cast<uint4*>(sQe + row * NS + n0) = pack<BF16>(qe);
+          *reinterpret_cast<uint4*>(q + row * NS + n0) = pack<BF16>(qq);
+          *reinterpret_cast<uint4*>(qe + row * NS + n0) = pack<BF16>(qqe);
         } else {
-          *reinterpret_cast<uint4*>(sQ + row * NS + n0) = rc[k];
+          *reinterpret_cast<uint4*>(q + row * NS + n0) = rc[k];
         }
       }
     }
@@ -279,28 +273,23 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
           const int tau = sl + e;
           if (tau < 0 || tau >= QT || (e == 0 && sl < 0)) continue;
           const int j = tau * KR + (e ? R : 0) + r;
-          const float w = gbt[e];
           float u[VEC], kk[VEC], ke[VEC];
 #pragma unroll
-          for (int i = 0; i < VEC; ++i) u[i] = vals[i] * w;
+          for (int i = 0; i < VEC; ++i) u[i] = vals[i] * gbt[e];
           if (COORD) {
-            const float cd = cdt[e];
-            unrotate(u, n0, cd);
+            unrotate(u, n0, cdt[e]);
 #pragma unroll
             for (int i = 0; i < VEC; ++i) {
               const float ar = sRate[n0 + i];
-              kk[i] = u[i] * __expf(-ar * (0.5f * cdend - cd));
-              ke[i] = u[i] * __expf(-ar * (cdend - cd));
+              kk[i] = u[i] * __expf(-ar * (0.5f * cdend - cdt[e]));
+              ke[i] = u[i] * __expf(-ar * (cdend - cdt[e]));
             }
+            *reinterpret_cast<uint4*>(keb + j * NS + n0) = pack<BF16>(ke);
           } else {
 #pragma unroll
-            for (int i = 0; i < VEC; ++i) {
-              kk[i] = u[i];
-              ke[i] = 0.f;
-            }
+            for (int i = 0; i < VEC; ++i) kk[i] = u[i];
           }
-          *reinterpret_cast<uint4*>(sK + j * NS + n0) = pack<BF16>(kk);
-          if (COORD) *reinterpret_cast<uint4*>(sKe + j * NS + n0) = pack<BF16>(ke);
+          *reinterpret_cast<uint4*>(kb + j * NS + n0) = pack<BF16>(kk);
         }
       }
     }
@@ -321,22 +310,45 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
           const int tau = sl + e;
           if (tau < 0 || tau >= QT || (e == 0 && sl < 0)) continue;
           const int j = tau * KR + (e ? R : 0) + r;
-          *reinterpret_cast<uint4*>(sV + j * VS + pv * VEC) = rx[k];
+          *reinterpret_cast<uint4*>(vb + j * VS + pv * VEC) = rx[k];
           if (!COORD) {
             float xv[VEC];
             unpack<BF16>(rx[k], xv);
-            const float ws = xw[e];
 #pragma unroll
-            for (int i = 0; i < VEC; ++i) xv[i] *= ws;
-            *reinterpret_cast<uint4*>(sVw + j * VS + pv * VEC) = pack<BF16>(xv);
+            for (int i = 0; i < VEC; ++i) xv[i] *= xw[e];
+            *reinterpret_cast<uint4*>(vwb + j * VS + pv * VEC) = pack<BF16>(xv);
           }
         }
       }
     }
-    if (c + 1 < nch) load_chunk(c + 1);
-    __syncthreads();
+  };
 
-    // ---- a3: masked intra-chunk scores
+  const int nch = p.nchunks;
+  const size_t sl_saved = (size_t)slice * (nch + 1);
+  if (p.saved) {
+    // slot 0: the zero initial state
+    for (int i = tid; i < N * PB; i += S::NTH) {
+      const int n = i / PB, pl = i % PB;
+      p.saved[(sl_saved * N + n) * P + p0 + pl] = 0.f;
+    }
+  }
+
+  load_chunk(0);
+  stage(0, 0);
+  if (nch > 1) load_chunk(1);
+  __syncthreads();
+
+  for (int c = 0; c < nch; ++c) {
+    const int t0 = c * QT;
+    const int bi = c & 1;
+    const T* q = sQ + bi * QSZ;
+    const T* qe = sQe + (COORD ? bi * QSZ : 0);
+    const T* kb = sK + bi * KSZ;
+    const T* keb = sKe + (COORD ? bi * KSZ : 0);
+    const T* vb = sV + bi * VSZ;
+    const T* vwb = sVw + (COORD ? 0 : bi * VSZ);
+
+    // ---- phase 1 -- a3: masked intra-chunk scores of chunk c
     for (int tile = wave; tile < S::TQ * S::TK; tile += NW) {
       const int ti = tile / S::TK, tj = tile % S::TK;
       const int tmax = (16 * ti + 15) / R;
@@ -345,8 +357,8 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
       if (smin <= tmax) {
 #pragma unroll
         for (int kk = 0; kk < S::NC / 32; ++kk) {
-          const auto a = load_frag<BF16>(sQ + (16 * ti + (lane & 15)) * NS + kk * 32 + 8 * (lane >> 4));
-          const auto bq = load_frag<BF16>(sK + (16 * tj + (lane & 15)) * NS + kk * 32 + 8 * (lane >> 4));
+          const auto a = load_frag<BF16>(q + (16 * ti + (lane & 15)) * NS + kk * 32 + 8 * (lane >> 4));
+          const auto bq = load_frag<BF16>(kb + (16 * tj + (lane & 15)) * NS + kk * 32 + 8 * (lane >> 4));
           mma<BF16>(acc, a, bq);
         }
       }
@@ -359,18 +371,19 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
         float val = 0.f;
         if (s <= t) {
           val = acc[i];
-          if (!COORD) val *= __expf(-Ah * (sCD[t] - sCD[s]));
+          if (!COORD) val *= __expf(-Ah * (sCD[bi][t] - sCD[bi][s]));
         }
         sS[row * KS + col] = from_f32<T>(val);
       }
     }
     __syncthreads();
 
-    // ---- a6: readout of the incoming state + intra-chunk output + feedthrough
+    // ---- phase 2 -- a6 readout + output of chunk c, a4/a5 state update of chunk c,
+    // a1/a2 staging of chunk c+1 (other buffer), loads of chunk c+2
     for (int tile = wave; tile < S::TQ * S::TP; tile += NW) {
       const int ti = tile / S::TP, tp = tile % S::TP;
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      const T* qsrc = COORD ? sQe : sQ;
+      const T* qsrc = COORD ? qe : q;
 #pragma unroll
       for (int kk = 0; kk < S::NC / 32; ++kk) {
         const auto a = load_frag<BF16>(qsrc + (16 * ti + (lane & 15)) * NS + kk * 32 + 8 * (lane >> 4));
@@ -379,13 +392,13 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
       }
       if (!COORD) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc[i] *= sEL[(16 * ti + 4 * (lane >> 4) + i) / R];
+        for (int i = 0; i < 4; ++i) acc[i] *= sEL[bi][(16 * ti + 4 * (lane >> 4) + i) / R];
       }
       const int tmax = (16 * ti + 15) / R;
       const int kend = ((tmax + 1) * KR + 31) / 32;
       for (int kk = 0; kk < kend; ++kk) {
         const auto a = load_frag<BF16>(sS + (16 * ti + (lane & 15)) * KS + kk * 32 + 8 * (lane >> 4));
-        const auto bv = load_frag_tr<BF16>(sV + (kk * 32) * VS + 16 * tp, VS);
+        const auto bv = load_frag_tr<BF16>(vb + (kk * 32) * VS + 16 * tp, VS);
         mma<BF16>(acc, a, bv);
       }
       const int pl = 16 * tp + (lane & 15);
@@ -395,58 +408,74 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
         const int t = row / R, o = row % R;
         const int tg = t0 + t;
         float val = acc[i];
-        if (p.has_D) val += Dh * to_f32(sV[(t * KR + o) * VS + pl]);
-        if (tg < L) yg[((((size_t)b * L + tg) * H + h) * R + o) * P + p0 + pl] = from_f32<T>(val);
+        if (p.has_D) val += Dh * to_f32(vb[(t * KR + o) * VS + pl]);
+        if (tg < L) yg[tg * tsH + o * P + pl] = from_f32<T>(val);
       }
     }
-
-    // ---- a4/a5: chunk state and state passing (registers)
+    {
+      const float cdend = sMisc[bi][0];
 #pragma unroll
-    for (int k = 0; k < S::ST_PER_WAVE; ++k) {
-      const int tile = wave + NW * k;
-      if (tile < S::ST_TILES) {
-        const int tn = tile / S::TP, tp = tile % S::TP;
-        f32x4 acc = st[k];
+      for (int k = 0; k < S::ST_PER_WAVE; ++k) {
+        const int tile = wave + NW * k;
+        if (tile < S::ST_TILES) {
+          const int tn = tile / S::TP, tp = tile % S::TP;
+          f32x4 acc = st[k];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int n = 16 * tn + 4 * (lane >> 4) + i;
-          acc[i] *= COORD ? __expf(-sRate[n] * cdend) : sMisc[1];
-        }
-#pragma unroll
-        for (int kk = 0; kk < S::QK / 32; ++kk) {
-          const auto a = load_frag_tr<BF16>((COORD ? sKe : sK) + (kk * 32) * NS + 16 * tn, NS);
-          const auto bv = load_frag_tr<BF16>((COORD ? sV : sVw) + (kk * 32) * VS + 16 * tp, VS);
-          mma<BF16>(acc, a, bv);
-        }
-        if (COORD) {
-#pragma unroll
-          for (int i = 0; i < 4; i += 2) {
+          for (int i = 0; i < 4; ++i) {
             const int n = 16 * tn + 4 * (lane >> 4) + i;
-            if (n >= nreal) {
-              const float th = sOmega[(n - nreal) >> 1] * cdend;
-              float sn, cs;
-              sincosf(th, &sn, &cs);
-              const float a0 = acc[i], a1 = acc[i + 1];
-              acc[i] = cs * a0 - sn * a1;
-              acc[i + 1] = sn * a0 + cs * a1;
+            acc[i] *= COORD ? __expf(-sRate[n] * cdend) : sMisc[bi][1];
+          }
+#pragma unroll
+          for (int kk = 0; kk < S::QK / 32; ++kk) {
+            const auto a = load_frag_tr<BF16>((COORD ? keb : kb) + (kk * 32) * NS + 16 * tn, NS);
+            const auto bv = load_frag_tr<BF16>((COORD ? vb : vwb) + (kk * 32) * VS + 16 * tp, VS);
+            mma<BF16>(acc, a, bv);
+          }
+          if (COORD) {
+#pragma unroll
+            for (int i = 0; i < 4; i += 2) {
+              const int n = 16 * tn + 4 * (lane >> 4) + i;
+              if (n >= nreal) {
+                const float th = sOmega[(n - nreal) >> 1] * cdend;
+                float sn, cs;
+                sincosf(th, &sn, &cs);
+                const float a0 = acc[i], a1 = acc[i + 1];
+                acc[i] = cs * a0 - sn * a1;
+                acc[i + 1] = sn * a0 + cs * a1;
+              }
             }
           }
+          st[k] = acc;
         }
-        st[k] = acc;
       }
     }
+    if (c + 1 < nch) {
+      stage(c + 1, bi ^ 1);
+      if (c + 2 < nch) load_chunk(c + 2);
+    }
     __syncthreads();
+
+    // ---- phase 3 -- the new state becomes the readout operand of chunk c+1
 #pragma unroll
     for (int k = 0; k < S::ST_PER_WAVE; ++k) {
       const int tile = wave + NW * k;
       if (tile < S::ST_TILES) {
         const int tn = tile / S::TP, tp = tile % S::TP;
         const int pl = 16 * tp + (lane & 15);
+        const int n0 = 16 * tn + 4 * (lane >> 4);
+        if constexpr (BF16) {
+          uint2 w;
+          w.x = pack_bf16x2(st[k][0], st[k][1]);
+          w.y = pack_bf16x2(st[k][2], st[k][3]);
+          *reinterpret_cast<uint2*>(sST + pl * NS + n0) = w;
+        } else {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int n = 16 * tn + 4 * (lane >> 4) + i;
-          sST[pl * NS + n] = from_f32<T>(st[k][i]);
-          if (p.saved) p.saved[((sl_saved + c + 1) * N + n) * P + p0 + pl] = st[k][i];
+          for (int i = 0; i < 4; ++i) sST[pl * NS + n0 + i] = from_f32<T>(st[k][i]);
+        }
+        if (p.saved) {
+          float* dst = p.saved + ((sl_saved + c + 1) * N + n0) * P + p0 + pl;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) dst[i * P] = st[k][i];
         }
       }
     }
