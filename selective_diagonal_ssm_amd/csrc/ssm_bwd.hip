@@ -129,7 +129,7 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_adjoint(BwdParams p) {
             const int n = 16 * tnn + 4 * (lane >> 4) + i;
             if (n >= nreal) {
               float sn, cs;
-              sincosf(sOmega[(n - nreal) >> 1] * cdx_end, &sn, &cs);
+              fast_sincos(sOmega[(n - nreal) >> 1] * cdx_end, &sn, &cs);
               const float a0 = st[k][i], a1 = st[k][i + 1];
               st[k][i] = cs * a0 + sn * a1;  // R(-theta)
               st[k][i + 1] = -sn * a0 + cs * a1;
@@ -158,7 +158,7 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_adjoint(BwdParams p) {
             const int n = n0 + i;
             if (n >= nreal) {
               float sn, cs;
-              sincosf(sOmega[(n - nreal) >> 1] * cdr, &sn, &cs);
+              fast_sincos(sOmega[(n - nreal) >> 1] * cdr, &sn, &cs);
               const float a = vals[i], bb = vals[i + 1];
               vals[i] = cs * a + sn * bb;
               vals[i + 1] = -sn * a + cs * bb;
@@ -394,7 +394,7 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
         const int n = n0 + i;
         if (n >= nreal) {
           float sn, cs;
-          sincosf(sOmega[(n - nreal) >> 1] * cd, &sn, &cs);
+          fast_sincos(sOmega[(n - nreal) >> 1] * cd, &sn, &cs);
           const float a = vals[i], bb = vals[i + 1];
           vals[i] = cs * a + sn * bb;
           vals[i + 1] = -sn * a + cs * bb;
@@ -435,7 +435,7 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
           const int n = n0 + i;
           if (n >= nreal) {
             float sn, cs;
-            sincosf(sOmega[(n - nreal) >> 1] * cdv[e], &sn, &cs);
+            fast_sincos(sOmega[(n - nreal) >> 1] * cdv[e], &sn, &cs);
             const float a = u[i], bb = u[i + 1];
             u[i] = cs * a + sn * bb;
             u[i + 1] = -sn * a + cs * bb;
@@ -511,7 +511,7 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
       const bool pair = COORD && n >= nreal;
       if (pair) {
         float sn, cs;
-        sincosf(sOmega[(n - nreal) >> 1] * (cdend + dnext), &sn, &cs);
+        fast_sincos(sOmega[(n - nreal) >> 1] * (cdend + dnext), &sn, &cs);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const float a0 = ga[i], a1 = gb[i];
@@ -738,7 +738,7 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
           rekt[i >> 1] = -(-kv[i] * er * ae[i + 1] + kv[i + 1] * er * ae[i]);
           // unfold the rotation of the key: u = R(+Theta_s) dK~
           float sn, cs;
-          sincosf(sOmega[kp] * cds, &sn, &cs);
+          fast_sincos(sOmega[kp] * cds, &sn, &cs);
           const float a0 = dk[i], a1 = dk[i + 1];
           dk[i] = cs * a0 - sn * a1;
           dk[i + 1] = sn * a0 + cs * a1;
@@ -878,7 +878,7 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
           tokacc += sOmega[kp] * dth;
           rpw[i >> 1] = cdt * dth;
           float sn, cs;
-          sincosf(sOmega[kp] * cdt, &sn, &cs);
+          fast_sincos(sOmega[kp] * cdt, &sn, &cs);
           const float a0 = dc[i], a1 = dc[i + 1];
           dc[i] = cs * a0 - sn * a1;
           dc[i + 1] = sn * a0 + cs * a1;

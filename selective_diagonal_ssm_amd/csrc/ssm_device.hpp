@@ -191,8 +191,22 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// softplus(v) = log(1 + e^v) with hardware exp/log: log1p(u) is evaluated as
+// log(w) * u / (w - 1), w = 1 + u, which keeps full relative accuracy for tiny u.
 __device__ __forceinline__ float softplus_f32(float v) {
-  return v > 20.f ? v : log1pf(expf(v));
+  if (v > 20.f) return v;
+  const float u = __expf(v);
+  const float w = 1.f + u;
+  return (w == 1.f) ? u : __logf(w) * (u / (w - 1.f));
+}
+
+// sin and cos of an angle in radians: reduce to revolutions in [-1/2, 1/2], then
+// the hardware sin / cos (which take revolutions)
+__device__ __forceinline__ void fast_sincos(float x, float* sn, float* cs) {
+  float r = x * 0.15915494309189535f;  // 1 / (2 pi)
+  r -= rintf(r);
+  *sn = __builtin_amdgcn_sinf(r);
+  *cs = __builtin_amdgcn_cosf(r);
 }
 
 __device__ __forceinline__ float sigmoid_f32(float v) { return 1.f / (1.f + expf(-v)); }

@@ -192,7 +192,7 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
       if (n >= nreal) {
         const float th = sOmega[(n - nreal) >> 1] * cd;
         float sn, cs;
-        sincosf(th, &sn, &cs);
+        fast_sincos(th, &sn, &cs);
         const float a = v[i], bb = v[i + 1];
         v[i] = cs * a + sn * bb;
         v[i + 1] = -sn * a + cs * bb;
@@ -438,7 +438,7 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
               if (n >= nreal) {
                 const float th = sOmega[(n - nreal) >> 1] * cdend;
                 float sn, cs;
-                sincosf(th, &sn, &cs);
+                fast_sincos(th, &sn, &cs);
                 const float a0 = acc[i], a1 = acc[i + 1];
                 acc[i] = cs * a0 - sn * a1;
                 acc[i + 1] = sn * a0 + cs * a1;
