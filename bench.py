@@ -57,16 +57,22 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(kernel: str, workload: str):
-    """HBM bytes per launch from committed rocprofv3 counter summaries, only if
-    they were taken on the current kernel sources."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
+def measured_traffic(kernel: str, workload: str, mode: str):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter summary
+    (FETCH_SIZE and WRITE_SIZE, scaled by a plain copy's reading), only if it was
+    taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", f"hbm_counters_{workload}_{mode}.md")
     if not os.path.exists(path):
         return None
-    rec = json.load(open(path))
+    rec = {}
+    for line in open(path):
+        if ":" in line and line.startswith(("kernel_hash", "traffic_bytes_per_launch")):
+            k, v = line.split(":", 1)
+            rec[k.strip()] = v.strip()
     if rec.get("kernel_hash") != kernel_source_hash():
         return None
-    return rec.get("bytes_per_launch")
+    v = rec.get(f"traffic_bytes_per_launch {kernel}")
+    return int(v) if v else None
 
 
 def cpu_baseline(prob: dict, mode: str, target_s: float = 15.0):
@@ -225,7 +231,7 @@ def main():
     abytes = algorithmic_bytes(d, io_bytes, direction) if kern in ("ssm_fwd_kernel",
                                                                    "ssm_bwd_chunk") else 0
     achieved = abytes / (kms * 1e-3) / 1e9
-    traffic = measured_traffic(kern, args.workload)
+    traffic = measured_traffic(kern, args.workload, args.mode)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                 "kernel": kern, "algorithmic_bytes_per_launch": abytes,

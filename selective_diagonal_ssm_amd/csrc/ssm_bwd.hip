@@ -9,7 +9,8 @@
 //      boundary adjoints Gpre[c] = g_{t0(c)} from
 //        Gpre[c] = sum_{t in c} Phi_{t,t0}^T C_t dy_t + Phi_{t0',t0}^T Gpre[c+1],
 //      Phi_{t,t0} = A_t ... A_{t0+1}; chunk-local folding as in the forward.
-//  ssm_bwd_chunk    (one workgroup per (slice, chunk), fully parallel): dX, dB, dC,
+//  ssm_bwd_chunk    (persistent: each workgroup walks (slice, chunk) items, the
+//      next item's reads in flight while the current one computes): dX, dB, dC,
 //      dDelta, dbeta, dgamma and per-chunk parameter partials from the chunked
 //      adjoint (transposed masked products on MFMA):
 //        dV  = (S o M)^T dY + Ke G~,   dK~ = (Z o M)^T Q + e^{L_end-L_s} (G~ V^T),
@@ -27,6 +28,9 @@
 // Sources: "When a Diagonal State Is Not Enough" (sungsoo.github.io), Part 01 and
 // Part 03 (recurrence, Theorem 24 masked-attention form, Theorem 8 pairs), Part 04
 // (verification compares outputs, input gradients and parameter gradients).
+#include <algorithm>
+#include <atomic>
+
 #include "ssm_device.hpp"
 #include "ssm_kernels.hpp"
 
@@ -93,51 +97,51 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_adjoint(BwdParams p) {
   for (int k = 0; k < S::ST_PER_WAVE; ++k) st[k] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int nch = p.nchunks;
+  // register prefetch of one chunk's C rows, dy rows and steps
+  uint4 pc[S::C_PER], py[S::Y_PER];
+  float pdt = 0.f;
+  auto prefetch = [&](int c) {
+    const int t0 = c * QT;
+#pragma unroll
+    for (int k = 0; k < S::C_PER; ++k) {
+      const int v = tid + S::NTH * k;
+      uint4 raw = make_uint4(0, 0, 0, 0);
+      if (v < S::C_VECS) {
+        const int row = v / (N / VEC), n0 = (v % (N / VEC)) * VEC;
+        const int t = t0 + row / R, o = row % R;
+        if (t < L) raw = *reinterpret_cast<const uint4*>(Cg + ((((size_t)b * L + t) * G + g) * R + o) * N + n0);
+      }
+      pc[k] = raw;
+    }
+#pragma unroll
+    for (int k = 0; k < S::Y_PER; ++k) {
+      const int v = tid + S::NTH * k;
+      uint4 raw = make_uint4(0, 0, 0, 0);
+      if (v < S::Y_VECS) {
+        const int row = v / (PB / VEC), pv = v % (PB / VEC);
+        const int t = t0 + row / R, o = row % R;
+        if (t < L)
+          raw = *reinterpret_cast<const uint4*>(dyg + ((((size_t)b * L + t) * H + h) * R + o) * P + p0 + pv * VEC);
+      }
+      py[k] = raw;
+    }
+    pdt = 0.f;
+    if (lane < QT && t0 + lane < L) pdt = p.dt[((size_t)b * L + t0 + lane) * H + h];
+  };
+
+  float dnext = 0.f;  // step of the first token of the chunk after the current one
+  prefetch(nch - 1);
   for (int c = nch - 1; c >= 0; --c) {
     const int t0 = c * QT;
-    const int tn = t0 + QT;  // first token of the next chunk
-    __syncthreads();
-    // step of this chunk's tokens (lane = token) and of the next chunk's first token
+    __syncthreads();  // the previous chunk's products are done with sQ / sY
+    // step of this chunk's tokens (lane = token)
     float dl = 0.f;
-    if (lane < QT && t0 + lane < L) {
-      const float raw = p.dt[((size_t)b * L + t0 + lane) * H + h];
-      dl = p.softplus ? softplus_f32(raw) : raw;
-    }
-    float dnext = 0.f;
-    if (tn < L) {
-      const float raw = p.dt[((size_t)b * L + tn) * H + h];
-      dnext = p.softplus ? softplus_f32(raw) : raw;
-    }
+    if (lane < QT && t0 + lane < L) dl = p.softplus ? softplus_f32(pdt) : pdt;
     const float cd = wave_prefix_sum(dl);
-    const float cdx = cd - __shfl(dl, 0, kWave);      // sum over (t0, t]
+    const float cdx = cd - __shfl(dl, 0, kWave);               // sum over (t0, t]
     const float cdx_end = __shfl(cdx, QT - 1, kWave) + dnext;  // sum over (t0, t0']
+    dnext = __shfl(dl, 0, kWave);
 
-    // carried adjoint: Gpre[c+1] -> Phi_{t0',t0}^T Gpre[c+1]
-#pragma unroll
-    for (int k = 0; k < S::ST_PER_WAVE; ++k) {
-      const int tile = wave + NW * k;
-      if (tile < S::ST_TILES) {
-        const int tnn = tile / S::TP;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int n = 16 * tnn + 4 * (lane >> 4) + i;
-          st[k][i] *= COORD ? __expf(-sRate[n] * cdx_end) : __expf(-Ah * cdx_end);
-        }
-        if (COORD) {
-#pragma unroll
-          for (int i = 0; i < 4; i += 2) {
-            const int n = 16 * tnn + 4 * (lane >> 4) + i;
-            if (n >= nreal) {
-              float sn, cs;
-              fast_sincos(sOmega[(n - nreal) >> 1] * cdx_end, &sn, &cs);
-              const float a0 = st[k][i], a1 = st[k][i + 1];
-              st[k][i] = cs * a0 + sn * a1;  // R(-theta)
-              st[k][i + 1] = -sn * a0 + cs * a1;
-            }
-          }
-        }
-      }
-    }
     // operands: rows (t, o) of  e^{L'_t} R(-Theta'_t) C_t  and  dy_t
 #pragma unroll
     for (int k = 0; k < S::C_PER; ++k) {
@@ -146,10 +150,7 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_adjoint(BwdParams p) {
       const float cdr = __shfl(cdx, row / R, kWave);
       if (v < S::C_VECS) {
         const int nv = v % (N / VEC), n0 = nv * VEC;
-        const int t = t0 + row / R, o = row % R;
-        uint4 raw = make_uint4(0, 0, 0, 0);
-        if (t < L)
-          raw = *reinterpret_cast<const uint4*>(Cg + ((((size_t)b * L + t) * G + g) * R + o) * N + n0);
+        uint4 raw = pc[k];
         if (COORD) {
           float vals[VEC];
           unpack<BF16>(raw, vals);
@@ -178,10 +179,7 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_adjoint(BwdParams p) {
       const float wr = COORD ? 1.f : __expf(-Ah * __shfl(cdx, row / R, kWave));
       if (v < S::Y_VECS) {
         const int pv = v % (PB / VEC);
-        const int t = t0 + row / R, o = row % R;
-        uint4 raw = make_uint4(0, 0, 0, 0);
-        if (t < L)
-          raw = *reinterpret_cast<const uint4*>(dyg + ((((size_t)b * L + t) * H + h) * R + o) * P + p0 + pv * VEC);
+        uint4 raw = py[k];
         if (!COORD) {
           float vals[VEC];
           unpack<BF16>(raw, vals);
@@ -190,6 +188,34 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_adjoint(BwdParams p) {
           raw = pack<BF16>(vals);
         }
         *reinterpret_cast<uint4*>(sY + row * VS + pv * VEC) = raw;
+      }
+    }
+    if (c > 0) prefetch(c - 1);  // in flight during this chunk's products
+
+    // carried adjoint: Gpre[c+1] -> Phi_{t0',t0}^T Gpre[c+1]
+#pragma unroll
+    for (int k = 0; k < S::ST_PER_WAVE; ++k) {
+      const int tile = wave + NW * k;
+      if (tile < S::ST_TILES) {
+        const int tnn = tile / S::TP;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int n = 16 * tnn + 4 * (lane >> 4) + i;
+          st[k][i] *= COORD ? __expf(-sRate[n] * cdx_end) : __expf(-Ah * cdx_end);
+        }
+        if (COORD) {
+#pragma unroll
+          for (int i = 0; i < 4; i += 2) {
+            const int n = 16 * tnn + 4 * (lane >> 4) + i;
+            if (n >= nreal) {
+              float sn, cs;
+              fast_sincos(sOmega[(n - nreal) >> 1] * cdx_end, &sn, &cs);
+              const float a0 = st[k][i], a1 = st[k][i + 1];
+              st[k][i] = cs * a0 + sn * a1;  // R(-theta)
+              st[k][i + 1] = -sn * a0 + cs * a1;
+            }
+          }
+        }
       }
     }
     __syncthreads();
@@ -298,11 +324,8 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int nch = p.nchunks;
-  const int slice = blockIdx.x / nch, c = blockIdx.x % nch;
-  const int b = slice / p.H, h = slice % p.H, g = h / (p.H / p.G);
   const int L = p.L, H = p.H, G = p.G, nreal = p.n_real, npairs = p.n_pairs;
-  const int t0 = c * QT, tn = t0 + QT;
-  const bool has_next = tn < L;
+  const int nitems = p.batch * H * nch;
 
   const T* xg = static_cast<const T*>(p.x);
   const T* Bg = static_cast<const T*>(p.B);
@@ -312,26 +335,8 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
   T* dBg = static_cast<T*>(p.dB);
   T* dCg = static_cast<T*>(p.dC);
 
-  if (COORD) {
-    const int na = nreal + npairs;
-    for (int n = tid; n < N; n += S::NTH) {
-      float r;
-      if (p.head_rates) r = p.A[h];
-      else if (n < nreal) r = p.A[(size_t)h * na + n];
-      else r = p.A[(size_t)h * na + nreal + ((n - nreal) >> 1)];
-      sRate[n] = r;
-    }
-    for (int k = tid; k < npairs; k += S::NTH) sOmega[k] = p.omega[(size_t)h * npairs + k];
-  }
-  for (int i = tid; i < WC * 64; i += S::NTH) (&sTok[0][0])[i] = 0.f;
-  for (int i = tid; i < WH * 64; i += S::NTH) {
-    (&sTT[0][0])[i] = 0.f; (&sSrc[0][0])[i] = 0.f; (&sRS[0][0])[i] = 0.f; (&sCS[0][0])[i] = 0.f;
-  }
-  for (int i = tid; i < WT * 64; i += S::NTH) { (&sDg[0][0])[i] = 0.f; (&sDb[0][0])[i] = 0.f; }
-  for (int i = tid; i < WC * NCO; i += S::NTH) { (&sEK[0][0])[i] = 0.f; (&sPA[0][0])[i] = 0.f; }
-  for (int i = tid; i < WC * PCO; i += S::NTH) { (&sEKth[0][0])[i] = 0.f; (&sPW[0][0])[i] = 0.f; }
+  // zero padding rows / columns (the staging never writes them)
   for (int i = tid; i < (S::NC - N) * PS; i += S::NTH) { sGh[N * PS + i] = T(0); sGl[N * PS + i] = T(0); }
-  // zero padding rows / columns
   for (int i = tid; i < (S::QOC - QO) * NS; i += S::NTH) sQ[QO * NS + i] = T(0);
   for (int i = tid; i < (S::QOC - QO) * PS; i += S::NTH) sY[QO * PS + i] = T(0);
   for (int i = tid; i < (S::QOC - QO) * KS; i += S::NTH) { sSM[QO * KS + i] = T(0); sZM[QO * KS + i] = T(0); }
@@ -350,694 +355,813 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
       sGh[r * PS + cc] = T(0); sGl[r * PS + cc] = T(0); sSh[r * PS + cc] = T(0); sSl[r * PS + cc] = T(0);
     }
   }
-  const float Ah = COORD ? 0.f : p.A[h];
-  const float Dh = p.has_D ? p.D[h] : 0.f;
 
-  // ---------------------------------------------------------------- scalars
-  float raw_l = 0.f, dl = 0.f, be_l = 0.f, ga_l = 1.f;
-  if (lane < QT && t0 + lane < L) {
-    const size_t idx = ((size_t)b * L + t0 + lane) * H + h;
-    raw_l = p.dt[idx];
-    dl = p.softplus ? softplus_f32(raw_l) : raw_l;
-    if (S::TE) { be_l = p.beta[idx]; ga_l = p.gamma[idx]; }
-  } else if (S::TE) {
-    ga_l = 0.f;
-  }
-  float dnext = 0.f, bnext = 0.f;
-  if (has_next) {
-    const size_t idx = ((size_t)b * L + tn) * H + h;
-    const float raw = p.dt[idx];
-    dnext = p.softplus ? softplus_f32(raw) : raw;
-    if (S::TE) bnext = p.beta[idx];
-  }
-  const float cd_l = wave_prefix_sum(dl);
-  const float cdend = __shfl(cd_l, QT - 1, kWave);
-  const float w_l = COORD ? 0.f : __expf(-Ah * (cdend - cd_l));   // e^{L_end - L_t}
-  const float el_l = COORD ? 0.f : __expf(-Ah * cd_l);            // e^{L_t}
+  // ---------------------------------------------------------------- prefetch
+  // The workgroup walks the (slice, chunk) items item = blockIdx.x + k gridDim.x.
+  // The global reads of the next item go into registers while the current item
+  // computes, so the loads overlap the MFMA / VALU work.
+  constexpr int PV = P / 4;  // fp32 vectors per state row
+  constexpr int CP = (S::C_VECS + S::NTH - 1) / S::NTH, BP = (S::B_VECS + S::NTH - 1) / S::NTH;
+  constexpr int XP = (S::X_VECS + S::NTH - 1) / S::NTH, YP = (S::Y_VECS + S::NTH - 1) / S::NTH;
+  constexpr int SPV = (N / 2) * PV, SP = (SPV + S::NTH - 1) / S::NTH;
+  uint4 pfc[CP], pfb[BP], pfx[XP], pfy[YP];
+  float4 pfs[SP][2], pfg[SP][2];
+  float pf_dt = 0.f, pf_be = 0.f, pf_ga = 0.f, pf_dtn = 0.f, pf_bn = 0.f;
+  const uint4 zero4 = make_uint4(0, 0, 0, 0);
+  const float4 zf4 = make_float4(0.f, 0.f, 0.f, 0.f);
 
-  // ---------------------------------------------------------------- staging
-  // queries (t, o)
-  for (int v0 = 0; v0 < S::C_VECS; v0 += S::NTH) {
-    const int v = v0 + tid;
-    const int vv = v < S::C_VECS ? v : 0;
-    const int row = vv / (N / VEC), n0 = (vv % (N / VEC)) * VEC;
-    const int tl = row / R, o = row % R, t = t0 + tl;
-    const float cd = __shfl(cd_l, tl, kWave);
-    if (v >= S::C_VECS) continue;
-    uint4 raw = make_uint4(0, 0, 0, 0);
-    if (t < L) raw = *reinterpret_cast<const uint4*>(Cg + ((((size_t)b * L + t) * G + g) * R + o) * N + n0);
-    if (COORD) {
-      float vals[VEC];
-      unpack<BF16>(raw, vals);
+  auto prefetch = [&](int item) {
+    const int slice = item / nch, c = item % nch;
+    const int b = slice / H, h = slice % H, g = h / (H / G);
+    const int t0 = c * QT, tn = t0 + QT;
+    const bool has_next = tn < L;
 #pragma unroll
-      for (int i = 0; i < VEC; i += 2) {
-        const int n = n0 + i;
-        if (n >= nreal) {
-          float sn, cs;
-          fast_sincos(sOmega[(n - nreal) >> 1] * cd, &sn, &cs);
-          const float a = vals[i], bb = vals[i + 1];
-          vals[i] = cs * a + sn * bb;
-          vals[i + 1] = -sn * a + cs * bb;
+    for (int k = 0; k < CP; ++k) {
+      const int v = tid + S::NTH * k;
+      uint4 raw = zero4;
+      if (v < S::C_VECS) {
+        const int row = v / (N / VEC), n0 = (v % (N / VEC)) * VEC;
+        const int t = t0 + row / R, o = row % R;
+        if (t < L) raw = *reinterpret_cast<const uint4*>(Cg + ((((size_t)b * L + t) * G + g) * R + o) * N + n0);
+      }
+      pfc[k] = raw;
+    }
+#pragma unroll
+    for (int k = 0; k < BP; ++k) {
+      const int v = tid + S::NTH * k;
+      uint4 raw = zero4;
+      if (v < S::B_VECS) {
+        const int row = v / (N / VEC), n0 = (v % (N / VEC)) * VEC;
+        const int t = t0 + row / R - S::TEH, r = row % R;
+        if (t >= 0 && t < L) raw = *reinterpret_cast<const uint4*>(Bg + ((((size_t)b * L + t) * G + g) * R + r) * N + n0);
+      }
+      pfb[k] = raw;
+    }
+#pragma unroll
+    for (int k = 0; k < XP; ++k) {
+      const int v = tid + S::NTH * k;
+      uint4 raw = zero4;
+      if (v < S::X_VECS) {
+        const int row = v / (P / VEC), p0 = (v % (P / VEC)) * VEC;
+        const int t = t0 + row / R - S::TEH, r = row % R;
+        if (t >= 0 && t < L) raw = *reinterpret_cast<const uint4*>(xg + ((((size_t)b * L + t) * H + h) * R + r) * P + p0);
+      }
+      pfx[k] = raw;
+    }
+#pragma unroll
+    for (int k = 0; k < YP; ++k) {
+      const int v = tid + S::NTH * k;
+      uint4 raw = zero4;
+      if (v < S::Y_VECS) {
+        const int row = v / (P / VEC), p0 = (v % (P / VEC)) * VEC;
+        const int t = t0 + row / R, o = row % R;
+        if (t < L) raw = *reinterpret_cast<const uint4*>(dyg + ((((size_t)b * L + t) * H + h) * R + o) * P + p0);
+      }
+      pfy[k] = raw;
+    }
+    const float* Sg = p.saved + ((size_t)slice * (nch + 1) + c) * N * P;
+    const float* Gg = p.gseg + ((size_t)slice * nch + (c + 1)) * N * P;
+#pragma unroll
+    for (int k = 0; k < SP; ++k) {
+      const int v = tid + S::NTH * k;
+      float4 s0 = zf4, s1 = zf4, g0 = zf4, g1 = zf4;
+      if (v < SPV) {
+        const int n = 2 * (v / PV), q0 = (v % PV) * 4;
+        s0 = *reinterpret_cast<const float4*>(Sg + (size_t)n * P + q0);
+        s1 = *reinterpret_cast<const float4*>(Sg + (size_t)(n + 1) * P + q0);
+        if (has_next) {
+          g0 = *reinterpret_cast<const float4*>(Gg + (size_t)n * P + q0);
+          g1 = *reinterpret_cast<const float4*>(Gg + (size_t)(n + 1) * P + q0);
         }
       }
-#pragma unroll
-      for (int i = 0; i < VEC; ++i) vals[i] *= __expf(-sRate[n0 + i] * (cd - 0.5f * cdend));
-      raw = pack<BF16>(vals);
+      pfs[k][0] = s0; pfs[k][1] = s1; pfg[k][0] = g0; pfg[k][1] = g1;
     }
-    *reinterpret_cast<uint4*>(sQ + row * NS + n0) = raw;
-  }
-  // keys j: gamma_s B_s at (s, r) and beta_s B_{s-1} at (s, R + r)
-  for (int v0 = 0; v0 < S::B_VECS; v0 += S::NTH) {
-    const int v = v0 + tid;
-    const int vv = v < S::B_VECS ? v : 0;
-    const int row = vv / (N / VEC), n0 = (vv % (N / VEC)) * VEC;
-    const int sl = row / R - S::TEH, r = row % R, t = t0 + sl;
-    const int ta = sl < 0 ? 0 : sl, tb = sl + 1 < QT ? sl + 1 : QT - 1;
-    const float cdv[2] = {__shfl(cd_l, ta, kWave), __shfl(cd_l, tb, kWave)};
-    const float wv[2] = {S::TE ? __shfl(ga_l, ta, kWave) : 1.f, S::TE ? __shfl(be_l, tb, kWave) : 0.f};
-    if (v >= S::B_VECS) continue;
-    uint4 raw = make_uint4(0, 0, 0, 0);
-    if (t >= 0 && t < L) raw = *reinterpret_cast<const uint4*>(Bg + ((((size_t)b * L + t) * G + g) * R + r) * N + n0);
-    float vals[VEC];
-    unpack<BF16>(raw, vals);
-#pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      if (e == 1 && !S::TE) break;
-      const int tau = sl + e;
-      if (tau < 0 || tau >= QT || (e == 0 && sl < 0)) continue;
-      const int j = tau * KR + (e ? R : 0) + r;
-      float u[VEC], kk[VEC], ke[VEC];
-#pragma unroll
-      for (int i = 0; i < VEC; ++i) u[i] = vals[i] * wv[e];
+    pf_dt = pf_be = pf_ga = 0.f;
+    if (lane < QT && t0 + lane < L) {
+      const size_t idx = ((size_t)b * L + t0 + lane) * H + h;
+      pf_dt = p.dt[idx];
+      if (S::TE) { pf_be = p.beta[idx]; pf_ga = p.gamma[idx]; }
+    }
+    pf_dtn = pf_bn = 0.f;
+    if (has_next) {
+      const size_t idx = ((size_t)b * L + tn) * H + h;
+      pf_dtn = p.dt[idx];
+      if (S::TE) pf_bn = p.beta[idx];
+    }
+  };
+
+  int item = blockIdx.x;
+  if (item < nitems) prefetch(item);
+  for (; item < nitems; item += gridDim.x) {
+    const int slice = item / nch, c = item % nch;
+    const int b = slice / H, h = slice % H, g = h / (H / G);
+    const int t0 = c * QT, tn = t0 + QT;
+    const bool has_next = tn < L;
+
+    __syncthreads();  // the previous item is done with every shared buffer
+    if (COORD) {
+      const int na = nreal + npairs;
+      for (int n = tid; n < N; n += S::NTH) {
+        float r;
+        if (p.head_rates) r = p.A[h];
+        else if (n < nreal) r = p.A[(size_t)h * na + n];
+        else r = p.A[(size_t)h * na + nreal + ((n - nreal) >> 1)];
+        sRate[n] = r;
+      }
+      for (int k = tid; k < npairs; k += S::NTH) sOmega[k] = p.omega[(size_t)h * npairs + k];
+    }
+    for (int i = tid; i < WC * 64; i += S::NTH) (&sTok[0][0])[i] = 0.f;
+    for (int i = tid; i < WH * 64; i += S::NTH) {
+      (&sTT[0][0])[i] = 0.f; (&sSrc[0][0])[i] = 0.f; (&sRS[0][0])[i] = 0.f; (&sCS[0][0])[i] = 0.f;
+    }
+    for (int i = tid; i < WT * 64; i += S::NTH) { (&sDg[0][0])[i] = 0.f; (&sDb[0][0])[i] = 0.f; }
+    for (int i = tid; i < WC * NCO; i += S::NTH) { (&sEK[0][0])[i] = 0.f; (&sPA[0][0])[i] = 0.f; }
+    for (int i = tid; i < WC * PCO; i += S::NTH) { (&sEKth[0][0])[i] = 0.f; (&sPW[0][0])[i] = 0.f; }
+    if (COORD) __syncthreads();  // rates and pair frequencies before the staging reads them
+    const float Ah = COORD ? 0.f : p.A[h];
+    const float Dh = p.has_D ? p.D[h] : 0.f;
+
+    // ---------------------------------------------------------------- scalars
+    float raw_l = 0.f, dl = 0.f, be_l = 0.f, ga_l = 1.f;
+    if (lane < QT && t0 + lane < L) {
+      raw_l = pf_dt;
+      dl = p.softplus ? softplus_f32(raw_l) : raw_l;
+      if (S::TE) { be_l = pf_be; ga_l = pf_ga; }
+    } else if (S::TE) {
+      ga_l = 0.f;
+    }
+    float dnext = 0.f, bnext = 0.f;
+    if (has_next) {
+      dnext = p.softplus ? softplus_f32(pf_dtn) : pf_dtn;
+      if (S::TE) bnext = pf_bn;
+    }
+    const float cd_l = wave_prefix_sum(dl);
+    const float cdend = __shfl(cd_l, QT - 1, kWave);
+    const float w_l = COORD ? 0.f : __expf(-Ah * (cdend - cd_l));   // e^{L_end - L_t}
+    const float el_l = COORD ? 0.f : __expf(-Ah * cd_l);            // e^{L_t}
+
+    // ---------------------------------------------------------------- staging
+    // queries (t, o)
+  #pragma unroll
+    for (int k = 0; k < CP; ++k) {
+      const int v = tid + S::NTH * k;
+      const int vv = v < S::C_VECS ? v : 0;
+      const int row = vv / (N / VEC), n0 = (vv % (N / VEC)) * VEC;
+      const int tl = row / R;
+      const float cd = __shfl(cd_l, tl, kWave);
+      if (v >= S::C_VECS) continue;
+      uint4 raw = pfc[k];
       if (COORD) {
-#pragma unroll
+        float vals[VEC];
+        unpack<BF16>(raw, vals);
+  #pragma unroll
         for (int i = 0; i < VEC; i += 2) {
           const int n = n0 + i;
           if (n >= nreal) {
             float sn, cs;
-            fast_sincos(sOmega[(n - nreal) >> 1] * cdv[e], &sn, &cs);
-            const float a = u[i], bb = u[i + 1];
-            u[i] = cs * a + sn * bb;
-            u[i + 1] = -sn * a + cs * bb;
+            fast_sincos(sOmega[(n - nreal) >> 1] * cd, &sn, &cs);
+            const float a = vals[i], bb = vals[i + 1];
+            vals[i] = cs * a + sn * bb;
+            vals[i + 1] = -sn * a + cs * bb;
           }
         }
-#pragma unroll
-        for (int i = 0; i < VEC; ++i) {
-          kk[i] = u[i] * __expf(-sRate[n0 + i] * (0.5f * cdend - cdv[e]));
-          ke[i] = u[i] * __expf(-sRate[n0 + i] * (cdend - cdv[e]));
+  #pragma unroll
+        for (int i = 0; i < VEC; ++i) vals[i] *= __expf(-sRate[n0 + i] * (cd - 0.5f * cdend));
+        raw = pack<BF16>(vals);
+      }
+      *reinterpret_cast<uint4*>(sQ + row * NS + n0) = raw;
+    }
+    // keys j: gamma_s B_s at (s, r) and beta_s B_{s-1} at (s, R + r)
+  #pragma unroll
+    for (int k = 0; k < BP; ++k) {
+      const int v = tid + S::NTH * k;
+      const int vv = v < S::B_VECS ? v : 0;
+      const int row = vv / (N / VEC), n0 = (vv % (N / VEC)) * VEC;
+      const int sl = row / R - S::TEH, r = row % R;
+      const int ta = sl < 0 ? 0 : sl, tb = sl + 1 < QT ? sl + 1 : QT - 1;
+      const float cdv[2] = {__shfl(cd_l, ta, kWave), __shfl(cd_l, tb, kWave)};
+      const float wv[2] = {S::TE ? __shfl(ga_l, ta, kWave) : 1.f, S::TE ? __shfl(be_l, tb, kWave) : 0.f};
+      if (v >= S::B_VECS) continue;
+      float vals[VEC];
+      unpack<BF16>(pfb[k], vals);
+  #pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        if (e == 1 && !S::TE) break;
+        const int tau = sl + e;
+        if (tau < 0 || tau >= QT || (e == 0 && sl < 0)) continue;
+        const int j = tau * KR + (e ? R : 0) + r;
+        float u[VEC], kk[VEC], ke[VEC];
+  #pragma unroll
+        for (int i = 0; i < VEC; ++i) u[i] = vals[i] * wv[e];
+        if (COORD) {
+  #pragma unroll
+          for (int i = 0; i < VEC; i += 2) {
+            const int n = n0 + i;
+            if (n >= nreal) {
+              float sn, cs;
+              fast_sincos(sOmega[(n - nreal) >> 1] * cdv[e], &sn, &cs);
+              const float a = u[i], bb = u[i + 1];
+              u[i] = cs * a + sn * bb;
+              u[i + 1] = -sn * a + cs * bb;
+            }
+          }
+  #pragma unroll
+          for (int i = 0; i < VEC; ++i) {
+            kk[i] = u[i] * __expf(-sRate[n0 + i] * (0.5f * cdend - cdv[e]));
+            ke[i] = u[i] * __expf(-sRate[n0 + i] * (cdend - cdv[e]));
+          }
+          *reinterpret_cast<uint4*>(sKe + j * NS + n0) = pack<BF16>(ke);
+        } else {
+  #pragma unroll
+          for (int i = 0; i < VEC; ++i) kk[i] = u[i];
         }
-        *reinterpret_cast<uint4*>(sKe + j * NS + n0) = pack<BF16>(ke);
-      } else {
-#pragma unroll
-        for (int i = 0; i < VEC; ++i) kk[i] = u[i];
-      }
-      *reinterpret_cast<uint4*>(sK + j * NS + n0) = pack<BF16>(kk);
-    }
-  }
-  // values j and dy rows
-  float dDp = 0.f;
-  for (int v = tid; v < S::X_VECS; v += S::NTH) {
-    const int row = v / (P / VEC), p0 = (v % (P / VEC)) * VEC;
-    const int sl = row / R - S::TEH, r = row % R, t = t0 + sl;
-    uint4 raw = make_uint4(0, 0, 0, 0);
-    if (t >= 0 && t < L) raw = *reinterpret_cast<const uint4*>(xg + ((((size_t)b * L + t) * H + h) * R + r) * P + p0);
-    if (sl >= 0) *reinterpret_cast<uint4*>(sV + (sl * KR + r) * PS + p0) = raw;
-    if (S::TE && sl + 1 < QT) *reinterpret_cast<uint4*>(sV + ((sl + 1) * KR + R + r) * PS + p0) = raw;
-  }
-  for (int v = tid; v < S::Y_VECS; v += S::NTH) {
-    const int row = v / (P / VEC), p0 = (v % (P / VEC)) * VEC;
-    const int tl = row / R, o = row % R, t = t0 + tl;
-    uint4 raw = make_uint4(0, 0, 0, 0);
-    if (t < L) raw = *reinterpret_cast<const uint4*>(dyg + ((((size_t)b * L + t) * H + h) * R + o) * P + p0);
-    *reinterpret_cast<uint4*>(sY + row * PS + p0) = raw;
-  }
-  // incoming state S_in and folded adjoint G~ = e^{-A Dnext} R(-omega (cd_end + Dnext)) g'
-  // (split into bf16 hi + lo), final-state terms per row / pair
-  {
-    const float* Sg = p.saved + ((size_t)slice * (nch + 1) + c) * N * P;
-    const float* Gg = p.gseg + ((size_t)slice * nch + (c + 1)) * N * P;
-    const bool gvalid = has_next && (c + 1 < nch);
-    const float lend_h = COORD ? 0.f : __expf(-Ah * cdend);
-    const float gdec_h = COORD ? 0.f : __expf(-Ah * dnext);
-    constexpr int PV = P / 4;  // fp32 vectors per row
-    for (int v = tid; v < (N / 2) * PV; v += S::NTH) {
-      const int rp = v / PV, pc = v % PV;
-      const int n = 2 * rp, q0 = pc * 4;
-      float sa[4], sb[4], ga[4], gb[4];
-      {
-        const float4 a = *reinterpret_cast<const float4*>(Sg + (size_t)n * P + q0);
-        const float4 bb = *reinterpret_cast<const float4*>(Sg + (size_t)(n + 1) * P + q0);
-        sa[0] = a.x; sa[1] = a.y; sa[2] = a.z; sa[3] = a.w;
-        sb[0] = bb.x; sb[1] = bb.y; sb[2] = bb.z; sb[3] = bb.w;
-      }
-      if (gvalid) {
-        const float4 a = *reinterpret_cast<const float4*>(Gg + (size_t)n * P + q0);
-        const float4 bb = *reinterpret_cast<const float4*>(Gg + (size_t)(n + 1) * P + q0);
-        ga[0] = a.x; ga[1] = a.y; ga[2] = a.z; ga[3] = a.w;
-        gb[0] = bb.x; gb[1] = bb.y; gb[2] = bb.z; gb[3] = bb.w;
-      } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) ga[i] = gb[i] = 0.f;
-      }
-      float fa, fb, lea, leb;
-      if (COORD) {
-        fa = __expf(-sRate[n] * dnext); fb = __expf(-sRate[n + 1] * dnext);
-        lea = __expf(-sRate[n] * cdend); leb = __expf(-sRate[n + 1] * cdend);
-      } else {
-        fa = fb = gdec_h; lea = leb = lend_h;
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) { ga[i] *= fa; gb[i] *= fb; }
-      const bool pair = COORD && n >= nreal;
-      if (pair) {
-        float sn, cs;
-        fast_sincos(sOmega[(n - nreal) >> 1] * (cdend + dnext), &sn, &cs);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float a0 = ga[i], a1 = gb[i];
-          ga[i] = cs * a0 + sn * a1;
-          gb[i] = -sn * a0 + cs * a1;
-        }
-      }
-      float ea = 0.f, eb = 0.f, eth = 0.f;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        ea += ga[i] * sa[i];
-        eb += gb[i] * sb[i];
-        eth += -ga[i] * sb[i] + gb[i] * sa[i];  // <G~, J S>
-      }
-      ea *= lea; eb *= leb; eth *= lea;
-      // reduce over the PV p-vectors of this row pair (consecutive lanes)
-#pragma unroll
-      for (int off = 1; off < PV; off <<= 1) {
-        ea += __shfl_xor(ea, off, kWave);
-        eb += __shfl_xor(eb, off, kWave);
-        eth += __shfl_xor(eth, off, kWave);
-      }
-      if (pc == 0) {
-        sE[n] = ea; sE[n + 1] = eb;
-        if (pair) sEth[(n - nreal) >> 1] = eth;
-      }
-      // bf16 hi / lo copies
-      float hi[4], lo[4];
-      auto split = [&](const float* x, T* dh, T* dlo) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          hi[i] = to_f32(from_f32<T>(x[i]));
-          lo[i] = x[i] - hi[i];
-          dh[i] = from_f32<T>(hi[i]);
-          dlo[i] = from_f32<T>(lo[i]);
-        }
-      };
-      split(sa, sSh + n * PS + q0, sSl + n * PS + q0);
-      split(sb, sSh + (n + 1) * PS + q0, sSl + (n + 1) * PS + q0);
-      split(ga, sGh + n * PS + q0, sGl + n * PS + q0);
-      split(gb, sGh + (n + 1) * PS + q0, sGl + (n + 1) * PS + q0);
-    }
-    // two-endpoint tails of the last token: beta_{t0'} B_{t1}^T g' and g' X_{t1}^T
-    if (S::TE) {
-      const int t1 = t0 + QT - 1;
-      for (int i = tid; i < R * P; i += S::NTH) {
-        const int r = i / P, pp = i % P;
-        float acc = 0.f;
-        if (gvalid) {
-          for (int n = 0; n < N; ++n)
-            acc += to_f32(Bg[((((size_t)b * L + t1) * G + g) * R + r) * N + n]) * Gg[(size_t)n * P + pp];
-        }
-        sTailX[i] = bnext * acc;
-      }
-      for (int i = tid; i < R * N; i += S::NTH) {
-        const int r = i / N, n = i % N;
-        float acc = 0.f;
-        if (gvalid) {
-          for (int pp = 0; pp < P; ++pp)
-            acc += Gg[(size_t)n * P + pp] * to_f32(xg[((((size_t)b * L + t1) * H + h) * R + r) * P + pp]);
-        }
-        sTailB[i] = bnext * acc;
+        *reinterpret_cast<uint4*>(sK + j * NS + n0) = pack<BF16>(kk);
       }
     }
-  }
-  __syncthreads();
-  if (p.has_D) {
-    for (int i = tid; i < QO * P; i += S::NTH) {
-      const int row = i / P, pp = i % P, tl = row / R, o = row % R;
-      dDp += to_f32(sY[row * PS + pp]) * to_f32(sV[(tl * KR + o) * PS + pp]);
+    // values j and dy rows
+    float dDp = 0.f;
+  #pragma unroll
+    for (int k = 0; k < XP; ++k) {
+      const int v = tid + S::NTH * k;
+      if (v >= S::X_VECS) continue;
+      const int row = v / (P / VEC), p0 = (v % (P / VEC)) * VEC;
+      const int sl = row / R - S::TEH, r = row % R;
+      if (sl >= 0) *reinterpret_cast<uint4*>(sV + (sl * KR + r) * PS + p0) = pfx[k];
+      if (S::TE && sl + 1 < QT) *reinterpret_cast<uint4*>(sV + ((sl + 1) * KR + R + r) * PS + p0) = pfx[k];
     }
-  }
-  dDp = wave_sum(dDp);
-  if (lane == 0) sMisc[wave] = dDp;
-
-  // ---------------------------------------------------------------- scores
-  for (int tile = wave; tile < S::TQ * S::TK; tile += NW) {
-    const int ti = tile / S::TK, tj = tile % S::TK;
-    const int tmax = (16 * ti + 15) / R, smin = (16 * tj) / KR;
-    f32x4 sc = {0.f, 0.f, 0.f, 0.f}, z = {0.f, 0.f, 0.f, 0.f};
-    if (smin <= tmax) {
-#pragma unroll
-      for (int kk = 0; kk < S::NC / 32; ++kk) {
-        const auto a = load_frag<BF16>(sQ + (16 * ti + (lane & 15)) * NS + kk * 32 + 8 * (lane >> 4));
-        const auto bq = load_frag<BF16>(sK + (16 * tj + (lane & 15)) * NS + kk * 32 + 8 * (lane >> 4));
-        mma<BF16>(sc, a, bq);
-      }
-#pragma unroll
-      for (int kk = 0; kk < S::PC / 32; ++kk) {
-        const auto a = load_frag<BF16>(sY + (16 * ti + (lane & 15)) * PS + kk * 32 + 8 * (lane >> 4));
-        const auto bv = load_frag<BF16>(sV + (16 * tj + (lane & 15)) * PS + kk * 32 + 8 * (lane >> 4));
-        mma<BF16>(z, a, bv);
-      }
+  #pragma unroll
+    for (int k = 0; k < YP; ++k) {
+      const int v = tid + S::NTH * k;
+      if (v >= S::Y_VECS) continue;
+      const int row = v / (P / VEC), p0 = (v % (P / VEC)) * VEC;
+      *reinterpret_cast<uint4*>(sY + row * PS + p0) = pfy[k];
     }
-    const int col = 16 * tj + (lane & 15), s = col / KR;
-    const float cds = __shfl(cd_l, s, kWave);
-    float csum = 0.f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = 16 * ti + 4 * (lane >> 4) + i, t = row / R;
-      const float cdt = __shfl(cd_l, t, kWave);
-      float m = 0.f;
-      if (s <= t) m = COORD ? 1.f : __expf(-Ah * (cdt - cds));
-      sSM[row * KS + col] = from_f32<T>(sc[i] * m);
-      sZM[row * KS + col] = from_f32<T>(z[i] * m);
-      if (!COORD) {
-        float wv = z[i] * sc[i] * m;
-        // row sum over the 16 columns of this tile
-        float rs = wv;
-#pragma unroll
-        for (int off = 1; off < 16; off <<= 1) rs += __shfl_xor(rs, off, kWave);
-        if ((lane & 15) == 0) sRS[wave][t] += rs;
-        csum += wv;
-      }
-    }
-    if (!COORD) {
-      csum += __shfl_xor(csum, 16, kWave);
-      csum += __shfl_xor(csum, 32, kWave);
-#pragma unroll
-      for (int off = 1; off < KR; off <<= 1) csum += __shfl_xor(csum, off, kWave);
-      if (lane < 16 && (lane % KR) == 0) sCS[wave][s] += csum;
-    }
-  }
-  __syncthreads();
-
-  // ---------------------------------------------------------------- dV -> dX
-  for (int tile = wave; tile < S::TK * S::TP; tile += NW) {
-    const int tj = tile / S::TP, tp = tile % S::TP;
-    f32x4 ai = {0.f, 0.f, 0.f, 0.f}, ae = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kk = 0; kk < S::QOC / 32; ++kk) {
-      const auto a = load_frag_tr<BF16>(sSM + (kk * 32) * KS + 16 * tj, KS);
-      const auto bq = load_frag_tr<BF16>(sY + (kk * 32) * PS + 16 * tp, PS);
-      mma<BF16>(ai, a, bq);
-    }
-#pragma unroll
-    for (int kk = 0; kk < S::NC / 32; ++kk) {
-      const auto a = load_frag<BF16>((COORD ? sKe : sK) + (16 * tj + (lane & 15)) * NS + kk * 32 + 8 * (lane >> 4));
-      if (kk * 32 < N) {
-        const auto bh = load_frag_tr<BF16>(sGh + (kk * 32) * PS + 16 * tp, PS);
-        const auto bl = load_frag_tr<BF16>(sGl + (kk * 32) * PS + 16 * tp, PS);
-        mma<BF16>(ae, a, bh);
-        mma<BF16>(ae, a, bl);
-      }
-    }
-    const int pp = 16 * tp + (lane & 15);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int j = 16 * tj + 4 * (lane >> 4) + i;
-      const int s = j / KR, kr = j % KR;
-      const float wj = COORD ? 1.f : __shfl(w_l, s, kWave);
-      const float dv = ai[i] + wj * ae[i];
-      if (!S::TE) {
-        const int t = t0 + s;
-        const float val = dv + (p.has_D ? Dh * to_f32(sY[(s * R + kr) * PS + pp]) : 0.f);
-        if (t < L) dxg[((((size_t)b * L + t) * H + h) * R + kr) * P + pp] = from_f32<T>(val);
-      } else if (kr < R) {
-        sDX[((s + 1) * R + kr) * P + pp] = dv;                       // gamma row -> X_s
-      } else if (s >= 1) {
-        sDX[(QT + 1) * R * P + (s * R + kr - R) * P + pp] = dv;      // beta row -> X_{s-1}
-      }
-    }
-  }
-
-  // ---------------------------------------------------------------- dK~ -> dB, dbeta, dgamma
-  for (int tile = wave; tile < S::TN * S::TK; tile += NW) {
-    const int tnn = tile / S::TK, tj = tile % S::TK;
-    f32x4 ai = {0.f, 0.f, 0.f, 0.f}, ae = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kk = 0; kk < S::QOC / 32; ++kk) {
-      const auto a = load_frag_tr<BF16>(sQ + (kk * 32) * NS + 16 * tnn, NS);
-      const auto bz = load_frag_tr<BF16>(sZM + (kk * 32) * KS + 16 * tj, KS);
-      mma<BF16>(ai, a, bz);
-    }
-#pragma unroll
-    for (int kk = 0; kk < S::PC / 32; ++kk) {
-      const auto bv = load_frag<BF16>(sV + (16 * tj + (lane & 15)) * PS + kk * 32 + 8 * (lane >> 4));
-      const auto ah = load_frag<BF16>(sGh + (16 * tnn + (lane & 15)) * PS + kk * 32 + 8 * (lane >> 4));
-      const auto al = load_frag<BF16>(sGl + (16 * tnn + (lane & 15)) * PS + kk * 32 + 8 * (lane >> 4));
-      mma<BF16>(ae, ah, bv);
-      mma<BF16>(ae, al, bv);
-    }
-    const int j = 16 * tj + (lane & 15), s = j / KR, kr = j % KR;
-    const float cds = __shfl(cd_l, s, kWave);
-    const float wj = COORD ? 1.f : __shfl(w_l, s, kWave);
-    const float gam = S::TE ? __shfl(ga_l, s, kWave) : 1.f;
-    const float bet = S::TE ? __shfl(be_l, s, kWave) : 0.f;
-    const bool brow = S::TE && kr >= R;
-    const int rr = brow ? kr - R : kr;
-    const int tb = t0 + (brow ? s - 1 : s);  // token whose B row this key carries
-    float tokacc = 0.f, dgb = 0.f;
-    float dk[4], kv[4], rpa[4], rek[4], rpw[2] = {0.f, 0.f}, rekt[2] = {0.f, 0.f};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int n = 16 * tnn + 4 * (lane >> 4) + i;
-      kv[i] = to_f32(sK[j * NS + n]);
-      rpa[i] = 0.f; rek[i] = 0.f;
-      if (COORD) {
-        const float er = __expf(-sRate[n] * 0.5f * cdend);  // e^{r_n}
-        const float ck = ai[i] + er * ae[i];
-        dk[i] = __expf(-sRate[n] * (0.5f * cdend - cds)) * ck;  // e^{r - L_s} ck  (dK~)
-        // source terms: -k o cK  (rows); the inter part also feeds the final-state term
-        const float dr = -kv[i] * ck;
-        tokacc += -sRate[n] * dr;
-        rpa[i] = -cds * dr;
-        rek[i] = kv[i] * er * ae[i];
-      } else {
-        dk[i] = ai[i] + wj * ae[i];
-        tokacc += kv[i] * wj * ae[i];  // K~ o dK~ (inter part)
-      }
-    }
-    if (COORD) {
-#pragma unroll
-      for (int i = 0; i < 4; i += 2) {
-        const int n = 16 * tnn + 4 * (lane >> 4) + i;
-        if (n >= nreal) {
-          const int kp = (n - nreal) >> 1;
-          const float er = __expf(-sRate[n] * 0.5f * cdend);
-          const float ca = ai[i] + er * ae[i], cb = ai[i + 1] + er * ae[i + 1];
-          // K~^T J dK~ in scaled form: -k_a cK_b + k_b cK_a
-          const float dth = -kv[i] * cb + kv[i + 1] * ca;
-          tokacc += sOmega[kp] * dth;
-          rpw[i >> 1] = cds * dth;
-          rekt[i >> 1] = -(-kv[i] * er * ae[i + 1] + kv[i + 1] * er * ae[i]);
-          // unfold the rotation of the key: u = R(+Theta_s) dK~
-          float sn, cs;
-          fast_sincos(sOmega[kp] * cds, &sn, &cs);
-          const float a0 = dk[i], a1 = dk[i + 1];
-          dk[i] = cs * a0 - sn * a1;
-          dk[i + 1] = sn * a0 + cs * a1;
-        }
-      }
-    }
-    // gradient w.r.t. the stored B row and the endpoint weights
-    const bool own = !(brow && s == 0) && tb < L;  // the halo row's B belongs to the previous chunk
-    float braw[4];
+    // incoming state S_in and folded adjoint G~ = e^{-A Dnext} R(-omega (cd_end + Dnext)) g'
+    // (split into bf16 hi + lo), final-state terms per row / pair
     {
-      const int tbc = tb < 0 ? 0 : tb;
-      const int n0 = 16 * tnn + 4 * (lane >> 4);
-      const T* src = Bg + ((((size_t)b * L + tbc) * G + g) * R + rr) * N + n0;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) braw[i] = (tb >= 0 && tb < L) ? to_f32(src[i]) : 0.f;
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) dgb += dk[i] * braw[i];
-    const float wgt = brow ? bet : gam;
-    if (!S::TE) {
-      if (own) {
-        const int n0 = 16 * tnn + 4 * (lane >> 4);
-        T* dst = dBg + ((((size_t)b * L + tb) * G + g) * R + rr) * N + n0;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) dst[i] = from_f32<T>(dk[i]);
-      }
-    } else {
-      const int n0 = 16 * tnn + 4 * (lane >> 4);
-      if (!brow) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sDB[((s + 1) * R + rr) * N + n0 + i] = wgt * dk[i];
-      } else if (s >= 1) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sDB[(QT + 1) * R * N + (s * R + rr) * N + n0 + i] = wgt * dk[i];
-      }
-    }
-    if (COORD) {
-      // per-row sums over the 16 key columns of this tile
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-#pragma unroll
-        for (int off = 1; off < 16; off <<= 1) {
-          rpa[i] += __shfl_xor(rpa[i], off, kWave);
-          rek[i] += __shfl_xor(rek[i], off, kWave);
+      const float* Gg = p.gseg + ((size_t)slice * nch + (c + 1)) * N * P;
+      const bool gvalid = has_next;
+      const float lend_h = COORD ? 0.f : __expf(-Ah * cdend);
+      const float gdec_h = COORD ? 0.f : __expf(-Ah * dnext);
+  #pragma unroll
+      for (int k = 0; k < SP; ++k) {
+        const int v = tid + S::NTH * k;
+        if (v >= SPV) continue;
+        const int rp = v / PV, pc = v % PV;
+        const int n = 2 * rp, q0 = pc * 4;
+        float sa[4] = {pfs[k][0].x, pfs[k][0].y, pfs[k][0].z, pfs[k][0].w};
+        float sb[4] = {pfs[k][1].x, pfs[k][1].y, pfs[k][1].z, pfs[k][1].w};
+        float ga[4] = {pfg[k][0].x, pfg[k][0].y, pfg[k][0].z, pfg[k][0].w};
+        float gb[4] = {pfg[k][1].x, pfg[k][1].y, pfg[k][1].z, pfg[k][1].w};
+        float fa, fb, lea, leb;
+        if (COORD) {
+          fa = __expf(-sRate[n] * dnext); fb = __expf(-sRate[n + 1] * dnext);
+          lea = __expf(-sRate[n] * cdend); leb = __expf(-sRate[n + 1] * cdend);
+        } else {
+          fa = fb = gdec_h; lea = leb = lend_h;
         }
-      }
-#pragma unroll
-      for (int q = 0; q < 2; ++q) {
-#pragma unroll
-        for (int off = 1; off < 16; off <<= 1) {
-          rpw[q] += __shfl_xor(rpw[q], off, kWave);
-          rekt[q] += __shfl_xor(rekt[q], off, kWave);
+  #pragma unroll
+        for (int i = 0; i < 4; ++i) { ga[i] *= fa; gb[i] *= fb; }
+        const bool pair = COORD && n >= nreal;
+        if (pair) {
+          float sn, cs;
+          fast_sincos(sOmega[(n - nreal) >> 1] * (cdend + dnext), &sn, &cs);
+  #pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float a0 = ga[i], a1 = gb[i];
+            ga[i] = cs * a0 + sn * a1;
+            gb[i] = -sn * a0 + cs * a1;
+          }
         }
-      }
-      if ((lane & 15) == 0) {
-#pragma unroll
+        float ea = 0.f, eb = 0.f, eth = 0.f;
+  #pragma unroll
         for (int i = 0; i < 4; ++i) {
+          ea += ga[i] * sa[i];
+          eb += gb[i] * sb[i];
+          eth += -ga[i] * sb[i] + gb[i] * sa[i];  // <G~, J S>
+        }
+        ea *= lea; eb *= leb; eth *= lea;
+        // reduce over the PV p-vectors of this row pair (consecutive lanes)
+  #pragma unroll
+        for (int off = 1; off < PV; off <<= 1) {
+          ea += __shfl_xor(ea, off, kWave);
+          eb += __shfl_xor(eb, off, kWave);
+          eth += __shfl_xor(eth, off, kWave);
+        }
+        if (pc == 0) {
+          sE[n] = ea; sE[n + 1] = eb;
+          if (pair) sEth[(n - nreal) >> 1] = eth;
+        }
+        // bf16 hi / lo copies
+        float hi[4], lo[4];
+        auto split = [&](const float* x, T* dh, T* dlo) {
+  #pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            hi[i] = to_f32(from_f32<T>(x[i]));
+            lo[i] = x[i] - hi[i];
+            dh[i] = from_f32<T>(hi[i]);
+            dlo[i] = from_f32<T>(lo[i]);
+          }
+        };
+        split(sa, sSh + n * PS + q0, sSl + n * PS + q0);
+        split(sb, sSh + (n + 1) * PS + q0, sSl + (n + 1) * PS + q0);
+        split(ga, sGh + n * PS + q0, sGl + n * PS + q0);
+        split(gb, sGh + (n + 1) * PS + q0, sGl + (n + 1) * PS + q0);
+      }
+      // two-endpoint tails of the last token: beta_{t0'} B_{t1}^T g' and g' X_{t1}^T
+      if (S::TE) {
+        const int t1 = t0 + QT - 1;
+        for (int i = tid; i < R * P; i += S::NTH) {
+          const int r = i / P, pp = i % P;
+          float acc = 0.f;
+          if (gvalid) {
+            for (int n = 0; n < N; ++n)
+              acc += to_f32(Bg[((((size_t)b * L + t1) * G + g) * R + r) * N + n]) * Gg[(size_t)n * P + pp];
+          }
+          sTailX[i] = bnext * acc;
+        }
+        for (int i = tid; i < R * N; i += S::NTH) {
+          const int r = i / N, n = i % N;
+          float acc = 0.f;
+          if (gvalid) {
+            for (int pp = 0; pp < P; ++pp)
+              acc += Gg[(size_t)n * P + pp] * to_f32(xg[((((size_t)b * L + t1) * H + h) * R + r) * P + pp]);
+          }
+          sTailB[i] = bnext * acc;
+        }
+      }
+    }
+    // the next item's loads go out now and land while this one computes
+    if (item + static_cast<int>(gridDim.x) < nitems) prefetch(item + gridDim.x);
+    __syncthreads();
+    if (p.has_D) {
+      for (int i = tid; i < QO * P; i += S::NTH) {
+        const int row = i / P, pp = i % P, tl = row / R, o = row % R;
+        dDp += to_f32(sY[row * PS + pp]) * to_f32(sV[(tl * KR + o) * PS + pp]);
+      }
+    }
+    dDp = wave_sum(dDp);
+    if (lane == 0) sMisc[wave] = dDp;
+
+    // ---------------------------------------------------------------- scores
+    for (int tile = wave; tile < S::TQ * S::TK; tile += NW) {
+      const int ti = tile / S::TK, tj = tile % S::TK;
+      const int tmax = (16 * ti + 15) / R, smin = (16 * tj) / KR;
+      f32x4 sc = {0.f, 0.f, 0.f, 0.f}, z = {0.f, 0.f, 0.f, 0.f};
+      if (smin <= tmax) {
+  #pragma unroll
+        for (int kk = 0; kk < S::NC / 32; ++kk) {
+          const auto a = load_frag<BF16>(sQ + (16 * ti + (lane & 15)) * NS + kk * 32 + 8 * (lane >> 4));
+          const auto bq = load_frag<BF16>(sK + (16 * tj + (lane & 15)) * NS + kk * 32 + 8 * (lane >> 4));
+          mma<BF16>(sc, a, bq);
+        }
+  #pragma unroll
+        for (int kk = 0; kk < S::PC / 32; ++kk) {
+          const auto a = load_frag<BF16>(sY + (16 * ti + (lane & 15)) * PS + kk * 32 + 8 * (lane >> 4));
+          const auto bv = load_frag<BF16>(sV + (16 * tj + (lane & 15)) * PS + kk * 32 + 8 * (lane >> 4));
+          mma<BF16>(z, a, bv);
+        }
+      }
+      const int col = 16 * tj + (lane & 15), s = col / KR;
+      const float cds = __shfl(cd_l, s, kWave);
+      float csum = 0.f;
+  #pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = 16 * ti + 4 * (lane >> 4) + i, t = row / R;
+        const float cdt = __shfl(cd_l, t, kWave);
+        float m = 0.f;
+        if (s <= t) m = COORD ? 1.f : __expf(-Ah * (cdt - cds));
+        sSM[row * KS + col] = from_f32<T>(sc[i] * m);
+        sZM[row * KS + col] = from_f32<T>(z[i] * m);
+        if (!COORD) {
+          float wv = z[i] * sc[i] * m;
+          // row sum over the 16 columns of this tile
+          float rs = wv;
+  #pragma unroll
+          for (int off = 1; off < 16; off <<= 1) rs += __shfl_xor(rs, off, kWave);
+          if ((lane & 15) == 0) sRS[wave][t] += rs;
+          csum += wv;
+        }
+      }
+      if (!COORD) {
+        csum += __shfl_xor(csum, 16, kWave);
+        csum += __shfl_xor(csum, 32, kWave);
+  #pragma unroll
+        for (int off = 1; off < KR; off <<= 1) csum += __shfl_xor(csum, off, kWave);
+        if (lane < 16 && (lane % KR) == 0) sCS[wave][s] += csum;
+      }
+    }
+    __syncthreads();
+
+    // ---------------------------------------------------------------- dV -> dX
+    for (int tile = wave; tile < S::TK * S::TP; tile += NW) {
+      const int tj = tile / S::TP, tp = tile % S::TP;
+      f32x4 ai = {0.f, 0.f, 0.f, 0.f}, ae = {0.f, 0.f, 0.f, 0.f};
+  #pragma unroll
+      for (int kk = 0; kk < S::QOC / 32; ++kk) {
+        const auto a = load_frag_tr<BF16>(sSM + (kk * 32) * KS + 16 * tj, KS);
+        const auto bq = load_frag_tr<BF16>(sY + (kk * 32) * PS + 16 * tp, PS);
+        mma<BF16>(ai, a, bq);
+      }
+  #pragma unroll
+      for (int kk = 0; kk < S::NC / 32; ++kk) {
+        const auto a = load_frag<BF16>((COORD ? sKe : sK) + (16 * tj + (lane & 15)) * NS + kk * 32 + 8 * (lane >> 4));
+        if (kk * 32 < N) {
+          const auto bh = load_frag_tr<BF16>(sGh + (kk * 32) * PS + 16 * tp, PS);
+          const auto bl = load_frag_tr<BF16>(sGl + (kk * 32) * PS + 16 * tp, PS);
+          mma<BF16>(ae, a, bh);
+          mma<BF16>(ae, a, bl);
+        }
+      }
+      const int pp = 16 * tp + (lane & 15);
+  #pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int j = 16 * tj + 4 * (lane >> 4) + i;
+        const int s = j / KR, kr = j % KR;
+        const float wj = COORD ? 1.f : __shfl(w_l, s, kWave);
+        const float dv = ai[i] + wj * ae[i];
+        if (!S::TE) {
+          const int t = t0 + s;
+          const float val = dv + (p.has_D ? Dh * to_f32(sY[(s * R + kr) * PS + pp]) : 0.f);
+          if (t < L) dxg[((((size_t)b * L + t) * H + h) * R + kr) * P + pp] = from_f32<T>(val);
+        } else if (kr < R) {
+          sDX[((s + 1) * R + kr) * P + pp] = dv;                       // gamma row -> X_s
+        } else if (s >= 1) {
+          sDX[(QT + 1) * R * P + (s * R + kr - R) * P + pp] = dv;      // beta row -> X_{s-1}
+        }
+      }
+    }
+
+    // ---------------------------------------------------------------- dK~ -> dB, dbeta, dgamma
+    for (int tile = wave; tile < S::TN * S::TK; tile += NW) {
+      const int tnn = tile / S::TK, tj = tile % S::TK;
+      f32x4 ai = {0.f, 0.f, 0.f, 0.f}, ae = {0.f, 0.f, 0.f, 0.f};
+  #pragma unroll
+      for (int kk = 0; kk < S::QOC / 32; ++kk) {
+        const auto a = load_frag_tr<BF16>(sQ + (kk * 32) * NS + 16 * tnn, NS);
+        const auto bz = load_frag_tr<BF16>(sZM + (kk * 32) * KS + 16 * tj, KS);
+        mma<BF16>(ai, a, bz);
+      }
+  #pragma unroll
+      for (int kk = 0; kk < S::PC / 32; ++kk) {
+        const auto bv = load_frag<BF16>(sV + (16 * tj + (lane & 15)) * PS + kk * 32 + 8 * (lane >> 4));
+        const auto ah = load_frag<BF16>(sGh + (16 * tnn + (lane & 15)) * PS + kk * 32 + 8 * (lane >> 4));
+        const auto al = load_frag<BF16>(sGl + (16 * tnn + (lane & 15)) * PS + kk * 32 + 8 * (lane >> 4));
+        mma<BF16>(ae, ah, bv);
+        mma<BF16>(ae, al, bv);
+      }
+      const int j = 16 * tj + (lane & 15), s = j / KR, kr = j % KR;
+      const float cds = __shfl(cd_l, s, kWave);
+      const float wj = COORD ? 1.f : __shfl(w_l, s, kWave);
+      const float gam = S::TE ? __shfl(ga_l, s, kWave) : 1.f;
+      const float bet = S::TE ? __shfl(be_l, s, kWave) : 0.f;
+      const bool brow = S::TE && kr >= R;
+      const int rr = brow ? kr - R : kr;
+      const int tb = t0 + (brow ? s - 1 : s);  // token whose B row this key carries
+      float tokacc = 0.f, dgb = 0.f;
+      float dk[4], kv[4], rpa[4], rek[4], rpw[2] = {0.f, 0.f}, rekt[2] = {0.f, 0.f};
+  #pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int n = 16 * tnn + 4 * (lane >> 4) + i;
+        kv[i] = to_f32(sK[j * NS + n]);
+        rpa[i] = 0.f; rek[i] = 0.f;
+        if (COORD) {
+          const float er = __expf(-sRate[n] * 0.5f * cdend);  // e^{r_n}
+          const float ck = ai[i] + er * ae[i];
+          dk[i] = __expf(-sRate[n] * (0.5f * cdend - cds)) * ck;  // e^{r - L_s} ck  (dK~)
+          // source terms: -k o cK  (rows); the inter part also feeds the final-state term
+          const float dr = -kv[i] * ck;
+          tokacc += -sRate[n] * dr;
+          rpa[i] = -cds * dr;
+          rek[i] = kv[i] * er * ae[i];
+        } else {
+          dk[i] = ai[i] + wj * ae[i];
+          tokacc += kv[i] * wj * ae[i];  // K~ o dK~ (inter part)
+        }
+      }
+      if (COORD) {
+  #pragma unroll
+        for (int i = 0; i < 4; i += 2) {
           const int n = 16 * tnn + 4 * (lane >> 4) + i;
-          sPA[wave][n] += rpa[i];
-          sEK[wave][n] += rek[i];
-          if ((i & 1) == 0 && n >= nreal) {
-            sPW[wave][(n - nreal) >> 1] += rpw[i >> 1];
-            sEKth[wave][(n - nreal) >> 1] += rekt[i >> 1];
+          if (n >= nreal) {
+            const int kp = (n - nreal) >> 1;
+            const float er = __expf(-sRate[n] * 0.5f * cdend);
+            const float ca = ai[i] + er * ae[i], cb = ai[i + 1] + er * ae[i + 1];
+            // K~^T J dK~ in scaled form: -k_a cK_b + k_b cK_a
+            const float dth = -kv[i] * cb + kv[i + 1] * ca;
+            tokacc += sOmega[kp] * dth;
+            rpw[i >> 1] = cds * dth;
+            rekt[i >> 1] = -(-kv[i] * er * ae[i + 1] + kv[i + 1] * er * ae[i]);
+            // unfold the rotation of the key: u = R(+Theta_s) dK~
+            float sn, cs;
+            fast_sincos(sOmega[kp] * cds, &sn, &cs);
+            const float a0 = dk[i], a1 = dk[i + 1];
+            dk[i] = cs * a0 - sn * a1;
+            dk[i + 1] = sn * a0 + cs * a1;
           }
         }
       }
-    }
-    // per-key sums over the 4 row groups, then over the keys of one token
-    tokacc += __shfl_xor(tokacc, 16, kWave);
-    tokacc += __shfl_xor(tokacc, 32, kWave);
-    dgb += __shfl_xor(dgb, 16, kWave);
-    dgb += __shfl_xor(dgb, 32, kWave);
-#pragma unroll
-    for (int off = 1; off < R; off <<= 1) dgb += __shfl_xor(dgb, off, kWave);
-#pragma unroll
-    for (int off = 1; off < KR; off <<= 1) tokacc += __shfl_xor(tokacc, off, kWave);
-    if (lane < 16) {
-      if ((lane % KR) == 0) {
-        if (COORD) sTok[wave][s] += tokacc;  // weighted source contribution
-        else sSrc[wave][s] += tokacc;        // K~ o dK~ (inter), unweighted
+      // gradient w.r.t. the stored B row and the endpoint weights
+      const bool own = !(brow && s == 0) && tb < L;  // the halo row's B belongs to the previous chunk
+      float braw[4];
+      {
+        const int tbc = tb < 0 ? 0 : tb;
+        const int n0 = 16 * tnn + 4 * (lane >> 4);
+        const T* src = Bg + ((((size_t)b * L + tbc) * G + g) * R + rr) * N + n0;
+  #pragma unroll
+        for (int i = 0; i < 4; ++i) braw[i] = (tb >= 0 && tb < L) ? to_f32(src[i]) : 0.f;
       }
-      if (S::TE && (lane % R) == 0) {
-        if (brow) sDb[wave][s] += dgb;
-        else sDg[wave][s] += dgb;
+  #pragma unroll
+      for (int i = 0; i < 4; ++i) dgb += dk[i] * braw[i];
+      const float wgt = brow ? bet : gam;
+      if (!S::TE) {
+        if (own) {
+          const int n0 = 16 * tnn + 4 * (lane >> 4);
+          T* dst = dBg + ((((size_t)b * L + tb) * G + g) * R + rr) * N + n0;
+  #pragma unroll
+          for (int i = 0; i < 4; ++i) dst[i] = from_f32<T>(dk[i]);
+        }
+      } else {
+        const int n0 = 16 * tnn + 4 * (lane >> 4);
+        if (!brow) {
+  #pragma unroll
+          for (int i = 0; i < 4; ++i) sDB[((s + 1) * R + rr) * N + n0 + i] = wgt * dk[i];
+        } else if (s >= 1) {
+  #pragma unroll
+          for (int i = 0; i < 4; ++i) sDB[(QT + 1) * R * N + (s * R + rr) * N + n0 + i] = wgt * dk[i];
+        }
       }
-    }
-  }
-
-  // ---------------------------------------------------------------- dC~ -> dC
-  for (int tile = wave; tile < S::TN * S::TQ; tile += NW) {
-    const int tnn = tile / S::TQ, tq = tile % S::TQ;
-    f32x4 ai = {0.f, 0.f, 0.f, 0.f}, ae = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kk = 0; kk < QK / 32; ++kk) {
-      const auto a = load_frag_tr<BF16>(sK + (kk * 32) * NS + 16 * tnn, NS);
-      const auto bz = load_frag<BF16>(sZM + (16 * tq + (lane & 15)) * KS + kk * 32 + 8 * (lane >> 4));
-      mma<BF16>(ai, a, bz);
-    }
-#pragma unroll
-    for (int kk = 0; kk < S::PC / 32; ++kk) {
-      const auto by = load_frag<BF16>(sY + (16 * tq + (lane & 15)) * PS + kk * 32 + 8 * (lane >> 4));
-      const auto ah = load_frag<BF16>(sSh + (16 * tnn + (lane & 15)) * PS + kk * 32 + 8 * (lane >> 4));
-      const auto al = load_frag<BF16>(sSl + (16 * tnn + (lane & 15)) * PS + kk * 32 + 8 * (lane >> 4));
-      mma<BF16>(ae, ah, by);
-      mma<BF16>(ae, al, by);
-    }
-    const int row = 16 * tq + (lane & 15), t = row / R, o = row % R, tg = t0 + t;
-    const float cdt = __shfl(cd_l, t, kWave);
-    const float elt = COORD ? 0.f : __shfl(el_l, t, kWave);
-    float tokacc = 0.f, dc[4], qv[4], rpa[4], rpw[2] = {0.f, 0.f};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int n = 16 * tnn + 4 * (lane >> 4) + i;
-      qv[i] = to_f32(sQ[row * NS + n]);
-      rpa[i] = 0.f;
       if (COORD) {
-        const float er = __expf(-sRate[n] * 0.5f * cdend);
-        const float cc = ai[i] + er * ae[i];
-        dc[i] = __expf(-sRate[n] * (cdt - 0.5f * cdend)) * cc;
-        const float dr = qv[i] * cc;
-        tokacc += -sRate[n] * dr;
-        rpa[i] = -cdt * dr;
-      } else {
-        dc[i] = ai[i] + elt * ae[i];
-        tokacc += qv[i] * elt * ae[i];  // C~ o dC~ (inter part)
-      }
-    }
-    if (COORD) {
-#pragma unroll
-      for (int i = 0; i < 4; i += 2) {
-        const int n = 16 * tnn + 4 * (lane >> 4) + i;
-        if (n >= nreal) {
-          const int kp = (n - nreal) >> 1;
-          const float er = __expf(-sRate[n] * 0.5f * cdend);
-          const float ca = ai[i] + er * ae[i], cb = ai[i + 1] + er * ae[i + 1];
-          const float dth = -qv[i] * cb + qv[i + 1] * ca;  // C~^T J dC~ (scaled form)
-          tokacc += sOmega[kp] * dth;
-          rpw[i >> 1] = cdt * dth;
-          float sn, cs;
-          fast_sincos(sOmega[kp] * cdt, &sn, &cs);
-          const float a0 = dc[i], a1 = dc[i + 1];
-          dc[i] = cs * a0 - sn * a1;
-          dc[i + 1] = sn * a0 + cs * a1;
-        }
-      }
-    }
-    if (tg < L) {
-      const int n0 = 16 * tnn + 4 * (lane >> 4);
-      T* dst = dCg + ((((size_t)b * L + tg) * G + g) * R + o) * N + n0;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) dst[i] = from_f32<T>(dc[i]);
-    }
-    if (COORD) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-#pragma unroll
-        for (int off = 1; off < 16; off <<= 1) rpa[i] += __shfl_xor(rpa[i], off, kWave);
-      }
-#pragma unroll
-      for (int q = 0; q < 2; ++q) {
-#pragma unroll
-        for (int off = 1; off < 16; off <<= 1) rpw[q] += __shfl_xor(rpw[q], off, kWave);
-      }
-      if ((lane & 15) == 0) {
-#pragma unroll
+        // per-row sums over the 16 key columns of this tile
+  #pragma unroll
         for (int i = 0; i < 4; ++i) {
+  #pragma unroll
+          for (int off = 1; off < 16; off <<= 1) {
+            rpa[i] += __shfl_xor(rpa[i], off, kWave);
+            rek[i] += __shfl_xor(rek[i], off, kWave);
+          }
+        }
+  #pragma unroll
+        for (int q = 0; q < 2; ++q) {
+  #pragma unroll
+          for (int off = 1; off < 16; off <<= 1) {
+            rpw[q] += __shfl_xor(rpw[q], off, kWave);
+            rekt[q] += __shfl_xor(rekt[q], off, kWave);
+          }
+        }
+        if ((lane & 15) == 0) {
+  #pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int n = 16 * tnn + 4 * (lane >> 4) + i;
+            sPA[wave][n] += rpa[i];
+            sEK[wave][n] += rek[i];
+            if ((i & 1) == 0 && n >= nreal) {
+              sPW[wave][(n - nreal) >> 1] += rpw[i >> 1];
+              sEKth[wave][(n - nreal) >> 1] += rekt[i >> 1];
+            }
+          }
+        }
+      }
+      // per-key sums over the 4 row groups, then over the keys of one token
+      tokacc += __shfl_xor(tokacc, 16, kWave);
+      tokacc += __shfl_xor(tokacc, 32, kWave);
+      dgb += __shfl_xor(dgb, 16, kWave);
+      dgb += __shfl_xor(dgb, 32, kWave);
+  #pragma unroll
+      for (int off = 1; off < R; off <<= 1) dgb += __shfl_xor(dgb, off, kWave);
+  #pragma unroll
+      for (int off = 1; off < KR; off <<= 1) tokacc += __shfl_xor(tokacc, off, kWave);
+      if (lane < 16) {
+        if ((lane % KR) == 0) {
+          if (COORD) sTok[wave][s] += tokacc;  // weighted source contribution
+          else sSrc[wave][s] += tokacc;        // K~ o dK~ (inter), unweighted
+        }
+        if (S::TE && (lane % R) == 0) {
+          if (brow) sDb[wave][s] += dgb;
+          else sDg[wave][s] += dgb;
+        }
+      }
+    }
+
+    // ---------------------------------------------------------------- dC~ -> dC
+    for (int tile = wave; tile < S::TN * S::TQ; tile += NW) {
+      const int tnn = tile / S::TQ, tq = tile % S::TQ;
+      f32x4 ai = {0.f, 0.f, 0.f, 0.f}, ae = {0.f, 0.f, 0.f, 0.f};
+  #pragma unroll
+      for (int kk = 0; kk < QK / 32; ++kk) {
+        const auto a = load_frag_tr<BF16>(sK + (kk * 32) * NS + 16 * tnn, NS);
+        const auto bz = load_frag<BF16>(sZM + (16 * tq + (lane & 15)) * KS + kk * 32 + 8 * (lane >> 4));
+        mma<BF16>(ai, a, bz);
+      }
+  #pragma unroll
+      for (int kk = 0; kk < S::PC / 32; ++kk) {
+        const auto by = load_frag<BF16>(sY + (16 * tq + (lane & 15)) * PS + kk * 32 + 8 * (lane >> 4));
+        const auto ah = load_frag<BF16>(sSh + (16 * tnn + (lane & 15)) * PS + kk * 32 + 8 * (lane >> 4));
+        const auto al = load_frag<BF16>(sSl + (16 * tnn + (lane & 15)) * PS + kk * 32 + 8 * (lane >> 4));
+        mma<BF16>(ae, ah, by);
+        mma<BF16>(ae, al, by);
+      }
+      const int row = 16 * tq + (lane & 15), t = row / R, o = row % R, tg = t0 + t;
+      const float cdt = __shfl(cd_l, t, kWave);
+      const float elt = COORD ? 0.f : __shfl(el_l, t, kWave);
+      float tokacc = 0.f, dc[4], qv[4], rpa[4], rpw[2] = {0.f, 0.f};
+  #pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int n = 16 * tnn + 4 * (lane >> 4) + i;
+        qv[i] = to_f32(sQ[row * NS + n]);
+        rpa[i] = 0.f;
+        if (COORD) {
+          const float er = __expf(-sRate[n] * 0.5f * cdend);
+          const float cc = ai[i] + er * ae[i];
+          dc[i] = __expf(-sRate[n] * (cdt - 0.5f * cdend)) * cc;
+          const float dr = qv[i] * cc;
+          tokacc += -sRate[n] * dr;
+          rpa[i] = -cdt * dr;
+        } else {
+          dc[i] = ai[i] + elt * ae[i];
+          tokacc += qv[i] * elt * ae[i];  // C~ o dC~ (inter part)
+        }
+      }
+      if (COORD) {
+  #pragma unroll
+        for (int i = 0; i < 4; i += 2) {
           const int n = 16 * tnn + 4 * (lane >> 4) + i;
-          sPA[wave][n] += rpa[i];
-          if ((i & 1) == 0 && n >= nreal) sPW[wave][(n - nreal) >> 1] += rpw[i >> 1];
+          if (n >= nreal) {
+            const int kp = (n - nreal) >> 1;
+            const float er = __expf(-sRate[n] * 0.5f * cdend);
+            const float ca = ai[i] + er * ae[i], cb = ai[i + 1] + er * ae[i + 1];
+            const float dth = -qv[i] * cb + qv[i + 1] * ca;  // C~^T J dC~ (scaled form)
+            tokacc += sOmega[kp] * dth;
+            rpw[i >> 1] = cdt * dth;
+            float sn, cs;
+            fast_sincos(sOmega[kp] * cdt, &sn, &cs);
+            const float a0 = dc[i], a1 = dc[i + 1];
+            dc[i] = cs * a0 - sn * a1;
+            dc[i + 1] = sn * a0 + cs * a1;
+          }
         }
       }
-    }
-    tokacc += __shfl_xor(tokacc, 16, kWave);
-    tokacc += __shfl_xor(tokacc, 32, kWave);
-#pragma unroll
-    for (int off = 1; off < R; off <<= 1) tokacc += __shfl_xor(tokacc, off, kWave);
-    if (lane < 16 && (lane % R) == 0) {
-      if (COORD) sTok[wave][t] += tokacc;
-      else sTT[wave][t] += tokacc;
-    }
-  }
-  __syncthreads();
-
-  // ---------------------------------------------------------------- two-endpoint assembly
-  if (S::TE) {
-    for (int i = tid; i < QT * R * P; i += S::NTH) {
-      const int s = i / (R * P), rem = i % (R * P), r = rem / P, pp = rem % P;
-      const int t = t0 + s;
-      float v = sDX[((s + 1) * R + r) * P + pp];
-      if (s + 1 < QT) v += sDX[(QT + 1) * R * P + ((s + 1) * R + r) * P + pp];
-      else v += sTailX[r * P + pp];
-      if (p.has_D) v += Dh * to_f32(sY[(s * R + r) * PS + pp]);
-      if (t < L) dxg[((((size_t)b * L + t) * H + h) * R + r) * P + pp] = from_f32<T>(v);
-    }
-    for (int i = tid; i < QT * R * N; i += S::NTH) {
-      const int s = i / (R * N), rem = i % (R * N), r = rem / N, n = rem % N;
-      const int t = t0 + s;
-      float v = sDB[((s + 1) * R + r) * N + n];
-      if (s + 1 < QT) v += sDB[(QT + 1) * R * N + ((s + 1) * R + r) * N + n];
-      else v += sTailB[r * N + n];
-      if (t < L) dBg[((((size_t)b * L + t) * G + g) * R + r) * N + n] = from_f32<T>(v);
-    }
-  }
-
-  // ---------------------------------------------------------------- step gradient
-  // per-token d(loss)/d(L_t) contributions; the final-state term sits on the last
-  // position of the chunk; dDelta_r = sum_{t >= r} dcd_t (reverse cumsum).
-  if (wave == 0) {
-    float tok = 0.f, dunw = 0.f;  // weighted dcd_t, and (head) the unweighted D_t
-    float srcsum = 0.f, e = 0.f;
-    if (COORD) {
-      if (lane < QT) tok = wsum<WC>(sTok, lane);
-      float eterm = 0.f;
-      for (int n = lane; n < N; n += kWave) {
-        const float en = sE[n] + wsum<WC>(sEK, n);
-        eterm += -sRate[n] * en;
+      if (tg < L) {
+        const int n0 = 16 * tnn + 4 * (lane >> 4);
+        T* dst = dCg + ((((size_t)b * L + tg) * G + g) * R + o) * N + n0;
+  #pragma unroll
+        for (int i = 0; i < 4; ++i) dst[i] = from_f32<T>(dc[i]);
       }
-      for (int k = lane; k < npairs; k += kWave) {
-        const float et = sEth[k] + wsum<WC>(sEKth, k);
-        eterm += sOmega[k] * et;
-      }
-      eterm = wave_sum(eterm);
-      if (lane == QT - 1) tok += eterm;
-    } else {
-      float src = 0.f;
-      if (lane < QT) {
-        const float rs = wsum<WH>(sRS, lane);
-        const float cs = wsum<WH>(sCS, lane);
-        const float tt = wsum<WH>(sTT, lane);
-        src = wsum<WH>(sSrc, lane);
-        dunw = rs - cs + tt - src;
-      }
-      srcsum = wave_sum(src);
-      for (int n = lane; n < N; n += kWave) e += sE[n];
-      e = wave_sum(e);
-      if (lane == QT - 1) dunw += e + srcsum;
-      tok = -Ah * dunw;
-    }
-    const float tot = wave_sum(tok);
-    const float pre = wave_prefix_sum(tok);
-    const float rev = tot - pre + tok;
-    const int t = t0 + lane;
-    if (lane < QT && t < L) {
-      const size_t idx = ((size_t)b * L + t) * H + h;
-      p.ddt[idx] = p.softplus ? rev * sigmoid_f32(raw_l) : rev;
-      if (S::TE) {
-        if (p.dgamma) p.dgamma[idx] = wsum<WT>(sDg, lane);
-        if (p.dbeta) p.dbeta[idx] = wsum<WT>(sDb, lane);
-      }
-    }
-    if (!COORD && p.part) {
-      // dA_h partial = sum_t (-cd_t) D_t
-      const float v = wave_sum(lane < QT ? -cd_l * dunw : 0.f);
-      if (lane == 0) p.part[((size_t)slice * nch + c) * p.npart] = v;
-    }
-  }
-  // parameter partials of this chunk (per-row mode)
-  if (p.part) {
-    float* dst = p.part + ((size_t)slice * nch + c) * p.npart;
-    const int na = (COORD && !p.head_rates) ? nreal + npairs : 1;
-    if (COORD) {
-      __syncthreads();
-      for (int n = tid; n < N; n += S::NTH) {
-        const float en = sE[n] + wsum<WC>(sEK, n);
-        sEK[0][n] = wsum<WC>(sPA, n) + (-cdend) * en;
-      }
-      __syncthreads();
-      if (p.head_rates) {
-        if (wave == 0) {
-          float v = 0.f;
-          for (int n = lane; n < N; n += kWave) v += sEK[0][n];
-          v = wave_sum(v);
-          if (lane == 0) dst[0] = v;
+      if (COORD) {
+  #pragma unroll
+        for (int i = 0; i < 4; ++i) {
+  #pragma unroll
+          for (int off = 1; off < 16; off <<= 1) rpa[i] += __shfl_xor(rpa[i], off, kWave);
         }
-      } else {
-        for (int n = tid; n < nreal; n += S::NTH) dst[n] = sEK[0][n];
-        for (int k = tid; k < npairs; k += S::NTH) {
-          const int n = nreal + 2 * k;
-          dst[nreal + k] = sEK[0][n] + sEK[0][n + 1];
+  #pragma unroll
+        for (int q = 0; q < 2; ++q) {
+  #pragma unroll
+          for (int off = 1; off < 16; off <<= 1) rpw[q] += __shfl_xor(rpw[q], off, kWave);
+        }
+        if ((lane & 15) == 0) {
+  #pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int n = 16 * tnn + 4 * (lane >> 4) + i;
+            sPA[wave][n] += rpa[i];
+            if ((i & 1) == 0 && n >= nreal) sPW[wave][(n - nreal) >> 1] += rpw[i >> 1];
+          }
+        }
+      }
+      tokacc += __shfl_xor(tokacc, 16, kWave);
+      tokacc += __shfl_xor(tokacc, 32, kWave);
+  #pragma unroll
+      for (int off = 1; off < R; off <<= 1) tokacc += __shfl_xor(tokacc, off, kWave);
+      if (lane < 16 && (lane % R) == 0) {
+        if (COORD) sTok[wave][t] += tokacc;
+        else sTT[wave][t] += tokacc;
+      }
+    }
+    __syncthreads();
+
+    // ---------------------------------------------------------------- two-endpoint assembly
+    if (S::TE) {
+      for (int i = tid; i < QT * R * P; i += S::NTH) {
+        const int s = i / (R * P), rem = i % (R * P), r = rem / P, pp = rem % P;
+        const int t = t0 + s;
+        float v = sDX[((s + 1) * R + r) * P + pp];
+        if (s + 1 < QT) v += sDX[(QT + 1) * R * P + ((s + 1) * R + r) * P + pp];
+        else v += sTailX[r * P + pp];
+        if (p.has_D) v += Dh * to_f32(sY[(s * R + r) * PS + pp]);
+        if (t < L) dxg[((((size_t)b * L + t) * H + h) * R + r) * P + pp] = from_f32<T>(v);
+      }
+      for (int i = tid; i < QT * R * N; i += S::NTH) {
+        const int s = i / (R * N), rem = i % (R * N), r = rem / N, n = rem % N;
+        const int t = t0 + s;
+        float v = sDB[((s + 1) * R + r) * N + n];
+        if (s + 1 < QT) v += sDB[(QT + 1) * R * N + ((s + 1) * R + r) * N + n];
+        else v += sTailB[r * N + n];
+        if (t < L) dBg[((((size_t)b * L + t) * G + g) * R + r) * N + n] = from_f32<T>(v);
+      }
+    }
+
+    // ---------------------------------------------------------------- step gradient
+    // per-token d(loss)/d(L_t) contributions; the final-state term sits on the last
+    // position of the chunk; dDelta_r = sum_{t >= r} dcd_t (reverse cumsum).
+    if (wave == 0) {
+      float tok = 0.f, dunw = 0.f;  // weighted dcd_t, and (head) the unweighted D_t
+      float srcsum = 0.f, e = 0.f;
+      if (COORD) {
+        if (lane < QT) tok = wsum<WC>(sTok, lane);
+        float eterm = 0.f;
+        for (int n = lane; n < N; n += kWave) {
+          const float en = sE[n] + wsum<WC>(sEK, n);
+          eterm += -sRate[n] * en;
+        }
+        for (int k = lane; k < npairs; k += kWave) {
           const float et = sEth[k] + wsum<WC>(sEKth, k);
-          dst[na + k] = wsum<WC>(sPW, k) + cdend * et;
+          eterm += sOmega[k] * et;
+        }
+        eterm = wave_sum(eterm);
+        if (lane == QT - 1) tok += eterm;
+      } else {
+        float src = 0.f;
+        if (lane < QT) {
+          const float rs = wsum<WH>(sRS, lane);
+          const float cs = wsum<WH>(sCS, lane);
+          const float tt = wsum<WH>(sTT, lane);
+          src = wsum<WH>(sSrc, lane);
+          dunw = rs - cs + tt - src;
+        }
+        srcsum = wave_sum(src);
+        for (int n = lane; n < N; n += kWave) e += sE[n];
+        e = wave_sum(e);
+        if (lane == QT - 1) dunw += e + srcsum;
+        tok = -Ah * dunw;
+      }
+      const float tot = wave_sum(tok);
+      const float pre = wave_prefix_sum(tok);
+      const float rev = tot - pre + tok;
+      const int t = t0 + lane;
+      if (lane < QT && t < L) {
+        const size_t idx = ((size_t)b * L + t) * H + h;
+        p.ddt[idx] = p.softplus ? rev * sigmoid_f32(raw_l) : rev;
+        if (S::TE) {
+          if (p.dgamma) p.dgamma[idx] = wsum<WT>(sDg, lane);
+          if (p.dbeta) p.dbeta[idx] = wsum<WT>(sDb, lane);
         }
       }
+      if (!COORD && p.part) {
+        // dA_h partial = sum_t (-cd_t) D_t
+        const float v = wave_sum(lane < QT ? -cd_l * dunw : 0.f);
+        if (lane == 0) p.part[((size_t)slice * nch + c) * p.npart] = v;
+      }
     }
-    if (tid == 0) dst[na + npairs] = wsum1<NW>(sMisc);
-  }
+    // parameter partials of this chunk (per-row mode)
+    if (p.part) {
+      float* dst = p.part + ((size_t)slice * nch + c) * p.npart;
+      const int na = (COORD && !p.head_rates) ? nreal + npairs : 1;
+      if (COORD) {
+        __syncthreads();
+        for (int n = tid; n < N; n += S::NTH) {
+          const float en = sE[n] + wsum<WC>(sEK, n);
+          sEK[0][n] = wsum<WC>(sPA, n) + (-cdend) * en;
+        }
+        __syncthreads();
+        if (p.head_rates) {
+          if (wave == 0) {
+            float v = 0.f;
+            for (int n = lane; n < N; n += kWave) v += sEK[0][n];
+            v = wave_sum(v);
+            if (lane == 0) dst[0] = v;
+          }
+        } else {
+          for (int n = tid; n < nreal; n += S::NTH) dst[n] = sEK[0][n];
+          for (int k = tid; k < npairs; k += S::NTH) {
+            const int n = nreal + 2 * k;
+            dst[nreal + k] = sEK[0][n] + sEK[0][n + 1];
+            const float et = sEth[k] + wsum<WC>(sEKth, k);
+            dst[na + k] = wsum<WC>(sPW, k) + cdend * et;
+          }
+        }
+      }
+      if (tid == 0) dst[na + npairs] = wsum1<NW>(sMisc);
+    }
+  }  // items
 }
 
 // ============================================================== parameter sums
-__global__ void ssm_bwd_params(BwdParams p, int nA) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+// One wave per output: lane l sums the partials j = l, l + 64, ... of the (batch,
+// chunk) items in order, then a fixed butterfly combines the lanes, so the result
+// does not depend on timing.
+__global__ __launch_bounds__(256) void ssm_bwd_params(BwdParams p, int nA) {
+  const int i = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
   const int per_head = p.npart;
   if (i >= p.H * per_head) return;
   const int h = i / per_head, k = i % per_head;
+  const int nch = p.nchunks, items = p.batch * nch;
   float acc = 0.f;
-  for (int b = 0; b < p.batch; ++b) {
-    const float* src = p.part + ((size_t)(b * p.H + h) * p.nchunks) * per_head + k;
-    for (int c = 0; c < p.nchunks; ++c) acc += src[(size_t)c * per_head];
+  for (int j = lane; j < items; j += kWave) {
+    const int b = j / nch, c = j % nch;
+    acc += p.part[((size_t)(b * p.H + h) * nch + c) * per_head + k];
   }
+  acc = wave_sum(acc);
+  if (lane != 0) return;
   if (k < nA) {
     if (p.dA) p.dA[(size_t)h * nA + k] = acc;
   } else if (k < nA + p.n_pairs) {
@@ -1082,12 +1206,37 @@ bool bwd_variant_exists(const BwdKey& k) {
 #endif
 #define ADJ_PB(PP) (PP)
 
+// compute units of the current device (cached per device)
+static int device_cus() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  int v = cache[dev].load(std::memory_order_relaxed);
+  if (v <= 0) {
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
+      v = 256;
+    cache[dev].store(v, std::memory_order_relaxed);
+  }
+  return v;
+}
+
+// workgroups of `kernel` resident per compute unit (cached by the caller)
+static int blocks_per_cu(const void* kernel, int nthreads, std::atomic<int>& cache) {
+  int v = cache.load(std::memory_order_relaxed);
+  if (v <= 0) {
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, kernel, nthreads, 0) != hipSuccess || v <= 0)
+      v = 1;
+    cache.store(v, std::memory_order_relaxed);
+  }
+  return v;
+}
+
 hipError_t launch_bwd(const BwdKey& k, const BwdParams& p, hipStream_t stream,
                       void* const* events) {
   const int slices = p.batch * p.H;
   if (slices == 0 || p.nchunks == 0) return hipSuccess;
   auto mark = [&](int i) {
-    if (events && events[i]) hipEventRecord(static_cast<hipEvent_t>(events[i]), stream);
+    if (events && events[i]) (void)hipEventRecord(static_cast<hipEvent_t>(events[i]), stream);
   };
   const int nA = k.coord && !p.head_rates ? p.n_real + p.n_pairs : 1;
 #define SSM_BWD_LAUNCH(BF, NN, PP, RR, KRR, QTT, CO)                                          \
@@ -1098,10 +1247,17 @@ hipError_t launch_bwd(const BwdKey& k, const BwdParams& p, hipStream_t stream,
     hipLaunchKernelGGL((ssm_bwd_adjoint<BF, NN, PB, RR, QTT, CO, ADJ_NT>),                     \
                        dim3(slices * (PP / PB)), dim3(ADJ_NT), 0, stream, p);                 \
     mark(1);                                                                                  \
-    hipLaunchKernelGGL((ssm_bwd_chunk<BF, NN, PP, RR, KRR, QTT, CO, CHUNK_NT>),                \
-                       dim3(slices * p.nchunks), dim3(CHUNK_NT), 0, stream, p);               \
+    {                                                                                         \
+      static std::atomic<int> occ{0};                                                         \
+      const void* kfn = reinterpret_cast<const void*>(                                        \
+          &ssm_bwd_chunk<BF, NN, PP, RR, KRR, QTT, CO, CHUNK_NT>);                            \
+      const int items = slices * p.nchunks;                                                   \
+      const int grid = std::min(items, device_cus() * blocks_per_cu(kfn, CHUNK_NT, occ));      \
+      hipLaunchKernelGGL((ssm_bwd_chunk<BF, NN, PP, RR, KRR, QTT, CO, CHUNK_NT>), dim3(grid),  \
+                         dim3(CHUNK_NT), 0, stream, p);                                       \
+    }                                                                                         \
     mark(2);                                                                                  \
-    hipLaunchKernelGGL(ssm_bwd_params, dim3((p.H * p.npart + 255) / 256), dim3(256), 0,      \
+    hipLaunchKernelGGL(ssm_bwd_params, dim3((p.H * p.npart + 3) / 4), dim3(256), 0,          \
                        stream, p, nA);                                                        \
     mark(3);                                                                                  \
     return hipGetLastError();                                                                 \

@@ -158,6 +158,33 @@ __device__ __forceinline__ Frag<BF16> load_frag_tr(const typename Elem<BF16>::T*
   return f;
 }
 
+// four consecutive elements <-> floats (8 bytes bf16, 16 bytes fp32; aligned to that)
+template <bool BF16>
+__device__ __forceinline__ void store4(typename Elem<BF16>::T* dst, const float* v) {
+  if constexpr (BF16) {
+    uint2 w;
+    w.x = pack_bf16x2(v[0], v[1]);
+    w.y = pack_bf16x2(v[2], v[3]);
+    *reinterpret_cast<uint2*>(dst) = w;
+  } else {
+    *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
+  }
+}
+
+template <bool BF16>
+__device__ __forceinline__ void load4(const typename Elem<BF16>::T* src, float* v) {
+  if constexpr (BF16) {
+    const uint2 w = *reinterpret_cast<const uint2*>(src);
+    v[0] = __uint_as_float(w.x << 16);
+    v[1] = __uint_as_float(w.x & 0xffff0000u);
+    v[2] = __uint_as_float(w.y << 16);
+    v[3] = __uint_as_float(w.y & 0xffff0000u);
+  } else {
+    const float4 w = *reinterpret_cast<const float4*>(src);
+    v[0] = w.x; v[1] = w.y; v[2] = w.z; v[3] = w.w;
+  }
+}
+
 // acc += A(16x32) * B(32x16)
 template <bool BF16>
 __device__ __forceinline__ void mma(f32x4& acc, const Frag<BF16>& a, const Frag<BF16>& b) {
@@ -185,6 +212,11 @@ __device__ __forceinline__ float wave_prefix_sum(float v) {
   return v;
 }
 
+// value of the neighbouring lane (l ^ 1), by a DPP quad permutation [1, 0, 3, 2]
+__device__ __forceinline__ float swap_adjacent_lanes(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
@@ -195,9 +227,12 @@ __device__ __forceinline__ float wave_sum(float v) {
 // log(w) * u / (w - 1), w = 1 + u, which keeps full relative accuracy for tiny u.
 __device__ __forceinline__ float softplus_f32(float v) {
   if (v > 20.f) return v;
-  const float u = __expf(v);
+  const float u = __builtin_amdgcn_exp2f(v * 1.4426950408889634f);
   const float w = 1.f + u;
-  return (w == 1.f) ? u : __logf(w) * (u / (w - 1.f));
+  // w >= 1 is a normal number, so the raw hardware log2 is exact to its ulp bound
+  return (w == 1.f) ? u
+                    : __builtin_amdgcn_logf(w) * 0.6931471805599453f * u *
+                          __builtin_amdgcn_rcpf(w - 1.f);
 }
 
 // sin and cos of an angle in radians: reduce to revolutions in [-1/2, 1/2], then

@@ -1,9 +1,13 @@
 // ssm_fwd.hip -- forward chunked scan of the state-mediated selective SSM kernel
 // for gfx950 (MI355X).
 //
-// One workgroup (4 waves) owns one (batch, head) slice and one block of PB value
-// columns, and walks the sequence chunk by chunk with the N x PB state held in
-// MFMA accumulator registers (fp32).  Per chunk of QT tokens:
+// One workgroup owns one (batch, head) slice and one block of PB value columns,
+// and walks the sequence chunk by chunk with the N x PB state held in MFMA
+// accumulator registers (fp32).  Score, output and state tiles are computed
+// transposed (operands swapped), so that each lane holds four consecutive keys or
+// value columns: one decay factor per lane, 8-byte LDS and global writes.  One
+// wave forms the next chunk's per-token factors while the others compute scores.
+// Per chunk of QT tokens:
 //
 //  a1  chunk-local cumulative step CD_t = sum_{r<=t} Delta_r by a wave prefix sum
 //      (Delta = softplus(dt) when flagged); the log-decay of row n is
@@ -43,7 +47,7 @@ struct FwdShape {
   static constexpr int TEH = TE ? 1 : 0;
   static constexpr int NS = NC + PAD;  // row stride of n-contiguous buffers
   static constexpr int KS = QK + PAD;  // row stride of key-contiguous buffers (scores)
-  static constexpr int VS = PB + PAD;  // row stride of value buffers
+  static constexpr int VS = PB + PAD;  // row stride of p-contiguous buffers (values, state)
   static constexpr int BROWS = (QT + TEH) * R;
   static constexpr int NTH = NTHREADS;
   static constexpr int NW = NTHREADS / 64;  // waves per workgroup
@@ -58,9 +62,22 @@ struct FwdShape {
   static constexpr int TQ = QO / 16, TK = QK / 16, TP = PB / 16, TN = N / 16;
   static constexpr int ST_TILES = TN * TP;
   static constexpr int ST_PER_WAVE = (ST_TILES + NW - 1) / NW;
+  // score tiles (16 query rows ti x 16 keys tj) that hold at least one causal
+  // entry: key token floor(16 tj / KR) <= query token floor((16 ti + 15) / R)
+  static constexpr int row_tiles(int ti) {
+    const int c = (((16 * ti + 15) / R) * KR) / 16 + 1;
+    return c < TK ? c : TK;
+  }
+  static constexpr int score_tiles() {
+    int n = 0;
+    for (int ti = 0; ti < TQ; ++ti) n += row_tiles(ti);
+    return n;
+  }
+  static constexpr int SC_TILES = score_tiles();
   static_assert(QO % 16 == 0 && QK % 32 == 0, "chunk rows must fill MFMA tiles");
   static_assert(N % 16 == 0 && PB % 16 == 0 && QT <= 64, "unsupported tile shape");
   static_assert(KR == R || KR == 2 * R, "keys per token are R or 2R");
+  static_assert(16 % KR == 0 && 16 % R == 0, "a tile spans whole tokens");
 };
 
 template <bool BF16, int N, int PB, int R, int KR, int QT, bool COORD, int NTHREADS>
@@ -70,6 +87,8 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
   constexpr int NW = S::NW;
   constexpr int NS = S::NS, KS = S::KS, VS = S::VS, VEC = S::VEC;
   constexpr int QSZ = S::QO * NS, KSZ = S::QK * NS, VSZ = S::QK * S::VS;
+  constexpr float kLog2e = 1.4426950408889634f;
+  constexpr int PW = NW - 1;  // the wave that computes the per-token factors
 
   // double-buffered chunk operands: chunk c is consumed while chunk c+1 is staged
   __shared__ __align__(16) T sQ[2 * QSZ];                     // queries (folded; per-row: scaled)
@@ -78,9 +97,15 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
   __shared__ __align__(16) T sKe[COORD ? 2 * KSZ : 8];        // per-row: keys scaled to the chunk end
   __shared__ __align__(16) T sV[2 * VSZ];                     // values, natural [key row][p]
   __shared__ __align__(16) T sVw[COORD ? 8 : 2 * VSZ];        // head: values scaled to the chunk end
-  __shared__ __align__(16) T sS[S::QO * KS];                  // masked scores of the current chunk
-  __shared__ __align__(16) T sST[PB * NS];                    // state entering the current chunk (bf16)
-  __shared__ float sCD[2][64], sEL[2][64], sMisc[2][4];
+  __shared__ __align__(16) T sS[S::QO * KS];                  // masked scores [query row][key]
+  __shared__ __align__(16) T sST[S::NC * VS];                 // state entering the chunk [n][p]
+  // per-token factors of a chunk (double-buffered, written by wave PW one chunk ahead)
+  __shared__ __align__(16) float sCD[2][64];   // cumulative step inside the chunk
+  __shared__ __align__(16) float sLC[2][64];   // head: -A CD log2(e)
+  __shared__ __align__(16) float sEL[2][64];   // head: e^{-A CD}
+  __shared__ __align__(16) float sW[2][64];    // head: e^{-A (CD_end - CD)}
+  __shared__ __align__(16) float sGa[2][S::TE ? 64 : 1], sBe[2][S::TE ? 64 : 1];
+  __shared__ float sMisc[2][2];                // CD_end, head: e^{-A CD_end}
   __shared__ float sRate[N], sOmega[N / 2 + 1];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -103,8 +128,10 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
     }
     for (int k = tid; k < p.n_pairs; k += S::NTH) sOmega[k] = p.omega[(size_t)h * p.n_pairs + k];
   }
-  // zero the state copy and the contraction padding columns of both buffers
-  for (int i = tid; i < PB * NS; i += S::NTH) sST[i] = T(0);
+  // the state entering chunk 0 is zero, and so are its padding rows n >= N for good;
+  // score entries above the causal diagonal are zero and never rewritten
+  for (int i = tid; i < S::NC * VS; i += S::NTH) sST[i] = T(0);
+  for (int i = tid; i < S::QO * KS; i += S::NTH) sS[i] = T(0);
   if (S::NC > N) {
     for (int i = tid; i < 2 * S::QO * (S::NC - N); i += S::NTH) {
       const int r = i / (S::NC - N), c = N + i % (S::NC - N);
@@ -114,6 +141,7 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
     for (int i = tid; i < 2 * S::QK * (S::NC - N); i += S::NTH) {
       const int r = i / (S::NC - N), c = N + i % (S::NC - N);
       sK[r * NS + c] = T(0);
+      if (COORD) sKe[r * NS + c] = T(0);
     }
   }
   const float Ah = COORD ? 0.f : p.A[h];
@@ -130,6 +158,7 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
   const float* gag = S::TE ? p.gamma + (size_t)b * L * H + h : nullptr;
   const int tsG = G * R * N, tsH = H * R * P;  // per-token strides
 
+  // state tiles, transposed: st[k][i] = S[n = 16 tn + (lane & 15)][p = 16 tp + 4 (lane >> 4) + i]
   f32x4 st[S::ST_PER_WAVE];
 #pragma unroll
   for (int k = 0; k < S::ST_PER_WAVE; ++k) st[k] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -173,7 +202,7 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
       }
       rx[k] = val;
     }
-    {
+    if (wave == PW) {
       const int t = t0 + lane;
       const bool ok = lane < QT && t < L;
       rdt = ok ? dtg[t * H] : 0.f;
@@ -181,6 +210,32 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
         rbe = ok ? beg[t * H] : 0.f;
         rga = ok ? gag[t * H] : 0.f;
       }
+    }
+  };
+
+  // ---- a1: per-token factors of chunk c into buffer bi (wave PW only; lane = token)
+  auto factors = [&](int c, int bi) {
+    const int t0 = c * QT;
+    float dl = 0.f;
+    if (lane < QT && t0 + lane < L) dl = p.softplus ? softplus_f32(rdt) : rdt;
+    const float cd = wave_prefix_sum(dl);
+    const float cdend = __shfl(cd, QT - 1, kWave);
+    if (lane < QT) {
+      sCD[bi][lane] = cd;
+      if (!COORD) {
+        const float lc = -Ah * kLog2e * cd;
+        sLC[bi][lane] = lc;
+        sEL[bi][lane] = __builtin_amdgcn_exp2f(lc);
+        sW[bi][lane] = __builtin_amdgcn_exp2f(-Ah * kLog2e * (cdend - cd));
+      }
+      if (S::TE) {
+        sGa[bi][lane] = rga;
+        sBe[bi][lane] = rbe;
+      }
+    }
+    if (lane == 0) {
+      sMisc[bi][0] = cdend;
+      sMisc[bi][1] = COORD ? 0.f : __builtin_amdgcn_exp2f(-Ah * kLog2e * cdend);
     }
   };
 
@@ -200,26 +255,11 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
     }
   };
 
-  // ---- a1 + a2: prefix of the step (every wave, lane = token) and the operands of
-  // the chunk held in registers, written into buffer `bi`
+  // ---- a2: the operands of chunk c (held in registers) into buffer bi, using the
+  // chunk's per-token factors
   auto stage = [&](int c, int bi) {
-    const int t0 = c * QT;
-    float dl = 0.f;
-    if (lane < QT && t0 + lane < L) dl = p.softplus ? softplus_f32(rdt) : rdt;
-    const float cd_l = wave_prefix_sum(dl);
-    const float cdend = __shfl(cd_l, QT - 1, kWave);
-    const float w_l = COORD ? 0.f : __expf(-Ah * (cdend - cd_l));
-    const float be_l = rbe, ga_l = rga;
-    if (wave == 0) {
-      if (lane < QT) {
-        sCD[bi][lane] = cd_l;
-        if (!COORD) sEL[bi][lane] = __expf(-Ah * cd_l);
-      }
-      if (lane == 0) {
-        sMisc[bi][0] = cdend;
-        sMisc[bi][1] = COORD ? 0.f : __expf(-Ah * cdend);
-      }
-    }
+    (void)c;
+    const float cdend = sMisc[bi][0];
     T* q = sQ + bi * QSZ;
     T* qe = sQe + (COORD ? bi * QSZ : 0);
     T* kb = sK + bi * KSZ;
@@ -229,12 +269,11 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
 #pragma unroll
     for (int k = 0; k < S::C_PER; ++k) {
       const int v = tid + S::NTH * k;
-      const int crow = (v < S::C_VECS ? v : 0) / S::NVEC_N;
-      const float cd_c = COORD ? __shfl(cd_l, crow / R, kWave) : 0.f;
       if (v < S::C_VECS) {
         const int row = v / S::NVEC_N, nv = v % S::NVEC_N;
         const int n0 = nv * VEC;
         if (COORD) {
+          const float cd_c = sCD[bi][row / R];
           float vals[VEC], qq[VEC], qqe[VEC];
           unpack<BF16>(rc[k], vals);
           unrotate(vals, n0, cd_c);
@@ -254,16 +293,14 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
 #pragma unroll
     for (int k = 0; k < S::B_PER; ++k) {
       const int v = tid + S::NTH * k;
-      const int brow = (v < S::B_VECS ? v : 0) / S::NVEC_N;
-      const int bsl = brow / R - S::TEH;
-      const int tau0 = bsl < 0 ? 0 : bsl, tau1 = bsl + 1 < QT ? bsl + 1 : QT - 1;
-      const float cdt[2] = {__shfl(cd_l, tau0, kWave), __shfl(cd_l, tau1, kWave)};
-      const float gbt[2] = {S::TE ? __shfl(ga_l, tau0, kWave) : 1.f,
-                            S::TE ? __shfl(be_l, tau1, kWave) : 0.f};
       if (v < S::B_VECS) {
         const int row = v / S::NVEC_N, nv = v % S::NVEC_N;
         const int n0 = nv * VEC;
         const int sl = row / R - S::TEH, r = row % R;
+        if (!COORD && !S::TE) {
+          *reinterpret_cast<uint4*>(kb + (sl * KR + r) * NS + n0) = rb[k];
+          continue;
+        }
         float vals[VEC];
         unpack<BF16>(rb[k], vals);
 #pragma unroll
@@ -273,16 +310,18 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
           const int tau = sl + e;
           if (tau < 0 || tau >= QT || (e == 0 && sl < 0)) continue;
           const int j = tau * KR + (e ? R : 0) + r;
+          const float gb = S::TE ? (e ? sBe[bi][tau] : sGa[bi][tau]) : 1.f;
           float u[VEC], kk[VEC], ke[VEC];
 #pragma unroll
-          for (int i = 0; i < VEC; ++i) u[i] = vals[i] * gbt[e];
+          for (int i = 0; i < VEC; ++i) u[i] = vals[i] * gb;
           if (COORD) {
-            unrotate(u, n0, cdt[e]);
+            const float cdt = sCD[bi][tau];
+            unrotate(u, n0, cdt);
 #pragma unroll
             for (int i = 0; i < VEC; ++i) {
               const float ar = sRate[n0 + i];
-              kk[i] = u[i] * __expf(-ar * (0.5f * cdend - cdt[e]));
-              ke[i] = u[i] * __expf(-ar * (cdend - cdt[e]));
+              kk[i] = u[i] * __expf(-ar * (0.5f * cdend - cdt));
+              ke[i] = u[i] * __expf(-ar * (cdend - cdt));
             }
             *reinterpret_cast<uint4*>(keb + j * NS + n0) = pack<BF16>(ke);
           } else {
@@ -296,11 +335,6 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
 #pragma unroll
     for (int k = 0; k < S::X_PER; ++k) {
       const int v = tid + S::NTH * k;
-      const int xrow = (v < S::X_VECS ? v : 0) / S::NVEC_P;
-      const int xsl = xrow / R - S::TEH;
-      const int xt0 = xsl < 0 ? 0 : xsl, xt1 = xsl + 1 < QT ? xsl + 1 : QT - 1;
-      const float xw[2] = {COORD ? 0.f : __shfl(w_l, xt0, kWave),
-                           COORD ? 0.f : __shfl(w_l, xt1, kWave)};
       if (v < S::X_VECS) {
         const int row = v / S::NVEC_P, pv = v % S::NVEC_P;
         const int sl = row / R - S::TEH, r = row % R;
@@ -312,10 +346,11 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
           const int j = tau * KR + (e ? R : 0) + r;
           *reinterpret_cast<uint4*>(vb + j * VS + pv * VEC) = rx[k];
           if (!COORD) {
+            const float w = sW[bi][tau];
             float xv[VEC];
             unpack<BF16>(rx[k], xv);
 #pragma unroll
-            for (int i = 0; i < VEC; ++i) xv[i] *= xw[e];
+            for (int i = 0; i < VEC; ++i) xv[i] *= w;
             *reinterpret_cast<uint4*>(vwb + j * VS + pv * VEC) = pack<BF16>(xv);
           }
         }
@@ -334,6 +369,8 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
   }
 
   load_chunk(0);
+  if (wave == PW) factors(0, 0);
+  __syncthreads();
   stage(0, 0);
   if (nch > 1) load_chunk(1);
   __syncthreads();
@@ -348,69 +385,81 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
     const T* vb = sV + bi * VSZ;
     const T* vwb = sVw + (COORD ? 0 : bi * VSZ);
 
-    // ---- phase 1 -- a3: masked intra-chunk scores of chunk c
-    for (int tile = wave; tile < S::TQ * S::TK; tile += NW) {
-      const int ti = tile / S::TK, tj = tile % S::TK;
-      const int tmax = (16 * ti + 15) / R;
-      const int smin = (16 * tj) / KR;
+    // ---- phase 1 -- a3: masked intra-chunk scores of chunk c (computed transposed:
+    // lane l holds query row 16 ti + (l & 15) against keys 16 tj + 4 (l >> 4) + i);
+    // wave PW also forms the per-token factors of chunk c+1
+    for (int tile = wave; tile < S::SC_TILES; tile += NW) {
+      int ti = 0, tj = tile;
+#pragma unroll
+      for (int a = 0; a < S::TQ - 1; ++a) {
+        if (tj >= S::row_tiles(ti)) {
+          tj -= S::row_tiles(ti);
+          ++ti;
+        }
+      }
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      if (smin <= tmax) {
 #pragma unroll
-        for (int kk = 0; kk < S::NC / 32; ++kk) {
-          const auto a = load_frag<BF16>(q + (16 * ti + (lane & 15)) * NS + kk * 32 + 8 * (lane >> 4));
-          const auto bq = load_frag<BF16>(kb + (16 * tj + (lane & 15)) * NS + kk * 32 + 8 * (lane >> 4));
-          mma<BF16>(acc, a, bq);
+      for (int kk = 0; kk < S::NC / 32; ++kk) {
+        const auto fk = load_frag<BF16>(kb + (16 * tj + (lane & 15)) * NS + kk * 32 + 8 * (lane >> 4));
+        const auto fq = load_frag<BF16>(q + (16 * ti + (lane & 15)) * NS + kk * 32 + 8 * (lane >> 4));
+        mma<BF16>(acc, fk, fq);
+      }
+      const int row = 16 * ti + (lane & 15);
+      const int t = row / R;
+      const int j0 = 16 * tj + 4 * (lane >> 4);
+      float val[4];
+      if (COORD) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) val[i] = ((j0 + i) / KR <= t) ? acc[i] : 0.f;
+      } else {
+        const float lt = sLC[bi][t];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int s = (j0 + i) / KR;
+          val[i] = (s <= t) ? acc[i] * __builtin_amdgcn_exp2f(lt - sLC[bi][s]) : 0.f;
         }
       }
-      const int col = 16 * tj + (lane & 15);
-      const int s = col / KR;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = 16 * ti + 4 * (lane >> 4) + i;
-        const int t = row / R;
-        float val = 0.f;
-        if (s <= t) {
-          val = acc[i];
-          if (!COORD) val *= __expf(-Ah * (sCD[bi][t] - sCD[bi][s]));
-        }
-        sS[row * KS + col] = from_f32<T>(val);
-      }
+      store4<BF16>(sS + row * KS + j0, val);
     }
+    if (wave == PW && c + 1 < nch) factors(c + 1, bi ^ 1);
     __syncthreads();
 
     // ---- phase 2 -- a6 readout + output of chunk c, a4/a5 state update of chunk c,
-    // a1/a2 staging of chunk c+1 (other buffer), loads of chunk c+2
+    // a2 staging of chunk c+1 (other buffer), loads of chunk c+2.  Output tiles are
+    // transposed: lane l holds row 16 ti + (l & 15), columns p = 16 tp + 4 (l >> 4) + i.
     for (int tile = wave; tile < S::TQ * S::TP; tile += NW) {
       const int ti = tile / S::TP, tp = tile % S::TP;
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
       const T* qsrc = COORD ? qe : q;
 #pragma unroll
       for (int kk = 0; kk < S::NC / 32; ++kk) {
-        const auto a = load_frag<BF16>(qsrc + (16 * ti + (lane & 15)) * NS + kk * 32 + 8 * (lane >> 4));
-        const auto bs = load_frag<BF16>(sST + (16 * tp + (lane & 15)) * NS + kk * 32 + 8 * (lane >> 4));
-        mma<BF16>(acc, a, bs);
+        const auto fs = load_frag_tr<BF16>(sST + (kk * 32) * VS + 16 * tp, VS);
+        const auto fq = load_frag<BF16>(qsrc + (16 * ti + (lane & 15)) * NS + kk * 32 + 8 * (lane >> 4));
+        mma<BF16>(acc, fs, fq);
       }
+      const int row = 16 * ti + (lane & 15);
+      const int t = row / R, o = row % R;
       if (!COORD) {
+        const float el = sEL[bi][t];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc[i] *= sEL[bi][(16 * ti + 4 * (lane >> 4) + i) / R];
+        for (int i = 0; i < 4; ++i) acc[i] *= el;
       }
       const int tmax = (16 * ti + 15) / R;
       const int kend = ((tmax + 1) * KR + 31) / 32;
       for (int kk = 0; kk < kend; ++kk) {
-        const auto a = load_frag<BF16>(sS + (16 * ti + (lane & 15)) * KS + kk * 32 + 8 * (lane >> 4));
-        const auto bv = load_frag_tr<BF16>(vb + (kk * 32) * VS + 16 * tp, VS);
-        mma<BF16>(acc, a, bv);
+        const auto fv = load_frag_tr<BF16>(vb + (kk * 32) * VS + 16 * tp, VS);
+        const auto fsc = load_frag<BF16>(sS + (16 * ti + (lane & 15)) * KS + kk * 32 + 8 * (lane >> 4));
+        mma<BF16>(acc, fv, fsc);
       }
-      const int pl = 16 * tp + (lane & 15);
+      const int pl = 16 * tp + 4 * (lane >> 4);
+      float val[4] = {acc[0], acc[1], acc[2], acc[3]};
+      if (p.has_D) {
+        float xv[4];
+        load4<BF16>(vb + (t * KR + o) * VS + pl, xv);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = 16 * ti + 4 * (lane >> 4) + i;
-        const int t = row / R, o = row % R;
-        const int tg = t0 + t;
-        float val = acc[i];
-        if (p.has_D) val += Dh * to_f32(vb[(t * KR + o) * VS + pl]);
-        if (tg < L) yg[tg * tsH + o * P + pl] = from_f32<T>(val);
+        for (int i = 0; i < 4; ++i) val[i] += Dh * xv[i];
       }
+      if (t0 + t < L) store4<BF16>(yg + (t0 + t) * tsH + o * P + pl, val);
     }
     {
       const float cdend = sMisc[bi][0];
@@ -419,30 +468,27 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
         const int tile = wave + NW * k;
         if (tile < S::ST_TILES) {
           const int tn = tile / S::TP, tp = tile % S::TP;
+          const int n = 16 * tn + (lane & 15);
           f32x4 acc = st[k];
+          const float dec = COORD ? __expf(-sRate[n] * cdend) : sMisc[bi][1];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int n = 16 * tn + 4 * (lane >> 4) + i;
-            acc[i] *= COORD ? __expf(-sRate[n] * cdend) : sMisc[bi][1];
-          }
+          for (int i = 0; i < 4; ++i) acc[i] *= dec;
 #pragma unroll
           for (int kk = 0; kk < S::QK / 32; ++kk) {
-            const auto a = load_frag_tr<BF16>((COORD ? keb : kb) + (kk * 32) * NS + 16 * tn, NS);
-            const auto bv = load_frag_tr<BF16>((COORD ? vb : vwb) + (kk * 32) * VS + 16 * tp, VS);
-            mma<BF16>(acc, a, bv);
+            const auto fv = load_frag_tr<BF16>((COORD ? vb : vwb) + (kk * 32) * VS + 16 * tp, VS);
+            const auto fk = load_frag_tr<BF16>((COORD ? keb : kb) + (kk * 32) * NS + 16 * tn, NS);
+            mma<BF16>(acc, fv, fk);
           }
           if (COORD) {
+            // chunk-total rotation of the pairs: rows (n, n+1) sit in lanes (l, l^1)
+            const bool pair = n >= nreal;
+            float sn = 0.f, cs = 1.f;
+            if (pair) fast_sincos(sOmega[(n - nreal) >> 1] * cdend, &sn, &cs);
+            const float sg = (lane & 1) ? sn : -sn;
 #pragma unroll
-            for (int i = 0; i < 4; i += 2) {
-              const int n = 16 * tn + 4 * (lane >> 4) + i;
-              if (n >= nreal) {
-                const float th = sOmega[(n - nreal) >> 1] * cdend;
-                float sn, cs;
-                fast_sincos(th, &sn, &cs);
-                const float a0 = acc[i], a1 = acc[i + 1];
-                acc[i] = cs * a0 - sn * a1;
-                acc[i + 1] = sn * a0 + cs * a1;
-              }
+            for (int i = 0; i < 4; ++i) {
+              const float other = swap_adjacent_lanes(acc[i]);
+              acc[i] = pair ? cs * acc[i] + sg * other : acc[i];
             }
           }
           st[k] = acc;
@@ -461,22 +507,13 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
       const int tile = wave + NW * k;
       if (tile < S::ST_TILES) {
         const int tn = tile / S::TP, tp = tile % S::TP;
-        const int pl = 16 * tp + (lane & 15);
-        const int n0 = 16 * tn + 4 * (lane >> 4);
-        if constexpr (BF16) {
-          uint2 w;
-          w.x = pack_bf16x2(st[k][0], st[k][1]);
-          w.y = pack_bf16x2(st[k][2], st[k][3]);
-          *reinterpret_cast<uint2*>(sST + pl * NS + n0) = w;
-        } else {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) sST[pl * NS + n0 + i] = from_f32<T>(st[k][i]);
-        }
-        if (p.saved) {
-          float* dst = p.saved + ((sl_saved + c + 1) * N + n0) * P + p0 + pl;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) dst[i * P] = st[k][i];
-        }
+        const int n = 16 * tn + (lane & 15);
+        const int pl = 16 * tp + 4 * (lane >> 4);
+        const float v4[4] = {st[k][0], st[k][1], st[k][2], st[k][3]};
+        store4<BF16>(sST + n * VS + pl, v4);
+        if (p.saved)
+          *reinterpret_cast<float4*>(p.saved + ((sl_saved + c + 1) * N + n) * P + p0 + pl) =
+              make_float4(v4[0], v4[1], v4[2], v4[3]);
       }
     }
   }
@@ -547,7 +584,7 @@ hipError_t launch_fwd(const FwdKey& k, const FwdParams& p, hipStream_t stream,
   const int nwg = p.batch * p.H * p.npblk;
   if (nwg == 0 || p.nchunks == 0) return hipSuccess;
   auto mark = [&](int i) {
-    if (events && events[i]) hipEventRecord(static_cast<hipEvent_t>(events[i]), stream);
+    if (events && events[i]) (void)hipEventRecord(static_cast<hipEvent_t>(events[i]), stream);
   };
 #define SSM_FWD_LAUNCH(BF, NN, PBB, RR, KRR, QTT, CO, NT)                                    \
   if (k.bf16 == BF && k.N == NN && k.PB == PBB && k.R == RR && k.KR == KRR && k.QT == QTT && \
