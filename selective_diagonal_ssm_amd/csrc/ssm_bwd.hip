@@ -284,8 +284,20 @@ struct BwdShape {
   static constexpr int X_VECS = BROWS * (P / VEC);
   static constexpr int Y_VECS = QO * (P / VEC);
   static constexpr int TQ = QO / 16, TK = QK / 16, TN = N / 16, TP = P / 16;
+  // score tiles (16 query rows ti x 16 keys tj) holding at least one causal entry
+  static constexpr int row_tiles(int ti) {
+    const int c = (((16 * ti + 15) / R) * KR) / 16 + 1;
+    return c < TK ? c : TK;
+  }
+  static constexpr int score_tiles() {
+    int n = 0;
+    for (int ti = 0; ti < TQ; ++ti) n += row_tiles(ti);
+    return n;
+  }
+  static constexpr int SC_TILES = score_tiles();
   static_assert(QO % 16 == 0 && QK % 32 == 0, "chunk rows must fill MFMA tiles");
   static_assert(N % 16 == 0 && P % 16 == 0 && QT <= 64, "unsupported tile shape");
+  static_assert(KR <= 4 && 16 % KR == 0 && 16 % R == 0, "a tile spans whole tokens");
 };
 
 template <bool BF16, int N, int P, int R, int KR, int QT, bool COORD, int NTHREADS>
@@ -317,9 +329,13 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
   __shared__ float sTT[WH][64], sSrc[WH][64];     // head: target / source inter terms per token
   __shared__ float sRS[WH][64], sCS[WH][64];      // head: row / column sums of Z o S o M
   __shared__ float sDg[WT][64], sDb[WT][64];      // per-wave dgamma / dbeta sums
-  __shared__ float sDX[S::TE ? 2 * (QT + 1) * R * P : 1];  // two-endpoint dX assembly
-  __shared__ float sDB[S::TE ? 2 * (QT + 1) * R * N : 1];  // two-endpoint dB assembly
-  __shared__ float sTailX[S::TE ? R * P : 1], sTailB[S::TE ? R * N : 1];
+  __shared__ __align__(16) float sDX[S::TE ? 2 * (QT + 1) * R * P : 4];  // two-endpoint dX assembly
+  __shared__ __align__(16) float sDB[S::TE ? 2 * (QT + 1) * R * N : 4];  // two-endpoint dB assembly
+  __shared__ __align__(16) float sTailX[S::TE ? R * P : 4], sTailB[S::TE ? R * N : 4];
+  // per-token factors of the current item (token = index)
+  __shared__ float sTcd[64];                       // cumulative step inside the chunk
+  __shared__ float sTw[64], sTel[64], sTlc[64];    // head: e^{L_end - L_t}, e^{L_t}, -A CD log2(e)
+  __shared__ float sTga[S::TE ? 64 : 1], sTbe[S::TE ? 64 : 1];
   __shared__ float sMisc[NW];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -339,7 +355,8 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
   for (int i = tid; i < (S::NC - N) * PS; i += S::NTH) { sGh[N * PS + i] = T(0); sGl[N * PS + i] = T(0); }
   for (int i = tid; i < (S::QOC - QO) * NS; i += S::NTH) sQ[QO * NS + i] = T(0);
   for (int i = tid; i < (S::QOC - QO) * PS; i += S::NTH) sY[QO * PS + i] = T(0);
-  for (int i = tid; i < (S::QOC - QO) * KS; i += S::NTH) { sSM[QO * KS + i] = T(0); sZM[QO * KS + i] = T(0); }
+  // score entries above the causal diagonal (and padding rows) stay zero for good
+  for (int i = tid; i < S::QOC * KS; i += S::NTH) { sSM[i] = T(0); sZM[i] = T(0); }
   if (S::NC > N) {
     for (int i = tid; i < S::QOC * (S::NC - N); i += S::NTH) sQ[(i / (S::NC - N)) * NS + N + i % (S::NC - N)] = T(0);
     for (int i = tid; i < QK * (S::NC - N); i += S::NTH) {
@@ -499,6 +516,18 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
     const float cdend = __shfl(cd_l, QT - 1, kWave);
     const float w_l = COORD ? 0.f : __expf(-Ah * (cdend - cd_l));   // e^{L_end - L_t}
     const float el_l = COORD ? 0.f : __expf(-Ah * cd_l);            // e^{L_t}
+    if (wave == 0 && lane < QT) {
+      sTcd[lane] = cd_l;
+      if (!COORD) {
+        sTw[lane] = w_l;
+        sTel[lane] = el_l;
+        sTlc[lane] = -Ah * 1.4426950408889634f * cd_l;
+      }
+      if (S::TE) {
+        sTga[lane] = ga_l;
+        sTbe[lane] = be_l;
+      }
+    }
 
     // ---------------------------------------------------------------- staging
     // queries (t, o)
@@ -641,27 +670,24 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
           eth += -ga[i] * sb[i] + gb[i] * sa[i];  // <G~, J S>
         }
         ea *= lea; eb *= leb; eth *= lea;
-        // reduce over the PV p-vectors of this row pair (consecutive lanes)
-  #pragma unroll
-        for (int off = 1; off < PV; off <<= 1) {
-          ea += __shfl_xor(ea, off, kWave);
-          eb += __shfl_xor(eb, off, kWave);
-          eth += __shfl_xor(eth, off, kWave);
-        }
+        // reduce over the PV p-vectors of this row pair (an aligned group of lanes)
+        ea = group_sum<PV>(ea);
+        eb = group_sum<PV>(eb);
+        if (COORD) eth = group_sum<PV>(eth);
         if (pc == 0) {
           sE[n] = ea; sE[n + 1] = eb;
           if (pair) sEth[(n - nreal) >> 1] = eth;
         }
-        // bf16 hi / lo copies
-        float hi[4], lo[4];
+        // bf16 hi / lo copies (hi = x rounded to the storage type, lo = the remainder)
         auto split = [&](const float* x, T* dh, T* dlo) {
+          float hi[4], lo[4];
   #pragma unroll
           for (int i = 0; i < 4; ++i) {
             hi[i] = to_f32(from_f32<T>(x[i]));
             lo[i] = x[i] - hi[i];
-            dh[i] = from_f32<T>(hi[i]);
-            dlo[i] = from_f32<T>(lo[i]);
           }
+          store4<BF16>(dh, hi);
+          store4<BF16>(dlo, lo);
         };
         split(sa, sSh + n * PS + q0, sSl + n * PS + q0);
         split(sb, sSh + (n + 1) * PS + q0, sSl + (n + 1) * PS + q0);
@@ -704,105 +730,130 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
     if (lane == 0) sMisc[wave] = dDp;
 
     // ---------------------------------------------------------------- scores
-    for (int tile = wave; tile < S::TQ * S::TK; tile += NW) {
-      const int ti = tile / S::TK, tj = tile % S::TK;
-      const int tmax = (16 * ti + 15) / R, smin = (16 * tj) / KR;
+    // S^T = K Q^T and Z^T = V dY^T, computed transposed: lane l holds query row
+    // 16 ti + (l & 15) against keys 16 tj + 4 (l >> 4) + i.  Only tiles with a causal
+    // entry are formed; the others stay zero from the start.
+    for (int tile = wave; tile < S::SC_TILES; tile += NW) {
+      int ti = 0, tj = tile;
+#pragma unroll
+      for (int a = 0; a < S::TQ - 1; ++a) {
+        if (tj >= S::row_tiles(ti)) {
+          tj -= S::row_tiles(ti);
+          ++ti;
+        }
+      }
       f32x4 sc = {0.f, 0.f, 0.f, 0.f}, z = {0.f, 0.f, 0.f, 0.f};
-      if (smin <= tmax) {
-  #pragma unroll
-        for (int kk = 0; kk < S::NC / 32; ++kk) {
-          const auto a = load_frag<BF16>(sQ + (16 * ti + (lane & 15)) * NS + kk * 32 + 8 * (lane >> 4));
-          const auto bq = load_frag<BF16>(sK + (16 * tj + (lane & 15)) * NS + kk * 32 + 8 * (lane >> 4));
-          mma<BF16>(sc, a, bq);
-        }
-  #pragma unroll
-        for (int kk = 0; kk < S::PC / 32; ++kk) {
-          const auto a = load_frag<BF16>(sY + (16 * ti + (lane & 15)) * PS + kk * 32 + 8 * (lane >> 4));
-          const auto bv = load_frag<BF16>(sV + (16 * tj + (lane & 15)) * PS + kk * 32 + 8 * (lane >> 4));
-          mma<BF16>(z, a, bv);
-        }
+#pragma unroll
+      for (int kk = 0; kk < S::NC / 32; ++kk) {
+        const auto fk = load_frag<BF16>(sK + (16 * tj + (lane & 15)) * NS + kk * 32 + 8 * (lane >> 4));
+        const auto fq = load_frag<BF16>(sQ + (16 * ti + (lane & 15)) * NS + kk * 32 + 8 * (lane >> 4));
+        mma<BF16>(sc, fk, fq);
       }
-      const int col = 16 * tj + (lane & 15), s = col / KR;
-      const float cds = __shfl(cd_l, s, kWave);
-      float csum = 0.f;
-  #pragma unroll
+#pragma unroll
+      for (int kk = 0; kk < S::PC / 32; ++kk) {
+        const auto fv = load_frag<BF16>(sV + (16 * tj + (lane & 15)) * PS + kk * 32 + 8 * (lane >> 4));
+        const auto fy = load_frag<BF16>(sY + (16 * ti + (lane & 15)) * PS + kk * 32 + 8 * (lane >> 4));
+        mma<BF16>(z, fv, fy);
+      }
+      const int row = 16 * ti + (lane & 15), t = row / R;
+      const int j0 = 16 * tj + 4 * (lane >> 4);
+      const float lt = COORD ? 0.f : sTlc[t];
+      float smv[4], zmv[4], wv[4];
+#pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int row = 16 * ti + 4 * (lane >> 4) + i, t = row / R;
-        const float cdt = __shfl(cd_l, t, kWave);
+        const int s = (j0 + i) / KR;
         float m = 0.f;
-        if (s <= t) m = COORD ? 1.f : __expf(-Ah * (cdt - cds));
-        sSM[row * KS + col] = from_f32<T>(sc[i] * m);
-        sZM[row * KS + col] = from_f32<T>(z[i] * m);
-        if (!COORD) {
-          float wv = z[i] * sc[i] * m;
-          // row sum over the 16 columns of this tile
-          float rs = wv;
-  #pragma unroll
-          for (int off = 1; off < 16; off <<= 1) rs += __shfl_xor(rs, off, kWave);
-          if ((lane & 15) == 0) sRS[wave][t] += rs;
-          csum += wv;
-        }
+        if (s <= t) m = COORD ? 1.f : __builtin_amdgcn_exp2f(lt - sTlc[s]);
+        smv[i] = sc[i] * m;
+        zmv[i] = z[i] * m;
+        wv[i] = z[i] * smv[i];
       }
+      store4<BF16>(sSM + row * KS + j0, smv);
+      store4<BF16>(sZM + row * KS + j0, zmv);
       if (!COORD) {
-        csum += __shfl_xor(csum, 16, kWave);
-        csum += __shfl_xor(csum, 32, kWave);
-  #pragma unroll
-        for (int off = 1; off < KR; off <<= 1) csum += __shfl_xor(csum, off, kWave);
-        if (lane < 16 && (lane % KR) == 0) sCS[wave][s] += csum;
+        // W = Z o S o M: row sums per query token (the four lane groups hold disjoint
+        // keys of one row), column sums per key token (the 16 lanes of a group hold
+        // the 16 rows of each key)
+        float rs = (wv[0] + wv[1]) + (wv[2] + wv[3]);
+        rs += __shfl_xor(rs, 16, kWave);
+        rs += __shfl_xor(rs, 32, kWave);
+        rs = group_sum<R>(rs);
+        if (lane < 16 && (lane % R) == 0) sRS[wave][t] += rs;
+        float cs[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) cs[i] = group_sum<16>(wv[i]);
+        if ((lane & 15) == 0) {
+#pragma unroll
+          for (int i = 0; i < 4; i += KR) {
+            float v = 0.f;
+#pragma unroll
+            for (int e = 0; e < KR; ++e) v += cs[i + e];
+            sCS[wave][(j0 + i) / KR] += v;
+          }
+        }
       }
     }
     __syncthreads();
 
     // ---------------------------------------------------------------- dV -> dX
+    // dV^T = dY^T (S o M) + G~^T Ke^T, computed transposed: lane l holds key
+    // 16 tj + (l & 15) and value columns 16 tp + 4 (l >> 4) + i
     for (int tile = wave; tile < S::TK * S::TP; tile += NW) {
       const int tj = tile / S::TP, tp = tile % S::TP;
       f32x4 ai = {0.f, 0.f, 0.f, 0.f}, ae = {0.f, 0.f, 0.f, 0.f};
-  #pragma unroll
+#pragma unroll
       for (int kk = 0; kk < S::QOC / 32; ++kk) {
-        const auto a = load_frag_tr<BF16>(sSM + (kk * 32) * KS + 16 * tj, KS);
-        const auto bq = load_frag_tr<BF16>(sY + (kk * 32) * PS + 16 * tp, PS);
-        mma<BF16>(ai, a, bq);
+        const auto fy = load_frag_tr<BF16>(sY + (kk * 32) * PS + 16 * tp, PS);
+        const auto fs = load_frag_tr<BF16>(sSM + (kk * 32) * KS + 16 * tj, KS);
+        mma<BF16>(ai, fy, fs);
       }
-  #pragma unroll
+#pragma unroll
       for (int kk = 0; kk < S::NC / 32; ++kk) {
-        const auto a = load_frag<BF16>((COORD ? sKe : sK) + (16 * tj + (lane & 15)) * NS + kk * 32 + 8 * (lane >> 4));
         if (kk * 32 < N) {
-          const auto bh = load_frag_tr<BF16>(sGh + (kk * 32) * PS + 16 * tp, PS);
-          const auto bl = load_frag_tr<BF16>(sGl + (kk * 32) * PS + 16 * tp, PS);
-          mma<BF16>(ae, a, bh);
-          mma<BF16>(ae, a, bl);
+          const auto fk = load_frag<BF16>((COORD ? sKe : sK) + (16 * tj + (lane & 15)) * NS + kk * 32 + 8 * (lane >> 4));
+          const auto fgh = load_frag_tr<BF16>(sGh + (kk * 32) * PS + 16 * tp, PS);
+          const auto fgl = load_frag_tr<BF16>(sGl + (kk * 32) * PS + 16 * tp, PS);
+          mma<BF16>(ae, fgh, fk);
+          mma<BF16>(ae, fgl, fk);
         }
       }
-      const int pp = 16 * tp + (lane & 15);
-  #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int j = 16 * tj + 4 * (lane >> 4) + i;
-        const int s = j / KR, kr = j % KR;
-        const float wj = COORD ? 1.f : __shfl(w_l, s, kWave);
-        const float dv = ai[i] + wj * ae[i];
-        if (!S::TE) {
-          const int t = t0 + s;
-          const float val = dv + (p.has_D ? Dh * to_f32(sY[(s * R + kr) * PS + pp]) : 0.f);
-          if (t < L) dxg[((((size_t)b * L + t) * H + h) * R + kr) * P + pp] = from_f32<T>(val);
-        } else if (kr < R) {
-          sDX[((s + 1) * R + kr) * P + pp] = dv;                       // gamma row -> X_s
-        } else if (s >= 1) {
-          sDX[(QT + 1) * R * P + (s * R + kr - R) * P + pp] = dv;      // beta row -> X_{s-1}
+      const int j = 16 * tj + (lane & 15), s = j / KR, kr = j % KR;
+      const int pl = 16 * tp + 4 * (lane >> 4);
+      const float wj = COORD ? 1.f : sTw[s];
+      float dv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dv[i] = ai[i] + wj * ae[i];
+      if (!S::TE) {
+        if (p.has_D) {
+          float yv[4];
+          load4<BF16>(sY + (s * R + kr) * PS + pl, yv);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) dv[i] += Dh * yv[i];
         }
+        const int t = t0 + s;
+        if (t < L) store4<BF16>(dxg + ((((size_t)b * L + t) * H + h) * R + kr) * P + pl, dv);
+      } else if (kr < R) {
+        // gamma row -> X_s
+        *reinterpret_cast<float4*>(sDX + ((s + 1) * R + kr) * P + pl) = make_float4(dv[0], dv[1], dv[2], dv[3]);
+      } else if (s >= 1) {
+        // beta row -> X_{s-1}
+        *reinterpret_cast<float4*>(sDX + (QT + 1) * R * P + (s * R + kr - R) * P + pl) =
+            make_float4(dv[0], dv[1], dv[2], dv[3]);
       }
     }
 
     // ---------------------------------------------------------------- dK~ -> dB, dbeta, dgamma
+    // lane l holds key 16 tj + (l & 15) and state rows 16 tnn + 4 (l >> 4) + i
     for (int tile = wave; tile < S::TN * S::TK; tile += NW) {
       const int tnn = tile / S::TK, tj = tile % S::TK;
       f32x4 ai = {0.f, 0.f, 0.f, 0.f}, ae = {0.f, 0.f, 0.f, 0.f};
-  #pragma unroll
+#pragma unroll
       for (int kk = 0; kk < S::QOC / 32; ++kk) {
         const auto a = load_frag_tr<BF16>(sQ + (kk * 32) * NS + 16 * tnn, NS);
         const auto bz = load_frag_tr<BF16>(sZM + (kk * 32) * KS + 16 * tj, KS);
         mma<BF16>(ai, a, bz);
       }
-  #pragma unroll
+#pragma unroll
       for (int kk = 0; kk < S::PC / 32; ++kk) {
         const auto bv = load_frag<BF16>(sV + (16 * tj + (lane & 15)) * PS + kk * 32 + 8 * (lane >> 4));
         const auto ah = load_frag<BF16>(sGh + (16 * tnn + (lane & 15)) * PS + kk * 32 + 8 * (lane >> 4));
@@ -811,19 +862,18 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
         mma<BF16>(ae, al, bv);
       }
       const int j = 16 * tj + (lane & 15), s = j / KR, kr = j % KR;
-      const float cds = __shfl(cd_l, s, kWave);
-      const float wj = COORD ? 1.f : __shfl(w_l, s, kWave);
-      const float gam = S::TE ? __shfl(ga_l, s, kWave) : 1.f;
-      const float bet = S::TE ? __shfl(be_l, s, kWave) : 0.f;
+      const int n0 = 16 * tnn + 4 * (lane >> 4);
+      const float cds = sTcd[s];
+      const float wj = COORD ? 1.f : sTw[s];
       const bool brow = S::TE && kr >= R;
       const int rr = brow ? kr - R : kr;
       const int tb = t0 + (brow ? s - 1 : s);  // token whose B row this key carries
-      float tokacc = 0.f, dgb = 0.f;
+      float tokacc = 0.f;
       float dk[4], kv[4], rpa[4], rek[4], rpw[2] = {0.f, 0.f}, rekt[2] = {0.f, 0.f};
-  #pragma unroll
+      load4<BF16>(sK + j * NS + n0, kv);
+#pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int n = 16 * tnn + 4 * (lane >> 4) + i;
-        kv[i] = to_f32(sK[j * NS + n]);
+        const int n = n0 + i;
         rpa[i] = 0.f; rek[i] = 0.f;
         if (COORD) {
           const float er = __expf(-sRate[n] * 0.5f * cdend);  // e^{r_n}
@@ -840,9 +890,9 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
         }
       }
       if (COORD) {
-  #pragma unroll
+#pragma unroll
         for (int i = 0; i < 4; i += 2) {
-          const int n = 16 * tnn + 4 * (lane >> 4) + i;
+          const int n = n0 + i;
           if (n >= nreal) {
             const int kp = (n - nreal) >> 1;
             const float er = __expf(-sRate[n] * 0.5f * cdend);
@@ -862,57 +912,41 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
         }
       }
       // gradient w.r.t. the stored B row and the endpoint weights
-      const bool own = !(brow && s == 0) && tb < L;  // the halo row's B belongs to the previous chunk
-      float braw[4];
-      {
-        const int tbc = tb < 0 ? 0 : tb;
-        const int n0 = 16 * tnn + 4 * (lane >> 4);
-        const T* src = Bg + ((((size_t)b * L + tbc) * G + g) * R + rr) * N + n0;
-  #pragma unroll
-        for (int i = 0; i < 4; ++i) braw[i] = (tb >= 0 && tb < L) ? to_f32(src[i]) : 0.f;
-      }
-  #pragma unroll
-      for (int i = 0; i < 4; ++i) dgb += dk[i] * braw[i];
-      const float wgt = brow ? bet : gam;
-      if (!S::TE) {
-        if (own) {
-          const int n0 = 16 * tnn + 4 * (lane >> 4);
-          T* dst = dBg + ((((size_t)b * L + tb) * G + g) * R + rr) * N + n0;
-  #pragma unroll
-          for (int i = 0; i < 4; ++i) dst[i] = from_f32<T>(dk[i]);
+      float dgb = 0.f;
+      if (S::TE) {
+        const float wgt = brow ? sTbe[s] : sTga[s];
+        if (tb >= 0 && tb < L) {
+          float braw[4];
+          load4<BF16>(Bg + ((((size_t)b * L + tb) * G + g) * R + rr) * N + n0, braw);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) dgb += dk[i] * braw[i];
         }
-      } else {
-        const int n0 = 16 * tnn + 4 * (lane >> 4);
         if (!brow) {
-  #pragma unroll
-          for (int i = 0; i < 4; ++i) sDB[((s + 1) * R + rr) * N + n0 + i] = wgt * dk[i];
+          *reinterpret_cast<float4*>(sDB + ((s + 1) * R + rr) * N + n0) =
+              make_float4(wgt * dk[0], wgt * dk[1], wgt * dk[2], wgt * dk[3]);
         } else if (s >= 1) {
-  #pragma unroll
-          for (int i = 0; i < 4; ++i) sDB[(QT + 1) * R * N + (s * R + rr) * N + n0 + i] = wgt * dk[i];
+          *reinterpret_cast<float4*>(sDB + (QT + 1) * R * N + (s * R + rr) * N + n0) =
+              make_float4(wgt * dk[0], wgt * dk[1], wgt * dk[2], wgt * dk[3]);
         }
+      } else if (tb < L) {
+        store4<BF16>(dBg + ((((size_t)b * L + tb) * G + g) * R + rr) * N + n0, dk);
       }
       if (COORD) {
-        // per-row sums over the 16 key columns of this tile
-  #pragma unroll
+        // per-row sums over the 16 key columns of this tile (one 16-lane group)
+#pragma unroll
         for (int i = 0; i < 4; ++i) {
-  #pragma unroll
-          for (int off = 1; off < 16; off <<= 1) {
-            rpa[i] += __shfl_xor(rpa[i], off, kWave);
-            rek[i] += __shfl_xor(rek[i], off, kWave);
-          }
+          rpa[i] = group_sum<16>(rpa[i]);
+          rek[i] = group_sum<16>(rek[i]);
         }
-  #pragma unroll
+#pragma unroll
         for (int q = 0; q < 2; ++q) {
-  #pragma unroll
-          for (int off = 1; off < 16; off <<= 1) {
-            rpw[q] += __shfl_xor(rpw[q], off, kWave);
-            rekt[q] += __shfl_xor(rekt[q], off, kWave);
-          }
+          rpw[q] = group_sum<16>(rpw[q]);
+          rekt[q] = group_sum<16>(rekt[q]);
         }
         if ((lane & 15) == 0) {
-  #pragma unroll
+#pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const int n = 16 * tnn + 4 * (lane >> 4) + i;
+            const int n = n0 + i;
             sPA[wave][n] += rpa[i];
             sEK[wave][n] += rek[i];
             if ((i & 1) == 0 && n >= nreal) {
@@ -925,12 +959,12 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
       // per-key sums over the 4 row groups, then over the keys of one token
       tokacc += __shfl_xor(tokacc, 16, kWave);
       tokacc += __shfl_xor(tokacc, 32, kWave);
-      dgb += __shfl_xor(dgb, 16, kWave);
-      dgb += __shfl_xor(dgb, 32, kWave);
-  #pragma unroll
-      for (int off = 1; off < R; off <<= 1) dgb += __shfl_xor(dgb, off, kWave);
-  #pragma unroll
-      for (int off = 1; off < KR; off <<= 1) tokacc += __shfl_xor(tokacc, off, kWave);
+      tokacc = group_sum<KR>(tokacc);
+      if (S::TE) {
+        dgb += __shfl_xor(dgb, 16, kWave);
+        dgb += __shfl_xor(dgb, 32, kWave);
+        dgb = group_sum<R>(dgb);
+      }
       if (lane < 16) {
         if ((lane % KR) == 0) {
           if (COORD) sTok[wave][s] += tokacc;  // weighted source contribution
@@ -944,16 +978,17 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
     }
 
     // ---------------------------------------------------------------- dC~ -> dC
+    // lane l holds query row 16 tq + (l & 15) and state rows 16 tnn + 4 (l >> 4) + i
     for (int tile = wave; tile < S::TN * S::TQ; tile += NW) {
       const int tnn = tile / S::TQ, tq = tile % S::TQ;
       f32x4 ai = {0.f, 0.f, 0.f, 0.f}, ae = {0.f, 0.f, 0.f, 0.f};
-  #pragma unroll
+#pragma unroll
       for (int kk = 0; kk < QK / 32; ++kk) {
         const auto a = load_frag_tr<BF16>(sK + (kk * 32) * NS + 16 * tnn, NS);
         const auto bz = load_frag<BF16>(sZM + (16 * tq + (lane & 15)) * KS + kk * 32 + 8 * (lane >> 4));
         mma<BF16>(ai, a, bz);
       }
-  #pragma unroll
+#pragma unroll
       for (int kk = 0; kk < S::PC / 32; ++kk) {
         const auto by = load_frag<BF16>(sY + (16 * tq + (lane & 15)) * PS + kk * 32 + 8 * (lane >> 4));
         const auto ah = load_frag<BF16>(sSh + (16 * tnn + (lane & 15)) * PS + kk * 32 + 8 * (lane >> 4));
@@ -962,13 +997,14 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
         mma<BF16>(ae, al, by);
       }
       const int row = 16 * tq + (lane & 15), t = row / R, o = row % R, tg = t0 + t;
-      const float cdt = __shfl(cd_l, t, kWave);
-      const float elt = COORD ? 0.f : __shfl(el_l, t, kWave);
+      const int n0 = 16 * tnn + 4 * (lane >> 4);
+      const float cdt = sTcd[t];
+      const float elt = COORD ? 0.f : sTel[t];
       float tokacc = 0.f, dc[4], qv[4], rpa[4], rpw[2] = {0.f, 0.f};
-  #pragma unroll
+      load4<BF16>(sQ + row * NS + n0, qv);
+#pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int n = 16 * tnn + 4 * (lane >> 4) + i;
-        qv[i] = to_f32(sQ[row * NS + n]);
+        const int n = n0 + i;
         rpa[i] = 0.f;
         if (COORD) {
           const float er = __expf(-sRate[n] * 0.5f * cdend);
@@ -983,9 +1019,9 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
         }
       }
       if (COORD) {
-  #pragma unroll
+#pragma unroll
         for (int i = 0; i < 4; i += 2) {
-          const int n = 16 * tnn + 4 * (lane >> 4) + i;
+          const int n = n0 + i;
           if (n >= nreal) {
             const int kp = (n - nreal) >> 1;
             const float er = __expf(-sRate[n] * 0.5f * cdend);
@@ -1001,27 +1037,16 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
           }
         }
       }
-      if (tg < L) {
-        const int n0 = 16 * tnn + 4 * (lane >> 4);
-        T* dst = dCg + ((((size_t)b * L + tg) * G + g) * R + o) * N + n0;
-  #pragma unroll
-        for (int i = 0; i < 4; ++i) dst[i] = from_f32<T>(dc[i]);
-      }
+      if (tg < L) store4<BF16>(dCg + ((((size_t)b * L + tg) * G + g) * R + o) * N + n0, dc);
       if (COORD) {
-  #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-  #pragma unroll
-          for (int off = 1; off < 16; off <<= 1) rpa[i] += __shfl_xor(rpa[i], off, kWave);
-        }
-  #pragma unroll
-        for (int q = 0; q < 2; ++q) {
-  #pragma unroll
-          for (int off = 1; off < 16; off <<= 1) rpw[q] += __shfl_xor(rpw[q], off, kWave);
-        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) rpa[i] = group_sum<16>(rpa[i]);
+#pragma unroll
+        for (int q = 0; q < 2; ++q) rpw[q] = group_sum<16>(rpw[q]);
         if ((lane & 15) == 0) {
-  #pragma unroll
+#pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const int n = 16 * tnn + 4 * (lane >> 4) + i;
+            const int n = n0 + i;
             sPA[wave][n] += rpa[i];
             if ((i & 1) == 0 && n >= nreal) sPW[wave][(n - nreal) >> 1] += rpw[i >> 1];
           }
@@ -1029,8 +1054,7 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
       }
       tokacc += __shfl_xor(tokacc, 16, kWave);
       tokacc += __shfl_xor(tokacc, 32, kWave);
-  #pragma unroll
-      for (int off = 1; off < R; off <<= 1) tokacc += __shfl_xor(tokacc, off, kWave);
+      tokacc = group_sum<R>(tokacc);
       if (lane < 16 && (lane % R) == 0) {
         if (COORD) sTok[wave][t] += tokacc;
         else sTT[wave][t] += tokacc;
@@ -1039,23 +1063,36 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
     __syncthreads();
 
     // ---------------------------------------------------------------- two-endpoint assembly
+    // dX_s = B_s^T (gamma_s g_s) + B_s^T (beta_{s+1} g_{s+1}) (+ D dy_s), dB likewise;
+    // the second term of the last token comes from the next chunk's first state
     if (S::TE) {
-      for (int i = tid; i < QT * R * P; i += S::NTH) {
+      for (int i4 = tid; i4 < QT * R * P / 4; i4 += S::NTH) {
+        const int i = 4 * i4;
         const int s = i / (R * P), rem = i % (R * P), r = rem / P, pp = rem % P;
         const int t = t0 + s;
-        float v = sDX[((s + 1) * R + r) * P + pp];
-        if (s + 1 < QT) v += sDX[(QT + 1) * R * P + ((s + 1) * R + r) * P + pp];
-        else v += sTailX[r * P + pp];
-        if (p.has_D) v += Dh * to_f32(sY[(s * R + r) * PS + pp]);
-        if (t < L) dxg[((((size_t)b * L + t) * H + h) * R + r) * P + pp] = from_f32<T>(v);
+        const float4 a = *reinterpret_cast<const float4*>(sDX + ((s + 1) * R + r) * P + pp);
+        const float4 e = (s + 1 < QT)
+            ? *reinterpret_cast<const float4*>(sDX + (QT + 1) * R * P + ((s + 1) * R + r) * P + pp)
+            : *reinterpret_cast<const float4*>(sTailX + r * P + pp);
+        float v[4] = {a.x + e.x, a.y + e.y, a.z + e.z, a.w + e.w};
+        if (p.has_D) {
+          float yv[4];
+          load4<BF16>(sY + (s * R + r) * PS + pp, yv);
+  #pragma unroll
+          for (int q = 0; q < 4; ++q) v[q] += Dh * yv[q];
+        }
+        if (t < L) store4<BF16>(dxg + ((((size_t)b * L + t) * H + h) * R + r) * P + pp, v);
       }
-      for (int i = tid; i < QT * R * N; i += S::NTH) {
+      for (int i4 = tid; i4 < QT * R * N / 4; i4 += S::NTH) {
+        const int i = 4 * i4;
         const int s = i / (R * N), rem = i % (R * N), r = rem / N, n = rem % N;
         const int t = t0 + s;
-        float v = sDB[((s + 1) * R + r) * N + n];
-        if (s + 1 < QT) v += sDB[(QT + 1) * R * N + ((s + 1) * R + r) * N + n];
-        else v += sTailB[r * N + n];
-        if (t < L) dBg[((((size_t)b * L + t) * G + g) * R + r) * N + n] = from_f32<T>(v);
+        const float4 a = *reinterpret_cast<const float4*>(sDB + ((s + 1) * R + r) * N + n);
+        const float4 e = (s + 1 < QT)
+            ? *reinterpret_cast<const float4*>(sDB + (QT + 1) * R * N + ((s + 1) * R + r) * N + n)
+            : *reinterpret_cast<const float4*>(sTailB + r * N + n);
+        const float v[4] = {a.x + e.x, a.y + e.y, a.z + e.z, a.w + e.w};
+        if (t < L) store4<BF16>(dBg + ((((size_t)b * L + t) * G + g) * R + r) * N + n, v);
       }
     }
 

@@ -217,6 +217,25 @@ __device__ __forceinline__ float swap_adjacent_lanes(float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
 }
 
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over aligned groups of K consecutive lanes (K = 1, 2, 4, 8, 16), by DPP lane
+// permutations inside 16-lane rows: every lane of a group receives the group's
+// sum, added in the same order on every call.
+template <int K>
+__device__ __forceinline__ float group_sum(float v) {
+  static_assert(K == 1 || K == 2 || K == 4 || K == 8 || K == 16, "group of 1..16 lanes");
+  if constexpr (K >= 2) v += dpp_f32<0xB1>(v);   // quad permutation [1, 0, 3, 2]
+  if constexpr (K >= 4) v += dpp_f32<0x4E>(v);   // quad permutation [2, 3, 0, 1]
+  if constexpr (K >= 8) v += dpp_f32<0x141>(v);  // mirror inside each half row
+  if constexpr (K >= 16) v += dpp_f32<0x140>(v); // mirror inside the row
+  return v;
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
