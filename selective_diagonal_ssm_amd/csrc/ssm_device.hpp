@@ -201,15 +201,20 @@ __device__ __forceinline__ void mma(f32x4& acc, const Frag<BF16>& a, const Frag<
 // ---------------------------------------------------------------- wave primitives
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
 
-// inclusive prefix sum across the 64 lanes of a wave
+// inclusive prefix sum across the 64 lanes of a wave: a Hillis-Steele scan inside
+// each 16-lane row by DPP row shifts (lanes shifted in from outside the row add 0),
+// then the totals of the earlier rows (lanes 15, 31, 47) are added in
 __device__ __forceinline__ float wave_prefix_sum(float v) {
-  const int lane = lane_id();
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) {
-    const float o = __shfl_up(v, off, kWave);
-    if (lane >= off) v += o;
-  }
-  return v;
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x111, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x112, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x114, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x118, 0xF, 0xF, false));
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 15));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 31));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 47));
+  const int row = lane_id() >> 4;
+  const float carry = row == 0 ? 0.f : row == 1 ? r0 : row == 2 ? r0 + r1 : (r0 + r1) + r2;
+  return v + carry;
 }
 
 // value of the neighbouring lane (l ^ 1), by a DPP quad permutation [1, 0, 3, 2]

@@ -98,15 +98,16 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
   __shared__ __align__(16) T sV[2 * VSZ];                     // values, natural [key row][p]
   __shared__ __align__(16) T sVw[COORD ? 8 : 2 * VSZ];        // head: values scaled to the chunk end
   __shared__ __align__(16) T sS[S::QO * KS];                  // masked scores [query row][key]
-  __shared__ __align__(16) T sST[S::NC * VS];                 // state entering the chunk [n][p]
+  __shared__ __align__(16) T sST[2 * S::NC * VS];             // state entering chunk c in buffer c & 1 [n][p]
   // per-token factors of a chunk (double-buffered, written by wave PW one chunk ahead)
-  __shared__ __align__(16) float sCD[2][64];   // cumulative step inside the chunk
-  __shared__ __align__(16) float sLC[2][64];   // head: -A CD log2(e)
-  __shared__ __align__(16) float sEL[2][64];   // head: e^{-A CD}
-  __shared__ __align__(16) float sW[2][64];    // head: e^{-A (CD_end - CD)}
+  constexpr int TC = COORD ? 64 : 1, TH = COORD ? 1 : 64;
+  __shared__ __align__(16) float sCD[2][TC];   // per-row decay: cumulative step inside the chunk
+  __shared__ __align__(16) float sLC[2][TH];   // head: -A CD log2(e), so e^{L_t - L_s} = 2^{LC_t - LC_s}
+  __shared__ __align__(16) float sDT[2][64];   // steps Delta (staged one chunk ahead)
   __shared__ __align__(16) float sGa[2][S::TE ? 64 : 1], sBe[2][S::TE ? 64 : 1];
   __shared__ float sMisc[2][2];                // CD_end, head: e^{-A CD_end}
-  __shared__ float sRate[N], sOmega[N / 2 + 1];
+  __shared__ float sRate[COORD ? N : 1], sOmega[COORD ? N / 2 + 1 : 1];
+  __shared__ __align__(16) T sYo[S::QO * VS];                 // output rows of the previous chunk
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int lid = xcd_logical_id(blockIdx.x, gridDim.x);
@@ -130,7 +131,7 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
   }
   // the state entering chunk 0 is zero, and so are its padding rows n >= N for good;
   // score entries above the causal diagonal are zero and never rewritten
-  for (int i = tid; i < S::NC * VS; i += S::NTH) sST[i] = T(0);
+  for (int i = tid; i < 2 * S::NC * VS; i += S::NTH) sST[i] = T(0);
   for (int i = tid; i < S::QO * KS; i += S::NTH) sS[i] = T(0);
   if (S::NC > N) {
     for (int i = tid; i < 2 * S::QO * (S::NC - N); i += S::NTH) {
@@ -203,7 +204,9 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
       rx[k] = val;
     }
     if (wave == PW) {
-      const int t = t0 + lane;
+      // per-token scalars of the NEXT chunk: the staging of chunk c writes them to
+      // LDS, so the factor wave never waits on global memory
+      const int t = t0 + QT + lane;
       const bool ok = lane < QT && t < L;
       rdt = ok ? dtg[t * H] : 0.f;
       if (S::TE) {
@@ -217,20 +220,13 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
   auto factors = [&](int c, int bi) {
     const int t0 = c * QT;
     float dl = 0.f;
-    if (lane < QT && t0 + lane < L) dl = p.softplus ? softplus_f32(rdt) : rdt;
+    if (lane < QT && t0 + lane < L) dl = sDT[bi][lane];
     const float cd = wave_prefix_sum(dl);
-    const float cdend = __shfl(cd, QT - 1, kWave);
+    const float cdend = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cd), QT - 1));
     if (lane < QT) {
-      sCD[bi][lane] = cd;
+      if (COORD) sCD[bi][lane] = cd;
       if (!COORD) {
-        const float lc = -Ah * kLog2e * cd;
-        sLC[bi][lane] = lc;
-        sEL[bi][lane] = __builtin_amdgcn_exp2f(lc);
-        sW[bi][lane] = __builtin_amdgcn_exp2f(-Ah * kLog2e * (cdend - cd));
-      }
-      if (S::TE) {
-        sGa[bi][lane] = rga;
-        sBe[bi][lane] = rbe;
+        sLC[bi][lane] = -Ah * kLog2e * cd;
       }
     }
     if (lane == 0) {
@@ -259,6 +255,14 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
   // chunk's per-token factors
   auto stage = [&](int c, int bi) {
     (void)c;
+    if (wave == PW && lane < 64) {
+      // per-token scalars of chunk c+1 (loaded with chunk c's operands)
+      sDT[bi ^ 1][lane] = p.softplus ? softplus_f32(rdt) : rdt;
+      if (S::TE) {
+        sGa[bi ^ 1][lane] = rga;
+        sBe[bi ^ 1][lane] = rbe;
+      }
+    }
     const float cdend = sMisc[bi][0];
     T* q = sQ + bi * QSZ;
     T* qe = sQe + (COORD ? bi * QSZ : 0);
@@ -346,7 +350,7 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
           const int j = tau * KR + (e ? R : 0) + r;
           *reinterpret_cast<uint4*>(vb + j * VS + pv * VEC) = rx[k];
           if (!COORD) {
-            const float w = sW[bi][tau];
+            const float w = __builtin_amdgcn_exp2f(sLC[bi][QT - 1] - sLC[bi][tau]);  // e^{L_end - L_s}
             float xv[VEC];
             unpack<BF16>(rx[k], xv);
 #pragma unroll
@@ -355,6 +359,19 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
           }
         }
       }
+    }
+  };
+
+  // output rows of chunk c (staged in sYo) to HBM: whole PB-wide row segments,
+  // one 16-byte vector per thread
+  auto store_rows = [&](int c) {
+    const int t0 = c * QT;
+    for (int v = tid; v < S::QO * S::NVEC_P; v += S::NTH) {
+      const int row = v / S::NVEC_P, pv = v % S::NVEC_P;
+      const int t = row / R, o = row % R;
+      if (t0 + t < L)
+        *reinterpret_cast<uint4*>(yg + (t0 + t) * tsH + o * P + pv * VEC) =
+            *reinterpret_cast<const uint4*>(sYo + row * VS + pv * VEC);
     }
   };
 
@@ -368,7 +385,17 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
     }
   }
 
+  if (wave == PW) {
+    const bool ok = lane < QT && lane < L;
+    const float raw = ok ? dtg[lane * H] : 0.f;
+    sDT[0][lane] = p.softplus ? softplus_f32(raw) : raw;
+    if (S::TE) {
+      sBe[0][lane] = ok ? beg[lane * H] : 0.f;
+      sGa[0][lane] = ok ? gag[lane * H] : 0.f;
+    }
+  }
   load_chunk(0);
+  __syncthreads();
   if (wave == PW) factors(0, 0);
   __syncthreads();
   stage(0, 0);
@@ -376,8 +403,8 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
   __syncthreads();
 
   for (int c = 0; c < nch; ++c) {
-    const int t0 = c * QT;
     const int bi = c & 1;
+    if (c > 0) store_rows(c - 1);  // drains while the scores compute
     const T* q = sQ + bi * QSZ;
     const T* qe = sQe + (COORD ? bi * QSZ : 0);
     const T* kb = sK + bi * KSZ;
@@ -386,8 +413,9 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
     const T* vwb = sVw + (COORD ? 0 : bi * VSZ);
 
     // ---- phase 1 -- a3: masked intra-chunk scores of chunk c (computed transposed:
-    // lane l holds query row 16 ti + (l & 15) against keys 16 tj + 4 (l >> 4) + i);
-    // wave PW also forms the per-token factors of chunk c+1
+    // lane l holds query row 16 ti + (l & 15) against keys 16 tj + 4 (l >> 4) + i),
+    // the a4/a5 state update of chunk c; wave PW also forms the per-token factors
+    // of chunk c+1
     for (int tile = wave; tile < S::SC_TILES; tile += NW) {
       int ti = 0, tj = tile;
 #pragma unroll
@@ -421,26 +449,98 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
       }
       store4<BF16>(sS + row * KS + j0, val);
     }
+    // a4/a5: state update of chunk c (needs only this chunk's keys / values and the
+    // state entering it); its bf16 copy is the readout operand of chunk c+1
+    {
+      // state tiles of this wave: wave * ST_PER_WAVE + k, so a wave's tiles share
+      // their n-block whenever TP is a multiple of ST_PER_WAVE (one key fragment
+      // then serves all of them)
+      const float cdend = sMisc[bi][0];
+      constexpr bool SHARE = S::TP % S::ST_PER_WAVE == 0;
+      f32x4 acc[S::ST_PER_WAVE];
+#pragma unroll
+      for (int k = 0; k < S::ST_PER_WAVE; ++k) {
+        const int tile = wave * S::ST_PER_WAVE + k;
+        const int n = 16 * (tile / S::TP) + (lane & 15);
+        const float dec = COORD ? __expf(-sRate[n < N ? n : 0] * cdend) : sMisc[bi][1];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[k][i] = st[k][i] * dec;
+      }
+#pragma unroll
+      for (int kk = 0; kk < S::QK / 32; ++kk) {
+        Frag<BF16> fk;
+        if (SHARE) {
+          const int tn = (wave * S::ST_PER_WAVE) / S::TP;
+          if (wave * S::ST_PER_WAVE < S::ST_TILES)
+            fk = load_frag_tr<BF16>((COORD ? keb : kb) + (kk * 32) * NS + 16 * tn, NS);
+        }
+#pragma unroll
+        for (int k = 0; k < S::ST_PER_WAVE; ++k) {
+          const int tile = wave * S::ST_PER_WAVE + k;
+          if (tile < S::ST_TILES) {
+            const int tn = tile / S::TP, tp = tile % S::TP;
+            if (!SHARE) fk = load_frag_tr<BF16>((COORD ? keb : kb) + (kk * 32) * NS + 16 * tn, NS);
+            const auto fv = load_frag_tr<BF16>((COORD ? vb : vwb) + (kk * 32) * VS + 16 * tp, VS);
+            mma<BF16>(acc[k], fv, fk);
+          }
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < S::ST_PER_WAVE; ++k) {
+        const int tile = wave * S::ST_PER_WAVE + k;
+        if (tile < S::ST_TILES) {
+          const int tn = tile / S::TP, tp = tile % S::TP;
+          const int n = 16 * tn + (lane & 15);
+          if (COORD) {
+            // chunk-total rotation of the pairs: rows (n, n+1) sit in lanes (l, l^1)
+            const bool pair = n >= nreal;
+            float sn = 0.f, cs = 1.f;
+            if (pair) fast_sincos(sOmega[(n - nreal) >> 1] * cdend, &sn, &cs);
+            const float sg = (lane & 1) ? sn : -sn;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const float other = swap_adjacent_lanes(acc[k][i]);
+              acc[k][i] = pair ? cs * acc[k][i] + sg * other : acc[k][i];
+            }
+          }
+          st[k] = acc[k];
+          // the new state is the readout operand of chunk c+1 (other buffer)
+          const int pl = 16 * tp + 4 * (lane >> 4);
+          const float v4[4] = {acc[k][0], acc[k][1], acc[k][2], acc[k][3]};
+          store4<BF16>(sST + (bi ^ 1) * S::NC * VS + n * VS + pl, v4);
+          if (p.saved)
+            *reinterpret_cast<float4*>(p.saved + ((sl_saved + c + 1) * N + n) * P + p0 + pl) =
+                make_float4(v4[0], v4[1], v4[2], v4[3]);
+        }
+      }
+    }
     if (wave == PW && c + 1 < nch) factors(c + 1, bi ^ 1);
     __syncthreads();
 
-    // ---- phase 2 -- a6 readout + output of chunk c, a4/a5 state update of chunk c,
-    // a2 staging of chunk c+1 (other buffer), loads of chunk c+2.  Output tiles are
-    // transposed: lane l holds row 16 ti + (l & 15), columns p = 16 tp + 4 (l >> 4) + i.
+    // ---- phase 2 -- a2 staging of chunk c+1 (other buffer) and the loads of chunk
+    // c+2 first: the staging waits on this wave's outstanding memory operations, so
+    // it runs before this phase's stores are issued (they then drain for a whole
+    // chunk).  Then a6 readout + output of chunk c.
+    // Output tiles are transposed: lane l holds row 16 ti + (l & 15), columns
+    // p = 16 tp + 4 (l >> 4) + i.
+    if (c + 1 < nch) {
+      stage(c + 1, bi ^ 1);
+      if (c + 2 < nch) load_chunk(c + 2);
+    }
     for (int tile = wave; tile < S::TQ * S::TP; tile += NW) {
       const int ti = tile / S::TP, tp = tile % S::TP;
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
       const T* qsrc = COORD ? qe : q;
 #pragma unroll
       for (int kk = 0; kk < S::NC / 32; ++kk) {
-        const auto fs = load_frag_tr<BF16>(sST + (kk * 32) * VS + 16 * tp, VS);
+        const auto fs = load_frag_tr<BF16>(sST + bi * S::NC * VS + (kk * 32) * VS + 16 * tp, VS);
         const auto fq = load_frag<BF16>(qsrc + (16 * ti + (lane & 15)) * NS + kk * 32 + 8 * (lane >> 4));
         mma<BF16>(acc, fs, fq);
       }
       const int row = 16 * ti + (lane & 15);
       const int t = row / R, o = row % R;
       if (!COORD) {
-        const float el = sEL[bi][t];
+        const float el = __builtin_amdgcn_exp2f(sLC[bi][t]);  // e^{L_t}
 #pragma unroll
         for (int i = 0; i < 4; ++i) acc[i] *= el;
       }
@@ -459,64 +559,11 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) val[i] += Dh * xv[i];
       }
-      if (t0 + t < L) store4<BF16>(yg + (t0 + t) * tsH + o * P + pl, val);
-    }
-    {
-      const float cdend = sMisc[bi][0];
-#pragma unroll
-      for (int k = 0; k < S::ST_PER_WAVE; ++k) {
-        const int tile = wave + NW * k;
-        if (tile < S::ST_TILES) {
-          const int tn = tile / S::TP, tp = tile % S::TP;
-          const int n = 16 * tn + (lane & 15);
-          f32x4 acc = st[k];
-          const float dec = COORD ? __expf(-sRate[n] * cdend) : sMisc[bi][1];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) acc[i] *= dec;
-#pragma unroll
-          for (int kk = 0; kk < S::QK / 32; ++kk) {
-            const auto fv = load_frag_tr<BF16>((COORD ? vb : vwb) + (kk * 32) * VS + 16 * tp, VS);
-            const auto fk = load_frag_tr<BF16>((COORD ? keb : kb) + (kk * 32) * NS + 16 * tn, NS);
-            mma<BF16>(acc, fv, fk);
-          }
-          if (COORD) {
-            // chunk-total rotation of the pairs: rows (n, n+1) sit in lanes (l, l^1)
-            const bool pair = n >= nreal;
-            float sn = 0.f, cs = 1.f;
-            if (pair) fast_sincos(sOmega[(n - nreal) >> 1] * cdend, &sn, &cs);
-            const float sg = (lane & 1) ? sn : -sn;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const float other = swap_adjacent_lanes(acc[i]);
-              acc[i] = pair ? cs * acc[i] + sg * other : acc[i];
-            }
-          }
-          st[k] = acc;
-        }
-      }
-    }
-    if (c + 1 < nch) {
-      stage(c + 1, bi ^ 1);
-      if (c + 2 < nch) load_chunk(c + 2);
+      store4<BF16>(sYo + row * VS + pl, val);
     }
     __syncthreads();
-
-    // ---- phase 3 -- the new state becomes the readout operand of chunk c+1
-#pragma unroll
-    for (int k = 0; k < S::ST_PER_WAVE; ++k) {
-      const int tile = wave + NW * k;
-      if (tile < S::ST_TILES) {
-        const int tn = tile / S::TP, tp = tile % S::TP;
-        const int n = 16 * tn + (lane & 15);
-        const int pl = 16 * tp + 4 * (lane >> 4);
-        const float v4[4] = {st[k][0], st[k][1], st[k][2], st[k][3]};
-        store4<BF16>(sST + n * VS + pl, v4);
-        if (p.saved)
-          *reinterpret_cast<float4*>(p.saved + ((sl_saved + c + 1) * N + n) * P + p0 + pl) =
-              make_float4(v4[0], v4[1], v4[2], v4[3]);
-      }
-    }
   }
+  store_rows(nch - 1);
 }
 
 // ------------------------------------------------------------------ dispatch
