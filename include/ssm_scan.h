@@ -51,6 +51,15 @@
  *   - `saved` (fp32, ssm_saved_bytes(desc) bytes) receives the chunk-boundary
  *     states from the forward when non-NULL; ssm_scan_bwd requires the buffer a
  *     forward with the same descriptor and inputs filled.
+ *   - State carry (all optional, fp32, [batch][nheads][N][P], 16-byte aligned):
+ *     h0 is the state before token 0 (NULL = zero), h_final receives the state
+ *     after the last token, dh0 receives dLoss/dh0 = A_0^T g_0.  The backward
+ *     takes h0 through `saved` (the forward stores it as the first boundary
+ *     state), so a forward with h0 must precede a backward that wants dh0 or
+ *     the h0-dependent parts of the other gradients.  The two-endpoint term of
+ *     token 0 (beta_0 B_{-1} X_{-1}) stays zero with or without h0: an exact
+ *     continuation of a two-endpoint run folds A_0^{-1} beta_0 B_{-1} X_{-1}
+ *     into h0 on the caller's side.
  *   - `ws` is device scratch of at least ssm_workspace_bytes(desc, dir) bytes
  *     (may be NULL when that is 0).  Calls that share a workspace on one
  *     stream are ordered; concurrent calls need separate workspaces.
@@ -66,7 +75,7 @@
 extern "C" {
 #endif
 
-#define SSM_ABI_VERSION 1
+#define SSM_ABI_VERSION 2
 
 typedef enum {
   SSM_OK = 0,
@@ -110,6 +119,8 @@ typedef struct {
   const float *dt, *A, *omega, *beta, *gamma, *D;
   void *y;
   float *saved; /* optional: chunk-boundary states for the backward */
+  const float *h0;  /* optional: state before token 0 (NULL = zero) */
+  float *h_final;   /* optional: receives the state after the last token */
   void *const *events; /* optional: 2 hipEvent_t recorded on `stream` before and after
                           the kernel (per-kernel timing); NULL = none */
 } ssm_fwd_args;
@@ -120,6 +131,7 @@ typedef struct {
   const float *saved; /* filled by ssm_scan_fwd with the same inputs */
   void *dx, *dB, *dC;
   float *ddt, *dA, *domega, *dbeta, *dgamma, *dD;
+  float *dh0;       /* optional: receives dLoss/dh0 */
   void *const *events; /* optional: 4 hipEvent_t recorded on `stream` around the three
                           kernels of the pass (boundary adjoints, chunk gradients,
                           parameter sums); NULL = none */

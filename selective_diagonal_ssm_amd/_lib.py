@@ -39,13 +39,13 @@ _vp = ctypes.c_void_p
 
 class SsmFwdArgs(ctypes.Structure):
     _fields_ = [(n, _vp) for n in ("x", "B", "C", "dt", "A", "omega", "beta", "gamma", "D", "y",
-                                   "saved", "events")]
+                                   "saved", "h0", "h_final", "events")]
 
 
 class SsmBwdArgs(ctypes.Structure):
     _fields_ = [(n, _vp) for n in ("x", "B", "C", "dy", "dt", "A", "omega", "beta", "gamma", "D",
                                    "saved", "dx", "dB", "dC", "ddt", "dA", "domega", "dbeta",
-                                   "dgamma", "dD", "events")]
+                                   "dgamma", "dD", "dh0", "events")]
 
 
 class SsmError(RuntimeError):
@@ -129,12 +129,13 @@ def _events(events):
 
 
 def scan_fwd(desc: SsmDesc, x, B, C, dt, A, y, omega=None, beta=None, gamma=None, D=None,
-             saved=None, ws=None, stream=None, events=None) -> None:
+             saved=None, ws=None, stream=None, events=None, h0=None, h_final=None) -> None:
     """Enqueue the forward scan; all tensors are caller-allocated device tensors.
+    `h0` / `h_final`: optional fp32 [batch][nheads][N][P] initial / final states.
     `events`: optional 2 torch.cuda.Event recorded around the kernel."""
     ev, _keep = _events(events)
     args = SsmFwdArgs(_ptr(x), _ptr(B), _ptr(C), _ptr(dt), _ptr(A), _ptr(omega), _ptr(beta),
-                      _ptr(gamma), _ptr(D), _ptr(y), _ptr(saved), ev)
+                      _ptr(gamma), _ptr(D), _ptr(y), _ptr(saved), _ptr(h0), _ptr(h_final), ev)
     ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
     rc = load().ssm_scan_fwd(ctypes.byref(desc), ctypes.byref(args), _ptr(ws), ws_bytes,
                              _stream(stream))
@@ -144,14 +145,15 @@ def scan_fwd(desc: SsmDesc, x, B, C, dt, A, y, omega=None, beta=None, gamma=None
 
 def scan_bwd(desc: SsmDesc, x, B, C, dy, dt, A, saved, dx, dB, dC, ddt, omega=None, beta=None,
              gamma=None, D=None, dA=None, domega=None, dbeta=None, dgamma=None, dD=None, ws=None,
-             stream=None, events=None) -> None:
+             stream=None, events=None, dh0=None) -> None:
     """Enqueue the fused reverse pass; all tensors are caller-allocated device tensors.
+    `dh0`: optional fp32 [batch][nheads][N][P] gradient of the initial state.
     `events`: optional 4 torch.cuda.Event recorded around the pass's three kernels."""
     ev, _keep = _events(events)
     args = SsmBwdArgs(_ptr(x), _ptr(B), _ptr(C), _ptr(dy), _ptr(dt), _ptr(A), _ptr(omega),
                       _ptr(beta), _ptr(gamma), _ptr(D), _ptr(saved), _ptr(dx), _ptr(dB),
                       _ptr(dC), _ptr(ddt), _ptr(dA), _ptr(domega), _ptr(dbeta), _ptr(dgamma),
-                      _ptr(dD), ev)
+                      _ptr(dD), _ptr(dh0), ev)
     ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
     rc = load().ssm_scan_bwd(ctypes.byref(desc), ctypes.byref(args), _ptr(ws), ws_bytes,
                              _stream(stream))

@@ -190,9 +190,10 @@ int ssm_scan_fwd(const ssm_desc* d, const ssm_fwd_args* a, void* ws, size_t ws_b
   for (const void* q : {a->x, a->B, a->C, (const void*)a->y})
     if (!aligned(q, 16)) return SSM_ERR_ALIGN;
   for (const void* q : {(const void*)a->dt, (const void*)a->A, (const void*)a->omega,
-                        (const void*)a->beta, (const void*)a->gamma, (const void*)a->D,
-                        (const void*)a->saved})
+                        (const void*)a->beta, (const void*)a->gamma, (const void*)a->D})
     if (q && !aligned(q, 4)) return SSM_ERR_ALIGN;
+  for (const void* q : {(const void*)a->saved, (const void*)a->h0, (const void*)a->h_final})
+    if (q && !aligned(q, 16)) return SSM_ERR_ALIGN;
 
   const FwdKey key = choose_fwd(d, pl);
   if (key.PB <= 0 || d->headdim % key.PB) return SSM_ERR_UNSUPPORTED;
@@ -200,6 +201,7 @@ int ssm_scan_fwd(const ssm_desc* d, const ssm_fwd_args* a, void* ws, size_t ws_b
   ssm::FwdParams p{};
   p.x = a->x; p.B = a->B; p.C = a->C; p.dt = a->dt; p.A = a->A; p.omega = a->omega;
   p.beta = a->beta; p.gamma = a->gamma; p.D = a->D; p.y = a->y; p.saved = a->saved;
+  p.h0 = a->h0; p.h_final = a->h_final;
   p.batch = d->batch; p.L = d->seqlen; p.H = d->nheads; p.G = d->ngroups; p.P = d->headdim;
   p.n_real = d->n_real; p.n_pairs = d->n_pairs; p.nchunks = pl.nchunks;
   p.npblk = d->headdim / pb;
@@ -240,6 +242,7 @@ int ssm_scan_bwd(const ssm_desc* d, const ssm_bwd_args* a, void* ws, size_t ws_b
                         (const void*)a->ddt, (const void*)a->dA, (const void*)a->domega,
                         (const void*)a->dbeta, (const void*)a->dgamma, (const void*)a->dD})
     if (q && !aligned(q, 4)) return SSM_ERR_ALIGN;
+  if (a->dh0 && !aligned(a->dh0, 16)) return SSM_ERR_ALIGN;
   const size_t need = ssm_workspace_bytes(d, 1);
   if (!ws || ws_bytes < need) return SSM_ERR_WORKSPACE;
 
@@ -247,7 +250,7 @@ int ssm_scan_bwd(const ssm_desc* d, const ssm_bwd_args* a, void* ws, size_t ws_b
   p.x = a->x; p.B = a->B; p.C = a->C; p.dy = a->dy; p.dt = a->dt; p.A = a->A;
   p.omega = a->omega; p.beta = a->beta; p.gamma = a->gamma; p.D = a->D; p.saved = a->saved;
   p.dx = a->dx; p.dB = a->dB; p.dC = a->dC; p.ddt = a->ddt; p.dbeta = a->dbeta;
-  p.dgamma = a->dgamma; p.dA = a->dA; p.domega = a->domega; p.dD = a->dD;
+  p.dgamma = a->dgamma; p.dA = a->dA; p.domega = a->domega; p.dD = a->dD; p.dh0 = a->dh0;
   p.gseg = static_cast<float*>(ws);
   p.part = reinterpret_cast<float*>(static_cast<char*>(ws) +
                                     (bwd_gseg_bytes(d, pl) + 255) / 256 * 256);

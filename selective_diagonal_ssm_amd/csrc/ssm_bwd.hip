@@ -242,6 +242,41 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_adjoint(BwdParams p) {
       }
     }
   }
+  // dLoss/dh0 = A_0^T g_0, with g_0 (the adjoint at token 0) now in st
+  if (p.dh0) {
+    const float raw = p.dt[(size_t)b * L * H + h];
+    const float d0 = p.softplus ? softplus_f32(raw) : raw;
+    float* dst = p.dh0 + (size_t)slice * N * P + p0;
+#pragma unroll
+    for (int k = 0; k < S::ST_PER_WAVE; ++k) {
+      const int tile = wave + NW * k;
+      if (tile < S::ST_TILES) {
+        const int tnn = tile / S::TP, tp = tile % S::TP;
+        const int pl = 16 * tp + (lane & 15);
+        float v[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int n = 16 * tnn + 4 * (lane >> 4) + i;
+          v[i] = st[k][i] * (COORD ? __expf(-sRate[n] * d0) : __expf(-Ah * d0));
+        }
+        if (COORD) {
+#pragma unroll
+          for (int i = 0; i < 4; i += 2) {
+            const int n = 16 * tnn + 4 * (lane >> 4) + i;
+            if (n >= nreal) {
+              float sn, cs;
+              fast_sincos(sOmega[(n - nreal) >> 1] * d0, &sn, &cs);
+              const float a0 = v[i], a1 = v[i + 1];
+              v[i] = cs * a0 + sn * a1;  // R(-theta_0) = R(theta_0)^T
+              v[i + 1] = -sn * a0 + cs * a1;
+            }
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dst[(size_t)(16 * tnn + 4 * (lane >> 4) + i) * P + pl] = v[i];
+      }
+    }
+  }
 }
 
 // ============================================================== chunk gradients

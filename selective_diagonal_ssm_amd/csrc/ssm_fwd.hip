@@ -131,7 +131,12 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
   }
   // the state entering chunk 0 is zero, and so are its padding rows n >= N for good;
   // score entries above the causal diagonal are zero and never rewritten
-  for (int i = tid; i < 2 * S::NC * VS; i += S::NTH) sST[i] = T(0);
+  // buffer 0 holds the state entering chunk 0: h0 (rows < N, this P-block) or zero
+  const float* h0s = p.h0 ? p.h0 + (size_t)slice * N * P + p0 : nullptr;
+  for (int i = tid; i < 2 * S::NC * VS; i += S::NTH) {
+    const int n = i / VS, col = i % VS;
+    sST[i] = (h0s && n < N && col < PB) ? from_f32<T>(h0s[n * P + col]) : T(0);
+  }
   for (int i = tid; i < S::QO * KS; i += S::NTH) sS[i] = T(0);
   if (S::NC > N) {
     for (int i = tid; i < 2 * S::QO * (S::NC - N); i += S::NTH) {
@@ -162,7 +167,15 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
   // state tiles, transposed: st[k][i] = S[n = 16 tn + (lane & 15)][p = 16 tp + 4 (lane >> 4) + i]
   f32x4 st[S::ST_PER_WAVE];
 #pragma unroll
-  for (int k = 0; k < S::ST_PER_WAVE; ++k) st[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int k = 0; k < S::ST_PER_WAVE; ++k) {
+    st[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int tile = wave * S::ST_PER_WAVE + k;
+    if (h0s && tile < S::ST_TILES) {
+      const int n = 16 * (tile / S::TP) + (lane & 15), pl = 16 * (tile % S::TP) + 4 * (lane >> 4);
+      const float4 v = *reinterpret_cast<const float4*>(h0s + n * P + pl);
+      st[k] = f32x4{v.x, v.y, v.z, v.w};
+    }
+  }
 
   uint4 rc[S::C_PER], rb[S::B_PER], rx[S::X_PER];
   float rdt = 0.f, rbe = 0.f, rga = 0.f;
@@ -378,10 +391,10 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
   const int nch = p.nchunks;
   const size_t sl_saved = (size_t)slice * (nch + 1);
   if (p.saved) {
-    // slot 0: the zero initial state
+    // slot 0: the state entering chunk 0
     for (int i = tid; i < N * PB; i += S::NTH) {
       const int n = i / PB, pl = i % PB;
-      p.saved[(sl_saved * N + n) * P + p0 + pl] = 0.f;
+      p.saved[(sl_saved * N + n) * P + p0 + pl] = h0s ? h0s[n * P + pl] : 0.f;
     }
   }
 
@@ -564,6 +577,17 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
     __syncthreads();
   }
   store_rows(nch - 1);
+  if (p.h_final) {
+    float* hf = p.h_final + (size_t)slice * N * P + p0;
+#pragma unroll
+    for (int k = 0; k < S::ST_PER_WAVE; ++k) {
+      const int tile = wave * S::ST_PER_WAVE + k;
+      if (tile < S::ST_TILES) {
+        const int n = 16 * (tile / S::TP) + (lane & 15), pl = 16 * (tile % S::TP) + 4 * (lane >> 4);
+        *reinterpret_cast<float4*>(hf + n * P + pl) = make_float4(st[k][0], st[k][1], st[k][2], st[k][3]);
+      }
+    }
+  }
 }
 
 // ------------------------------------------------------------------ dispatch

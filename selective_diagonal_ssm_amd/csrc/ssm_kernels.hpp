@@ -18,6 +18,8 @@ struct FwdParams {
   const float* D;
   void* y;
   float* saved;  // [batch][nheads][nchunks + 1][N][P] fp32, or null
+  const float* h0;  // [batch][nheads][N][P] fp32 state before token 0, or null
+  float* h_final;   // [batch][nheads][N][P] fp32 state after the last token, or null
   int batch, L, H, G, P, n_real, n_pairs, nchunks, npblk;
   int softplus, has_D;
   int head_rates;  // A holds one rate per head even though the per-row kernel runs
@@ -46,6 +48,7 @@ struct BwdParams {
   float* dA;
   float* domega;
   float* dD;
+  float* dh0;  // [batch][nheads][N][P] fp32, or null
   int batch, L, H, G, P, n_real, n_pairs, nchunks, nseg, chunks_per_seg;
   int softplus, has_D, npart;
   int head_rates;

@@ -14,9 +14,11 @@ def _dtype(io_dtype: str):
 
 
 def forward(desc_dict: dict, io_dtype: str, x, B, C, dt, A, omega=None, beta=None, gamma=None,
-            D=None, save_for_backward: bool = False, chunk: int = 0, stream=None):
+            D=None, save_for_backward: bool = False, chunk: int = 0, stream=None, h0=None,
+            return_final_state: bool = False):
     """Run the forward scan.  Returns (y, saved) where saved is None unless
-    ``save_for_backward``."""
+    ``save_for_backward``; with ``return_final_state`` returns (y, saved, h_final).
+    ``h0``: optional fp32 [batch][nheads][N][P] state before token 0."""
     desc = _lib.make_desc(desc_dict, io_dtype, chunk)
     d = desc_dict
     y = torch.empty((d["batch"], d["seqlen"], d["nheads"], d["rank_out"], d["headdim"]),
@@ -27,15 +29,22 @@ def forward(desc_dict: dict, io_dtype: str, x, B, C, dt, A, omega=None, beta=Non
         saved = torch.empty(max(nbytes // 4, 1), dtype=torch.float32, device=x.device)
     wsb = _lib.workspace_bytes(desc, False)
     ws = torch.empty(wsb, dtype=torch.uint8, device=x.device) if wsb else None
+    h_final = None
+    if return_final_state:
+        h_final = torch.empty((d["batch"], d["nheads"], d["dstate"], d["headdim"]),
+                              dtype=torch.float32, device=x.device)
     _lib.scan_fwd(desc, x, B, C, dt, A, y, omega=omega, beta=beta, gamma=gamma, D=D, saved=saved,
-                  ws=ws, stream=stream)
+                  ws=ws, stream=stream, h0=h0, h_final=h_final)
+    if return_final_state:
+        return y, saved, h_final
     return y, saved
 
 
 def backward(desc_dict: dict, io_dtype: str, x, B, C, dy, dt, A, saved, omega=None, beta=None,
              gamma=None, D=None, chunk: int = 0, stream=None, want=("dA", "domega", "dbeta",
                                                                      "dgamma", "dD")):
-    """Run the fused reverse pass.  Returns a dict of gradient tensors."""
+    """Run the fused reverse pass.  Returns a dict of gradient tensors (``dh0`` too
+    when "dh0" is in ``want``)."""
     desc = _lib.make_desc(desc_dict, io_dtype, chunk)
     d = desc_dict
     dev = x.device
@@ -57,10 +66,13 @@ def backward(desc_dict: dict, io_dtype: str, x, B, C, dy, dt, A, saved, omega=No
             g["dgamma"] = torch.empty_like(dt)
     if d["has_D"] and "dD" in want:
         g["dD"] = torch.empty((d["nheads"],), dtype=f32, device=dev)
+    if "dh0" in want:
+        g["dh0"] = torch.empty((d["batch"], d["nheads"], d["dstate"], d["headdim"]), dtype=f32,
+                               device=dev)
     wsb = _lib.workspace_bytes(desc, True)
     ws = torch.empty(wsb, dtype=torch.uint8, device=dev) if wsb else None
     _lib.scan_bwd(desc, x, B, C, dy, dt, A, saved, g["dx"], g["dB"], g["dC"], g["ddt"],
                   omega=omega, beta=beta, gamma=gamma, D=D, dA=g.get("dA"),
                   domega=g.get("domega"), dbeta=g.get("dbeta"), dgamma=g.get("dgamma"),
-                  dD=g.get("dD"), ws=ws, stream=stream)
+                  dD=g.get("dD"), ws=ws, stream=stream, dh0=g.get("dh0"))
     return g

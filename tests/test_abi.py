@@ -27,7 +27,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_abi_version_and_status_strings():
     lib = ssm.load()
-    assert lib.ssm_abi_version() == 1
+    assert lib.ssm_abi_version() == 2
     for s in range(0, -8, -1):
         assert lib.ssm_status_string(s)
 
@@ -96,3 +96,37 @@ def test_null_pointers_rejected_before_launch():
     d2 = _lib.make_desc(base_desc(has_D=False), "bf16")
     args.x = 0x1000
     assert lib.ssm_scan_fwd(ctypes.byref(d2), ctypes.byref(args), None, 0, None) == -1
+
+
+def header_struct_fields(name):
+    """Member names of a typedef struct in include/ssm_scan.h, in declaration order."""
+    import re
+    text = open(os.path.join(ROOT, "include", "ssm_scan.h")).read()
+    body = re.search(r"typedef struct \{([^{}]*)\}\s*" + name + ";", text).group(1)
+    body = re.sub(r"/\*.*?\*/", "", body, flags=re.S)
+    names = []
+    for decl in body.split(";"):
+        decl = decl.strip()
+        if not decl:
+            continue
+        for part in decl.split(","):
+            names.append(re.findall(r"[A-Za-z_][A-Za-z0-9_]*", part)[-1])
+    return names
+
+
+def test_ctypes_structs_match_header_layout():
+    assert [f[0] for f in _lib.SsmDesc._fields_] == header_struct_fields("ssm_desc")
+    assert [f[0] for f in _lib.SsmFwdArgs._fields_] == header_struct_fields("ssm_fwd_args")
+    assert [f[0] for f in _lib.SsmBwdArgs._fields_] == header_struct_fields("ssm_bwd_args")
+
+
+def test_state_carry_pointers_must_be_aligned():
+    lib = ssm.load()
+    d = _lib.make_desc(base_desc(), "bf16")
+    args = _lib.SsmFwdArgs(*[0x1000 * (i + 1) for i in range(11)])
+    args.omega = args.beta = args.gamma = args.saved = None
+    args.h0 = 0x2008  # 8-byte aligned only
+    assert lib.ssm_scan_fwd(ctypes.byref(d), ctypes.byref(args), None, 0, None) == -4
+    args.h0 = None
+    args.h_final = 0x2004
+    assert lib.ssm_scan_fwd(ctypes.byref(d), ctypes.byref(args), None, 0, None) == -4

@@ -1,0 +1,116 @@
+"""GPU parity of the state carry (initial state h0, final state, dLoss/dh0)
+against the fp64 oracle, which takes h0 as the state before token 0 and returns
+the state after the last token and A_0^T g_0 (its pin P9 checks that a split
+run carries the state exactly).
+
+Tolerances as everywhere: rel-L2 1e-4 (fp32 path), 1e-2 (bf16 path).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import selective_diagonal_ssm_amd as ssm
+import workloads
+from gpu_util import rel_l2, tol
+
+pytestmark = pytest.mark.gpu
+
+CASES = {
+    "f32_head": ("ssd_siso", dict(dtype="f32", dstate=32, n_real=32, headdim=16, batch=2,
+                                  nheads=2, ngroups=2, seqlen=150)),
+    "f32_head_r2": ("ssd_mimo", dict(dtype="f32", dstate=32, n_real=32, headdim=16, rank_in=2,
+                                     rank_out=2, batch=2, nheads=2, ngroups=2, seqlen=90)),
+    "f32_coord_plain": ("hybrid", dict(dtype="f32", two_endpoint=False, dstate=32, n_real=16,
+                                       n_pairs=8, headdim=16, batch=2, nheads=2, ngroups=2,
+                                       seqlen=75)),
+    "f32_hybrid": ("hybrid", dict(dtype="f32", dstate=32, n_real=16, n_pairs=8, headdim=16,
+                                  batch=2, nheads=2, ngroups=2, seqlen=77)),
+    "bf16_ssd_siso": ("ssd_siso", dict(batch=2, seqlen=200, nheads=2, ngroups=2)),
+    "bf16_ssd_mimo": ("ssd_mimo", dict(batch=2, seqlen=100, nheads=2, ngroups=2)),
+    "bf16_hybrid": ("hybrid", dict(batch=2, seqlen=90, nheads=2, ngroups=2)),
+}
+
+
+def _fwd(prob, t, h0=None, save=False):
+    y, saved, hf = ssm.forward(prob["desc"], prob["dtype"], t["x"], t["B"], t["C"], t["dt"],
+                               t["A"], omega=t.get("omega"), beta=t.get("beta"),
+                               gamma=t.get("gamma"), D=t.get("D"), save_for_backward=save,
+                               h0=h0, return_final_state=True)
+    return y, saved, hf
+
+
+def _np(v):
+    return v.float().cpu().numpy().astype(np.float64)
+
+
+@pytest.mark.parametrize("case", sorted(CASES))
+def test_forward_with_initial_state_matches_oracle(case):
+    name, kw = CASES[case]
+    prob = workloads.make_problem(workloads.spec(name, **kw), seed=3)
+    h0 = workloads.make_state(prob["desc"], seed=5)
+    print(f"[state-fwd] case={case} desc={prob['desc']}", flush=True)
+    t = workloads.to_device(prob)
+    y, _, hf = _fwd(prob, t, h0=torch.from_numpy(h0).cuda())
+    torch.cuda.synchronize()
+    yr, hr = oracle.fwd(prob, h0=h0.astype(np.float64))
+    ey, eh = rel_l2(_np(y), yr), rel_l2(_np(hf), hr)
+    print(f"[state-fwd] case={case} y={ey:.2e} h_final={eh:.2e}", flush=True)
+    assert ey <= tol(prob) and eh <= tol(prob), (ey, eh)
+
+
+@pytest.mark.parametrize("case", ["f32_head", "f32_head_r2", "f32_coord_plain", "bf16_ssd_siso",
+                                  "bf16_ssd_mimo"])
+def test_split_run_carries_state(case):
+    """Two GPU runs chained through h_final -> h0 reproduce one run over the whole
+    sequence (writes without a two-endpoint term, whose token-0 part is not
+    carried)."""
+    name, kw = CASES[case]
+    prob = workloads.make_problem(workloads.spec(name, **kw), seed=7)
+    L = prob["desc"]["seqlen"]
+    L1 = L // 2 + 5  # not a chunk multiple
+    print(f"[state-split] case={case} L={L} L1={L1}", flush=True)
+    t = workloads.to_device(prob)
+    y_full, _, h_full = _fwd(prob, t)
+
+    def part(lo, hi):
+        q = dict(prob)
+        q["desc"] = dict(prob["desc"], seqlen=hi - lo)
+        tq = {k: (v[:, lo:hi].contiguous() if k in ("x", "B", "C", "dt") else v)
+              for k, v in t.items()}
+        return q, tq
+
+    q1, t1 = part(0, L1)
+    y1, _, h1 = _fwd(q1, t1)
+    q2, t2 = part(L1, L)
+    y2, _, h2 = _fwd(q2, t2, h0=h1)
+    torch.cuda.synchronize()
+    ey = rel_l2(np.concatenate([_np(y1), _np(y2)], axis=1), _np(y_full))
+    eh = rel_l2(_np(h2), _np(h_full))
+    print(f"[state-split] case={case} y={ey:.2e} h={eh:.2e}", flush=True)
+    assert ey <= tol(prob) and eh <= tol(prob), (ey, eh)
+
+
+GRADS = ["dx", "dB", "dC", "ddt", "dA", "domega", "dbeta", "dgamma", "dD", "dh0"]
+
+
+@pytest.mark.parametrize("case", sorted(CASES))
+def test_backward_with_initial_state_matches_oracle(case):
+    name, kw = CASES[case]
+    prob = workloads.make_problem(workloads.spec(name, **kw), seed=11, with_dy=True)
+    h0 = workloads.make_state(prob["desc"], seed=13)
+    print(f"[state-bwd] case={case} desc={prob['desc']}", flush=True)
+    t = workloads.to_device(prob)
+    _, saved, _ = _fwd(prob, t, h0=torch.from_numpy(h0).cuda(), save=True)
+    g = ssm.backward(prob["desc"], prob["dtype"], t["x"], t["B"], t["C"], t["dy"], t["dt"],
+                     t["A"], saved, omega=t.get("omega"), beta=t.get("beta"),
+                     gamma=t.get("gamma"), D=t.get("D"),
+                     want=("dA", "domega", "dbeta", "dgamma", "dD", "dh0"))
+    torch.cuda.synchronize()
+    ref = oracle.bwd(prob, prob["dy"], h0=h0.astype(np.float64))
+    errs = {k: rel_l2(_np(g[k]), ref[k]) for k in GRADS if k in g and ref.get(k) is not None}
+    print(f"[state-bwd] case={case} " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()),
+          flush=True)
+    assert "dh0" in errs
+    bad = {k: v for k, v in errs.items() if not v <= tol(prob)}
+    assert not bad, bad

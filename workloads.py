@@ -127,6 +127,13 @@ def make_problem(spec_or_name, seed: int = 0, with_dy: bool | None = None) -> di
     return prob
 
 
+def make_state(desc: dict, seed: int = 0, scale: float = 1.0) -> np.ndarray:
+    """A seeded initial state h0, fp32 [batch][nheads][dstate][headdim] ~ N(0, scale^2)."""
+    rng = np.random.default_rng(seed)
+    shape = (desc["batch"], desc["nheads"], desc["dstate"], desc["headdim"])
+    return (rng.standard_normal(shape, dtype=np.float32) * np.float32(scale)).astype(np.float32)
+
+
 def to_device(prob: dict, device="cuda"):
     """Copy a problem's arrays to torch tensors on `device` (x, B, C, dy in the
     io dtype; the rest fp32)."""
