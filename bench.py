@@ -97,11 +97,15 @@ def cpu_baseline(prob: dict, mode: str, target_s: float = 15.0):
     k2 = max(threads, (k2 // threads) * threads) if k2 >= threads else k2
     k2 = min(k2, len(all_slices))
     sample = all_slices[:k2]
-    t = run(sample)
-    tokens = k2 * d["seqlen"] / d["nheads"]  # (batch, position) tokens across all heads
+    # a whole-workload pass that is short is repeated up to ~2/3 of the target time
+    reps, t = 0, 0.0
+    while reps == 0 or (k2 == len(all_slices) and t < target_s * 2 / 3 and reps < 64):
+        t += run(sample)
+        reps += 1
+    tokens = reps * k2 * d["seqlen"] / d["nheads"]  # (batch, position) tokens across all heads
     return {"value": tokens / t / 1e6, "unit": "Mtokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"{k2} of {len(all_slices)} (batch, head) slices, full length "
-                      f"{d['seqlen']}, {'forward + reverse' if mode == 'fwdbwd' else 'forward'}"
+            "sample": f"{k2} of {len(all_slices)} (batch, head) slices x {reps} pass(es), full "
+                      f"length {d['seqlen']}, {'forward + reverse' if mode == 'fwdbwd' else 'forward'}"
                       f", fp64, {t:.1f} s"}
 
 
