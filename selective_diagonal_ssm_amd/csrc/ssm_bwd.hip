@@ -138,9 +138,9 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_adjoint(BwdParams p) {
     float dl = 0.f;
     if (lane < QT && t0 + lane < L) dl = p.softplus ? softplus_f32(pdt) : pdt;
     const float cd = wave_prefix_sum(dl);
-    const float cdx = cd - __shfl(dl, 0, kWave);               // sum over (t0, t]
-    const float cdx_end = __shfl(cdx, QT - 1, kWave) + dnext;  // sum over (t0, t0']
-    dnext = __shfl(dl, 0, kWave);
+    const float cdx = cd - read_lane(dl, 0);               // sum over (t0, t]
+    const float cdx_end = read_lane(cdx, QT - 1) + dnext;  // sum over (t0, t0']
+    dnext = read_lane(dl, 0);
 
     // operands: rows (t, o) of  e^{L'_t} R(-Theta'_t) C_t  and  dy_t
 #pragma unroll
@@ -372,6 +372,7 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
   __shared__ float sTw[64], sTel[64], sTlc[64];    // head: e^{L_end - L_t}, e^{L_t}, -A CD log2(e)
   __shared__ float sTga[S::TE ? 64 : 1], sTbe[S::TE ? 64 : 1];
   __shared__ float sMisc[NW];
+  __shared__ float sPartOut[N + N / 2 + 2];  // parameter partials of the item (stored a step later)
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int nch = p.nchunks;
@@ -502,6 +503,28 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
     }
   };
 
+  // The per-token scalar gradients and the parameter partials of an item are
+  // stored during the next item, after its prefetch: they come from wave 0 at the
+  // very end of an item, and storing them at once would make wave 0's wait for its
+  // next prefetched loads include them, with every other wave held at the barrier.
+  float o_ddt = 0.f, o_dg = 0.f, o_db = 0.f;
+  auto flush_scalars = [&](int it) {
+    const int slice = it / nch, c = it % nch;
+    const int b = slice / H, h = slice % H;
+    const int t0 = c * QT;
+    if (wave == 0 && lane < QT && t0 + lane < L) {
+      const size_t idx = ((size_t)b * L + t0 + lane) * H + h;
+      p.ddt[idx] = o_ddt;
+      if (S::TE) {
+        if (p.dgamma) p.dgamma[idx] = o_dg;
+        if (p.dbeta) p.dbeta[idx] = o_db;
+      }
+    }
+    if (p.part)
+      for (int k = tid; k < p.npart; k += S::NTH) p.part[((size_t)slice * nch + c) * p.npart + k] = sPartOut[k];
+  };
+
+  int prev = -1;
   int item = blockIdx.x;
   if (item < nitems) prefetch(item);
   for (; item < nitems; item += gridDim.x) {
@@ -548,7 +571,7 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
       if (S::TE) bnext = pf_bn;
     }
     const float cd_l = wave_prefix_sum(dl);
-    const float cdend = __shfl(cd_l, QT - 1, kWave);
+    const float cdend = read_lane(cd_l, QT - 1);
     const float w_l = COORD ? 0.f : __expf(-Ah * (cdend - cd_l));   // e^{L_end - L_t}
     const float el_l = COORD ? 0.f : __expf(-Ah * cd_l);            // e^{L_t}
     if (wave == 0 && lane < QT) {
@@ -754,6 +777,7 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
     }
     // the next item's loads go out now and land while this one computes
     if (item + static_cast<int>(gridDim.x) < nitems) prefetch(item + gridDim.x);
+    if (prev >= 0) flush_scalars(prev);
     __syncthreads();
     if (p.has_D) {
       for (int i = tid; i < QO * P; i += S::NTH) {
@@ -810,8 +834,8 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
         // keys of one row), column sums per key token (the 16 lanes of a group hold
         // the 16 rows of each key)
         float rs = (wv[0] + wv[1]) + (wv[2] + wv[3]);
-        rs += __shfl_xor(rs, 16, kWave);
-        rs += __shfl_xor(rs, 32, kWave);
+        rs = add_xor16(rs);
+        rs = add_xor32(rs);
         rs = group_sum<R>(rs);
         if (lane < 16 && (lane % R) == 0) sRS[wave][t] += rs;
         float cs[4];
@@ -992,12 +1016,12 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
         }
       }
       // per-key sums over the 4 row groups, then over the keys of one token
-      tokacc += __shfl_xor(tokacc, 16, kWave);
-      tokacc += __shfl_xor(tokacc, 32, kWave);
+      tokacc = add_xor16(tokacc);
+      tokacc = add_xor32(tokacc);
       tokacc = group_sum<KR>(tokacc);
       if (S::TE) {
-        dgb += __shfl_xor(dgb, 16, kWave);
-        dgb += __shfl_xor(dgb, 32, kWave);
+        dgb = add_xor16(dgb);
+        dgb = add_xor32(dgb);
         dgb = group_sum<R>(dgb);
       }
       if (lane < 16) {
@@ -1087,8 +1111,8 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
           }
         }
       }
-      tokacc += __shfl_xor(tokacc, 16, kWave);
-      tokacc += __shfl_xor(tokacc, 32, kWave);
+      tokacc = add_xor16(tokacc);
+      tokacc = add_xor32(tokacc);
       tokacc = group_sum<R>(tokacc);
       if (lane < 16 && (lane % R) == 0) {
         if (COORD) sTok[wave][t] += tokacc;
@@ -1170,22 +1194,21 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
       const float rev = tot - pre + tok;
       const int t = t0 + lane;
       if (lane < QT && t < L) {
-        const size_t idx = ((size_t)b * L + t) * H + h;
-        p.ddt[idx] = p.softplus ? rev * sigmoid_f32(raw_l) : rev;
+        o_ddt = p.softplus ? rev * sigmoid_f32(raw_l) : rev;
         if (S::TE) {
-          if (p.dgamma) p.dgamma[idx] = wsum<WT>(sDg, lane);
-          if (p.dbeta) p.dbeta[idx] = wsum<WT>(sDb, lane);
+          o_dg = wsum<WT>(sDg, lane);
+          o_db = wsum<WT>(sDb, lane);
         }
       }
       if (!COORD && p.part) {
         // dA_h partial = sum_t (-cd_t) D_t
         const float v = wave_sum(lane < QT ? -cd_l * dunw : 0.f);
-        if (lane == 0) p.part[((size_t)slice * nch + c) * p.npart] = v;
+        if (lane == 0) sPartOut[0] = v;
       }
     }
     // parameter partials of this chunk (per-row mode)
     if (p.part) {
-      float* dst = p.part + ((size_t)slice * nch + c) * p.npart;
+      float* dst = sPartOut;
       const int na = (COORD && !p.head_rates) ? nreal + npairs : 1;
       if (COORD) {
         __syncthreads();
@@ -1213,7 +1236,10 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
       }
       if (tid == 0) dst[na + npairs] = wsum1<NW>(sMisc);
     }
+    prev = item;
   }  // items
+  __syncthreads();
+  if (prev >= 0) flush_scalars(prev);
 }
 
 // ============================================================== parameter sums

@@ -241,10 +241,34 @@ __device__ __forceinline__ float group_sum(float v) {
   return v;
 }
 
+// value of v in lane `src` (src must be the same for the whole wave)
+__device__ __forceinline__ float read_lane(float v, int src) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), src));
+}
+
+// v + (v of lane l ^ 16) and v + (v of lane l ^ 32), by the gfx950 VALU row swaps
+// v_permlane16_swap / v_permlane32_swap applied to two copies of v (both lanes of a
+// pair add their two values in the same order)
+__device__ __forceinline__ float add_xor16(float v) {
+  const unsigned u = __float_as_uint(v);
+  const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float add_xor32(float v) {
+  const unsigned u = __float_as_uint(v);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// sum over the 64 lanes of a wave (every lane receives the same value): DPP sums
+// inside the four 16-lane rows, then the row totals read from lanes 0, 16, 32, 48
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
-  return v;
+  v = group_sum<16>(v);
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return (r0 + r1) + (r2 + r3);
 }
 
 // softplus(v) = log(1 + e^v) with hardware exp/log: log1p(u) is evaluated as
