@@ -367,6 +367,10 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
   __shared__ __align__(16) float sDX[S::TE ? 2 * (QT + 1) * R * P : 4];  // two-endpoint dX assembly
   __shared__ __align__(16) float sDB[S::TE ? 2 * (QT + 1) * R * N : 4];  // two-endpoint dB assembly
   __shared__ __align__(16) float sTailX[S::TE ? R * P : 4], sTailB[S::TE ? R * N : 4];
+  // two-endpoint tail inputs: the next chunk's raw first adjoint g', B and X of the
+  // chunk's last token
+  __shared__ __align__(16) float sGraw[S::TE ? N * P : 4];
+  __shared__ __align__(16) T sBt1[S::TE ? R * N : 8], sXt1[S::TE ? R * P : 8];
   // per-token factors of the current item (token = index)
   __shared__ float sTcd[64];                       // cumulative step inside the chunk
   __shared__ float sTw[64], sTel[64], sTlc[64];    // head: e^{L_end - L_t}, e^{L_t}, -A CD log2(e)
@@ -629,6 +633,7 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
       const float cdv[2] = {__shfl(cd_l, ta, kWave), __shfl(cd_l, tb, kWave)};
       const float wv[2] = {S::TE ? __shfl(ga_l, ta, kWave) : 1.f, S::TE ? __shfl(be_l, tb, kWave) : 0.f};
       if (v >= S::B_VECS) continue;
+      if (S::TE && sl == QT - 1) *reinterpret_cast<uint4*>(sBt1 + r * N + n0) = pfb[k];
       float vals[VEC];
       unpack<BF16>(pfb[k], vals);
   #pragma unroll
@@ -674,6 +679,7 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
       const int row = v / (P / VEC), p0 = (v % (P / VEC)) * VEC;
       const int sl = row / R - S::TEH, r = row % R;
       if (sl >= 0) *reinterpret_cast<uint4*>(sV + (sl * KR + r) * PS + p0) = pfx[k];
+      if (S::TE && sl == QT - 1) *reinterpret_cast<uint4*>(sXt1 + r * P + p0) = pfx[k];
       if (S::TE && sl + 1 < QT) *reinterpret_cast<uint4*>(sV + ((sl + 1) * KR + R + r) * PS + p0) = pfx[k];
     }
   #pragma unroll
@@ -686,8 +692,6 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
     // incoming state S_in and folded adjoint G~ = e^{-A Dnext} R(-omega (cd_end + Dnext)) g'
     // (split into bf16 hi + lo), final-state terms per row / pair
     {
-      const float* Gg = p.gseg + ((size_t)slice * nch + (c + 1)) * N * P;
-      const bool gvalid = has_next;
       const float lend_h = COORD ? 0.f : __expf(-Ah * cdend);
       const float gdec_h = COORD ? 0.f : __expf(-Ah * dnext);
   #pragma unroll
@@ -700,6 +704,10 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
         float sb[4] = {pfs[k][1].x, pfs[k][1].y, pfs[k][1].z, pfs[k][1].w};
         float ga[4] = {pfg[k][0].x, pfg[k][0].y, pfg[k][0].z, pfg[k][0].w};
         float gb[4] = {pfg[k][1].x, pfg[k][1].y, pfg[k][1].z, pfg[k][1].w};
+        if (S::TE) {
+          *reinterpret_cast<float4*>(sGraw + n * P + q0) = pfg[k][0];
+          *reinterpret_cast<float4*>(sGraw + (n + 1) * P + q0) = pfg[k][1];
+        }
         float fa, fb, lea, leb;
         if (COORD) {
           fa = __expf(-sRate[n] * dnext); fb = __expf(-sRate[n + 1] * dnext);
@@ -752,33 +760,27 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
         split(ga, sGh + n * PS + q0, sGl + n * PS + q0);
         split(gb, sGh + (n + 1) * PS + q0, sGl + (n + 1) * PS + q0);
       }
-      // two-endpoint tails of the last token: beta_{t0'} B_{t1}^T g' and g' X_{t1}^T
-      if (S::TE) {
-        const int t1 = t0 + QT - 1;
-        for (int i = tid; i < R * P; i += S::NTH) {
-          const int r = i / P, pp = i % P;
-          float acc = 0.f;
-          if (gvalid) {
-            for (int n = 0; n < N; ++n)
-              acc += to_f32(Bg[((((size_t)b * L + t1) * G + g) * R + r) * N + n]) * Gg[(size_t)n * P + pp];
-          }
-          sTailX[i] = bnext * acc;
-        }
-        for (int i = tid; i < R * N; i += S::NTH) {
-          const int r = i / N, n = i % N;
-          float acc = 0.f;
-          if (gvalid) {
-            for (int pp = 0; pp < P; ++pp)
-              acc += Gg[(size_t)n * P + pp] * to_f32(xg[((((size_t)b * L + t1) * H + h) * R + r) * P + pp]);
-          }
-          sTailB[i] = bnext * acc;
-        }
-      }
     }
     // the next item's loads go out now and land while this one computes
     if (item + static_cast<int>(gridDim.x) < nitems) prefetch(item + gridDim.x);
     if (prev >= 0) flush_scalars(prev);
     __syncthreads();
+    // two-endpoint tails of the last token from the staged rows: beta_{t0'} B_{t1}^T g'
+    // and g' X_{t1}^T (zero without a next chunk, where g' and beta_{t0'} are zero)
+    if (S::TE) {
+      for (int i = tid; i < R * P; i += S::NTH) {
+        const int r = i / P, pp = i % P;
+        float acc = 0.f;
+        for (int n = 0; n < N; ++n) acc += to_f32(sBt1[r * N + n]) * sGraw[n * P + pp];
+        sTailX[i] = bnext * acc;
+      }
+      for (int i = tid; i < R * N; i += S::NTH) {
+        const int r = i / N, n = i % N;
+        float acc = 0.f;
+        for (int pp = 0; pp < P; ++pp) acc += sGraw[n * P + pp] * to_f32(sXt1[r * P + pp]);
+        sTailB[i] = bnext * acc;
+      }
+    }
     if (p.has_D) {
       for (int i = tid; i < QO * P; i += S::NTH) {
         const int row = i / P, pp = i % P, tl = row / R, o = row % R;
