@@ -2,6 +2,7 @@
 // plan selection (kernel variant, chunk length, P-blocks), launches.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdlib>
 #include <cstring>
 
@@ -82,6 +83,30 @@ int make_plan(const ssm_desc* d, Plan* pl) {
 // P-blocks) workgroups cover the machine without needless P-splitting (a split
 // recomputes the chunk scores once per block).  SSM_FWD_PB / SSM_FWD_THREADS
 // force a choice among the instantiated variants (experiments).
+// Sequence segments: when the (slice, P-block) units alone leave compute units idle,
+// each sequence is split into segments that run in parallel and exchange their
+// boundary states (local pass, combine, full pass).  Each segment keeps at least
+// kMinSegChunks chunks.  The choice depends on the descriptor only, because the
+// workspace size follows from it.
+constexpr long kTargetUnits = 256;  // compute units of an MI355X
+constexpr int kMinSegChunks = 4;
+struct Segs {
+  int nseg, cps;
+};
+Segs segments(long units, int nch) {
+  if (nch <= 0) return {1, 1};  // empty sequence: nothing to split
+  int nseg = 1;
+  const int force = env_int("SSM_NSEG", 0);
+  if (force > 0) {
+    nseg = force;
+  } else if (units < kTargetUnits * 3 / 4) {
+    nseg = (int)std::min<long>(kTargetUnits / std::max(units, 1L), nch / kMinSegChunks);
+  }
+  nseg = std::max(1, std::min(nseg, std::max(nch, 1)));
+  const int cps = (nch + nseg - 1) / nseg;
+  return {(nch + cps - 1) / cps, cps};  // no empty segment
+}
+
 FwdKey choose_fwd(const ssm_desc* d, const Plan& pl) {
   const int force_pb = env_int("SSM_FWD_PB", 0);
   const int force_nt = env_int("SSM_FWD_THREADS", 0);
@@ -95,10 +120,13 @@ FwdKey choose_fwd(const ssm_desc* d, const Plan& pl) {
       if (force_nt && nt != force_nt) continue;
       FwdKey k{pl.bf16, d->dstate, pb, pl.R, pl.KR, pl.QT, pl.coord_kernel, nt};
       if (!ssm::fwd_variant_exists(k)) continue;
-      // score: enough workgroups to occupy the 256 compute units (at least
-      // ~0.75 of them), then the widest P-block, then the widest workgroup
+      // score: enough workgroups (counting sequence segments) to occupy the 256
+      // compute units (at least ~0.75 of them), then the widest P-block, then the
+      // fewest segments, then the widest workgroup
       const long wgs = slices * (d->headdim / pb);
-      const long score = (wgs >= 192 ? 1000000L : wgs * 1000L) + pb * 100L + nt / 16;
+      const Segs sg = segments(wgs, pl.nchunks);
+      const long units = wgs * sg.nseg;
+      const long score = (units >= 192 ? 1000000L : units * 1000L) + pb * 100L - sg.nseg + nt / 64;
       if (score > best_score) {
         best_score = score;
         best = k;
@@ -162,10 +190,21 @@ static size_t bwd_gseg_bytes(const ssm_desc* d, const Plan& pl) {
   return (size_t)d->batch * d->nheads * pl.nchunks * d->dstate * d->headdim * sizeof(float);
 }
 
+static size_t fwd_segment_bytes(const ssm_desc* d, const Plan& pl, const FwdKey& key) {
+  const long slices = (long)d->batch * d->nheads;
+  const Segs sg = segments(slices * (d->headdim / key.PB), pl.nchunks);
+  if (sg.nseg <= 1) return 0;
+  const size_t st = (size_t)slices * sg.nseg * d->dstate * d->headdim * sizeof(float);
+  return 2 * st + ((size_t)slices * sg.nseg * sizeof(float) + 255) / 256 * 256;
+}
+
 size_t ssm_workspace_bytes(const ssm_desc* d, int for_backward) {
   Plan pl;
   if (make_plan(d, &pl)) return 0;
-  if (!for_backward) return 0;
+  if (!for_backward) {
+    const FwdKey key = choose_fwd(d, pl);
+    return key.PB > 0 ? fwd_segment_bytes(d, pl, key) : 0;
+  }
   const size_t g = (bwd_gseg_bytes(d, pl) + 255) / 256 * 256;
   const size_t part = (size_t)d->batch * d->nheads * pl.nchunks * npart_of(d, pl) * sizeof(float);
   return g + part;
@@ -177,8 +216,6 @@ int ssm_scan_fwd(const ssm_desc* d, const ssm_fwd_args* a, void* ws, size_t ws_b
   int rc = make_plan(d, &pl);
   if (rc) return rc;
   if (!a) return SSM_ERR_NULL;
-  (void)ws;
-  (void)ws_bytes;
   // an empty problem touches no memory (empty tensors may have NULL pointers)
   if (d->batch == 0 || d->seqlen == 0) return SSM_OK;
   const bool te = (d->flags & SSM_F_TWO_ENDPOINT) != 0;
@@ -208,6 +245,18 @@ int ssm_scan_fwd(const ssm_desc* d, const ssm_fwd_args* a, void* ws, size_t ws_b
   p.softplus = (d->flags & SSM_F_DT_SOFTPLUS) ? 1 : 0;
   p.has_D = hasD ? 1 : 0;
   p.head_rates = pl.head_rates ? 1 : 0;
+  const Segs sg = segments((long)d->batch * d->nheads * p.npblk, pl.nchunks);
+  p.nseg = sg.nseg;
+  p.cps = sg.cps;
+  if (sg.nseg > 1) {
+    const size_t need = fwd_segment_bytes(d, pl, key);
+    if (!ws || ws_bytes < need) return SSM_ERR_WORKSPACE;
+    if (!aligned(ws, 16)) return SSM_ERR_ALIGN;
+    const size_t st = (size_t)d->batch * d->nheads * sg.nseg * d->dstate * d->headdim;
+    p.seg_local = static_cast<float*>(ws);
+    p.seg_in = p.seg_local + st;
+    p.seg_delta = p.seg_in + st;
+  }
   const hipError_t e = ssm::launch_fwd(key, p, static_cast<hipStream_t>(stream), a->events);
   return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
 }

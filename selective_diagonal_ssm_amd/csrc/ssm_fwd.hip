@@ -30,6 +30,8 @@
 // Part 03 (recurrence; Theorem 24 masked linear attention form; Theorem 8 rotating
 // pairs), Parts 03 / 08.3 (SSD-MIMO rank-R writes, HybridMamba rows and
 // two-endpoint writes).
+#include <algorithm>
+
 #include "ssm_device.hpp"
 #include "ssm_kernels.hpp"
 
@@ -111,7 +113,10 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int lid = xcd_logical_id(blockIdx.x, gridDim.x);
-  const int slice = lid / p.npblk, pblk = lid % p.npblk;
+  const int slice = lid / (p.npblk * p.nseg), seg = (lid / p.npblk) % p.nseg, pblk = lid % p.npblk;
+  const bool local = p.state_only != 0;
+  if (local && seg == p.nseg - 1) return;  // the last segment's local state is never needed
+  const int c0 = seg * p.cps, c1 = min(p.nchunks, c0 + p.cps);  // this workgroup's chunks
   const int b = slice / p.H, h = slice % p.H;
   const int g = h / (p.H / p.G);
   const int p0 = pblk * PB;
@@ -131,8 +136,10 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
   }
   // the state entering chunk 0 is zero, and so are its padding rows n >= N for good;
   // score entries above the causal diagonal are zero and never rewritten
-  // buffer 0 holds the state entering chunk 0: h0 (rows < N, this P-block) or zero
-  const float* h0s = p.h0 ? p.h0 + (size_t)slice * N * P + p0 : nullptr;
+  // buffer 0 holds the state entering the first chunk: h0 (rows < N, this P-block),
+  // the combined state entering a later segment, or zero
+  const float* h0s = seg == 0 ? (p.h0 ? p.h0 + (size_t)slice * N * P + p0 : nullptr)
+                              : (local ? nullptr : p.seg_in + ((size_t)slice * p.nseg + seg) * N * P + p0);
   for (int i = tid; i < 2 * S::NC * VS; i += S::NTH) {
     const int n = i / VS, col = i % VS;
     sST[i] = (h0s && n < N && col < PB) ? from_f32<T>(h0s[n * P + col]) : T(0);
@@ -187,7 +194,7 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
     for (int k = 0; k < S::C_PER; ++k) {
       const int v = tid + S::NTH * k;
       uint4 val = zero4;
-      if (v < S::C_VECS) {
+      if (v < S::C_VECS && !local) {
         const int row = v / S::NVEC_N, nv = v % S::NVEC_N;
         const int t = t0 + row / R, o = row % R;
         if (t < L) val = *reinterpret_cast<const uint4*>(Cg + t * tsG + o * N + nv * VEC);
@@ -230,6 +237,7 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
   };
 
   // ---- a1: per-token factors of chunk c into buffer bi (wave PW only; lane = token)
+  float segsum = 0.f;  // wave PW: sum of Delta over the chunks formed so far
   auto factors = [&](int c, int bi) {
     const int t0 = c * QT;
     float dl = 0.f;
@@ -242,6 +250,7 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
         sLC[bi][lane] = -Ah * kLog2e * cd;
       }
     }
+    segsum += cdend;
     if (lane == 0) {
       sMisc[bi][0] = cdend;
       sMisc[bi][1] = COORD ? 0.f : __builtin_amdgcn_exp2f(-Ah * kLog2e * cdend);
@@ -286,7 +295,7 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
 #pragma unroll
     for (int k = 0; k < S::C_PER; ++k) {
       const int v = tid + S::NTH * k;
-      if (v < S::C_VECS) {
+      if (v < S::C_VECS && !local) {
         const int row = v / S::NVEC_N, nv = v % S::NVEC_N;
         const int n0 = nv * VEC;
         if (COORD) {
@@ -390,7 +399,7 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
 
   const int nch = p.nchunks;
   const size_t sl_saved = (size_t)slice * (nch + 1);
-  if (p.saved) {
+  if (p.saved && !local && seg == 0) {
     // slot 0: the state entering chunk 0
     for (int i = tid; i < N * PB; i += S::NTH) {
       const int n = i / PB, pl = i % PB;
@@ -399,25 +408,26 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
   }
 
   if (wave == PW) {
-    const bool ok = lane < QT && lane < L;
-    const float raw = ok ? dtg[lane * H] : 0.f;
+    const int t = c0 * QT + lane;
+    const bool ok = lane < QT && t < L;
+    const float raw = ok ? dtg[t * H] : 0.f;
     sDT[0][lane] = p.softplus ? softplus_f32(raw) : raw;
     if (S::TE) {
-      sBe[0][lane] = ok ? beg[lane * H] : 0.f;
-      sGa[0][lane] = ok ? gag[lane * H] : 0.f;
+      sBe[0][lane] = ok ? beg[t * H] : 0.f;
+      sGa[0][lane] = ok ? gag[t * H] : 0.f;
     }
   }
-  load_chunk(0);
+  load_chunk(c0);
   __syncthreads();
-  if (wave == PW) factors(0, 0);
+  if (wave == PW) factors(c0, 0);
   __syncthreads();
-  stage(0, 0);
-  if (nch > 1) load_chunk(1);
+  stage(c0, 0);
+  if (c0 + 1 < c1) load_chunk(c0 + 1);
   __syncthreads();
 
-  for (int c = 0; c < nch; ++c) {
-    const int bi = c & 1;
-    if (c > 0) store_rows(c - 1);  // drains while the scores compute
+  for (int c = c0; c < c1; ++c) {
+    const int bi = (c - c0) & 1;
+    if (c > c0 && !local) store_rows(c - 1);  // drains while the scores compute
     const T* q = sQ + bi * QSZ;
     const T* qe = sQe + (COORD ? bi * QSZ : 0);
     const T* kb = sK + bi * KSZ;
@@ -429,7 +439,7 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
     // lane l holds query row 16 ti + (l & 15) against keys 16 tj + 4 (l >> 4) + i),
     // the a4/a5 state update of chunk c; wave PW also forms the per-token factors
     // of chunk c+1
-    for (int tile = wave; tile < S::SC_TILES; tile += NW) {
+    for (int tile = wave; tile < (local ? 0 : S::SC_TILES); tile += NW) {
       int ti = 0, tj = tile;
 #pragma unroll
       for (int a = 0; a < S::TQ - 1; ++a) {
@@ -521,13 +531,13 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
           const int pl = 16 * tp + 4 * (lane >> 4);
           const float v4[4] = {acc[k][0], acc[k][1], acc[k][2], acc[k][3]};
           store4<BF16>(sST + (bi ^ 1) * S::NC * VS + n * VS + pl, v4);
-          if (p.saved)
+          if (p.saved && !local)
             *reinterpret_cast<float4*>(p.saved + ((sl_saved + c + 1) * N + n) * P + p0 + pl) =
                 make_float4(v4[0], v4[1], v4[2], v4[3]);
         }
       }
     }
-    if (wave == PW && c + 1 < nch) factors(c + 1, bi ^ 1);
+    if (wave == PW && c + 1 < c1) factors(c + 1, bi ^ 1);
     __syncthreads();
 
     // ---- phase 2 -- a2 staging of chunk c+1 (other buffer) and the loads of chunk
@@ -536,11 +546,11 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
     // chunk).  Then a6 readout + output of chunk c.
     // Output tiles are transposed: lane l holds row 16 ti + (l & 15), columns
     // p = 16 tp + 4 (l >> 4) + i.
-    if (c + 1 < nch) {
+    if (c + 1 < c1) {
       stage(c + 1, bi ^ 1);
-      if (c + 2 < nch) load_chunk(c + 2);
+      if (c + 2 < c1) load_chunk(c + 2);
     }
-    for (int tile = wave; tile < S::TQ * S::TP; tile += NW) {
+    for (int tile = wave; tile < (local ? 0 : S::TQ * S::TP); tile += NW) {
       const int ti = tile / S::TP, tp = tile % S::TP;
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
       const T* qsrc = COORD ? qe : q;
@@ -576,9 +586,13 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
     }
     __syncthreads();
   }
-  store_rows(nch - 1);
-  if (p.h_final) {
-    float* hf = p.h_final + (size_t)slice * N * P + p0;
+  if (!local) store_rows(c1 - 1);
+  // local pass: the segment's final state (from a zero start) and its summed Delta
+  // for the combine step; full pass: the final state after the last segment
+  float* hf = local ? p.seg_local + ((size_t)slice * p.nseg + seg) * N * P + p0
+                    : (seg == p.nseg - 1 && p.h_final ? p.h_final + (size_t)slice * N * P + p0 : nullptr);
+  if (local && pblk == 0 && wave == PW && lane == 0) p.seg_delta[(size_t)slice * p.nseg + seg] = segsum;
+  if (hf) {
 #pragma unroll
     for (int k = 0; k < S::ST_PER_WAVE; ++k) {
       const int tile = wave * S::ST_PER_WAVE + k;
@@ -586,6 +600,54 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
         const int n = 16 * (tile / S::TP) + (lane & 15), pl = 16 * (tile % S::TP) + 4 * (lane >> 4);
         *reinterpret_cast<float4*>(hf + n * P + pl) = make_float4(st[k][0], st[k][1], st[k][2], st[k][3]);
       }
+    }
+  }
+}
+
+// ------------------------------------------------------------------ segment combine
+// States entering the segments of each slice, in order:
+//   S_in[0] = h0 (or 0),   S_in[s+1] = rho_s R(theta_s) S_in[s] + S_local[s],
+// with rho_s = e^{-A_n D_s} per row, theta_s = omega_k D_s per pair and D_s the
+// segment's summed step (the chunk-by-chunk decays and rotations of a segment
+// compose to exactly these).  One thread per (slice, row pair, value column).
+__global__ __launch_bounds__(256) void ssm_fwd_combine(FwdParams p, int per_row) {
+  const int N = p.n_real + 2 * p.n_pairs, P = p.P, nreal = p.n_real, na = p.n_real + p.n_pairs;
+  const long total = (long)p.batch * p.H * (N / 2) * P;
+  for (long i = (long)blockIdx.x * 256 + threadIdx.x; i < total; i += (long)gridDim.x * 256) {
+    const int pp = (int)(i % P);
+    const long r = i / P;
+    const int n = 2 * (int)(r % (N / 2));
+    const long slice = r / (N / 2);
+    const int h = (int)(slice % p.H);
+    auto rate = [&](int m) {
+      if (!per_row || p.head_rates) return p.A[h];
+      return m < nreal ? p.A[(size_t)h * na + m] : p.A[(size_t)h * na + nreal + ((m - nreal) >> 1)];
+    };
+    const float ra = rate(n), rb = rate(n + 1);
+    const bool pair = per_row && n >= nreal;
+    const float om = pair ? p.omega[(size_t)h * p.n_pairs + ((n - nreal) >> 1)] : 0.f;
+    const size_t sb = (size_t)slice * p.nseg;
+    float a = 0.f, bv = 0.f;
+    if (p.h0) {
+      a = p.h0[((size_t)slice * N + n) * P + pp];
+      bv = p.h0[((size_t)slice * N + n + 1) * P + pp];
+    }
+    for (int s = 0; s + 1 < p.nseg; ++s) {
+      const float dsum = p.seg_delta[sb + s];
+      float a2 = a * expf(-ra * dsum), b2 = bv * expf(-rb * dsum);
+      if (pair) {
+        float sn, cs;
+        sincosf(om * dsum, &sn, &cs);
+        const float x0 = a2, x1 = b2;
+        a2 = cs * x0 - sn * x1;
+        b2 = sn * x0 + cs * x1;
+      }
+      const float* loc = p.seg_local + ((sb + s) * N + n) * P + pp;
+      a = a2 + loc[0];
+      bv = b2 + loc[P];
+      float* out = p.seg_in + ((sb + s + 1) * N + n) * P + pp;
+      out[0] = a;
+      out[P] = bv;
     }
   }
 }
@@ -652,7 +714,7 @@ bool fwd_variant_exists(const FwdKey& k) {
 
 hipError_t launch_fwd(const FwdKey& k, const FwdParams& p, hipStream_t stream,
                       void* const* events) {
-  const int nwg = p.batch * p.H * p.npblk;
+  const int nwg = p.batch * p.H * p.npblk * p.nseg;
   if (nwg == 0 || p.nchunks == 0) return hipSuccess;
   auto mark = [&](int i) {
     if (events && events[i]) (void)hipEventRecord(static_cast<hipEvent_t>(events[i]), stream);
@@ -661,8 +723,19 @@ hipError_t launch_fwd(const FwdKey& k, const FwdParams& p, hipStream_t stream,
   if (k.bf16 == BF && k.N == NN && k.PB == PBB && k.R == RR && k.KR == KRR && k.QT == QTT && \
       k.coord == CO && k.nthreads == NT) {                                                   \
     mark(0);                                                                                 \
+    if (p.nseg > 1) {                                                                        \
+      FwdParams lp = p;                                                                      \
+      lp.state_only = 1;                                                                     \
+      hipLaunchKernelGGL((ssm_fwd_kernel<BF, NN, PBB, RR, KRR, QTT, CO, NT>), dim3(nwg),      \
+                         dim3(NT), 0, stream, lp);                                           \
+      const long total = (long)p.batch * p.H * (NN / 2) * p.P;                               \
+      const int cb = (int)std::min<long>((total + 255) / 256, 2048);                         \
+      hipLaunchKernelGGL(ssm_fwd_combine, dim3(cb), dim3(256), 0, stream, p, CO ? 1 : 0);    \
+    }                                                                                        \
+    FwdParams fp = p;                                                                        \
+    fp.state_only = 0;                                                                       \
     hipLaunchKernelGGL((ssm_fwd_kernel<BF, NN, PBB, RR, KRR, QTT, CO, NT>), dim3(nwg),        \
-                       dim3(NT), 0, stream, p);                                              \
+                       dim3(NT), 0, stream, fp);                                             \
     mark(1);                                                                                 \
     return hipGetLastError();                                                                \
   }

@@ -23,6 +23,12 @@ struct FwdParams {
   int batch, L, H, G, P, n_real, n_pairs, nchunks, npblk;
   int softplus, has_D;
   int head_rates;  // A holds one rate per head even though the per-row kernel runs
+  // sequence segments (nseg = 1: one workgroup walks the whole sequence)
+  int nseg, cps;     // segments per slice, chunks per segment
+  int state_only;    // local pass: each segment's final state from a zero start, no outputs
+  float* seg_local;  // [slice][nseg][N][P] local final states (local pass output)
+  float* seg_in;     // [slice][nseg][N][P] states entering the segments (combine output)
+  float* seg_delta;  // [slice][nseg] sum of Delta over each segment (local pass output)
 };
 
 struct BwdParams {

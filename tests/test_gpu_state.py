@@ -114,3 +114,47 @@ def test_backward_with_initial_state_matches_oracle(case):
     assert "dh0" in errs
     bad = {k: v for k, v in errs.items() if not v <= tol(prob)}
     assert not bad, bad
+
+
+SEG_CASES = {
+    "f32_head": ("ssd_siso", dict(dtype="f32", dstate=32, n_real=32, headdim=16, batch=1,
+                                  nheads=2, ngroups=2, seqlen=700)),
+    "f32_hybrid": ("hybrid", dict(dtype="f32", dstate=32, n_real=16, n_pairs=8, headdim=16,
+                                  batch=1, nheads=2, ngroups=2, seqlen=333)),
+    "bf16_ssd_mimo": ("ssd_mimo", dict(batch=1, seqlen=700, nheads=2, ngroups=2)),
+    "bf16_hybrid": ("hybrid", dict(batch=1, seqlen=500, nheads=2, ngroups=2)),
+}
+
+
+@pytest.mark.parametrize("nseg", [1, 3, 7])
+@pytest.mark.parametrize("case", sorted(SEG_CASES))
+def test_sequence_segments_match_oracle(case, nseg, monkeypatch):
+    """The forward split into sequence segments (local pass, combine, full pass)
+    gives the oracle's outputs, final state and saved boundary states, with an
+    initial state."""
+    monkeypatch.setenv("SSM_NSEG", str(nseg))
+    name, kw = SEG_CASES[case]
+    prob = workloads.make_problem(workloads.spec(name, **kw), seed=17)
+    h0 = workloads.make_state(prob["desc"], seed=19)
+    print(f"[segments] case={case} nseg={nseg} desc={prob['desc']}", flush=True)
+    t = workloads.to_device(prob)
+    y, saved, hf = _fwd(prob, t, h0=torch.from_numpy(h0).cuda(), save=True)
+    torch.cuda.synchronize()
+    yr, hr = oracle.fwd(prob, h0=h0.astype(np.float64))
+    ey, eh = rel_l2(_np(y), yr), rel_l2(_np(hf), hr)
+    print(f"[segments] case={case} nseg={nseg} y={ey:.2e} h_final={eh:.2e}", flush=True)
+    assert ey <= tol(prob) and eh <= tol(prob), (ey, eh)
+    # the gradients read the saved boundary states: check them through the backward
+    if name != "ssd_siso" or prob["dtype"] == "f32":
+        pd = workloads.make_problem(workloads.spec(name, **kw), seed=17, with_dy=True)
+        td = workloads.to_device(pd)
+        g = ssm.backward(pd["desc"], pd["dtype"], td["x"], td["B"], td["C"], td["dy"], td["dt"],
+                         td["A"], saved, omega=td.get("omega"), beta=td.get("beta"),
+                         gamma=td.get("gamma"), D=td.get("D"), want=("dA", "dD", "dh0"))
+        torch.cuda.synchronize()
+        ref = oracle.bwd(pd, pd["dy"], h0=h0.astype(np.float64))
+        errs = {k: rel_l2(_np(g[k]), ref[k]) for k in ("dx", "dC", "ddt", "dh0")}
+        print(f"[segments] case={case} nseg={nseg} " +
+              " ".join(f"{k}={v:.2e}" for k, v in errs.items()), flush=True)
+        bad = {k: v for k, v in errs.items() if not v <= tol(pd)}
+        assert not bad, bad
