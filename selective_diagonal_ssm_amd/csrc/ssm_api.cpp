@@ -198,6 +198,18 @@ static size_t fwd_segment_bytes(const ssm_desc* d, const Plan& pl, const FwdKey&
   return 2 * st + ((size_t)slices * sg.nseg * sizeof(float) + 255) / 256 * 256;
 }
 
+// boundary-adjoint sweep segments: one workgroup per (slice, segment)
+static Segs adj_segments(const ssm_desc* d, const Plan& pl) {
+  return segments((long)d->batch * d->nheads, pl.nchunks);
+}
+
+static size_t adj_segment_bytes(const ssm_desc* d, const Plan& pl) {
+  const Segs sg = adj_segments(d, pl);
+  if (sg.nseg <= 1) return 0;
+  const size_t st = (size_t)d->batch * d->nheads * sg.nseg * d->dstate * d->headdim * sizeof(float);
+  return 2 * st + ((size_t)d->batch * d->nheads * sg.nseg * sizeof(float) + 255) / 256 * 256;
+}
+
 size_t ssm_workspace_bytes(const ssm_desc* d, int for_backward) {
   Plan pl;
   if (make_plan(d, &pl)) return 0;
@@ -207,7 +219,7 @@ size_t ssm_workspace_bytes(const ssm_desc* d, int for_backward) {
   }
   const size_t g = (bwd_gseg_bytes(d, pl) + 255) / 256 * 256;
   const size_t part = (size_t)d->batch * d->nheads * pl.nchunks * npart_of(d, pl) * sizeof(float);
-  return g + part;
+  return g + (part + 255) / 256 * 256 + adj_segment_bytes(d, pl);
 }
 
 int ssm_scan_fwd(const ssm_desc* d, const ssm_fwd_args* a, void* ws, size_t ws_bytes,
@@ -305,7 +317,17 @@ int ssm_scan_bwd(const ssm_desc* d, const ssm_bwd_args* a, void* ws, size_t ws_b
                                     (bwd_gseg_bytes(d, pl) + 255) / 256 * 256);
   p.batch = d->batch; p.L = d->seqlen; p.H = d->nheads; p.G = d->ngroups; p.P = d->headdim;
   p.n_real = d->n_real; p.n_pairs = d->n_pairs; p.nchunks = pl.nchunks;
-  p.nseg = 1; p.chunks_per_seg = pl.nchunks;
+  const Segs sg = adj_segments(d, pl);
+  p.nseg = sg.nseg;
+  p.chunks_per_seg = sg.cps;
+  if (sg.nseg > 1) {
+    const size_t part = (size_t)d->batch * d->nheads * pl.nchunks * npart_of(d, pl) * sizeof(float);
+    char* base = reinterpret_cast<char*>(p.part) + (part + 255) / 256 * 256;
+    const size_t st = (size_t)d->batch * d->nheads * sg.nseg * d->dstate * d->headdim;
+    p.gloc = reinterpret_cast<float*>(base);
+    p.gin = p.gloc + st;
+    p.gdel = p.gin + st;
+  }
   p.softplus = (d->flags & SSM_F_DT_SOFTPLUS) ? 1 : 0;
   p.has_D = hasD ? 1 : 0;
   p.npart = npart_of(d, pl);

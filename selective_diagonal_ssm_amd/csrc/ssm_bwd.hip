@@ -70,7 +70,10 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_adjoint(BwdParams p) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int npblk = p.P / PB;
   const int lid = xcd_logical_id(blockIdx.x, gridDim.x);
-  const int slice = lid / npblk, pblk = lid % npblk;
+  const int slice = lid / (npblk * p.nseg), seg = (lid / npblk) % p.nseg, pblk = lid % npblk;
+  const bool local = p.state_only != 0;
+  if (local && seg == 0) return;  // the first segment's local adjoint is never needed
+  const int c0 = seg * p.chunks_per_seg, c1 = min(p.nchunks, c0 + p.chunks_per_seg);
   const int b = slice / p.H, h = slice % p.H, g = h / (p.H / p.G);
   const int p0 = pblk * PB;
   const int L = p.L, H = p.H, G = p.G, P = p.P, nreal = p.n_real;
@@ -92,9 +95,20 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_adjoint(BwdParams p) {
   const T* Cg = static_cast<const T*>(p.C);
   const T* dyg = static_cast<const T*>(p.dy);
 
+  // carried adjoint: zero past the sequence end, else (full pass of a segment) the
+  // adjoint flowing in from the segments on the right
+  const float* g_in = (!local && seg + 1 < p.nseg) ? p.gin + ((size_t)slice * p.nseg + seg) * N * p.P + p0 : nullptr;
   f32x4 st[S::ST_PER_WAVE];
 #pragma unroll
-  for (int k = 0; k < S::ST_PER_WAVE; ++k) st[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int k = 0; k < S::ST_PER_WAVE; ++k) {
+    st[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int tile = wave + NW * k;
+    if (g_in && tile < S::ST_TILES) {
+      const int tnn = tile / S::TP, pl = 16 * (tile % S::TP) + (lane & 15);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) st[k][i] = g_in[(size_t)(16 * tnn + 4 * (lane >> 4) + i) * p.P + pl];
+    }
+  }
 
   const int nch = p.nchunks;
   // register prefetch of one chunk's C rows, dy rows and steps
@@ -130,8 +144,13 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_adjoint(BwdParams p) {
   };
 
   float dnext = 0.f;  // step of the first token of the chunk after the current one
-  prefetch(nch - 1);
-  for (int c = nch - 1; c >= 0; --c) {
+  if (c1 < nch) {
+    const float raw = p.dt[((size_t)b * L + c1 * QT) * H + h];
+    dnext = p.softplus ? softplus_f32(raw) : raw;
+  }
+  float segsum = 0.f;  // summed step of this segment's transition (local pass)
+  prefetch(c1 - 1);
+  for (int c = c1 - 1; c >= c0; --c) {
     const int t0 = c * QT;
     __syncthreads();  // the previous chunk's products are done with sQ / sY
     // step of this chunk's tokens (lane = token)
@@ -141,6 +160,7 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_adjoint(BwdParams p) {
     const float cdx = cd - read_lane(dl, 0);               // sum over (t0, t]
     const float cdx_end = read_lane(cdx, QT - 1) + dnext;  // sum over (t0, t0']
     dnext = read_lane(dl, 0);
+    segsum += cdx_end;
 
     // operands: rows (t, o) of  e^{L'_t} R(-Theta'_t) C_t  and  dy_t
 #pragma unroll
@@ -190,7 +210,7 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_adjoint(BwdParams p) {
         *reinterpret_cast<uint4*>(sY + row * VS + pv * VEC) = raw;
       }
     }
-    if (c > 0) prefetch(c - 1);  // in flight during this chunk's products
+    if (c > c0) prefetch(c - 1);  // in flight during this chunk's products
 
     // carried adjoint: Gpre[c+1] -> Phi_{t0',t0}^T Gpre[c+1]
 #pragma unroll
@@ -232,18 +252,35 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_adjoint(BwdParams p) {
           mma<BF16>(acc, a, bq);
         }
         st[k] = acc;
-        const int pl = 16 * tp + (lane & 15);
-        float* dst = p.gseg + ((size_t)slice * nch + c) * N * P;
+        if (!local) {
+          const int pl = 16 * tp + (lane & 15);
+          float* dst = p.gseg + ((size_t)slice * nch + c) * N * P;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int n = 16 * tnn + 4 * (lane >> 4) + i;
-          dst[(size_t)n * P + p0 + pl] = acc[i];
+          for (int i = 0; i < 4; ++i) {
+            const int n = 16 * tnn + 4 * (lane >> 4) + i;
+            dst[(size_t)n * P + p0 + pl] = acc[i];
+          }
         }
       }
     }
   }
+  if (local) {
+    // the segment's local adjoint at its first token, and its summed step
+    float* dst = p.gloc + ((size_t)slice * p.nseg + seg) * N * P + p0;
+#pragma unroll
+    for (int k = 0; k < S::ST_PER_WAVE; ++k) {
+      const int tile = wave + NW * k;
+      if (tile < S::ST_TILES) {
+        const int tnn = tile / S::TP, pl = 16 * (tile % S::TP) + (lane & 15);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dst[(size_t)(16 * tnn + 4 * (lane >> 4) + i) * P + pl] = st[k][i];
+      }
+    }
+    if (pblk == 0 && tid == 0) p.gdel[(size_t)slice * p.nseg + seg] = segsum;
+    return;
+  }
   // dLoss/dh0 = A_0^T g_0, with g_0 (the adjoint at token 0) now in st
-  if (p.dh0) {
+  if (p.dh0 && seg == 0) {
     const float raw = p.dt[(size_t)b * L * H + h];
     const float d0 = p.softplus ? softplus_f32(raw) : raw;
     float* dst = p.dh0 + (size_t)slice * N * P + p0;
@@ -275,6 +312,50 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_adjoint(BwdParams p) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) dst[(size_t)(16 * tnn + 4 * (lane >> 4) + i) * P + pl] = v[i];
       }
+    }
+  }
+}
+
+// ============================================================== adjoint segment combine
+// Adjoints flowing into the segments of each slice, from the last one back:
+//   E_{nseg-1} = 0,   E_{s-1} = rho_s R(-theta_s) E_s + G_loc[s],
+// with rho_s = e^{-A_n D_s}, theta_s = omega_k D_s and D_s the summed step of
+// segment s's transition (the per-chunk transposed decays and rotations of the
+// sweep compose to exactly these).  One thread per (slice, row pair, value column).
+__global__ __launch_bounds__(256) void ssm_adj_combine(BwdParams p, int per_row) {
+  const int N = p.n_real + 2 * p.n_pairs, P = p.P, nreal = p.n_real, na = p.n_real + p.n_pairs;
+  const long total = (long)p.batch * p.H * (N / 2) * P;
+  for (long i = (long)blockIdx.x * 256 + threadIdx.x; i < total; i += (long)gridDim.x * 256) {
+    const int pp = (int)(i % P);
+    const long r = i / P;
+    const int n = 2 * (int)(r % (N / 2));
+    const long slice = r / (N / 2);
+    const int h = (int)(slice % p.H);
+    auto rate = [&](int m) {
+      if (!per_row || p.head_rates) return p.A[h];
+      return m < nreal ? p.A[(size_t)h * na + m] : p.A[(size_t)h * na + nreal + ((m - nreal) >> 1)];
+    };
+    const float ra = rate(n), rb = rate(n + 1);
+    const bool pair = per_row && n >= nreal;
+    const float om = pair ? p.omega[(size_t)h * p.n_pairs + ((n - nreal) >> 1)] : 0.f;
+    const size_t sb = (size_t)slice * p.nseg;
+    float a = 0.f, bv = 0.f;
+    for (int s = p.nseg - 1; s >= 1; --s) {
+      const float dsum = p.gdel[sb + s];
+      float a2 = a * expf(-ra * dsum), b2 = bv * expf(-rb * dsum);
+      if (pair) {
+        float sn, cs;
+        sincosf(om * dsum, &sn, &cs);
+        const float x0 = a2, x1 = b2;
+        a2 = cs * x0 + sn * x1;  // R(-theta) = R(theta)^T
+        b2 = -sn * x0 + cs * x1;
+      }
+      const float* loc = p.gloc + ((sb + s) * N + n) * P + pp;
+      a = a2 + loc[0];
+      bv = b2 + loc[P];
+      float* out = p.gin + ((sb + s - 1) * N + n) * P + pp;
+      out[0] = a;
+      out[P] = bv;
     }
   }
 }
@@ -1344,8 +1425,22 @@ hipError_t launch_bwd(const BwdKey& k, const BwdParams& p, hipStream_t stream,
       k.coord == CO) {                                                                        \
     constexpr int PB = ADJ_PB(PP);                                                            \
     mark(0);                                                                                  \
-    hipLaunchKernelGGL((ssm_bwd_adjoint<BF, NN, PB, RR, QTT, CO, ADJ_NT>),                     \
-                       dim3(slices * (PP / PB)), dim3(ADJ_NT), 0, stream, p);                 \
+    const int agrid = slices * (PP / PB) * p.nseg;                                            \
+    if (p.nseg > 1) {                                                                         \
+      BwdParams lp = p;                                                                       \
+      lp.state_only = 1;                                                                      \
+      hipLaunchKernelGGL((ssm_bwd_adjoint<BF, NN, PB, RR, QTT, CO, ADJ_NT>), dim3(agrid),     \
+                         dim3(ADJ_NT), 0, stream, lp);                                        \
+      const long total = (long)slices * (NN / 2) * PP;                                        \
+      const int cb = (int)std::min<long>((total + 255) / 256, 2048);                          \
+      hipLaunchKernelGGL(ssm_adj_combine, dim3(cb), dim3(256), 0, stream, p, CO ? 1 : 0);     \
+    }                                                                                         \
+    {                                                                                         \
+      BwdParams fp = p;                                                                       \
+      fp.state_only = 0;                                                                      \
+      hipLaunchKernelGGL((ssm_bwd_adjoint<BF, NN, PB, RR, QTT, CO, ADJ_NT>), dim3(agrid),     \
+                         dim3(ADJ_NT), 0, stream, fp);                                        \
+    }                                                                                         \
     mark(1);                                                                                  \
     {                                                                                         \
       static std::atomic<int> occ{0};                                                         \

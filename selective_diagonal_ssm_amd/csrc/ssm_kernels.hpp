@@ -55,9 +55,14 @@ struct BwdParams {
   float* domega;
   float* dD;
   float* dh0;  // [batch][nheads][N][P] fp32, or null
-  int batch, L, H, G, P, n_real, n_pairs, nchunks, nseg, chunks_per_seg;
+  int batch, L, H, G, P, n_real, n_pairs, nchunks;
+  int nseg, chunks_per_seg;  // sequence segments of the boundary-adjoint sweep
   int softplus, has_D, npart;
   int head_rates;
+  int state_only;  // adjoint local pass: each segment from a zero incoming adjoint
+  float* gloc;     // [slice][nseg][N][P] local adjoints at the segments' first tokens
+  float* gin;      // [slice][nseg][N][P] adjoints flowing into the segments from the right
+  float* gdel;     // [slice][nseg] summed step of each segment's transition
 };
 
 // Kernel variant key: io dtype, state size, P-block, rank, keys per token, tokens
