@@ -171,6 +171,40 @@ int ssm_scan_fwd(const ssm_desc *desc, const ssm_fwd_args *args, void *ws, size_
 int ssm_scan_bwd(const ssm_desc *desc, const ssm_bwd_args *args, void *ws, size_t ws_bytes,
                  void *stream);
 
+/* ---------------------------------------------------------------- recurrent step
+ * One token of the same recurrence, run step by step with a constant-size state
+ * (the inference mode of "When a Diagonal State Is Not Enough", Part 01: the
+ * state-space recurrence h_t = A_t h_{t-1} + B_t u_t, y_t = C_t h_t + D_t u_t, and
+ * Part 03: its selective, rotating-pair and two-endpoint forms):
+ *
+ *   state <- A_t state + gamma_t B_t X_t + beta_t B_{t-1} X_{t-1}
+ *   y_t    = C_t^T state + D_h X_t
+ *
+ * with A_t, Delta_t, beta, gamma and D exactly as in the scan above.  The
+ * descriptor is the scan's with seqlen = 1 (chunk is ignored); rank_in and
+ * rank_out may differ, each at most 8; headdim must be a multiple of 4 and at
+ * most 1024; n_real must be even.
+ * Layouts (the scan's at seqlen = 1):
+ *   x, x_prev [batch][nheads][rank_in][headdim]   B, B_prev [batch][ngroups][rank_in][dstate]
+ *   C [batch][ngroups][rank_out][dstate]          y [batch][nheads][rank_out][headdim]
+ *   dt, beta, gamma [batch][nheads]               A, omega, D as in the scan
+ *   state [batch][nheads][dstate][headdim] fp32, read and overwritten in place
+ *       (the layout of h0 / h_final: a scan's h_final continues as this state).
+ * x_prev and B_prev (the previous token's x and B) are used only with
+ * SSM_F_TWO_ENDPOINT, where both NULL means the first token (no previous write)
+ * and otherwise both are set; without the flag both must be NULL.
+ * Same ownership, alignment and error rules as the scan (state 16-byte aligned).
+ * The step needs no workspace; y does not alias state. */
+typedef struct {
+  const void *x, *B, *C;
+  const float *dt, *A, *omega, *beta, *gamma, *D;
+  const void *x_prev, *B_prev;
+  float *state;
+  void *y;
+} ssm_decode_args;
+
+int ssm_decode_step(const ssm_desc *desc, const ssm_decode_args *args, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -1,4 +1,5 @@
-"""MI355X-native state-mediated selective SSM scan (SISO, SSD-MIMO, HybridMamba rows).
+"""MI355X-native state-mediated selective SSM scan and recurrent step (SISO, SSD-MIMO,
+HybridMamba rows).
 
 The computation lives in hand-written HIP kernels for gfx950 behind the C ABI of
 ``include/ssm_scan.h`` (``libssmscan.so``); this package is the thin ctypes
@@ -24,4 +25,4 @@ from ._lib import (  # noqa: F401
     scan_fwd,
     workspace_bytes,
 )
-from .scan import forward, backward  # noqa: F401
+from .scan import backward, decode_step, forward  # noqa: F401

@@ -21,7 +21,8 @@ SSM_DECAY_HEAD, SSM_DECAY_COORD = 0, 1
 SSM_F_DT_SOFTPLUS, SSM_F_TWO_ENDPOINT, SSM_F_HAS_D = 1, 2, 4
 
 EXPORTS = ("ssm_abi_version", "ssm_status_string", "ssm_check_desc", "ssm_chunk_tokens",
-           "ssm_saved_bytes", "ssm_workspace_bytes", "ssm_scan_fwd", "ssm_scan_bwd")
+           "ssm_saved_bytes", "ssm_workspace_bytes", "ssm_scan_fwd", "ssm_scan_bwd",
+           "ssm_decode_step")
 
 
 class SsmDesc(ctypes.Structure):
@@ -46,6 +47,11 @@ class SsmBwdArgs(ctypes.Structure):
     _fields_ = [(n, _vp) for n in ("x", "B", "C", "dy", "dt", "A", "omega", "beta", "gamma", "D",
                                    "saved", "dx", "dB", "dC", "ddt", "dA", "domega", "dbeta",
                                    "dgamma", "dD", "dh0", "events")]
+
+
+class SsmDecodeArgs(ctypes.Structure):
+    _fields_ = [(n, _vp) for n in ("x", "B", "C", "dt", "A", "omega", "beta", "gamma", "D",
+                                   "x_prev", "B_prev", "state", "y")]
 
 
 class SsmError(RuntimeError):
@@ -77,6 +83,7 @@ def load():
         lib.ssm_workspace_bytes.restype = ctypes.c_size_t
         lib.ssm_scan_fwd.argtypes = [dp, ctypes.POINTER(SsmFwdArgs), _vp, ctypes.c_size_t, _vp]
         lib.ssm_scan_bwd.argtypes = [dp, ctypes.POINTER(SsmBwdArgs), _vp, ctypes.c_size_t, _vp]
+        lib.ssm_decode_step.argtypes = [dp, ctypes.POINTER(SsmDecodeArgs), _vp]
         _lib = lib
     return _lib
 
@@ -159,3 +166,15 @@ def scan_bwd(desc: SsmDesc, x, B, C, dy, dt, A, saved, dx, dB, dC, ddt, omega=No
                              _stream(stream))
     if rc != SSM_OK:
         raise SsmError(rc, "ssm_scan_bwd")
+
+
+def decode_step(desc: SsmDesc, x, B, C, dt, A, state, y, omega=None, beta=None, gamma=None,
+                D=None, x_prev=None, B_prev=None, stream=None) -> None:
+    """Enqueue one recurrent step (descriptor with seqlen 1): updates the fp32
+    [batch][nheads][N][P] `state` in place and writes y.  `x_prev` / `B_prev`: the
+    previous token's x and B for two-endpoint writes (None at the first token)."""
+    args = SsmDecodeArgs(_ptr(x), _ptr(B), _ptr(C), _ptr(dt), _ptr(A), _ptr(omega), _ptr(beta),
+                         _ptr(gamma), _ptr(D), _ptr(x_prev), _ptr(B_prev), _ptr(state), _ptr(y))
+    rc = load().ssm_decode_step(ctypes.byref(desc), ctypes.byref(args), _stream(stream))
+    if rc != SSM_OK:
+        raise SsmError(rc, "ssm_decode_step")

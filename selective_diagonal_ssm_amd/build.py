@@ -20,7 +20,7 @@ LIB = os.path.join(PKG, "libssmscan.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["ssm_api.cpp", "ssm_fwd.hip", "ssm_bwd.hip"]
+SOURCES = ["ssm_api.cpp", "ssm_fwd.hip", "ssm_bwd.hip", "ssm_decode.hip"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", os.path.join(ROOT, "include"),
           "-I", CSRC, "-Wall", "-Wno-unused-function",

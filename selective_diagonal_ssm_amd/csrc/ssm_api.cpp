@@ -336,4 +336,42 @@ int ssm_scan_bwd(const ssm_desc* d, const ssm_bwd_args* a, void* ws, size_t ws_b
   return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
 }
 
+int ssm_decode_step(const ssm_desc* d, const ssm_decode_args* a, void* stream) {
+  int rc = check_operation(d);
+  if (rc) return rc;
+  if (!a) return SSM_ERR_NULL;
+  if (d->seqlen != 1) return SSM_ERR_SHAPE;
+  if (d->rank_in > ssm::kDecodeMaxRank || d->rank_out > ssm::kDecodeMaxRank ||
+      d->headdim % 4 || d->headdim > 1024 || (d->n_real % 2))
+    return SSM_ERR_UNSUPPORTED;
+  if ((double)d->batch * d->nheads * d->dstate * d->headdim >= 2147483648.0)
+    return SSM_ERR_UNSUPPORTED;
+  if (d->batch == 0) return SSM_OK;
+  const bool te = (d->flags & SSM_F_TWO_ENDPOINT) != 0;
+  const bool hasD = (d->flags & SSM_F_HAS_D) != 0;
+  if (!a->x || !a->B || !a->C || !a->dt || !a->A || !a->state || !a->y) return SSM_ERR_NULL;
+  if ((d->n_pairs > 0) != (a->omega != nullptr)) return SSM_ERR_NULL;
+  if (te != (a->beta != nullptr) || te != (a->gamma != nullptr)) return SSM_ERR_NULL;
+  if (hasD != (a->D != nullptr)) return SSM_ERR_NULL;
+  if ((a->x_prev != nullptr) != (a->B_prev != nullptr)) return SSM_ERR_NULL;
+  if (!te && a->x_prev) return SSM_ERR_NULL;
+  for (const void* q : {a->x, a->B, a->C, (const void*)a->y, a->x_prev, a->B_prev,
+                        (const void*)a->state})
+    if (q && !aligned(q, 16)) return SSM_ERR_ALIGN;
+  for (const void* q : {(const void*)a->dt, (const void*)a->A, (const void*)a->omega,
+                        (const void*)a->beta, (const void*)a->gamma, (const void*)a->D})
+    if (q && !aligned(q, 4)) return SSM_ERR_ALIGN;
+  ssm::DecodeParams p{};
+  p.x = a->x; p.B = a->B; p.C = a->C; p.dt = a->dt; p.A = a->A; p.omega = a->omega;
+  p.beta = a->beta; p.gamma = a->gamma; p.D = a->D; p.x_prev = a->x_prev; p.B_prev = a->B_prev;
+  p.state = a->state; p.y = a->y;
+  p.batch = d->batch; p.H = d->nheads; p.G = d->ngroups; p.P = d->headdim;
+  p.R = d->rank_in; p.O = d->rank_out; p.n_real = d->n_real; p.n_pairs = d->n_pairs;
+  p.softplus = (d->flags & SSM_F_DT_SOFTPLUS) ? 1 : 0;
+  p.head_rates = d->decay_mode == SSM_DECAY_HEAD ? 1 : 0;
+  const hipError_t e =
+      ssm::launch_decode(d->io_dtype == SSM_BF16, p, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+}
+
 }  // extern "C"

@@ -65,6 +65,27 @@ struct BwdParams {
   float* gdel;     // [slice][nseg] summed step of each segment's transition
 };
 
+// Single-token recurrent step (one token per slice, state updated in place).
+constexpr int kDecodeMaxRank = 8;  // rank_in and rank_out limit of the step kernel
+struct DecodeParams {
+  const void* x;       // [batch][nheads][R][P]
+  const void* B;       // [batch][ngroups][R][N]
+  const void* C;       // [batch][ngroups][O][N]
+  const float* dt;     // [batch][nheads]
+  const float* A;
+  const float* omega;
+  const float* beta;
+  const float* gamma;
+  const float* D;
+  const void* x_prev;  // previous token's x and B (two-endpoint writes), or null
+  const void* B_prev;
+  float* state;        // [batch][nheads][N][P] fp32, read and overwritten
+  void* y;             // [batch][nheads][O][P]
+  int batch, H, G, P, R, O, n_real, n_pairs;
+  int softplus, head_rates;
+};
+hipError_t launch_decode(bool bf16, const DecodeParams& p, hipStream_t stream);
+
 // Kernel variant key: io dtype, state size, P-block, rank, keys per token, tokens
 // per chunk, decay mode.
 struct FwdKey {

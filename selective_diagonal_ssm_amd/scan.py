@@ -76,3 +76,18 @@ def backward(desc_dict: dict, io_dtype: str, x, B, C, dy, dt, A, saved, omega=No
                   domega=g.get("domega"), dbeta=g.get("dbeta"), dgamma=g.get("dgamma"),
                   dD=g.get("dD"), ws=ws, stream=stream, dh0=g.get("dh0"))
     return g
+
+
+def decode_step(desc_dict: dict, io_dtype: str, x, B, C, dt, A, state, omega=None, beta=None,
+                gamma=None, D=None, x_prev=None, B_prev=None, stream=None):
+    """One recurrent step for every (batch, head) slice.  ``x`` [batch][nheads][R][P],
+    ``B`` [batch][ngroups][R][N], ``C`` [batch][ngroups][O][N], ``dt`` [batch][nheads];
+    ``state`` (fp32 [batch][nheads][N][P]) is updated in place.  Returns y
+    [batch][nheads][O][P]."""
+    d = dict(desc_dict, seqlen=1)
+    desc = _lib.make_desc(d, io_dtype, 0)
+    y = torch.empty((d["batch"], d["nheads"], d["rank_out"], d["headdim"]),
+                    dtype=_dtype(io_dtype), device=x.device)
+    _lib.decode_step(desc, x, B, C, dt, A, state, y, omega=omega, beta=beta, gamma=gamma, D=D,
+                     x_prev=x_prev, B_prev=B_prev, stream=stream)
+    return y

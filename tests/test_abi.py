@@ -118,6 +118,7 @@ def test_ctypes_structs_match_header_layout():
     assert [f[0] for f in _lib.SsmDesc._fields_] == header_struct_fields("ssm_desc")
     assert [f[0] for f in _lib.SsmFwdArgs._fields_] == header_struct_fields("ssm_fwd_args")
     assert [f[0] for f in _lib.SsmBwdArgs._fields_] == header_struct_fields("ssm_bwd_args")
+    assert [f[0] for f in _lib.SsmDecodeArgs._fields_] == header_struct_fields("ssm_decode_args")
 
 
 def test_state_carry_pointers_must_be_aligned():
@@ -130,3 +131,34 @@ def test_state_carry_pointers_must_be_aligned():
     args.h0 = None
     args.h_final = 0x2004
     assert lib.ssm_scan_fwd(ctypes.byref(d), ctypes.byref(args), None, 0, None) == -4
+
+
+def _decode_args(**kw):
+    """Recurrent-step arguments with distinct fake (never dereferenced) pointers."""
+    names = [f[0] for f in _lib.SsmDecodeArgs._fields_]
+    a = _lib.SsmDecodeArgs(*[0x1000 * (i + 1) for i in range(len(names))])
+    a.omega = a.beta = a.gamma = a.x_prev = a.B_prev = None
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+@pytest.mark.parametrize("dkw,akw,status", [
+    (dict(seqlen=2), {}, -2),                          # a step is one token
+    (dict(rank_in=9, rank_out=9), {}, -5),             # rank above the step kernel's limit
+    (dict(headdim=1028), {}, -5),
+    (dict(headdim=18), {}, -5),                        # 4 | headdim
+    (dict(), dict(D=None), -1),                        # HAS_D without D
+    (dict(), dict(x_prev=0x9000, B_prev=0x9100), -1),  # previous token without two-endpoint
+    (dict(two_endpoint=True, decay_mode="coord", n_real=32, n_pairs=16, rank_in=2, rank_out=2),
+     dict(omega=0x9000, beta=0x9100, gamma=0x9200, x_prev=0x9300), -1),  # x_prev without B_prev
+    (dict(), dict(state=0x9004), -4),                  # state not 16-byte aligned
+    (dict(), dict(state=None), -1),
+])
+def test_decode_step_validation_before_launch(dkw, akw, status):
+    lib = ssm.load()
+    d = _lib.make_desc(base_desc(**dict(dict(seqlen=1), **dkw)), "bf16")
+    a = _decode_args(**akw)
+    assert lib.ssm_decode_step(ctypes.byref(d), ctypes.byref(a), None) == status
+    assert lib.ssm_decode_step(None, ctypes.byref(a), None) == -1
+    assert lib.ssm_decode_step(ctypes.byref(d), None, None) in (-1, status)
