@@ -75,7 +75,18 @@ def measured_traffic(kernel: str, workload: str, mode: str):
     return int(v) if v else None
 
 
-def cpu_baseline(prob: dict, mode: str, target_s: float = 15.0):
+def decode_bytes(desc: dict, io_bytes: int) -> int:
+    """Compulsory HBM bytes of one recurrent step over all slices: the fp32 state
+    read and written once, plus x, x_prev, y, B, B_prev, C and the per-slice scalars."""
+    b, H, G = desc["batch"], desc["nheads"], desc["ngroups"]
+    P, N, R, O = desc["headdim"], desc["dstate"], desc["rank_in"], desc["rank_out"]
+    te = 1 if desc["two_endpoint"] else 0
+    per_h = 2 * N * P * 4 + ((1 + te) * R * P + O * P) * io_bytes + 4 + 8 * te
+    per_g = ((1 + te) * R * N + O * N) * io_bytes
+    return b * (H * per_h + G * per_g)
+
+
+def cpu_baseline(prob: dict, mode: str, target_s: float = 15.0, h0=None):
     import oracle
 
     oracle.build(force=False)
@@ -86,7 +97,7 @@ def cpu_baseline(prob: dict, mode: str, target_s: float = 15.0):
 
     def run(sl):
         t0 = time.perf_counter()
-        oracle.fwd(prob, slices=sl)
+        oracle.fwd(prob, slices=sl, h0=h0)
         if mode == "fwdbwd":
             oracle.bwd(prob, prob["dy"], slices=sl)
         return time.perf_counter() - t0
@@ -105,7 +116,8 @@ def cpu_baseline(prob: dict, mode: str, target_s: float = 15.0):
     tokens = reps * k2 * d["seqlen"] / d["nheads"]  # (batch, position) tokens across all heads
     return {"value": tokens / t / 1e6, "unit": "Mtokens/s", "cores": threads, "kind": "oracle",
             "sample": f"{k2} of {len(all_slices)} (batch, head) slices x {reps} pass(es), full "
-                      f"length {d['seqlen']}, {'forward + reverse' if mode == 'fwdbwd' else 'forward'}"
+                      f"length {d['seqlen']}, "
+                      f"{ {'fwdbwd': 'forward + reverse', 'fwd': 'forward'}.get(mode, 'recurrent steps')}"
                       f", fp64, {t:.1f} s"}
 
 
@@ -115,7 +127,9 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="ssd_siso", choices=sorted(workloads.WORKLOADS))
-    ap.add_argument("--mode", default="fwdbwd", choices=["fwd", "fwdbwd"])
+    ap.add_argument("--mode", default="fwdbwd", choices=["fwd", "fwdbwd", "decode"])
+    ap.add_argument("--decode-batch", type=int, default=256,
+                    help="batch of the recurrent-step measurement (--mode decode)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (for HBM counter scaling)")
@@ -138,6 +152,10 @@ def main():
               "(every (batch, head) slice is independent; see the sharding notes).",
               file=sys.stderr)
         sys.exit(2)
+
+    if args.mode == "decode":
+        run_decode(args)
+        return
 
     import torch
 
@@ -263,6 +281,81 @@ def main():
                       "fwd_mtok_s": round(tokens / (fwd_ms * 1e-3) / 1e6, 3),
                       "fwd_hbm_frac": round(fwd_bytes / (fwd_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                       "wall_s": round(wall, 3)},
+    }
+    print(json.dumps(out), flush=True)
+
+
+def run_decode(args):
+    """Recurrent-step throughput: one step = one token of every (batch, head) slice
+    of a serving batch, the fp32 state updated in place in HBM (token 1 of a
+    two-token draw, token 0 serving as the previous token of two-endpoint writes)."""
+    import torch
+
+    from selective_diagonal_ssm_amd import _lib
+
+    prob = workloads.make_problem(workloads.spec(args.workload, seqlen=2,
+                                                 batch=args.decode_batch), seed=0, with_dy=False)
+    d = prob["desc"]
+    io = prob["dtype"]
+    h0 = workloads.make_state(d, seed=1)
+    t = workloads.to_device(prob)
+    te = d["two_endpoint"]
+    tok = {k: t[k][:, 1].contiguous() for k in ("x", "B", "C", "dt")}
+    for k in ("beta", "gamma"):
+        if t.get(k) is not None:
+            tok[k] = t[k][:, 1].contiguous()
+    xp = t["x"][:, 0].contiguous() if te else None
+    bp = t["B"][:, 0].contiguous() if te else None
+    state = torch.from_numpy(h0).cuda()
+    dd = dict(d, seqlen=1)
+    desc = _lib.make_desc(dd, io, 0)
+    y = torch.empty((d["batch"], d["nheads"], d["rank_out"], d["headdim"]), dtype=t["x"].dtype,
+                    device=t["x"].device)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        _lib.decode_step(desc, tok["x"], tok["B"], tok["C"], tok["dt"], t["A"], state, y,
+                         omega=t.get("omega"), beta=tok.get("beta"), gamma=tok.get("gamma"),
+                         D=t.get("D"), x_prev=xp, B_prev=bp, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    mk = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    ev = [[mk(), mk()] for _ in range(args.steps)]
+    start, end = mk(), mk()
+    wall0 = time.perf_counter()
+    start.record(stream)
+    for k in range(args.steps):
+        ev[k][0].record(stream)
+        step()
+        ev[k][1].record(stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_per_step = start.elapsed_time(end) / args.steps
+    kms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    io_bytes = 2 if io == "bf16" else 4
+    abytes = decode_bytes(dd, io_bytes)
+    achieved = abytes / (kms * 1e-3) / 1e9
+    value = d["batch"] / (ms_per_step * 1e-3) / 1e6
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "kernel": "ssm_decode_kernel", "algorithmic_bytes_per_launch": abytes,
+                "avg_launch_ms": round(kms, 4)}
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(prob, "decode", h0=h0.astype(np.float64))
+    out = {
+        "metric": "SSM recurrent step Mtokens/s on 1 MI355X", "value": round(value, 3),
+        "unit": "Mtokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16" if io == "bf16" else "f32", "data": "synthetic",
+        "config": {"workload": f"{args.workload} recurrent step", "batch": d["batch"],
+                   "nheads": d["nheads"], "headdim": d["headdim"], "dstate": d["dstate"],
+                   "rank": d["rank_in"], "decay": d["decay_mode"], "n_pairs": d["n_pairs"],
+                   "two_endpoint": te, "step": "one token per (batch, head) slice"},
+        "roofline": roofline, "cpu_baseline": cpu, "breakdown": {"wall_s": round(wall, 3)},
     }
     print(json.dumps(out), flush=True)
 

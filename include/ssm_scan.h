@@ -183,7 +183,9 @@ int ssm_scan_bwd(const ssm_desc *desc, const ssm_bwd_args *args, void *ws, size_
  * with A_t, Delta_t, beta, gamma and D exactly as in the scan above.  The
  * descriptor is the scan's with seqlen = 1 (chunk is ignored); rank_in and
  * rank_out may differ, each at most 8; headdim must be a multiple of 4 and at
- * most 1024; n_real must be even.
+ * most 1024; n_real must be even; and dstate * (1 + 2 rank_in + rank_out) +
+ * 1024 rank_out must not exceed 16384 (the step's per-slice tables in LDS);
+ * otherwise SSM_ERR_UNSUPPORTED.
  * Layouts (the scan's at seqlen = 1):
  *   x, x_prev [batch][nheads][rank_in][headdim]   B, B_prev [batch][ngroups][rank_in][dstate]
  *   C [batch][ngroups][rank_out][dstate]          y [batch][nheads][rank_out][headdim]

@@ -346,6 +346,13 @@ int ssm_decode_step(const ssm_desc* d, const ssm_decode_args* a, void* stream) {
     return SSM_ERR_UNSUPPORTED;
   if ((double)d->batch * d->nheads * d->dstate * d->headdim >= 2147483648.0)
     return SSM_ERR_UNSUPPORTED;
+  const int tps = env_int("SSM_DECODE_TPS", 0) > 0 ? env_int("SSM_DECODE_TPS", 0)
+                                                   : ssm::decode_tps(d->dstate, d->headdim);
+  if (tps != 64 && tps != 128 && tps != 256) return SSM_ERR_UNSUPPORTED;
+  if (d->headdim / 4 > tps) return SSM_ERR_UNSUPPORTED;
+  if ((long)(256 / tps) * ssm::decode_lds_floats(d->dstate, d->rank_in, d->rank_out, d->headdim, tps) * 4 >
+      ssm::kDecodeMaxLdsBytes)
+    return SSM_ERR_UNSUPPORTED;
   if (d->batch == 0) return SSM_OK;
   const bool te = (d->flags & SSM_F_TWO_ENDPOINT) != 0;
   const bool hasD = (d->flags & SSM_F_HAS_D) != 0;
@@ -369,6 +376,7 @@ int ssm_decode_step(const ssm_desc* d, const ssm_decode_args* a, void* stream) {
   p.R = d->rank_in; p.O = d->rank_out; p.n_real = d->n_real; p.n_pairs = d->n_pairs;
   p.softplus = (d->flags & SSM_F_DT_SOFTPLUS) ? 1 : 0;
   p.head_rates = d->decay_mode == SSM_DECAY_HEAD ? 1 : 0;
+  p.tps = tps;
   const hipError_t e =
       ssm::launch_decode(d->io_dtype == SSM_BF16, p, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;

@@ -83,8 +83,26 @@ struct DecodeParams {
   void* y;             // [batch][nheads][O][P]
   int batch, H, G, P, R, O, n_real, n_pairs;
   int softplus, head_rates;
+  int tps;  // threads per slice (64, 128 or 256); 256 / tps slices per workgroup
 };
 hipError_t launch_decode(bool bf16, const DecodeParams& p, hipStream_t stream);
+// LDS of one slice of the step kernel (tps threads), in floats: the transition
+// table, the staged gamma B_t, beta B_{t-1} and C_t rows, and the readout partials
+// [O][groups][P].
+__host__ __device__ inline int decode_lds_floats(int N, int R, int O, int P, int tps) {
+  const int groups = tps / (P / 4);
+  return N + (2 * R + O) * N + O * groups * P;
+}
+// Threads per slice: the fewest (down to one wave) that still give each thread
+// kDecodePairs row pairs of 4 columns, so that small states share a workgroup.
+constexpr int kDecodePairs = 4;
+inline int decode_tps(int N, int P) {
+  const long units = (long)(N / 2) * (P / 4);  // (row pair, 4 columns) units
+  int tps = 256;
+  while (tps > 64 && units < (long)tps * kDecodePairs && tps / 2 >= P / 4) tps /= 2;
+  return tps;
+}
+constexpr long kDecodeMaxLdsBytes = 65536;
 
 // Kernel variant key: io dtype, state size, P-block, rank, keys per token, tokens
 // per chunk, decay mode.

@@ -147,6 +147,7 @@ def _decode_args(**kw):
     (dict(seqlen=2), {}, -2),                          # a step is one token
     (dict(rank_in=9, rank_out=9), {}, -5),             # rank above the step kernel's limit
     (dict(headdim=1028), {}, -5),
+    (dict(dstate=512, n_real=512, rank_in=8, rank_out=8), {}, -5),  # tables exceed the LDS budget
     (dict(headdim=18), {}, -5),                        # 4 | headdim
     (dict(), dict(D=None), -1),                        # HAS_D without D
     (dict(), dict(x_prev=0x9000, B_prev=0x9100), -1),  # previous token without two-endpoint

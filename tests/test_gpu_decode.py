@@ -120,3 +120,25 @@ def test_decode_is_reproducible_and_leaves_inputs():
         y = _steps(prob, t, state, 0, 2)
         outs.append((y, _np(state)))
     assert np.array_equal(outs[0][0], outs[1][0]) and np.array_equal(outs[0][1], outs[1][1])
+
+
+@pytest.mark.parametrize("tps", [64, 128, 256])
+@pytest.mark.parametrize("case", ["f32_hybrid", "bf16_ssd_mimo", "f32_siso"])
+def test_decode_slices_per_workgroup(case, tps, monkeypatch):
+    """1, 2 or 4 slices share a workgroup (the library picks by state size; the
+    override forces each), including a tail workgroup with fewer live slices."""
+    name, kw = CASES[case]
+    kw = dict(kw, batch=3)
+    prob = workloads.make_problem(workloads.spec(name, seqlen=3, **kw), seed=29)
+    if prob["desc"]["headdim"] // 4 > tps:
+        pytest.skip("a state row needs more threads than the slice has")
+    monkeypatch.setenv("SSM_DECODE_TPS", str(tps))
+    h0 = workloads.make_state(prob["desc"], seed=31, scale=0.5)
+    print(f"[decode-tps] case={case} tps={tps}", flush=True)
+    t = workloads.to_device(prob)
+    state = torch.from_numpy(h0).cuda()
+    y = _steps(prob, t, state, 0, 3)
+    yr, hr = oracle.fwd(prob, h0=h0.astype(np.float64))
+    ey, eh = rel_l2(y, yr), rel_l2(_np(state), hr)
+    print(f"[decode-tps] case={case} tps={tps} y={ey:.2e} state={eh:.2e}", flush=True)
+    assert ey <= tol(prob) and eh <= tol(prob), (ey, eh)
