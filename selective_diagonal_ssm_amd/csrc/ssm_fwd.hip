@@ -58,11 +58,19 @@ struct FwdShape {
   static constexpr int C_VECS = QO * NVEC_N;
   static constexpr int B_VECS = BROWS * NVEC_N;
   static constexpr int X_VECS = BROWS * NVEC_P;
-  static constexpr int C_PER = (C_VECS + NTH - 1) / NTH;
-  static constexpr int B_PER = (B_VECS + NTH - 1) / NTH;
-  static constexpr int X_PER = (X_VECS + NTH - 1) / NTH;
+  // staging items: C vectors, then key items (a B vector and the endpoint it is
+  // written at: two per vector with two-endpoint writes), then X vectors
+  static constexpr int K_ITEMS = TE ? 2 * B_VECS : B_VECS;
+  static constexpr int ALL_VECS = C_VECS + K_ITEMS + X_VECS;
+  static constexpr int ALL_PER = (ALL_VECS + NTH - 1) / NTH;
   static constexpr int TQ = QO / 16, TK = QK / 16, TP = PB / 16, TN = N / 16;
   static constexpr int ST_TILES = TN * TP;
+  // output tiles per wave: a YBQ x YBP block (query tiles x value-column tiles),
+  // 2 x 2 only when there are at least four tiles per wave anyway (a block then
+  // halves the fragment reads at the same MFMA count per wave)
+  static constexpr bool YBLK = TQ % 2 == 0 && TP % 2 == 0 && TQ * TP >= 4 * NW;
+  static constexpr int YBQ = YBLK ? 2 : 1;
+  static constexpr int YBP = YBLK ? 2 : 1;
   static constexpr int ST_PER_WAVE = (ST_TILES + NW - 1) / NW;
   // score tiles (16 query rows ti x 16 keys tj) that hold at least one causal
   // entry: key token floor(16 tj / KR) <= query token floor((16 ti + 15) / R)
@@ -109,6 +117,9 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
   __shared__ __align__(16) float sGa[2][S::TE ? 64 : 1], sBe[2][S::TE ? 64 : 1];
   __shared__ float sMisc[2][2];                // CD_end, head: e^{-A CD_end}
   __shared__ float sRate[COORD ? N : 1], sOmega[COORD ? N / 2 + 1 : 1];
+  // per-row decay: the staged chunk's factor tables (see stage)
+  __shared__ __align__(16) float sE[COORD ? QT * N : 4], sEi[COORD ? QT * N : 4], sHh[COORD ? N : 4];
+  __shared__ __align__(16) float2 sRot[COORD ? QT * (N / 2) : 2];
   __shared__ __align__(16) T sYo[S::QO * VS];                 // output rows of the previous chunk
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -184,44 +195,35 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
     }
   }
 
-  uint4 rc[S::C_PER], rb[S::B_PER], rx[S::X_PER];
+  // The operand vectors of a chunk form one item list -- C rows, then B rows, then
+  // X rows (16 bytes each) -- dealt round-robin over all threads, so that every
+  // wave takes a share of the staging.
+  uint4 rr[S::ALL_PER];
   float rdt = 0.f, rbe = 0.f, rga = 0.f;
   const uint4 zero4 = make_uint4(0, 0, 0, 0);
 
   auto load_chunk = [&](int c) {
     const int t0 = c * QT;
 #pragma unroll
-    for (int k = 0; k < S::C_PER; ++k) {
-      const int v = tid + S::NTH * k;
+    for (int k = 0; k < S::ALL_PER; ++k) {
+      const int u = tid + S::NTH * k;
       uint4 val = zero4;
-      if (v < S::C_VECS && !local) {
-        const int row = v / S::NVEC_N, nv = v % S::NVEC_N;
+      if (u < S::C_VECS) {
+        const int row = u / S::NVEC_N, nv = u % S::NVEC_N;
         const int t = t0 + row / R, o = row % R;
-        if (t < L) val = *reinterpret_cast<const uint4*>(Cg + t * tsG + o * N + nv * VEC);
-      }
-      rc[k] = val;
-    }
-#pragma unroll
-    for (int k = 0; k < S::B_PER; ++k) {
-      const int v = tid + S::NTH * k;
-      uint4 val = zero4;
-      if (v < S::B_VECS) {
+        if (t < L && !local) val = *reinterpret_cast<const uint4*>(Cg + t * tsG + o * N + nv * VEC);
+      } else if (u < S::C_VECS + S::K_ITEMS) {
+        const int v = (u - S::C_VECS) >> S::TEH;  // the two endpoints of a vector load it twice
         const int row = v / S::NVEC_N, nv = v % S::NVEC_N;
         const int t = t0 + row / R - S::TEH, r = row % R;
         if (t >= 0 && t < L) val = *reinterpret_cast<const uint4*>(Bg + t * tsG + r * N + nv * VEC);
-      }
-      rb[k] = val;
-    }
-#pragma unroll
-    for (int k = 0; k < S::X_PER; ++k) {
-      const int v = tid + S::NTH * k;
-      uint4 val = zero4;
-      if (v < S::X_VECS) {
+      } else if (u < S::ALL_VECS) {
+        const int v = u - S::C_VECS - S::K_ITEMS;
         const int row = v / S::NVEC_P, pv = v % S::NVEC_P;
         const int t = t0 + row / R - S::TEH, r = row % R;
         if (t >= 0 && t < L) val = *reinterpret_cast<const uint4*>(xg + t * tsH + r * P + pv * VEC);
       }
-      rx[k] = val;
+      rr[k] = val;
     }
     if (wave == PW) {
       // per-token scalars of the NEXT chunk: the staging of chunk c writes them to
@@ -257,24 +259,27 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
     }
   };
 
-  // fold a rotation by -Theta into consecutive (even, odd) pair rows of a vector
-  auto unrotate = [&](float* v, int n0, float cd) {
+  // fold the rotation by -Theta_t (table row t) into consecutive (even, odd) pair
+  // rows of a vector
+  auto unrotate = [&](float* v, int n0, int t) {
 #pragma unroll
     for (int i = 0; i < VEC; i += 2) {
       const int n = n0 + i;
       if (n >= nreal) {
-        const float th = sOmega[(n - nreal) >> 1] * cd;
-        float sn, cs;
-        fast_sincos(th, &sn, &cs);
+        const float2 r = sRot[t * (N / 2) + ((n - nreal) >> 1)];  // (cos, sin)
         const float a = v[i], bb = v[i + 1];
-        v[i] = cs * a + sn * bb;
-        v[i + 1] = -sn * a + cs * bb;
+        v[i] = r.x * a + r.y * bb;
+        v[i + 1] = -r.y * a + r.x * bb;
       }
     }
   };
 
   // ---- a2: the operands of chunk c (held in registers) into buffer bi, using the
-  // chunk's per-token factors
+  // chunk's per-token factors.  Per-row decay: first the chunk's factor tables
+  //   E[t][n] = e^{-A_n (CD_t - CD_end/2)},  Einv = 1 / E,  Hh[n] = e^{-A_n CD_end/2},
+  //   Rot[t][k] = (cos, sin)(omega_k CD_t),
+  // computed by all threads (one exponential per entry), then per element
+  //   q = C~ E,  qe = q Hh = C~ e^{L_t},  k = K~ Einv,  ke = k Hh = K~ e^{L_end - L_s}.
   auto stage = [&](int c, int bi) {
     (void)c;
     if (wave == PW && lane < 64) {
@@ -285,7 +290,24 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
         sBe[bi ^ 1][lane] = rbe;
       }
     }
-    const float cdend = sMisc[bi][0];
+    if constexpr (COORD) {
+      const float hc = 0.5f * sMisc[bi][0];
+      for (int i = tid; i < QT * N; i += S::NTH) {
+        const int t = i / N, n = i % N;
+        const float x = sRate[n] * (sCD[bi][t] - hc);
+        sE[i] = __expf(-x);
+        sEi[i] = __expf(x);
+      }
+      for (int n = tid; n < N; n += S::NTH) sHh[n] = __expf(-sRate[n] * hc);
+      const int np = p.n_pairs;
+      for (int i = tid; i < QT * np; i += S::NTH) {
+        const int t = i / np, k = i % np;
+        float sn, cs;
+        fast_sincos(sOmega[k] * sCD[bi][t], &sn, &cs);
+        sRot[t * (N / 2) + k] = make_float2(cs, sn);
+      }
+      __syncthreads();
+    }
     T* q = sQ + bi * QSZ;
     T* qe = sQe + (COORD ? bi * QSZ : 0);
     T* kb = sK + bi * KSZ;
@@ -293,75 +315,61 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
     T* vb = sV + bi * VSZ;
     T* vwb = sVw + (COORD ? 0 : bi * VSZ);
 #pragma unroll
-    for (int k = 0; k < S::C_PER; ++k) {
-      const int v = tid + S::NTH * k;
-      if (v < S::C_VECS && !local) {
-        const int row = v / S::NVEC_N, nv = v % S::NVEC_N;
+    for (int k = 0; k < S::ALL_PER; ++k) {
+      const int u = tid + S::NTH * k;
+      if (u < S::C_VECS) {
+        if (local) continue;
+        const int row = u / S::NVEC_N, nv = u % S::NVEC_N;
         const int n0 = nv * VEC;
         if (COORD) {
-          const float cd_c = sCD[bi][row / R];
+          const int t = row / R;
           float vals[VEC], qq[VEC], qqe[VEC];
-          unpack<BF16>(rc[k], vals);
-          unrotate(vals, n0, cd_c);
+          unpack<BF16>(rr[k], vals);
+          unrotate(vals, n0, t);
 #pragma unroll
           for (int i = 0; i < VEC; ++i) {
-            const float ar = sRate[n0 + i];
-            qq[i] = vals[i] * __expf(-ar * (cd_c - 0.5f * cdend));
-            qqe[i] = vals[i] * __expf(-ar * cd_c);
+            qq[i] = vals[i] * sE[t * N + n0 + i];
+            qqe[i] = qq[i] * sHh[n0 + i];
           }
           *reinterpret_cast<uint4*>(q + row * NS + n0) = pack<BF16>(qq);
           *reinterpret_cast<uint4*>(qe + row * NS + n0) = pack<BF16>(qqe);
         } else {
-          *reinterpret_cast<uint4*>(q + row * NS + n0) = rc[k];
+          *reinterpret_cast<uint4*>(q + row * NS + n0) = rr[k];
         }
-      }
-    }
-#pragma unroll
-    for (int k = 0; k < S::B_PER; ++k) {
-      const int v = tid + S::NTH * k;
-      if (v < S::B_VECS) {
+      } else if (u < S::C_VECS + S::K_ITEMS) {
+        const int v = (u - S::C_VECS) >> S::TEH;
         const int row = v / S::NVEC_N, nv = v % S::NVEC_N;
         const int n0 = nv * VEC;
         const int sl = row / R - S::TEH, r = row % R;
         if (!COORD && !S::TE) {
-          *reinterpret_cast<uint4*>(kb + (sl * KR + r) * NS + n0) = rb[k];
+          *reinterpret_cast<uint4*>(kb + (sl * KR + r) * NS + n0) = rr[k];
           continue;
         }
-        float vals[VEC];
-        unpack<BF16>(rb[k], vals);
+        // e = 0: gamma_s B_s written at s = sl; e = 1: beta_{s+1} B_s written at s+1
+        const int e = S::TE ? ((u - S::C_VECS) & 1) : 0;
+        const int tau = sl + e;
+        if (tau < 0 || tau >= QT) continue;
+        const int j = tau * KR + (e ? R : 0) + r;
+        const float gb = S::TE ? (e ? sBe[bi][tau] : sGa[bi][tau]) : 1.f;
+        float uu[VEC], kk[VEC], ke[VEC];
+        unpack<BF16>(rr[k], uu);
 #pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          // e = 0: gamma_s B_s written at s = sl; e = 1: beta_{s+1} B_s written at s+1
-          if (e == 1 && !S::TE) break;
-          const int tau = sl + e;
-          if (tau < 0 || tau >= QT || (e == 0 && sl < 0)) continue;
-          const int j = tau * KR + (e ? R : 0) + r;
-          const float gb = S::TE ? (e ? sBe[bi][tau] : sGa[bi][tau]) : 1.f;
-          float u[VEC], kk[VEC], ke[VEC];
+        for (int i = 0; i < VEC; ++i) uu[i] *= gb;
+        if (COORD) {
+          unrotate(uu, n0, tau);
 #pragma unroll
-          for (int i = 0; i < VEC; ++i) u[i] = vals[i] * gb;
-          if (COORD) {
-            const float cdt = sCD[bi][tau];
-            unrotate(u, n0, cdt);
-#pragma unroll
-            for (int i = 0; i < VEC; ++i) {
-              const float ar = sRate[n0 + i];
-              kk[i] = u[i] * __expf(-ar * (0.5f * cdend - cdt));
-              ke[i] = u[i] * __expf(-ar * (cdend - cdt));
-            }
-            *reinterpret_cast<uint4*>(keb + j * NS + n0) = pack<BF16>(ke);
-          } else {
-#pragma unroll
-            for (int i = 0; i < VEC; ++i) kk[i] = u[i];
+          for (int i = 0; i < VEC; ++i) {
+            kk[i] = uu[i] * sEi[tau * N + n0 + i];
+            ke[i] = kk[i] * sHh[n0 + i];
           }
-          *reinterpret_cast<uint4*>(kb + j * NS + n0) = pack<BF16>(kk);
-        }
-      }
-    }
+          *reinterpret_cast<uint4*>(keb + j * NS + n0) = pack<BF16>(ke);
+        } else {
 #pragma unroll
-    for (int k = 0; k < S::X_PER; ++k) {
-      const int v = tid + S::NTH * k;
-      if (v < S::X_VECS) {
+          for (int i = 0; i < VEC; ++i) kk[i] = uu[i];
+        }
+        *reinterpret_cast<uint4*>(kb + j * NS + n0) = pack<BF16>(kk);
+      } else if (u < S::ALL_VECS) {
+        const int v = u - S::C_VECS - S::K_ITEMS;
         const int row = v / S::NVEC_P, pv = v % S::NVEC_P;
         const int sl = row / R - S::TEH, r = row % R;
 #pragma unroll
@@ -370,11 +378,11 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
           const int tau = sl + e;
           if (tau < 0 || tau >= QT || (e == 0 && sl < 0)) continue;
           const int j = tau * KR + (e ? R : 0) + r;
-          *reinterpret_cast<uint4*>(vb + j * VS + pv * VEC) = rx[k];
+          *reinterpret_cast<uint4*>(vb + j * VS + pv * VEC) = rr[k];
           if (!COORD) {
             const float w = __builtin_amdgcn_exp2f(sLC[bi][QT - 1] - sLC[bi][tau]);  // e^{L_end - L_s}
             float xv[VEC];
-            unpack<BF16>(rx[k], xv);
+            unpack<BF16>(rr[k], xv);
 #pragma unroll
             for (int i = 0; i < VEC; ++i) xv[i] *= w;
             *reinterpret_cast<uint4*>(vwb + j * VS + pv * VEC) = pack<BF16>(xv);
@@ -550,39 +558,80 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
       stage(c + 1, bi ^ 1);
       if (c + 2 < c1) load_chunk(c + 2);
     }
-    for (int tile = wave; tile < (local ? 0 : S::TQ * S::TP); tile += NW) {
-      const int ti = tile / S::TP, tp = tile % S::TP;
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      const T* qsrc = COORD ? qe : q;
+    // Output tiles in blocks of YBQ x YBP per wave (each fragment read from LDS feeds
+    // YBP or YBQ MFMAs), taken from the last wave down so that they overlap the
+    // staging, which loads the first waves.
+    {
+      constexpr int BQ = S::YBQ, BP = S::YBP, NBP = S::TP / BP;
+      constexpr int NBLK = (S::TQ / BQ) * NBP;
+      for (int blk = NW - 1 - wave; blk < (local ? 0 : NBLK); blk += NW) {
+        const int ti0 = (blk / NBP) * BQ, tp0 = (blk % NBP) * BP;
+        f32x4 acc[BQ][BP];
 #pragma unroll
-      for (int kk = 0; kk < S::NC / 32; ++kk) {
-        const auto fs = load_frag_tr<BF16>(sST + bi * S::NC * VS + (kk * 32) * VS + 16 * tp, VS);
-        const auto fq = load_frag<BF16>(qsrc + (16 * ti + (lane & 15)) * NS + kk * 32 + 8 * (lane >> 4));
-        mma<BF16>(acc, fs, fq);
-      }
-      const int row = 16 * ti + (lane & 15);
-      const int t = row / R, o = row % R;
-      if (!COORD) {
-        const float el = __builtin_amdgcn_exp2f(sLC[bi][t]);  // e^{L_t}
+        for (int a = 0; a < BQ; ++a)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc[i] *= el;
-      }
-      const int tmax = (16 * ti + 15) / R;
-      const int kend = ((tmax + 1) * KR + 31) / 32;
-      for (int kk = 0; kk < kend; ++kk) {
-        const auto fv = load_frag_tr<BF16>(vb + (kk * 32) * VS + 16 * tp, VS);
-        const auto fsc = load_frag<BF16>(sS + (16 * ti + (lane & 15)) * KS + kk * 32 + 8 * (lane >> 4));
-        mma<BF16>(acc, fv, fsc);
-      }
-      const int pl = 16 * tp + 4 * (lane >> 4);
-      float val[4] = {acc[0], acc[1], acc[2], acc[3]};
-      if (p.has_D) {
-        float xv[4];
-        load4<BF16>(vb + (t * KR + o) * VS + pl, xv);
+          for (int bb = 0; bb < BP; ++bb) acc[a][bb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const T* qsrc = COORD ? qe : q;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) val[i] += Dh * xv[i];
+        for (int kk = 0; kk < S::NC / 32; ++kk) {
+          Frag<BF16> fs[BP], fq[BQ];
+#pragma unroll
+          for (int bb = 0; bb < BP; ++bb)
+            fs[bb] = load_frag_tr<BF16>(sST + bi * S::NC * VS + (kk * 32) * VS + 16 * (tp0 + bb), VS);
+#pragma unroll
+          for (int a = 0; a < BQ; ++a)
+            fq[a] = load_frag<BF16>(qsrc + (16 * (ti0 + a) + (lane & 15)) * NS + kk * 32 + 8 * (lane >> 4));
+#pragma unroll
+          for (int a = 0; a < BQ; ++a)
+#pragma unroll
+            for (int bb = 0; bb < BP; ++bb) mma<BF16>(acc[a][bb], fs[bb], fq[a]);
+        }
+        if (!COORD) {
+#pragma unroll
+          for (int a = 0; a < BQ; ++a) {
+            const int t = (16 * (ti0 + a) + (lane & 15)) / R;
+            const float el = __builtin_amdgcn_exp2f(sLC[bi][t]);  // e^{L_t}
+#pragma unroll
+            for (int bb = 0; bb < BP; ++bb)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) acc[a][bb][i] *= el;
+          }
+        }
+        // intra-chunk part: keys up to the block's last query token (the lower query
+        // tiles see zero scores past their own diagonal)
+        const int tmax = (16 * (ti0 + BQ - 1) + 15) / R;
+        const int kend = ((tmax + 1) * KR + 31) / 32;
+        for (int kk = 0; kk < kend; ++kk) {
+          Frag<BF16> fv[BP], fsc[BQ];
+#pragma unroll
+          for (int bb = 0; bb < BP; ++bb)
+            fv[bb] = load_frag_tr<BF16>(vb + (kk * 32) * VS + 16 * (tp0 + bb), VS);
+#pragma unroll
+          for (int a = 0; a < BQ; ++a)
+            fsc[a] = load_frag<BF16>(sS + (16 * (ti0 + a) + (lane & 15)) * KS + kk * 32 + 8 * (lane >> 4));
+#pragma unroll
+          for (int a = 0; a < BQ; ++a)
+#pragma unroll
+            for (int bb = 0; bb < BP; ++bb) mma<BF16>(acc[a][bb], fv[bb], fsc[a]);
+        }
+#pragma unroll
+        for (int a = 0; a < BQ; ++a) {
+          const int row = 16 * (ti0 + a) + (lane & 15);
+          const int t = row / R, o = row % R;
+#pragma unroll
+          for (int bb = 0; bb < BP; ++bb) {
+            const int pl = 16 * (tp0 + bb) + 4 * (lane >> 4);
+            float val[4] = {acc[a][bb][0], acc[a][bb][1], acc[a][bb][2], acc[a][bb][3]};
+            if (p.has_D) {
+              float xv[4];
+              load4<BF16>(vb + (t * KR + o) * VS + pl, xv);
+#pragma unroll
+              for (int i = 0; i < 4; ++i) val[i] += Dh * xv[i];
+            }
+            store4<BF16>(sYo + row * VS + pl, val);
+          }
+        }
       }
-      store4<BF16>(sYo + row * VS + pl, val);
     }
     __syncthreads();
   }
