@@ -411,6 +411,10 @@ struct BwdShape {
     return n;
   }
   static constexpr int SC_TILES = score_tiles();
+  // dK~ and dC~ tiles in 2 x 2 blocks per wave where there are at least four tiles
+  // per wave anyway
+  static constexpr bool KBLK = TN % 2 == 0 && TK % 2 == 0 && TN * TK >= 4 * NW;
+  static constexpr bool CBLK = TN % 2 == 0 && TQ % 2 == 0 && TN * TQ >= 4 * NW;
   static_assert(QO % 16 == 0 && QK % 32 == 0, "chunk rows must fill MFMA tiles");
   static_assert(N % 16 == 0 && P % 16 == 0 && QT <= 64, "unsupported tile shape");
   static_assert(KR <= 4 && 16 % KR == 0 && 16 % R == 0, "a tile spans whole tokens");
@@ -508,11 +512,14 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
   const uint4 zero4 = make_uint4(0, 0, 0, 0);
   const float4 zf4 = make_float4(0.f, 0.f, 0.f, 0.f);
 
-  auto prefetch = [&](int item) {
+  // The loads of an item, in four parts (C / B rows, X / dy rows and the per-token
+  // scalars, incoming states, outgoing adjoints).
+  auto prefetch = [&](int item, int part) {
     const int slice = item / nch, c = item % nch;
     const int b = slice / H, h = slice % H, g = h / (H / G);
     const int t0 = c * QT, tn = t0 + QT;
     const bool has_next = tn < L;
+    if (part == 0) {
 #pragma unroll
     for (int k = 0; k < CP; ++k) {
       const int v = tid + S::NTH * k;
@@ -535,6 +542,8 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
       }
       pfb[k] = raw;
     }
+    }
+    if (part == 1) {
 #pragma unroll
     for (int k = 0; k < XP; ++k) {
       const int v = tid + S::NTH * k;
@@ -557,23 +566,38 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
       }
       pfy[k] = raw;
     }
-    const float* Sg = p.saved + ((size_t)slice * (nch + 1) + c) * N * P;
-    const float* Gg = p.gseg + ((size_t)slice * nch + (c + 1)) * N * P;
+    }
+    if (part == 2) {
+      const float* Sg = p.saved + ((size_t)slice * (nch + 1) + c) * N * P;
 #pragma unroll
-    for (int k = 0; k < SP; ++k) {
-      const int v = tid + S::NTH * k;
-      float4 s0 = zf4, s1 = zf4, g0 = zf4, g1 = zf4;
-      if (v < SPV) {
-        const int n = 2 * (v / PV), q0 = (v % PV) * 4;
-        s0 = *reinterpret_cast<const float4*>(Sg + (size_t)n * P + q0);
-        s1 = *reinterpret_cast<const float4*>(Sg + (size_t)(n + 1) * P + q0);
-        if (has_next) {
+      for (int k = 0; k < SP; ++k) {
+        const int v = tid + S::NTH * k;
+        float4 s0 = zf4, s1 = zf4;
+        if (v < SPV) {
+          const int n = 2 * (v / PV), q0 = (v % PV) * 4;
+          s0 = *reinterpret_cast<const float4*>(Sg + (size_t)n * P + q0);
+          s1 = *reinterpret_cast<const float4*>(Sg + (size_t)(n + 1) * P + q0);
+        }
+        pfs[k][0] = s0; pfs[k][1] = s1;
+      }
+      return;
+    }
+    if (part == 3) {
+      const float* Gg = p.gseg + ((size_t)slice * nch + (c + 1)) * N * P;
+#pragma unroll
+      for (int k = 0; k < SP; ++k) {
+        const int v = tid + S::NTH * k;
+        float4 g0 = zf4, g1 = zf4;
+        if (v < SPV && has_next) {
+          const int n = 2 * (v / PV), q0 = (v % PV) * 4;
           g0 = *reinterpret_cast<const float4*>(Gg + (size_t)n * P + q0);
           g1 = *reinterpret_cast<const float4*>(Gg + (size_t)(n + 1) * P + q0);
         }
+        pfg[k][0] = g0; pfg[k][1] = g1;
       }
-      pfs[k][0] = s0; pfs[k][1] = s1; pfg[k][0] = g0; pfg[k][1] = g1;
+      return;
     }
+    if (part != 1) return;
     pf_dt = pf_be = pf_ga = 0.f;
     if (lane < QT && t0 + lane < L) {
       const size_t idx = ((size_t)b * L + t0 + lane) * H + h;
@@ -611,7 +635,8 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
 
   int prev = -1;
   int item = blockIdx.x;
-  if (item < nitems) prefetch(item);
+  if (item < nitems)
+    for (int part = 0; part < 4; ++part) prefetch(item, part);
   for (; item < nitems; item += gridDim.x) {
     const int slice = item / nch, c = item % nch;
     const int b = slice / H, h = slice % H, g = h / (H / G);
@@ -843,7 +868,9 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
       }
     }
     // the next item's loads go out now and land while this one computes
-    if (item + static_cast<int>(gridDim.x) < nitems) prefetch(item + gridDim.x);
+    const int nxt = item + static_cast<int>(gridDim.x);
+    if (nxt < nitems)
+      for (int part = 0; part < 4; ++part) prefetch(nxt, part);
     if (prev >= 0) flush_scalars(prev);
     __syncthreads();
     // two-endpoint tails of the last token from the staged rows: beta_{t0'} B_{t1}^T g'
@@ -985,24 +1012,10 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
     }
 
     // ---------------------------------------------------------------- dK~ -> dB, dbeta, dgamma
-    // lane l holds key 16 tj + (l & 15) and state rows 16 tnn + 4 (l >> 4) + i
-    for (int tile = wave; tile < S::TN * S::TK; tile += NW) {
-      const int tnn = tile / S::TK, tj = tile % S::TK;
-      f32x4 ai = {0.f, 0.f, 0.f, 0.f}, ae = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kk = 0; kk < S::QOC / 32; ++kk) {
-        const auto a = load_frag_tr<BF16>(sQ + (kk * 32) * NS + 16 * tnn, NS);
-        const auto bz = load_frag_tr<BF16>(sZM + (kk * 32) * KS + 16 * tj, KS);
-        mma<BF16>(ai, a, bz);
-      }
-#pragma unroll
-      for (int kk = 0; kk < S::PC / 32; ++kk) {
-        const auto bv = load_frag<BF16>(sV + (16 * tj + (lane & 15)) * PS + kk * 32 + 8 * (lane >> 4));
-        const auto ah = load_frag<BF16>(sGh + (16 * tnn + (lane & 15)) * PS + kk * 32 + 8 * (lane >> 4));
-        const auto al = load_frag<BF16>(sGl + (16 * tnn + (lane & 15)) * PS + kk * 32 + 8 * (lane >> 4));
-        mma<BF16>(ae, ah, bv);
-        mma<BF16>(ae, al, bv);
-      }
+    // lane l holds key 16 tj + (l & 15) and state rows 16 tnn + 4 (l >> 4) + i.  Tiles
+    // go in BN x BJ blocks per wave: a block's fragments are read once for all of its
+    // tiles, and its tiles are independent MFMA chains.
+    auto dk_tile = [&](const int tnn, const int tj, const f32x4& ai, const f32x4& ae) {
       const int j = 16 * tj + (lane & 15), s = j / KR, kr = j % KR;
       const int n0 = 16 * tnn + 4 * (lane >> 4);
       const float cds = sTcd[s];
@@ -1117,27 +1130,58 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
           else sDg[wave][s] += dgb;
         }
       }
+    };
+    {
+      constexpr int BN = S::KBLK ? 2 : 1, BJ = S::KBLK ? 2 : 1, NBJ = S::TK / BJ;
+      for (int blk = wave; blk < (S::TN / BN) * NBJ; blk += NW) {
+        const int tn0 = (blk / NBJ) * BN, tj0 = (blk % NBJ) * BJ;
+        f32x4 ai[BN][BJ], ae[BN][BJ];
+#pragma unroll
+        for (int x = 0; x < BN; ++x)
+#pragma unroll
+          for (int y = 0; y < BJ; ++y) ai[x][y] = ae[x][y] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < S::QOC / 32; ++kk) {
+          Frag<BF16> a[BN], bz[BJ];
+#pragma unroll
+          for (int x = 0; x < BN; ++x) a[x] = load_frag_tr<BF16>(sQ + (kk * 32) * NS + 16 * (tn0 + x), NS);
+#pragma unroll
+          for (int y = 0; y < BJ; ++y) bz[y] = load_frag_tr<BF16>(sZM + (kk * 32) * KS + 16 * (tj0 + y), KS);
+#pragma unroll
+          for (int x = 0; x < BN; ++x)
+#pragma unroll
+            for (int y = 0; y < BJ; ++y) mma<BF16>(ai[x][y], a[x], bz[y]);
+        }
+#pragma unroll
+        for (int kk = 0; kk < S::PC / 32; ++kk) {
+          Frag<BF16> bv[BJ], ah[BN], al[BN];
+#pragma unroll
+          for (int y = 0; y < BJ; ++y)
+            bv[y] = load_frag<BF16>(sV + (16 * (tj0 + y) + (lane & 15)) * PS + kk * 32 + 8 * (lane >> 4));
+#pragma unroll
+          for (int x = 0; x < BN; ++x) {
+            ah[x] = load_frag<BF16>(sGh + (16 * (tn0 + x) + (lane & 15)) * PS + kk * 32 + 8 * (lane >> 4));
+            al[x] = load_frag<BF16>(sGl + (16 * (tn0 + x) + (lane & 15)) * PS + kk * 32 + 8 * (lane >> 4));
+          }
+#pragma unroll
+          for (int x = 0; x < BN; ++x)
+#pragma unroll
+            for (int y = 0; y < BJ; ++y) {
+              mma<BF16>(ae[x][y], ah[x], bv[y]);
+              mma<BF16>(ae[x][y], al[x], bv[y]);
+            }
+        }
+#pragma unroll
+        for (int x = 0; x < BN; ++x)
+#pragma unroll
+          for (int y = 0; y < BJ; ++y) dk_tile(tn0 + x, tj0 + y, ai[x][y], ae[x][y]);
+      }
     }
 
     // ---------------------------------------------------------------- dC~ -> dC
     // lane l holds query row 16 tq + (l & 15) and state rows 16 tnn + 4 (l >> 4) + i
-    for (int tile = wave; tile < S::TN * S::TQ; tile += NW) {
-      const int tnn = tile / S::TQ, tq = tile % S::TQ;
-      f32x4 ai = {0.f, 0.f, 0.f, 0.f}, ae = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kk = 0; kk < QK / 32; ++kk) {
-        const auto a = load_frag_tr<BF16>(sK + (kk * 32) * NS + 16 * tnn, NS);
-        const auto bz = load_frag<BF16>(sZM + (16 * tq + (lane & 15)) * KS + kk * 32 + 8 * (lane >> 4));
-        mma<BF16>(ai, a, bz);
-      }
-#pragma unroll
-      for (int kk = 0; kk < S::PC / 32; ++kk) {
-        const auto by = load_frag<BF16>(sY + (16 * tq + (lane & 15)) * PS + kk * 32 + 8 * (lane >> 4));
-        const auto ah = load_frag<BF16>(sSh + (16 * tnn + (lane & 15)) * PS + kk * 32 + 8 * (lane >> 4));
-        const auto al = load_frag<BF16>(sSl + (16 * tnn + (lane & 15)) * PS + kk * 32 + 8 * (lane >> 4));
-        mma<BF16>(ae, ah, by);
-        mma<BF16>(ae, al, by);
-      }
+    // (blocked like dK~)
+    auto dc_tile = [&](const int tnn, const int tq, const f32x4& ai, const f32x4& ae) {
       const int row = 16 * tq + (lane & 15), t = row / R, o = row % R, tg = t0 + t;
       const int n0 = 16 * tnn + 4 * (lane >> 4);
       const float cdt = sTcd[t];
@@ -1200,6 +1244,53 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
       if (lane < 16 && (lane % R) == 0) {
         if (COORD) sTok[wave][t] += tokacc;
         else sTT[wave][t] += tokacc;
+      }
+    };
+    {
+      constexpr int BN = S::CBLK ? 2 : 1, BQ = S::CBLK ? 2 : 1, NBQ = S::TQ / BQ;
+      for (int blk = wave; blk < (S::TN / BN) * NBQ; blk += NW) {
+        const int tn0 = (blk / NBQ) * BN, tq0 = (blk % NBQ) * BQ;
+        f32x4 ai[BN][BQ], ae[BN][BQ];
+#pragma unroll
+        for (int x = 0; x < BN; ++x)
+#pragma unroll
+          for (int y = 0; y < BQ; ++y) ai[x][y] = ae[x][y] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < QK / 32; ++kk) {
+          Frag<BF16> a[BN], bz[BQ];
+#pragma unroll
+          for (int x = 0; x < BN; ++x) a[x] = load_frag_tr<BF16>(sK + (kk * 32) * NS + 16 * (tn0 + x), NS);
+#pragma unroll
+          for (int y = 0; y < BQ; ++y)
+            bz[y] = load_frag<BF16>(sZM + (16 * (tq0 + y) + (lane & 15)) * KS + kk * 32 + 8 * (lane >> 4));
+#pragma unroll
+          for (int x = 0; x < BN; ++x)
+#pragma unroll
+            for (int y = 0; y < BQ; ++y) mma<BF16>(ai[x][y], a[x], bz[y]);
+        }
+#pragma unroll
+        for (int kk = 0; kk < S::PC / 32; ++kk) {
+          Frag<BF16> by[BQ], ah[BN], al[BN];
+#pragma unroll
+          for (int y = 0; y < BQ; ++y)
+            by[y] = load_frag<BF16>(sY + (16 * (tq0 + y) + (lane & 15)) * PS + kk * 32 + 8 * (lane >> 4));
+#pragma unroll
+          for (int x = 0; x < BN; ++x) {
+            ah[x] = load_frag<BF16>(sSh + (16 * (tn0 + x) + (lane & 15)) * PS + kk * 32 + 8 * (lane >> 4));
+            al[x] = load_frag<BF16>(sSl + (16 * (tn0 + x) + (lane & 15)) * PS + kk * 32 + 8 * (lane >> 4));
+          }
+#pragma unroll
+          for (int x = 0; x < BN; ++x)
+#pragma unroll
+            for (int y = 0; y < BQ; ++y) {
+              mma<BF16>(ae[x][y], ah[x], by[y]);
+              mma<BF16>(ae[x][y], al[x], by[y]);
+            }
+        }
+#pragma unroll
+        for (int x = 0; x < BN; ++x)
+#pragma unroll
+          for (int y = 0; y < BQ; ++y) dc_tile(tn0 + x, tq0 + y, ai[x][y], ae[x][y]);
       }
     }
     __syncthreads();
