@@ -60,8 +60,6 @@ __device__ __forceinline__ float2 load_pair(const typename Elem<BF16>::T* p) {
 
 }  // namespace
 
-// RMAX: bound on rank_in and rank_out of the variant (the per-thread x and y
-// registers scale with it)
 // Workgroup barrier for data exchanged through LDS only: the global stores in
 // flight (the updated state) need not complete before the workgroup proceeds.
 __device__ __forceinline__ void lds_barrier() {
