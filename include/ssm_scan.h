@@ -48,9 +48,11 @@
  *     SSM_F_TWO_ENDPOINT is clear; D iff SSM_F_HAS_D is clear (D requires
  *     rank_out == rank_in).  In the backward, a NULL gradient output is not
  *     computed; dx, dB, dC, ddt must be non-NULL.
- *   - `saved` (fp32, ssm_saved_bytes(desc) bytes) receives the chunk-boundary
- *     states from the forward when non-NULL; ssm_scan_bwd requires the buffer a
- *     forward with the same descriptor and inputs filled.
+ *   - `saved` (ssm_saved_bytes(desc) bytes) receives the chunk-boundary states
+ *     from the forward when non-NULL, stored in the io dtype (they enter the
+ *     reverse pass's products in that dtype); ssm_scan_bwd requires the buffer a
+ *     forward with the same descriptor and inputs filled.  Its contents are
+ *     internal to the library.
  *   - State carry (all optional, fp32, [batch][nheads][N][P], 16-byte aligned):
  *     h0 is the state before token 0 (NULL = zero), h_final receives the state
  *     after the last token, dh0 receives dLoss/dh0 = A_0^T g_0.  The backward
@@ -75,7 +77,7 @@
 extern "C" {
 #endif
 
-#define SSM_ABI_VERSION 2
+#define SSM_ABI_VERSION 3
 
 typedef enum {
   SSM_OK = 0,
@@ -118,7 +120,7 @@ typedef struct {
   const void *x, *B, *C;
   const float *dt, *A, *omega, *beta, *gamma, *D;
   void *y;
-  float *saved; /* optional: chunk-boundary states for the backward */
+  void *saved;  /* optional: chunk-boundary states for the backward */
   const float *h0;  /* optional: state before token 0 (NULL = zero) */
   float *h_final;   /* optional: receives the state after the last token */
   void *const *events; /* optional: 2 hipEvent_t recorded on `stream` before and after
@@ -128,7 +130,7 @@ typedef struct {
 typedef struct {
   const void *x, *B, *C, *dy;
   const float *dt, *A, *omega, *beta, *gamma, *D;
-  const float *saved; /* filled by ssm_scan_fwd with the same inputs */
+  const void *saved; /* filled by ssm_scan_fwd with the same inputs */
   void *dx, *dB, *dC;
   float *ddt, *dA, *domega, *dbeta, *dgamma, *dD;
   float *dh0;       /* optional: receives dLoss/dh0 */
@@ -150,7 +152,8 @@ int ssm_check_desc(const ssm_desc *desc);
    negative status. */
 int ssm_chunk_tokens(const ssm_desc *desc);
 
-/* Bytes of the `saved` buffer (fp32 chunk-boundary states); 0 on an invalid descriptor. */
+/* Bytes of the `saved` buffer (chunk-boundary states in the io dtype); 0 on an invalid
+   descriptor. */
 size_t ssm_saved_bytes(const ssm_desc *desc);
 
 /* Device scratch needed by ssm_scan_fwd (for_backward = 0) or ssm_scan_bwd

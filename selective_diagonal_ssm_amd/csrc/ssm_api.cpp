@@ -178,7 +178,7 @@ int ssm_chunk_tokens(const ssm_desc* d) {
 size_t ssm_saved_bytes(const ssm_desc* d) {
   Plan pl;
   if (make_plan(d, &pl)) return 0;
-  return (size_t)d->batch * d->nheads * (pl.nchunks + 1) * d->dstate * d->headdim * sizeof(float);
+  return (size_t)d->batch * d->nheads * (pl.nchunks + 1) * d->dstate * d->headdim * (pl.bf16 ? 2 : 4);
 }
 
 static int npart_of(const ssm_desc* d, const Plan& pl) {
@@ -187,7 +187,7 @@ static int npart_of(const ssm_desc* d, const Plan& pl) {
 }
 
 static size_t bwd_gseg_bytes(const ssm_desc* d, const Plan& pl) {
-  return (size_t)d->batch * d->nheads * pl.nchunks * d->dstate * d->headdim * sizeof(float);
+  return (size_t)d->batch * d->nheads * pl.nchunks * d->dstate * d->headdim * (pl.bf16 ? 2 : 4);
 }
 
 static size_t fwd_segment_bytes(const ssm_desc* d, const Plan& pl, const FwdKey& key) {
@@ -312,7 +312,7 @@ int ssm_scan_bwd(const ssm_desc* d, const ssm_bwd_args* a, void* ws, size_t ws_b
   p.omega = a->omega; p.beta = a->beta; p.gamma = a->gamma; p.D = a->D; p.saved = a->saved;
   p.dx = a->dx; p.dB = a->dB; p.dC = a->dC; p.ddt = a->ddt; p.dbeta = a->dbeta;
   p.dgamma = a->dgamma; p.dA = a->dA; p.domega = a->domega; p.dD = a->dD; p.dh0 = a->dh0;
-  p.gseg = static_cast<float*>(ws);
+  p.gseg = ws;
   p.part = reinterpret_cast<float*>(static_cast<char*>(ws) +
                                     (bwd_gseg_bytes(d, pl) + 255) / 256 * 256);
   p.batch = d->batch; p.L = d->seqlen; p.H = d->nheads; p.G = d->ngroups; p.P = d->headdim;

@@ -33,6 +33,8 @@
 #include <algorithm>
 #include <atomic>
 
+#include <type_traits>
+
 #include "ssm_device.hpp"
 #include "ssm_kernels.hpp"
 
@@ -100,15 +102,18 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_adjoint(BwdParams p) {
   // carried adjoint: zero past the sequence end, else (full pass of a segment) the
   // adjoint flowing in from the segments on the right
   const float* g_in = (!local && seg + 1 < p.nseg) ? p.gin + ((size_t)slice * p.nseg + seg) * N * p.P + p0 : nullptr;
+  // adjoint tiles, transposed: st[k][i] = G[n = 16 tn + (lane & 15)][p = 16 tp + 4 (lane >> 4) + i]
+  // (one state row per lane, so each lane stores a 4-column piece; a pair's two rows
+  // sit in lanes l, l ^ 1)
   f32x4 st[S::ST_PER_WAVE];
 #pragma unroll
   for (int k = 0; k < S::ST_PER_WAVE; ++k) {
     st[k] = f32x4{0.f, 0.f, 0.f, 0.f};
     const int tile = wave + NW * k;
     if (g_in && tile < S::ST_TILES) {
-      const int tnn = tile / S::TP, pl = 16 * (tile % S::TP) + (lane & 15);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) st[k][i] = g_in[(size_t)(16 * tnn + 4 * (lane >> 4) + i) * p.P + pl];
+      const int n = 16 * (tile / S::TP) + (lane & 15), pl = 16 * (tile % S::TP) + 4 * (lane >> 4);
+      const float4 v = *reinterpret_cast<const float4*>(g_in + (size_t)n * p.P + pl);
+      st[k] = f32x4{v.x, v.y, v.z, v.w};
     }
   }
 
@@ -219,23 +224,20 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_adjoint(BwdParams p) {
     for (int k = 0; k < S::ST_PER_WAVE; ++k) {
       const int tile = wave + NW * k;
       if (tile < S::ST_TILES) {
-        const int tnn = tile / S::TP;
+        const int n = 16 * (tile / S::TP) + (lane & 15);
+        const float dec = COORD ? __expf(-sRate[n] * cdx_end) : __expf(-Ah * cdx_end);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int n = 16 * tnn + 4 * (lane >> 4) + i;
-          st[k][i] *= COORD ? __expf(-sRate[n] * cdx_end) : __expf(-Ah * cdx_end);
-        }
+        for (int i = 0; i < 4; ++i) st[k][i] *= dec;
         if (COORD) {
+          // R(-theta) on the pair (n, n ^ 1) held by lanes (l, l ^ 1)
+          const bool pair = n >= nreal;
+          float sn = 0.f, cs = 1.f;
+          if (pair) fast_sincos(sOmega[(n - nreal) >> 1] * cdx_end, &sn, &cs);
+          const float sg = (lane & 1) ? -sn : sn;
 #pragma unroll
-          for (int i = 0; i < 4; i += 2) {
-            const int n = 16 * tnn + 4 * (lane >> 4) + i;
-            if (n >= nreal) {
-              float sn, cs;
-              fast_sincos(sOmega[(n - nreal) >> 1] * cdx_end, &sn, &cs);
-              const float a0 = st[k][i], a1 = st[k][i + 1];
-              st[k][i] = cs * a0 + sn * a1;  // R(-theta)
-              st[k][i + 1] = -sn * a0 + cs * a1;
-            }
+          for (int i = 0; i < 4; ++i) {
+            const float other = swap_adjacent_lanes(st[k][i]);
+            st[k][i] = pair ? cs * st[k][i] + sg * other : st[k][i];
           }
         }
       }
@@ -251,17 +253,15 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_adjoint(BwdParams p) {
         for (int kk = 0; kk < S::QOC / 32; ++kk) {
           const auto a = load_frag_tr<BF16>(sQ + (kk * 32) * NS + 16 * tnn, NS);
           const auto bq = load_frag_tr<BF16>(sY + (kk * 32) * VS + 16 * tp, VS);
-          mma<BF16>(acc, a, bq);
+          mma<BF16>(acc, bq, a);  // transposed: rows p, columns n
         }
         st[k] = acc;
         if (!local) {
-          const int pl = 16 * tp + (lane & 15);
-          float* dst = p.gseg + ((size_t)slice * nch + c) * N * P;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int n = 16 * tnn + 4 * (lane >> 4) + i;
-            dst[(size_t)n * P + p0 + pl] = acc[i];
-          }
+          // the boundary adjoint in the io dtype (it enters the chunk products so)
+          const int n = 16 * tnn + (lane & 15), pl = 16 * tp + 4 * (lane >> 4);
+          T* dst = static_cast<T*>(p.gseg) + ((size_t)slice * nch + c) * N * P;
+          const float v4[4] = {acc[0], acc[1], acc[2], acc[3]};
+          store4<BF16>(dst + (size_t)n * P + p0 + pl, v4);
         }
       }
     }
@@ -273,9 +273,8 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_adjoint(BwdParams p) {
     for (int k = 0; k < S::ST_PER_WAVE; ++k) {
       const int tile = wave + NW * k;
       if (tile < S::ST_TILES) {
-        const int tnn = tile / S::TP, pl = 16 * (tile % S::TP) + (lane & 15);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) dst[(size_t)(16 * tnn + 4 * (lane >> 4) + i) * P + pl] = st[k][i];
+        const int n = 16 * (tile / S::TP) + (lane & 15), pl = 16 * (tile % S::TP) + 4 * (lane >> 4);
+        *reinterpret_cast<float4*>(dst + (size_t)n * P + pl) = make_float4(st[k][0], st[k][1], st[k][2], st[k][3]);
       }
     }
     if (pblk == 0 && tid == 0) p.gdel[(size_t)slice * p.nseg + seg] = segsum;
@@ -290,29 +289,24 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_adjoint(BwdParams p) {
     for (int k = 0; k < S::ST_PER_WAVE; ++k) {
       const int tile = wave + NW * k;
       if (tile < S::ST_TILES) {
-        const int tnn = tile / S::TP, tp = tile % S::TP;
-        const int pl = 16 * tp + (lane & 15);
+        const int n = 16 * (tile / S::TP) + (lane & 15), pl = 16 * (tile % S::TP) + 4 * (lane >> 4);
+        const float dec = COORD ? __expf(-sRate[n] * d0) : __expf(-Ah * d0);
         float v[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int n = 16 * tnn + 4 * (lane >> 4) + i;
-          v[i] = st[k][i] * (COORD ? __expf(-sRate[n] * d0) : __expf(-Ah * d0));
-        }
+        for (int i = 0; i < 4; ++i) v[i] = st[k][i] * dec;
         if (COORD) {
+          // R(-theta_0) = R(theta_0)^T on the pair held by lanes (l, l ^ 1)
+          const bool pair = n >= nreal;
+          float sn = 0.f, cs = 1.f;
+          if (pair) fast_sincos(sOmega[(n - nreal) >> 1] * d0, &sn, &cs);
+          const float sg = (lane & 1) ? -sn : sn;
 #pragma unroll
-          for (int i = 0; i < 4; i += 2) {
-            const int n = 16 * tnn + 4 * (lane >> 4) + i;
-            if (n >= nreal) {
-              float sn, cs;
-              fast_sincos(sOmega[(n - nreal) >> 1] * d0, &sn, &cs);
-              const float a0 = v[i], a1 = v[i + 1];
-              v[i] = cs * a0 + sn * a1;  // R(-theta_0) = R(theta_0)^T
-              v[i + 1] = -sn * a0 + cs * a1;
-            }
+          for (int i = 0; i < 4; ++i) {
+            const float other = swap_adjacent_lanes(v[i]);
+            v[i] = pair ? cs * v[i] + sg * other : v[i];
           }
         }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) dst[(size_t)(16 * tnn + 4 * (lane >> 4) + i) * P + pl] = v[i];
+        *reinterpret_cast<float4*>(dst + (size_t)n * P + pl) = make_float4(v[0], v[1], v[2], v[3]);
       }
     }
   }
@@ -507,10 +501,23 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
   constexpr int XP = (S::X_VECS + S::NTH - 1) / S::NTH, YP = (S::Y_VECS + S::NTH - 1) / S::NTH;
   constexpr int SPV = (N / 2) * PV, SP = (SPV + S::NTH - 1) / S::NTH;
   uint4 pfc[CP], pfb[BP], pfx[XP], pfy[YP];
-  float4 pfs[SP][2], pfg[SP][2];
+  // 4-column pieces of the incoming state and the outgoing adjoint rows, as stored (io dtype)
+  using Raw4 = typename std::conditional<BF16, uint2, float4>::type;
+  Raw4 pfs[SP][2], pfg[SP][2];
+  auto raw4_f32 = [](const Raw4& r, float* v) {
+    if constexpr (BF16) {
+      v[0] = __uint_as_float(r.x << 16);
+      v[1] = __uint_as_float(r.x & 0xffff0000u);
+      v[2] = __uint_as_float(r.y << 16);
+      v[3] = __uint_as_float(r.y & 0xffff0000u);
+    } else {
+      v[0] = r.x; v[1] = r.y; v[2] = r.z; v[3] = r.w;
+    }
+  };
+  Raw4 zr4;
+  if constexpr (BF16) zr4 = make_uint2(0, 0); else zr4 = make_float4(0.f, 0.f, 0.f, 0.f);
   float pf_dt = 0.f, pf_be = 0.f, pf_ga = 0.f, pf_dtn = 0.f, pf_bn = 0.f;
   const uint4 zero4 = make_uint4(0, 0, 0, 0);
-  const float4 zf4 = make_float4(0.f, 0.f, 0.f, 0.f);
 
   // The loads of an item, in four parts (C / B rows, X / dy rows and the per-token
   // scalars, incoming states, outgoing adjoints).
@@ -568,30 +575,30 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
     }
     }
     if (part == 2) {
-      const float* Sg = p.saved + ((size_t)slice * (nch + 1) + c) * N * P;
+      const T* Sg = static_cast<const T*>(p.saved) + ((size_t)slice * (nch + 1) + c) * N * P;
 #pragma unroll
       for (int k = 0; k < SP; ++k) {
         const int v = tid + S::NTH * k;
-        float4 s0 = zf4, s1 = zf4;
+        Raw4 s0 = zr4, s1 = zr4;
         if (v < SPV) {
           const int n = 2 * (v / PV), q0 = (v % PV) * 4;
-          s0 = *reinterpret_cast<const float4*>(Sg + (size_t)n * P + q0);
-          s1 = *reinterpret_cast<const float4*>(Sg + (size_t)(n + 1) * P + q0);
+          s0 = *reinterpret_cast<const Raw4*>(Sg + (size_t)n * P + q0);
+          s1 = *reinterpret_cast<const Raw4*>(Sg + (size_t)(n + 1) * P + q0);
         }
         pfs[k][0] = s0; pfs[k][1] = s1;
       }
       return;
     }
     if (part == 3) {
-      const float* Gg = p.gseg + ((size_t)slice * nch + (c + 1)) * N * P;
+      const T* Gg = static_cast<const T*>(p.gseg) + ((size_t)slice * nch + (c + 1)) * N * P;
 #pragma unroll
       for (int k = 0; k < SP; ++k) {
         const int v = tid + S::NTH * k;
-        float4 g0 = zf4, g1 = zf4;
+        Raw4 g0 = zr4, g1 = zr4;
         if (v < SPV && has_next) {
           const int n = 2 * (v / PV), q0 = (v % PV) * 4;
-          g0 = *reinterpret_cast<const float4*>(Gg + (size_t)n * P + q0);
-          g1 = *reinterpret_cast<const float4*>(Gg + (size_t)(n + 1) * P + q0);
+          g0 = *reinterpret_cast<const Raw4*>(Gg + (size_t)n * P + q0);
+          g1 = *reinterpret_cast<const Raw4*>(Gg + (size_t)(n + 1) * P + q0);
         }
         pfg[k][0] = g0; pfg[k][1] = g1;
       }
@@ -806,13 +813,14 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
         if (v >= SPV) continue;
         const int rp = v / PV, pc = v % PV;
         const int n = 2 * rp, q0 = pc * 4;
-        float sa[4] = {pfs[k][0].x, pfs[k][0].y, pfs[k][0].z, pfs[k][0].w};
-        float sb[4] = {pfs[k][1].x, pfs[k][1].y, pfs[k][1].z, pfs[k][1].w};
-        float ga[4] = {pfg[k][0].x, pfg[k][0].y, pfg[k][0].z, pfg[k][0].w};
-        float gb[4] = {pfg[k][1].x, pfg[k][1].y, pfg[k][1].z, pfg[k][1].w};
+        float sa[4], sb[4], ga[4], gb[4];
+        raw4_f32(pfs[k][0], sa);
+        raw4_f32(pfs[k][1], sb);
+        raw4_f32(pfg[k][0], ga);
+        raw4_f32(pfg[k][1], gb);
         if (S::TE) {
-          *reinterpret_cast<float4*>(sGraw + n * P + q0) = pfg[k][0];
-          *reinterpret_cast<float4*>(sGraw + (n + 1) * P + q0) = pfg[k][1];
+          *reinterpret_cast<float4*>(sGraw + n * P + q0) = make_float4(ga[0], ga[1], ga[2], ga[3]);
+          *reinterpret_cast<float4*>(sGraw + (n + 1) * P + q0) = make_float4(gb[0], gb[1], gb[2], gb[3]);
         }
         float fa, fb, lea, leb;
         if (COORD) {

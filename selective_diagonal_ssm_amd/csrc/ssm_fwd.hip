@@ -407,11 +407,12 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
 
   const int nch = p.nchunks;
   const size_t sl_saved = (size_t)slice * (nch + 1);
-  if (p.saved && !local && seg == 0) {
+  T* saved = static_cast<T*>(p.saved);  // chunk-boundary states, stored in the io dtype
+  if (saved && !local && seg == 0) {
     // slot 0: the state entering chunk 0
     for (int i = tid; i < N * PB; i += S::NTH) {
       const int n = i / PB, pl = i % PB;
-      p.saved[(sl_saved * N + n) * P + p0 + pl] = h0s ? h0s[n * P + pl] : 0.f;
+      saved[(sl_saved * N + n) * P + p0 + pl] = from_f32<T>(h0s ? h0s[n * P + pl] : 0.f);
     }
   }
 
@@ -539,9 +540,7 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
           const int pl = 16 * tp + 4 * (lane >> 4);
           const float v4[4] = {acc[k][0], acc[k][1], acc[k][2], acc[k][3]};
           store4<BF16>(sST + (bi ^ 1) * S::NC * VS + n * VS + pl, v4);
-          if (p.saved && !local)
-            *reinterpret_cast<float4*>(p.saved + ((sl_saved + c + 1) * N + n) * P + p0 + pl) =
-                make_float4(v4[0], v4[1], v4[2], v4[3]);
+          if (saved && !local) store4<BF16>(saved + ((sl_saved + c + 1) * N + n) * P + p0 + pl, v4);
         }
       }
     }

@@ -17,7 +17,7 @@ struct FwdParams {
   const float* gamma;
   const float* D;
   void* y;
-  float* saved;  // [batch][nheads][nchunks + 1][N][P] fp32, or null
+  void* saved;   // [batch][nheads][nchunks + 1][N][P] in the io dtype, or null
   const float* h0;  // [batch][nheads][N][P] fp32 state before token 0, or null
   float* h_final;   // [batch][nheads][N][P] fp32 state after the last token, or null
   int batch, L, H, G, P, n_real, n_pairs, nchunks, npblk;
@@ -42,7 +42,7 @@ struct BwdParams {
   const float* beta;
   const float* gamma;
   const float* D;
-  const float* saved;
+  const void* saved;  // forward's chunk-boundary states (io dtype)
   void* dx;
   void* dB;
   void* dC;
@@ -50,7 +50,7 @@ struct BwdParams {
   float* dbeta;
   float* dgamma;
   float* part;     // per-(slice, segment) parameter-gradient partials (workspace)
-  float* gseg;     // segment-boundary adjoint states (workspace)
+  void* gseg;      // chunk-boundary adjoint states, io dtype (workspace)
   float* dA;
   float* domega;
   float* dD;

@@ -27,7 +27,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_abi_version_and_status_strings():
     lib = ssm.load()
-    assert lib.ssm_abi_version() == 2
+    assert lib.ssm_abi_version() == 3
     for s in range(0, -8, -1):
         assert lib.ssm_status_string(s)
 
@@ -70,7 +70,9 @@ def test_chunk_and_saved_bytes():
     d = _lib.make_desc(base_desc(), "bf16")
     assert ssm.chunk_tokens(d) == 64
     nch = (100 + 63) // 64
-    assert ssm.saved_bytes(d) == 2 * 4 * (nch + 1) * 64 * 64 * 4
+    assert ssm.saved_bytes(d) == 2 * 4 * (nch + 1) * 64 * 64 * 2  # bf16 states
+    df = _lib.make_desc(base_desc(), "f32")
+    assert ssm.saved_bytes(df) == 2 * 4 * (nch + 1) * 64 * 64 * 4
     dh = _lib.make_desc(base_desc(decay_mode="coord", n_real=32, n_pairs=16, rank_in=2,
                                   rank_out=2, two_endpoint=True), "bf16")
     assert ssm.chunk_tokens(dh) == 16
