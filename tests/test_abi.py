@@ -71,8 +71,8 @@ def test_chunk_and_saved_bytes():
     assert ssm.chunk_tokens(d) == 64
     nch = (100 + 63) // 64
     assert ssm.saved_bytes(d) == 2 * 4 * (nch + 1) * 64 * 64 * 2  # bf16 states
-    df = _lib.make_desc(base_desc(), "f32")
-    assert ssm.saved_bytes(df) == 2 * 4 * (nch + 1) * 64 * 64 * 4
+    df = _lib.make_desc(base_desc(dstate=32, n_real=32, headdim=16), "f32")  # fp32 states
+    assert ssm.saved_bytes(df) == 2 * 4 * (nch + 1) * 32 * 16 * 4
     dh = _lib.make_desc(base_desc(decay_mode="coord", n_real=32, n_pairs=16, rank_in=2,
                                   rank_out=2, two_endpoint=True), "bf16")
     assert ssm.chunk_tokens(dh) == 16
