@@ -434,7 +434,7 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
   __shared__ __align__(16) T sGh[S::NC * PS];   // folded adjoint G~ (io dtype)
   __shared__ __align__(16) T sSh[N * PS];        // incoming state (io dtype)
   __shared__ float sRate[N], sOmega[N / 2 + 1];
-  __shared__ float sE[N], sEth[N / 2 + 1];       // final-state terms per row / pair
+  __shared__ float sE2[2][N], sEth[N / 2 + 1];   // final-state terms per row (by item parity) / pair
   constexpr int WC = COORD ? NW : 1, WH = COORD ? 1 : NW, WT = S::TE ? NW : 1;
   constexpr int NCO = COORD ? N : 1, PCO = COORD ? N / 2 + 1 : 1;
   __shared__ float sEK[WC][NCO], sEKth[WC][PCO];  // per-wave inter source sums per row / pair
@@ -644,13 +644,20 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
   int item = blockIdx.x;
   if (item < nitems)
     for (int part = 0; part < 4; ++part) prefetch(item, part);
-  for (; item < nitems; item += gridDim.x) {
+  // Plain head decay: wave 0's step-gradient tail of an item reads only per-wave sums
+  // (zeroed by their own wave after the staging barrier) and the final-state terms
+  // (double-buffered by item parity), so the other waves go on with the next item's
+  // staging while it runs; the staging barrier then waits for wave 0.
+  constexpr bool RELAXED = !COORD && !S::TE;
+  int par = 0;
+  for (; item < nitems; item += gridDim.x, par ^= 1) {
     const int slice = item / nch, c = item % nch;
     const int b = slice / H, h = slice % H, g = h / (H / G);
     const int t0 = c * QT, tn = t0 + QT;
     const bool has_next = tn < L;
+    float* sE = sE2[par];
 
-    __syncthreads();  // the previous item is done with every shared buffer
+    if (!RELAXED) __syncthreads();  // the previous item is done with every shared buffer
     if (COORD) {
       const int na = nreal + npairs;
       for (int n = tid; n < N; n += S::NTH) {
@@ -662,13 +669,15 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
       }
       for (int k = tid; k < npairs; k += S::NTH) sOmega[k] = p.omega[(size_t)h * npairs + k];
     }
-    for (int i = tid; i < WC * 64; i += S::NTH) (&sTok[0][0])[i] = 0.f;
-    for (int i = tid; i < WH * 64; i += S::NTH) {
-      (&sTT[0][0])[i] = 0.f; (&sSrc[0][0])[i] = 0.f; (&sRS[0][0])[i] = 0.f; (&sCS[0][0])[i] = 0.f;
+    if (!RELAXED) {
+      for (int i = tid; i < WC * 64; i += S::NTH) (&sTok[0][0])[i] = 0.f;
+      for (int i = tid; i < WH * 64; i += S::NTH) {
+        (&sTT[0][0])[i] = 0.f; (&sSrc[0][0])[i] = 0.f; (&sRS[0][0])[i] = 0.f; (&sCS[0][0])[i] = 0.f;
+      }
+      for (int i = tid; i < WT * 64; i += S::NTH) { (&sDg[0][0])[i] = 0.f; (&sDb[0][0])[i] = 0.f; }
+      for (int i = tid; i < WC * NCO; i += S::NTH) { (&sEK[0][0])[i] = 0.f; (&sPA[0][0])[i] = 0.f; }
+      for (int i = tid; i < WC * PCO; i += S::NTH) { (&sEKth[0][0])[i] = 0.f; (&sPW[0][0])[i] = 0.f; }
     }
-    for (int i = tid; i < WT * 64; i += S::NTH) { (&sDg[0][0])[i] = 0.f; (&sDb[0][0])[i] = 0.f; }
-    for (int i = tid; i < WC * NCO; i += S::NTH) { (&sEK[0][0])[i] = 0.f; (&sPA[0][0])[i] = 0.f; }
-    for (int i = tid; i < WC * PCO; i += S::NTH) { (&sEKth[0][0])[i] = 0.f; (&sPW[0][0])[i] = 0.f; }
     if (COORD) __syncthreads();  // rates and pair frequencies before the staging reads them
     const float Ah = COORD ? 0.f : p.A[h];
     const float Dh = p.has_D ? p.D[h] : 0.f;
@@ -870,6 +879,10 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
       for (int part = 0; part < 4; ++part) prefetch(nxt, part);
     if (prev >= 0) flush_scalars(prev);
     __syncthreads();
+    if (RELAXED) {
+      // this wave's own per-token sums (only it accumulates into them)
+      sTT[wave][lane] = 0.f; sSrc[wave][lane] = 0.f; sRS[wave][lane] = 0.f; sCS[wave][lane] = 0.f;
+    }
     // two-endpoint tails of the last token from the staged rows: beta_{t0'} B_{t1}^T g'
     // and g' X_{t1}^T (zero without a next chunk, where g' and beta_{t0'} are zero)
     if (S::TE) {
