@@ -885,18 +885,30 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
     }
     // two-endpoint tails of the last token from the staged rows: beta_{t0'} B_{t1}^T g'
     // and g' X_{t1}^T (zero without a next chunk, where g' and beta_{t0'} are zero)
+    // Each of the R P + R N outputs is a dot product of length N or P split over TT
+    // adjacent lanes, summed by a fixed butterfly.
     if (S::TE) {
-      for (int i = tid; i < R * P; i += S::NTH) {
-        const int r = i / P, pp = i % P;
+      constexpr int O1 = R * P, OT = R * P + R * N;
+      constexpr int TQ = S::NTH / OT;
+      constexpr int TT = TQ >= 16 ? 16 : TQ >= 8 ? 8 : TQ >= 4 ? 4 : TQ >= 2 ? 2 : 1;
+      static_assert(N % TT == 0 && P % TT == 0, "tail dot products split evenly");
+      for (int base = 0; base < OT * TT; base += S::NTH) {
+        const int u = base + tid, o = u / TT, part = u % TT;
         float acc = 0.f;
-        for (int n = 0; n < N; ++n) acc += to_f32(sBt1[r * N + n]) * sGraw[n * P + pp];
-        sTailX[i] = bnext * acc;
-      }
-      for (int i = tid; i < R * N; i += S::NTH) {
-        const int r = i / N, n = i % N;
-        float acc = 0.f;
-        for (int pp = 0; pp < P; ++pp) acc += sGraw[n * P + pp] * to_f32(sXt1[r * P + pp]);
-        sTailB[i] = bnext * acc;
+        if (o < O1) {
+          const int r = o / P, pp = o % P;
+#pragma unroll 2
+          for (int n = part * (N / TT); n < (part + 1) * (N / TT); ++n)
+            acc += to_f32(sBt1[r * N + n]) * sGraw[n * P + pp];
+        } else if (o < OT) {
+          const int r = (o - O1) / N, n = (o - O1) % N;
+#pragma unroll 2
+          for (int pp = part * (P / TT); pp < (part + 1) * (P / TT); ++pp)
+            acc += sGraw[n * P + pp] * to_f32(sXt1[r * P + pp]);
+        }
+        acc = group_sum<TT>(acc);
+        if (part == 0 && o < O1) sTailX[o] = bnext * acc;
+        else if (part == 0 && o < OT) sTailB[o - O1] = bnext * acc;
       }
     }
     if (p.has_D) {
