@@ -170,7 +170,9 @@ int ssm_scan_fwd(const ssm_desc *desc, const ssm_fwd_args *args, void *ws, size_
 
 /* Fused reverse-mode pass: dx, dB, dC, ddt and the requested parameter
    gradients (dA, domega, dbeta, dgamma, dD), given dy and the forward's
-   `saved` states. */
+   `saved` states.  When groups are shared by several heads (ngroups < nheads),
+   dB and dC of a group are the sums over its heads, taken in a fixed head order
+   from per-head partials in the workspace, so every call gives the same bits. */
 int ssm_scan_bwd(const ssm_desc *desc, const ssm_bwd_args *args, void *ws, size_t ws_bytes,
                  void *stream);
 

@@ -190,6 +190,15 @@ static size_t bwd_gseg_bytes(const ssm_desc* d, const Plan& pl) {
   return (size_t)d->batch * d->nheads * pl.nchunks * d->dstate * d->headdim * (pl.bf16 ? 2 : 4);
 }
 
+// head groups shared by several heads: per-head dB and dC partials in the io dtype
+static size_t group_partial_one(const ssm_desc* d, const Plan& pl) {
+  const size_t one = (size_t)d->batch * d->seqlen * d->nheads * d->rank_in * d->dstate * (pl.bf16 ? 2 : 4);
+  return (one + 255) / 256 * 256;
+}
+static size_t group_partial_bytes(const ssm_desc* d, const Plan& pl) {
+  return d->ngroups == d->nheads ? 0 : 2 * group_partial_one(d, pl);
+}
+
 static size_t fwd_segment_bytes(const ssm_desc* d, const Plan& pl, const FwdKey& key) {
   const long slices = (long)d->batch * d->nheads;
   const Segs sg = segments(slices * (d->headdim / key.PB), pl.nchunks);
@@ -219,7 +228,7 @@ size_t ssm_workspace_bytes(const ssm_desc* d, int for_backward) {
   }
   const size_t g = (bwd_gseg_bytes(d, pl) + 255) / 256 * 256;
   const size_t part = (size_t)d->batch * d->nheads * pl.nchunks * npart_of(d, pl) * sizeof(float);
-  return g + (part + 255) / 256 * 256 + adj_segment_bytes(d, pl);
+  return g + (part + 255) / 256 * 256 + adj_segment_bytes(d, pl) + group_partial_bytes(d, pl);
 }
 
 int ssm_scan_fwd(const ssm_desc* d, const ssm_fwd_args* a, void* ws, size_t ws_bytes,
@@ -279,8 +288,6 @@ int ssm_scan_bwd(const ssm_desc* d, const ssm_bwd_args* a, void* ws, size_t ws_b
   int rc = make_plan(d, &pl);
   if (rc) return rc;
   if (!a) return SSM_ERR_NULL;
-  // head groups shared by several heads would need a cross-head sum of dB / dC
-  if (d->ngroups != d->nheads) return SSM_ERR_UNSUPPORTED;
   BwdKey key{pl.bf16, d->dstate, d->headdim, pl.R, pl.KR, pl.QT, pl.coord_kernel};
   if (!ssm::bwd_variant_exists(key)) return SSM_ERR_UNSUPPORTED;
   if (d->batch == 0 || d->seqlen == 0) return SSM_OK;
@@ -327,6 +334,12 @@ int ssm_scan_bwd(const ssm_desc* d, const ssm_bwd_args* a, void* ws, size_t ws_b
     p.gloc = reinterpret_cast<float*>(base);
     p.gin = p.gloc + st;
     p.gdel = p.gin + st;
+  }
+  if (d->ngroups != d->nheads) {
+    // per-head dB / dC partials at the end of the workspace
+    char* base = static_cast<char*>(ws) + (need - group_partial_bytes(d, pl));
+    p.dBh = base;
+    p.dCh = base + group_partial_one(d, pl);
   }
   p.softplus = (d->flags & SSM_F_DT_SOFTPLUS) ? 1 : 0;
   p.has_D = hasD ? 1 : 0;

@@ -467,8 +467,15 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
   const T* Cg = static_cast<const T*>(p.C);
   const T* dyg = static_cast<const T*>(p.dy);
   T* dxg = static_cast<T*>(p.dx);
-  T* dBg = static_cast<T*>(p.dB);
-  T* dCg = static_cast<T*>(p.dC);
+  // dB / dC rows go straight to the outputs when every head has its own group; else to
+  // per-head partials [batch][L][nheads][R][N], summed over each group by ssm_bwd_group_sum
+  const bool part = p.dBh != nullptr;
+  T* dBg = static_cast<T*>(part ? p.dBh : p.dB);
+  T* dCg = static_cast<T*>(part ? p.dCh : p.dC);
+  const int GO = part ? H : G;  // rows per token of those buffers
+  auto store_bc = [&](T* out, int bb, int t, int go, int r, int n, const float* v) {
+    store4<BF16>(out + ((((size_t)bb * L + t) * GO + go) * R + r) * N + n, v);
+  };
 
   // zero padding rows / columns (the staging never writes them)
   for (int i = tid; i < (S::NC - N) * PS; i += S::NTH) sGh[N * PS + i] = T(0);
@@ -1104,7 +1111,7 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
               make_float4(wgt * dk[0], wgt * dk[1], wgt * dk[2], wgt * dk[3]);
         }
       } else if (tb < L) {
-        store4<BF16>(dBg + ((((size_t)b * L + tb) * G + g) * R + rr) * N + n0, dk);
+        store_bc(dBg, b, tb, part ? h : g, rr, n0, dk);
       }
       if (COORD) {
         // per-row sums over the 16 key columns of this tile (one 16-lane group)
@@ -1241,7 +1248,7 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
           }
         }
       }
-      if (tg < L) store4<BF16>(dCg + ((((size_t)b * L + tg) * G + g) * R + o) * N + n0, dc);
+      if (tg < L) store_bc(dCg, b, tg, part ? h : g, o, n0, dc);
       if (COORD) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) rpa[i] = group_sum<16>(rpa[i]);
@@ -1341,7 +1348,7 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
             ? *reinterpret_cast<const float4*>(sDB + (QT + 1) * R * N + ((s + 1) * R + r) * N + n)
             : *reinterpret_cast<const float4*>(sTailB + r * N + n);
         const float v[4] = {a.x + e.x, a.y + e.y, a.z + e.z, a.w + e.w};
-        if (t < L) store4<BF16>(dBg + ((((size_t)b * L + t) * G + g) * R + r) * N + n, v);
+        if (t < L) store_bc(dBg, b, t, part ? h : g, r, n, v);
       }
     }
 
@@ -1430,6 +1437,37 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
   }  // items
   __syncthreads();
   if (prev >= 0) flush_scalars(prev);
+}
+
+// ============================================================== group sums of dB / dC
+// dB and dC of a head group are the sums of its heads' partials (io dtype), added in head
+// order in fp32 (deterministic).  One thread per 4-element piece of a (batch, token, group,
+// row).
+template <bool BF16>
+__global__ __launch_bounds__(256) void ssm_bwd_group_sum(BwdParams p, int R) {
+  using T = typename Elem<BF16>::T;
+  const int N = p.n_real + 2 * p.n_pairs, H = p.H, G = p.G, hpg = H / G;
+  const long total = (long)p.batch * p.L * G * R * (N / 4);
+  for (long i = (long)blockIdx.x * 256 + threadIdx.x; i < total; i += (long)gridDim.x * 256) {
+    const int n4 = (int)(i % (N / 4)) * 4;
+    long r = i / (N / 4);
+    const int rr = (int)(r % R);
+    r /= R;
+    const int g = (int)(r % G);
+    const long bt = r / G;  // batch * L + token
+#pragma unroll 1
+    for (int which = 0; which < 2; ++which) {
+      const T* part = static_cast<const T*>(which ? p.dCh : p.dBh);
+      T* out = static_cast<T*>(which ? p.dC : p.dB);
+      float v[4] = {0.f, 0.f, 0.f, 0.f};
+      for (int k = 0; k < hpg; ++k) {
+        float a[4];
+        load4<BF16>(part + ((bt * H + g * hpg + k) * R + rr) * N + n4, a);
+        v[0] += a[0]; v[1] += a[1]; v[2] += a[2]; v[3] += a[3];
+      }
+      store4<BF16>(out + ((bt * G + g) * R + rr) * N + n4, v);
+    }
+  }
 }
 
 // ============================================================== parameter sums
@@ -1557,6 +1595,11 @@ hipError_t launch_bwd(const BwdKey& k, const BwdParams& p, hipStream_t stream,
       const int grid = std::min(items, device_cus() * blocks_per_cu(kfn, CHUNK_NT, occ));      \
       hipLaunchKernelGGL((ssm_bwd_chunk<BF, NN, PP, RR, KRR, QTT, CO, CHUNK_NT>), dim3(grid),  \
                          dim3(CHUNK_NT), 0, stream, p);                                       \
+    }                                                                                         \
+    if (p.dBh) {                                                                              \
+      const long total = (long)p.batch * p.L * p.G * RR * (NN / 4);                          \
+      const int gb = (int)std::min<long>((total + 255) / 256, 4096);                         \
+      hipLaunchKernelGGL(ssm_bwd_group_sum<BF>, dim3(gb), dim3(256), 0, stream, p, RR);      \
     }                                                                                         \
     mark(2);                                                                                  \
     hipLaunchKernelGGL(ssm_bwd_params, dim3((p.H * p.npart + 3) / 4), dim3(256), 0,          \

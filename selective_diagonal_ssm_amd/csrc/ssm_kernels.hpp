@@ -55,6 +55,11 @@ struct BwdParams {
   float* domega;
   float* dD;
   float* dh0;  // [batch][nheads][N][P] fp32, or null
+  // head groups shared by several heads: per-head dB / dC partials in the io dtype,
+  // [batch][L][nheads][R][N] (workspace), summed over each group's heads afterwards;
+  // null when every head has its own group
+  void* dBh;
+  void* dCh;
   int batch, L, H, G, P, n_real, n_pairs, nchunks;
   int nseg, chunks_per_seg;  // sequence segments of the boundary-adjoint sweep
   int softplus, has_D, npart;

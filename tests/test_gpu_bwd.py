@@ -44,6 +44,15 @@ SMALL = {
     "bf16_hybrid": ("hybrid", dict(batch=2, seqlen=150, nheads=2, ngroups=2)),
     "bf16_hybrid_r1": ("hybrid_r1", dict(batch=2, seqlen=150, nheads=2, ngroups=2)),
     "bf16_len_chunk1": ("hybrid", dict(batch=1, seqlen=17, nheads=2, ngroups=2)),
+    # B / C groups shared by several heads: dB / dC sum over the group's heads
+    "f32_groups_siso": ("ssd_siso", dict(dtype="f32", dstate=32, n_real=32, headdim=16, batch=2,
+                                         nheads=4, ngroups=2, seqlen=150)),
+    "f32_groups_hybrid": ("hybrid", dict(dtype="f32", dstate=32, n_real=16, n_pairs=8,
+                                         headdim=16, batch=2, nheads=3, ngroups=1, seqlen=77)),
+    "bf16_groups_siso": ("ssd_siso", dict(batch=2, seqlen=130, nheads=4, ngroups=2)),
+    "bf16_groups_mimo": ("ssd_mimo", dict(batch=1, seqlen=200, nheads=4, ngroups=1)),
+    "bf16_groups_hybrid": ("hybrid", dict(batch=2, seqlen=150, nheads=4, ngroups=2)),
+    "bf16_groups_hybrid_r1": ("hybrid_r1", dict(batch=1, seqlen=90, nheads=6, ngroups=3)),
 }
 
 

@@ -58,8 +58,6 @@ def test_wide_forward_matches_oracle(case, nseg, monkeypatch):
     ey, eh = rel_l2(_np(y), yr), rel_l2(_np(hf), hr)
     print(f"[fwd-wide] case={case} nseg={nseg} y={ey:.2e} h_final={eh:.2e}", flush=True)
     assert ey <= tol(prob) and eh <= tol(prob), (ey, eh)
-    if prob["desc"]["ngroups"] != prob["desc"]["nheads"]:
-        return  # the reverse pass takes one B / C group per head
     # the saved boundary states feed the reverse pass
     g = ssm.backward(prob["desc"], prob["dtype"], t["x"], t["B"], t["C"], t["dy"], t["dt"], t["A"],
                      saved, D=t.get("D"), want=("dA", "dD", "dh0"))
