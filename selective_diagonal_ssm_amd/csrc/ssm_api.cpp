@@ -199,12 +199,27 @@ static size_t group_partial_bytes(const ssm_desc* d, const Plan& pl) {
   return d->ngroups == d->nheads ? 0 : 2 * group_partial_one(d, pl);
 }
 
+// local-pass ranges of a segment: as few as keep each within kLocalMaxTokens tokens
+struct LocalRanges {
+  int seg_tokens, nsub, lsub;
+};
+static LocalRanges local_ranges(const Plan& pl, const Segs& sg) {
+  const int st = sg.cps * pl.QT;
+  const int nsub = (st + ssm::kLocalMaxTokens - 1) / ssm::kLocalMaxTokens;
+  return {st, nsub, (st + nsub - 1) / nsub};
+}
+
+// workspace of the segmented forward: the range states of the local pass, the states
+// entering the segments and the ranges' summed steps
 static size_t fwd_segment_bytes(const ssm_desc* d, const Plan& pl, const FwdKey& key) {
   const long slices = (long)d->batch * d->nheads;
   const Segs sg = segments(slices * (d->headdim / key.PB), pl.nchunks);
   if (sg.nseg <= 1) return 0;
-  const size_t st = (size_t)slices * sg.nseg * d->dstate * d->headdim * sizeof(float);
-  return 2 * st + ((size_t)slices * sg.nseg * sizeof(float) + 255) / 256 * 256;
+  const LocalRanges lr = local_ranges(pl, sg);
+  const size_t np = (size_t)d->dstate * d->headdim;
+  const size_t loc = (size_t)slices * (sg.nseg - 1) * lr.nsub * np * sizeof(float);
+  const size_t in = (size_t)slices * sg.nseg * np * sizeof(float);
+  return loc + in + ((size_t)slices * (sg.nseg - 1) * lr.nsub * sizeof(float) + 255) / 256 * 256;
 }
 
 // boundary-adjoint sweep segments: one workgroup per (slice, segment)
@@ -273,10 +288,14 @@ int ssm_scan_fwd(const ssm_desc* d, const ssm_fwd_args* a, void* ws, size_t ws_b
     const size_t need = fwd_segment_bytes(d, pl, key);
     if (!ws || ws_bytes < need) return SSM_ERR_WORKSPACE;
     if (!aligned(ws, 16)) return SSM_ERR_ALIGN;
-    const size_t st = (size_t)d->batch * d->nheads * sg.nseg * d->dstate * d->headdim;
+    const LocalRanges lr = local_ranges(pl, sg);
+    p.seg_tokens = lr.seg_tokens;
+    p.nsub = lr.nsub;
+    p.lsub = lr.lsub;
+    const size_t slices = (size_t)d->batch * d->nheads, np = (size_t)d->dstate * d->headdim;
     p.seg_local = static_cast<float*>(ws);
-    p.seg_in = p.seg_local + st;
-    p.seg_delta = p.seg_in + st;
+    p.seg_in = p.seg_local + slices * (sg.nseg - 1) * lr.nsub * np;
+    p.seg_delta = p.seg_in + slices * sg.nseg * np;
   }
   const hipError_t e = ssm::launch_fwd(key, p, static_cast<hipStream_t>(stream), a->events);
   return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;

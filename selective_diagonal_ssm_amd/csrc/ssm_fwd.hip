@@ -61,7 +61,15 @@ struct FwdShape {
   // staging items: C vectors, then key items (a B vector and the endpoint it is
   // written at: two per vector with two-endpoint writes), then X vectors
   static constexpr int K_ITEMS = TE ? 2 * B_VECS : B_VECS;
-  static constexpr int ALL_VECS = C_VECS + K_ITEMS + X_VECS;
+  // Each kind starts on a wave boundary (a wave holding two kinds runs both code
+  // paths).  With per-row decay the key items, the costliest to stage, come first:
+  // they land on the first waves, which take no output tiles (those go from the last
+  // wave down).  Head decay keeps C, K, X.
+  static constexpr int CP = (C_VECS + 63) / 64 * 64, KP = (K_ITEMS + 63) / 64 * 64;
+  static constexpr int K0 = COORD ? 0 : CP;
+  static constexpr int C0 = COORD ? KP : 0;
+  static constexpr int X0 = CP + KP;
+  static constexpr int ALL_VECS = X0 + X_VECS;
   static constexpr int ALL_PER = (ALL_VECS + NTH - 1) / NTH;
   static constexpr int TQ = QO / 16, TK = QK / 16, TP = PB / 16, TN = N / 16;
   static constexpr int ST_TILES = TN * TP;
@@ -125,8 +133,6 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int lid = xcd_logical_id(blockIdx.x, gridDim.x);
   const int slice = lid / (p.npblk * p.nseg), seg = (lid / p.npblk) % p.nseg, pblk = lid % p.npblk;
-  const bool local = p.state_only != 0;
-  if (local && seg == p.nseg - 1) return;  // the last segment's local state is never needed
   const int c0 = seg * p.cps, c1 = min(p.nchunks, c0 + p.cps);  // this workgroup's chunks
   const int b = slice / p.H, h = slice % p.H;
   const int g = h / (p.H / p.G);
@@ -150,7 +156,7 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
   // buffer 0 holds the state entering the first chunk: h0 (rows < N, this P-block),
   // the combined state entering a later segment, or zero
   const float* h0s = seg == 0 ? (p.h0 ? p.h0 + (size_t)slice * N * P + p0 : nullptr)
-                              : (local ? nullptr : p.seg_in + ((size_t)slice * p.nseg + seg) * N * P + p0);
+                              : p.seg_in + ((size_t)slice * p.nseg + seg) * N * P + p0;
   for (int i = tid; i < 2 * S::NC * VS; i += S::NTH) {
     const int n = i / VS, col = i % VS;
     sST[i] = (h0s && n < N && col < PB) ? from_f32<T>(h0s[n * P + col]) : T(0);
@@ -194,10 +200,14 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
       st[k] = f32x4{v.x, v.y, v.z, v.w};
     }
   }
+  // take the h0 loads here: left pending into the chunk loop, they would make the
+  // compiler wait on every outstanding memory operation before each state update
+#pragma unroll
+  for (int k = 0; k < S::ST_PER_WAVE; ++k) asm volatile("" : "+v"(st[k]));
 
-  // The operand vectors of a chunk form one item list -- C rows, then B rows, then
-  // X rows (16 bytes each) -- dealt round-robin over all threads, so that every
-  // wave takes a share of the staging.
+  // The operand vectors of a chunk form one item list -- C rows, B rows (key items)
+  // and X rows, 16 bytes each, in the order of FwdShape -- dealt round-robin over all
+  // threads, so that every wave takes a share of the staging.
   uint4 rr[S::ALL_PER];
   float rdt = 0.f, rbe = 0.f, rga = 0.f;
   const uint4 zero4 = make_uint4(0, 0, 0, 0);
@@ -208,17 +218,17 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
     for (int k = 0; k < S::ALL_PER; ++k) {
       const int u = tid + S::NTH * k;
       uint4 val = zero4;
-      if (u < S::C_VECS) {
-        const int row = u / S::NVEC_N, nv = u % S::NVEC_N;
+      if (u >= S::C0 && u < S::C0 + S::C_VECS) {
+        const int row = (u - S::C0) / S::NVEC_N, nv = (u - S::C0) % S::NVEC_N;
         const int t = t0 + row / R, o = row % R;
-        if (t < L && !local) val = *reinterpret_cast<const uint4*>(Cg + t * tsG + o * N + nv * VEC);
-      } else if (u < S::C_VECS + S::K_ITEMS) {
-        const int v = (u - S::C_VECS) >> S::TEH;  // the two endpoints of a vector load it twice
+        if (t < L) val = *reinterpret_cast<const uint4*>(Cg + t * tsG + o * N + nv * VEC);
+      } else if (u >= S::K0 && u < S::K0 + S::K_ITEMS) {
+        const int v = (u - S::K0) >> S::TEH;  // the two endpoints of a vector load it twice
         const int row = v / S::NVEC_N, nv = v % S::NVEC_N;
         const int t = t0 + row / R - S::TEH, r = row % R;
         if (t >= 0 && t < L) val = *reinterpret_cast<const uint4*>(Bg + t * tsG + r * N + nv * VEC);
-      } else if (u < S::ALL_VECS) {
-        const int v = u - S::C_VECS - S::K_ITEMS;
+      } else if (u >= S::X0 && u < S::ALL_VECS) {
+        const int v = u - S::X0;
         const int row = v / S::NVEC_P, pv = v % S::NVEC_P;
         const int t = t0 + row / R - S::TEH, r = row % R;
         if (t >= 0 && t < L) val = *reinterpret_cast<const uint4*>(xg + t * tsH + r * P + pv * VEC);
@@ -239,7 +249,6 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
   };
 
   // ---- a1: per-token factors of chunk c into buffer bi (wave PW only; lane = token)
-  float segsum = 0.f;  // wave PW: sum of Delta over the chunks formed so far
   auto factors = [&](int c, int bi) {
     const int t0 = c * QT;
     float dl = 0.f;
@@ -252,7 +261,6 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
         sLC[bi][lane] = -Ah * kLog2e * cd;
       }
     }
-    segsum += cdend;
     if (lane == 0) {
       sMisc[bi][0] = cdend;
       sMisc[bi][1] = COORD ? 0.f : __builtin_amdgcn_exp2f(-Ah * kLog2e * cdend);
@@ -317,9 +325,8 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
 #pragma unroll
     for (int k = 0; k < S::ALL_PER; ++k) {
       const int u = tid + S::NTH * k;
-      if (u < S::C_VECS) {
-        if (local) continue;
-        const int row = u / S::NVEC_N, nv = u % S::NVEC_N;
+      if (u >= S::C0 && u < S::C0 + S::C_VECS) {
+        const int row = (u - S::C0) / S::NVEC_N, nv = (u - S::C0) % S::NVEC_N;
         const int n0 = nv * VEC;
         if (COORD) {
           const int t = row / R;
@@ -336,8 +343,8 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
         } else {
           *reinterpret_cast<uint4*>(q + row * NS + n0) = rr[k];
         }
-      } else if (u < S::C_VECS + S::K_ITEMS) {
-        const int v = (u - S::C_VECS) >> S::TEH;
+      } else if (u >= S::K0 && u < S::K0 + S::K_ITEMS) {
+        const int v = (u - S::K0) >> S::TEH;
         const int row = v / S::NVEC_N, nv = v % S::NVEC_N;
         const int n0 = nv * VEC;
         const int sl = row / R - S::TEH, r = row % R;
@@ -346,7 +353,7 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
           continue;
         }
         // e = 0: gamma_s B_s written at s = sl; e = 1: beta_{s+1} B_s written at s+1
-        const int e = S::TE ? ((u - S::C_VECS) & 1) : 0;
+        const int e = S::TE ? ((u - S::K0) & 1) : 0;
         const int tau = sl + e;
         if (tau < 0 || tau >= QT) continue;
         const int j = tau * KR + (e ? R : 0) + r;
@@ -368,8 +375,8 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
           for (int i = 0; i < VEC; ++i) kk[i] = uu[i];
         }
         *reinterpret_cast<uint4*>(kb + j * NS + n0) = pack<BF16>(kk);
-      } else if (u < S::ALL_VECS) {
-        const int v = u - S::C_VECS - S::K_ITEMS;
+      } else if (u >= S::X0 && u < S::ALL_VECS) {
+        const int v = u - S::X0;
         const int row = v / S::NVEC_P, pv = v % S::NVEC_P;
         const int sl = row / R - S::TEH, r = row % R;
 #pragma unroll
@@ -408,7 +415,7 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
   const int nch = p.nchunks;
   const size_t sl_saved = (size_t)slice * (nch + 1);
   T* saved = static_cast<T*>(p.saved);  // chunk-boundary states, stored in the io dtype
-  if (saved && !local && seg == 0) {
+  if (saved && seg == 0) {
     // slot 0: the state entering chunk 0
     for (int i = tid; i < N * PB; i += S::NTH) {
       const int n = i / PB, pl = i % PB;
@@ -436,7 +443,7 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
 
   for (int c = c0; c < c1; ++c) {
     const int bi = (c - c0) & 1;
-    if (c > c0 && !local) store_rows(c - 1);  // drains while the scores compute
+    if (c > c0) store_rows(c - 1);  // drains while the scores compute
     const T* q = sQ + bi * QSZ;
     const T* qe = sQe + (COORD ? bi * QSZ : 0);
     const T* kb = sK + bi * KSZ;
@@ -448,7 +455,7 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
     // lane l holds query row 16 ti + (l & 15) against keys 16 tj + 4 (l >> 4) + i),
     // the a4/a5 state update of chunk c; wave PW also forms the per-token factors
     // of chunk c+1
-    for (int tile = wave; tile < (local ? 0 : S::SC_TILES); tile += NW) {
+    for (int tile = wave; tile < S::SC_TILES; tile += NW) {
       int ti = 0, tj = tile;
 #pragma unroll
       for (int a = 0; a < S::TQ - 1; ++a) {
@@ -540,7 +547,7 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
           const int pl = 16 * tp + 4 * (lane >> 4);
           const float v4[4] = {acc[k][0], acc[k][1], acc[k][2], acc[k][3]};
           store4<BF16>(sST + (bi ^ 1) * S::NC * VS + n * VS + pl, v4);
-          if (saved && !local) store4<BF16>(saved + ((sl_saved + c + 1) * N + n) * P + p0 + pl, v4);
+          if (saved) store4<BF16>(saved + ((sl_saved + c + 1) * N + n) * P + p0 + pl, v4);
         }
       }
     }
@@ -563,7 +570,7 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
     {
       constexpr int BQ = S::YBQ, BP = S::YBP, NBP = S::TP / BP;
       constexpr int NBLK = (S::TQ / BQ) * NBP;
-      for (int blk = NW - 1 - wave; blk < (local ? 0 : NBLK); blk += NW) {
+      for (int blk = NW - 1 - wave; blk < NBLK; blk += NW) {
         const int ti0 = (blk / NBP) * BQ, tp0 = (blk % NBP) * BP;
         f32x4 acc[BQ][BP];
 #pragma unroll
@@ -634,12 +641,9 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
     }
     __syncthreads();
   }
-  if (!local) store_rows(c1 - 1);
-  // local pass: the segment's final state (from a zero start) and its summed Delta
-  // for the combine step; full pass: the final state after the last segment
-  float* hf = local ? p.seg_local + ((size_t)slice * p.nseg + seg) * N * P + p0
-                    : (seg == p.nseg - 1 && p.h_final ? p.h_final + (size_t)slice * N * P + p0 : nullptr);
-  if (local && pblk == 0 && wave == PW && lane == 0) p.seg_delta[(size_t)slice * p.nseg + seg] = segsum;
+  store_rows(c1 - 1);
+  // the final state after the last segment
+  float* hf = (seg == p.nseg - 1 && p.h_final) ? p.h_final + (size_t)slice * N * P + p0 : nullptr;
   if (hf) {
 #pragma unroll
     for (int k = 0; k < S::ST_PER_WAVE; ++k) {
@@ -652,12 +656,296 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
   }
 }
 
+// ------------------------------------------------------------------ segment local pass
+// The state at the end of a token range [ta, tb] from a zero start, with no outputs
+// (the segment chain's input):
+//   S = sum_{tau in [ta, tb]} Phi(tb, tau) W_tau,
+//   W_tau = gamma_tau B_tau X_tau + beta_tau B_{tau-1} X_{tau-1}   (plain write: B_tau X_tau),
+// where Phi(tb, tau) scales row n by e^{-A_n d_tau} and turns pair k by R(omega_k d_tau),
+// d_tau = sum_{r = tau+1 .. tb} Delta_r.  The two writes of X_tau (the gamma term at tau,
+// the beta term at tau + 1) fold into one key row per (token, rank):
+//   K_tau = [tau >= ta] gamma_tau Phi(tb, tau) B_tau + [tau < tb] beta_{tau+1} Phi(tb, tau+1) B_tau,
+// so S = sum_{tau = ta-1 .. tb} K_tau^T X_tau (token ta - 1 carries only its beta term):
+// one contraction over the range, with no sequential dependence.  Each wave takes
+// steps of 32 key rows on its own (wave-private LDS, no workgroup barrier inside the
+// loop; the next step's loads are in flight while a step is staged), and the four
+// waves' partial states are added in a fixed order at the end.
+template <bool BF16, int N, int PBL, int R, bool TE, bool COORD>
+struct LocalShape {
+  using T = typename Elem<BF16>::T;
+  static constexpr int VEC = Elem<BF16>::kVec;
+  static constexpr int PAD = 16 / static_cast<int>(sizeof(T));
+  static constexpr int QL = 32 / R;  // tokens per step (32 key rows)
+  static constexpr int KS = N + PAD, VS = PBL + PAD;
+  static constexpr int NV = N / VEC, PV = PBL / VEC;
+  static constexpr int TN = N / 16, TP = PBL / 16;
+  static constexpr int BI = QL * NV;      // key items per step: (token, n-vector), all ranks
+  static constexpr int XI = QL * R * PV;  // value vectors per step
+  static constexpr int BI_PER = (BI + 63) / 64, XI_PER = (XI + 63) / 64;
+  static constexpr int STAGE_BYTES = 4 * 32 * (KS + VS) * static_cast<int>(sizeof(T));
+  static constexpr int RED_BYTES = 3 * N * PBL * 4;  // partial states of waves 1..3
+  static constexpr int SMEM = STAGE_BYTES > RED_BYTES ? STAGE_BYTES : RED_BYTES;
+  static_assert(32 % R == 0 && N % 16 == 0 && PBL % 16 == 0, "unsupported local shape");
+};
+
+template <bool BF16, int N, int PBL, int R, bool TE, bool COORD>
+__global__ __launch_bounds__(256) void ssm_fwd_local(FwdParams p) {
+  using S = LocalShape<BF16, N, PBL, R, TE, COORD>;
+  using T = typename S::T;
+  constexpr int VEC = S::VEC, QL = S::QL, KS = S::KS, VS = S::VS, NV = S::NV, PV = S::PV;
+  constexpr int LM = kLocalMaxTokens;
+  constexpr float kLog2e = 1.4426950408889634f;
+  __shared__ __align__(16) unsigned char smem[S::SMEM];
+  __shared__ float sD[LM];                                   // Delta, then d_tau
+  __shared__ float sGa[TE ? LM : 1], sBe[TE ? LM : 1];
+  __shared__ float sBlk[LM / 64];
+  __shared__ float sRate[COORD ? N : 1], sOm[COORD ? N / 2 + 1 : 1];
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int nlp = p.P / PBL, nsegl = p.nseg - 1;
+  const int lid = xcd_logical_id(blockIdx.x, gridDim.x);
+  const int pblk = lid % nlp;
+  int rest = lid / nlp;
+  const int sub = rest % p.nsub;
+  rest /= p.nsub;
+  const int seg = rest % nsegl, slice = rest / nsegl;
+  const int b = slice / p.H, h = slice % p.H, g = h / (p.H / p.G);
+  const int L = p.L, H = p.H, G = p.G, P = p.P, p0 = pblk * PBL;
+  const int s0 = seg * p.seg_tokens;
+  const int ta = s0 + sub * p.lsub;
+  const int tb = min(min(ta + p.lsub, s0 + p.seg_tokens), L) - 1;
+  const int len = tb - ta + 1;  // >= 1 by construction of the ranges
+  const size_t unit = ((size_t)slice * nsegl + seg) * p.nsub + sub;
+
+  if (COORD) {
+    const int na = p.n_real + p.n_pairs, nreal = p.n_real;
+    for (int n = tid; n < N; n += 256) {
+      float r;
+      if (p.head_rates) r = p.A[h];
+      else if (n < nreal) r = p.A[(size_t)h * na + n];
+      else r = p.A[(size_t)h * na + nreal + ((n - nreal) >> 1)];
+      sRate[n] = r * kLog2e;
+    }
+    for (int k = tid; k < p.n_pairs; k += 256) sOm[k] = p.omega[(size_t)h * p.n_pairs + k];
+  }
+  const float* dtg = p.dt + (size_t)b * L * H + h;
+  for (int i = tid; i < len; i += 256) {
+    const float raw = dtg[(size_t)(ta + i) * H];
+    sD[i] = p.softplus ? softplus_f32(raw) : raw;
+    if (TE) {
+      sGa[i] = p.gamma[((size_t)b * L + ta + i) * H + h];
+      sBe[i] = p.beta[((size_t)b * L + ta + i) * H + h];
+    }
+  }
+  __syncthreads();
+  // d_i = sum of Delta over the tokens after i: exclusive suffix sums inside blocks
+  // of 64 tokens (lanes in reverse token order), then the later blocks' totals
+  const int nblk = (len + 63) / 64;
+  for (int blk = wave; blk < nblk; blk += 4) {
+    const int i = blk * 64 + 63 - lane;
+    const float v = i < len ? sD[i] : 0.f;
+    const float incl = wave_prefix_sum(v);
+    if (lane == 63) sBlk[blk] = incl;
+    if (i < len) sD[i] = incl - v;
+  }
+  __syncthreads();
+  for (int i = tid; i < len; i += 256) {
+    float after = 0.f;
+    for (int k = i / 64 + 1; k < nblk; ++k) after += sBlk[k];
+    sD[i] += after;
+  }
+  if (tid == 0 && pblk == 0) {
+    float tot = 0.f;
+    for (int k = 0; k < nblk; ++k) tot += sBlk[k];
+    p.seg_delta[unit] = tot;
+  }
+  __syncthreads();
+
+  const T* Bg = static_cast<const T*>(p.B) + ((size_t)b * L * G + g) * R * N;
+  const T* xg = static_cast<const T*>(p.x) + ((size_t)b * L * H + h) * R * P + p0;
+  const int tsG = G * R * N, tsH = H * R * P;
+  T* kw = reinterpret_cast<T*>(smem) + wave * 32 * KS;
+  T* vw = reinterpret_cast<T*>(smem) + 4 * 32 * KS + wave * 32 * VS;
+  const float ah = COORD ? 0.f : p.A[h] * kLog2e;
+  const int i_first = TE ? -1 : 0;  // relative token of the first key row
+  const int nsteps = (len - i_first + QL - 1) / QL;
+  // a loaded vector, or zero (selected per component: a whole-struct select can be
+  // lowered through scratch memory)
+  auto keep = [](bool ok, const uint4& v) {
+    return make_uint4(ok ? v.x : 0u, ok ? v.y : 0u, ok ? v.z : 0u, ok ? v.w : 0u);
+  };
+
+  f32x4 acc[S::TN][S::TP];
+#pragma unroll
+  for (int a = 0; a < S::TN; ++a)
+#pragma unroll
+    for (int c = 0; c < S::TP; ++c) acc[a][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // raw B vectors (all ranks of a (token, n-vector) item) and X vectors of one step;
+  // loads are branch-free (clamped token, zero for rows outside the range)
+  uint4 rb[S::BI_PER][R], rx[S::XI_PER];
+  auto load = [&](int k) {
+    const int i0 = i_first + k * QL;
+#pragma unroll
+    for (int q = 0; q < S::BI_PER; ++q) {
+      const int u = lane + 64 * q;
+      const int j = u / NV, v = u % NV;
+      const int t = ta + i0 + j;
+      const bool ok = u < S::BI && i0 + j < len && t >= 0;
+      const int tc = ok ? t : ta;
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const uint4 val = *reinterpret_cast<const uint4*>(Bg + (size_t)tc * tsG + r * N + v * VEC);
+        rb[q][r] = keep(ok, val);
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < S::XI_PER; ++q) {
+      const int u = lane + 64 * q;
+      const int jr = u / PV, pv = u % PV;
+      const int j = jr / R, r = jr % R;
+      const int t = ta + i0 + j;
+      const bool ok = u < S::XI && i0 + j < len && t >= 0;
+      const int tc = ok ? t : ta;
+      const uint4 val = *reinterpret_cast<const uint4*>(xg + (size_t)tc * tsH + r * P + pv * VEC);
+      rx[q] = keep(ok, val);
+    }
+  };
+
+  // key rows of one step into the wave's LDS: K_tau = coefficient (x) B_tau
+  auto stage = [&](int k) {
+    const int i0 = i_first + k * QL;
+#pragma unroll
+    for (int q = 0; q < S::BI_PER; ++q) {
+      const int u = lane + 64 * q;
+      if (u >= S::BI) break;
+      const int j = u / NV, v = u % NV, n0 = v * VEC;
+      const int i = i0 + j;
+      // the gamma term (write at token i) and the beta term (write at token i + 1)
+      const bool h0 = i >= 0 && i < len;
+      const bool h1 = TE && i + 1 < len;
+      const float d0 = h0 ? sD[i] : 0.f, d1 = h1 ? sD[i + 1] : 0.f;
+      const float g0 = h0 ? (TE ? sGa[i] : 1.f) : 0.f, g1 = h1 ? sBe[i + 1] : 0.f;
+      float cf[VEC], sf[VEC];  // per-row factor; pairs: (cos-part, sin-part) on the even row
+      if (!COORD) {
+        float c = g0 * __builtin_amdgcn_exp2f(-ah * d0);
+        if (TE) c += g1 * __builtin_amdgcn_exp2f(-ah * d1);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) { cf[e] = c; sf[e] = 0.f; }
+      } else {
+#pragma unroll
+        for (int e = 0; e < VEC; e += 2) {
+          const int n = n0 + e;
+          if (n >= p.n_real) {
+            const float a = sRate[n], om = sOm[(n - p.n_real) >> 1];
+            float s0v, c0v, s1v = 0.f, c1v = 0.f;
+            fast_sincos(om * d0, &s0v, &c0v);
+            const float w0 = g0 * __builtin_amdgcn_exp2f(-a * d0);
+            float cc = w0 * c0v, ss = w0 * s0v;
+            if (TE) {
+              fast_sincos(om * d1, &s1v, &c1v);
+              const float w1 = g1 * __builtin_amdgcn_exp2f(-a * d1);
+              cc += w1 * c1v;
+              ss += w1 * s1v;
+            }
+            cf[e] = cc; sf[e] = ss; cf[e + 1] = cc; sf[e + 1] = ss;
+          } else {
+#pragma unroll
+            for (int f = 0; f < 2; ++f) {
+              const float a = sRate[n + f];
+              float c = g0 * __builtin_amdgcn_exp2f(-a * d0);
+              if (TE) c += g1 * __builtin_amdgcn_exp2f(-a * d1);
+              cf[e + f] = c; sf[e + f] = 0.f;
+            }
+          }
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        float bv[VEC], kv[VEC];
+        unpack<BF16>(rb[q][r], bv);
+#pragma unroll
+        for (int e = 0; e < VEC; e += 2) {
+          // [[c, -s], [s, c]] on a pair (s = 0 on real rows)
+          kv[e] = cf[e] * bv[e] - sf[e] * bv[e + 1];
+          kv[e + 1] = sf[e] * bv[e] + cf[e + 1] * bv[e + 1];
+        }
+        *reinterpret_cast<uint4*>(kw + (j * R + r) * KS + n0) = pack<BF16>(kv);
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < S::XI_PER; ++q) {
+      const int u = lane + 64 * q;
+      if (u >= S::XI) break;
+      const int jr = u / PV, pv = u % PV;
+      *reinterpret_cast<uint4*>(vw + jr * VS + pv * VEC) = rx[q];
+    }
+  };
+
+  int k = wave;
+  if (k < nsteps) load(k);
+  for (; k < nsteps; k += 4) {
+    stage(k);
+    if (k + 4 < nsteps) load(k + 4);
+    // the wave's own LDS writes before its transposed reads
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+#pragma unroll
+    for (int tn = 0; tn < S::TN; ++tn) {
+      const auto fk = load_frag_tr<BF16>(kw + 16 * tn, KS);
+#pragma unroll
+      for (int tp = 0; tp < S::TP; ++tp) {
+        const auto fv = load_frag_tr<BF16>(vw + 16 * tp, VS);
+        mma<BF16>(acc[tn][tp], fv, fk);
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+  }
+
+  // partial states of waves 1..3 through LDS, added to wave 0's in order;
+  // acc[tn][tp][i] = S[n = 16 tn + (lane & 15)][p = 16 tp + 4 (lane >> 4) + i]
+  __syncthreads();
+  float* red = reinterpret_cast<float*>(smem);
+  if (wave > 0) {
+#pragma unroll
+    for (int tn = 0; tn < S::TN; ++tn)
+#pragma unroll
+      for (int tp = 0; tp < S::TP; ++tp) {
+        const int n = 16 * tn + (lane & 15), pl = 16 * tp + 4 * (lane >> 4);
+        *reinterpret_cast<float4*>(red + ((wave - 1) * N + n) * PBL + pl) =
+            make_float4(acc[tn][tp][0], acc[tn][tp][1], acc[tn][tp][2], acc[tn][tp][3]);
+      }
+  }
+  __syncthreads();
+  if (wave == 0) {
+    float* dst = p.seg_local + unit * N * P + p0;
+#pragma unroll
+    for (int tn = 0; tn < S::TN; ++tn)
+#pragma unroll
+      for (int tp = 0; tp < S::TP; ++tp) {
+        const int n = 16 * tn + (lane & 15), pl = 16 * tp + 4 * (lane >> 4);
+        float4 s = make_float4(acc[tn][tp][0], acc[tn][tp][1], acc[tn][tp][2], acc[tn][tp][3]);
+#pragma unroll
+        for (int w = 0; w < 3; ++w) {
+          const float4 o = *reinterpret_cast<const float4*>(red + (w * N + n) * PBL + pl);
+          s.x += o.x; s.y += o.y; s.z += o.z; s.w += o.w;
+        }
+        *reinterpret_cast<float4*>(dst + (size_t)n * P + pl) = s;
+      }
+  }
+}
+
 // ------------------------------------------------------------------ segment combine
-// States entering the segments of each slice, in order:
-//   S_in[0] = h0 (or 0),   S_in[s+1] = rho_s R(theta_s) S_in[s] + S_local[s],
-// with rho_s = e^{-A_n D_s} per row, theta_s = omega_k D_s per pair and D_s the
-// segment's summed step (the chunk-by-chunk decays and rotations of a segment
-// compose to exactly these).  One thread per (slice, row pair, value column).
+// States entering the segments of each slice, in order: starting from h0 (or 0), the
+// local-pass ranges of every segment are chained in token order,
+//   S <- rho_u R(theta_u) S + S_local[u],
+// with rho_u = e^{-A_n D_u} per row, theta_u = omega_k D_u per pair and D_u the range's
+// summed step (the token-by-token decays and rotations of a range compose to exactly
+// these); after the last range of segment s, S is the state entering segment s + 1.
+// One thread per (slice, row pair, value column).
 __global__ __launch_bounds__(256) void ssm_fwd_combine(FwdParams p, int per_row) {
   const int N = p.n_real + 2 * p.n_pairs, P = p.P, nreal = p.n_real, na = p.n_real + p.n_pairs;
   const long total = (long)p.batch * p.H * (N / 2) * P;
@@ -674,25 +962,28 @@ __global__ __launch_bounds__(256) void ssm_fwd_combine(FwdParams p, int per_row)
     const float ra = rate(n), rb = rate(n + 1);
     const bool pair = per_row && n >= nreal;
     const float om = pair ? p.omega[(size_t)h * p.n_pairs + ((n - nreal) >> 1)] : 0.f;
-    const size_t sb = (size_t)slice * p.nseg;
+    const size_t sb = (size_t)slice * p.nseg, sl = (size_t)slice * (p.nseg - 1) * p.nsub;
     float a = 0.f, bv = 0.f;
     if (p.h0) {
       a = p.h0[((size_t)slice * N + n) * P + pp];
       bv = p.h0[((size_t)slice * N + n + 1) * P + pp];
     }
     for (int s = 0; s + 1 < p.nseg; ++s) {
-      const float dsum = p.seg_delta[sb + s];
-      float a2 = a * expf(-ra * dsum), b2 = bv * expf(-rb * dsum);
-      if (pair) {
-        float sn, cs;
-        sincosf(om * dsum, &sn, &cs);
-        const float x0 = a2, x1 = b2;
-        a2 = cs * x0 - sn * x1;
-        b2 = sn * x0 + cs * x1;
+      for (int u = 0; u < p.nsub; ++u) {
+        const size_t unit = sl + (size_t)s * p.nsub + u;
+        const float dsum = p.seg_delta[unit];
+        float a2 = a * expf(-ra * dsum), b2 = bv * expf(-rb * dsum);
+        if (pair) {
+          float sn, cs;
+          sincosf(om * dsum, &sn, &cs);
+          const float x0 = a2, x1 = b2;
+          a2 = cs * x0 - sn * x1;
+          b2 = sn * x0 + cs * x1;
+        }
+        const float* loc = p.seg_local + (unit * N + n) * P + pp;
+        a = a2 + loc[0];
+        bv = b2 + loc[P];
       }
-      const float* loc = p.seg_local + ((sb + s) * N + n) * P + pp;
-      a = a2 + loc[0];
-      bv = b2 + loc[P];
       float* out = p.seg_in + ((sb + s + 1) * N + n) * P + pp;
       out[0] = a;
       out[P] = bv;
@@ -772,18 +1063,19 @@ hipError_t launch_fwd(const FwdKey& k, const FwdParams& p, hipStream_t stream,
       k.coord == CO && k.nthreads == NT) {                                                   \
     mark(0);                                                                                 \
     if (p.nseg > 1) {                                                                        \
-      FwdParams lp = p;                                                                      \
-      lp.state_only = 1;                                                                     \
-      hipLaunchKernelGGL((ssm_fwd_kernel<BF, NN, PBB, RR, KRR, QTT, CO, NT>), dim3(nwg),      \
-                         dim3(NT), 0, stream, lp);                                           \
+      const int lgrid = p.batch * p.H * (p.nseg - 1) * p.nsub;                               \
+      if (p.P % 32 == 0)                                                                     \
+        hipLaunchKernelGGL((ssm_fwd_local<BF, NN, 32, RR, (KRR > RR), CO>),                  \
+                           dim3(lgrid * (p.P / 32)), dim3(256), 0, stream, p);               \
+      else                                                                                   \
+        hipLaunchKernelGGL((ssm_fwd_local<BF, NN, 16, RR, (KRR > RR), CO>),                  \
+                           dim3(lgrid * (p.P / 16)), dim3(256), 0, stream, p);               \
       const long total = (long)p.batch * p.H * (NN / 2) * p.P;                               \
       const int cb = (int)std::min<long>((total + 255) / 256, 2048);                         \
       hipLaunchKernelGGL(ssm_fwd_combine, dim3(cb), dim3(256), 0, stream, p, CO ? 1 : 0);    \
     }                                                                                        \
-    FwdParams fp = p;                                                                        \
-    fp.state_only = 0;                                                                       \
     hipLaunchKernelGGL((ssm_fwd_kernel<BF, NN, PBB, RR, KRR, QTT, CO, NT>), dim3(nwg),        \
-                       dim3(NT), 0, stream, fp);                                             \
+                       dim3(NT), 0, stream, p);                                              \
     mark(1);                                                                                 \
     return hipGetLastError();                                                                \
   }

@@ -25,11 +25,16 @@ struct FwdParams {
   int head_rates;  // A holds one rate per head even though the per-row kernel runs
   // sequence segments (nseg = 1: one workgroup walks the whole sequence)
   int nseg, cps;     // segments per slice, chunks per segment
-  int state_only;    // local pass: each segment's final state from a zero start, no outputs
-  float* seg_local;  // [slice][nseg][N][P] local final states (local pass output)
+  // local pass: every segment but the last is cut into nsub ranges of lsub tokens
+  // (the last range may be shorter); each range's final state from a zero start
+  int seg_tokens, nsub, lsub;
+  float* seg_local;  // [slice][nseg - 1][nsub][N][P] range final states (local pass output)
   float* seg_in;     // [slice][nseg][N][P] states entering the segments (combine output)
-  float* seg_delta;  // [slice][nseg] sum of Delta over each segment (local pass output)
+  float* seg_delta;  // [slice][nseg - 1][nsub] sum of Delta over each range (local pass output)
 };
+
+// tokens of one local-pass range (bounds the kernel's per-token LDS tables)
+constexpr int kLocalMaxTokens = 512;
 
 struct BwdParams {
   const void* x;
