@@ -110,24 +110,24 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
 
   // double-buffered chunk operands: chunk c is consumed while chunk c+1 is staged
   __shared__ __align__(16) T sQ[2 * QSZ];                     // queries (folded; per-row: scaled)
-  __shared__ __align__(16) T sQe[COORD ? 2 * QSZ : 8];        // per-row: queries scaled by e^{L_t}
-  __shared__ __align__(16) T sK[2 * KSZ];                     // keys
-  __shared__ __align__(16) T sKe[COORD ? 2 * KSZ : 8];        // per-row: keys scaled to the chunk end
+  __shared__ __align__(16) T sK[2 * KSZ];                     // keys (per-row: scaled)
   __shared__ __align__(16) T sV[2 * VSZ];                     // values, natural [key row][p]
   __shared__ __align__(16) T sVw[COORD ? 8 : 2 * VSZ];        // head: values scaled to the chunk end
   __shared__ __align__(16) T sS[S::QO * KS];                  // masked scores [query row][key]
-  __shared__ __align__(16) T sST[2 * S::NC * VS];             // state entering chunk c in buffer c & 1 [n][p]
-  // per-token factors of a chunk (double-buffered, written by wave PW one chunk ahead)
+  // state entering chunk c (buffer (c - c0) & 1, [n][p]), the readout operand; with
+  // per-row decay row n is stored scaled by e^{-A_n CD_end / 2} of that chunk
+  __shared__ __align__(16) T sST[2 * S::NC * VS];
+  // per-token factors of chunk c in slot c & 3 (written by wave PW two chunks ahead)
   constexpr int TC = COORD ? 64 : 1, TH = COORD ? 1 : 64;
-  __shared__ __align__(16) float sCD[2][TC];   // per-row decay: cumulative step inside the chunk
-  __shared__ __align__(16) float sLC[2][TH];   // head: -A CD log2(e), so e^{L_t - L_s} = 2^{LC_t - LC_s}
-  __shared__ __align__(16) float sDT[2][64];   // steps Delta (staged one chunk ahead)
-  __shared__ __align__(16) float sGa[2][S::TE ? 64 : 1], sBe[2][S::TE ? 64 : 1];
-  __shared__ float sMisc[2][2];                // CD_end, head: e^{-A CD_end}
+  __shared__ __align__(16) float sCD[4][TC];   // per-row decay: cumulative step inside the chunk
+  __shared__ __align__(16) float sLC[4][TH];   // head: -A CD log2(e), so e^{L_t - L_s} = 2^{LC_t - LC_s}
+  __shared__ __align__(16) float sDT[2][64];   // steps Delta of chunk c in slot c & 1
+  __shared__ __align__(16) float sGa[2][S::TE ? 64 : 1], sBe[2][S::TE ? 64 : 1];  // chunk c: c & 1
+  __shared__ float sMisc[4][2];                // CD_end, head: e^{-A CD_end}
   __shared__ float sRate[COORD ? N : 1], sOmega[COORD ? N / 2 + 1 : 1];
-  // per-row decay: the staged chunk's factor tables (see stage)
-  __shared__ __align__(16) float sE[COORD ? QT * N : 4], sEi[COORD ? QT * N : 4], sHh[COORD ? N : 4];
-  __shared__ __align__(16) float2 sRot[COORD ? QT * (N / 2) : 2];
+  // per-row decay: factor tables of the next chunk to stage, [token][n] (see tables)
+  __shared__ __align__(16) float sTC[COORD ? QT * N : 4], sTK0[COORD ? QT * N : 4];
+  __shared__ __align__(16) float sTK1[COORD && S::TE ? QT * N : 4];
   __shared__ __align__(16) T sYo[S::QO * VS];                 // output rows of the previous chunk
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -157,21 +157,15 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
   // the combined state entering a later segment, or zero
   const float* h0s = seg == 0 ? (p.h0 ? p.h0 + (size_t)slice * N * P + p0 : nullptr)
                               : p.seg_in + ((size_t)slice * p.nseg + seg) * N * P + p0;
-  for (int i = tid; i < 2 * S::NC * VS; i += S::NTH) {
-    const int n = i / VS, col = i % VS;
-    sST[i] = (h0s && n < N && col < PB) ? from_f32<T>(h0s[n * P + col]) : T(0);
-  }
   for (int i = tid; i < S::QO * KS; i += S::NTH) sS[i] = T(0);
   if (S::NC > N) {
     for (int i = tid; i < 2 * S::QO * (S::NC - N); i += S::NTH) {
       const int r = i / (S::NC - N), c = N + i % (S::NC - N);
       sQ[r * NS + c] = T(0);
-      if (COORD) sQe[r * NS + c] = T(0);
     }
     for (int i = tid; i < 2 * S::QK * (S::NC - N); i += S::NTH) {
       const int r = i / (S::NC - N), c = N + i % (S::NC - N);
       sK[r * NS + c] = T(0);
-      if (COORD) sKe[r * NS + c] = T(0);
     }
   }
   const float Ah = COORD ? 0.f : p.A[h];
@@ -236,23 +230,23 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
       rr[k] = val;
     }
     if (wave == PW) {
-      // per-token scalars of the NEXT chunk: the staging of chunk c writes them to
-      // LDS, so the factor wave never waits on global memory
-      const int t = t0 + QT + lane;
-      const bool ok = lane < QT && t < L;
-      rdt = ok ? dtg[t * H] : 0.f;
+      // per-token scalars ahead of the operands (Delta of chunk c+2, beta / gamma of
+      // chunk c+1): the staging of chunk c writes them to LDS, so the factor wave
+      // never waits on global memory
+      const int t2 = t0 + 2 * QT + lane, t1 = t0 + QT + lane;
+      rdt = (lane < QT && t2 < L) ? dtg[t2 * H] : 0.f;
       if (S::TE) {
-        rbe = ok ? beg[t * H] : 0.f;
-        rga = ok ? gag[t * H] : 0.f;
+        const bool ok = lane < QT && t1 < L;
+        rbe = ok ? beg[t1 * H] : 0.f;
+        rga = ok ? gag[t1 * H] : 0.f;
       }
     }
   };
 
-  // ---- a1: per-token factors of chunk c into buffer bi (wave PW only; lane = token)
-  auto factors = [&](int c, int bi) {
-    const int t0 = c * QT;
-    float dl = 0.f;
-    if (lane < QT && t0 + lane < L) dl = sDT[bi][lane];
+  // ---- a1: per-token factors of chunk c into slot c & 3 (wave PW only; lane = token,
+  // dl = its step, 0 past the sequence end)
+  auto factors = [&](int c, float dl) {
+    const int bi = c & 3;
     const float cd = wave_prefix_sum(dl);
     const float cdend = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cd), QT - 1));
     if (lane < QT) {
@@ -267,59 +261,79 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
     }
   };
 
-  // fold the rotation by -Theta_t (table row t) into consecutive (even, odd) pair
-  // rows of a vector
-  auto unrotate = [&](float* v, int n0, int t) {
+  // Per-row decay: factor tables of chunk c (all threads, one entry pair per thread),
+  // with E_t[n] = e^{-A_n (CD_t - CD_end/2)} and Theta_t[k] = omega_k CD_t:
+  //   TC[t]  = E_t on real rows; (E_t cos, E_t sin)(Theta_t) on the rows of pair k,
+  //   TK0[t] = g_t / E_t, likewise with the pair rotation (g = gamma with two-endpoint
+  //            writes, else 1),   TK1[t] = beta_t / E_t, likewise.
+  // A staged element is then one multiply (real rows) or one 2 x 2 product (pairs):
+  //   q = R(-Theta_t) C_t E_t,  k = R(-Theta_s) (g B) / E_s.
+  auto tables = [&](int c) {
+    const int sc = c & 3, sg = c & 1;
+    const float hc = 0.5f * sMisc[sc][0];
+    for (int i = tid; i < QT * (N / 2); i += S::NTH) {
+      const int t = i / (N / 2), n = 2 * (i % (N / 2));
+      const float cd = sCD[sc][t] - hc;
+      const float g0 = S::TE ? sGa[sg][t] : 1.f, g1 = S::TE ? sBe[sg][t] : 0.f;
+      float2 tc, tk0, tk1;
+      if (n >= nreal) {
+        const float x = sRate[n] * cd;
+        const float e = __expf(-x), ei = __expf(x);
+        float sn, cs;
+        fast_sincos(sOmega[(n - nreal) >> 1] * sCD[sc][t], &sn, &cs);
+        tc = make_float2(e * cs, e * sn);
+        tk0 = make_float2(g0 * ei * cs, g0 * ei * sn);
+        tk1 = make_float2(g1 * ei * cs, g1 * ei * sn);
+      } else {
+        const float x0 = sRate[n] * cd, x1 = sRate[n + 1] * cd;
+        const float ei0 = __expf(x0), ei1 = __expf(x1);
+        tc = make_float2(__expf(-x0), __expf(-x1));
+        tk0 = make_float2(g0 * ei0, g0 * ei1);
+        tk1 = make_float2(g1 * ei0, g1 * ei1);
+      }
+      *reinterpret_cast<float2*>(sTC + t * N + n) = tc;
+      *reinterpret_cast<float2*>(sTK0 + t * N + n) = tk0;
+      if (S::TE) *reinterpret_cast<float2*>(sTK1 + t * N + n) = tk1;
+    }
+  };
+
+  // one staged vector times its table row: per-row factors, or (cos, sin)-style 2 x 2
+  // products on pair rows, q = (a u0 + b u1, -b u0 + a u1)
+  auto apply_table = [&](float* v, const float* tab, int n0) {
+    float f[VEC];
+#pragma unroll
+    for (int i = 0; i < VEC; i += 4) {
+      const float4 w = *reinterpret_cast<const float4*>(tab + n0 + i);
+      f[i] = w.x; f[i + 1] = w.y; f[i + 2] = w.z; f[i + 3] = w.w;
+    }
 #pragma unroll
     for (int i = 0; i < VEC; i += 2) {
-      const int n = n0 + i;
-      if (n >= nreal) {
-        const float2 r = sRot[t * (N / 2) + ((n - nreal) >> 1)];  // (cos, sin)
-        const float a = v[i], bb = v[i + 1];
-        v[i] = r.x * a + r.y * bb;
-        v[i + 1] = -r.y * a + r.x * bb;
+      const float a = v[i], bb = v[i + 1];
+      if (n0 + i >= nreal) {
+        v[i] = f[i] * a + f[i + 1] * bb;
+        v[i + 1] = -f[i + 1] * a + f[i] * bb;
+      } else {
+        v[i] = f[i] * a;
+        v[i + 1] = f[i + 1] * bb;
       }
     }
   };
 
-  // ---- a2: the operands of chunk c (held in registers) into buffer bi, using the
-  // chunk's per-token factors.  Per-row decay: first the chunk's factor tables
-  //   E[t][n] = e^{-A_n (CD_t - CD_end/2)},  Einv = 1 / E,  Hh[n] = e^{-A_n CD_end/2},
-  //   Rot[t][k] = (cos, sin)(omega_k CD_t),
-  // computed by all threads (one exponential per entry), then per element
-  //   q = C~ E,  qe = q Hh = C~ e^{L_t},  k = K~ Einv,  ke = k Hh = K~ e^{L_end - L_s}.
+  // ---- a2: the operands of chunk c (held in registers) into operand buffer bi, using
+  // the chunk's per-token factors (head decay) or its factor tables (per-row decay).
+  // Wave PW also stores the per-token scalars loaded with the operands (Delta of chunk
+  // c+2, beta / gamma of chunk c+1).
   auto stage = [&](int c, int bi) {
-    (void)c;
     if (wave == PW && lane < 64) {
-      // per-token scalars of chunk c+1 (loaded with chunk c's operands)
-      sDT[bi ^ 1][lane] = p.softplus ? softplus_f32(rdt) : rdt;
+      sDT[c & 1][lane] = p.softplus ? softplus_f32(rdt) : rdt;
       if (S::TE) {
-        sGa[bi ^ 1][lane] = rga;
-        sBe[bi ^ 1][lane] = rbe;
+        sGa[(c + 1) & 1][lane] = rga;
+        sBe[(c + 1) & 1][lane] = rbe;
       }
     }
-    if constexpr (COORD) {
-      const float hc = 0.5f * sMisc[bi][0];
-      for (int i = tid; i < QT * N; i += S::NTH) {
-        const int t = i / N, n = i % N;
-        const float x = sRate[n] * (sCD[bi][t] - hc);
-        sE[i] = __expf(-x);
-        sEi[i] = __expf(x);
-      }
-      for (int n = tid; n < N; n += S::NTH) sHh[n] = __expf(-sRate[n] * hc);
-      const int np = p.n_pairs;
-      for (int i = tid; i < QT * np; i += S::NTH) {
-        const int t = i / np, k = i % np;
-        float sn, cs;
-        fast_sincos(sOmega[k] * sCD[bi][t], &sn, &cs);
-        sRot[t * (N / 2) + k] = make_float2(cs, sn);
-      }
-      __syncthreads();
-    }
+    const int sc = c & 3;
     T* q = sQ + bi * QSZ;
-    T* qe = sQe + (COORD ? bi * QSZ : 0);
     T* kb = sK + bi * KSZ;
-    T* keb = sKe + (COORD ? bi * KSZ : 0);
     T* vb = sV + bi * VSZ;
     T* vwb = sVw + (COORD ? 0 : bi * VSZ);
 #pragma unroll
@@ -330,16 +344,10 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
         const int n0 = nv * VEC;
         if (COORD) {
           const int t = row / R;
-          float vals[VEC], qq[VEC], qqe[VEC];
+          float vals[VEC];
           unpack<BF16>(rr[k], vals);
-          unrotate(vals, n0, t);
-#pragma unroll
-          for (int i = 0; i < VEC; ++i) {
-            qq[i] = vals[i] * sE[t * N + n0 + i];
-            qqe[i] = qq[i] * sHh[n0 + i];
-          }
-          *reinterpret_cast<uint4*>(q + row * NS + n0) = pack<BF16>(qq);
-          *reinterpret_cast<uint4*>(qe + row * NS + n0) = pack<BF16>(qqe);
+          apply_table(vals, sTC + t * N, n0);
+          *reinterpret_cast<uint4*>(q + row * NS + n0) = pack<BF16>(vals);
         } else {
           *reinterpret_cast<uint4*>(q + row * NS + n0) = rr[k];
         }
@@ -357,24 +365,10 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
         const int tau = sl + e;
         if (tau < 0 || tau >= QT) continue;
         const int j = tau * KR + (e ? R : 0) + r;
-        const float gb = S::TE ? (e ? sBe[bi][tau] : sGa[bi][tau]) : 1.f;
-        float uu[VEC], kk[VEC], ke[VEC];
+        float uu[VEC];
         unpack<BF16>(rr[k], uu);
-#pragma unroll
-        for (int i = 0; i < VEC; ++i) uu[i] *= gb;
-        if (COORD) {
-          unrotate(uu, n0, tau);
-#pragma unroll
-          for (int i = 0; i < VEC; ++i) {
-            kk[i] = uu[i] * sEi[tau * N + n0 + i];
-            ke[i] = kk[i] * sHh[n0 + i];
-          }
-          *reinterpret_cast<uint4*>(keb + j * NS + n0) = pack<BF16>(ke);
-        } else {
-#pragma unroll
-          for (int i = 0; i < VEC; ++i) kk[i] = uu[i];
-        }
-        *reinterpret_cast<uint4*>(kb + j * NS + n0) = pack<BF16>(kk);
+        apply_table(uu, (S::TE && e ? sTK1 : sTK0) + tau * N, n0);
+        *reinterpret_cast<uint4*>(kb + j * NS + n0) = pack<BF16>(uu);
       } else if (u >= S::X0 && u < S::ALL_VECS) {
         const int v = u - S::X0;
         const int row = v / S::NVEC_P, pv = v % S::NVEC_P;
@@ -387,7 +381,7 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
           const int j = tau * KR + (e ? R : 0) + r;
           *reinterpret_cast<uint4*>(vb + j * VS + pv * VEC) = rr[k];
           if (!COORD) {
-            const float w = __builtin_amdgcn_exp2f(sLC[bi][QT - 1] - sLC[bi][tau]);  // e^{L_end - L_s}
+            const float w = __builtin_amdgcn_exp2f(sLC[sc][QT - 1] - sLC[sc][tau]);  // e^{L_end - L_s}
             float xv[VEC];
             unpack<BF16>(rr[k], xv);
 #pragma unroll
@@ -423,19 +417,33 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
     }
   }
 
+  // prologue: the factors of the first two chunks, beta / gamma of the first, the
+  // readout copy of the incoming state, then the first chunk's staging
   if (wave == PW) {
-    const int t = c0 * QT + lane;
-    const bool ok = lane < QT && t < L;
-    const float raw = ok ? dtg[t * H] : 0.f;
-    sDT[0][lane] = p.softplus ? softplus_f32(raw) : raw;
-    if (S::TE) {
-      sBe[0][lane] = ok ? beg[t * H] : 0.f;
-      sGa[0][lane] = ok ? gag[t * H] : 0.f;
+#pragma unroll
+    for (int a = 0; a < 2; ++a) {
+      const int t = (c0 + a) * QT + lane;
+      const bool ok = lane < QT && t < L;
+      const float raw = ok ? dtg[t * H] : 0.f;
+      if (c0 + a < c1) factors(c0 + a, ok ? (p.softplus ? softplus_f32(raw) : raw) : 0.f);
+      if (S::TE && a == 0) {
+        sBe[c0 & 1][lane] = ok ? beg[t * H] : 0.f;
+        sGa[c0 & 1][lane] = ok ? gag[t * H] : 0.f;
+      }
     }
   }
   load_chunk(c0);
   __syncthreads();
-  if (wave == PW) factors(c0, 0);
+  {
+    const float hc0 = 0.5f * sMisc[c0 & 3][0];
+    for (int i = tid; i < 2 * S::NC * VS; i += S::NTH) {
+      const int n = i / VS, col = i % VS;
+      float v = (h0s && n < N && col < PB) ? h0s[n * P + col] : 0.f;
+      if (COORD && n < N) v *= __expf(-sRate[n] * hc0);
+      sST[i] = from_f32<T>(v);
+    }
+  }
+  if (COORD) tables(c0);
   __syncthreads();
   stage(c0, 0);
   if (c0 + 1 < c1) load_chunk(c0 + 1);
@@ -444,17 +452,16 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
   for (int c = c0; c < c1; ++c) {
     const int bi = (c - c0) & 1;
     if (c > c0) store_rows(c - 1);  // drains while the scores compute
+    const int sc = c & 3;
     const T* q = sQ + bi * QSZ;
-    const T* qe = sQe + (COORD ? bi * QSZ : 0);
     const T* kb = sK + bi * KSZ;
-    const T* keb = sKe + (COORD ? bi * KSZ : 0);
     const T* vb = sV + bi * VSZ;
     const T* vwb = sVw + (COORD ? 0 : bi * VSZ);
 
     // ---- phase 1 -- a3: masked intra-chunk scores of chunk c (computed transposed:
     // lane l holds query row 16 ti + (l & 15) against keys 16 tj + 4 (l >> 4) + i),
-    // the a4/a5 state update of chunk c; wave PW also forms the per-token factors
-    // of chunk c+1
+    // the a4/a5 state update of chunk c, the factor tables of chunk c+1; wave PW also
+    // forms the per-token factors of chunk c+2
     for (int tile = wave; tile < S::SC_TILES; tile += NW) {
       int ti = 0, tj = tile;
 #pragma unroll
@@ -479,31 +486,37 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) val[i] = ((j0 + i) / KR <= t) ? acc[i] : 0.f;
       } else {
-        const float lt = sLC[bi][t];
+        const float lt = sLC[sc][t];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int s = (j0 + i) / KR;
-          val[i] = (s <= t) ? acc[i] * __builtin_amdgcn_exp2f(lt - sLC[bi][s]) : 0.f;
+          val[i] = (s <= t) ? acc[i] * __builtin_amdgcn_exp2f(lt - sLC[sc][s]) : 0.f;
         }
       }
       store4<BF16>(sS + row * KS + j0, val);
     }
     // a4/a5: state update of chunk c (needs only this chunk's keys / values and the
-    // state entering it); its bf16 copy is the readout operand of chunk c+1
+    // state entering it); its bf16 copy is the readout operand of chunk c+1.
+    // Head decay: S <- e^{-A CD_end} S + K^T (V scaled to the chunk end).  Per-row decay,
+    // with the keys k = K~ e^{L_end/2 - L_s} folded around the chunk midpoint and
+    // hh = e^{-A_n CD_end/2}:  S <- hh o (hh o S + k^T V)  (= e^{L_end} S + sum_s
+    // e^{L_end - L_s} K~_s V_s), then the chunk-total rotation of the pairs.
     {
       // state tiles of this wave: wave * ST_PER_WAVE + k, so a wave's tiles share
       // their n-block whenever TP is a multiple of ST_PER_WAVE (one key fragment
       // then serves all of them)
-      const float cdend = sMisc[bi][0];
+      const float cdend = sMisc[sc][0];
+      const float cdnext = c + 1 < c1 ? sMisc[(c + 1) & 3][0] : 0.f;
       constexpr bool SHARE = S::TP % S::ST_PER_WAVE == 0;
       f32x4 acc[S::ST_PER_WAVE];
+      float hh[S::ST_PER_WAVE];
 #pragma unroll
       for (int k = 0; k < S::ST_PER_WAVE; ++k) {
         const int tile = wave * S::ST_PER_WAVE + k;
         const int n = 16 * (tile / S::TP) + (lane & 15);
-        const float dec = COORD ? __expf(-sRate[n < N ? n : 0] * cdend) : sMisc[bi][1];
+        hh[k] = COORD ? __expf(-0.5f * sRate[n < N ? n : 0] * cdend) : sMisc[sc][1];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc[k][i] = st[k][i] * dec;
+        for (int i = 0; i < 4; ++i) acc[k][i] = st[k][i] * hh[k];
       }
 #pragma unroll
       for (int kk = 0; kk < S::QK / 32; ++kk) {
@@ -511,14 +524,14 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
         if (SHARE) {
           const int tn = (wave * S::ST_PER_WAVE) / S::TP;
           if (wave * S::ST_PER_WAVE < S::ST_TILES)
-            fk = load_frag_tr<BF16>((COORD ? keb : kb) + (kk * 32) * NS + 16 * tn, NS);
+            fk = load_frag_tr<BF16>(kb + (kk * 32) * NS + 16 * tn, NS);
         }
 #pragma unroll
         for (int k = 0; k < S::ST_PER_WAVE; ++k) {
           const int tile = wave * S::ST_PER_WAVE + k;
           if (tile < S::ST_TILES) {
             const int tn = tile / S::TP, tp = tile % S::TP;
-            if (!SHARE) fk = load_frag_tr<BF16>((COORD ? keb : kb) + (kk * 32) * NS + 16 * tn, NS);
+            if (!SHARE) fk = load_frag_tr<BF16>(kb + (kk * 32) * NS + 16 * tn, NS);
             const auto fv = load_frag_tr<BF16>((COORD ? vb : vwb) + (kk * 32) * VS + 16 * tp, VS);
             mma<BF16>(acc[k], fv, fk);
           }
@@ -530,7 +543,11 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
         if (tile < S::ST_TILES) {
           const int tn = tile / S::TP, tp = tile % S::TP;
           const int n = 16 * tn + (lane & 15);
+          float sst = 1.f;  // scale of the readout copy
           if (COORD) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[k][i] *= hh[k];
+            sst = __expf(-0.5f * sRate[n] * cdnext);
             // chunk-total rotation of the pairs: rows (n, n+1) sit in lanes (l, l^1)
             const bool pair = n >= nreal;
             float sn = 0.f, cs = 1.f;
@@ -546,12 +563,14 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
           // the new state is the readout operand of chunk c+1 (other buffer)
           const int pl = 16 * tp + 4 * (lane >> 4);
           const float v4[4] = {acc[k][0], acc[k][1], acc[k][2], acc[k][3]};
-          store4<BF16>(sST + (bi ^ 1) * S::NC * VS + n * VS + pl, v4);
+          const float r4[4] = {sst * acc[k][0], sst * acc[k][1], sst * acc[k][2], sst * acc[k][3]};
+          store4<BF16>(sST + (bi ^ 1) * S::NC * VS + n * VS + pl, COORD ? r4 : v4);
           if (saved) store4<BF16>(saved + ((sl_saved + c + 1) * N + n) * P + p0 + pl, v4);
         }
       }
     }
-    if (wave == PW && c + 1 < c1) factors(c + 1, bi ^ 1);
+    if (COORD && c + 1 < c1) tables(c + 1);
+    if (wave == PW && c + 2 < c1) factors(c + 2, (lane < QT && (c + 2) * QT + lane < L) ? sDT[c & 1][lane] : 0.f);
     __syncthreads();
 
     // ---- phase 2 -- a2 staging of chunk c+1 (other buffer) and the loads of chunk
@@ -577,7 +596,6 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
         for (int a = 0; a < BQ; ++a)
 #pragma unroll
           for (int bb = 0; bb < BP; ++bb) acc[a][bb] = f32x4{0.f, 0.f, 0.f, 0.f};
-        const T* qsrc = COORD ? qe : q;
 #pragma unroll
         for (int kk = 0; kk < S::NC / 32; ++kk) {
           Frag<BF16> fs[BP], fq[BQ];
@@ -586,7 +604,7 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
             fs[bb] = load_frag_tr<BF16>(sST + bi * S::NC * VS + (kk * 32) * VS + 16 * (tp0 + bb), VS);
 #pragma unroll
           for (int a = 0; a < BQ; ++a)
-            fq[a] = load_frag<BF16>(qsrc + (16 * (ti0 + a) + (lane & 15)) * NS + kk * 32 + 8 * (lane >> 4));
+            fq[a] = load_frag<BF16>(q + (16 * (ti0 + a) + (lane & 15)) * NS + kk * 32 + 8 * (lane >> 4));
 #pragma unroll
           for (int a = 0; a < BQ; ++a)
 #pragma unroll
@@ -596,7 +614,7 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
 #pragma unroll
           for (int a = 0; a < BQ; ++a) {
             const int t = (16 * (ti0 + a) + (lane & 15)) / R;
-            const float el = __builtin_amdgcn_exp2f(sLC[bi][t]);  // e^{L_t}
+            const float el = __builtin_amdgcn_exp2f(sLC[sc][t]);  // e^{L_t}
 #pragma unroll
             for (int bb = 0; bb < BP; ++bb)
 #pragma unroll
