@@ -60,7 +60,7 @@ struct FwdShape {
   static constexpr int X_VECS = BROWS * NVEC_P;
   // staging items: C vectors, then key items (a B vector and the endpoint it is
   // written at: two per vector with two-endpoint writes), then X vectors
-  static constexpr int K_ITEMS = TE ? 2 * B_VECS : B_VECS;
+  static constexpr int K_ITEMS = B_VECS;  // with two-endpoint writes one B vector gives two key rows
   // Each kind starts on a wave boundary (a wave holding two kinds runs both code
   // paths).  With per-row decay the key items, the costliest to stage, come first:
   // they land on the first waves, which take no output tiles (those go from the last
@@ -217,7 +217,7 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
         const int t = t0 + row / R, o = row % R;
         if (t < L) val = *reinterpret_cast<const uint4*>(Cg + t * tsG + o * N + nv * VEC);
       } else if (u >= S::K0 && u < S::K0 + S::K_ITEMS) {
-        const int v = (u - S::K0) >> S::TEH;  // the two endpoints of a vector load it twice
+        const int v = u - S::K0;
         const int row = v / S::NVEC_N, nv = v % S::NVEC_N;
         const int t = t0 + row / R - S::TEH, r = row % R;
         if (t >= 0 && t < L) val = *reinterpret_cast<const uint4*>(Bg + t * tsG + r * N + nv * VEC);
@@ -352,7 +352,7 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
           *reinterpret_cast<uint4*>(q + row * NS + n0) = rr[k];
         }
       } else if (u >= S::K0 && u < S::K0 + S::K_ITEMS) {
-        const int v = (u - S::K0) >> S::TEH;
+        const int v = u - S::K0;
         const int row = v / S::NVEC_N, nv = v % S::NVEC_N;
         const int n0 = nv * VEC;
         const int sl = row / R - S::TEH, r = row % R;
@@ -360,15 +360,20 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
           *reinterpret_cast<uint4*>(kb + (sl * KR + r) * NS + n0) = rr[k];
           continue;
         }
+        float bv[VEC];
+        unpack<BF16>(rr[k], bv);
         // e = 0: gamma_s B_s written at s = sl; e = 1: beta_{s+1} B_s written at s+1
-        const int e = S::TE ? ((u - S::K0) & 1) : 0;
-        const int tau = sl + e;
-        if (tau < 0 || tau >= QT) continue;
-        const int j = tau * KR + (e ? R : 0) + r;
-        float uu[VEC];
-        unpack<BF16>(rr[k], uu);
-        apply_table(uu, (S::TE && e ? sTK1 : sTK0) + tau * N, n0);
-        *reinterpret_cast<uint4*>(kb + j * NS + n0) = pack<BF16>(uu);
+#pragma unroll
+        for (int e = 0; e < 1 + S::TEH; ++e) {
+          const int tau = sl + e;
+          if (tau < 0 || tau >= QT) continue;
+          const int j = tau * KR + (e ? R : 0) + r;
+          float uu[VEC];
+#pragma unroll
+          for (int i = 0; i < VEC; ++i) uu[i] = bv[i];
+          apply_table(uu, (e ? sTK1 : sTK0) + tau * N, n0);
+          *reinterpret_cast<uint4*>(kb + j * NS + n0) = pack<BF16>(uu);
+        }
       } else if (u >= S::X0 && u < S::ALL_VECS) {
         const int v = u - S::X0;
         const int row = v / S::NVEC_P, pv = v % S::NVEC_P;
