@@ -1087,7 +1087,10 @@ hipError_t launch_fwd(const FwdKey& k, const FwdParams& p, hipStream_t stream,
     mark(0);                                                                                 \
     if (p.nseg > 1) {                                                                        \
       const int lgrid = p.batch * p.H * (p.nseg - 1) * p.nsub;                               \
-      if (p.P % 32 == 0)                                                                     \
+      if (NN <= 64 && p.P % 64 == 0)                                                         \
+        hipLaunchKernelGGL((ssm_fwd_local<BF, NN, 64, RR, (KRR > RR), CO>),                  \
+                           dim3(lgrid * (p.P / 64)), dim3(256), 0, stream, p);               \
+      else if (p.P % 32 == 0)                                                                \
         hipLaunchKernelGGL((ssm_fwd_local<BF, NN, 32, RR, (KRR > RR), CO>),                  \
                            dim3(lgrid * (p.P / 32)), dim3(256), 0, stream, p);               \
       else                                                                                   \
