@@ -227,11 +227,16 @@ static Segs adj_segments(const ssm_desc* d, const Plan& pl) {
   return segments((long)d->batch * d->nheads, pl.nchunks);
 }
 
+// workspace of the segmented boundary-adjoint sweep: the range adjoints of the local
+// pass, the adjoints flowing into the segments and the ranges' summed steps
 static size_t adj_segment_bytes(const ssm_desc* d, const Plan& pl) {
   const Segs sg = adj_segments(d, pl);
   if (sg.nseg <= 1) return 0;
-  const size_t st = (size_t)d->batch * d->nheads * sg.nseg * d->dstate * d->headdim * sizeof(float);
-  return 2 * st + ((size_t)d->batch * d->nheads * sg.nseg * sizeof(float) + 255) / 256 * 256;
+  const LocalRanges lr = local_ranges(pl, sg);
+  const size_t slices = (size_t)d->batch * d->nheads, np = (size_t)d->dstate * d->headdim;
+  const size_t loc = slices * (sg.nseg - 1) * lr.nsub * np * sizeof(float);
+  const size_t in = slices * sg.nseg * np * sizeof(float);
+  return loc + in + (slices * (sg.nseg - 1) * lr.nsub * sizeof(float) + 255) / 256 * 256;
 }
 
 size_t ssm_workspace_bytes(const ssm_desc* d, int for_backward) {
@@ -349,10 +354,14 @@ int ssm_scan_bwd(const ssm_desc* d, const ssm_bwd_args* a, void* ws, size_t ws_b
   if (sg.nseg > 1) {
     const size_t part = (size_t)d->batch * d->nheads * pl.nchunks * npart_of(d, pl) * sizeof(float);
     char* base = reinterpret_cast<char*>(p.part) + (part + 255) / 256 * 256;
-    const size_t st = (size_t)d->batch * d->nheads * sg.nseg * d->dstate * d->headdim;
+    const LocalRanges lr = local_ranges(pl, sg);
+    p.seg_tokens = lr.seg_tokens;
+    p.nsub = lr.nsub;
+    p.lsub = lr.lsub;
+    const size_t slices = (size_t)d->batch * d->nheads, np = (size_t)d->dstate * d->headdim;
     p.gloc = reinterpret_cast<float*>(base);
-    p.gin = p.gloc + st;
-    p.gdel = p.gin + st;
+    p.gin = p.gloc + slices * (sg.nseg - 1) * lr.nsub * np;
+    p.gdel = p.gin + slices * sg.nseg * np;
   }
   if (d->ngroups != d->nheads) {
     // per-head dB / dC partials at the end of the workspace

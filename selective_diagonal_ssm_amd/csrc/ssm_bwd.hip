@@ -37,6 +37,7 @@
 
 #include "ssm_device.hpp"
 #include "ssm_kernels.hpp"
+#include "ssm_local.hpp"
 
 namespace ssm {
 
@@ -75,8 +76,6 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_adjoint(BwdParams p) {
   const int npblk = p.P / PB;
   const int lid = xcd_logical_id(blockIdx.x, gridDim.x);
   const int slice = lid / (npblk * p.nseg), seg = (lid / npblk) % p.nseg, pblk = lid % npblk;
-  const bool local = p.state_only != 0;
-  if (local && seg == 0) return;  // the first segment's local adjoint is never needed
   const int c0 = seg * p.chunks_per_seg, c1 = min(p.nchunks, c0 + p.chunks_per_seg);
   const int b = slice / p.H, h = slice % p.H, g = h / (p.H / p.G);
   const int p0 = pblk * PB;
@@ -101,7 +100,7 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_adjoint(BwdParams p) {
 
   // carried adjoint: zero past the sequence end, else (full pass of a segment) the
   // adjoint flowing in from the segments on the right
-  const float* g_in = (!local && seg + 1 < p.nseg) ? p.gin + ((size_t)slice * p.nseg + seg) * N * p.P + p0 : nullptr;
+  const float* g_in = seg + 1 < p.nseg ? p.gin + ((size_t)slice * p.nseg + seg) * N * p.P + p0 : nullptr;
   // adjoint tiles, transposed: st[k][i] = G[n = 16 tn + (lane & 15)][p = 16 tp + 4 (lane >> 4) + i]
   // (one state row per lane, so each lane stores a 4-column piece; a pair's two rows
   // sit in lanes l, l ^ 1)
@@ -155,7 +154,6 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_adjoint(BwdParams p) {
     const float raw = p.dt[((size_t)b * L + c1 * QT) * H + h];
     dnext = p.softplus ? softplus_f32(raw) : raw;
   }
-  float segsum = 0.f;  // summed step of this segment's transition (local pass)
   prefetch(c1 - 1);
   for (int c = c1 - 1; c >= c0; --c) {
     const int t0 = c * QT;
@@ -167,7 +165,6 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_adjoint(BwdParams p) {
     const float cdx = cd - read_lane(dl, 0);               // sum over (t0, t]
     const float cdx_end = read_lane(cdx, QT - 1) + dnext;  // sum over (t0, t0']
     dnext = read_lane(dl, 0);
-    segsum += cdx_end;
 
     // operands: rows (t, o) of  e^{L'_t} R(-Theta'_t) C_t  and  dy_t
 #pragma unroll
@@ -256,29 +253,13 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_adjoint(BwdParams p) {
           mma<BF16>(acc, bq, a);  // transposed: rows p, columns n
         }
         st[k] = acc;
-        if (!local) {
-          // the boundary adjoint in the io dtype (it enters the chunk products so)
-          const int n = 16 * tnn + (lane & 15), pl = 16 * tp + 4 * (lane >> 4);
-          T* dst = static_cast<T*>(p.gseg) + ((size_t)slice * nch + c) * N * P;
-          const float v4[4] = {acc[0], acc[1], acc[2], acc[3]};
-          store4<BF16>(dst + (size_t)n * P + p0 + pl, v4);
-        }
+        // the boundary adjoint in the io dtype (it enters the chunk products so)
+        const int n = 16 * tnn + (lane & 15), pl = 16 * tp + 4 * (lane >> 4);
+        T* dst = static_cast<T*>(p.gseg) + ((size_t)slice * nch + c) * N * P;
+        const float v4[4] = {acc[0], acc[1], acc[2], acc[3]};
+        store4<BF16>(dst + (size_t)n * P + p0 + pl, v4);
       }
     }
-  }
-  if (local) {
-    // the segment's local adjoint at its first token, and its summed step
-    float* dst = p.gloc + ((size_t)slice * p.nseg + seg) * N * P + p0;
-#pragma unroll
-    for (int k = 0; k < S::ST_PER_WAVE; ++k) {
-      const int tile = wave + NW * k;
-      if (tile < S::ST_TILES) {
-        const int n = 16 * (tile / S::TP) + (lane & 15), pl = 16 * (tile % S::TP) + 4 * (lane >> 4);
-        *reinterpret_cast<float4*>(dst + (size_t)n * P + pl) = make_float4(st[k][0], st[k][1], st[k][2], st[k][3]);
-      }
-    }
-    if (pblk == 0 && tid == 0) p.gdel[(size_t)slice * p.nseg + seg] = segsum;
-    return;
   }
   // dLoss/dh0 = A_0^T g_0, with g_0 (the adjoint at token 0) now in st
   if (p.dh0 && seg == 0) {
@@ -313,11 +294,14 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_adjoint(BwdParams p) {
 }
 
 // ============================================================== adjoint segment combine
-// Adjoints flowing into the segments of each slice, from the last one back:
-//   E_{nseg-1} = 0,   E_{s-1} = rho_s R(-theta_s) E_s + G_loc[s],
-// with rho_s = e^{-A_n D_s}, theta_s = omega_k D_s and D_s the summed step of
-// segment s's transition (the per-chunk transposed decays and rotations of the
-// sweep compose to exactly these).  One thread per (slice, row pair, value column).
+// Adjoints flowing into the segments of each slice, from the last one back: starting
+// from zero after the sequence end, the local-pass ranges of segments nseg-1 .. 1 are
+// chained right to left,
+//   E <- rho_u R(-theta_u) E + G_loc[u],
+// with rho_u = e^{-A_n D_u}, theta_u = omega_k D_u and D_u the summed step of range u's
+// transition (the token-by-token transposed decays and rotations compose to exactly
+// these); after the first range of segment s, E is the adjoint flowing into segment
+// s - 1.  One thread per (slice, row pair, value column).
 __global__ __launch_bounds__(256) void ssm_adj_combine(BwdParams p, int per_row) {
   const int N = p.n_real + 2 * p.n_pairs, P = p.P, nreal = p.n_real, na = p.n_real + p.n_pairs;
   const long total = (long)p.batch * p.H * (N / 2) * P;
@@ -334,21 +318,24 @@ __global__ __launch_bounds__(256) void ssm_adj_combine(BwdParams p, int per_row)
     const float ra = rate(n), rb = rate(n + 1);
     const bool pair = per_row && n >= nreal;
     const float om = pair ? p.omega[(size_t)h * p.n_pairs + ((n - nreal) >> 1)] : 0.f;
-    const size_t sb = (size_t)slice * p.nseg;
+    const size_t sb = (size_t)slice * p.nseg, sl = (size_t)slice * (p.nseg - 1) * p.nsub;
     float a = 0.f, bv = 0.f;
     for (int s = p.nseg - 1; s >= 1; --s) {
-      const float dsum = p.gdel[sb + s];
-      float a2 = a * expf(-ra * dsum), b2 = bv * expf(-rb * dsum);
-      if (pair) {
-        float sn, cs;
-        sincosf(om * dsum, &sn, &cs);
-        const float x0 = a2, x1 = b2;
-        a2 = cs * x0 + sn * x1;  // R(-theta) = R(theta)^T
-        b2 = -sn * x0 + cs * x1;
+      for (int u = p.nsub - 1; u >= 0; --u) {
+        const size_t unit = sl + (size_t)(s - 1) * p.nsub + u;
+        const float dsum = p.gdel[unit];
+        float a2 = a * expf(-ra * dsum), b2 = bv * expf(-rb * dsum);
+        if (pair) {
+          float sn, cs;
+          sincosf(om * dsum, &sn, &cs);
+          const float x0 = a2, x1 = b2;
+          a2 = cs * x0 + sn * x1;  // R(-theta) = R(theta)^T
+          b2 = -sn * x0 + cs * x1;
+        }
+        const float* loc = p.gloc + (unit * N + n) * P + pp;
+        a = a2 + loc[0];
+        bv = b2 + loc[P];
       }
-      const float* loc = p.gloc + ((sb + s) * N + n) * P + pp;
-      a = a2 + loc[0];
-      bv = b2 + loc[P];
       float* out = p.gin + ((sb + s - 1) * N + n) * P + pp;
       out[0] = a;
       out[P] = bv;
@@ -1557,6 +1544,18 @@ static int blocks_per_cu(const void* kernel, int nthreads, std::atomic<int>& cac
   return v;
 }
 
+// the boundary-adjoint sweep's local pass: C keys and dy values over the ranges of
+// segments 1 .. nseg-1
+static LocalParams adj_local_params(const BwdParams& p) {
+  LocalParams l{};
+  l.key = p.C; l.val = p.dy; l.dt = p.dt; l.A = p.A; l.omega = p.omega;
+  l.out = p.gloc; l.delta = p.gdel;
+  l.batch = p.batch; l.L = p.L; l.H = p.H; l.G = p.G; l.P = p.P; l.n_real = p.n_real;
+  l.n_pairs = p.n_pairs; l.softplus = p.softplus; l.head_rates = p.head_rates;
+  l.nseg = p.nseg; l.seg_tokens = p.seg_tokens; l.nsub = p.nsub; l.lsub = p.lsub;
+  return l;
+}
+
 hipError_t launch_bwd(const BwdKey& k, const BwdParams& p, hipStream_t stream,
                       void* const* events) {
   const int slices = p.batch * p.H;
@@ -1572,20 +1571,13 @@ hipError_t launch_bwd(const BwdKey& k, const BwdParams& p, hipStream_t stream,
     mark(0);                                                                                  \
     const int agrid = slices * (PP / PB) * p.nseg;                                            \
     if (p.nseg > 1) {                                                                         \
-      BwdParams lp = p;                                                                       \
-      lp.state_only = 1;                                                                      \
-      hipLaunchKernelGGL((ssm_bwd_adjoint<BF, NN, PB, RR, QTT, CO, ADJ_NT>), dim3(agrid),     \
-                         dim3(ADJ_NT), 0, stream, lp);                                        \
+      launch_local<BF, NN, RR, false, CO, true>(adj_local_params(p), stream);                 \
       const long total = (long)slices * (NN / 2) * PP;                                        \
       const int cb = (int)std::min<long>((total + 255) / 256, 2048);                          \
       hipLaunchKernelGGL(ssm_adj_combine, dim3(cb), dim3(256), 0, stream, p, CO ? 1 : 0);     \
     }                                                                                         \
-    {                                                                                         \
-      BwdParams fp = p;                                                                       \
-      fp.state_only = 0;                                                                      \
-      hipLaunchKernelGGL((ssm_bwd_adjoint<BF, NN, PB, RR, QTT, CO, ADJ_NT>), dim3(agrid),     \
-                         dim3(ADJ_NT), 0, stream, fp);                                        \
-    }                                                                                         \
+    hipLaunchKernelGGL((ssm_bwd_adjoint<BF, NN, PB, RR, QTT, CO, ADJ_NT>), dim3(agrid),       \
+                       dim3(ADJ_NT), 0, stream, p);                                           \
     mark(1);                                                                                  \
     {                                                                                         \
       static std::atomic<int> occ{0};                                                         \

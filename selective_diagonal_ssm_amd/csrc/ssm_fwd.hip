@@ -34,6 +34,7 @@
 
 #include "ssm_device.hpp"
 #include "ssm_kernels.hpp"
+#include "ssm_local.hpp"
 
 namespace ssm {
 
@@ -679,288 +680,6 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
   }
 }
 
-// ------------------------------------------------------------------ segment local pass
-// The state at the end of a token range [ta, tb] from a zero start, with no outputs
-// (the segment chain's input):
-//   S = sum_{tau in [ta, tb]} Phi(tb, tau) W_tau,
-//   W_tau = gamma_tau B_tau X_tau + beta_tau B_{tau-1} X_{tau-1}   (plain write: B_tau X_tau),
-// where Phi(tb, tau) scales row n by e^{-A_n d_tau} and turns pair k by R(omega_k d_tau),
-// d_tau = sum_{r = tau+1 .. tb} Delta_r.  The two writes of X_tau (the gamma term at tau,
-// the beta term at tau + 1) fold into one key row per (token, rank):
-//   K_tau = [tau >= ta] gamma_tau Phi(tb, tau) B_tau + [tau < tb] beta_{tau+1} Phi(tb, tau+1) B_tau,
-// so S = sum_{tau = ta-1 .. tb} K_tau^T X_tau (token ta - 1 carries only its beta term):
-// one contraction over the range, with no sequential dependence.  Each wave takes
-// steps of 32 key rows on its own (wave-private LDS, no workgroup barrier inside the
-// loop; the next step's loads are in flight while a step is staged), and the four
-// waves' partial states are added in a fixed order at the end.
-template <bool BF16, int N, int PBL, int R, bool TE, bool COORD>
-struct LocalShape {
-  using T = typename Elem<BF16>::T;
-  static constexpr int VEC = Elem<BF16>::kVec;
-  static constexpr int PAD = 16 / static_cast<int>(sizeof(T));
-  static constexpr int QL = 32 / R;  // tokens per step (32 key rows)
-  static constexpr int KS = N + PAD, VS = PBL + PAD;
-  static constexpr int NV = N / VEC, PV = PBL / VEC;
-  static constexpr int TN = N / 16, TP = PBL / 16;
-  static constexpr int BI = QL * NV;      // key items per step: (token, n-vector), all ranks
-  static constexpr int XI = QL * R * PV;  // value vectors per step
-  static constexpr int BI_PER = (BI + 63) / 64, XI_PER = (XI + 63) / 64;
-  static constexpr int STAGE_BYTES = 4 * 32 * (KS + VS) * static_cast<int>(sizeof(T));
-  static constexpr int RED_BYTES = 3 * N * PBL * 4;  // partial states of waves 1..3
-  static constexpr int SMEM = STAGE_BYTES > RED_BYTES ? STAGE_BYTES : RED_BYTES;
-  static_assert(32 % R == 0 && N % 16 == 0 && PBL % 16 == 0, "unsupported local shape");
-};
-
-template <bool BF16, int N, int PBL, int R, bool TE, bool COORD>
-__global__ __launch_bounds__(256) void ssm_fwd_local(FwdParams p) {
-  using S = LocalShape<BF16, N, PBL, R, TE, COORD>;
-  using T = typename S::T;
-  constexpr int VEC = S::VEC, QL = S::QL, KS = S::KS, VS = S::VS, NV = S::NV, PV = S::PV;
-  constexpr int LM = kLocalMaxTokens;
-  constexpr float kLog2e = 1.4426950408889634f;
-  __shared__ __align__(16) unsigned char smem[S::SMEM];
-  __shared__ float sD[LM];                                   // Delta, then d_tau
-  __shared__ float sGa[TE ? LM : 1], sBe[TE ? LM : 1];
-  __shared__ float sBlk[LM / 64];
-  __shared__ float sRate[COORD ? N : 1], sOm[COORD ? N / 2 + 1 : 1];
-
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int nlp = p.P / PBL, nsegl = p.nseg - 1;
-  const int lid = xcd_logical_id(blockIdx.x, gridDim.x);
-  const int pblk = lid % nlp;
-  int rest = lid / nlp;
-  const int sub = rest % p.nsub;
-  rest /= p.nsub;
-  const int seg = rest % nsegl, slice = rest / nsegl;
-  const int b = slice / p.H, h = slice % p.H, g = h / (p.H / p.G);
-  const int L = p.L, H = p.H, G = p.G, P = p.P, p0 = pblk * PBL;
-  const int s0 = seg * p.seg_tokens;
-  const int ta = s0 + sub * p.lsub;
-  const int tb = min(min(ta + p.lsub, s0 + p.seg_tokens), L) - 1;
-  const int len = tb - ta + 1;  // >= 1 by construction of the ranges
-  const size_t unit = ((size_t)slice * nsegl + seg) * p.nsub + sub;
-
-  if (COORD) {
-    const int na = p.n_real + p.n_pairs, nreal = p.n_real;
-    for (int n = tid; n < N; n += 256) {
-      float r;
-      if (p.head_rates) r = p.A[h];
-      else if (n < nreal) r = p.A[(size_t)h * na + n];
-      else r = p.A[(size_t)h * na + nreal + ((n - nreal) >> 1)];
-      sRate[n] = r * kLog2e;
-    }
-    for (int k = tid; k < p.n_pairs; k += 256) sOm[k] = p.omega[(size_t)h * p.n_pairs + k];
-  }
-  const float* dtg = p.dt + (size_t)b * L * H + h;
-  for (int i = tid; i < len; i += 256) {
-    const float raw = dtg[(size_t)(ta + i) * H];
-    sD[i] = p.softplus ? softplus_f32(raw) : raw;
-    if (TE) {
-      sGa[i] = p.gamma[((size_t)b * L + ta + i) * H + h];
-      sBe[i] = p.beta[((size_t)b * L + ta + i) * H + h];
-    }
-  }
-  __syncthreads();
-  // d_i = sum of Delta over the tokens after i: exclusive suffix sums inside blocks
-  // of 64 tokens (lanes in reverse token order), then the later blocks' totals
-  const int nblk = (len + 63) / 64;
-  for (int blk = wave; blk < nblk; blk += 4) {
-    const int i = blk * 64 + 63 - lane;
-    const float v = i < len ? sD[i] : 0.f;
-    const float incl = wave_prefix_sum(v);
-    if (lane == 63) sBlk[blk] = incl;
-    if (i < len) sD[i] = incl - v;
-  }
-  __syncthreads();
-  for (int i = tid; i < len; i += 256) {
-    float after = 0.f;
-    for (int k = i / 64 + 1; k < nblk; ++k) after += sBlk[k];
-    sD[i] += after;
-  }
-  if (tid == 0 && pblk == 0) {
-    float tot = 0.f;
-    for (int k = 0; k < nblk; ++k) tot += sBlk[k];
-    p.seg_delta[unit] = tot;
-  }
-  __syncthreads();
-
-  const T* Bg = static_cast<const T*>(p.B) + ((size_t)b * L * G + g) * R * N;
-  const T* xg = static_cast<const T*>(p.x) + ((size_t)b * L * H + h) * R * P + p0;
-  const int tsG = G * R * N, tsH = H * R * P;
-  T* kw = reinterpret_cast<T*>(smem) + wave * 32 * KS;
-  T* vw = reinterpret_cast<T*>(smem) + 4 * 32 * KS + wave * 32 * VS;
-  const float ah = COORD ? 0.f : p.A[h] * kLog2e;
-  const int i_first = TE ? -1 : 0;  // relative token of the first key row
-  const int nsteps = (len - i_first + QL - 1) / QL;
-  // a loaded vector, or zero (selected per component: a whole-struct select can be
-  // lowered through scratch memory)
-  auto keep = [](bool ok, const uint4& v) {
-    return make_uint4(ok ? v.x : 0u, ok ? v.y : 0u, ok ? v.z : 0u, ok ? v.w : 0u);
-  };
-
-  f32x4 acc[S::TN][S::TP];
-#pragma unroll
-  for (int a = 0; a < S::TN; ++a)
-#pragma unroll
-    for (int c = 0; c < S::TP; ++c) acc[a][c] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  // raw B vectors (all ranks of a (token, n-vector) item) and X vectors of one step;
-  // loads are branch-free (clamped token, zero for rows outside the range)
-  uint4 rb[S::BI_PER][R], rx[S::XI_PER];
-  auto load = [&](int k) {
-    const int i0 = i_first + k * QL;
-#pragma unroll
-    for (int q = 0; q < S::BI_PER; ++q) {
-      const int u = lane + 64 * q;
-      const int j = u / NV, v = u % NV;
-      const int t = ta + i0 + j;
-      const bool ok = u < S::BI && i0 + j < len && t >= 0;
-      const int tc = ok ? t : ta;
-#pragma unroll
-      for (int r = 0; r < R; ++r) {
-        const uint4 val = *reinterpret_cast<const uint4*>(Bg + (size_t)tc * tsG + r * N + v * VEC);
-        rb[q][r] = keep(ok, val);
-      }
-    }
-#pragma unroll
-    for (int q = 0; q < S::XI_PER; ++q) {
-      const int u = lane + 64 * q;
-      const int jr = u / PV, pv = u % PV;
-      const int j = jr / R, r = jr % R;
-      const int t = ta + i0 + j;
-      const bool ok = u < S::XI && i0 + j < len && t >= 0;
-      const int tc = ok ? t : ta;
-      const uint4 val = *reinterpret_cast<const uint4*>(xg + (size_t)tc * tsH + r * P + pv * VEC);
-      rx[q] = keep(ok, val);
-    }
-  };
-
-  // key rows of one step into the wave's LDS: K_tau = coefficient (x) B_tau
-  auto stage = [&](int k) {
-    const int i0 = i_first + k * QL;
-#pragma unroll
-    for (int q = 0; q < S::BI_PER; ++q) {
-      const int u = lane + 64 * q;
-      if (u >= S::BI) break;
-      const int j = u / NV, v = u % NV, n0 = v * VEC;
-      const int i = i0 + j;
-      // the gamma term (write at token i) and the beta term (write at token i + 1)
-      const bool h0 = i >= 0 && i < len;
-      const bool h1 = TE && i + 1 < len;
-      const float d0 = h0 ? sD[i] : 0.f, d1 = h1 ? sD[i + 1] : 0.f;
-      const float g0 = h0 ? (TE ? sGa[i] : 1.f) : 0.f, g1 = h1 ? sBe[i + 1] : 0.f;
-      float cf[VEC], sf[VEC];  // per-row factor; pairs: (cos-part, sin-part) on the even row
-      if (!COORD) {
-        float c = g0 * __builtin_amdgcn_exp2f(-ah * d0);
-        if (TE) c += g1 * __builtin_amdgcn_exp2f(-ah * d1);
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) { cf[e] = c; sf[e] = 0.f; }
-      } else {
-#pragma unroll
-        for (int e = 0; e < VEC; e += 2) {
-          const int n = n0 + e;
-          if (n >= p.n_real) {
-            const float a = sRate[n], om = sOm[(n - p.n_real) >> 1];
-            float s0v, c0v, s1v = 0.f, c1v = 0.f;
-            fast_sincos(om * d0, &s0v, &c0v);
-            const float w0 = g0 * __builtin_amdgcn_exp2f(-a * d0);
-            float cc = w0 * c0v, ss = w0 * s0v;
-            if (TE) {
-              fast_sincos(om * d1, &s1v, &c1v);
-              const float w1 = g1 * __builtin_amdgcn_exp2f(-a * d1);
-              cc += w1 * c1v;
-              ss += w1 * s1v;
-            }
-            cf[e] = cc; sf[e] = ss; cf[e + 1] = cc; sf[e + 1] = ss;
-          } else {
-#pragma unroll
-            for (int f = 0; f < 2; ++f) {
-              const float a = sRate[n + f];
-              float c = g0 * __builtin_amdgcn_exp2f(-a * d0);
-              if (TE) c += g1 * __builtin_amdgcn_exp2f(-a * d1);
-              cf[e + f] = c; sf[e + f] = 0.f;
-            }
-          }
-        }
-      }
-#pragma unroll
-      for (int r = 0; r < R; ++r) {
-        float bv[VEC], kv[VEC];
-        unpack<BF16>(rb[q][r], bv);
-#pragma unroll
-        for (int e = 0; e < VEC; e += 2) {
-          // [[c, -s], [s, c]] on a pair (s = 0 on real rows)
-          kv[e] = cf[e] * bv[e] - sf[e] * bv[e + 1];
-          kv[e + 1] = sf[e] * bv[e] + cf[e + 1] * bv[e + 1];
-        }
-        *reinterpret_cast<uint4*>(kw + (j * R + r) * KS + n0) = pack<BF16>(kv);
-      }
-    }
-#pragma unroll
-    for (int q = 0; q < S::XI_PER; ++q) {
-      const int u = lane + 64 * q;
-      if (u >= S::XI) break;
-      const int jr = u / PV, pv = u % PV;
-      *reinterpret_cast<uint4*>(vw + jr * VS + pv * VEC) = rx[q];
-    }
-  };
-
-  int k = wave;
-  if (k < nsteps) load(k);
-  for (; k < nsteps; k += 4) {
-    stage(k);
-    if (k + 4 < nsteps) load(k + 4);
-    // the wave's own LDS writes before its transposed reads
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
-#pragma unroll
-    for (int tn = 0; tn < S::TN; ++tn) {
-      const auto fk = load_frag_tr<BF16>(kw + 16 * tn, KS);
-#pragma unroll
-      for (int tp = 0; tp < S::TP; ++tp) {
-        const auto fv = load_frag_tr<BF16>(vw + 16 * tp, VS);
-        mma<BF16>(acc[tn][tp], fv, fk);
-      }
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
-  }
-
-  // partial states of waves 1..3 through LDS, added to wave 0's in order;
-  // acc[tn][tp][i] = S[n = 16 tn + (lane & 15)][p = 16 tp + 4 (lane >> 4) + i]
-  __syncthreads();
-  float* red = reinterpret_cast<float*>(smem);
-  if (wave > 0) {
-#pragma unroll
-    for (int tn = 0; tn < S::TN; ++tn)
-#pragma unroll
-      for (int tp = 0; tp < S::TP; ++tp) {
-        const int n = 16 * tn + (lane & 15), pl = 16 * tp + 4 * (lane >> 4);
-        *reinterpret_cast<float4*>(red + ((wave - 1) * N + n) * PBL + pl) =
-            make_float4(acc[tn][tp][0], acc[tn][tp][1], acc[tn][tp][2], acc[tn][tp][3]);
-      }
-  }
-  __syncthreads();
-  if (wave == 0) {
-    float* dst = p.seg_local + unit * N * P + p0;
-#pragma unroll
-    for (int tn = 0; tn < S::TN; ++tn)
-#pragma unroll
-      for (int tp = 0; tp < S::TP; ++tp) {
-        const int n = 16 * tn + (lane & 15), pl = 16 * tp + 4 * (lane >> 4);
-        float4 s = make_float4(acc[tn][tp][0], acc[tn][tp][1], acc[tn][tp][2], acc[tn][tp][3]);
-#pragma unroll
-        for (int w = 0; w < 3; ++w) {
-          const float4 o = *reinterpret_cast<const float4*>(red + (w * N + n) * PBL + pl);
-          s.x += o.x; s.y += o.y; s.z += o.z; s.w += o.w;
-        }
-        *reinterpret_cast<float4*>(dst + (size_t)n * P + pl) = s;
-      }
-  }
-}
-
 // ------------------------------------------------------------------ segment combine
 // States entering the segments of each slice, in order: starting from h0 (or 0), the
 // local-pass ranges of every segment are chained in token order,
@@ -1074,6 +793,17 @@ bool fwd_variant_exists(const FwdKey& k) {
   return false;
 }
 
+// the forward's local pass: B keys and x values over the ranges of segments 0 .. nseg-2
+static LocalParams local_params(const FwdParams& p) {
+  LocalParams l{};
+  l.key = p.B; l.val = p.x; l.dt = p.dt; l.A = p.A; l.omega = p.omega; l.beta = p.beta;
+  l.gamma = p.gamma; l.out = p.seg_local; l.delta = p.seg_delta;
+  l.batch = p.batch; l.L = p.L; l.H = p.H; l.G = p.G; l.P = p.P; l.n_real = p.n_real;
+  l.n_pairs = p.n_pairs; l.softplus = p.softplus; l.head_rates = p.head_rates;
+  l.nseg = p.nseg; l.seg_tokens = p.seg_tokens; l.nsub = p.nsub; l.lsub = p.lsub;
+  return l;
+}
+
 hipError_t launch_fwd(const FwdKey& k, const FwdParams& p, hipStream_t stream,
                       void* const* events) {
   const int nwg = p.batch * p.H * p.npblk * p.nseg;
@@ -1086,16 +816,7 @@ hipError_t launch_fwd(const FwdKey& k, const FwdParams& p, hipStream_t stream,
       k.coord == CO && k.nthreads == NT) {                                                   \
     mark(0);                                                                                 \
     if (p.nseg > 1) {                                                                        \
-      const int lgrid = p.batch * p.H * (p.nseg - 1) * p.nsub;                               \
-      if (NN <= 64 && p.P % 64 == 0)                                                         \
-        hipLaunchKernelGGL((ssm_fwd_local<BF, NN, 64, RR, (KRR > RR), CO>),                  \
-                           dim3(lgrid * (p.P / 64)), dim3(256), 0, stream, p);               \
-      else if (p.P % 32 == 0)                                                                \
-        hipLaunchKernelGGL((ssm_fwd_local<BF, NN, 32, RR, (KRR > RR), CO>),                  \
-                           dim3(lgrid * (p.P / 32)), dim3(256), 0, stream, p);               \
-      else                                                                                   \
-        hipLaunchKernelGGL((ssm_fwd_local<BF, NN, 16, RR, (KRR > RR), CO>),                  \
-                           dim3(lgrid * (p.P / 16)), dim3(256), 0, stream, p);               \
+      launch_local<BF, NN, RR, (KRR > RR), CO, false>(local_params(p), stream);            \
       const long total = (long)p.batch * p.H * (NN / 2) * p.P;                               \
       const int cb = (int)std::min<long>((total + 255) / 256, 2048);                         \
       hipLaunchKernelGGL(ssm_fwd_combine, dim3(cb), dim3(256), 0, stream, p, CO ? 1 : 0);    \

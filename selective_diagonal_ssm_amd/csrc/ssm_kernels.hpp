@@ -36,6 +36,22 @@ struct FwdParams {
 // tokens of one local-pass range (bounds the kernel's per-token LDS tables)
 constexpr int kLocalMaxTokens = 512;
 
+// operands of a segment local pass: forward ranges (states from a zero start) or
+// boundary-adjoint ranges (adjoints from a zero adjoint after the range)
+struct LocalParams {
+  const void* key;  // B (forward) or C (adjoint): [batch][L][G][R][N], io dtype
+  const void* val;  // x (forward) or dy (adjoint): [batch][L][H][R][P], io dtype
+  const float* dt;
+  const float* A;
+  const float* omega;
+  const float* beta;
+  const float* gamma;
+  float* out;    // [slice][nseg - 1][nsub][N][P] range states
+  float* delta;  // [slice][nseg - 1][nsub] range summed steps
+  int batch, L, H, G, P, n_real, n_pairs, softplus, head_rates;
+  int nseg, seg_tokens, nsub, lsub;
+};
+
 struct BwdParams {
   const void* x;
   const void* B;
@@ -69,10 +85,11 @@ struct BwdParams {
   int nseg, chunks_per_seg;  // sequence segments of the boundary-adjoint sweep
   int softplus, has_D, npart;
   int head_rates;
-  int state_only;  // adjoint local pass: each segment from a zero incoming adjoint
-  float* gloc;     // [slice][nseg][N][P] local adjoints at the segments' first tokens
+  // local pass: every segment but the first is cut into nsub ranges of lsub tokens
+  int seg_tokens, nsub, lsub;
+  float* gloc;     // [slice][nseg - 1][nsub][N][P] range adjoints at the ranges' first tokens
   float* gin;      // [slice][nseg][N][P] adjoints flowing into the segments from the right
-  float* gdel;     // [slice][nseg] summed step of each segment's transition
+  float* gdel;     // [slice][nseg - 1][nsub] summed step of each range's transition
 };
 
 // Single-token recurrent step (one token per slice, state updated in place).
