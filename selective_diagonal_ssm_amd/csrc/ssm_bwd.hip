@@ -115,6 +115,10 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_adjoint(BwdParams p) {
       st[k] = f32x4{v.x, v.y, v.z, v.w};
     }
   }
+  // take these loads here: left pending into the chunk loop, they would make the
+  // compiler wait on every outstanding memory operation inside it
+#pragma unroll
+  for (int k = 0; k < S::ST_PER_WAVE; ++k) asm volatile("" : "+v"(st[k]));
 
   const int nch = p.nchunks;
   // register prefetch of one chunk's C rows, dy rows and steps
