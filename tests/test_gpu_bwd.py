@@ -53,6 +53,15 @@ SMALL = {
     "bf16_groups_mimo": ("ssd_mimo", dict(batch=1, seqlen=200, nheads=4, ngroups=1)),
     "bf16_groups_hybrid": ("hybrid", dict(batch=2, seqlen=150, nheads=4, ngroups=2)),
     "bf16_groups_hybrid_r1": ("hybrid_r1", dict(batch=1, seqlen=90, nheads=6, ngroups=3)),
+    # HybridMamba row mixes: real rows only, rotating pairs only, a quarter of the rows paired
+    "bf16_hm_real_only": ("hybrid", dict(batch=2, seqlen=150, nheads=2, ngroups=2, n_real=64,
+                                         n_pairs=0)),
+    "bf16_hm_pairs_only": ("hybrid", dict(batch=2, seqlen=150, nheads=2, ngroups=2, n_real=0,
+                                          n_pairs=32)),
+    "bf16_hm_quarter_pairs": ("hybrid", dict(batch=2, seqlen=150, nheads=2, ngroups=2,
+                                             n_real=48, n_pairs=8)),
+    "f32_hm_pairs_only": ("hybrid", dict(dtype="f32", dstate=32, n_real=0, n_pairs=16,
+                                         headdim=16, batch=2, nheads=2, ngroups=2, seqlen=77)),
 }
 
 

@@ -53,6 +53,15 @@ SMALL_CASES = {
     "bf16_len_chunk": ("ssd_siso", dict(batch=1, seqlen=64, nheads=2, ngroups=2, dstate=64,
                                         n_real=64)),
     "bf16_len_chunk1": ("hybrid", dict(batch=1, seqlen=17, nheads=2, ngroups=2)),
+    # HybridMamba row mixes: real rows only, rotating pairs only, a quarter of the rows paired
+    "bf16_hm_real_only": ("hybrid", dict(batch=2, seqlen=150, nheads=2, ngroups=2, n_real=64,
+                                         n_pairs=0)),
+    "bf16_hm_pairs_only": ("hybrid", dict(batch=2, seqlen=150, nheads=2, ngroups=2, n_real=0,
+                                          n_pairs=32)),
+    "bf16_hm_quarter_pairs": ("hybrid", dict(batch=2, seqlen=150, nheads=2, ngroups=2,
+                                             n_real=48, n_pairs=8)),
+    "f32_hm_pairs_only": ("hybrid", dict(dtype="f32", dstate=32, n_real=0, n_pairs=16,
+                                         headdim=16, batch=2, nheads=2, ngroups=2, seqlen=77)),
 }
 
 
