@@ -48,6 +48,9 @@
  *     SSM_F_TWO_ENDPOINT is clear; D iff SSM_F_HAS_D is clear (D requires
  *     rank_out == rank_in).  In the backward, a NULL gradient output is not
  *     computed; dx, dB, dC, ddt must be non-NULL.
+ *   - rank_in (R) and rank_out (O) may differ ("SSD-MIMO" with different input
+ *     and output widths); the scans tile with the larger of the two (at most 4)
+ *     and treat the narrower side's missing rows as zero.
  *   - `saved` (ssm_saved_bytes(desc) bytes) receives the chunk-boundary states
  *     from the forward when non-NULL, stored in the io dtype (they enter the
  *     reverse pass's products in that dtype); ssm_scan_bwd requires the buffer a

@@ -48,22 +48,23 @@ int check_operation(const ssm_desc* d) {
 int make_plan(const ssm_desc* d, Plan* pl) {
   int rc = check_operation(d);
   if (rc) return rc;
-  if (d->rank_out != d->rank_in) return SSM_ERR_UNSUPPORTED;
   if (d->headdim % 16) return SSM_ERR_UNSUPPORTED;
   if (d->n_pairs > 0 && (d->n_real % 2)) return SSM_ERR_UNSUPPORTED;
   // kernels index inside a tensor with 32-bit offsets
-  const double elems = (double)d->batch * d->seqlen * d->nheads * d->rank_in *
+  const int rmax = std::max(d->rank_in, d->rank_out);
+  const double elems = (double)d->batch * d->seqlen * d->nheads * rmax *
                        (d->headdim > d->dstate ? d->headdim : d->dstate);
   if (elems >= 2147483648.0) return SSM_ERR_UNSUPPORTED;
   const bool te = (d->flags & SSM_F_TWO_ENDPOINT) != 0;
   pl->bf16 = d->io_dtype == SSM_BF16;
   pl->coord_kernel = d->decay_mode == SSM_DECAY_COORD || te || d->n_pairs > 0;
   pl->head_rates = d->decay_mode == SSM_DECAY_HEAD;
-  pl->R = d->rank_in;
-  pl->KR = te ? 2 * d->rank_in : d->rank_in;
+  // the kernels tile with the larger rank; the narrower side's extra rows are zero
+  pl->R = rmax;
+  pl->KR = te ? 2 * rmax : rmax;
   int qt = d->chunk;
   if (qt == 0) {
-    if (!pl->coord_kernel) qt = 64 / d->rank_in;
+    if (!pl->coord_kernel) qt = 64 / rmax;
     else qt = (16 * pl->KR >= 32) ? 16 : 32 / pl->KR;
     if (qt < 1) qt = 1;
   }
@@ -192,7 +193,7 @@ static size_t bwd_gseg_bytes(const ssm_desc* d, const Plan& pl) {
 
 // head groups shared by several heads: per-head dB and dC partials in the io dtype
 static size_t group_partial_one(const ssm_desc* d, const Plan& pl) {
-  const size_t one = (size_t)d->batch * d->seqlen * d->nheads * d->rank_in * d->dstate * (pl.bf16 ? 2 : 4);
+  const size_t one = (size_t)d->batch * d->seqlen * d->nheads * pl.R * d->dstate * (pl.bf16 ? 2 : 4);
   return (one + 255) / 256 * 256;
 }
 static size_t group_partial_bytes(const ssm_desc* d, const Plan& pl) {
@@ -283,6 +284,8 @@ int ssm_scan_fwd(const ssm_desc* d, const ssm_fwd_args* a, void* ws, size_t ws_b
   p.batch = d->batch; p.L = d->seqlen; p.H = d->nheads; p.G = d->ngroups; p.P = d->headdim;
   p.n_real = d->n_real; p.n_pairs = d->n_pairs; p.nchunks = pl.nchunks;
   p.npblk = d->headdim / pb;
+  p.rin = d->rank_in;
+  p.rout = d->rank_out;
   p.softplus = (d->flags & SSM_F_DT_SOFTPLUS) ? 1 : 0;
   p.has_D = hasD ? 1 : 0;
   p.head_rates = pl.head_rates ? 1 : 0;
@@ -312,7 +315,8 @@ int ssm_scan_bwd(const ssm_desc* d, const ssm_bwd_args* a, void* ws, size_t ws_b
   int rc = make_plan(d, &pl);
   if (rc) return rc;
   if (!a) return SSM_ERR_NULL;
-  BwdKey key{pl.bf16, d->dstate, d->headdim, pl.R, pl.KR, pl.QT, pl.coord_kernel};
+  BwdKey key{pl.bf16, d->dstate, d->headdim, pl.R, pl.KR, pl.QT, pl.coord_kernel,
+             d->rank_in != d->rank_out};
   if (!ssm::bwd_variant_exists(key)) return SSM_ERR_UNSUPPORTED;
   if (d->batch == 0 || d->seqlen == 0) return SSM_OK;
   const bool te = (d->flags & SSM_F_TWO_ENDPOINT) != 0;
@@ -348,6 +352,7 @@ int ssm_scan_bwd(const ssm_desc* d, const ssm_bwd_args* a, void* ws, size_t ws_b
                                     (bwd_gseg_bytes(d, pl) + 255) / 256 * 256);
   p.batch = d->batch; p.L = d->seqlen; p.H = d->nheads; p.G = d->ngroups; p.P = d->headdim;
   p.n_real = d->n_real; p.n_pairs = d->n_pairs; p.nchunks = pl.nchunks;
+  p.rin = d->rank_in; p.rout = d->rank_out;
   const Segs sg = adj_segments(d, pl);
   p.nseg = sg.nseg;
   p.chunks_per_seg = sg.cps;

@@ -133,7 +133,8 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_adjoint(BwdParams p) {
       if (v < S::C_VECS) {
         const int row = v / (N / VEC), n0 = (v % (N / VEC)) * VEC;
         const int t = t0 + row / R, o = row % R;
-        if (t < L) raw = *reinterpret_cast<const uint4*>(Cg + ((((size_t)b * L + t) * G + g) * R + o) * N + n0);
+        if (t < L && o < p.rout)
+          raw = *reinterpret_cast<const uint4*>(Cg + ((((size_t)b * L + t) * G + g) * p.rout + o) * N + n0);
       }
       pc[k] = raw;
     }
@@ -144,8 +145,8 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_adjoint(BwdParams p) {
       if (v < S::Y_VECS) {
         const int row = v / (PB / VEC), pv = v % (PB / VEC);
         const int t = t0 + row / R, o = row % R;
-        if (t < L)
-          raw = *reinterpret_cast<const uint4*>(dyg + ((((size_t)b * L + t) * H + h) * R + o) * P + p0 + pv * VEC);
+        if (t < L && o < p.rout)
+          raw = *reinterpret_cast<const uint4*>(dyg + ((((size_t)b * L + t) * H + h) * p.rout + o) * P + p0 + pv * VEC);
       }
       py[k] = raw;
     }
@@ -407,7 +408,9 @@ struct BwdShape {
   static_assert(KR <= 4 && 16 % KR == 0 && 16 % R == 0, "a tile spans whole tokens");
 };
 
-template <bool BF16, int N, int P, int R, int KR, int QT, bool COORD, int NTHREADS>
+// SPLIT: write and readout ranks differ (taken from the parameters; R is the larger);
+// otherwise both are R, known at compile time
+template <bool BF16, int N, int P, int R, int KR, int QT, bool COORD, int NTHREADS, bool SPLIT>
 __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
   using S = BwdShape<BF16, N, P, R, KR, QT, COORD, NTHREADS>;
   constexpr int NW = S::NW;
@@ -464,8 +467,11 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
   T* dBg = static_cast<T*>(part ? p.dBh : p.dB);
   T* dCg = static_cast<T*>(part ? p.dCh : p.dC);
   const int GO = part ? H : G;  // rows per token of those buffers
-  auto store_bc = [&](T* out, int bb, int t, int go, int r, int n, const float* v) {
-    store4<BF16>(out + ((((size_t)bb * L + t) * GO + go) * R + r) * N + n, v);
+  // rows per token: the side's own rank in the outputs, R in the partials
+  const int rin = SPLIT ? p.rin : R, rout = SPLIT ? p.rout : R;
+  auto store_bc = [&](T* out, int rows, int bb, int t, int go, int r, int n, const float* v) {
+    const int rs = part ? R : rows;
+    store4<BF16>(out + ((((size_t)bb * L + t) * GO + go) * rs + r) * N + n, v);
   };
 
   // zero padding rows / columns (the staging never writes them)
@@ -532,7 +538,7 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
       if (v < S::C_VECS) {
         const int row = v / (N / VEC), n0 = (v % (N / VEC)) * VEC;
         const int t = t0 + row / R, o = row % R;
-        if (t < L) raw = *reinterpret_cast<const uint4*>(Cg + ((((size_t)b * L + t) * G + g) * R + o) * N + n0);
+        if (t < L && o < rout) raw = *reinterpret_cast<const uint4*>(Cg + ((((size_t)b * L + t) * G + g) * rout + o) * N + n0);
       }
       pfc[k] = raw;
     }
@@ -543,7 +549,7 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
       if (v < S::B_VECS) {
         const int row = v / (N / VEC), n0 = (v % (N / VEC)) * VEC;
         const int t = t0 + row / R - S::TEH, r = row % R;
-        if (t >= 0 && t < L) raw = *reinterpret_cast<const uint4*>(Bg + ((((size_t)b * L + t) * G + g) * R + r) * N + n0);
+        if (t >= 0 && t < L && r < rin) raw = *reinterpret_cast<const uint4*>(Bg + ((((size_t)b * L + t) * G + g) * rin + r) * N + n0);
       }
       pfb[k] = raw;
     }
@@ -556,7 +562,7 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
       if (v < S::X_VECS) {
         const int row = v / (P / VEC), p0 = (v % (P / VEC)) * VEC;
         const int t = t0 + row / R - S::TEH, r = row % R;
-        if (t >= 0 && t < L) raw = *reinterpret_cast<const uint4*>(xg + ((((size_t)b * L + t) * H + h) * R + r) * P + p0);
+        if (t >= 0 && t < L && r < rin) raw = *reinterpret_cast<const uint4*>(xg + ((((size_t)b * L + t) * H + h) * rin + r) * P + p0);
       }
       pfx[k] = raw;
     }
@@ -567,7 +573,7 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
       if (v < S::Y_VECS) {
         const int row = v / (P / VEC), p0 = (v % (P / VEC)) * VEC;
         const int t = t0 + row / R, o = row % R;
-        if (t < L) raw = *reinterpret_cast<const uint4*>(dyg + ((((size_t)b * L + t) * H + h) * R + o) * P + p0);
+        if (t < L && o < rout) raw = *reinterpret_cast<const uint4*>(dyg + ((((size_t)b * L + t) * H + h) * rout + o) * P + p0);
       }
       pfy[k] = raw;
     }
@@ -1018,7 +1024,7 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
           for (int i = 0; i < 4; ++i) dv[i] += Dh * yv[i];
         }
         const int t = t0 + s;
-        if (t < L) store4<BF16>(dxg + ((((size_t)b * L + t) * H + h) * R + kr) * P + pl, dv);
+        if (t < L && kr < rin) store4<BF16>(dxg + ((((size_t)b * L + t) * H + h) * rin + kr) * P + pl, dv);
       } else if (kr < R) {
         // gamma row -> X_s
         *reinterpret_cast<float4*>(sDX + ((s + 1) * R + kr) * P + pl) = make_float4(dv[0], dv[1], dv[2], dv[3]);
@@ -1088,9 +1094,9 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
       float dgb = 0.f;
       if (S::TE) {
         const float wgt = brow ? sTbe[s] : sTga[s];
-        if (tb >= 0 && tb < L) {
+        if (tb >= 0 && tb < L && rr < rin) {
           float braw[4];
-          load4<BF16>(Bg + ((((size_t)b * L + tb) * G + g) * R + rr) * N + n0, braw);
+          load4<BF16>(Bg + ((((size_t)b * L + tb) * G + g) * rin + rr) * N + n0, braw);
 #pragma unroll
           for (int i = 0; i < 4; ++i) dgb += dk[i] * braw[i];
         }
@@ -1101,8 +1107,8 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
           *reinterpret_cast<float4*>(sDB + (QT + 1) * R * N + (s * R + rr) * N + n0) =
               make_float4(wgt * dk[0], wgt * dk[1], wgt * dk[2], wgt * dk[3]);
         }
-      } else if (tb < L) {
-        store_bc(dBg, b, tb, part ? h : g, rr, n0, dk);
+      } else if (tb < L && rr < rin) {
+        store_bc(dBg, rin, b, tb, part ? h : g, rr, n0, dk);
       }
       if (COORD) {
         // per-row sums over the 16 key columns of this tile (one 16-lane group)
@@ -1239,7 +1245,7 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
           }
         }
       }
-      if (tg < L) store_bc(dCg, b, tg, part ? h : g, o, n0, dc);
+      if (tg < L && o < rout) store_bc(dCg, rout, b, tg, part ? h : g, o, n0, dc);
       if (COORD) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) rpa[i] = group_sum<16>(rpa[i]);
@@ -1328,7 +1334,7 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
   #pragma unroll
           for (int q = 0; q < 4; ++q) v[q] += Dh * yv[q];
         }
-        if (t < L) store4<BF16>(dxg + ((((size_t)b * L + t) * H + h) * R + r) * P + pp, v);
+        if (t < L && r < rin) store4<BF16>(dxg + ((((size_t)b * L + t) * H + h) * rin + r) * P + pp, v);
       }
       for (int i4 = tid; i4 < QT * R * N / 4; i4 += S::NTH) {
         const int i = 4 * i4;
@@ -1339,7 +1345,7 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
             ? *reinterpret_cast<const float4*>(sDB + (QT + 1) * R * N + ((s + 1) * R + r) * N + n)
             : *reinterpret_cast<const float4*>(sTailB + r * N + n);
         const float v[4] = {a.x + e.x, a.y + e.y, a.z + e.z, a.w + e.w};
-        if (t < L) store_bc(dBg, b, t, part ? h : g, r, n, v);
+        if (t < L && r < rin) store_bc(dBg, rin, b, t, part ? h : g, r, n, v);
       }
     }
 
@@ -1448,6 +1454,9 @@ __global__ __launch_bounds__(256) void ssm_bwd_group_sum(BwdParams p, int R) {
     const long bt = r / G;  // batch * L + token
 #pragma unroll 1
     for (int which = 0; which < 2; ++which) {
+      // partials hold R rows per token; dB has rank_in rows, dC rank_out
+      const int rows = which ? p.rout : p.rin;
+      if (rr >= rows) continue;
       const T* part = static_cast<const T*>(which ? p.dCh : p.dBh);
       T* out = static_cast<T*>(which ? p.dC : p.dB);
       float v[4] = {0.f, 0.f, 0.f, 0.f};
@@ -1456,7 +1465,7 @@ __global__ __launch_bounds__(256) void ssm_bwd_group_sum(BwdParams p, int R) {
         load4<BF16>(part + ((bt * H + g * hpg + k) * R + rr) * N + n4, a);
         v[0] += a[0]; v[1] += a[1]; v[2] += a[2]; v[3] += a[3];
       }
-      store4<BF16>(out + ((bt * G + g) * R + rr) * N + n4, v);
+      store4<BF16>(out + ((bt * G + g) * rows + rr) * N + n4, v);
     }
   }
 }
@@ -1489,26 +1498,31 @@ __global__ __launch_bounds__(256) void ssm_bwd_params(BwdParams p, int nA) {
 }
 
 // ------------------------------------------------------------------ dispatch
-// (io bf16?, N, P, R, keys per token, tokens per chunk, per-row decay)
+// (io bf16?, N, P, R, keys per token, tokens per chunk, per-row decay, ranks differ)
 #define SSM_BWD_VARIANTS(X)            \
-  X(false, 16, 16, 1, 1, 64, false)    \
-  X(false, 32, 16, 1, 1, 64, false)    \
-  X(false, 32, 16, 2, 2, 32, false)    \
-  X(false, 16, 16, 1, 2, 16, true)     \
-  X(false, 32, 16, 1, 2, 16, true)     \
-  X(false, 32, 16, 2, 4, 16, true)     \
-  X(false, 32, 16, 1, 1, 32, true)     \
-  X(false, 32, 16, 2, 2, 16, true)     \
-  X(true, 64, 64, 1, 1, 64, false)     \
-  X(true, 128, 64, 1, 1, 64, false)    \
-  X(true, 64, 64, 4, 4, 16, false)     \
-  X(true, 64, 64, 1, 2, 16, true)      \
-  X(true, 64, 64, 2, 4, 16, true)
+  X(false, 16, 16, 1, 1, 64, false, false)    \
+  X(false, 32, 16, 1, 1, 64, false, false)    \
+  X(false, 32, 16, 2, 2, 32, false, false)    \
+  X(false, 16, 16, 1, 2, 16, true, false)     \
+  X(false, 32, 16, 1, 2, 16, true, false)     \
+  X(false, 32, 16, 2, 4, 16, true, false)     \
+  X(false, 32, 16, 1, 1, 32, true, false)     \
+  X(false, 32, 16, 2, 2, 16, true, false)     \
+  X(true, 64, 64, 1, 1, 64, false, false)     \
+  X(true, 128, 64, 1, 1, 64, false, false)    \
+  X(true, 64, 64, 4, 4, 16, false, false)     \
+  X(true, 64, 64, 1, 2, 16, true, false)      \
+  X(true, 64, 64, 2, 4, 16, true, false)     \
+  /* write and readout ranks that differ */ \
+  X(false, 32, 16, 2, 2, 32, false, true)    \
+  X(false, 32, 16, 2, 4, 16, true, true)     \
+  X(true, 64, 64, 4, 4, 16, false, true)     \
+  X(true, 64, 64, 2, 4, 16, true, true)
 
 bool bwd_variant_exists(const BwdKey& k) {
-#define SSM_BWD_MATCH(BF, NN, PP, RR, KRR, QTT, CO)                                          \
+#define SSM_BWD_MATCH(BF, NN, PP, RR, KRR, QTT, CO, SP)                                      \
   if (k.bf16 == BF && k.N == NN && k.P == PP && k.R == RR && k.KR == KRR && k.QT == QTT &&   \
-      k.coord == CO)                                                                         \
+      k.coord == CO && k.split == SP)                                                        \
     return true;
   SSM_BWD_VARIANTS(SSM_BWD_MATCH)
 #undef SSM_BWD_MATCH
@@ -1553,7 +1567,7 @@ static int blocks_per_cu(const void* kernel, int nthreads, std::atomic<int>& cac
 static LocalParams adj_local_params(const BwdParams& p) {
   LocalParams l{};
   l.key = p.C; l.val = p.dy; l.dt = p.dt; l.A = p.A; l.omega = p.omega;
-  l.out = p.gloc; l.delta = p.gdel;
+  l.out = p.gloc; l.delta = p.gdel; l.rk = p.rout;
   l.batch = p.batch; l.L = p.L; l.H = p.H; l.G = p.G; l.P = p.P; l.n_real = p.n_real;
   l.n_pairs = p.n_pairs; l.softplus = p.softplus; l.head_rates = p.head_rates;
   l.nseg = p.nseg; l.seg_tokens = p.seg_tokens; l.nsub = p.nsub; l.lsub = p.lsub;
@@ -1568,9 +1582,9 @@ hipError_t launch_bwd(const BwdKey& k, const BwdParams& p, hipStream_t stream,
     if (events && events[i]) (void)hipEventRecord(static_cast<hipEvent_t>(events[i]), stream);
   };
   const int nA = k.coord && !p.head_rates ? p.n_real + p.n_pairs : 1;
-#define SSM_BWD_LAUNCH(BF, NN, PP, RR, KRR, QTT, CO)                                          \
+#define SSM_BWD_LAUNCH(BF, NN, PP, RR, KRR, QTT, CO, SP)                                      \
   if (k.bf16 == BF && k.N == NN && k.P == PP && k.R == RR && k.KR == KRR && k.QT == QTT &&    \
-      k.coord == CO) {                                                                        \
+      k.coord == CO && k.split == SP) {                                                       \
     constexpr int PB = ADJ_PB(PP);                                                            \
     mark(0);                                                                                  \
     const int agrid = slices * (PP / PB) * p.nseg;                                            \
@@ -1586,10 +1600,10 @@ hipError_t launch_bwd(const BwdKey& k, const BwdParams& p, hipStream_t stream,
     {                                                                                         \
       static std::atomic<int> occ{0};                                                         \
       const void* kfn = reinterpret_cast<const void*>(                                        \
-          &ssm_bwd_chunk<BF, NN, PP, RR, KRR, QTT, CO, CHUNK_NT>);                            \
+          &ssm_bwd_chunk<BF, NN, PP, RR, KRR, QTT, CO, CHUNK_NT, SP>);                        \
       const int items = slices * p.nchunks;                                                   \
       const int grid = std::min(items, device_cus() * blocks_per_cu(kfn, CHUNK_NT, occ));      \
-      hipLaunchKernelGGL((ssm_bwd_chunk<BF, NN, PP, RR, KRR, QTT, CO, CHUNK_NT>), dim3(grid),  \
+      hipLaunchKernelGGL((ssm_bwd_chunk<BF, NN, PP, RR, KRR, QTT, CO, CHUNK_NT, SP>), dim3(grid), \
                          dim3(CHUNK_NT), 0, stream, p);                                       \
     }                                                                                         \
     if (p.dBh) {                                                                              \

@@ -174,14 +174,16 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
 
   // slice bases (64-bit once); offsets inside a slice fit in 32 bits (the host
   // rejects tensors of 2^31 or more elements)
-  const T* xg = static_cast<const T*>(p.x) + ((size_t)b * L * H + h) * R * P + p0;
-  const T* Bg = static_cast<const T*>(p.B) + ((size_t)b * L * G + g) * R * N;
-  const T* Cg = static_cast<const T*>(p.C) + ((size_t)b * L * G + g) * R * N;
-  T* yg = static_cast<T*>(p.y) + ((size_t)b * L * H + h) * R * P + p0;
+  const int rin = p.rin, rout = p.rout;
+  const T* xg = static_cast<const T*>(p.x) + ((size_t)b * L * H + h) * rin * P + p0;
+  const T* Bg = static_cast<const T*>(p.B) + ((size_t)b * L * G + g) * rin * N;
+  const T* Cg = static_cast<const T*>(p.C) + ((size_t)b * L * G + g) * rout * N;
+  T* yg = static_cast<T*>(p.y) + ((size_t)b * L * H + h) * rout * P + p0;
   const float* dtg = p.dt + (size_t)b * L * H + h;
   const float* beg = S::TE ? p.beta + (size_t)b * L * H + h : nullptr;
   const float* gag = S::TE ? p.gamma + (size_t)b * L * H + h : nullptr;
-  const int tsG = G * R * N, tsH = H * R * P;  // per-token strides
+  // per-token strides of B, C, x, y
+  const int tsB = G * rin * N, tsC = G * rout * N, tsX = H * rin * P, tsY = H * rout * P;
 
   // state tiles, transposed: st[k][i] = S[n = 16 tn + (lane & 15)][p = 16 tp + 4 (lane >> 4) + i]
   f32x4 st[S::ST_PER_WAVE];
@@ -216,17 +218,17 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
       if (u >= S::C0 && u < S::C0 + S::C_VECS) {
         const int row = (u - S::C0) / S::NVEC_N, nv = (u - S::C0) % S::NVEC_N;
         const int t = t0 + row / R, o = row % R;
-        if (t < L) val = *reinterpret_cast<const uint4*>(Cg + t * tsG + o * N + nv * VEC);
+        if (t < L && o < rout) val = *reinterpret_cast<const uint4*>(Cg + t * tsC + o * N + nv * VEC);
       } else if (u >= S::K0 && u < S::K0 + S::K_ITEMS) {
         const int v = u - S::K0;
         const int row = v / S::NVEC_N, nv = v % S::NVEC_N;
         const int t = t0 + row / R - S::TEH, r = row % R;
-        if (t >= 0 && t < L) val = *reinterpret_cast<const uint4*>(Bg + t * tsG + r * N + nv * VEC);
+        if (t >= 0 && t < L && r < rin) val = *reinterpret_cast<const uint4*>(Bg + t * tsB + r * N + nv * VEC);
       } else if (u >= S::X0 && u < S::ALL_VECS) {
         const int v = u - S::X0;
         const int row = v / S::NVEC_P, pv = v % S::NVEC_P;
         const int t = t0 + row / R - S::TEH, r = row % R;
-        if (t >= 0 && t < L) val = *reinterpret_cast<const uint4*>(xg + t * tsH + r * P + pv * VEC);
+        if (t >= 0 && t < L && r < rin) val = *reinterpret_cast<const uint4*>(xg + t * tsX + r * P + pv * VEC);
       }
       rr[k] = val;
     }
@@ -406,8 +408,8 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
     for (int v = tid; v < S::QO * S::NVEC_P; v += S::NTH) {
       const int row = v / S::NVEC_P, pv = v % S::NVEC_P;
       const int t = row / R, o = row % R;
-      if (t0 + t < L)
-        *reinterpret_cast<uint4*>(yg + (t0 + t) * tsH + o * P + pv * VEC) =
+      if (t0 + t < L && o < rout)
+        *reinterpret_cast<uint4*>(yg + (t0 + t) * tsY + o * P + pv * VEC) =
             *reinterpret_cast<const uint4*>(sYo + row * VS + pv * VEC);
     }
   };
@@ -797,7 +799,7 @@ bool fwd_variant_exists(const FwdKey& k) {
 static LocalParams local_params(const FwdParams& p) {
   LocalParams l{};
   l.key = p.B; l.val = p.x; l.dt = p.dt; l.A = p.A; l.omega = p.omega; l.beta = p.beta;
-  l.gamma = p.gamma; l.out = p.seg_local; l.delta = p.seg_delta;
+  l.gamma = p.gamma; l.out = p.seg_local; l.delta = p.seg_delta; l.rk = p.rin;
   l.batch = p.batch; l.L = p.L; l.H = p.H; l.G = p.G; l.P = p.P; l.n_real = p.n_real;
   l.n_pairs = p.n_pairs; l.softplus = p.softplus; l.head_rates = p.head_rates;
   l.nseg = p.nseg; l.seg_tokens = p.seg_tokens; l.nsub = p.nsub; l.lsub = p.lsub;

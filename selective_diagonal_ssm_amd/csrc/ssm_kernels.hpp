@@ -21,6 +21,9 @@ struct FwdParams {
   const float* h0;  // [batch][nheads][N][P] fp32 state before token 0, or null
   float* h_final;   // [batch][nheads][N][P] fp32 state after the last token, or null
   int batch, L, H, G, P, n_real, n_pairs, nchunks, npblk;
+  // ranks of the write (B, x) and of the readout (C, y); the kernel's rank R is the
+  // larger, rows past a side's own rank are zero on load and dropped on store
+  int rin, rout;
   int softplus, has_D;
   int head_rates;  // A holds one rate per head even though the per-row kernel runs
   // sequence segments (nseg = 1: one workgroup walks the whole sequence)
@@ -48,6 +51,7 @@ struct LocalParams {
   const float* gamma;
   float* out;    // [slice][nseg - 1][nsub][N][P] range states
   float* delta;  // [slice][nseg - 1][nsub] range summed steps
+  int rk;        // rows per token of key and value (rank_in forward, rank_out adjoint)
   int batch, L, H, G, P, n_real, n_pairs, softplus, head_rates;
   int nseg, seg_tokens, nsub, lsub;
 };
@@ -82,6 +86,9 @@ struct BwdParams {
   void* dBh;
   void* dCh;
   int batch, L, H, G, P, n_real, n_pairs, nchunks;
+  // ranks of the write (B, x, dB, dx) and of the readout (C, dy, dC); the kernels' rank
+  // R is the larger, rows past a side's own rank are zero on load and dropped on store
+  int rin, rout;
   int nseg, chunks_per_seg;  // sequence segments of the boundary-adjoint sweep
   int softplus, has_D, npart;
   int head_rates;
@@ -149,6 +156,7 @@ struct BwdKey {
   bool bf16;
   int N, P, R, KR, QT;
   bool coord;
+  bool split;  // rank_in != rank_out (the chunk kernel then takes both ranks at run time)
 };
 hipError_t launch_bwd(const BwdKey& key, const BwdParams& p, hipStream_t stream,
                       void* const* events);

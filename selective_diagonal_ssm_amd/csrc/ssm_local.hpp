@@ -135,9 +135,11 @@ __global__ __launch_bounds__(256) void ssm_local(LocalParams p) {
   }
   __syncthreads();
 
-  const T* Kg = static_cast<const T*>(p.key) + ((size_t)b * L * G + g) * R * N;
-  const T* Vg = static_cast<const T*>(p.val) + ((size_t)b * L * H + h) * R * P + p0;
-  const int tsG = G * R * N, tsH = H * R * P;
+  // key / value rows per token: rk <= R (rows rk .. R-1 load as zero)
+  const int rk = p.rk;
+  const T* Kg = static_cast<const T*>(p.key) + ((size_t)b * L * G + g) * rk * N;
+  const T* Vg = static_cast<const T*>(p.val) + ((size_t)b * L * H + h) * rk * P + p0;
+  const int tsG = G * rk * N, tsH = H * rk * P;
   T* kw = reinterpret_cast<T*>(smem) + wave * 32 * KS;
   T* vw = reinterpret_cast<T*>(smem) + 4 * 32 * KS + wave * 32 * VS;
   const float ah = COORD ? 0.f : p.A[h] * kLog2e;
@@ -170,8 +172,9 @@ __global__ __launch_bounds__(256) void ssm_local(LocalParams p) {
       const int tc = ok ? t : ta;
 #pragma unroll
       for (int r = 0; r < R; ++r) {
-        const uint4 val = *reinterpret_cast<const uint4*>(Kg + (size_t)tc * tsG + r * N + v * VEC);
-        rb[q][r] = keep(ok, val);
+        const int rc = r < rk ? r : 0;
+        const uint4 val = *reinterpret_cast<const uint4*>(Kg + (size_t)tc * tsG + rc * N + v * VEC);
+        rb[q][r] = keep(ok && r < rk, val);
       }
     }
 #pragma unroll
@@ -180,9 +183,9 @@ __global__ __launch_bounds__(256) void ssm_local(LocalParams p) {
       const int jr = u / PV, pv = u % PV;
       const int j = jr / R, r = jr % R;
       const int t = ta + i0 + j;
-      const bool ok = u < S::XI && i0 + j < len && t >= 0;
-      const int tc = ok ? t : ta;
-      const uint4 val = *reinterpret_cast<const uint4*>(Vg + (size_t)tc * tsH + r * P + pv * VEC);
+      const bool ok = u < S::XI && i0 + j < len && t >= 0 && r < rk;
+      const int tc = ok ? t : ta, rc = ok ? r : 0;
+      const uint4 val = *reinterpret_cast<const uint4*>(Vg + (size_t)tc * tsH + rc * P + pv * VEC);
       rx[q] = keep(ok, val);
     }
   };

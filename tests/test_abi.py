@@ -46,7 +46,9 @@ def base_desc(**kw):
     (dict(n_real=60), -2),                      # n_real + 2 n_pairs != dstate
     (dict(decay_mode="head", n_real=32, n_pairs=16), -2),  # pairs need per-row mode
     (dict(rank_in=2, rank_out=1), -2),          # D needs O == R
-    (dict(rank_in=2, rank_out=1, has_D=False), -5),  # O != R not implemented on GPU
+    (dict(rank_in=2, rank_out=1, has_D=False), 0),   # O != R without feedthrough
+    (dict(rank_in=1, rank_out=4, has_D=False), 0),
+    (dict(rank_in=8, rank_out=1, has_D=False), -5),  # widest rank the scans tile is 4
     (dict(headdim=24), -5),
     (dict(dstate=48, n_real=48), -5),
     (dict(decay_mode="coord", n_real=31, n_pairs=16, dstate=63), -5),

@@ -62,6 +62,19 @@ SMALL_CASES = {
                                              n_real=48, n_pairs=8)),
     "f32_hm_pairs_only": ("hybrid", dict(dtype="f32", dstate=32, n_real=0, n_pairs=16,
                                          headdim=16, batch=2, nheads=2, ngroups=2, seqlen=77)),
+    # write and readout widths that differ (O != R; no feedthrough then)
+    "f32_head_r2o1": ("ssd_mimo", dict(dtype="f32", dstate=32, n_real=32, headdim=16, rank_in=2,
+                                       rank_out=1, has_D=False, batch=2, nheads=2, ngroups=2,
+                                       seqlen=100)),
+    "f32_hybrid_r1o2": ("hybrid", dict(dtype="f32", dstate=32, n_real=16, n_pairs=8, headdim=16,
+                                       rank_in=1, rank_out=2, has_D=False, batch=2, nheads=2,
+                                       ngroups=2, seqlen=77)),
+    "bf16_mimo_r4o2": ("ssd_mimo", dict(batch=2, seqlen=130, nheads=2, ngroups=2, rank_in=4,
+                                        rank_out=2, has_D=False)),
+    "bf16_mimo_r1o4": ("ssd_mimo", dict(batch=2, seqlen=130, nheads=2, ngroups=2, rank_in=1,
+                                        rank_out=4, has_D=False)),
+    "bf16_hybrid_r2o1": ("hybrid", dict(batch=2, seqlen=150, nheads=4, ngroups=2, rank_in=2,
+                                        rank_out=1, has_D=False)),
 }
 
 
