@@ -274,7 +274,7 @@ int ssm_scan_fwd(const ssm_desc* d, const ssm_fwd_args* a, void* ws, size_t ws_b
   for (const void* q : {(const void*)a->saved, (const void*)a->h0, (const void*)a->h_final})
     if (q && !aligned(q, 16)) return SSM_ERR_ALIGN;
 
-  const FwdKey key = choose_fwd(d, pl);
+  FwdKey key = choose_fwd(d, pl);
   if (key.PB <= 0 || d->headdim % key.PB) return SSM_ERR_UNSUPPORTED;
   const int pb = key.PB;
   ssm::FwdParams p{};
@@ -292,6 +292,20 @@ int ssm_scan_fwd(const ssm_desc* d, const ssm_fwd_args* a, void* ws, size_t ws_b
   const Segs sg = segments((long)d->batch * d->nheads * p.npblk, pl.nchunks);
   p.nseg = sg.nseg;
   p.cps = sg.cps;
+  // A forward that keeps no boundary states may walk two chunks per step (the saved
+  // states, when asked for, follow the plan's chunk).  Two-endpoint writes only, where
+  // the shift identity keeps a double chunk's keys within the plan chunk's tiles;
+  // segment boundaries stay where they are (an even number of chunks per segment).
+  if (!a->saved && (d->flags & SSM_F_TWO_ENDPOINT) && (sg.nseg == 1 || sg.cps % 2 == 0) &&
+      env_int("SSM_FWD_SINGLE", 0) == 0) {
+    FwdKey k2 = key;
+    k2.QT = 2 * pl.QT;
+    if (ssm::fwd_variant_exists(k2)) {
+      key = k2;
+      p.nchunks = (d->seqlen + k2.QT - 1) / k2.QT;
+      p.cps = sg.nseg == 1 ? p.nchunks : sg.cps / 2;
+    }
+  }
   if (sg.nseg > 1) {
     const size_t need = fwd_segment_bytes(d, pl, key);
     if (!ws || ws_bytes < need) return SSM_ERR_WORKSPACE;

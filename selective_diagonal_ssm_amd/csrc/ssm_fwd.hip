@@ -45,9 +45,18 @@ struct FwdShape {
   static constexpr int PAD = 16 / static_cast<int>(sizeof(T));
   static constexpr int NC = N < 32 ? 32 : N;  // contraction width over n (zero padded)
   static constexpr int QO = QT * R;
-  static constexpr int QK = QT * KR;
   static constexpr bool TE = KR > R;
   static constexpr int TEH = TE ? 1 : 0;
+  // Two-endpoint writes through the shift identity h'_t = h_t - gamma_t B_t X_t:
+  //   h'_t = A_t h'_{t-1} + B^_{t-1} X_{t-1},  B^_{t-1} = (gamma_{t-1} A_t + beta_t) B_{t-1},
+  //   y_t  = C_t^T h'_t + gamma_t (C_t . B_t) X_t + D X_t,
+  // one key row per (token, rank) instead of two, plus a same-token term.  Used for
+  // 32-token chunks (the two-chunk walk of a forward without saved states), where it
+  // keeps the keys within the tiles of a 16-token chunk; at 16 tokens the two-endpoint
+  // keys [gamma_s B_s | beta_s B_{s-1}] with values [X_s ; X_{s-1}] measured faster.
+  static constexpr bool SHIFT = TE && QT >= 32 && (QT * R) % 32 == 0;
+  static constexpr int KEYS = SHIFT ? R : KR;  // key rows per token
+  static constexpr int QK = QT * KEYS;
   static constexpr int NS = NC + PAD;  // row stride of n-contiguous buffers
   static constexpr int KS = QK + PAD;  // row stride of key-contiguous buffers (scores)
   static constexpr int VS = PB + PAD;  // row stride of p-contiguous buffers (values, state)
@@ -82,9 +91,9 @@ struct FwdShape {
   static constexpr int YBP = YBLK ? 2 : 1;
   static constexpr int ST_PER_WAVE = (ST_TILES + NW - 1) / NW;
   // score tiles (16 query rows ti x 16 keys tj) that hold at least one causal
-  // entry: key token floor(16 tj / KR) <= query token floor((16 ti + 15) / R)
+  // entry: key token floor(16 tj / KEYS) <= query token floor((16 ti + 15) / R)
   static constexpr int row_tiles(int ti) {
-    const int c = (((16 * ti + 15) / R) * KR) / 16 + 1;
+    const int c = (((16 * ti + 15) / R) * KEYS) / 16 + 1;
     return c < TK ? c : TK;
   }
   static constexpr int score_tiles() {
@@ -96,7 +105,7 @@ struct FwdShape {
   static_assert(QO % 16 == 0 && QK % 32 == 0, "chunk rows must fill MFMA tiles");
   static_assert(N % 16 == 0 && PB % 16 == 0 && QT <= 64, "unsupported tile shape");
   static_assert(KR == R || KR == 2 * R, "keys per token are R or 2R");
-  static_assert(16 % KR == 0 && 16 % R == 0, "a tile spans whole tokens");
+  static_assert(16 % KEYS == 0 && 16 % R == 0, "a tile spans whole tokens");
 };
 
 template <bool BF16, int N, int PB, int R, int KR, int QT, bool COORD, int NTHREADS>
@@ -123,12 +132,21 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
   __shared__ __align__(16) float sCD[4][TC];   // per-row decay: cumulative step inside the chunk
   __shared__ __align__(16) float sLC[4][TH];   // head: -A CD log2(e), so e^{L_t - L_s} = 2^{LC_t - LC_s}
   __shared__ __align__(16) float sDT[2][64];   // steps Delta of chunk c in slot c & 1
-  __shared__ __align__(16) float sGa[2][S::TE ? 64 : 1], sBe[2][S::TE ? 64 : 1];  // chunk c: c & 1
+  // beta / gamma of chunk c in slot c & 3 (a chunk's readout still reads its own after the
+  // next-but-one chunk's are staged)
+  __shared__ __align__(16) float sGa[4][S::TE ? 64 : 1], sBe[4][S::TE ? 64 : 1];
   __shared__ float sMisc[4][2];                // CD_end, head: e^{-A CD_end}
   __shared__ float sRate[COORD ? N : 1], sOmega[COORD ? N / 2 + 1 : 1];
   // per-row decay: factor tables of the next chunk to stage, [token][n] (see tables)
   __shared__ __align__(16) float sTC[COORD ? QT * N : 4], sTK0[COORD ? QT * N : 4];
-  __shared__ __align__(16) float sTK1[COORD && S::TE ? QT * N : 4];
+  __shared__ __align__(16) float sTK1[COORD && S::TE && !S::SHIFT ? QT * N : 4];
+  // shift identity: raw C and B rows of the chunk (for the same-token products
+  // C_t . B_t), the last token's X rows (by operand buffer), those products, and gamma
+  // of the token before the chunk
+  constexpr bool SH = S::SHIFT;
+  __shared__ __align__(16) T sCraw[SH ? S::QO * NS : 8], sBraw[SH ? QT * R * NS : 8];
+  __shared__ __align__(16) T sXl[SH ? 2 * R * VS : 8];
+  __shared__ __align__(16) float sDG[SH ? S::QO * R : 4];
   __shared__ __align__(16) T sYo[S::QO * VS];                 // output rows of the previous chunk
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -168,6 +186,12 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
       const int r = i / (S::NC - N), c = N + i % (S::NC - N);
       sK[r * NS + c] = T(0);
     }
+    if (SH)
+      for (int i = tid; i < S::QO * (S::NC - N); i += S::NTH) {
+        const int r = i / (S::NC - N), c = N + i % (S::NC - N);
+        sCraw[r * NS + c] = T(0);
+        sBraw[r * NS + c] = T(0);
+      }
   }
   const float Ah = COORD ? 0.f : p.A[h];
   const float Dh = p.has_D ? p.D[h] : 0.f;
@@ -185,6 +209,20 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
   // per-token strides of B, C, x, y
   const int tsB = G * rin * N, tsC = G * rout * N, tsX = H * rin * P, tsY = H * rout * P;
 
+  // shift identity: the state carried inside the kernel is h' = h - gamma B X of the
+  // last token; a later segment's incoming state (h) loses gamma_{t0-1} B_{t0-1} X_{t0-1}
+  const int tfirst = c0 * QT;
+  const float gprev0 = (SH && tfirst > 0) ? gag[(size_t)(tfirst - 1) * H] : 0.f;
+  auto shift_corr = [&](int n, int col) {
+    float v = 0.f;
+    if (SH && tfirst > 0) {
+      for (int r = 0; r < rin; ++r)
+        v += to_f32(Bg[(size_t)(tfirst - 1) * tsB + r * N + n]) * to_f32(xg[(size_t)(tfirst - 1) * tsX + r * P + col]);
+      v *= gprev0;
+    }
+    return v;
+  };
+
   // state tiles, transposed: st[k][i] = S[n = 16 tn + (lane & 15)][p = 16 tp + 4 (lane >> 4) + i]
   f32x4 st[S::ST_PER_WAVE];
 #pragma unroll
@@ -195,6 +233,8 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
       const int n = 16 * (tile / S::TP) + (lane & 15), pl = 16 * (tile % S::TP) + 4 * (lane >> 4);
       const float4 v = *reinterpret_cast<const float4*>(h0s + n * P + pl);
       st[k] = f32x4{v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) st[k][i] -= shift_corr(n, pl + i);
     }
   }
   // take the h0 loads here: left pending into the chunk loop, they would make the
@@ -271,13 +311,20 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
   //            writes, else 1),   TK1[t] = beta_t / E_t, likewise.
   // A staged element is then one multiply (real rows) or one 2 x 2 product (pairs):
   //   q = R(-Theta_t) C_t E_t,  k = R(-Theta_s) (g B) / E_s.
-  auto tables = [&](int c) {
-    const int sc = c & 3, sg = c & 1;
+  // With the shift identity the key table is TK0 = TK1[t] + TK0[t-1] (the key at t
+  // carries B_{t-1}), where the entry at t = -1 is gamma of the token before the chunk
+  // (gprev) at CD = 0, Theta = 0.
+  auto tables = [&](int c, float gprev) {
+    const int sc = c & 3, sg = c & 3;
     const float hc = 0.5f * sMisc[sc][0];
     for (int i = tid; i < QT * (N / 2); i += S::NTH) {
       const int t = i / (N / 2), n = 2 * (i % (N / 2));
       const float cd = sCD[sc][t] - hc;
       const float g0 = S::TE ? sGa[sg][t] : 1.f, g1 = S::TE ? sBe[sg][t] : 0.f;
+      // shift identity: gamma and the factors of the token before
+      const float cdm = t > 0 ? sCD[sc][t - 1] : 0.f;
+      float gm = 0.f;
+      if constexpr (SH) gm = t > 0 ? sGa[sg][t - 1] : gprev;
       float2 tc, tk0, tk1;
       if (n >= nreal) {
         const float x = sRate[n] * cd;
@@ -287,16 +334,25 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
         tc = make_float2(e * cs, e * sn);
         tk0 = make_float2(g0 * ei * cs, g0 * ei * sn);
         tk1 = make_float2(g1 * ei * cs, g1 * ei * sn);
+        if (SH) {
+          const float eim = __expf(sRate[n] * (cdm - hc));
+          float snm, csm;
+          fast_sincos(sOmega[(n - nreal) >> 1] * cdm, &snm, &csm);
+          tk0 = make_float2(tk1.x + gm * eim * csm, tk1.y + gm * eim * snm);
+        }
       } else {
         const float x0 = sRate[n] * cd, x1 = sRate[n + 1] * cd;
         const float ei0 = __expf(x0), ei1 = __expf(x1);
         tc = make_float2(__expf(-x0), __expf(-x1));
         tk0 = make_float2(g0 * ei0, g0 * ei1);
         tk1 = make_float2(g1 * ei0, g1 * ei1);
+        if (SH)
+          tk0 = make_float2(tk1.x + gm * __expf(sRate[n] * (cdm - hc)),
+                            tk1.y + gm * __expf(sRate[n + 1] * (cdm - hc)));
       }
       *reinterpret_cast<float2*>(sTC + t * N + n) = tc;
       *reinterpret_cast<float2*>(sTK0 + t * N + n) = tk0;
-      if (S::TE) *reinterpret_cast<float2*>(sTK1 + t * N + n) = tk1;
+      if (S::TE && !SH) *reinterpret_cast<float2*>(sTK1 + t * N + n) = tk1;
     }
   };
 
@@ -330,8 +386,8 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
     if (wave == PW && lane < 64) {
       sDT[c & 1][lane] = p.softplus ? softplus_f32(rdt) : rdt;
       if (S::TE) {
-        sGa[(c + 1) & 1][lane] = rga;
-        sBe[(c + 1) & 1][lane] = rbe;
+        sGa[(c + 1) & 3][lane] = rga;
+        sBe[(c + 1) & 3][lane] = rbe;
       }
     }
     const int sc = c & 3;
@@ -351,6 +407,7 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
           unpack<BF16>(rr[k], vals);
           apply_table(vals, sTC + t * N, n0);
           *reinterpret_cast<uint4*>(q + row * NS + n0) = pack<BF16>(vals);
+          if (SH) *reinterpret_cast<uint4*>(sCraw + row * NS + n0) = rr[k];
         } else {
           *reinterpret_cast<uint4*>(q + row * NS + n0) = rr[k];
         }
@@ -365,6 +422,15 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
         }
         float bv[VEC];
         unpack<BF16>(rr[k], bv);
+        if constexpr (SH) {
+          // the key at s = sl + 1 carries B_sl; the raw row feeds C_t . B_t
+          if (sl + 1 < QT) {
+            apply_table(bv, sTK0 + (sl + 1) * N, n0);
+            *reinterpret_cast<uint4*>(kb + ((sl + 1) * R + r) * NS + n0) = pack<BF16>(bv);
+          }
+          if (sl >= 0) *reinterpret_cast<uint4*>(sBraw + (sl * R + r) * NS + n0) = rr[k];
+          continue;
+        }
         // e = 0: gamma_s B_s written at s = sl; e = 1: beta_{s+1} B_s written at s+1
 #pragma unroll
         for (int e = 0; e < 1 + S::TEH; ++e) {
@@ -381,6 +447,12 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
         const int v = u - S::X0;
         const int row = v / S::NVEC_P, pv = v % S::NVEC_P;
         const int sl = row / R - S::TEH, r = row % R;
+        if constexpr (SH) {
+          // X_sl is the value of the key at sl + 1; the last token's goes aside
+          if (sl + 1 < QT) *reinterpret_cast<uint4*>(vb + ((sl + 1) * R + r) * VS + pv * VEC) = rr[k];
+          else *reinterpret_cast<uint4*>(sXl + (bi * R + r) * VS + pv * VEC) = rr[k];
+          continue;
+        }
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
           if (e == 1 && !S::TE) break;
@@ -414,6 +486,26 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
     }
   };
 
+  // shift identity: h = h' + gamma_t B_t X_t with t the last token of chunk c (operand
+  // buffer bi), for four columns pl.. of state row n.  A chunk cut by the sequence end
+  // already holds that write: the key at t + 1 (past the end, where beta = 0 and the
+  // transition is the identity) carries it.
+  auto add_last_write = [&](float* v, int c, int bi, int n, int pl) {
+    if constexpr (SH) {
+      if ((c + 1) * QT > L) return;
+      const int tl = QT - 1;
+      const float gl = sGa[c & 3][tl];
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        float xv[4];
+        load4<BF16>(sXl + (bi * R + r) * VS + pl, xv);
+        const float bw = gl * to_f32(sBraw[(tl * R + r) * NS + n]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] += bw * xv[i];
+      }
+    }
+  };
+
   const int nch = p.nchunks;
   const size_t sl_saved = (size_t)slice * (nch + 1);
   T* saved = static_cast<T*>(p.saved);  // chunk-boundary states, stored in the io dtype
@@ -435,8 +527,8 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
       const float raw = ok ? dtg[t * H] : 0.f;
       if (c0 + a < c1) factors(c0 + a, ok ? (p.softplus ? softplus_f32(raw) : raw) : 0.f);
       if (S::TE && a == 0) {
-        sBe[c0 & 1][lane] = ok ? beg[t * H] : 0.f;
-        sGa[c0 & 1][lane] = ok ? gag[t * H] : 0.f;
+        sBe[c0 & 3][lane] = ok ? beg[t * H] : 0.f;
+        sGa[c0 & 3][lane] = ok ? gag[t * H] : 0.f;
       }
     }
   }
@@ -446,12 +538,12 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
     const float hc0 = 0.5f * sMisc[c0 & 3][0];
     for (int i = tid; i < 2 * S::NC * VS; i += S::NTH) {
       const int n = i / VS, col = i % VS;
-      float v = (h0s && n < N && col < PB) ? h0s[n * P + col] : 0.f;
+      float v = (h0s && n < N && col < PB) ? h0s[n * P + col] - shift_corr(n, col) : 0.f;
       if (COORD && n < N) v *= __expf(-sRate[n] * hc0);
       sST[i] = from_f32<T>(v);
     }
   }
-  if (COORD) tables(c0);
+  if (COORD) tables(c0, gprev0);
   __syncthreads();
   stage(c0, 0);
   if (c0 + 1 < c1) load_chunk(c0 + 1);
@@ -492,16 +584,34 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
       float val[4];
       if (COORD) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) val[i] = ((j0 + i) / KR <= t) ? acc[i] : 0.f;
+        for (int i = 0; i < 4; ++i) val[i] = ((j0 + i) / S::KEYS <= t) ? acc[i] : 0.f;
       } else {
         const float lt = sLC[sc][t];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int s = (j0 + i) / KR;
+          const int s = (j0 + i) / S::KEYS;
           val[i] = (s <= t) ? acc[i] * __builtin_amdgcn_exp2f(lt - sLC[sc][s]) : 0.f;
         }
       }
       store4<BF16>(sS + row * KS + j0, val);
+    }
+    if constexpr (SH) {
+      // same-token products C_t[o] . B_t[r] (raw rows): the diagonal tiles of C B^T,
+      // one per query tile, from the wave below the factor wave down
+      for (int ti = (2 * NW - 2 - wave) % NW; ti < S::TQ; ti += NW) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < S::NC / 32; ++kk) {
+          const auto fb = load_frag<BF16>(sBraw + (16 * ti + (lane & 15)) * NS + kk * 32 + 8 * (lane >> 4));
+          const auto fc = load_frag<BF16>(sCraw + (16 * ti + (lane & 15)) * NS + kk * 32 + 8 * (lane >> 4));
+          mma<BF16>(acc, fb, fc);
+        }
+        // lane: query row 16 ti + (lane & 15), key rows 16 ti + 4 (lane >> 4) + i
+        const int row = 16 * ti + (lane & 15), j0 = 16 * ti + 4 * (lane >> 4);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if ((j0 + i) / R == row / R) sDG[row * R + (j0 + i) % R] = acc[i];
+      }
     }
     // a4/a5: state update of chunk c (needs only this chunk's keys / values and the
     // state entering it); its bf16 copy is the readout operand of chunk c+1.
@@ -570,14 +680,23 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
           st[k] = acc[k];
           // the new state is the readout operand of chunk c+1 (other buffer)
           const int pl = 16 * tp + 4 * (lane >> 4);
-          const float v4[4] = {acc[k][0], acc[k][1], acc[k][2], acc[k][3]};
+          float v4[4] = {acc[k][0], acc[k][1], acc[k][2], acc[k][3]};
           const float r4[4] = {sst * acc[k][0], sst * acc[k][1], sst * acc[k][2], sst * acc[k][3]};
           store4<BF16>(sST + (bi ^ 1) * S::NC * VS + n * VS + pl, COORD ? r4 : v4);
-          if (saved) store4<BF16>(saved + ((sl_saved + c + 1) * N + n) * P + p0 + pl, v4);
+          if (saved) {
+            if (SH) add_last_write(v4, c, bi, n, pl);  // saved states are h, not h'
+            store4<BF16>(saved + ((sl_saved + c + 1) * N + n) * P + p0 + pl, v4);
+          }
         }
       }
     }
-    if (COORD && c + 1 < c1) tables(c + 1);
+    if constexpr (COORD) {
+      if (c + 1 < c1) {
+        float gp = 0.f;  // shift identity: gamma of this chunk's last token
+        if constexpr (SH) gp = sGa[c & 3][QT - 1];
+        tables(c + 1, gp);
+      }
+    }
     if (wave == PW && c + 2 < c1) factors(c + 2, (lane < QT && (c + 2) * QT + lane < L) ? sDT[c & 1][lane] : 0.f);
     __syncthreads();
 
@@ -632,7 +751,7 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
         // intra-chunk part: keys up to the block's last query token (the lower query
         // tiles see zero scores past their own diagonal)
         const int tmax = (16 * (ti0 + BQ - 1) + 15) / R;
-        const int kend = ((tmax + 1) * KR + 31) / 32;
+        const int kend = ((tmax + 1) * S::KEYS + 31) / 32;
         for (int kk = 0; kk < kend; ++kk) {
           Frag<BF16> fv[BP], fsc[BQ];
 #pragma unroll
@@ -654,9 +773,27 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
           for (int bb = 0; bb < BP; ++bb) {
             const int pl = 16 * (tp0 + bb) + 4 * (lane >> 4);
             float val[4] = {acc[a][bb][0], acc[a][bb][1], acc[a][bb][2], acc[a][bb][3]};
+            // X_t of rank r: a value row of this chunk (shift identity: the key at t + 1,
+            // or the last token's rows set aside)
+            auto xrow = [&](int r) -> const T* {
+              if (!SH) return vb + (t * KR + r) * VS + pl;
+              return t + 1 < QT ? vb + ((t + 1) * R + r) * VS + pl : sXl + (bi * R + r) * VS + pl;
+            };
+            if constexpr (SH) {
+              // same-token term gamma_t (C_t . B_t) X_t
+              const float gt = sGa[c & 3][t];
+#pragma unroll
+              for (int r = 0; r < R; ++r) {
+                float xv[4];
+                load4<BF16>(xrow(r), xv);
+                const float w = gt * sDG[row * R + r];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) val[i] += w * xv[i];
+              }
+            }
             if (p.has_D) {
               float xv[4];
-              load4<BF16>(vb + (t * KR + o) * VS + pl, xv);
+              load4<BF16>(xrow(o), xv);
 #pragma unroll
               for (int i = 0; i < 4; ++i) val[i] += Dh * xv[i];
             }
@@ -676,7 +813,9 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
       const int tile = wave * S::ST_PER_WAVE + k;
       if (tile < S::ST_TILES) {
         const int n = 16 * (tile / S::TP) + (lane & 15), pl = 16 * (tile % S::TP) + 4 * (lane >> 4);
-        *reinterpret_cast<float4*>(hf + n * P + pl) = make_float4(st[k][0], st[k][1], st[k][2], st[k][3]);
+        float v[4] = {st[k][0], st[k][1], st[k][2], st[k][3]};
+        if (SH) add_last_write(v, c1 - 1, (c1 - 1 - c0) & 1, n, pl);
+        *reinterpret_cast<float4*>(hf + n * P + pl) = make_float4(v[0], v[1], v[2], v[3]);
       }
     }
   }
@@ -783,7 +922,22 @@ __global__ __launch_bounds__(256) void ssm_fwd_combine(FwdParams p, int per_row)
   X(true, 64, 16, 2, 4, 16, true, 512)     \
   X(true, 64, 64, 1, 2, 16, true, 1024)    \
   X(true, 64, 32, 1, 2, 16, true, 1024)    \
-  X(true, 64, 16, 1, 2, 16, true, 1024)
+  X(true, 64, 16, 1, 2, 16, true, 1024)    \
+  /* two-endpoint writes, two chunks per step (forward without saved states) */ \
+  X(false, 16, 16, 1, 2, 32, true, 256)    \
+  X(false, 32, 16, 1, 2, 32, true, 256)    \
+  X(false, 32, 16, 2, 4, 32, true, 256)    \
+  X(true, 32, 16, 1, 2, 32, true, 256)     \
+  X(true, 64, 16, 1, 2, 32, true, 256)     \
+  X(true, 64, 16, 2, 4, 32, true, 256)     \
+  X(true, 64, 32, 2, 4, 32, true, 256)     \
+  X(true, 64, 64, 2, 4, 32, true, 1024)    \
+  X(true, 64, 32, 2, 4, 32, true, 1024)    \
+  X(true, 64, 16, 2, 4, 32, true, 1024)    \
+  X(true, 64, 16, 2, 4, 32, true, 512)     \
+  X(true, 64, 64, 1, 2, 32, true, 1024)    \
+  X(true, 64, 32, 1, 2, 32, true, 1024)    \
+  X(true, 64, 16, 1, 2, 32, true, 1024)
 
 bool fwd_variant_exists(const FwdKey& k) {
 #define SSM_FWD_MATCH(BF, NN, PBB, RR, KRR, QTT, CO, NT)                                     \

@@ -158,3 +158,38 @@ def test_sequence_segments_match_oracle(case, nseg, monkeypatch):
               " ".join(f"{k}={v:.2e}" for k, v in errs.items()), flush=True)
         bad = {k: v for k, v in errs.items() if not v <= tol(pd)}
         assert not bad, bad
+
+
+# two-endpoint forwards without saved states walk two chunks per step; segment
+# boundaries at an even number of chunks (16 tokens each) keep that path
+DOUBLE_CASES = {
+    "f32_hybrid": ("hybrid", dict(dtype="f32", dstate=32, n_real=16, n_pairs=8, headdim=16,
+                                  batch=1, nheads=2, ngroups=2, seqlen=501)),
+    "bf16_hybrid": ("hybrid", dict(batch=1, seqlen=501, nheads=2, ngroups=2)),
+    "bf16_hybrid_r1": ("hybrid_r1", dict(batch=1, seqlen=250, nheads=2, ngroups=2)),
+}
+
+
+@pytest.mark.parametrize("nseg", [1, 2, 4])
+@pytest.mark.parametrize("case", sorted(DOUBLE_CASES))
+def test_double_chunk_forward_matches_oracle(case, nseg, monkeypatch):
+    """The two-chunk forward (no saved states) with h0 and sequence segments gives the
+    oracle's outputs and final state, and agrees with the one-chunk walk."""
+    monkeypatch.setenv("SSM_NSEG", str(nseg))
+    name, kw = DOUBLE_CASES[case]
+    prob = workloads.make_problem(workloads.spec(name, **kw), seed=23)
+    h0 = workloads.make_state(prob["desc"], seed=29)
+    print(f"[double] case={case} nseg={nseg} desc={prob['desc']}", flush=True)
+    t = workloads.to_device(prob)
+    h0t = torch.from_numpy(h0).cuda()
+    y, _, hf = _fwd(prob, t, h0=h0t)
+    monkeypatch.setenv("SSM_FWD_SINGLE", "1")
+    y1, _, hf1 = _fwd(prob, t, h0=h0t)
+    torch.cuda.synchronize()
+    yr, hr = oracle.fwd(prob, h0=h0.astype(np.float64))
+    ey, eh = rel_l2(_np(y), yr), rel_l2(_np(hf), hr)
+    e1, eh1 = rel_l2(_np(y), _np(y1)), rel_l2(_np(hf), _np(hf1))
+    print(f"[double] case={case} nseg={nseg} y={ey:.2e} h_final={eh:.2e} vs one-chunk "
+          f"y={e1:.2e} h_final={eh1:.2e}", flush=True)
+    assert ey <= tol(prob) and eh <= tol(prob), (ey, eh)
+    assert e1 <= tol(prob) and eh1 <= tol(prob), (e1, eh1)
