@@ -521,6 +521,8 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
   Raw4 zr4;
   if constexpr (BF16) zr4 = make_uint2(0, 0); else zr4 = make_float4(0.f, 0.f, 0.f, 0.f);
   float pf_dt = 0.f, pf_be = 0.f, pf_ga = 0.f, pf_dtn = 0.f, pf_bn = 0.f;
+  // per-row decay: the item's rate of row tid (tid < N) or frequency of pair tid - N
+  float pf_rate = 0.f;
   const uint4 zero4 = make_uint4(0, 0, 0, 0);
 
   // The loads of an item, in four parts (C / B rows, X / dy rows and the per-token
@@ -621,6 +623,15 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
       pf_dtn = p.dt[idx];
       if (S::TE) pf_bn = p.beta[idx];
     }
+    if (COORD) {
+      const int na = nreal + npairs;
+      pf_rate = 0.f;
+      if (tid < N)
+        pf_rate = p.head_rates ? p.A[h]
+                  : p.A[(size_t)h * na + (tid < nreal ? tid : nreal + ((tid - nreal) >> 1))];
+      else if (tid < N + npairs)
+        pf_rate = p.omega[(size_t)h * npairs + tid - N];
+    }
   };
 
   // The per-token scalar gradients and the parameter partials of an item are
@@ -663,15 +674,9 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
 
     if (!RELAXED) __syncthreads();  // the previous item is done with every shared buffer
     if (COORD) {
-      const int na = nreal + npairs;
-      for (int n = tid; n < N; n += S::NTH) {
-        float r;
-        if (p.head_rates) r = p.A[h];
-        else if (n < nreal) r = p.A[(size_t)h * na + n];
-        else r = p.A[(size_t)h * na + nreal + ((n - nreal) >> 1)];
-        sRate[n] = r;
-      }
-      for (int k = tid; k < npairs; k += S::NTH) sOmega[k] = p.omega[(size_t)h * npairs + k];
+      // rates and pair frequencies arrived with the item's prefetched operands
+      if (tid < N) sRate[tid] = pf_rate;
+      else if (tid < N + npairs) sOmega[tid - N] = pf_rate;
     }
     if (!RELAXED) {
       for (int i = tid; i < WC * 64; i += S::NTH) (&sTok[0][0])[i] = 0.f;
