@@ -127,7 +127,8 @@ typedef struct {
   const float *h0;  /* optional: state before token 0 (NULL = zero) */
   float *h_final;   /* optional: receives the state after the last token */
   void *const *events; /* optional: 2 hipEvent_t recorded on `stream` before and after
-                          the kernel (per-kernel timing); NULL = none */
+                          the kernel (per-kernel timing); NULL = none, and a NULL entry
+                          is not recorded */
 } ssm_fwd_args;
 
 typedef struct {
@@ -139,7 +140,8 @@ typedef struct {
   float *dh0;       /* optional: receives dLoss/dh0 */
   void *const *events; /* optional: 4 hipEvent_t recorded on `stream` around the three
                           kernels of the pass (boundary adjoints, chunk gradients,
-                          parameter sums); NULL = none */
+                          parameter sums); NULL = none, and a NULL entry is not
+                          recorded */
 } ssm_bwd_args;
 
 /* Library ABI version (SSM_ABI_VERSION of the build). */

@@ -128,10 +128,11 @@ def workspace_bytes(desc: SsmDesc, for_backward: bool) -> int:
 
 def _events(events):
     """ctypes array of hipEvent_t handles from torch.cuda.Event objects (recorded once
-    beforehand so that the handles exist), or None."""
+    beforehand so that the handles exist; a None entry is not recorded), or None."""
     if not events:
         return None, None
-    arr = (ctypes.c_void_p * len(events))(*[ctypes.c_void_p(e.cuda_event) for e in events])
+    arr = (ctypes.c_void_p * len(events))(
+        *[ctypes.c_void_p(None if e is None else e.cuda_event) for e in events])
     return ctypes.cast(arr, ctypes.c_void_p), arr
 
 

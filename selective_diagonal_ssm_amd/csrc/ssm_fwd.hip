@@ -106,6 +106,7 @@ struct FwdShape {
   static_assert(N % 16 == 0 && PB % 16 == 0 && QT <= 64, "unsupported tile shape");
   static_assert(KR == R || KR == 2 * R, "keys per token are R or 2R");
   static_assert(16 % KEYS == 0 && 16 % R == 0, "a tile spans whole tokens");
+  static_assert(N <= NTHREADS, "one thread per state row in the prologue");
 };
 
 template <bool BF16, int N, int PB, int R, int KR, int QT, bool COORD, int NTHREADS>
@@ -159,40 +160,20 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
   const int L = p.L, H = p.H, G = p.G, P = p.P;
   const int nreal = p.n_real;
 
+  // per-row rates (thread n < N) and pair frequencies (thread k < n_pairs): read first,
+  // written to LDS once the prologue's other reads are in flight
+  float r_rate = 0.f, r_om = 0.f;
   if (COORD) {
     const int na = p.n_real + p.n_pairs;
-    for (int n = tid; n < N; n += S::NTH) {
-      float r;
-      if (p.head_rates) r = p.A[h];  // one rate per head
-      else if (n < nreal) r = p.A[(size_t)h * na + n];
-      else r = p.A[(size_t)h * na + nreal + ((n - nreal) >> 1)];
-      sRate[n] = r;
-    }
-    for (int k = tid; k < p.n_pairs; k += S::NTH) sOmega[k] = p.omega[(size_t)h * p.n_pairs + k];
+    if (tid < N)
+      r_rate = p.head_rates ? p.A[h]  // one rate per head
+                            : p.A[(size_t)h * na + (tid < nreal ? tid : nreal + ((tid - nreal) >> 1))];
+    if (tid < p.n_pairs) r_om = p.omega[(size_t)h * p.n_pairs + tid];
   }
-  // the state entering chunk 0 is zero, and so are its padding rows n >= N for good;
-  // score entries above the causal diagonal are zero and never rewritten
-  // buffer 0 holds the state entering the first chunk: h0 (rows < N, this P-block),
-  // the combined state entering a later segment, or zero
+  // the state entering the first chunk: h0 (rows < N, this P-block), the combined
+  // state entering a later segment, or zero
   const float* h0s = seg == 0 ? (p.h0 ? p.h0 + (size_t)slice * N * P + p0 : nullptr)
                               : p.seg_in + ((size_t)slice * p.nseg + seg) * N * P + p0;
-  for (int i = tid; i < S::QO * KS; i += S::NTH) sS[i] = T(0);
-  if (S::NC > N) {
-    for (int i = tid; i < 2 * S::QO * (S::NC - N); i += S::NTH) {
-      const int r = i / (S::NC - N), c = N + i % (S::NC - N);
-      sQ[r * NS + c] = T(0);
-    }
-    for (int i = tid; i < 2 * S::QK * (S::NC - N); i += S::NTH) {
-      const int r = i / (S::NC - N), c = N + i % (S::NC - N);
-      sK[r * NS + c] = T(0);
-    }
-    if (SH)
-      for (int i = tid; i < S::QO * (S::NC - N); i += S::NTH) {
-        const int r = i / (S::NC - N), c = N + i % (S::NC - N);
-        sCraw[r * NS + c] = T(0);
-        sBraw[r * NS + c] = T(0);
-      }
-  }
   const float Ah = COORD ? 0.f : p.A[h];
   const float Dh = p.has_D ? p.D[h] : 0.f;
 
@@ -225,23 +206,6 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
 
   // state tiles, transposed: st[k][i] = S[n = 16 tn + (lane & 15)][p = 16 tp + 4 (lane >> 4) + i]
   f32x4 st[S::ST_PER_WAVE];
-#pragma unroll
-  for (int k = 0; k < S::ST_PER_WAVE; ++k) {
-    st[k] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const int tile = wave * S::ST_PER_WAVE + k;
-    if (h0s && tile < S::ST_TILES) {
-      const int n = 16 * (tile / S::TP) + (lane & 15), pl = 16 * (tile % S::TP) + 4 * (lane >> 4);
-      const float4 v = *reinterpret_cast<const float4*>(h0s + n * P + pl);
-      st[k] = f32x4{v.x, v.y, v.z, v.w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) st[k][i] -= shift_corr(n, pl + i);
-    }
-  }
-  // take the h0 loads here: left pending into the chunk loop, they would make the
-  // compiler wait on every outstanding memory operation before each state update
-#pragma unroll
-  for (int k = 0; k < S::ST_PER_WAVE; ++k) asm volatile("" : "+v"(st[k]));
-
   // The operand vectors of a chunk form one item list -- C rows, B rows (key items)
   // and X rows, 16 bytes each, in the order of FwdShape -- dealt round-robin over all
   // threads, so that every wave takes a share of the staging.
@@ -509,38 +473,109 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
   const int nch = p.nchunks;
   const size_t sl_saved = (size_t)slice * (nch + 1);
   T* saved = static_cast<T*>(p.saved);  // chunk-boundary states, stored in the io dtype
-  if (saved && seg == 0) {
-    // slot 0: the state entering chunk 0
-    for (int i = tid; i < N * PB; i += S::NTH) {
-      const int n = i / PB, pl = i % PB;
-      saved[(sl_saved * N + n) * P + p0 + pl] = from_f32<T>(h0s ? h0s[n * P + pl] : 0.f);
+
+  // prologue.  The global reads come first -- the factor wave's steps of the first two
+  // chunks and beta / gamma of the first, the first chunk's operands, the incoming
+  // state -- and are waited for before the first barrier.
+  float dt0 = 0.f, dt1 = 0.f, be0 = 0.f, ga0 = 0.f;
+  if (wave == PW) {
+    const int ta = c0 * QT + lane, tb = ta + QT;
+    if (lane < QT && ta < L) {
+      dt0 = dtg[ta * H];
+      if (S::TE) {
+        be0 = beg[ta * H];
+        ga0 = gag[ta * H];
+      }
+    }
+    if (lane < QT && tb < L) dt1 = dtg[tb * H];
+  }
+  load_chunk(c0);
+#pragma unroll
+  for (int k = 0; k < S::ST_PER_WAVE; ++k) {
+    st[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int tile = wave * S::ST_PER_WAVE + k;
+    if (h0s && tile < S::ST_TILES) {
+      const int n = 16 * (tile / S::TP) + (lane & 15), pl = 16 * (tile % S::TP) + 4 * (lane >> 4);
+      const float4 v = *reinterpret_cast<const float4*>(h0s + n * P + pl);
+      st[k] = f32x4{v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) st[k][i] -= shift_corr(n, pl + i);
     }
   }
-
-  // prologue: the factors of the first two chunks, beta / gamma of the first, the
-  // readout copy of the incoming state, then the first chunk's staging
-  if (wave == PW) {
+  // score entries above the causal diagonal are zero and never rewritten; so are the
+  // operands' padding columns n >= N
+  {
+    uint4* z = reinterpret_cast<uint4*>(sS);
+    for (int i = tid; i < S::QO * KS * (int)sizeof(T) / 16; i += S::NTH) z[i] = zero4;
+  }
+  if (S::NC > N) {
+    for (int i = tid; i < 2 * S::QO * (S::NC - N); i += S::NTH) {
+      const int r = i / (S::NC - N), c = N + i % (S::NC - N);
+      sQ[r * NS + c] = T(0);
+    }
+    for (int i = tid; i < 2 * S::QK * (S::NC - N); i += S::NTH) {
+      const int r = i / (S::NC - N), c = N + i % (S::NC - N);
+      sK[r * NS + c] = T(0);
+    }
+    if (SH)
+      for (int i = tid; i < S::QO * (S::NC - N); i += S::NTH) {
+        const int r = i / (S::NC - N), c = N + i % (S::NC - N);
+        sCraw[r * NS + c] = T(0);
+        sBraw[r * NS + c] = T(0);
+      }
+  }
+  // the readout copy's second buffer, padding rows and padding columns start at zero
+  {
+    uint4* z = reinterpret_cast<uint4*>(sST + S::NC * VS);
+    for (int i = tid; i < S::NC * VS * (int)sizeof(T) / 16; i += S::NTH) z[i] = zero4;
+    for (int i = tid; i < (S::NC - N) * VS; i += S::NTH) sST[N * VS + i] = T(0);
+    for (int i = tid; i < N * (VS - PB); i += S::NTH) sST[(i / (VS - PB)) * VS + PB + i % (VS - PB)] = T(0);
+  }
+  // take the incoming state here: left pending into the chunk loop, its loads would
+  // make the compiler wait on every outstanding memory operation before each state
+  // update
 #pragma unroll
-    for (int a = 0; a < 2; ++a) {
-      const int t = (c0 + a) * QT + lane;
-      const bool ok = lane < QT && t < L;
-      const float raw = ok ? dtg[t * H] : 0.f;
-      if (c0 + a < c1) factors(c0 + a, ok ? (p.softplus ? softplus_f32(raw) : raw) : 0.f);
-      if (S::TE && a == 0) {
-        sBe[c0 & 3][lane] = ok ? beg[t * H] : 0.f;
-        sGa[c0 & 3][lane] = ok ? gag[t * H] : 0.f;
+  for (int k = 0; k < S::ST_PER_WAVE; ++k) asm volatile("" : "+v"(st[k]));
+  if (COORD) {
+    if (tid < N) sRate[tid] = r_rate;
+    if (tid < p.n_pairs) sOmega[tid] = r_om;
+  }
+  if (saved && seg == 0) {
+    // slot 0: the state entering chunk 0 (h, not the shifted h')
+#pragma unroll
+    for (int k = 0; k < S::ST_PER_WAVE; ++k) {
+      const int tile = wave * S::ST_PER_WAVE + k;
+      if (tile < S::ST_TILES) {
+        const int n = 16 * (tile / S::TP) + (lane & 15), pl = 16 * (tile % S::TP) + 4 * (lane >> 4);
+        float v[4] = {st[k][0], st[k][1], st[k][2], st[k][3]};
+        if (SH)
+          for (int i = 0; i < 4; ++i) v[i] += shift_corr(n, pl + i);
+        store4<BF16>(saved + (sl_saved * N + n) * P + p0 + pl, v);
       }
     }
   }
-  load_chunk(c0);
+  if (wave == PW) {
+    factors(c0, (lane < QT && c0 * QT + lane < L) ? (p.softplus ? softplus_f32(dt0) : dt0) : 0.f);
+    if (c0 + 1 < c1) factors(c0 + 1, (lane < QT && (c0 + 1) * QT + lane < L) ? (p.softplus ? softplus_f32(dt1) : dt1) : 0.f);
+    if (S::TE) {
+      sBe[c0 & 3][lane] = be0;
+      sGa[c0 & 3][lane] = ga0;
+    }
+  }
   __syncthreads();
+  // buffer 0 of the readout copy: the incoming state from this wave's state tiles
+  // (per-row decay: pre-scaled by e^{-A CD_end / 2} of the first chunk)
   {
     const float hc0 = 0.5f * sMisc[c0 & 3][0];
-    for (int i = tid; i < 2 * S::NC * VS; i += S::NTH) {
-      const int n = i / VS, col = i % VS;
-      float v = (h0s && n < N && col < PB) ? h0s[n * P + col] - shift_corr(n, col) : 0.f;
-      if (COORD && n < N) v *= __expf(-sRate[n] * hc0);
-      sST[i] = from_f32<T>(v);
+#pragma unroll
+    for (int k = 0; k < S::ST_PER_WAVE; ++k) {
+      const int tile = wave * S::ST_PER_WAVE + k;
+      if (tile < S::ST_TILES) {
+        const int n = 16 * (tile / S::TP) + (lane & 15), pl = 16 * (tile % S::TP) + 4 * (lane >> 4);
+        const float sc0 = COORD ? __expf(-sRate[n] * hc0) : 1.f;
+        const float v[4] = {sc0 * st[k][0], sc0 * st[k][1], sc0 * st[k][2], sc0 * st[k][3]};
+        store4<BF16>(sST + n * VS + pl, v);
+      }
     }
   }
   if (COORD) tables(c0, gprev0);
