@@ -444,6 +444,9 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
   // chunk's last token
   __shared__ __align__(16) float sGraw[S::TE ? N * P : 4];
   __shared__ __align__(16) T sBt1[S::TE ? R * N : 8], sXt1[S::TE ? R * P : 8];
+  // two-endpoint: the item's raw B rows (token t0 - 1 + row / R), for the endpoint-weight
+  // gradients
+  __shared__ __align__(16) T sBraw[S::TE ? S::BROWS * N : 8];
   // per-token factors of the current item (token = index)
   __shared__ float sTcd[64];                       // cumulative step inside the chunk
   __shared__ float sTw[64], sTel[64], sTlc[64];    // head: e^{L_end - L_t}, e^{L_t}, -A CD log2(e)
@@ -765,6 +768,7 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
       const float wv[2] = {S::TE ? __shfl(ga_l, ta, kWave) : 1.f, S::TE ? __shfl(be_l, tb, kWave) : 0.f};
       if (v >= S::B_VECS) continue;
       if (S::TE && sl == QT - 1) *reinterpret_cast<uint4*>(sBt1 + r * N + n0) = pfb[k];
+      if (S::TE) *reinterpret_cast<uint4*>(sBraw + row * N + n0) = pfb[k];
       float vals[VEC];
       unpack<BF16>(pfb[k], vals);
   #pragma unroll
@@ -1099,9 +1103,10 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
       float dgb = 0.f;
       if (S::TE) {
         const float wgt = brow ? sTbe[s] : sTga[s];
-        if (tb >= 0 && tb < L && rr < rin) {
+        {
+          // the staged raw row (zero outside the sequence and for rows >= rank_in)
           float braw[4];
-          load4<BF16>(Bg + ((((size_t)b * L + tb) * G + g) * rin + rr) * N + n0, braw);
+          load4<BF16>(sBraw + (((brow ? s - 1 : s) + 1) * R + rr) * N + n0, braw);
 #pragma unroll
           for (int i = 0; i < 4; ++i) dgb += dk[i] * braw[i];
         }
