@@ -887,20 +887,34 @@ __global__ __launch_bounds__(256) void ssm_fwd_combine(FwdParams p, int per_row)
       bv = p.h0[((size_t)slice * N + n + 1) * P + pp];
     }
     for (int s = 0; s + 1 < p.nseg; ++s) {
-      for (int u = 0; u < p.nsub; ++u) {
-        const size_t unit = sl + (size_t)s * p.nsub + u;
-        const float dsum = p.seg_delta[unit];
-        float a2 = a * expf(-ra * dsum), b2 = bv * expf(-rb * dsum);
-        if (pair) {
-          float sn, cs;
-          sincosf(om * dsum, &sn, &cs);
-          const float x0 = a2, x1 = b2;
-          a2 = cs * x0 - sn * x1;
-          b2 = sn * x0 + cs * x1;
+      // ranges in blocks of kCombineBlock: a block's reads are issued together, then
+      // chained (one memory round trip per block instead of per range)
+      for (int u0 = 0; u0 < p.nsub; u0 += kCombineBlock) {
+        const int cnt = min(kCombineBlock, p.nsub - u0);
+        float ds[kCombineBlock], l0[kCombineBlock], l1[kCombineBlock];
+#pragma unroll
+        for (int k = 0; k < kCombineBlock; ++k) {
+          const size_t unit = sl + (size_t)s * p.nsub + u0 + (k < cnt ? k : 0);
+          const float* loc = p.seg_local + (unit * N + n) * P + pp;
+          ds[k] = p.seg_delta[unit];
+          l0[k] = loc[0];
+          l1[k] = loc[P];
         }
-        const float* loc = p.seg_local + (unit * N + n) * P + pp;
-        a = a2 + loc[0];
-        bv = b2 + loc[P];
+#pragma unroll
+        for (int k = 0; k < kCombineBlock; ++k) {
+          if (k >= cnt) break;
+          const float dsum = ds[k];
+          float a2 = a * expf(-ra * dsum), b2 = bv * expf(-rb * dsum);
+          if (pair) {
+            float sn, cs;
+            sincosf(om * dsum, &sn, &cs);
+            const float x0 = a2, x1 = b2;
+            a2 = cs * x0 - sn * x1;
+            b2 = sn * x0 + cs * x1;
+          }
+          a = a2 + l0[k];
+          bv = b2 + l1[k];
+        }
       }
       float* out = p.seg_in + ((sb + s + 1) * N + n) * P + pp;
       out[0] = a;

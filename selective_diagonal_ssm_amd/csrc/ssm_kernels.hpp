@@ -38,6 +38,8 @@ struct FwdParams {
 
 // tokens of one local-pass range (bounds the kernel's per-token LDS tables)
 constexpr int kLocalMaxTokens = 512;
+// ranges whose boundary states a combine thread reads in one batch
+constexpr int kCombineBlock = 8;
 
 // operands of a segment local pass: forward ranges (states from a zero start) or
 // boundary-adjoint ranges (adjoints from a zero adjoint after the range)
