@@ -467,6 +467,13 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
   __shared__ float sTga[S::TE ? 64 : 1], sTbe[S::TE ? 64 : 1];
   __shared__ float sMisc[NW];
   __shared__ float sPartOut[N + N / 2 + 2];  // parameter partials of the item (stored a step later)
+  // per-row decay: factor tables of the item (token t, row n), E_t = e^{-A_n (CD_t - CD_end/2)},
+  // Theta_t = omega CD_t:  TQ[t] = E_t on real rows, (E_t cos, E_t sin)(Theta_t) on the rows of
+  // a pair;  TK[t] = 1 / E_t likewise.  Per row Er = e^{-A_n CD_end / 2} and
+  // Fd = e^{-A_n Dnext}; per pair the turn (cos, sin)(omega (CD_end + Dnext)).
+  __shared__ __align__(16) float sTQ[COORD ? QT * N : 4], sTK[COORD ? QT * N : 4];
+  __shared__ float sEr[COORD ? N : 1], sFd[COORD ? N : 1];
+  __shared__ float2 sTurn[COORD ? N / 2 + 1 : 1];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int nch = p.nchunks;
@@ -672,6 +679,28 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
       for (int k = tid; k < p.npart; k += S::NTH) p.part[((size_t)slice * nch + c) * p.npart + k] = sPartOut[k];
   };
 
+  // VEC consecutive rows n0.. of a staged vector times their table entries: per-row
+  // factors, or on a pair (a, b) = table entries the product (a u0 + b u1, -b u0 + a u1)
+  auto apply_tab = [&](float* v, const float* tab, int n0) {
+    float f[VEC];
+#pragma unroll
+    for (int i = 0; i < VEC; i += 4) {
+      const float4 w = *reinterpret_cast<const float4*>(tab + n0 + i);
+      f[i] = w.x; f[i + 1] = w.y; f[i + 2] = w.z; f[i + 3] = w.w;
+    }
+#pragma unroll
+    for (int i = 0; i < VEC; i += 2) {
+      const float a = v[i], bb = v[i + 1];
+      if (n0 + i >= nreal) {
+        v[i] = f[i] * a + f[i + 1] * bb;
+        v[i + 1] = -f[i + 1] * a + f[i] * bb;
+      } else {
+        v[i] = f[i] * a;
+        v[i + 1] = f[i + 1] * bb;
+      }
+    }
+  };
+
   int prev = -1;
   int item = blockIdx.x;
   if (item < nitems)
@@ -738,6 +767,44 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
         sTbe[lane] = be_l;
       }
     }
+    if constexpr (COORD) {
+      // factor tables (one entry pair per thread; the shuffle runs on whole waves)
+      const float hc = 0.5f * cdend;
+      constexpr int TE_N = QT * (N / 2);
+#pragma unroll
+      for (int i0 = 0; i0 < TE_N; i0 += S::NTH) {
+        const int i = i0 + tid;
+        const int t = (i < TE_N ? i : 0) / (N / 2), n = 2 * (i % (N / 2));
+        const float cd = __shfl(cd_l, t, kWave);
+        if (i < TE_N) {
+          float2 q, k;
+          if (n >= nreal) {
+            const float x = sRate[n] * (cd - hc);
+            const float e = __expf(-x), ei = __expf(x);
+            float sn, cs;
+            fast_sincos(sOmega[(n - nreal) >> 1] * cd, &sn, &cs);
+            q = make_float2(e * cs, e * sn);
+            k = make_float2(ei * cs, ei * sn);
+          } else {
+            const float x0 = sRate[n] * (cd - hc), x1 = sRate[n + 1] * (cd - hc);
+            q = make_float2(__expf(-x0), __expf(-x1));
+            k = make_float2(__expf(x0), __expf(x1));
+          }
+          *reinterpret_cast<float2*>(sTQ + t * N + n) = q;
+          *reinterpret_cast<float2*>(sTK + t * N + n) = k;
+        }
+      }
+      for (int n = tid; n < N; n += S::NTH) {
+        sEr[n] = __expf(-sRate[n] * hc);
+        sFd[n] = __expf(-sRate[n] * dnext);
+        if (n >= nreal && ((n - nreal) & 1) == 0) {
+          float sn, cs;
+          fast_sincos(sOmega[(n - nreal) >> 1] * (cdend + dnext), &sn, &cs);
+          sTurn[(n - nreal) >> 1] = make_float2(cs, sn);
+        }
+      }
+      __syncthreads();
+    }
 
     // ---------------------------------------------------------------- staging
     // queries (t, o)
@@ -751,22 +818,12 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
       if (v >= S::C_VECS) continue;
       uint4 raw = pfc[k];
       if (COORD) {
+        // q = R(-Theta_t) C_t E_t
         float vals[VEC];
         unpack<BF16>(raw, vals);
-  #pragma unroll
-        for (int i = 0; i < VEC; i += 2) {
-          const int n = n0 + i;
-          if (n >= nreal) {
-            float sn, cs;
-            fast_sincos(sOmega[(n - nreal) >> 1] * cd, &sn, &cs);
-            const float a = vals[i], bb = vals[i + 1];
-            vals[i] = cs * a + sn * bb;
-            vals[i + 1] = -sn * a + cs * bb;
-          }
-        }
-  #pragma unroll
-        for (int i = 0; i < VEC; ++i) vals[i] *= __expf(-sRate[n0 + i] * (cd - 0.5f * cdend));
+        apply_tab(vals, sTQ + tl * N, n0);
         raw = pack<BF16>(vals);
+        (void)cd;
       }
       *reinterpret_cast<uint4*>(sQ + row * NS + n0) = raw;
     }
@@ -795,21 +852,13 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
   #pragma unroll
         for (int i = 0; i < VEC; ++i) u[i] = vals[i] * wv[e];
         if (COORD) {
-  #pragma unroll
-          for (int i = 0; i < VEC; i += 2) {
-            const int n = n0 + i;
-            if (n >= nreal) {
-              float sn, cs;
-              fast_sincos(sOmega[(n - nreal) >> 1] * cdv[e], &sn, &cs);
-              const float a = u[i], bb = u[i + 1];
-              u[i] = cs * a + sn * bb;
-              u[i + 1] = -sn * a + cs * bb;
-            }
-          }
+          // k = R(-Theta_tau) u / E_tau,  ke = k e^{-A CD_end / 2}
+          (void)cdv;
+          apply_tab(u, sTK + tau * N, n0);
   #pragma unroll
           for (int i = 0; i < VEC; ++i) {
-            kk[i] = u[i] * __expf(-sRate[n0 + i] * (0.5f * cdend - cdv[e]));
-            ke[i] = u[i] * __expf(-sRate[n0 + i] * (cdend - cdv[e]));
+            kk[i] = u[i];
+            ke[i] = u[i] * sEr[n0 + i];
           }
           *reinterpret_cast<uint4*>(sKe + j * NS + n0) = pack<BF16>(ke);
         } else {
@@ -860,8 +909,8 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
         }
         float fa, fb, lea, leb;
         if (COORD) {
-          fa = __expf(-sRate[n] * dnext); fb = __expf(-sRate[n + 1] * dnext);
-          lea = __expf(-sRate[n] * cdend); leb = __expf(-sRate[n + 1] * cdend);
+          fa = sFd[n]; fb = sFd[n + 1];
+          lea = sEr[n] * sEr[n]; leb = sEr[n + 1] * sEr[n + 1];
         } else {
           fa = fb = gdec_h; lea = leb = lend_h;
         }
@@ -869,8 +918,8 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
         for (int i = 0; i < 4; ++i) { ga[i] *= fa; gb[i] *= fb; }
         const bool pair = COORD && n >= nreal;
         if (pair) {
-          float sn, cs;
-          fast_sincos(sOmega[(n - nreal) >> 1] * (cdend + dnext), &sn, &cs);
+          const float2 tr = sTurn[(n - nreal) >> 1];
+          const float sn = tr.y, cs = tr.x;
   #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const float a0 = ga[i], a1 = gb[i];
@@ -1078,9 +1127,9 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
         const int n = n0 + i;
         rpa[i] = 0.f; rek[i] = 0.f;
         if (COORD) {
-          const float er = __expf(-sRate[n] * 0.5f * cdend);  // e^{r_n}
+          const float er = sEr[n];  // e^{r_n}
           const float ck = ai[i] + er * ae[i];
-          dk[i] = __expf(-sRate[n] * (0.5f * cdend - cds)) * ck;  // e^{r - L_s} ck  (dK~)
+          dk[i] = ck;  // scaled by e^{r - L_s} (with the pair's turn) below
           // source terms: -k o cK  (rows); the inter part also feeds the final-state term
           const float dr = -kv[i] * ck;
           tokacc += -sRate[n] * dr;
@@ -1097,19 +1146,28 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
           const int n = n0 + i;
           if (n >= nreal) {
             const int kp = (n - nreal) >> 1;
-            const float er = __expf(-sRate[n] * 0.5f * cdend);
+            const float er = sEr[n];
             const float ca = ai[i] + er * ae[i], cb = ai[i + 1] + er * ae[i + 1];
             // K~^T J dK~ in scaled form: -k_a cK_b + k_b cK_a
             const float dth = -kv[i] * cb + kv[i + 1] * ca;
             tokacc += sOmega[kp] * dth;
             rpw[i >> 1] = cds * dth;
             rekt[i >> 1] = -(-kv[i] * er * ae[i + 1] + kv[i + 1] * er * ae[i]);
-            // unfold the rotation of the key: u = R(+Theta_s) dK~
-            float sn, cs;
-            fast_sincos(sOmega[kp] * cds, &sn, &cs);
-            const float a0 = dk[i], a1 = dk[i + 1];
-            dk[i] = cs * a0 - sn * a1;
-            dk[i + 1] = sn * a0 + cs * a1;
+          }
+        }
+        // dK~ = e^{r - L_s} cK, and unfold the key's rotation: u = R(+Theta_s) dK~
+        // (table entries (a, b) = (cos, sin) / E_s on a pair)
+        const float4 tk = *reinterpret_cast<const float4*>(sTK + s * N + n0);
+        const float f[4] = {tk.x, tk.y, tk.z, tk.w};
+#pragma unroll
+        for (int i = 0; i < 4; i += 2) {
+          const float a0 = dk[i], a1 = dk[i + 1];
+          if (n0 + i >= nreal) {
+            dk[i] = f[i] * a0 - f[i + 1] * a1;
+            dk[i + 1] = f[i + 1] * a0 + f[i] * a1;
+          } else {
+            dk[i] = f[i] * a0;
+            dk[i + 1] = f[i + 1] * a1;
           }
         }
       }
@@ -1239,9 +1297,9 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
         const int n = n0 + i;
         rpa[i] = 0.f;
         if (COORD) {
-          const float er = __expf(-sRate[n] * 0.5f * cdend);
+          const float er = sEr[n];
           const float cc = ai[i] + er * ae[i];
-          dc[i] = __expf(-sRate[n] * (cdt - 0.5f * cdend)) * cc;
+          dc[i] = cc;  // scaled by E_t (with the pair's turn) below
           const float dr = qv[i] * cc;
           tokacc += -sRate[n] * dr;
           rpa[i] = -cdt * dr;
@@ -1256,16 +1314,25 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
           const int n = n0 + i;
           if (n >= nreal) {
             const int kp = (n - nreal) >> 1;
-            const float er = __expf(-sRate[n] * 0.5f * cdend);
+            const float er = sEr[n];
             const float ca = ai[i] + er * ae[i], cb = ai[i + 1] + er * ae[i + 1];
             const float dth = -qv[i] * cb + qv[i + 1] * ca;  // C~^T J dC~ (scaled form)
             tokacc += sOmega[kp] * dth;
             rpw[i >> 1] = cdt * dth;
-            float sn, cs;
-            fast_sincos(sOmega[kp] * cdt, &sn, &cs);
-            const float a0 = dc[i], a1 = dc[i + 1];
-            dc[i] = cs * a0 - sn * a1;
-            dc[i + 1] = sn * a0 + cs * a1;
+          }
+        }
+        // dC~ = E_t cC, unfolded by R(+Theta_t) (table entries (a, b) = E_t (cos, sin))
+        const float4 tq = *reinterpret_cast<const float4*>(sTQ + t * N + n0);
+        const float f[4] = {tq.x, tq.y, tq.z, tq.w};
+#pragma unroll
+        for (int i = 0; i < 4; i += 2) {
+          const float a0 = dc[i], a1 = dc[i + 1];
+          if (n0 + i >= nreal) {
+            dc[i] = f[i] * a0 - f[i + 1] * a1;
+            dc[i + 1] = f[i + 1] * a0 + f[i] * a1;
+          } else {
+            dc[i] = f[i] * a0;
+            dc[i + 1] = f[i + 1] * a1;
           }
         }
       }
