@@ -1111,7 +1111,11 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
     // lane l holds key 16 tj + (l & 15) and state rows 16 tnn + 4 (l >> 4) + i.  Tiles
     // go in BN x BJ blocks per wave: a block's fragments are read once for all of its
     // tiles, and its tiles are independent MFMA chains.
-    auto dk_tile = [&](const int tnn, const int tj, const f32x4& ai, const f32x4& ae) {
+    // per-row decay: the tile's per-row partial sums (over its 16 key columns, one per
+    // lane) are added into xpa / xek / xpw / xekt; flush_rows reduces them over the lanes
+    // and adds them to this wave's slots
+    auto dk_tile = [&](const int tnn, const int tj, const f32x4& ai, const f32x4& ae, float* xpa,
+                       float* xek, float* xpw, float* xekt) {
       const int j = 16 * tj + (lane & 15), s = j / KR, kr = j % KR;
       const int n0 = 16 * tnn + 4 * (lane >> 4);
       const float cds = sTcd[s];
@@ -1193,28 +1197,15 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
         store_bc(dBg, rin, b, tb, part ? h : g, rr, n0, dk);
       }
       if (COORD) {
-        // per-row sums over the 16 key columns of this tile (one 16-lane group)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          rpa[i] = group_sum<16>(rpa[i]);
-          rek[i] = group_sum<16>(rek[i]);
+          xpa[i] += rpa[i];
+          xek[i] += rek[i];
         }
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
-          rpw[q] = group_sum<16>(rpw[q]);
-          rekt[q] = group_sum<16>(rekt[q]);
-        }
-        if ((lane & 15) == 0) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int n = n0 + i;
-            sPA[wave][n] += rpa[i];
-            sEK[wave][n] += rek[i];
-            if ((i & 1) == 0 && n >= nreal) {
-              sPW[wave][(n - nreal) >> 1] += rpw[i >> 1];
-              sEKth[wave][(n - nreal) >> 1] += rekt[i >> 1];
-            }
-          }
+          xpw[q] += rpw[q];
+          xekt[q] += rekt[q];
         }
       }
       // per-key sums over the 4 row groups, then over the keys of one token
@@ -1238,9 +1229,51 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
       }
     };
     {
-      constexpr int BN = S::KBLK ? 2 : 1, BJ = S::KBLK ? 2 : 1, NBJ = S::TK / BJ;
-      for (int blk = wave; blk < (S::TN / BN) * NBJ; blk += NW) {
-        const int tn0 = (blk / NBJ) * BN, tj0 = (blk % NBJ) * BJ;
+      constexpr int BN = S::KBLK ? 2 : 1, BJ = S::KBLK ? 2 : 1, NBJ = S::TK / BJ, NBN = S::TN / BN;
+      // per-row decay: blocks go n-block fastest, so when NW is a multiple of the n-blocks
+      // all blocks of a wave share its n-block and their per-row sums are reduced once,
+      // after the loop
+      constexpr bool SHARE_N = NW % NBN == 0;
+      float apa[BN][4], aek[BN][4], apw[BN][2], aekt[BN][2];
+      auto zero_rows = [&]() {
+#pragma unroll
+        for (int x = 0; x < BN; ++x) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) apa[x][i] = aek[x][i] = 0.f;
+          apw[x][0] = apw[x][1] = aekt[x][0] = aekt[x][1] = 0.f;
+        }
+      };
+      auto flush_rows = [&](int tn0) {
+#pragma unroll
+        for (int x = 0; x < BN; ++x) {
+          const int n0 = 16 * (tn0 + x) + 4 * (lane >> 4);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            apa[x][i] = group_sum<16>(apa[x][i]);
+            aek[x][i] = group_sum<16>(aek[x][i]);
+          }
+#pragma unroll
+          for (int q = 0; q < 2; ++q) {
+            apw[x][q] = group_sum<16>(apw[x][q]);
+            aekt[x][q] = group_sum<16>(aekt[x][q]);
+          }
+          if ((lane & 15) == 0) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int n = n0 + i;
+              sPA[wave][n] += apa[x][i];
+              sEK[wave][n] += aek[x][i];
+              if ((i & 1) == 0 && n >= nreal) {
+                sPW[wave][(n - nreal) >> 1] += apw[x][i >> 1];
+                sEKth[wave][(n - nreal) >> 1] += aekt[x][i >> 1];
+              }
+            }
+          }
+        }
+      };
+      if (COORD) zero_rows();
+      for (int blk = wave; blk < NBN * NBJ; blk += NW) {
+        const int tn0 = (COORD ? blk % NBN : blk / NBJ) * BN, tj0 = (COORD ? blk / NBN : blk % NBJ) * BJ;
         f32x4 ai[BN][BJ], ae[BN][BJ];
 #pragma unroll
         for (int x = 0; x < BN; ++x)
@@ -1278,8 +1311,13 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
 #pragma unroll
         for (int x = 0; x < BN; ++x)
 #pragma unroll
-          for (int y = 0; y < BJ; ++y) dk_tile(tn0 + x, tj0 + y, ai[x][y], ae[x][y]);
+          for (int y = 0; y < BJ; ++y) dk_tile(tn0 + x, tj0 + y, ai[x][y], ae[x][y], apa[x], aek[x], apw[x], aekt[x]);
+        if (COORD && !SHARE_N) {
+          flush_rows(tn0);
+          zero_rows();
+        }
       }
+      if (COORD && SHARE_N && wave < NBN * NBJ) flush_rows((wave % NBN) * BN);
     }
 
     // ---------------------------------------------------------------- dC~ -> dC
