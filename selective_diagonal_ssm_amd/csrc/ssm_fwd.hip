@@ -117,7 +117,9 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
   constexpr int NS = S::NS, KS = S::KS, VS = S::VS, VEC = S::VEC;
   constexpr int QSZ = S::QO * NS, KSZ = S::QK * NS, VSZ = S::QK * S::VS;
   constexpr float kLog2e = 1.4426950408889634f;
-  constexpr int PW = NW - 1;  // the wave that computes the per-token factors
+  // the wave that computes the per-token factors: with per-row decay wave 0, which has the
+  // most slack before the first barrier (measured), else the last wave
+  constexpr int PW = COORD ? 0 : NW - 1;
 
   // double-buffered chunk operands: chunk c is consumed while chunk c+1 is staged
   __shared__ __align__(16) T sQ[2 * QSZ];                     // queries (folded; per-row: scaled)
