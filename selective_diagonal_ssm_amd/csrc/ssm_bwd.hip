@@ -814,7 +814,6 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
       const int vv = v < S::C_VECS ? v : 0;
       const int row = vv / (N / VEC), n0 = (vv % (N / VEC)) * VEC;
       const int tl = row / R;
-      const float cd = __shfl(cd_l, tl, kWave);
       if (v >= S::C_VECS) continue;
       uint4 raw = pfc[k];
       if (COORD) {
@@ -823,7 +822,6 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
         unpack<BF16>(raw, vals);
         apply_tab(vals, sTQ + tl * N, n0);
         raw = pack<BF16>(vals);
-        (void)cd;
       }
       *reinterpret_cast<uint4*>(sQ + row * NS + n0) = raw;
     }
@@ -835,7 +833,6 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
       const int row = vv / (N / VEC), n0 = (vv % (N / VEC)) * VEC;
       const int sl = row / R - S::TEH, r = row % R;
       const int ta = sl < 0 ? 0 : sl, tb = sl + 1 < QT ? sl + 1 : QT - 1;
-      const float cdv[2] = {__shfl(cd_l, ta, kWave), __shfl(cd_l, tb, kWave)};
       const float wv[2] = {S::TE ? __shfl(ga_l, ta, kWave) : 1.f, S::TE ? __shfl(be_l, tb, kWave) : 0.f};
       if (v >= S::B_VECS) continue;
       if (S::TE && sl == QT - 1) *reinterpret_cast<uint4*>(sBt1 + r * N + n0) = pfb[k];
@@ -853,7 +850,6 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
         for (int i = 0; i < VEC; ++i) u[i] = vals[i] * wv[e];
         if (COORD) {
           // k = R(-Theta_tau) u / E_tau,  ke = k e^{-A CD_end / 2}
-          (void)cdv;
           apply_tab(u, sTK + tau * N, n0);
   #pragma unroll
           for (int i = 0; i < VEC; ++i) {
