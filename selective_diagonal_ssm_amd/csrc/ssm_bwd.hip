@@ -984,9 +984,14 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
       }
     }
     if (p.has_D) {
-      for (int i = tid; i < QO * P; i += S::NTH) {
-        const int row = i / P, pp = i % P, tl = row / R, o = row % R;
-        dDp += to_f32(sY[row * PS + pp]) * to_f32(sV[(tl * KR + o) * PS + pp]);
+      // sum of dy . x over the item, one 16-byte vector of each per step
+      for (int v = tid; v < QO * (P / VEC); v += S::NTH) {
+        const int row = v / (P / VEC), p0 = (v % (P / VEC)) * VEC, tl = row / R, o = row % R;
+        float yv[VEC], xv[VEC];
+        unpack<BF16>(*reinterpret_cast<const uint4*>(sY + row * PS + p0), yv);
+        unpack<BF16>(*reinterpret_cast<const uint4*>(sV + (tl * KR + o) * PS + p0), xv);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) dDp += yv[e] * xv[e];
       }
     }
     dDp = wave_sum(dDp);
