@@ -1065,24 +1065,10 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
 
     // ---------------------------------------------------------------- dV -> dX
     // dV^T = dY^T (S o M) + G~^T Ke^T, computed transposed: lane l holds key
-    // 16 tj + (l & 15) and value columns 16 tp + 4 (l >> 4) + i
-    for (int tile = wave; tile < S::TK * S::TP; tile += NW) {
-      const int tj = tile / S::TP, tp = tile % S::TP;
-      f32x4 ai = {0.f, 0.f, 0.f, 0.f}, ae = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kk = 0; kk < S::QOC / 32; ++kk) {
-        const auto fy = load_frag_tr<BF16>(sY + (kk * 32) * PS + 16 * tp, PS);
-        const auto fs = load_frag_tr<BF16>(sSM + (kk * 32) * KS + 16 * tj, KS);
-        mma<BF16>(ai, fy, fs);
-      }
-#pragma unroll
-      for (int kk = 0; kk < S::NC / 32; ++kk) {
-        if (kk * 32 < N) {
-          const auto fk = load_frag<BF16>((COORD ? sKe : sK) + (16 * tj + (lane & 15)) * NS + kk * 32 + 8 * (lane >> 4));
-          const auto fgh = load_frag_tr<BF16>(sGh + (kk * 32) * PS + 16 * tp, PS);
-          mma<BF16>(ae, fgh, fk);
-        }
-      }
+    // 16 tj + (l & 15) and value columns 16 tp + 4 (l >> 4) + i.  When NW is a multiple
+    // of the column tiles, a wave takes two tiles of one column block (tiles t and
+    // t + NW), and their dY and G~ fragments are read once.
+    auto dv_tile = [&](const int tj, const int tp, const f32x4& ai, const f32x4& ae) {
       const int j = 16 * tj + (lane & 15), s = j / KR, kr = j % KR;
       const int pl = 16 * tp + 4 * (lane >> 4);
       const float wj = COORD ? 1.f : sTw[s];
@@ -1105,6 +1091,41 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
         // beta row -> X_{s-1}
         *reinterpret_cast<float4*>(sDX + (QT + 1) * R * P + (s * R + kr - R) * P + pl) =
             make_float4(dv[0], dv[1], dv[2], dv[3]);
+      }
+    };
+    {
+      constexpr int NT_DV = S::TK * S::TP;
+      constexpr int DVB = (NW % S::TP == 0 && NT_DV % (2 * NW) == 0) ? 2 : 1;
+      for (int tile = wave; tile < NT_DV; tile += NW * DVB) {
+        const int tp = tile % S::TP;
+        int tjs[DVB];
+#pragma unroll
+        for (int x = 0; x < DVB; ++x) tjs[x] = (tile + x * NW) / S::TP;
+        f32x4 ai[DVB], ae[DVB];
+#pragma unroll
+        for (int x = 0; x < DVB; ++x) ai[x] = ae[x] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < S::QOC / 32; ++kk) {
+          const auto fy = load_frag_tr<BF16>(sY + (kk * 32) * PS + 16 * tp, PS);
+#pragma unroll
+          for (int x = 0; x < DVB; ++x) {
+            const auto fs = load_frag_tr<BF16>(sSM + (kk * 32) * KS + 16 * tjs[x], KS);
+            mma<BF16>(ai[x], fy, fs);
+          }
+        }
+#pragma unroll
+        for (int kk = 0; kk < S::NC / 32; ++kk) {
+          if (kk * 32 < N) {
+            const auto fgh = load_frag_tr<BF16>(sGh + (kk * 32) * PS + 16 * tp, PS);
+#pragma unroll
+            for (int x = 0; x < DVB; ++x) {
+              const auto fk = load_frag<BF16>((COORD ? sKe : sK) + (16 * tjs[x] + (lane & 15)) * NS + kk * 32 + 8 * (lane >> 4));
+              mma<BF16>(ae[x], fgh, fk);
+            }
+          }
+        }
+#pragma unroll
+        for (int x = 0; x < DVB; ++x) dv_tile(tjs[x], tp, ai[x], ae[x]);
       }
     }
 
