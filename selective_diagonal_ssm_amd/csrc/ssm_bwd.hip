@@ -417,6 +417,10 @@ struct BwdShape {
   // per wave anyway
   static constexpr bool KBLK = TN % 2 == 0 && TK % 2 == 0 && TN * TK >= 4 * NW;
   static constexpr bool CBLK = TN % 2 == 0 && TQ % 2 == 0 && TN * TQ >= 4 * NW;
+  // exactly two tiles per wave otherwise: a wave takes them as one 1 x 2 block (one
+  // n-block, two key / query blocks), so the n-block's fragments serve both
+  static constexpr bool KPAIR = !KBLK && TK % 2 == 0 && TN * TK == 2 * NW;
+  static constexpr bool CPAIR = !CBLK && TQ % 2 == 0 && TN * TQ == 2 * NW;
   static_assert(QO % 16 == 0 && QK % 32 == 0, "chunk rows must fill MFMA tiles");
   static_assert(N % 16 == 0 && P % 16 == 0 && QT <= 64, "unsupported tile shape");
   static_assert(KR <= 4 && 16 % KR == 0 && 16 % R == 0, "a tile spans whole tokens");
@@ -1251,7 +1255,7 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
       }
     };
     {
-      constexpr int BN = S::KBLK ? 2 : 1, BJ = S::KBLK ? 2 : 1, NBJ = S::TK / BJ, NBN = S::TN / BN;
+      constexpr int BN = S::KBLK ? 2 : 1, BJ = (S::KBLK || S::KPAIR) ? 2 : 1, NBJ = S::TK / BJ, NBN = S::TN / BN;
       // per-row decay: blocks go n-block fastest, so when NW is a multiple of the n-blocks
       // all blocks of a wave share its n-block and their per-row sums are reduced once,
       // after the loop
@@ -1420,7 +1424,7 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
       }
     };
     {
-      constexpr int BN = S::CBLK ? 2 : 1, BQ = S::CBLK ? 2 : 1, NBQ = S::TQ / BQ;
+      constexpr int BN = S::CBLK ? 2 : 1, BQ = (S::CBLK || S::CPAIR) ? 2 : 1, NBQ = S::TQ / BQ;
       for (int blk = wave; blk < (S::TN / BN) * NBQ; blk += NW) {
         const int tn0 = (blk / NBQ) * BN, tq0 = (blk % NBQ) * BQ;
         f32x4 ai[BN][BQ], ae[BN][BQ];
