@@ -960,10 +960,64 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
       sTT[wave][lane] = 0.f; sSrc[wave][lane] = 0.f; sRS[wave][lane] = 0.f; sCS[wave][lane] = 0.f;
     }
     // two-endpoint tails of the last token from the staged rows: beta_{t0'} B_{t1}^T g'
-    // and g' X_{t1}^T (zero without a next chunk, where g' and beta_{t0'} are zero)
-    // Each of the R P + R N outputs is a dot product of length N or P split over TT
-    // adjacent lanes, summed by a fixed butterfly.
-    if (S::TE) {
+    // and g' X_{t1}^T (zero without a next chunk, where g' and beta_{t0'} are zero),
+    // as fp32 MFMA products with the R rows padded to 16:
+    //   tail X (R x P) = B_{t1} (R x N) g' (N x P),   tail B^T (N x R) = g' (N x P) X_{t1}^T (P x R),
+    // one 16-column output tile per wave (P / 16 tiles of tail X, then N / 16 of tail B)
+    if constexpr (S::TE && N % 32 == 0 && P % 32 == 0) {
+      static_assert(R <= 16, "tail products with the rows padded to 16");
+      // 8 consecutive elements of row m of a staged R-row buffer (zero for m >= R)
+      auto rows8 = [&](const T* buf, int ld, int m, int k0) {
+        Frag<false> f;
+        if (m < R) {
+          if constexpr (BF16) {
+            float v[8];
+            unpack<true>(*reinterpret_cast<const uint4*>(buf + m * ld + k0), v);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) f.v[i] = v[i];
+          } else {
+            f = load_frag<false>(reinterpret_cast<const float*>(buf) + m * ld + k0);
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) f.v[i] = 0.f;
+        }
+        return f;
+      };
+      for (int u = wave; u < P / 16 + N / 16; u += NW) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        if (u < P / 16) {
+          const int tp = u;
+#pragma unroll
+          for (int kk = 0; kk < N / 32; ++kk) {
+            const auto fa = rows8(sBt1, N, lane & 15, kk * 32 + 8 * (lane >> 4));
+            const auto fb = load_frag_tr<false>(sGraw + (kk * 32) * P + 16 * tp, P);
+            mma<false>(acc, fa, fb);
+          }
+          // lane l: rows r = 4 (l >> 4) + i, column p = 16 tp + (l & 15)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int r = 4 * (lane >> 4) + i;
+            if (r < R) sTailX[r * P + 16 * tp + (lane & 15)] = bnext * acc[i];
+          }
+        } else {
+          const int tn = u - P / 16;
+#pragma unroll
+          for (int kk = 0; kk < P / 32; ++kk) {
+            const auto fa = load_frag<false>(sGraw + (16 * tn + (lane & 15)) * P + kk * 32 + 8 * (lane >> 4));
+            const auto fb = rows8(sXt1, P, lane & 15, kk * 32 + 8 * (lane >> 4));
+            mma<false>(acc, fa, fb);
+          }
+          // lane l: rows n = 16 tn + 4 (l >> 4) + i, column r = l & 15
+          if ((lane & 15) < R) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sTailB[(lane & 15) * N + 16 * tn + 4 * (lane >> 4) + i] = bnext * acc[i];
+          }
+        }
+      }
+    } else if constexpr (S::TE) {
+      // narrow states: each of the R P + R N outputs is a dot product of length N or P
+      // split over TT adjacent lanes, summed by a fixed butterfly
       constexpr int O1 = R * P, OT = R * P + R * N;
       constexpr int TQ = S::NTH / OT;
       constexpr int TT = TQ >= 16 ? 16 : TQ >= 8 ? 8 : TQ >= 4 ? 4 : TQ >= 2 ? 2 : 1;
