@@ -1741,9 +1741,11 @@ bool bwd_variant_exists(const BwdKey& k) {
 #ifndef ADJ_NT
 #define ADJ_NT 1024
 #endif
-#ifndef CHUNK_NT
-#define CHUNK_NT 512
-#endif
+// Chunk-gradient workgroup size: 512 threads, or 256 for head decay with narrow states
+// (N <= 64), where two workgroups of 256 share a compute unit (LDS and registers allow
+// it) and hide each other's latencies (SSD-MIMO 0.78 -> 0.67 ms; SSD SISO with N = 128
+// and the per-row variants run best at 512)
+#define CHUNK_NT(NN, CO) ((!(CO) && (NN) <= 64) ? 256 : 512)
 #define ADJ_PB(PP) (PP)
 
 // compute units of the current device (cached per device)
@@ -1809,11 +1811,11 @@ hipError_t launch_bwd(const BwdKey& k, const BwdParams& p, hipStream_t stream,
     {                                                                                         \
       static std::atomic<int> occ{0};                                                         \
       const void* kfn = reinterpret_cast<const void*>(                                        \
-          &ssm_bwd_chunk<BF, NN, PP, RR, KRR, QTT, CO, CHUNK_NT, SP>);                        \
+          &ssm_bwd_chunk<BF, NN, PP, RR, KRR, QTT, CO, CHUNK_NT(NN, CO), SP>);                \
       const int items = slices * p.nchunks;                                                   \
-      const int grid = std::min(items, device_cus() * blocks_per_cu(kfn, CHUNK_NT, occ));      \
-      hipLaunchKernelGGL((ssm_bwd_chunk<BF, NN, PP, RR, KRR, QTT, CO, CHUNK_NT, SP>), dim3(grid), \
-                         dim3(CHUNK_NT), 0, stream, p);                                       \
+      const int grid = std::min(items, device_cus() * blocks_per_cu(kfn, CHUNK_NT(NN, CO), occ)); \
+      hipLaunchKernelGGL((ssm_bwd_chunk<BF, NN, PP, RR, KRR, QTT, CO, CHUNK_NT(NN, CO), SP>),     \
+                         dim3(grid), dim3(CHUNK_NT(NN, CO)), 0, stream, p);                   \
     }                                                                                         \
     if (p.dBh) {                                                                              \
       const long total = (long)p.batch * p.L * p.G * RR * (NN / 4);                          \
