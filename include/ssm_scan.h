@@ -65,6 +65,10 @@
  *     token 0 (beta_0 B_{-1} X_{-1}) stays zero with or without h0: an exact
  *     continuation of a two-endpoint run folds A_0^{-1} beta_0 B_{-1} X_{-1}
  *     into h0 on the caller's side.
+ *   - Empty problems (batch = 0 or seqlen = 0) read no inputs, and the pointers
+ *     of empty tensors may be NULL.  The outputs that are not empty are still
+ *     written: ssm_scan_fwd sets h_final to h0 (zero without h0);
+ *     ssm_scan_bwd zeroes dA, domega, dD and dh0, the sums over no tokens.
  *   - `ws` is device scratch of at least ssm_workspace_bytes(desc, dir) bytes
  *     (may be NULL when that is 0).  Calls that share a workspace on one
  *     stream are ordered; concurrent calls need separate workspaces.

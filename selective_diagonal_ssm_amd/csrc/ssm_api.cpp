@@ -14,6 +14,29 @@ namespace {
 using ssm::BwdKey;
 using ssm::FwdKey;
 
+// Fills for an empty sequence or batch, where no scan runs but some outputs are not empty:
+// the state after no tokens is the initial one, and sums over no tokens are zero.  A fill
+// kernel rather than a memset, so that a caller may capture the call in a graph.
+__global__ void __launch_bounds__(256) copy_or_zero_kernel(float* __restrict__ dst,
+                                                           const float* __restrict__ src,
+                                                           size_t n) {
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride)
+    dst[i] = src ? src[i] : 0.f;
+}
+
+// dst[0, n) = src[0, n), or zeros when src is NULL; nothing when dst is NULL or n is 0.
+hipError_t copy_or_zero(float* dst, const float* src, size_t n, hipStream_t s) {
+  if (!dst || n == 0) return hipSuccess;
+  const unsigned blocks = (unsigned)std::min<size_t>((n + 255) / 256, 2048);
+  hipLaunchKernelGGL(copy_or_zero_kernel, dim3(blocks), dim3(256), 0, s, dst, src, n);
+  return hipGetLastError();
+}
+
+size_t state_floats(const ssm_desc* d) {
+  return (size_t)d->batch * d->nheads * d->dstate * d->headdim;
+}
+
 struct Plan {
   bool coord_kernel;  // per-row kernel (per-row rates, pairs or two-endpoint writes)
   bool head_rates;    // per-row kernel fed one rate per head
@@ -258,8 +281,13 @@ int ssm_scan_fwd(const ssm_desc* d, const ssm_fwd_args* a, void* ws, size_t ws_b
   int rc = make_plan(d, &pl);
   if (rc) return rc;
   if (!a) return SSM_ERR_NULL;
-  // an empty problem touches no memory (empty tensors may have NULL pointers)
-  if (d->batch == 0 || d->seqlen == 0) return SSM_OK;
+  // an empty problem reads no inputs (empty tensors may have NULL pointers); with no tokens
+  // the final state is h0 (zero without it)
+  if (d->batch == 0 || d->seqlen == 0) {
+    const hipError_t e = copy_or_zero(a->h_final, a->h0, state_floats(d),
+                                      static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+  }
   const bool te = (d->flags & SSM_F_TWO_ENDPOINT) != 0;
   const bool hasD = (d->flags & SSM_F_HAS_D) != 0;
   if (!a->x || !a->B || !a->C || !a->dt || !a->A || !a->y) return SSM_ERR_NULL;
@@ -332,7 +360,16 @@ int ssm_scan_bwd(const ssm_desc* d, const ssm_bwd_args* a, void* ws, size_t ws_b
   BwdKey key{pl.bf16, d->dstate, d->headdim, pl.R, pl.KR, pl.QT, pl.coord_kernel,
              d->rank_in != d->rank_out};
   if (!ssm::bwd_variant_exists(key)) return SSM_ERR_UNSUPPORTED;
-  if (d->batch == 0 || d->seqlen == 0) return SSM_OK;
+  if (d->batch == 0 || d->seqlen == 0) {
+    // no tokens: the parameter gradients are sums over nothing, and no output depends on h0
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    const size_t na = (size_t)d->nheads * (pl.head_rates ? 1 : d->n_real + d->n_pairs);
+    hipError_t e = copy_or_zero(a->dA, nullptr, na, s);
+    if (e == hipSuccess) e = copy_or_zero(a->domega, nullptr, (size_t)d->nheads * d->n_pairs, s);
+    if (e == hipSuccess) e = copy_or_zero(a->dD, nullptr, (size_t)d->nheads, s);
+    if (e == hipSuccess) e = copy_or_zero(a->dh0, nullptr, state_floats(d), s);
+    return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+  }
   const bool te = (d->flags & SSM_F_TWO_ENDPOINT) != 0;
   const bool hasD = (d->flags & SSM_F_HAS_D) != 0;
   if (!a->x || !a->B || !a->C || !a->dy || !a->dt || !a->A || !a->saved || !a->dx || !a->dB ||

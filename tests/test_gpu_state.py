@@ -193,3 +193,48 @@ def test_double_chunk_forward_matches_oracle(case, nseg, monkeypatch):
           f"y={e1:.2e} h_final={eh1:.2e}", flush=True)
     assert ey <= tol(prob) and eh <= tol(prob), (ey, eh)
     assert e1 <= tol(prob) and eh1 <= tol(prob), (e1, eh1)
+
+
+@pytest.mark.parametrize("name,batch,seqlen", [("ssd_siso", 2, 0), ("hybrid", 2, 0),
+                                               ("ssd_siso", 0, 64), ("hybrid", 0, 64)])
+def test_empty_problem_writes_nonempty_outputs(name, batch, seqlen):
+    """No tokens (or no slices): the final state is h0 (zero without it), and dA, domega,
+    dD and dh0, sums over no tokens, are zero.  The outputs start as NaN, so one left
+    unwritten fails."""
+    from selective_diagonal_ssm_amd import _lib
+    prob = workloads.make_problem(workloads.spec(name, batch=batch, seqlen=seqlen, nheads=2,
+                                                 ngroups=2), seed=3, with_dy=True)
+    d = prob["desc"]
+    print(f"[empty] {name} batch={batch} seqlen={seqlen}", flush=True)
+    t = workloads.to_device(prob)
+    desc = _lib.make_desc(d, prob["dtype"])
+    dev = t["dt"].device
+    shape = (batch, d["nheads"], d["dstate"], d["headdim"])
+    nan = float("nan")
+    h0 = torch.randn(shape, dtype=torch.float32, device=dev)
+    y = torch.empty((batch, seqlen, d["nheads"], d["rank_out"], d["headdim"]),
+                    dtype=t["x"].dtype, device=dev)
+    for init in (h0, None):
+        hf = torch.full(shape, nan, dtype=torch.float32, device=dev)
+        _lib.scan_fwd(desc, t["x"], t["B"], t["C"], t["dt"], t["A"], y, omega=t.get("omega"),
+                      beta=t.get("beta"), gamma=t.get("gamma"), D=t.get("D"), h0=init,
+                      h_final=hf)
+        torch.cuda.synchronize()
+        assert torch.equal(hf, h0 if init is not None else torch.zeros_like(hf))
+
+    g = {"dA": torch.full_like(t["A"], nan), "dh0": torch.full(shape, nan, device=dev)}
+    if t.get("omega") is not None:
+        g["domega"] = torch.full_like(t["omega"], nan)
+    if t.get("D") is not None:
+        g["dD"] = torch.full_like(t["D"], nan)
+    te = t.get("beta") is not None
+    _lib.scan_bwd(desc, t["x"], t["B"], t["C"], t["dy"], t["dt"], t["A"], None,
+                  torch.empty_like(t["x"]), torch.empty_like(t["B"]), torch.empty_like(t["C"]),
+                  torch.empty_like(t["dt"]), omega=t.get("omega"), beta=t.get("beta"),
+                  gamma=t.get("gamma"), D=t.get("D"), dA=g["dA"], domega=g.get("domega"),
+                  dbeta=torch.empty_like(t["dt"]) if te else None,
+                  dgamma=torch.empty_like(t["dt"]) if te else None, dD=g.get("dD"),
+                  dh0=g["dh0"])
+    torch.cuda.synchronize()
+    for k, v in g.items():
+        assert torch.count_nonzero(v).item() == 0, k
