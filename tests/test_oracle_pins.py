@@ -111,6 +111,9 @@ def test_p1_constant_decay_is_first_order_iir(oracle_lib):
                       rank_in=3, rank_out=3)),
     ("hybrid", dict(batch=2, seqlen=8, nheads=2, ngroups=2, headdim=3, dstate=6, n_real=2,
                     n_pairs=2, rank_in=2, rank_out=2)),
+    # the pairs of a head decaying at different rates ("different decay laws", arXiv abstract)
+    ("hybrid", dict(batch=1, seqlen=8, nheads=2, ngroups=2, headdim=2, dstate=8, n_real=2,
+                    n_pairs=3, rank_in=2, rank_out=2, pair_rate_per_pair=True)),
 ])
 def test_p2_recurrence_equals_quadratic_form(oracle_lib, name, kw):
     p = workloads.make_problem(small(name, **kw), seed=11)
@@ -139,9 +142,13 @@ def test_p2_output_rank_mismatch_supported(oracle_lib):
 
 
 # ---------------------------------------------------------------- P3 complex pairs
-def test_p3_real_pairs_equal_complex_diagonal(oracle_lib):
+@pytest.mark.parametrize("per_pair", [False, True])
+def test_p3_real_pairs_equal_complex_diagonal(oracle_lib, per_pair):
     p = workloads.make_problem(small("hybrid", batch=2, seqlen=12, nheads=2, ngroups=2,
-                                     headdim=3, dstate=8, n_real=4, n_pairs=2), seed=21)
+                                     headdim=3, dstate=10, n_real=4, n_pairs=3,
+                                     pair_rate_per_pair=per_pair), seed=21)
+    if per_pair:
+        assert len(np.unique(p["A"][0, 4:])) == 3  # three distinct pair rates in one head
     y, _ = oracle.fwd(p)
     yc = forms.complex_y(p["desc"], p["x"], p["B"], p["C"], p["dt"], p["A"], p["omega"],
                          p["beta"], p["gamma"], p["D"])
@@ -344,6 +351,8 @@ GRAD_PAIRS = [("x", "dx"), ("B", "dB"), ("C", "dC"), ("dt", "ddt"), ("A", "dA"),
                     n_pairs=2, rank_in=2, rank_out=2)),
     ("hybrid", dict(batch=1, seqlen=8, nheads=4, ngroups=2, headdim=2, dstate=4, n_real=2,
                     n_pairs=1, rank_in=1, rank_out=1)),
+    ("hybrid", dict(batch=1, seqlen=7, nheads=2, ngroups=2, headdim=2, dstate=8, n_real=2,
+                    n_pairs=3, rank_in=2, rank_out=2, pair_rate_per_pair=True)),
 ])
 def test_p8_adjoint_matches_autograd_of_quadratic_form(oracle_lib, name, kw):
     p = workloads.make_problem(small(name, **kw), seed=81, with_dy=True)

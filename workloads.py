@@ -29,6 +29,16 @@ ssd_mimo_bwd           ssd_mimo at b=2, L=16384, fwd + bwd, dy ~ N(0,1)
 
 Draw order (numpy PCG64, ``default_rng(seed)``): dt, A, omega, beta, gamma, D,
 x, B, C, dy.
+
+Optional spec keys (absent from the workloads above, so their draws are unchanged):
+
+``pair_rate_per_pair``  draw the rotating pairs' decay rates per (head, pair) instead of
+                        one per head (the pairs of a head then decay at different rates)
+``dt_spike_prob``       probability (a float, or a list with one entry per head) that a
+                        token's raw step is replaced by a spike ~ N(dt_spike_mean,
+                        dt_spike_std): steps large enough to wipe a state row within a
+                        few tokens.  Spikes come from a second generator,
+                        ``default_rng([seed, 1])``, so the other draws do not move.
 """
 from __future__ import annotations
 
@@ -102,8 +112,12 @@ def make_problem(spec_or_name, seed: int = 0, with_dy: bool | None = None) -> di
             A = rng.uniform(s["A_lo"], s["A_hi"], size=(H,)).astype(f32)
     else:
         real = rng.uniform(s["A_lo"], s["A_hi"], size=(H, nr)).astype(f32)
-        pair_rate = rng.uniform(s["A_lo"], s["A_hi"], size=(H,)).astype(f32)
-        A = np.concatenate([real, np.repeat(pair_rate[:, None], npairs, axis=1)], axis=1)
+        if s.get("pair_rate_per_pair", False):
+            pair_rate = rng.uniform(s["A_lo"], s["A_hi"], size=(H, npairs)).astype(f32)
+        else:
+            pair_rate = np.repeat(rng.uniform(s["A_lo"], s["A_hi"], size=(H,)).astype(f32)[:, None],
+                                  npairs, axis=1)
+        A = np.concatenate([real, pair_rate], axis=1)
         A = np.ascontiguousarray(A, dtype=f32)
     omega = (rng.uniform(0.0, math.pi, size=(H, npairs)).astype(f32) if npairs
              else np.zeros((H, 0), dtype=f32))
@@ -119,6 +133,14 @@ def make_problem(spec_or_name, seed: int = 0, with_dy: bool | None = None) -> di
     C = rng.standard_normal((b, T, G, O, N), dtype=f32) * sc
     want_dy = s.get("backward", False) if with_dy is None else with_dy
     dy = rng.standard_normal((b, T, H, O, P), dtype=f32) if want_dy else None
+    spike = s.get("dt_spike_prob", 0.0)
+    if np.any(np.asarray(spike) > 0):
+        r2 = np.random.default_rng([seed, 1])
+        prob_h = np.broadcast_to(np.asarray(spike, dtype=np.float64), (H,))
+        hit = r2.random((b, T, H)) < prob_h
+        val = (r2.standard_normal((b, T, H), dtype=f32) * f32(s.get("dt_spike_std", 0.5))
+               + f32(s.get("dt_spike_mean", 2.0)))
+        dt = np.where(hit, val, dt).astype(f32)
     if s["dtype"] == "bf16":
         x, B, C = round_bf16(x), round_bf16(B), round_bf16(C)
         dy = round_bf16(dy) if dy is not None else None
