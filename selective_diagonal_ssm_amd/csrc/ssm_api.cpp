@@ -429,6 +429,7 @@ int ssm_scan_bwd(const ssm_desc* d, const ssm_bwd_args* a, void* ws, size_t ws_b
   p.has_D = hasD ? 1 : 0;
   p.npart = npart_of(d, pl);
   p.head_rates = pl.head_rates ? 1 : 0;
+  p.chunk_grid_cap = env_int("SSM_BWD_CHUNK_GRID", 0);
   const hipError_t e = ssm::launch_bwd(key, p, static_cast<hipStream_t>(stream), a->events);
   return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
 }

@@ -1813,7 +1813,8 @@ hipError_t launch_bwd(const BwdKey& k, const BwdParams& p, hipStream_t stream,
       const void* kfn = reinterpret_cast<const void*>(                                        \
           &ssm_bwd_chunk<BF, NN, PP, RR, KRR, QTT, CO, CHUNK_NT(NN, CO), SP>);                \
       const int items = slices * p.nchunks;                                                   \
-      const int grid = std::min(items, device_cus() * blocks_per_cu(kfn, CHUNK_NT(NN, CO), occ)); \
+      int grid = std::min(items, device_cus() * blocks_per_cu(kfn, CHUNK_NT(NN, CO), occ));   \
+      if (p.chunk_grid_cap > 0) grid = std::min(grid, p.chunk_grid_cap);                      \
       hipLaunchKernelGGL((ssm_bwd_chunk<BF, NN, PP, RR, KRR, QTT, CO, CHUNK_NT(NN, CO), SP>),     \
                          dim3(grid), dim3(CHUNK_NT(NN, CO)), 0, stream, p);                   \
     }                                                                                         \

@@ -94,6 +94,9 @@ struct BwdParams {
   int nseg, chunks_per_seg;  // sequence segments of the boundary-adjoint sweep
   int softplus, has_D, npart;
   int head_rates;
+  // upper bound on the persistent chunk-gradient grid (0 = one workgroup per resident
+  // slot); a smaller grid makes each workgroup walk more items, with the same results
+  int chunk_grid_cap;
   // local pass: every segment but the first is cut into nsub ranges of lsub tokens
   int seg_tokens, nsub, lsub;
   float* gloc;     // [slice][nseg - 1][nsub][N][P] range adjoints at the ranges' first tokens

@@ -22,6 +22,15 @@ def tol(prob):
     return BF16_TOL if prob["dtype"] == "bf16" else F32_TOL
 
 
+def rel_l2_by_position(a, ref, period, axis=1):
+    """rel-L2 of the tokens at each position inside a chunk of `period` tokens
+    (token index mod period along `axis`): a systematic error at one position of
+    every chunk stands out here, where the whole-tensor norm would dilute it."""
+    a = np.moveaxis(np.asarray(a, dtype=np.float64), axis, 0)
+    ref = np.moveaxis(np.asarray(ref, dtype=np.float64), axis, 0)
+    return np.array([rel_l2(a[j::period], ref[j::period]) for j in range(min(period, len(a)))])
+
+
 def run_fwd(prob, chunk=0, save=False):
     t = workloads.to_device(prob)
     y, saved = ssm.forward(prob["desc"], prob["dtype"], t["x"], t["B"], t["C"], t["dt"], t["A"],

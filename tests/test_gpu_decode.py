@@ -37,6 +37,15 @@ CASES = {
     "bf16_hybrid": ("hybrid", dict(batch=2, nheads=2, ngroups=2)),
     "bf16_p256": ("ssd_siso", dict(batch=1, nheads=2, ngroups=2, headdim=256, dstate=64,
                                    n_real=64)),
+    # one decay rate per (head, pair); steps given directly (no softplus)
+    "f32_hybrid_pair_rates": ("hybrid", dict(dtype="f32", dstate=32, n_real=16, n_pairs=8,
+                                             headdim=16, batch=2, nheads=2, ngroups=2,
+                                             pair_rate_per_pair=True)),
+    "bf16_hybrid_pair_rates": ("hybrid", dict(batch=2, nheads=2, ngroups=2,
+                                              pair_rate_per_pair=True)),
+    "f32_hybrid_no_softplus": ("hybrid", dict(dtype="f32", dstate=32, n_real=16, n_pairs=8,
+                                              headdim=16, batch=2, nheads=2, ngroups=2,
+                                              dt_softplus=False, dt_mean=0.1, dt_std=0.02)),
 }
 
 

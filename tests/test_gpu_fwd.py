@@ -11,7 +11,7 @@ import torch
 
 import oracle
 import workloads
-from gpu_util import rel_l2, run_fwd, tol
+from gpu_util import rel_l2, rel_l2_by_position, run_fwd, tol
 
 pytestmark = pytest.mark.gpu
 
@@ -75,6 +75,33 @@ SMALL_CASES = {
                                         rank_out=4, has_D=False)),
     "bf16_hybrid_r2o1": ("hybrid", dict(batch=2, seqlen=150, nheads=4, ngroups=2, rank_in=2,
                                         rank_out=1, has_D=False)),
+    # the pairs of a head decaying at different rates (one rate per (head, pair))
+    "f32_hybrid_pair_rates": ("hybrid", dict(dtype="f32", dstate=32, n_real=16, n_pairs=8,
+                                             headdim=16, batch=2, nheads=2, ngroups=2,
+                                             seqlen=77, pair_rate_per_pair=True)),
+    "f32_pairs_only_pair_rates": ("hybrid", dict(dtype="f32", dstate=32, n_real=0, n_pairs=16,
+                                                 headdim=16, rank_in=1, rank_out=1, batch=1,
+                                                 nheads=2, ngroups=2, seqlen=70,
+                                                 pair_rate_per_pair=True)),
+    "bf16_hybrid_pair_rates": ("hybrid", dict(batch=2, seqlen=150, nheads=2, ngroups=2,
+                                              pair_rate_per_pair=True)),
+    "bf16_hybrid_r1_pair_rates": ("hybrid_r1", dict(batch=2, seqlen=150, nheads=2, ngroups=2,
+                                                    pair_rate_per_pair=True)),
+    # steps given directly (no softplus in the kernel), positive
+    "f32_head_no_softplus": ("ssd_siso", dict(dtype="f32", dstate=32, n_real=32, headdim=16,
+                                              batch=2, nheads=2, ngroups=2, seqlen=150,
+                                              dt_softplus=False, dt_mean=0.1, dt_std=0.02)),
+    "f32_hybrid_no_softplus": ("hybrid", dict(dtype="f32", dstate=32, n_real=16, n_pairs=8,
+                                              headdim=16, batch=2, nheads=2, ngroups=2,
+                                              seqlen=77, dt_softplus=False, dt_mean=0.1,
+                                              dt_std=0.02)),
+    "bf16_ssd_siso_no_softplus": ("ssd_siso", dict(batch=2, seqlen=300, nheads=2, ngroups=2,
+                                                   dt_softplus=False, dt_mean=0.1,
+                                                   dt_std=0.02)),
+    "bf16_mimo_no_softplus": ("ssd_mimo", dict(batch=2, seqlen=200, nheads=2, ngroups=2,
+                                               dt_softplus=False, dt_mean=0.1, dt_std=0.02)),
+    "bf16_hybrid_no_softplus": ("hybrid", dict(batch=2, seqlen=150, nheads=2, ngroups=2,
+                                               dt_softplus=False, dt_mean=0.1, dt_std=0.02)),
 }
 
 
@@ -94,20 +121,24 @@ FULL = ["ssd_siso", "ssd_mimo", "hybrid", "hybrid_r1"]
 
 
 @pytest.mark.parametrize("name", FULL)
-def test_fwd_full_size_sampled_slices(name):
+@pytest.mark.parametrize("save", [False, True])
+def test_fwd_full_size_whole_tensor(name, save):
+    """The workload at its full size, in the launch configuration the bench times
+    (save=False: the forward alone; save=True: the forward of a training step, which
+    also writes the chunk-boundary states), against the oracle over every slice: one
+    rel-L2 over the whole output, and one per token position inside a chunk."""
     prob = workloads.make_problem(name, seed=0)
     d = prob["desc"]
-    print(f"[fwd-full] {name} desc={d}", flush=True)
-    y, _, _ = run_fwd(prob)
-    rng = np.random.default_rng(1)
-    slices = [(int(rng.integers(d["batch"])), int(rng.integers(d["nheads"]))) for _ in range(6)]
-    slices += [(0, 0), (d["batch"] - 1, d["nheads"] - 1)]
-    ref, _ = oracle.fwd(prob, slices=slices)
-    for b, h in slices:
-        err = rel_l2(y[b, :, h], ref[b, :, h])
-        print(f"[fwd-full] {name} slice=({b},{h}) rel_l2={err:.3e}", flush=True)
-        assert err <= tol(prob), (b, h, err)
+    print(f"[fwd-full] {name} save={save} desc={d}", flush=True)
+    y, _, _ = run_fwd(prob, save=save)
     assert np.isfinite(y).all()
+    ref, _ = oracle.fwd(prob)
+    err = rel_l2(y, ref)
+    pos = rel_l2_by_position(y, ref, 64)
+    print(f"[fwd-full] {name} save={save} rel_l2={err:.3e} worst position "
+          f"{int(pos.argmax())}: {pos.max():.3e}", flush=True)
+    assert err <= tol(prob), err
+    assert pos.max() <= tol(prob), pos
 
 
 def test_fwd_deterministic():

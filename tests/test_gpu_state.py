@@ -29,6 +29,11 @@ CASES = {
     "bf16_ssd_siso": ("ssd_siso", dict(batch=2, seqlen=200, nheads=2, ngroups=2)),
     "bf16_ssd_mimo": ("ssd_mimo", dict(batch=2, seqlen=100, nheads=2, ngroups=2)),
     "bf16_hybrid": ("hybrid", dict(batch=2, seqlen=90, nheads=2, ngroups=2)),
+    "f32_hybrid_pair_rates": ("hybrid", dict(dtype="f32", dstate=32, n_real=16, n_pairs=8,
+                                             headdim=16, batch=2, nheads=2, ngroups=2,
+                                             seqlen=77, pair_rate_per_pair=True)),
+    "bf16_hybrid_pair_rates": ("hybrid", dict(batch=2, seqlen=90, nheads=2, ngroups=2,
+                                              pair_rate_per_pair=True)),
 }
 
 
