@@ -103,6 +103,70 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+# ---------------------------------------------------------------- argument checks
+# The C ABI sees plain pointers, so a tensor of the wrong size, dtype or layout would be
+# read or written past its end (or misread) on the device.  The wrappers below check
+# every tensor against the descriptor first: the element count it implies, the dtype
+# (io dtype for x, B, C, y, dy and their gradients; fp32 for the rest), contiguity and
+# placement on the GPU.  Checks run before anything is enqueued.
+
+def _io_torch_dtype(desc: SsmDesc):
+    import torch
+    return torch.bfloat16 if desc.io_dtype == SSM_BF16 else torch.float32
+
+
+def _check(seen, name, t, numel, dtype, required=True, at_least=False):
+    if t is None:
+        if required and numel > 0:
+            raise SsmError(-1, f"{name} is required")
+        return
+    n = t.numel()
+    if (n < numel) if at_least else (n != numel):
+        raise SsmError(-2, f"{name} has {n} elements, the descriptor needs "
+                           f"{'at least ' if at_least else ''}{numel}")
+    if dtype is not None and t.dtype != dtype:
+        raise SsmError(-3, f"{name} is {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise SsmError(-2, f"{name} is not contiguous (the kernels read it row-major)")
+    seen.append((name, t))
+
+
+def _check_devices(seen):
+    """After every shape check of a call: each non-empty tensor lives on the GPU."""
+    for name, t in seen:
+        if t.numel() > 0 and not t.is_cuda:
+            raise SsmError(-1, f"{name} is not a GPU tensor")
+
+
+def _na(desc: SsmDesc) -> int:
+    return desc.nheads * (1 if desc.decay_mode == SSM_DECAY_HEAD else desc.n_real + desc.n_pairs)
+
+
+def _check_params(seen, desc: SsmDesc, dt, A, omega, beta, gamma, D, steps: int):
+    import torch
+    f32 = torch.float32
+    _check(seen, "dt", dt, steps, f32)
+    _check(seen, "A", A, _na(desc), f32)
+    _check(seen, "omega", omega, desc.nheads * desc.n_pairs, f32, required=desc.n_pairs > 0)
+    te = bool(desc.flags & SSM_F_TWO_ENDPOINT)
+    _check(seen, "beta", beta, steps, f32, required=te)
+    _check(seen, "gamma", gamma, steps, f32, required=te)
+    _check(seen, "D", D, desc.nheads, f32, required=bool(desc.flags & SSM_F_HAS_D))
+
+
+def _check_scan(seen, desc: SsmDesc, x, B, C, dt, A, omega, beta, gamma, D):
+    io = _io_torch_dtype(desc)
+    b, L, H, G = desc.batch, desc.seqlen, desc.nheads, desc.ngroups
+    _check(seen, "x", x, b * L * H * desc.rank_in * desc.headdim, io)
+    _check(seen, "B", B, b * L * G * desc.rank_in * desc.dstate, io)
+    _check(seen, "C", C, b * L * G * desc.rank_out * desc.dstate, io)
+    _check_params(seen, desc, dt, A, omega, beta, gamma, D, b * L * H)
+
+
+def _state_numel(desc: SsmDesc) -> int:
+    return desc.batch * desc.nheads * desc.dstate * desc.headdim
+
+
 def _stream(stream):
     if stream is None:
         import torch
@@ -141,6 +205,21 @@ def scan_fwd(desc: SsmDesc, x, B, C, dt, A, y, omega=None, beta=None, gamma=None
     """Enqueue the forward scan; all tensors are caller-allocated device tensors.
     `h0` / `h_final`: optional fp32 [batch][nheads][N][P] initial / final states.
     `events`: optional 2 torch.cuda.Event recorded around the kernel."""
+    import torch
+    seen = []
+    _check_scan(seen, desc, x, B, C, dt, A, omega, beta, gamma, D)
+    b, L, H = desc.batch, desc.seqlen, desc.nheads
+    _check(seen, "y", y, b * L * H * desc.rank_out * desc.headdim, _io_torch_dtype(desc))
+    if saved is not None:
+        _check(seen, "saved", saved, 0, None, at_least=True)
+        if saved.numel() * saved.element_size() < saved_bytes(desc):
+            raise SsmError(-2, f"saved holds {saved.numel() * saved.element_size()} bytes, "
+                               f"the descriptor needs {saved_bytes(desc)}")
+    _check(seen, "h0", h0, _state_numel(desc), torch.float32, required=False)
+    _check(seen, "h_final", h_final, _state_numel(desc), torch.float32, required=False)
+    if ws is not None:
+        _check(seen, "ws", ws, 0, None, at_least=True)
+    _check_devices(seen)
     ev, _keep = _events(events)
     args = SsmFwdArgs(_ptr(x), _ptr(B), _ptr(C), _ptr(dt), _ptr(A), _ptr(omega), _ptr(beta),
                       _ptr(gamma), _ptr(D), _ptr(y), _ptr(saved), _ptr(h0), _ptr(h_final), ev)
@@ -157,6 +236,30 @@ def scan_bwd(desc: SsmDesc, x, B, C, dy, dt, A, saved, dx, dB, dC, ddt, omega=No
     """Enqueue the fused reverse pass; all tensors are caller-allocated device tensors.
     `dh0`: optional fp32 [batch][nheads][N][P] gradient of the initial state.
     `events`: optional 4 torch.cuda.Event recorded around the pass's three kernels."""
+    import torch
+    seen = []
+    _check_scan(seen, desc, x, B, C, dt, A, omega, beta, gamma, D)
+    io, f32 = _io_torch_dtype(desc), torch.float32
+    b, L, H, G = desc.batch, desc.seqlen, desc.nheads, desc.ngroups
+    _check(seen, "dy", dy, b * L * H * desc.rank_out * desc.headdim, io)
+    _check(seen, "dx", dx, b * L * H * desc.rank_in * desc.headdim, io)
+    _check(seen, "dB", dB, b * L * G * desc.rank_in * desc.dstate, io)
+    _check(seen, "dC", dC, b * L * G * desc.rank_out * desc.dstate, io)
+    _check(seen, "ddt", ddt, b * L * H, f32)
+    if b * L > 0:
+        _check(seen, "saved", saved, 0, None, at_least=True)
+        if saved.numel() * saved.element_size() < saved_bytes(desc):
+            raise SsmError(-2, f"saved holds {saved.numel() * saved.element_size()} bytes, "
+                               f"the descriptor needs {saved_bytes(desc)}")
+    _check(seen, "dA", dA, _na(desc), f32, required=False)
+    _check(seen, "domega", domega, desc.nheads * desc.n_pairs, f32, required=False)
+    _check(seen, "dbeta", dbeta, b * L * H, f32, required=False)
+    _check(seen, "dgamma", dgamma, b * L * H, f32, required=False)
+    _check(seen, "dD", dD, desc.nheads, f32, required=False)
+    _check(seen, "dh0", dh0, _state_numel(desc), f32, required=False)
+    if ws is not None:
+        _check(seen, "ws", ws, 0, None, at_least=True)
+    _check_devices(seen)
     ev, _keep = _events(events)
     args = SsmBwdArgs(_ptr(x), _ptr(B), _ptr(C), _ptr(dy), _ptr(dt), _ptr(A), _ptr(omega),
                       _ptr(beta), _ptr(gamma), _ptr(D), _ptr(saved), _ptr(dx), _ptr(dB),
@@ -174,6 +277,19 @@ def decode_step(desc: SsmDesc, x, B, C, dt, A, state, y, omega=None, beta=None, 
     """Enqueue one recurrent step (descriptor with seqlen 1): updates the fp32
     [batch][nheads][N][P] `state` in place and writes y.  `x_prev` / `B_prev`: the
     previous token's x and B for two-endpoint writes (None at the first token)."""
+    import torch
+    seen = []
+    io = _io_torch_dtype(desc)
+    b, H, G = desc.batch, desc.nheads, desc.ngroups
+    _check(seen, "x", x, b * H * desc.rank_in * desc.headdim, io)
+    _check(seen, "B", B, b * G * desc.rank_in * desc.dstate, io)
+    _check(seen, "C", C, b * G * desc.rank_out * desc.dstate, io)
+    _check_params(seen, desc, dt, A, omega, beta, gamma, D, b * H)
+    _check(seen, "x_prev", x_prev, b * H * desc.rank_in * desc.headdim, io, required=False)
+    _check(seen, "B_prev", B_prev, b * G * desc.rank_in * desc.dstate, io, required=False)
+    _check(seen, "state", state, _state_numel(desc), torch.float32)
+    _check(seen, "y", y, b * H * desc.rank_out * desc.headdim, io)
+    _check_devices(seen)
     args = SsmDecodeArgs(_ptr(x), _ptr(B), _ptr(C), _ptr(dt), _ptr(A), _ptr(omega), _ptr(beta),
                          _ptr(gamma), _ptr(D), _ptr(x_prev), _ptr(B_prev), _ptr(state), _ptr(y))
     rc = load().ssm_decode_step(ctypes.byref(desc), ctypes.byref(args), _stream(stream))

@@ -1,8 +1,14 @@
 """torch-facing wrapper: allocate outputs / saved states / workspace and call the C ABI.
 
-Only allocation and argument marshalling happen here.
+Only allocation and argument marshalling happen here.  When a ``stream`` is given,
+every tensor of a call (outputs, saved states, workspace) is allocated with that stream
+current, so torch's caching allocator ties the memory to the stream the kernels run
+on: the workspace, dropped on return, goes back to that stream's pool and is not
+handed to work on another stream while the kernels may still use it.
 """
 from __future__ import annotations
+
+import contextlib
 
 import torch
 
@@ -13,6 +19,10 @@ def _dtype(io_dtype: str):
     return torch.bfloat16 if io_dtype == "bf16" else torch.float32
 
 
+def _on(stream):
+    return torch.cuda.stream(stream) if stream is not None else contextlib.nullcontext()
+
+
 def forward(desc_dict: dict, io_dtype: str, x, B, C, dt, A, omega=None, beta=None, gamma=None,
             D=None, save_for_backward: bool = False, chunk: int = 0, stream=None, h0=None,
             return_final_state: bool = False):
@@ -21,20 +31,21 @@ def forward(desc_dict: dict, io_dtype: str, x, B, C, dt, A, omega=None, beta=Non
     ``h0``: optional fp32 [batch][nheads][N][P] state before token 0."""
     desc = _lib.make_desc(desc_dict, io_dtype, chunk)
     d = desc_dict
-    y = torch.empty((d["batch"], d["seqlen"], d["nheads"], d["rank_out"], d["headdim"]),
-                    dtype=_dtype(io_dtype), device=x.device)
-    saved = None
-    if save_for_backward:
-        nbytes = _lib.saved_bytes(desc)
-        saved = torch.empty(max(nbytes // 4, 1), dtype=torch.float32, device=x.device)
-    wsb = _lib.workspace_bytes(desc, False)
-    ws = torch.empty(wsb, dtype=torch.uint8, device=x.device) if wsb else None
-    h_final = None
-    if return_final_state:
-        h_final = torch.empty((d["batch"], d["nheads"], d["dstate"], d["headdim"]),
-                              dtype=torch.float32, device=x.device)
-    _lib.scan_fwd(desc, x, B, C, dt, A, y, omega=omega, beta=beta, gamma=gamma, D=D, saved=saved,
-                  ws=ws, stream=stream, h0=h0, h_final=h_final)
+    with _on(stream):
+        y = torch.empty((d["batch"], d["seqlen"], d["nheads"], d["rank_out"], d["headdim"]),
+                        dtype=_dtype(io_dtype), device=x.device)
+        saved = None
+        if save_for_backward:
+            nbytes = _lib.saved_bytes(desc)
+            saved = torch.empty(max((nbytes + 3) // 4, 1), dtype=torch.float32, device=x.device)
+        wsb = _lib.workspace_bytes(desc, False)
+        ws = torch.empty(wsb, dtype=torch.uint8, device=x.device) if wsb else None
+        h_final = None
+        if return_final_state:
+            h_final = torch.empty((d["batch"], d["nheads"], d["dstate"], d["headdim"]),
+                                  dtype=torch.float32, device=x.device)
+        _lib.scan_fwd(desc, x, B, C, dt, A, y, omega=omega, beta=beta, gamma=gamma, D=D,
+                      saved=saved, ws=ws, stream=stream, h0=h0, h_final=h_final)
     if return_final_state:
         return y, saved, h_final
     return y, saved
@@ -49,32 +60,33 @@ def backward(desc_dict: dict, io_dtype: str, x, B, C, dy, dt, A, saved, omega=No
     d = desc_dict
     dev = x.device
     f32 = torch.float32
-    g = {
-        "dx": torch.empty_like(x),
-        "dB": torch.empty_like(B),
-        "dC": torch.empty_like(C),
-        "ddt": torch.empty_like(dt),
-    }
-    if "dA" in want:
-        g["dA"] = torch.empty_like(A)
-    if "domega" in want and d["n_pairs"] > 0:
-        g["domega"] = torch.empty((d["nheads"], d["n_pairs"]), dtype=f32, device=dev)
-    if d["two_endpoint"]:
-        if "dbeta" in want:
-            g["dbeta"] = torch.empty_like(dt)
-        if "dgamma" in want:
-            g["dgamma"] = torch.empty_like(dt)
-    if d["has_D"] and "dD" in want:
-        g["dD"] = torch.empty((d["nheads"],), dtype=f32, device=dev)
-    if "dh0" in want:
-        g["dh0"] = torch.empty((d["batch"], d["nheads"], d["dstate"], d["headdim"]), dtype=f32,
-                               device=dev)
-    wsb = _lib.workspace_bytes(desc, True)
-    ws = torch.empty(wsb, dtype=torch.uint8, device=dev) if wsb else None
-    _lib.scan_bwd(desc, x, B, C, dy, dt, A, saved, g["dx"], g["dB"], g["dC"], g["ddt"],
-                  omega=omega, beta=beta, gamma=gamma, D=D, dA=g.get("dA"),
-                  domega=g.get("domega"), dbeta=g.get("dbeta"), dgamma=g.get("dgamma"),
-                  dD=g.get("dD"), ws=ws, stream=stream, dh0=g.get("dh0"))
+    with _on(stream):
+        g = {
+            "dx": torch.empty_like(x),
+            "dB": torch.empty_like(B),
+            "dC": torch.empty_like(C),
+            "ddt": torch.empty_like(dt),
+        }
+        if "dA" in want:
+            g["dA"] = torch.empty_like(A)
+        if "domega" in want and d["n_pairs"] > 0:
+            g["domega"] = torch.empty((d["nheads"], d["n_pairs"]), dtype=f32, device=dev)
+        if d["two_endpoint"]:
+            if "dbeta" in want:
+                g["dbeta"] = torch.empty_like(dt)
+            if "dgamma" in want:
+                g["dgamma"] = torch.empty_like(dt)
+        if d["has_D"] and "dD" in want:
+            g["dD"] = torch.empty((d["nheads"],), dtype=f32, device=dev)
+        if "dh0" in want:
+            g["dh0"] = torch.empty((d["batch"], d["nheads"], d["dstate"], d["headdim"]),
+                                   dtype=f32, device=dev)
+        wsb = _lib.workspace_bytes(desc, True)
+        ws = torch.empty(wsb, dtype=torch.uint8, device=dev) if wsb else None
+        _lib.scan_bwd(desc, x, B, C, dy, dt, A, saved, g["dx"], g["dB"], g["dC"], g["ddt"],
+                      omega=omega, beta=beta, gamma=gamma, D=D, dA=g.get("dA"),
+                      domega=g.get("domega"), dbeta=g.get("dbeta"), dgamma=g.get("dgamma"),
+                      dD=g.get("dD"), ws=ws, stream=stream, dh0=g.get("dh0"))
     return g
 
 
@@ -86,8 +98,9 @@ def decode_step(desc_dict: dict, io_dtype: str, x, B, C, dt, A, state, omega=Non
     [batch][nheads][O][P]."""
     d = dict(desc_dict, seqlen=1)
     desc = _lib.make_desc(d, io_dtype, 0)
-    y = torch.empty((d["batch"], d["nheads"], d["rank_out"], d["headdim"]),
-                    dtype=_dtype(io_dtype), device=x.device)
-    _lib.decode_step(desc, x, B, C, dt, A, state, y, omega=omega, beta=beta, gamma=gamma, D=D,
-                     x_prev=x_prev, B_prev=B_prev, stream=stream)
+    with _on(stream):
+        y = torch.empty((d["batch"], d["nheads"], d["rank_out"], d["headdim"]),
+                        dtype=_dtype(io_dtype), device=x.device)
+        _lib.decode_step(desc, x, B, C, dt, A, state, y, omega=omega, beta=beta, gamma=gamma,
+                         D=D, x_prev=x_prev, B_prev=B_prev, stream=stream)
     return y

@@ -167,3 +167,77 @@ def test_decode_step_validation_before_launch(dkw, akw, status):
     assert lib.ssm_decode_step(ctypes.byref(d), ctypes.byref(a), None) == status
     assert lib.ssm_decode_step(None, ctypes.byref(a), None) == -1
     assert lib.ssm_decode_step(ctypes.byref(d), None, None) in (-1, status)
+
+
+# ---------------------------------------------------------------- binding argument checks
+def _cpu_problem(name="hybrid", **kw):
+    import torch
+
+    import workloads
+    spec = workloads.spec(name, batch=1, seqlen=20, nheads=2, ngroups=2, **kw)
+    prob = workloads.make_problem(spec, seed=0, with_dy=True)
+    io = torch.bfloat16 if prob["dtype"] == "bf16" else torch.float32
+    t = {k: torch.from_numpy(prob[k]).to(io) for k in ("x", "B", "C", "dy")}
+    for k in ("dt", "A", "omega", "beta", "gamma", "D"):
+        if prob.get(k) is not None:
+            t[k] = torch.from_numpy(prob[k]).contiguous()
+    desc = _lib.make_desc(prob["desc"], prob["dtype"])
+    t["y"] = torch.empty_like(t["dy"])
+    return desc, t
+
+
+def _fwd(desc, t, **over):
+    a = dict(t)
+    a.update(over)
+    _lib.scan_fwd(desc, a["x"], a["B"], a["C"], a["dt"], a["A"], a["y"], omega=a.get("omega"),
+                  beta=a.get("beta"), gamma=a.get("gamma"), D=a.get("D"))
+
+
+@pytest.mark.parametrize("what", ["numel", "dtype", "layout", "device", "missing", "params"])
+def test_binding_rejects_bad_tensors_before_the_call(what):
+    """The ctypes wrappers check every tensor against the descriptor (element count,
+    dtype, contiguity, GPU placement, required pointers) and raise before anything is
+    enqueued: on this CPU-only host the checks are reached with host tensors."""
+    import torch
+    desc, t = _cpu_problem()
+    if what == "numel":      # a tensor smaller than the descriptor implies
+        bad, msg = dict(x=t["x"][:, :-1]), "elements"
+    elif what == "dtype":    # fp32 where the io dtype is bf16
+        bad, msg = dict(B=t["B"].float()), "expected"
+    elif what == "layout":   # a strided view (e.g. a split of a packed projection)
+        wide = torch.cat([t["C"], t["C"]], dim=-1)
+        bad, msg = dict(C=wide[..., : t["C"].shape[-1]]), "contiguous"
+    elif what == "device":   # every check passes but the tensors are on the host
+        bad, msg = dict(), "GPU"
+    elif what == "missing":  # two-endpoint writes need beta and gamma
+        bad, msg = dict(beta=None), "required"
+    else:                    # per-head rates of the wrong length
+        bad, msg = dict(A=t["A"][:1]), "elements"
+    with pytest.raises(_lib.SsmError, match=msg):
+        _fwd(desc, t, **bad)
+
+
+def test_binding_checks_gradient_and_step_tensors():
+    import torch
+    desc, t = _cpu_problem()
+    saved = torch.empty(ssm.saved_bytes(desc) // 4 + 1, dtype=torch.float32)
+    g = dict(dx=torch.empty_like(t["x"]), dB=torch.empty_like(t["B"]),
+             dC=torch.empty_like(t["C"]), ddt=torch.empty_like(t["dt"]))
+    with pytest.raises(_lib.SsmError, match="dB"):
+        _lib.scan_bwd(desc, t["x"], t["B"], t["C"], t["dy"], t["dt"], t["A"], saved, g["dx"],
+                      g["dB"][:, :-1], g["dC"], g["ddt"], omega=t["omega"], beta=t["beta"],
+                      gamma=t["gamma"], D=t["D"])
+    with pytest.raises(_lib.SsmError, match="saved"):
+        _lib.scan_bwd(desc, t["x"], t["B"], t["C"], t["dy"], t["dt"], t["A"], saved[:8],
+                      g["dx"], g["dB"], g["dC"], g["ddt"], omega=t["omega"], beta=t["beta"],
+                      gamma=t["gamma"], D=t["D"])
+    step = _lib.make_desc(dict(batch=1, seqlen=1, nheads=2, ngroups=2, headdim=64, dstate=64,
+                               rank_in=2, rank_out=2, n_real=32, n_pairs=16, decay_mode="coord",
+                               dt_softplus=True, two_endpoint=True, has_D=True), "bf16")
+    x = t["x"][:, 0].contiguous()
+    state = torch.empty(1, 2, 64, 64, dtype=torch.float32)
+    with pytest.raises(_lib.SsmError, match="state"):
+        _lib.decode_step(step, x, t["B"][:, 0].contiguous(), t["C"][:, 0].contiguous(),
+                         t["dt"][:, 0].contiguous(), t["A"], state[:, :1], torch.empty_like(x),
+                         omega=t["omega"], beta=t["beta"][:, 0].contiguous(),
+                         gamma=t["gamma"][:, 0].contiguous(), D=t["D"])
