@@ -3,14 +3,18 @@
 
 One step = the whole hot path over one batch of synthetic input: the forward
 chunked scan (writing the chunk-boundary states the reverse pass needs) and the
-fused reverse-mode pass.  The default workload is the Mamba-2-style SSD SISO
-problem (batch 8, L 2048, 24 heads, P 64, N 128, bf16, chunk 64), seeded
-synthetic inputs already resident in HBM.
+fused reverse-mode pass.  The default workload is the largest one that fits one
+GPU: the HybridMamba training step (batch 2, L 16384, 32 heads, P 64, N 64 = 32
+per-row-decay rows + 16 rotating pairs, rank 2, two-endpoint writes, bf16, forward
++ reverse), seeded synthetic inputs already resident in HBM.  Each timed step is
+followed by a 1 GiB scratch write outside its events, so every step starts with
+cold caches; the value is the median over the timed steps.
 
 Prints ONE JSON line: metric, value (Mtokens/s; a token is one (batch, position)
-across all heads), ms_per_step, the roofline of the dominant kernel (timed live
-with HIP events on the stream the kernels run on), and the fp64 CPU oracle timed
-on a bounded sample of the same workload.
+across all heads), ms_per_step, the step-time percentiles and the warm-cache figure,
+the roofline of the dominant kernel (timed live with HIP events on the stream the
+kernels run on) and of the forward scan, the saved-for-backward and peak memory,
+and the fp64 CPU oracle timed on a bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -121,16 +125,39 @@ def cpu_baseline(prob: dict, mode: str, target_s: float = 15.0, h0=None):
                       f", fp64, {t:.1f} s"}
 
 
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+FLUSH_BYTES = 1 << 30  # scratch written between timed steps: beyond L2 and the 256 MB cache
+
+
+def pct(v, q):
+    return float(np.percentile(np.asarray(v, dtype=np.float64), q))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="ssd_siso", choices=sorted(workloads.WORKLOADS))
+    ap.add_argument("--workload", default="hybrid_bwd", choices=sorted(workloads.WORKLOADS))
     ap.add_argument("--mode", default="fwdbwd", choices=["fwd", "fwdbwd", "decode"])
     ap.add_argument("--decode-batch", type=int, default=256,
                     help="batch of the recurrent-step measurement (--mode decode)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-flush", action="store_true",
+                    help="time back-to-back steps with no scratch write between them "
+                         "(warm caches; not the reported number)")
+    ap.add_argument("--suite", action="store_true",
+                    help="time every workload (forward for the forward workloads, forward + "
+                         "reverse for the backward ones) and print their geometric means")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (for HBM counter scaling)")
     args = ap.parse_args()
@@ -156,15 +183,26 @@ def main():
     if args.mode == "decode":
         run_decode(args)
         return
+    if args.suite:
+        run_suite(args)
+        return
+    out = measure(args.workload, args.mode, args.steps, args.warmup, flush=not args.no_flush,
+                  cpu=not args.no_cpu_baseline)
+    print(json.dumps(out), flush=True)
 
+
+def measure(workload: str, mode: str, steps: int, warmup: int, flush: bool = True,
+            cpu: bool = True) -> dict:
+    """One bench line for `workload`: `steps` timed steps (forward, or forward + reverse),
+    each followed by a write of FLUSH_BYTES of scratch outside its events."""
     import torch
 
     import selective_diagonal_ssm_amd as ssm
 
-    prob = workloads.make_problem(args.workload, seed=0,
-                                  with_dy=(args.mode == "fwdbwd"))
+    prob = workloads.make_problem(workload, seed=0, with_dy=(mode == "fwdbwd"))
     d = prob["desc"]
     io = prob["dtype"]
+    torch.cuda.reset_peak_memory_stats()
     t = workloads.to_device(prob)
     chunk = prob.get("chunk", 0)
     desc = ssm.make_desc(d, io, chunk)
@@ -173,8 +211,9 @@ def main():
                     dtype=t["x"].dtype, device=dev)
     saved = None
     grads = {}
-    if args.mode == "fwdbwd":
-        saved = torch.empty(ssm.saved_bytes(desc) // 4, dtype=torch.float32, device=dev)
+    saved_bytes = ssm.saved_bytes(desc) if mode == "fwdbwd" else 0
+    if mode == "fwdbwd":
+        saved = torch.empty((saved_bytes + 3) // 4, dtype=torch.float32, device=dev)
         grads = {"dx": torch.empty_like(t["x"]), "dB": torch.empty_like(t["B"]),
                  "dC": torch.empty_like(t["C"]), "ddt": torch.empty_like(t["dt"]),
                  "dA": torch.empty_like(t["A"])}
@@ -186,7 +225,7 @@ def main():
         if d["has_D"]:
             grads["dD"] = torch.empty_like(t["D"])
     ws_f = ssm.workspace_bytes(desc, False)
-    ws_b = ssm.workspace_bytes(desc, True) if args.mode == "fwdbwd" else 0
+    ws_b = ssm.workspace_bytes(desc, True) if mode == "fwdbwd" else 0
     ws = torch.empty(max(ws_f, ws_b, 1), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
 
@@ -203,30 +242,35 @@ def main():
                      dgamma=grads.get("dgamma"), dD=grads.get("dD"), ws=ws, stream=stream,
                      events=events)
 
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         fwd()
-        if args.mode == "fwdbwd":
+        if mode == "fwdbwd":
             bwd()
     torch.cuda.synchronize()
+    # M3: every buffer of the step is allocated and one step has run
+    peak_bytes = torch.cuda.max_memory_allocated()
+    input_bytes = sum(v.numel() * v.element_size() for k, v in t.items() if k != "dy")
+    scratch = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device=dev) if flush else None
 
     # HIP events recorded by the library on the stream the kernels run on.  Each
     # record costs GPU time between kernels, so the per-kernel breakdown comes from a
     # pass of its own (events around every kernel); the timed region records events
-    # only around the dominant kernel of that breakdown.
+    # around each step and around the dominant kernel of that breakdown only.
     mk = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
     # event slots: forward (0, 1); reverse pass: adjoints (0, 1), chunk gradients
     # (1, 2), parameter sums (2, 3)
     slots = {"ssm_fwd_kernel": ("f", 0, 1), "ssm_bwd_adjoint": ("b", 0, 1),
              "ssm_bwd_chunk": ("b", 1, 2), "ssm_bwd_params": ("b", 2, 3)}
 
-    def run(steps, which=None):
-        """`steps` steps with events around every kernel (which=None) or around
-        one kernel only; returns (ms of the whole region, per-kernel mean ms)."""
+    def run(steps, which=None, flush_between=True):
+        """`steps` steps with events around each step and around every kernel
+        (which=None) or one kernel only; a scratch write follows each step, outside its
+        events.  Returns (per-step ms list, per-kernel per-step ms lists)."""
         evf = [[mk() for _ in range(2)] for _ in range(steps)]
         evb = [[mk() for _ in range(4)] for _ in range(steps)]
-        for e in [e for row in evf + evb for e in row]:
+        evs = [[mk(), mk()] for _ in range(steps)]
+        for e in [e for row in evf + evb + evs for e in row]:
             e.record(stream)  # materialize the handles
-        start, end = mk(), mk()
         torch.cuda.synchronize()
         args_f, args_b = [], []
         for k in range(steps):
@@ -239,34 +283,33 @@ def main():
                 sel = [e if n in (i, j) else None for n, e in enumerate(row)]
                 args_f.append(sel if side == "f" else None)
                 args_b.append(sel if side == "b" else None)
-        start.record(stream)
         for k in range(steps):
+            if scratch is not None and flush_between:
+                scratch.fill_(float(k))  # evicts L2 and the Infinity Cache
+            evs[k][0].record(stream)
             fwd(args_f[k])
-            if args.mode == "fwdbwd":
+            if mode == "fwdbwd":
                 bwd(args_b[k])
-        end.record(stream)
+            evs[k][1].record(stream)
         torch.cuda.synchronize()
-
-        def avg(rows, i, j):
-            return float(np.mean([r[i].elapsed_time(r[j]) for r in rows]))
-
-        names = [which] if which else (list(slots) if args.mode == "fwdbwd"
-                                       else ["ssm_fwd_kernel"])
-        ms = {}
+        names = [which] if which else (list(slots) if mode == "fwdbwd" else ["ssm_fwd_kernel"])
+        per = {}
         for n in names:
             side, i, j = slots[n]
-            ms[n] = avg(evf if side == "f" else evb, i, j)
-        return start.elapsed_time(end), ms
+            rows = evf if side == "f" else evb
+            per[n] = [r[i].elapsed_time(r[j]) for r in rows]
+        return [a.elapsed_time(b) for a, b in evs], per
 
-    _, kern_ms = run(min(args.steps, 10))          # breakdown pass (untimed)
+    _, kern = run(min(steps, 10))                   # breakdown pass (untimed)
+    kern_ms = {k: float(np.median(v)) for k, v in kern.items()}
     dominant = max(kern_ms, key=kern_ms.get)
+    warm_steps, _ = run(min(steps, 10), dominant, flush_between=False)  # warm caches
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
-    total_ms, timed_ms = run(args.steps, dominant)  # the timed region
+    step_ms, timed = run(steps, dominant)           # the timed region
+    torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    fwd_ms = kern_ms["ssm_fwd_kernel"]
-    bwd_ms = sum(v for k, v in kern_ms.items() if k.startswith("ssm_bwd"))
-    ms_per_step = total_ms / args.steps
+    ms_per_step = float(np.median(step_ms))
     tokens = d["batch"] * d["seqlen"]
     value = tokens / (ms_per_step * 1e-3) / 1e6
 
@@ -274,43 +317,90 @@ def main():
     # the dominant kernel; the compulsory bytes of a direction are carried by its
     # main kernel (the reverse pass's chunk-gradient kernel reads every input and
     # writes every gradient; its boundary-adjoint and parameter kernels are overhead)
-    kern = dominant
-    kms = timed_ms[kern]  # its mean launch duration over the timed region
-    direction = "fwd" if kern == "ssm_fwd_kernel" else "bwd"
-    abytes = algorithmic_bytes(d, io_bytes, direction) if kern in ("ssm_fwd_kernel",
-                                                                   "ssm_bwd_chunk") else 0
+    kms = float(np.mean(timed[dominant]))  # its mean launch duration over the timed region
+    direction = "fwd" if dominant == "ssm_fwd_kernel" else "bwd"
+    abytes = algorithmic_bytes(d, io_bytes, direction) if dominant in ("ssm_fwd_kernel",
+                                                                       "ssm_bwd_chunk") else 0
     achieved = abytes / (kms * 1e-3) / 1e9
-    traffic = measured_traffic(kern, args.workload, args.mode)
+    traffic = measured_traffic(dominant, workload, mode)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "kernel": kern, "algorithmic_bytes_per_launch": abytes,
+                "kernel": dominant, "algorithmic_bytes_per_launch": abytes,
                 "avg_launch_ms": round(kms, 4)}
+    fwd_ms = kern_ms["ssm_fwd_kernel"]
     fwd_bytes = algorithmic_bytes(d, io_bytes, "fwd")
+    fwd_ach = fwd_bytes / (fwd_ms * 1e-3) / 1e9
+    roofline_fwd = {"bound": "hbm", "achieved": round(fwd_ach, 1), "peak": HBM_PEAK_GBS,
+                    "unit": "GB/s", "frac": round(fwd_ach / HBM_PEAK_GBS, 4),
+                    "kernel": "forward scan (every forward launch)" +
+                              (", writing the chunk-boundary states" if mode == "fwdbwd" else ""),
+                    "algorithmic_bytes_per_launch": fwd_bytes, "median_launch_ms": round(fwd_ms, 4)}
+    bwd_ms = sum(v for k, v in kern_ms.items() if k.startswith("ssm_bwd"))
 
-    cpu = None
-    if not args.no_cpu_baseline:
-        cpu = cpu_baseline(prob, args.mode)
+    cpu_line = None
+    if cpu:
+        cpu_line = cpu_baseline(prob, mode)
+        cpu_line["cpu_model"] = cpu_model()
 
-    out = {
+    return {
         "metric": METRIC, "value": round(value, 3), "unit": "Mtokens/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "steps": steps, "warmup": warmup, "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16" if io == "bf16" else "f32", "data": "synthetic",
-        "config": {"workload": args.workload, "batch": d["batch"], "seq_len": d["seqlen"],
+        "config": {"workload": workload, "batch": d["batch"], "seq_len": d["seqlen"],
                    "nheads": d["nheads"], "headdim": d["headdim"], "dstate": d["dstate"],
-                   "rank": d["rank_in"], "decay": d["decay_mode"], "n_pairs": d["n_pairs"],
-                   "two_endpoint": d["two_endpoint"], "chunk": ssm.chunk_tokens(desc),
-                   "step": "forward + reverse" if args.mode == "fwdbwd" else "forward"},
+                   "rank": d["rank_in"], "decay": d["decay_mode"], "n_real": d["n_real"],
+                   "n_pairs": d["n_pairs"], "two_endpoint": d["two_endpoint"],
+                   "chunk": ssm.chunk_tokens(desc),
+                   "step": "forward + reverse" if mode == "fwdbwd" else "forward"},
+        "timing": {"statistic": "median over the timed steps", "flush_bytes_between_steps":
+                   FLUSH_BYTES if flush else 0,
+                   "step_ms_p10": round(pct(step_ms, 10), 4),
+                   "step_ms_p50": round(ms_per_step, 4),
+                   "step_ms_p90": round(pct(step_ms, 90), 4),
+                   "step_ms_mean": round(float(np.mean(step_ms)), 4),
+                   "warm_cache_step_ms_median": round(float(np.median(warm_steps)), 4),
+                   "wall_s": round(wall, 3)},
         "roofline": roofline,
-        "cpu_baseline": cpu,
-        # per-kernel means from the untimed pass with events around every kernel
+        "roofline_fwd": roofline_fwd,
+        "cpu_baseline": cpu_line,
+        # M3: saved-for-backward bytes against the peak device allocation of the step
+        "memory": {"saved_for_backward_bytes": saved_bytes,
+                   "workspace_bytes": {"fwd": ws_f, "bwd": ws_b},
+                   "input_bytes": input_bytes,
+                   "peak_allocated_bytes": int(peak_bytes)},
+        # per-kernel medians from the untimed pass with events around every kernel
         "breakdown": {"kernel_ms": {k: round(v, 4) for k, v in kern_ms.items()},
                       "fwd_ms": round(fwd_ms, 4), "bwd_ms": round(bwd_ms, 4),
-                      "fwd_mtok_s": round(tokens / (fwd_ms * 1e-3) / 1e6, 3),
-                      "fwd_hbm_frac": round(fwd_bytes / (fwd_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                      "wall_s": round(wall, 3)},
+                      "fwd_mtok_s": round(tokens / (fwd_ms * 1e-3) / 1e6, 3)},
     }
-    print(json.dumps(out), flush=True)
+
+
+SUITE = [("ssd_siso", "fwd"), ("ssd_mimo", "fwd"), ("hybrid", "fwd"), ("hybrid_r1", "fwd"),
+         ("hybrid_bwd", "fwdbwd"), ("ssd_mimo_bwd", "fwdbwd")]
+
+
+def run_suite(args):
+    """Every workload once, then geometric means over them (the pages aggregate their
+    per-workload kernel timings by geometric mean)."""
+    lines = []
+    for w, m in SUITE:
+        o = measure(w, m, args.steps, args.warmup, flush=not args.no_flush, cpu=False)
+        lines.append({"workload": w, "step": o["config"]["step"], "mtok_s": o["value"],
+                      "ms_per_step": o["ms_per_step"], "fwd_hbm_frac": o["roofline_fwd"]["frac"],
+                      "dominant_kernel": o["roofline"]["kernel"],
+                      "dominant_hbm_frac": o["roofline"]["frac"]})
+        print(json.dumps(lines[-1]), file=sys.stderr, flush=True)
+        import torch
+        torch.cuda.empty_cache()
+
+    def gmean(k):
+        return round(float(np.exp(np.mean([np.log(x[k]) for x in lines]))), 4)
+
+    print(json.dumps({"metric": "geometric mean over the workloads", "workloads": lines,
+                      "geomean_mtok_s": gmean("mtok_s"),
+                      "geomean_fwd_hbm_frac": gmean("fwd_hbm_frac"),
+                      "geomean_dominant_hbm_frac": gmean("dominant_hbm_frac")}), flush=True)
 
 
 def run_decode(args):
