@@ -84,7 +84,7 @@
 extern "C" {
 #endif
 
-#define SSM_ABI_VERSION 3
+#define SSM_ABI_VERSION 4
 
 typedef enum {
   SSM_OK = 0,
@@ -94,7 +94,9 @@ typedef enum {
   SSM_ERR_ALIGN = -4,       /* pointer not 16-byte aligned */
   SSM_ERR_UNSUPPORTED = -5, /* valid but not implemented for this shape / mode */
   SSM_ERR_WORKSPACE = -6,   /* workspace smaller than ssm_workspace_bytes() */
-  SSM_ERR_HIP = -7          /* a HIP launch failed */
+  SSM_ERR_HIP = -7,         /* a HIP launch failed */
+  SSM_ERR_SCRATCH = -8      /* ssm_scan_fwd_noalloc: the workspace the problem needs exceeds
+                               the static scratch array (ssm_scratch_bytes()) */
 } ssm_status;
 
 typedef enum { SSM_F32 = 0, SSM_BF16 = 1 } ssm_dtype;
@@ -184,6 +186,24 @@ int ssm_scan_fwd(const ssm_desc *desc, const ssm_fwd_args *args, void *ws, size_
    from per-head partials in the workspace, so every call gives the same bits. */
 int ssm_scan_bwd(const ssm_desc *desc, const ssm_bwd_args *args, void *ws, size_t ws_bytes,
                  void *stream);
+
+/* ---------------------------------------------------------------- no allocation
+ * For callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): ssm_scan_fwd with its workspace in
+ * a static array inside the library instead of a caller buffer.  Same descriptor,
+ * arguments, outputs and errors as ssm_scan_fwd; nothing is allocated or freed.
+ *   - The array holds ssm_scratch_bytes() bytes (32 MiB) on every device the library
+ *     runs on, from the device's first call until the process ends.  A problem whose
+ *     forward workspace (ssm_workspace_bytes(desc, 0)) exceeds it is rejected with
+ *     SSM_ERR_SCRATCH before anything is enqueued.
+ *   - All calls on one device share that device's array, and it keeps the last call's
+ *     contents (no call relies on them: every region a call reads is written by the
+ *     same call first).  Calls that overlap in time on one device -- concurrent
+ *     streams, or host threads -- race on it: order them on one stream.
+ *   - The first call on a device looks up the array's device address (not a kernel
+ *     launch); SSM_ERR_HIP if that fails. */
+size_t ssm_scratch_bytes(void);
+int ssm_scan_fwd_noalloc(const ssm_desc *desc, const ssm_fwd_args *args, void *stream);
 
 /* ---------------------------------------------------------------- recurrent step
  * One token of the same recurrence, run step by step with a constant-size state

@@ -23,6 +23,8 @@ from ._lib import (  # noqa: F401
     saved_bytes,
     scan_bwd,
     scan_fwd,
+    scan_fwd_noalloc,
+    scratch_bytes,
     workspace_bytes,
 )
 from .scan import backward, decode_step, forward  # noqa: F401

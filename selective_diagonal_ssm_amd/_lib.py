@@ -15,14 +15,14 @@ LIB_PATH = os.path.join(PKG, "libssmscan.so")
 SSM_OK = 0
 STATUS = {0: "SSM_OK", -1: "SSM_ERR_NULL", -2: "SSM_ERR_SHAPE", -3: "SSM_ERR_DTYPE",
           -4: "SSM_ERR_ALIGN", -5: "SSM_ERR_UNSUPPORTED", -6: "SSM_ERR_WORKSPACE",
-          -7: "SSM_ERR_HIP"}
+          -7: "SSM_ERR_HIP", -8: "SSM_ERR_SCRATCH"}
 SSM_F32, SSM_BF16 = 0, 1
 SSM_DECAY_HEAD, SSM_DECAY_COORD = 0, 1
 SSM_F_DT_SOFTPLUS, SSM_F_TWO_ENDPOINT, SSM_F_HAS_D = 1, 2, 4
 
 EXPORTS = ("ssm_abi_version", "ssm_status_string", "ssm_check_desc", "ssm_chunk_tokens",
            "ssm_saved_bytes", "ssm_workspace_bytes", "ssm_scan_fwd", "ssm_scan_bwd",
-           "ssm_decode_step")
+           "ssm_decode_step", "ssm_scratch_bytes", "ssm_scan_fwd_noalloc")
 
 
 class SsmDesc(ctypes.Structure):
@@ -84,6 +84,9 @@ def load():
         lib.ssm_scan_fwd.argtypes = [dp, ctypes.POINTER(SsmFwdArgs), _vp, ctypes.c_size_t, _vp]
         lib.ssm_scan_bwd.argtypes = [dp, ctypes.POINTER(SsmBwdArgs), _vp, ctypes.c_size_t, _vp]
         lib.ssm_decode_step.argtypes = [dp, ctypes.POINTER(SsmDecodeArgs), _vp]
+        lib.ssm_scratch_bytes.argtypes = []
+        lib.ssm_scratch_bytes.restype = ctypes.c_size_t
+        lib.ssm_scan_fwd_noalloc.argtypes = [dp, ctypes.POINTER(SsmFwdArgs), _vp]
         _lib = lib
     return _lib
 
@@ -228,6 +231,36 @@ def scan_fwd(desc: SsmDesc, x, B, C, dt, A, y, omega=None, beta=None, gamma=None
                              _stream(stream))
     if rc != SSM_OK:
         raise SsmError(rc, "ssm_scan_fwd")
+
+
+def scratch_bytes() -> int:
+    """Bytes of the static scratch array that scan_fwd_noalloc uses as its workspace."""
+    return load().ssm_scratch_bytes()
+
+
+def scan_fwd_noalloc(desc: SsmDesc, x, B, C, dt, A, y, omega=None, beta=None, gamma=None,
+                     D=None, saved=None, stream=None, h0=None, h_final=None) -> None:
+    """scan_fwd with the library's static scratch array as workspace: the call allocates
+    nothing.  Raises SsmError (SSM_ERR_SCRATCH) when the problem's forward workspace
+    exceeds scratch_bytes().  Calls that overlap on one GPU share the array and race."""
+    import torch
+    seen = []
+    _check_scan(seen, desc, x, B, C, dt, A, omega, beta, gamma, D)
+    b, L, H = desc.batch, desc.seqlen, desc.nheads
+    _check(seen, "y", y, b * L * H * desc.rank_out * desc.headdim, _io_torch_dtype(desc))
+    if saved is not None:
+        _check(seen, "saved", saved, 0, None, at_least=True)
+        if saved.numel() * saved.element_size() < saved_bytes(desc):
+            raise SsmError(-2, f"saved holds {saved.numel() * saved.element_size()} bytes, "
+                               f"the descriptor needs {saved_bytes(desc)}")
+    _check(seen, "h0", h0, _state_numel(desc), torch.float32, required=False)
+    _check(seen, "h_final", h_final, _state_numel(desc), torch.float32, required=False)
+    _check_devices(seen)
+    args = SsmFwdArgs(_ptr(x), _ptr(B), _ptr(C), _ptr(dt), _ptr(A), _ptr(omega), _ptr(beta),
+                      _ptr(gamma), _ptr(D), _ptr(y), _ptr(saved), _ptr(h0), _ptr(h_final), None)
+    rc = load().ssm_scan_fwd_noalloc(ctypes.byref(desc), ctypes.byref(args), _stream(stream))
+    if rc != SSM_OK:
+        raise SsmError(rc, "ssm_scan_fwd_noalloc")
 
 
 def scan_bwd(desc: SsmDesc, x, B, C, dy, dt, A, saved, dx, dB, dC, ddt, omega=None, beta=None,

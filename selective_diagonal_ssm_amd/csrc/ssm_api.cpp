@@ -3,8 +3,10 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 
 #include "ssm_kernels.hpp"
 #include "ssm_scan.h"
@@ -184,6 +186,7 @@ const char* ssm_status_string(int s) {
     case SSM_ERR_UNSUPPORTED: return "shape or mode not implemented by this library";
     case SSM_ERR_WORKSPACE: return "workspace too small";
     case SSM_ERR_HIP: return "HIP launch failed";
+    case SSM_ERR_SCRATCH: return "problem needs more workspace than the static scratch array holds";
     default: return "unknown status";
   }
 }
@@ -275,8 +278,44 @@ size_t ssm_workspace_bytes(const ssm_desc* d, int for_backward) {
   return g + (part + 255) / 256 * 256 + adj_segment_bytes(d, pl) + group_partial_bytes(d, pl);
 }
 
-int ssm_scan_fwd(const ssm_desc* d, const ssm_fwd_args* a, void* ws, size_t ws_bytes,
-                 void* stream) {
+}  // extern "C"
+
+namespace {
+
+// ------------------------------------------------------------------ static scratch
+// Workspace of ssm_scan_fwd_noalloc: one array per device in the library's code object,
+// held until the process ends.  Host code never passes `scratch` itself to a kernel (in
+// host code the name is a stand-in, not a device address): each device's address comes
+// from hipGetSymbolAddress, taken once per device with that device current.
+constexpr size_t kScratchBytes = size_t(32) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// The current device's scratch address (SSM_OK), or SSM_ERR_HIP.
+int scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return SSM_ERR_HIP;
+  void* ptr = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!ptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    ptr = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (!ptr) {
+      if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return SSM_ERR_HIP;
+      g_scratch_ptr[dev].store(ptr, std::memory_order_release);
+    }
+  }
+  *out = ptr;
+  return SSM_OK;
+}
+
+// The forward scan.  With `use_scratch` the workspace is the device's static scratch
+// array (ws / ws_bytes unused): a problem whose workspace exceeds it is rejected before
+// any HIP call.
+int scan_fwd_impl(const ssm_desc* d, const ssm_fwd_args* a, void* ws, size_t ws_bytes,
+                  void* stream, bool use_scratch) {
   Plan pl;
   int rc = make_plan(d, &pl);
   if (rc) return rc;
@@ -336,6 +375,12 @@ int ssm_scan_fwd(const ssm_desc* d, const ssm_fwd_args* a, void* ws, size_t ws_b
   }
   if (sg.nseg > 1) {
     const size_t need = fwd_segment_bytes(d, pl, key);
+    if (use_scratch) {
+      if (need > kScratchBytes) return SSM_ERR_SCRATCH;
+      const int src = scratch_address(&ws);
+      if (src != SSM_OK) return src;
+      ws_bytes = kScratchBytes;
+    }
     if (!ws || ws_bytes < need) return SSM_ERR_WORKSPACE;
     if (!aligned(ws, 16)) return SSM_ERR_ALIGN;
     const LocalRanges lr = local_ranges(pl, sg);
@@ -349,6 +394,21 @@ int ssm_scan_fwd(const ssm_desc* d, const ssm_fwd_args* a, void* ws, size_t ws_b
   }
   const hipError_t e = ssm::launch_fwd(key, p, static_cast<hipStream_t>(stream), a->events);
   return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ssm_scan_fwd(const ssm_desc* d, const ssm_fwd_args* a, void* ws, size_t ws_bytes,
+                 void* stream) {
+  return scan_fwd_impl(d, a, ws, ws_bytes, stream, false);
+}
+
+size_t ssm_scratch_bytes(void) { return kScratchBytes; }
+
+int ssm_scan_fwd_noalloc(const ssm_desc* d, const ssm_fwd_args* a, void* stream) {
+  return scan_fwd_impl(d, a, nullptr, 0, stream, true);
 }
 
 int ssm_scan_bwd(const ssm_desc* d, const ssm_bwd_args* a, void* ws, size_t ws_bytes,
