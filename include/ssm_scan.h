@@ -73,6 +73,9 @@
  *     (may be NULL when that is 0).  Calls that share a workspace on one
  *     stream are ordered; concurrent calls need separate workspaces.
  *   - The library is thread-safe and keeps no per-call state.
+ *   - Any step is valid: chunks whose per-row decay is too steep for the chunked
+ *     kernels' folded operands are recomputed token by token on the GPU (the
+ *     per-row scans therefore always need a small workspace for their flags).
  */
 #ifndef SSM_SCAN_H
 #define SSM_SCAN_H

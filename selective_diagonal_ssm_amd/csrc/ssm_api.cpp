@@ -226,6 +226,12 @@ static size_t group_partial_bytes(const ssm_desc* d, const Plan& pl) {
   return d->ngroups == d->nheads ? 0 : 2 * group_partial_one(d, pl);
 }
 
+// per-row kernel: one flag per (slice, chunk) item marking chunks too steep for the fold
+static size_t bwd_flags_bytes(const ssm_desc* d, const Plan& pl) {
+  if (!pl.coord_kernel) return 0;
+  return ((size_t)(d->batch * d->nheads * pl.nchunks + 1) * sizeof(int) + 255) / 256 * 256;
+}
+
 // local-pass ranges of a segment: as few as keep each within kLocalMaxTokens tokens
 struct LocalRanges {
   int seg_tokens, nsub, lsub;
@@ -247,6 +253,21 @@ static size_t fwd_segment_bytes(const ssm_desc* d, const Plan& pl, const FwdKey&
   const size_t loc = (size_t)slices * (sg.nseg - 1) * lr.nsub * np * sizeof(float);
   const size_t in = (size_t)slices * sg.nseg * np * sizeof(float);
   return loc + in + ((size_t)slices * (sg.nseg - 1) * lr.nsub * sizeof(float) + 255) / 256 * 256;
+}
+
+static size_t align256(size_t v) { return (v + 255) / 256 * 256; }
+
+// workspace of the forward: the segment buffers, then (per-row kernel) one flag per
+// workgroup marking ranges that hold a chunk too steep for the midpoint fold
+static size_t fwd_flags_bytes(const ssm_desc* d, const Plan& pl, const FwdKey& key) {
+  if (!pl.coord_kernel) return 0;
+  const long slices = (long)d->batch * d->nheads;
+  const int npblk = d->headdim / key.PB;
+  const Segs sg = segments(slices * npblk, pl.nchunks);
+  return align256((size_t)slices * npblk * sg.nseg * sizeof(int));
+}
+static size_t fwd_workspace(const ssm_desc* d, const Plan& pl, const FwdKey& key) {
+  return align256(fwd_segment_bytes(d, pl, key)) + fwd_flags_bytes(d, pl, key);
 }
 
 // boundary-adjoint sweep segments: one workgroup per (slice, segment)
@@ -271,11 +292,12 @@ size_t ssm_workspace_bytes(const ssm_desc* d, int for_backward) {
   if (make_plan(d, &pl)) return 0;
   if (!for_backward) {
     const FwdKey key = choose_fwd(d, pl);
-    return key.PB > 0 ? fwd_segment_bytes(d, pl, key) : 0;
+    return key.PB > 0 ? fwd_workspace(d, pl, key) : 0;
   }
   const size_t g = (bwd_gseg_bytes(d, pl) + 255) / 256 * 256;
   const size_t part = (size_t)d->batch * d->nheads * pl.nchunks * npart_of(d, pl) * sizeof(float);
-  return g + (part + 255) / 256 * 256 + adj_segment_bytes(d, pl) + group_partial_bytes(d, pl);
+  return g + (part + 255) / 256 * 256 + adj_segment_bytes(d, pl) + group_partial_bytes(d, pl) +
+         bwd_flags_bytes(d, pl);
 }
 
 }  // extern "C"
@@ -373,8 +395,8 @@ int scan_fwd_impl(const ssm_desc* d, const ssm_fwd_args* a, void* ws, size_t ws_
       p.cps = sg.nseg == 1 ? p.nchunks : sg.cps / 2;
     }
   }
-  if (sg.nseg > 1) {
-    const size_t need = fwd_segment_bytes(d, pl, key);
+  const size_t need = fwd_workspace(d, pl, key);
+  if (need > 0) {
     if (use_scratch) {
       if (need > kScratchBytes) return SSM_ERR_SCRATCH;
       const int src = scratch_address(&ws);
@@ -383,6 +405,10 @@ int scan_fwd_impl(const ssm_desc* d, const ssm_fwd_args* a, void* ws, size_t ws_
     }
     if (!ws || ws_bytes < need) return SSM_ERR_WORKSPACE;
     if (!aligned(ws, 16)) return SSM_ERR_ALIGN;
+    if (pl.coord_kernel)
+      p.wild = reinterpret_cast<int*>(static_cast<char*>(ws) + align256(fwd_segment_bytes(d, pl, key)));
+  }
+  if (sg.nseg > 1) {
     const LocalRanges lr = local_ranges(pl, sg);
     p.seg_tokens = lr.seg_tokens;
     p.nsub = lr.nsub;
@@ -479,9 +505,13 @@ int ssm_scan_bwd(const ssm_desc* d, const ssm_bwd_args* a, void* ws, size_t ws_b
     p.gin = p.gloc + slices * (sg.nseg - 1) * lr.nsub * np;
     p.gdel = p.gin + slices * sg.nseg * np;
   }
+  if (pl.coord_kernel) {  // item flags and the "any flagged" word at the end of the workspace
+    p.wild = reinterpret_cast<int*>(static_cast<char*>(ws) + (need - bwd_flags_bytes(d, pl)));
+    p.wild_any = p.wild + (size_t)d->batch * d->nheads * pl.nchunks;
+  }
   if (d->ngroups != d->nheads) {
-    // per-head dB / dC partials at the end of the workspace
-    char* base = static_cast<char*>(ws) + (need - group_partial_bytes(d, pl));
+    // per-head dB / dC partials before the flags
+    char* base = static_cast<char*>(ws) + (need - bwd_flags_bytes(d, pl) - group_partial_bytes(d, pl));
     p.dBh = base;
     p.dCh = base + group_partial_one(d, pl);
   }

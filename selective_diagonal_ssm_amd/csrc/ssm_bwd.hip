@@ -36,6 +36,7 @@
 #include <type_traits>
 
 #include "ssm_device.hpp"
+#include "ssm_exact.hpp"
 #include "ssm_kernels.hpp"
 #include "ssm_local.hpp"
 
@@ -73,6 +74,9 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_adjoint(BwdParams p) {
   __shared__ float sRate[N], sOmega[N / 2 + 1];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  // the chunk-gradient kernel that follows sets this word when a chunk is too steep for
+  // its fold
+  if (p.wild_any && blockIdx.x == 0 && tid == 0) *p.wild_any = 0;
   const int npblk = p.P / PB;
   const int lid = xcd_logical_id(blockIdx.x, gridDim.x);
   const int slice = lid / (npblk * p.nseg), seg = (lid / npblk) % p.nseg, pblk = lid % npblk;
@@ -757,6 +761,18 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
     }
     const float cd_l = wave_prefix_sum(dl);
     const float cdend = read_lane(cd_l, QT - 1);
+    if constexpr (COORD) {
+      // a chunk too steep for the midpoint fold is redone by the token-by-token reverse
+      // pass: the largest |rate| of the item's rows (lanes of wave 0 hold the rates)
+      if (wave == 0 && p.wild) {
+        const float amax = wave_max(lane < N ? fabsf(pf_rate) : 0.f);
+        const bool steep = amax * cdend > kFoldLimit;
+        if (lane == 0) {
+          p.wild[item] = steep ? 1 : 0;
+          if (steep) atomicOr(p.wild_any, 1);
+        }
+      }
+    }
     const float w_l = COORD ? 0.f : __expf(-Ah * (cdend - cd_l));   // e^{L_end - L_t}
     const float el_l = COORD ? 0.f : __expf(-Ah * cd_l);            // e^{L_t}
     if (wave == 0 && lane < QT) {
@@ -1088,11 +1104,16 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int s = (j0 + i) / KR;
-        float m = 0.f;
-        if (s <= t) m = COORD ? 1.f : __builtin_amdgcn_exp2f(lt - sTlc[s]);
-        smv[i] = sc[i] * m;
-        zmv[i] = z[i] * m;
-        wv[i] = z[i] * smv[i];
+        // masked by selection: with per-row decay the folded product of a masked entry
+        // (s > t) can overflow, and inf * 0 would be NaN
+        const bool causal = s <= t;
+        const float m = COORD ? 1.f : __builtin_amdgcn_exp2f(lt - sTlc[causal ? s : t]);
+        smv[i] = causal ? sc[i] * m : 0.f;
+        zmv[i] = causal ? z[i] * m : 0.f;
+        // same-token entries (mask 1 whatever the decay) add equally to the row and the
+        // column sum of a token, whose difference the step gradient takes: left out of
+        // both, so steep decay (tiny differences) does not meet fp32 rounding of them
+        wv[i] = s < t ? z[i] * smv[i] : 0.f;
       }
       store4<BF16>(sSM + row * KS + j0, smv);
       store4<BF16>(sZM + row * KS + j0, zmv);
@@ -1578,23 +1599,36 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
         eterm = wave_sum(eterm);
         if (lane == QT - 1) tok += eterm;
       } else {
+        // d(loss)/d(L_t) = rs_t - cs_t + tt_t - src_t, plus the final-state term e and
+        // the sum of the source terms on the last position.  Summed over t >= r (the step
+        // gradient of token r) the source terms of t >= r cancel; taking the sum as
+        // suffix(rs - cs + tt) + prefix_{s < r}(src) + e keeps that cancellation (and the
+        // same-token scores left out of rs and cs) out of fp32
         float src = 0.f;
         if (lane < QT) {
           const float rs = wsum<WH>(sRS, lane);
           const float cs = wsum<WH>(sCS, lane);
           const float tt = wsum<WH>(sTT, lane);
           src = wsum<WH>(sSrc, lane);
-          dunw = rs - cs + tt - src;
+          dunw = rs - cs + tt;
         }
-        srcsum = wave_sum(src);
         for (int n = lane; n < N; n += kWave) e += sE[n];
         e = wave_sum(e);
-        if (lane == QT - 1) dunw += e + srcsum;
-        tok = -Ah * dunw;
+        srcsum = wave_prefix_sum(src) - src;  // sources of the tokens before this one
       }
-      const float tot = wave_sum(tok);
-      const float pre = wave_prefix_sum(tok);
-      const float rev = tot - pre + tok;
+      // sum over t >= r, lane r, as a prefix sum of the lanes in reverse token order
+      auto suffix_sum = [&](float v) {
+        const float r = __shfl(lane < QT ? v : 0.f, lane < QT ? QT - 1 - lane : lane, kWave);
+        const float pr = wave_prefix_sum(r);
+        return __shfl(pr, lane < QT ? QT - 1 - lane : lane, kWave);
+      };
+      float rev;
+      if (COORD) {
+        rev = suffix_sum(tok);
+      } else {
+        dunw = suffix_sum(dunw) + srcsum + e;  // d(loss)/d(cumulative log-decay at r) summed over t >= r
+        rev = -Ah * dunw;
+      }
       const int t = t0 + lane;
       if (lane < QT && t < L) {
         o_ddt = p.softplus ? rev * sigmoid_f32(raw_l) : rev;
@@ -1604,8 +1638,8 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
         }
       }
       if (!COORD && p.part) {
-        // dA_h partial = sum_t (-cd_t) D_t
-        const float v = wave_sum(lane < QT ? -cd_l * dunw : 0.f);
+        // dA_h partial = sum_t (-cd_t) D_t = -sum_r Delta_r sum_{t >= r} D_t
+        const float v = wave_sum(lane < QT ? -dl * dunw : 0.f);
         if (lane == 0) sPartOut[0] = v;
       }
     }
@@ -1818,6 +1852,7 @@ hipError_t launch_bwd(const BwdKey& k, const BwdParams& p, hipStream_t stream,
       hipLaunchKernelGGL((ssm_bwd_chunk<BF, NN, PP, RR, KRR, QTT, CO, CHUNK_NT(NN, CO), SP>),     \
                          dim3(grid), dim3(CHUNK_NT(NN, CO)), 0, stream, p);                   \
     }                                                                                         \
+    if constexpr (CO) launch_bwd_exact<BF, NN, PP, RR, QTT>(p, device_cus(), stream);         \
     if (p.dBh) {                                                                              \
       const long total = (long)p.batch * p.L * p.G * RR * (NN / 4);                          \
       const int gb = (int)std::min<long>((total + 255) / 256, 4096);                         \

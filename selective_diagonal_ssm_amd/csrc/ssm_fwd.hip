@@ -33,6 +33,7 @@
 #include <algorithm>
 
 #include "ssm_device.hpp"
+#include "ssm_exact.hpp"
 #include "ssm_kernels.hpp"
 #include "ssm_local.hpp"
 
@@ -254,10 +255,16 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
 
   // ---- a1: per-token factors of chunk c into slot c & 3 (wave PW only; lane = token,
   // dl = its step, 0 past the sequence end)
+  // per-row decay: the largest |rate| of the head's rows (factor wave, from the rates its
+  // lanes read) and whether a chunk of this range is too steep for the midpoint fold
+  // (summed step times that rate above kFoldLimit)
+  float amax = 0.f;
+  bool steep = false;
   auto factors = [&](int c, float dl) {
     const int bi = c & 3;
     const float cd = wave_prefix_sum(dl);
     const float cdend = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cd), QT - 1));
+    if (COORD) steep = steep || amax * cdend > kFoldLimit;
     if (lane < QT) {
       if (COORD) sCD[bi][lane] = cd;
       if (!COORD) {
@@ -556,6 +563,7 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
       }
     }
   }
+  if (COORD && wave == PW) amax = wave_max(tid < N ? fabsf(r_rate) : 0.f);
   if (wave == PW) {
     factors(c0, (lane < QT && c0 * QT + lane < L) ? (p.softplus ? softplus_f32(dt0) : dt0) : 0.f);
     if (c0 + 1 < c1) factors(c0 + 1, (lane < QT && (c0 + 1) * QT + lane < L) ? (p.softplus ? softplus_f32(dt1) : dt1) : 0.f);
@@ -841,6 +849,10 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
     }
     __syncthreads();
   }
+  // per-row decay: flag the range when one of its chunks was too steep for the fold (its
+  // outputs are then rewritten by the token-by-token forward)
+  if constexpr (COORD)
+    if (tid == 0 && p.wild) p.wild[lid] = steep ? 1 : 0;
   store_rows(c1 - 1);
   // the final state after the last segment
   float* hf = (seg == p.nseg - 1 && p.h_final) ? p.h_final + (size_t)slice * N * P + p0 : nullptr;
@@ -1030,6 +1042,7 @@ hipError_t launch_fwd(const FwdKey& k, const FwdParams& p, hipStream_t stream,
     }                                                                                        \
     hipLaunchKernelGGL((ssm_fwd_kernel<BF, NN, PBB, RR, KRR, QTT, CO, NT>), dim3(nwg),        \
                        dim3(NT), 0, stream, p);                                              \
+    if constexpr (CO) launch_fwd_exact<BF, NN, RR>(p, QTT, stream);                           \
     mark(1);                                                                                 \
     return hipGetLastError();                                                                \
   }

@@ -34,7 +34,17 @@ struct FwdParams {
   float* seg_local;  // [slice][nseg - 1][nsub][N][P] range final states (local pass output)
   float* seg_in;     // [slice][nseg][N][P] states entering the segments (combine output)
   float* seg_delta;  // [slice][nseg - 1][nsub] sum of Delta over each range (local pass output)
+  // per-row kernel: one flag per workgroup (logical id), set when its range holds a chunk
+  // too steep for the fold (workspace); null for the head-decay kernel
+  int* wild;
 };
+
+// Largest chunk exponent the per-row kernels fold: a chunk whose summed step times the
+// largest |rate| of the head's rows exceeds it is flagged and redone by the token-by-token
+// kernels (ssm_exact.hpp).  The folded factors then stay below e^{kFoldLimit / 2} = e^60.
+constexpr float kFoldLimit = 120.f;
+// tokens the token-by-token forward stages per block
+constexpr int kExactTokens = 16;
 
 // tokens of one local-pass range (bounds the kernel's per-token LDS tables)
 constexpr int kLocalMaxTokens = 512;
@@ -102,6 +112,11 @@ struct BwdParams {
   float* gloc;     // [slice][nseg - 1][nsub][N][P] range adjoints at the ranges' first tokens
   float* gin;      // [slice][nseg][N][P] adjoints flowing into the segments from the right
   float* gdel;     // [slice][nseg - 1][nsub] summed step of each range's transition
+  // per-row kernel: one flag per (slice, chunk) item, set when the chunk is too steep for
+  // the fold, and one word set when any item is (workspace; zeroed by the boundary-adjoint
+  // sweep, which runs first); null for the head-decay kernel
+  int* wild;
+  int* wild_any;
 };
 
 // Single-token recurrent step (one token per slice, state updated in place).

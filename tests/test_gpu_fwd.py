@@ -102,6 +102,39 @@ SMALL_CASES = {
                                                dt_softplus=False, dt_mean=0.1, dt_std=0.02)),
     "bf16_hybrid_no_softplus": ("hybrid", dict(batch=2, seqlen=150, nheads=2, ngroups=2,
                                                dt_softplus=False, dt_mean=0.1, dt_std=0.02)),
+    # steep per-row decay: steps ~ softplus(N(2, 0.5)) with rates 16 (a row decays by
+    # ~e^-34 per token), so every chunk is redone token by token; and spike mixes, where
+    # some ranges and chunks stay on the chunked path and others are redone
+    "f32_hybrid_steep": ("hybrid", dict(dtype="f32", dstate=32, n_real=16, n_pairs=8,
+                                        headdim=16, batch=2, nheads=2, ngroups=2, seqlen=77,
+                                        dt_mean=2.0, A_lo=16.0, A_hi=16.0)),
+    "f32_coord_plain_steep": ("hybrid", dict(dtype="f32", two_endpoint=False, dstate=32,
+                                             n_real=16, n_pairs=8, headdim=16, batch=2,
+                                             nheads=2, ngroups=2, seqlen=61, dt_mean=2.0,
+                                             A_lo=16.0, A_hi=16.0)),
+    "f32_hybrid_r1_steep": ("hybrid", dict(dtype="f32", dstate=32, n_real=16, n_pairs=8,
+                                           headdim=16, rank_in=1, rank_out=1, batch=2,
+                                           nheads=2, ngroups=2, seqlen=70, dt_mean=2.0,
+                                           A_lo=16.0, A_hi=16.0)),
+    "bf16_hybrid_steep": ("hybrid", dict(batch=2, seqlen=150, nheads=2, ngroups=2, dt_mean=2.0,
+                                         A_lo=16.0, A_hi=16.0)),
+    "bf16_hybrid_r1_steep": ("hybrid_r1", dict(batch=2, seqlen=150, nheads=2, ngroups=2,
+                                               dt_mean=2.0, A_lo=16.0, A_hi=16.0)),
+    "bf16_hybrid_spikes": ("hybrid", dict(batch=2, seqlen=300, nheads=4, ngroups=4,
+                                          dt_spike_prob=[0.0, 0.05, 0.3, 0.7], dt_spike_mean=3.0,
+                                          pair_rate_per_pair=True)),
+    "f32_hybrid_spikes": ("hybrid", dict(dtype="f32", dstate=32, n_real=16, n_pairs=8,
+                                         headdim=16, batch=2, nheads=4, ngroups=2, seqlen=150,
+                                         dt_spike_prob=[0.0, 0.05, 0.3, 0.7],
+                                         dt_spike_mean=3.0)),
+    "bf16_te_head_steep": ("ssd_siso", dict(batch=2, seqlen=150, nheads=2, ngroups=2, dstate=64,
+                                            n_real=64, two_endpoint=True, dt_mean=2.0,
+                                            A_lo=16.0, A_hi=16.0, chunk=0)),
+    # head decay needs no fallback (its masks and factors are exponents <= 0): a check
+    "bf16_ssd_siso_steep": ("ssd_siso", dict(batch=2, seqlen=300, nheads=2, ngroups=2,
+                                             dt_mean=2.0, A_lo=16.0, A_hi=16.0)),
+    "bf16_mimo_steep": ("ssd_mimo", dict(batch=2, seqlen=200, nheads=2, ngroups=2, dt_mean=2.0,
+                                         A_lo=16.0, A_hi=16.0)),
 }
 
 
