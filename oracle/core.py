@@ -80,10 +80,11 @@ def load():
         fp = ctypes.POINTER(ctypes.c_float)
         dp = ctypes.POINTER(ctypes.c_double)
         ip = ctypes.POINTER(ctypes.c_int)
-        lib.oracle_fwd.argtypes = [ctypes.POINTER(_Desc)] + [fp] * 9 + [dp, dp, dp, ip, ctypes.c_int]
+        lib.oracle_fwd.argtypes = ([ctypes.POINTER(_Desc)] + [fp] * 9 + [dp, fp, fp, dp, dp, ip,
+                                                                           ctypes.c_int])
         lib.oracle_fwd.restype = ctypes.c_int
-        lib.oracle_bwd.argtypes = ([ctypes.POINTER(_Desc)] + [fp] * 9 + [dp, fp] + [dp] * 10
-                                   + [ip, ctypes.c_int])
+        lib.oracle_bwd.argtypes = ([ctypes.POINTER(_Desc)] + [fp] * 9 + [dp, fp, fp, fp, dp]
+                                   + [dp] * 12 + [ip, ctypes.c_int])
         lib.oracle_bwd.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -120,9 +121,10 @@ def _inputs(prob):
     return [_f32(prob.get(k)) for k in keys]
 
 
-def fwd(prob: dict, slices=None, h0=None):
+def fwd(prob: dict, slices=None, h0=None, x_prev=None, B_prev=None):
     """Run the oracle forward.  Returns (y, h_final) as float64 arrays; entries
-    of slices that were not requested are NaN."""
+    of slices that were not requested are NaN.  `x_prev` [b][h][R][P] and `B_prev`
+    [b][g][R][N]: the token before the sequence (two-endpoint carry)."""
     desc = OracleDesc.from_dict(prob["desc"])
     lib = load()
     x, B, C, dt, A, om, be, ga, D = _inputs(prob)
@@ -132,19 +134,23 @@ def fwd(prob: dict, slices=None, h0=None):
     h0 = None if h0 is None else np.ascontiguousarray(h0, dtype=np.float64)
     sl = _slices(desc, slices)
     dc = desc.c()
+    xp, bp = _f32(x_prev), _f32(B_prev)
     rc = lib.oracle_fwd(ctypes.byref(dc), _fptr(x), _fptr(B), _fptr(C), _fptr(dt), _fptr(A),
-                        _fptr(om), _fptr(be), _fptr(ga), _fptr(D), _dptr(h0), _dptr(y), _dptr(hf),
+                        _fptr(om), _fptr(be), _fptr(ga), _fptr(D), _dptr(h0), _fptr(xp),
+                        _fptr(bp), _dptr(y), _dptr(hf),
                         sl.ctypes.data_as(ctypes.POINTER(ctypes.c_int)), len(sl))
     if rc:
         raise ValueError(f"oracle_fwd rejected the descriptor (rc={rc})")
     return y, hf
 
 
-def bwd(prob: dict, dy, slices=None, h0=None):
+def bwd(prob: dict, dy, slices=None, h0=None, x_prev=None, B_prev=None, dh_final=None):
     """Run the oracle reverse mode.  Returns a dict with dx, dB, dC, ddt, dA,
-    domega, dbeta, dgamma, dD, dh0 (float64).  Per-token gradients of slices
-    that were not requested are NaN (dB/dC: zero); dA/domega/dD sum over the
-    requested slices only."""
+    domega, dbeta, dgamma, dD, dh0, dx_prev, dB_prev (float64).  Per-token gradients of
+    slices that were not requested are NaN (dB/dC: zero); dA/domega/dD sum over the
+    requested slices only.  `x_prev` / `B_prev`: the token before the sequence (its
+    gradients come back as dx_prev / dB_prev); `dh_final`: upstream gradient of the final
+    state [b][h][N][P]."""
     desc = OracleDesc.from_dict(prob["desc"])
     lib = load()
     x, B, C, dt, A, om, be, ga, D = _inputs(prob)
@@ -163,17 +169,23 @@ def bwd(prob: dict, dy, slices=None, h0=None):
         "dbeta": np.full((b, T, H), np.nan),
         "dgamma": np.full((b, T, H), np.nan),
         "dh0": np.full((b, H, N, P), np.nan),
+        "dx_prev": np.full((b, H, R, P), np.nan),
+        "dB_prev": np.zeros((b, G, R, N)),
     }
     dA_s = np.zeros((ns, nA))
     dw_s = np.zeros((ns, max(npairs, 1)))
     dD_s = np.zeros((ns,))
     h0 = None if h0 is None else np.ascontiguousarray(h0, dtype=np.float64)
     dc = desc.c()
+    xp, bp = _f32(x_prev), _f32(B_prev)
+    dhf = None if dh_final is None else np.ascontiguousarray(dh_final, dtype=np.float64)
     rc = lib.oracle_bwd(ctypes.byref(dc), _fptr(x), _fptr(B), _fptr(C), _fptr(dt), _fptr(A),
-                        _fptr(om), _fptr(be), _fptr(ga), _fptr(D), _dptr(h0), _fptr(dy),
+                        _fptr(om), _fptr(be), _fptr(ga), _fptr(D), _dptr(h0), _fptr(xp),
+                        _fptr(bp), _fptr(dy), _dptr(dhf),
                         _dptr(out["dx"]), _dptr(out["dB"]), _dptr(out["dC"]), _dptr(out["ddt"]),
                         _dptr(dA_s), _dptr(dw_s), _dptr(out["dbeta"]), _dptr(out["dgamma"]),
-                        _dptr(dD_s), _dptr(out["dh0"]),
+                        _dptr(dD_s), _dptr(out["dh0"]), _dptr(out["dx_prev"]),
+                        _dptr(out["dB_prev"]),
                         sl.ctypes.data_as(ctypes.POINTER(ctypes.c_int)), ns)
     if rc:
         raise ValueError(f"oracle_bwd rejected the descriptor (rc={rc})")

@@ -53,8 +53,13 @@ def transition_matrices(desc: dict, dt, A, omega):
     return Am
 
 
-def quadratic_y(desc: dict, x, B, C, dt, A, omega=None, beta=None, gamma=None, D=None, h0=None):
-    """O(L^2) form of Theorem 24 with explicit transfer products (torch fp64 tensors in/out)."""
+def quadratic_y(desc: dict, x, B, C, dt, A, omega=None, beta=None, gamma=None, D=None, h0=None,
+                x_prev=None, B_prev=None, return_state=False):
+    """O(L^2) form of Theorem 24 with explicit transfer products (torch fp64 tensors in/out).
+    `x_prev` [b][H][R][P] / `B_prev` [b][G][R][N]: the token before the sequence, whose
+    two-endpoint write beta_0 B_prev X_prev enters at token 0 and reaches token t through
+    Phi_{t,0}.  With `return_state`, returns (y, h_final), h_final [b][H][N][P] being the
+    state after the last token summed the same way."""
     b, T, H, G = desc["batch"], desc["seqlen"], desc["nheads"], desc["ngroups"]
     P, N, R, O = desc["headdim"], desc["dstate"], desc["rank_in"], desc["rank_out"]
     if omega is None:
@@ -62,6 +67,7 @@ def quadratic_y(desc: dict, x, B, C, dt, A, omega=None, beta=None, gamma=None, D
     Am = transition_matrices(desc, dt, A, omega)
     eye = torch.eye(N, dtype=torch.float64)
     ys = []
+    finals = []  # h_{T-1} per (batch, head), in that order
     for bb in range(b):
         yb = []
         for t in range(T):
@@ -83,13 +89,20 @@ def quadratic_y(desc: dict, x, B, C, dt, A, omega=None, beta=None, gamma=None, D
                         acc = acc + beta[bb, s + 1, h] * (phis[s + 1] @ w)
                 if h0 is not None:
                     acc = acc + phis[-1] @ h0[bb, h]
+                if desc["two_endpoint"] and x_prev is not None:
+                    acc = acc + beta[bb, 0, h] * (phis[0] @ (B_prev[bb, g].T @ x_prev[bb, h]))
+                if return_state and t == T - 1:
+                    finals.append(acc)
                 yt = C[bb, t, g] @ acc  # O x P
                 if desc["has_D"]:
                     yt = yt + D[h] * x[bb, t, h]
                 yh.append(yt)
             yb.append(torch.stack(yh))
         ys.append(torch.stack(yb))
-    return torch.stack(ys)  # [b, T, H, O, P]
+    y = torch.stack(ys)  # [b, T, H, O, P]
+    if return_state:
+        return y, torch.stack(finals).reshape(b, H, N, P)
+    return y
 
 
 def complex_y(desc: dict, x, B, C, dt, A, omega, beta=None, gamma=None, D=None):

@@ -62,6 +62,10 @@ typedef struct {
   double *rate;  /* [N]  decay rate per row (pairs: both rows share Ac_k) */
   double *omega; /* [n_pairs] */
   double D;
+  /* two-endpoint carry: the previous call's last token (written at t = 0 with beta_0) */
+  int has_prev;
+  double *xprev; /* [R][P] */
+  double *Bprev; /* [R][N] */
 } slice_t;
 
 static void gather_slice(const oracle_desc *d, int b, int h, const float *x, const float *B,
@@ -103,6 +107,20 @@ static void gather_slice(const oracle_desc *d, int b, int h, const float *x, con
   s->D = d->has_D ? D[h] : 0.0;
 }
 
+/* The token before the sequence (two-endpoint carry): x_prev [b][h][R][P], B_prev [b][g][R][N]. */
+static void gather_prev(const oracle_desc *d, int b, int h, const float *x_prev,
+                        const float *B_prev, slice_t *s) {
+  const int H = d->nheads, G = d->ngroups, P = d->headdim, N = d->dstate, R = d->rank_in;
+  const int g = h / (H / G);
+  s->has_prev = d->two_endpoint && x_prev && B_prev;
+  for (int r = 0; r < R; ++r) {
+    for (int p = 0; p < P; ++p)
+      s->xprev[(size_t)r * P + p] = s->has_prev ? x_prev[(((size_t)b * H + h) * R + r) * P + p] : 0.0;
+    for (int n = 0; n < N; ++n)
+      s->Bprev[(size_t)r * N + n] = s->has_prev ? B_prev[(((size_t)b * G + g) * R + r) * N + n] : 0.0;
+  }
+}
+
 static slice_t alloc_slice(const oracle_desc *d) {
   slice_t s;
   const size_t T = d->seqlen;
@@ -115,12 +133,26 @@ static slice_t alloc_slice(const oracle_desc *d) {
   s.gamma = malloc(sizeof(double) * T);
   s.rate = malloc(sizeof(double) * d->dstate);
   s.omega = malloc(sizeof(double) * (d->n_pairs > 0 ? d->n_pairs : 1));
+  s.has_prev = 0;
+  s.xprev = calloc((size_t)d->rank_in * d->headdim, sizeof(double));
+  s.Bprev = calloc((size_t)d->rank_in * d->dstate, sizeof(double));
   return s;
 }
 
 static void free_slice(slice_t *s) {
   free(s->x); free(s->B); free(s->C); free(s->delta); free(s->draw);
-  free(s->beta); free(s->gamma); free(s->rate); free(s->omega);
+  free(s->beta); free(s->gamma); free(s->rate); free(s->omega); free(s->xprev); free(s->Bprev);
+}
+
+/* B and X of token t - 1 for the beta write of token t (the carried token at t = 0), or
+   NULL when there is none. */
+static const double *prev_B(const slice_t *s, int t, int r) {
+  if (t > 0) return s->B + ((size_t)(t - 1) * s->R + r) * s->N;
+  return s->has_prev ? s->Bprev + (size_t)r * s->N : NULL;
+}
+static const double *prev_X(const slice_t *s, int t, int r) {
+  if (t > 0) return s->x + ((size_t)(t - 1) * s->R + r) * s->P;
+  return s->has_prev ? s->xprev + (size_t)r * s->P : NULL;
 }
 
 /* h <- A_t h  (block-diagonal transition of step t). */
@@ -177,9 +209,9 @@ static void add_write(const slice_t *s, int t, double *h) {
       const double bn = gm * Bt[n];
       for (int p = 0; p < P; ++p) h[(size_t)n * P + p] += bn * Xt[p];
     }
-    if (s->two_endpoint && t > 0) {
-      const double *Bp = s->B + ((size_t)(t - 1) * R + r) * N;
-      const double *Xp = s->x + ((size_t)(t - 1) * R + r) * P;
+    if (s->two_endpoint && prev_B(s, t, r)) {
+      const double *Bp = prev_B(s, t, r);
+      const double *Xp = prev_X(s, t, r);
       const double bt = s->beta[t];
       for (int n = 0; n < N; ++n) {
         const double bn = bt * Bp[n];
@@ -222,8 +254,9 @@ static int check_desc(const oracle_desc *d) {
 
 int oracle_fwd(const oracle_desc *d, const float *x, const float *B, const float *C,
                const float *dt, const float *A, const float *omega, const float *beta,
-               const float *gamma, const float *D, const double *h0, double *y,
-               double *h_final, const int *slices, int n_slices) {
+               const float *gamma, const float *D, const double *h0, const float *x_prev,
+               const float *B_prev, double *y, double *h_final, const int *slices,
+               int n_slices) {
   int rc = check_desc(d);
   if (rc) return rc;
   const int T = d->seqlen, H = d->nheads, P = d->headdim, N = d->dstate, O = d->rank_out;
@@ -232,6 +265,7 @@ int oracle_fwd(const oracle_desc *d, const float *x, const float *B, const float
     const int b = slices[2 * si], hh = slices[2 * si + 1];
     slice_t s = alloc_slice(d);
     gather_slice(d, b, hh, x, B, C, dt, A, omega, beta, gamma, D, &s);
+    gather_prev(d, b, hh, x_prev, B_prev, &s);
     double *h = calloc((size_t)N * P, sizeof(double));
     double *yt = malloc(sizeof(double) * O * P);
     if (h0) memcpy(h, h0 + ((size_t)b * H + hh) * N * P, sizeof(double) * N * P);
@@ -251,10 +285,11 @@ int oracle_fwd(const oracle_desc *d, const float *x, const float *B, const float
 
 int oracle_bwd(const oracle_desc *d, const float *x, const float *B, const float *C,
                const float *dt, const float *A, const float *omega, const float *beta,
-               const float *gamma, const float *D, const double *h0, const float *dy,
-               double *dx, double *dB, double *dC, double *ddt, double *dA_slices,
-               double *domega_slices, double *dbeta, double *dgamma, double *dD_slices,
-               double *dh0, const int *slices, int n_slices) {
+               const float *gamma, const float *D, const double *h0, const float *x_prev,
+               const float *B_prev, const float *dy, const double *dh_final, double *dx,
+               double *dB, double *dC, double *ddt, double *dA_slices, double *domega_slices,
+               double *dbeta, double *dgamma, double *dD_slices, double *dh0, double *dx_prev,
+               double *dB_prev, const int *slices, int n_slices) {
   int rc = check_desc(d);
   if (rc) return rc;
   const int T = d->seqlen, H = d->nheads, G = d->ngroups, P = d->headdim, N = d->dstate;
@@ -265,6 +300,7 @@ int oracle_bwd(const oracle_desc *d, const float *x, const float *B, const float
     const int b = slices[2 * si], hh = slices[2 * si + 1], g = hh / (H / G);
     slice_t s = alloc_slice(d);
     gather_slice(d, b, hh, x, B, C, dt, A, omega, beta, gamma, D, &s);
+    gather_prev(d, b, hh, x_prev, B_prev, &s);
     const size_t NP = (size_t)N * P;
     const int nck = (T + CKPT - 1) / CKPT;
     /* checkpoints: state h_{c*CKPT - 1} entering segment c */
@@ -278,6 +314,10 @@ int oracle_bwd(const oracle_desc *d, const float *x, const float *B, const float
     /* seg[i] holds h_{t0-1+i}, i = 0..CKPT */
     double *seg = malloc(sizeof(double) * NP * (CKPT + 1));
     double *gs = calloc(NP, sizeof(double));   /* running adjoint */
+    /* an upstream gradient of the final state enters as the adjoint after the last token */
+    if (dh_final) memcpy(gs, dh_final + ((size_t)b * H + hh) * NP, sizeof(double) * NP);
+    double *dxp = calloc((size_t)R * P, sizeof(double));  /* carried token's gradients */
+    double *dBp = calloc((size_t)R * N, sizeof(double));
     double *dA_loc = calloc(nA, sizeof(double));
     double *dw_loc = calloc(np > 0 ? np : 1, sizeof(double));
     double dD_loc = 0.0;
@@ -333,15 +373,18 @@ int oracle_bwd(const oracle_desc *d, const float *x, const float *B, const float
               dgam += gv * Bt[n] * Xt[p];
             }
           dgs[t] += dgam;
-          if (s.two_endpoint && t > 0) {
-            const double *Bp = s.B + ((size_t)(t - 1) * R + r) * N;
-            const double *Xp = s.x + ((size_t)(t - 1) * R + r) * P;
+          if (s.two_endpoint && prev_B(&s, t, r)) {
+            const double *Bp = prev_B(&s, t, r);
+            const double *Xp = prev_X(&s, t, r);
+            /* token t - 1's gradients, or the carried token's at t = 0 */
+            double *gx = t > 0 ? dxs + ((size_t)(t - 1) * R + r) * P : dxp + (size_t)r * P;
+            double *gb = t > 0 ? dBs + ((size_t)(t - 1) * R + r) * N : dBp + (size_t)r * N;
             double dbet = 0.0;
             for (int n = 0; n < N; ++n)
               for (int p = 0; p < P; ++p) {
                 const double gv = gs[(size_t)n * P + p];
-                dxs[((size_t)(t - 1) * R + r) * P + p] += s.beta[t] * Bp[n] * gv;
-                dBs[((size_t)(t - 1) * R + r) * N + n] += s.beta[t] * gv * Xp[p];
+                gx[p] += s.beta[t] * Bp[n] * gv;
+                gb[n] += s.beta[t] * gv * Xp[p];
                 dbet += gv * Bp[n] * Xp[p];
               }
             dbs[t] += dbet;
@@ -421,6 +464,14 @@ int oracle_bwd(const oracle_desc *d, const float *x, const float *B, const float
     for (int k = 0; k < np; ++k) domega_slices[(size_t)si * np + k] = dw_loc[k];
     dD_slices[si] = dD_loc;
     if (dh0) memcpy(dh0 + ((size_t)b * H + hh) * NP, gs, sizeof(double) * NP);
+    if (dx_prev)
+      for (size_t i = 0; i < (size_t)R * P; ++i) dx_prev[((size_t)b * H + hh) * R * P + i] = dxp[i];
+    if (dB_prev) {
+      /* per group: the sum over its heads (accumulated; the caller zeroes it) */
+#pragma omp critical(oracle_group_accum)
+      for (size_t i = 0; i < (size_t)R * N; ++i) dB_prev[((size_t)b * G + g) * R * N + i] += dBp[i];
+    }
+    free(dxp); free(dBp);
     free(ck); free(h); free(seg); free(gs); free(dA_loc); free(dw_loc);
     free(dxs); free(dBs); free(dCs); free(dDel); free(dbs); free(dgs);
     free_slice(&s);

@@ -10,7 +10,11 @@
  *   dt, beta, gamma [b][t][h]
  *   A     head mode: [h]; coordinate mode: [h][n_real + n_pairs]
  *         (first n_real entries: real-row rates; then one rate per pair)
- *   omega [h][n_pairs]        D [h]        h0, h_final, dh0 [b][h][n][p]
+ *   omega [h][n_pairs]        D [h]        h0, h_final, dh0, dh_final [b][h][n][p]
+ *   x_prev, dx_prev [b][h][r][p], B_prev, dB_prev [b][g][r][n]: the token before the
+ *         sequence (two-endpoint carry: its write beta_0 B_prev X_prev enters at token 0);
+ *         NULL = none.  dh_final: upstream gradient of the final state (NULL = zero).
+ *         dB_prev is accumulated (+=) per group and must be zeroed by the caller.
  *   y, dy [b][t][h][o][p]
  * Inputs are fp32 values, outputs fp64.  `slices` lists (b, h) pairs to
  * compute; outputs of other slices are left untouched.  With ngroups < nheads
@@ -37,15 +41,17 @@ typedef struct {
 
 int oracle_fwd(const oracle_desc *d, const float *x, const float *B, const float *C,
                const float *dt, const float *A, const float *omega, const float *beta,
-               const float *gamma, const float *D, const double *h0, double *y,
-               double *h_final, const int *slices, int n_slices);
+               const float *gamma, const float *D, const double *h0, const float *x_prev,
+               const float *B_prev, double *y, double *h_final, const int *slices,
+               int n_slices);
 
 int oracle_bwd(const oracle_desc *d, const float *x, const float *B, const float *C,
                const float *dt, const float *A, const float *omega, const float *beta,
-               const float *gamma, const float *D, const double *h0, const float *dy,
-               double *dx, double *dB, double *dC, double *ddt, double *dA_slices,
-               double *domega_slices, double *dbeta, double *dgamma, double *dD_slices,
-               double *dh0, const int *slices, int n_slices);
+               const float *gamma, const float *D, const double *h0, const float *x_prev,
+               const float *B_prev, const float *dy, const double *dh_final, double *dx,
+               double *dB, double *dC, double *ddt, double *dA_slices, double *domega_slices,
+               double *dbeta, double *dgamma, double *dD_slices, double *dh0, double *dx_prev,
+               double *dB_prev, const int *slices, int n_slices);
 
 #ifdef __cplusplus
 }

@@ -451,3 +451,88 @@ def test_slice_selection_matches_full_run(oracle_lib):
     ys, _ = oracle.fwd(p, slices=[(2, 1), (0, 3)])
     assert np.array_equal(ys[2, :, 1], y[2, :, 1]) and np.array_equal(ys[0, :, 3], y[0, :, 3])
     assert np.isnan(ys[1]).all()
+
+
+# ---------------------------------------------------------------- P9 two-endpoint carry
+def _carry_problem(seed=93, T=21):
+    s = small("hybrid", batch=2, seqlen=T, nheads=2, ngroups=1, headdim=3, dstate=6, n_real=2,
+              n_pairs=2, rank_in=2, rank_out=2)
+    return workloads.make_problem(s, seed=seed, with_dy=True)
+
+
+def _part(p, lo, hi):
+    q = dict(p)
+    q["desc"] = dict(p["desc"], seqlen=hi - lo)
+    for k in ("x", "B", "C", "dt", "beta", "gamma", "dy"):
+        q[k] = np.ascontiguousarray(p[k][:, lo:hi])
+    return q
+
+
+def test_p9_two_endpoint_split_run_carries_state_and_last_write_bitwise(oracle_lib):
+    """A two-endpoint run split at L1 and continued with h0 = the first part's final state
+    and the first part's last token (x, B) as the carried token reproduces one run bit for
+    bit ("carry continuation", Blog Part 10; the initial state of Theorem 24, Part 03)."""
+    p = _carry_problem()
+    T, L1 = p["desc"]["seqlen"], 9
+    y, hf = oracle.fwd(p)
+    y1, h1 = oracle.fwd(_part(p, 0, L1))
+    y2, h2 = oracle.fwd(_part(p, L1, T), h0=h1, x_prev=p["x"][:, L1 - 1], B_prev=p["B"][:, L1 - 1])
+    assert np.array_equal(np.concatenate([y1, y2], axis=1), y)
+    assert np.array_equal(h2, hf)
+    # without the carried token the continuation misses beta_{L1} B_{L1-1} X_{L1-1}
+    y2n, _ = oracle.fwd(_part(p, L1, T), h0=h1)
+    assert not np.allclose(y2n, y[:, L1:])
+
+
+def test_p9_split_gradients_chain_through_the_carry(oracle_lib):
+    """The gradients of one run equal those of the split run chained backwards: the second
+    part's dh0 enters the first part as dh_final, and its dx_prev / dB_prev add to the
+    first part's last token; parameter gradients add."""
+    p = _carry_problem(seed=94)
+    T, L1 = p["desc"]["seqlen"], 12
+    g = oracle.bwd(p, p["dy"])
+    _, h1 = oracle.fwd(_part(p, 0, L1))
+    p2 = _part(p, L1, T)
+    g2 = oracle.bwd(p2, p2["dy"], h0=h1, x_prev=p["x"][:, L1 - 1], B_prev=p["B"][:, L1 - 1])
+    p1 = _part(p, 0, L1)
+    g1 = oracle.bwd(p1, p1["dy"], dh_final=g2["dh0"])
+    dx1, dB1 = g1["dx"].copy(), g1["dB"].copy()
+    dx1[:, L1 - 1] += g2["dx_prev"]
+    dB1[:, L1 - 1] += g2["dB_prev"]
+    tol = dict(rtol=1e-11, atol=1e-13)
+    np.testing.assert_allclose(np.concatenate([dx1, g2["dx"]], axis=1), g["dx"], **tol)
+    np.testing.assert_allclose(np.concatenate([dB1, g2["dB"]], axis=1), g["dB"], **tol)
+    for k in ("dC", "ddt", "dbeta", "dgamma"):
+        np.testing.assert_allclose(np.concatenate([g1[k], g2[k]], axis=1), g[k], err_msg=k, **tol)
+    for k in ("dA", "domega", "dD"):
+        np.testing.assert_allclose(g1[k] + g2[k], g[k], err_msg=k, **tol)
+    np.testing.assert_allclose(g1["dh0"], g["dh0"], **tol)
+
+
+def test_p8_carry_gradients_match_autograd_of_quadratic_form(oracle_lib):
+    """dx_prev, dB_prev, dbeta_0 and the effect of dh_final, against torch autograd of the
+    O(L^2) form with the carried write and the final state (loss <y, dy> + <h_final, dh_final>)."""
+    p = _carry_problem(seed=95, T=7)
+    d = p["desc"]
+    rng = np.random.default_rng(96)
+    xp = rng.standard_normal((d["batch"], d["nheads"], d["rank_in"], d["headdim"])).astype(np.float32)
+    bp = rng.standard_normal((d["batch"], d["ngroups"], d["rank_in"], d["dstate"])).astype(np.float32)
+    dhf = rng.standard_normal((d["batch"], d["nheads"], d["dstate"], d["headdim"]))
+    h0 = rng.standard_normal((d["batch"], d["nheads"], d["dstate"], d["headdim"]))
+    ins = {k: T64(p[k]).requires_grad_() for k in ("x", "B", "C", "dt", "A", "omega", "beta",
+                                                    "gamma", "D")}
+    xpt, bpt = T64(xp).requires_grad_(), T64(bp).requires_grad_()
+    y, hf = forms.quadratic_y(d, ins["x"], ins["B"], ins["C"], ins["dt"], ins["A"], ins["omega"],
+                              ins["beta"], ins["gamma"], ins["D"], h0=T64(h0), x_prev=xpt,
+                              B_prev=bpt, return_state=True)
+    ((y * T64(p["dy"])).sum() + (hf * T64(dhf)).sum()).backward()
+    g = oracle.bwd(p, p["dy"], h0=h0, x_prev=xp, B_prev=bp, dh_final=dhf)
+    yo, hfo = oracle.fwd(p, h0=h0, x_prev=xp, B_prev=bp)
+    np.testing.assert_allclose(yo, y.detach().numpy(), rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(hfo, hf.detach().numpy(), rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(g["dx_prev"], xpt.grad.numpy(), rtol=1e-9, atol=1e-12)
+    np.testing.assert_allclose(g["dB_prev"], bpt.grad.numpy(), rtol=1e-9, atol=1e-12)
+    for k, gk in GRAD_PAIRS:
+        ref = ins[k].grad.numpy()
+        np.testing.assert_allclose(g[gk], ref, rtol=1e-9, atol=1e-12 * max(1, np.abs(ref).max()),
+                                   err_msg=gk)
