@@ -62,9 +62,8 @@
  *     takes h0 through `saved` (the forward stores it as the first boundary
  *     state), so a forward with h0 must precede a backward that wants dh0 or
  *     the h0-dependent parts of the other gradients.  The two-endpoint term of
- *     token 0 (beta_0 B_{-1} X_{-1}) stays zero with or without h0: an exact
- *     continuation of a two-endpoint run folds A_0^{-1} beta_0 B_{-1} X_{-1}
- *     into h0 on the caller's side.
+ *     token 0 (beta_0 B_{-1} X_{-1}) is zero unless the carried token x_prev /
+ *     B_prev is given (see the args).
  *   - Empty problems (batch = 0 or seqlen = 0) read no inputs, and the pointers
  *     of empty tensors may be NULL.  The outputs that are not empty are still
  *     written: ssm_scan_fwd sets h_final to h0 (zero without h0);
@@ -87,7 +86,7 @@
 extern "C" {
 #endif
 
-#define SSM_ABI_VERSION 4
+#define SSM_ABI_VERSION 5
 
 typedef enum {
   SSM_OK = 0,
@@ -138,6 +137,12 @@ typedef struct {
   void *const *events; /* optional: 2 hipEvent_t recorded on `stream` before and after
                           the kernel (per-kernel timing); NULL = none, and a NULL entry
                           is not recorded */
+  /* optional two-endpoint carry: the token before the sequence (x_prev
+     [batch][nheads][rank_in][headdim], B_prev [batch][ngroups][rank_in][dstate], io
+     dtype), whose write beta_0 B_prev x_prev enters at token 0; both or neither, and
+     only with SSM_F_TWO_ENDPOINT.  A run continued with h0 = the previous call's h_final
+     and these = its last token's x and B equals one run over both parts. */
+  const void *x_prev, *B_prev;
 } ssm_fwd_args;
 
 typedef struct {
@@ -151,6 +156,15 @@ typedef struct {
                           kernels of the pass (boundary adjoints, chunk gradients,
                           parameter sums); NULL = none, and a NULL entry is not
                           recorded */
+  /* optional carry across calls: x_prev / B_prev as given to the forward; dh_final, the
+     upstream gradient of the forward's h_final (fp32 [batch][nheads][N][P], NULL =
+     zero); dx_prev / dB_prev receive the carried token's gradients (shapes and dtype of
+     x_prev / B_prev; dB_prev summed over a group's heads), which need x_prev / B_prev.
+     Chained backwards (dh0 of a call -> dh_final of the call before it, dx_prev /
+     dB_prev added to its last token) the calls give the gradients of one run. */
+  const void *x_prev, *B_prev;
+  const float *dh_final;
+  void *dx_prev, *dB_prev;
 } ssm_bwd_args;
 
 /* Library ABI version (SSM_ABI_VERSION of the build). */

@@ -40,13 +40,14 @@ _vp = ctypes.c_void_p
 
 class SsmFwdArgs(ctypes.Structure):
     _fields_ = [(n, _vp) for n in ("x", "B", "C", "dt", "A", "omega", "beta", "gamma", "D", "y",
-                                   "saved", "h0", "h_final", "events")]
+                                   "saved", "h0", "h_final", "events", "x_prev", "B_prev")]
 
 
 class SsmBwdArgs(ctypes.Structure):
     _fields_ = [(n, _vp) for n in ("x", "B", "C", "dy", "dt", "A", "omega", "beta", "gamma", "D",
                                    "saved", "dx", "dB", "dC", "ddt", "dA", "domega", "dbeta",
-                                   "dgamma", "dD", "dh0", "events")]
+                                   "dgamma", "dD", "dh0", "events", "x_prev", "B_prev",
+                                   "dh_final", "dx_prev", "dB_prev")]
 
 
 class SsmDecodeArgs(ctypes.Structure):
@@ -170,6 +171,14 @@ def _state_numel(desc: SsmDesc) -> int:
     return desc.batch * desc.nheads * desc.dstate * desc.headdim
 
 
+def _check_prev(seen, desc: SsmDesc, x_prev, B_prev, names=("x_prev", "B_prev")):
+    io = _io_torch_dtype(desc)
+    _check(seen, names[0], x_prev, desc.batch * desc.nheads * desc.rank_in * desc.headdim, io,
+           required=False)
+    _check(seen, names[1], B_prev, desc.batch * desc.ngroups * desc.rank_in * desc.dstate, io,
+           required=False)
+
+
 def _stream(stream):
     if stream is None:
         import torch
@@ -204,9 +213,11 @@ def _events(events):
 
 
 def scan_fwd(desc: SsmDesc, x, B, C, dt, A, y, omega=None, beta=None, gamma=None, D=None,
-             saved=None, ws=None, stream=None, events=None, h0=None, h_final=None) -> None:
+             saved=None, ws=None, stream=None, events=None, h0=None, h_final=None, x_prev=None,
+             B_prev=None) -> None:
     """Enqueue the forward scan; all tensors are caller-allocated device tensors.
     `h0` / `h_final`: optional fp32 [batch][nheads][N][P] initial / final states.
+    `x_prev` / `B_prev`: the token before the sequence (two-endpoint carry).
     `events`: optional 2 torch.cuda.Event recorded around the kernel."""
     import torch
     seen = []
@@ -220,12 +231,14 @@ def scan_fwd(desc: SsmDesc, x, B, C, dt, A, y, omega=None, beta=None, gamma=None
                                f"the descriptor needs {saved_bytes(desc)}")
     _check(seen, "h0", h0, _state_numel(desc), torch.float32, required=False)
     _check(seen, "h_final", h_final, _state_numel(desc), torch.float32, required=False)
+    _check_prev(seen, desc, x_prev, B_prev)
     if ws is not None:
         _check(seen, "ws", ws, 0, None, at_least=True)
     _check_devices(seen)
     ev, _keep = _events(events)
     args = SsmFwdArgs(_ptr(x), _ptr(B), _ptr(C), _ptr(dt), _ptr(A), _ptr(omega), _ptr(beta),
-                      _ptr(gamma), _ptr(D), _ptr(y), _ptr(saved), _ptr(h0), _ptr(h_final), ev)
+                      _ptr(gamma), _ptr(D), _ptr(y), _ptr(saved), _ptr(h0), _ptr(h_final), ev,
+                      _ptr(x_prev), _ptr(B_prev))
     ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
     rc = load().ssm_scan_fwd(ctypes.byref(desc), ctypes.byref(args), _ptr(ws), ws_bytes,
                              _stream(stream))
@@ -239,7 +252,8 @@ def scratch_bytes() -> int:
 
 
 def scan_fwd_noalloc(desc: SsmDesc, x, B, C, dt, A, y, omega=None, beta=None, gamma=None,
-                     D=None, saved=None, stream=None, h0=None, h_final=None) -> None:
+                     D=None, saved=None, stream=None, h0=None, h_final=None, x_prev=None,
+                     B_prev=None) -> None:
     """scan_fwd with the library's static scratch array as workspace: the call allocates
     nothing.  Raises SsmError (SSM_ERR_SCRATCH) when the problem's forward workspace
     exceeds scratch_bytes().  Calls that overlap on one GPU share the array and race."""
@@ -255,9 +269,11 @@ def scan_fwd_noalloc(desc: SsmDesc, x, B, C, dt, A, y, omega=None, beta=None, ga
                                f"the descriptor needs {saved_bytes(desc)}")
     _check(seen, "h0", h0, _state_numel(desc), torch.float32, required=False)
     _check(seen, "h_final", h_final, _state_numel(desc), torch.float32, required=False)
+    _check_prev(seen, desc, x_prev, B_prev)
     _check_devices(seen)
     args = SsmFwdArgs(_ptr(x), _ptr(B), _ptr(C), _ptr(dt), _ptr(A), _ptr(omega), _ptr(beta),
-                      _ptr(gamma), _ptr(D), _ptr(y), _ptr(saved), _ptr(h0), _ptr(h_final), None)
+                      _ptr(gamma), _ptr(D), _ptr(y), _ptr(saved), _ptr(h0), _ptr(h_final), None,
+                      _ptr(x_prev), _ptr(B_prev))
     rc = load().ssm_scan_fwd_noalloc(ctypes.byref(desc), ctypes.byref(args), _stream(stream))
     if rc != SSM_OK:
         raise SsmError(rc, "ssm_scan_fwd_noalloc")
@@ -265,9 +281,12 @@ def scan_fwd_noalloc(desc: SsmDesc, x, B, C, dt, A, y, omega=None, beta=None, ga
 
 def scan_bwd(desc: SsmDesc, x, B, C, dy, dt, A, saved, dx, dB, dC, ddt, omega=None, beta=None,
              gamma=None, D=None, dA=None, domega=None, dbeta=None, dgamma=None, dD=None, ws=None,
-             stream=None, events=None, dh0=None) -> None:
+             stream=None, events=None, dh0=None, x_prev=None, B_prev=None, dh_final=None,
+             dx_prev=None, dB_prev=None) -> None:
     """Enqueue the fused reverse pass; all tensors are caller-allocated device tensors.
     `dh0`: optional fp32 [batch][nheads][N][P] gradient of the initial state.
+    `x_prev` / `B_prev`: the carried token given to the forward; `dh_final`: upstream
+    gradient of the final state; `dx_prev` / `dB_prev`: the carried token's gradients.
     `events`: optional 4 torch.cuda.Event recorded around the pass's three kernels."""
     import torch
     seen = []
@@ -290,6 +309,9 @@ def scan_bwd(desc: SsmDesc, x, B, C, dy, dt, A, saved, dx, dB, dC, ddt, omega=No
     _check(seen, "dgamma", dgamma, b * L * H, f32, required=False)
     _check(seen, "dD", dD, desc.nheads, f32, required=False)
     _check(seen, "dh0", dh0, _state_numel(desc), f32, required=False)
+    _check_prev(seen, desc, x_prev, B_prev)
+    _check_prev(seen, desc, dx_prev, dB_prev, names=("dx_prev", "dB_prev"))
+    _check(seen, "dh_final", dh_final, _state_numel(desc), f32, required=False)
     if ws is not None:
         _check(seen, "ws", ws, 0, None, at_least=True)
     _check_devices(seen)
@@ -297,7 +319,8 @@ def scan_bwd(desc: SsmDesc, x, B, C, dy, dt, A, saved, dx, dB, dC, ddt, omega=No
     args = SsmBwdArgs(_ptr(x), _ptr(B), _ptr(C), _ptr(dy), _ptr(dt), _ptr(A), _ptr(omega),
                       _ptr(beta), _ptr(gamma), _ptr(D), _ptr(saved), _ptr(dx), _ptr(dB),
                       _ptr(dC), _ptr(ddt), _ptr(dA), _ptr(domega), _ptr(dbeta), _ptr(dgamma),
-                      _ptr(dD), _ptr(dh0), ev)
+                      _ptr(dD), _ptr(dh0), ev, _ptr(x_prev), _ptr(B_prev), _ptr(dh_final),
+                      _ptr(dx_prev), _ptr(dB_prev))
     ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
     rc = load().ssm_scan_bwd(ctypes.byref(desc), ctypes.byref(args), _ptr(ws), ws_bytes,
                              _stream(stream))

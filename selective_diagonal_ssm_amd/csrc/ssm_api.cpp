@@ -35,6 +35,20 @@ hipError_t copy_or_zero(float* dst, const float* src, size_t n, hipStream_t s) {
   return hipGetLastError();
 }
 
+__global__ void __launch_bounds__(256) zero_bytes_kernel(unsigned char* __restrict__ dst, size_t n) {
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) dst[i] = 0;
+}
+
+// dst[0, n) = 0 (any element type); nothing when dst is NULL or n is 0
+hipError_t zero_bytes(void* dst, size_t n, hipStream_t s) {
+  if (!dst || n == 0) return hipSuccess;
+  const unsigned blocks = (unsigned)std::min<size_t>((n + 255) / 256, 2048);
+  hipLaunchKernelGGL(zero_bytes_kernel, dim3(blocks), dim3(256), 0, s,
+                     static_cast<unsigned char*>(dst), n);
+  return hipGetLastError();
+}
+
 size_t state_floats(const ssm_desc* d) {
   return (size_t)d->batch * d->nheads * d->dstate * d->headdim;
 }
@@ -213,8 +227,9 @@ static int npart_of(const ssm_desc* d, const Plan& pl) {
   return na + d->n_pairs + 1;
 }
 
+// boundary adjoints: one slot per chunk and one after the last token (dh_final or zero)
 static size_t bwd_gseg_bytes(const ssm_desc* d, const Plan& pl) {
-  return (size_t)d->batch * d->nheads * pl.nchunks * d->dstate * d->headdim * (pl.bf16 ? 2 : 4);
+  return (size_t)d->batch * d->nheads * (pl.nchunks + 1) * d->dstate * d->headdim * (pl.bf16 ? 2 : 4);
 }
 
 // head groups shared by several heads: per-head dB and dC partials in the io dtype
@@ -355,8 +370,11 @@ int scan_fwd_impl(const ssm_desc* d, const ssm_fwd_args* a, void* ws, size_t ws_
   if ((d->n_pairs > 0) != (a->omega != nullptr)) return SSM_ERR_NULL;
   if (te != (a->beta != nullptr) || te != (a->gamma != nullptr)) return SSM_ERR_NULL;
   if (hasD != (a->D != nullptr)) return SSM_ERR_NULL;
+  if ((a->x_prev != nullptr) != (a->B_prev != nullptr) || (a->x_prev && !te)) return SSM_ERR_NULL;
   for (const void* q : {a->x, a->B, a->C, (const void*)a->y})
     if (!aligned(q, 16)) return SSM_ERR_ALIGN;
+  for (const void* q : {a->x_prev, a->B_prev})
+    if (q && !aligned(q, 16)) return SSM_ERR_ALIGN;
   for (const void* q : {(const void*)a->dt, (const void*)a->A, (const void*)a->omega,
                         (const void*)a->beta, (const void*)a->gamma, (const void*)a->D})
     if (q && !aligned(q, 4)) return SSM_ERR_ALIGN;
@@ -369,7 +387,7 @@ int scan_fwd_impl(const ssm_desc* d, const ssm_fwd_args* a, void* ws, size_t ws_
   ssm::FwdParams p{};
   p.x = a->x; p.B = a->B; p.C = a->C; p.dt = a->dt; p.A = a->A; p.omega = a->omega;
   p.beta = a->beta; p.gamma = a->gamma; p.D = a->D; p.y = a->y; p.saved = a->saved;
-  p.h0 = a->h0; p.h_final = a->h_final;
+  p.h0 = a->h0; p.h_final = a->h_final; p.x_prev = a->x_prev; p.B_prev = a->B_prev;
   p.batch = d->batch; p.L = d->seqlen; p.H = d->nheads; p.G = d->ngroups; p.P = d->headdim;
   p.n_real = d->n_real; p.n_pairs = d->n_pairs; p.nchunks = pl.nchunks;
   p.npblk = d->headdim / pb;
@@ -453,7 +471,14 @@ int ssm_scan_bwd(const ssm_desc* d, const ssm_bwd_args* a, void* ws, size_t ws_b
     hipError_t e = copy_or_zero(a->dA, nullptr, na, s);
     if (e == hipSuccess) e = copy_or_zero(a->domega, nullptr, (size_t)d->nheads * d->n_pairs, s);
     if (e == hipSuccess) e = copy_or_zero(a->dD, nullptr, (size_t)d->nheads, s);
-    if (e == hipSuccess) e = copy_or_zero(a->dh0, nullptr, state_floats(d), s);
+    // with no tokens h_final is h0, so dh0 is the final state's gradient; the carried
+    // token writes nothing, so its gradients are zero
+    if (e == hipSuccess) e = copy_or_zero(a->dh0, d->seqlen == 0 ? a->dh_final : nullptr, state_floats(d), s);
+    const size_t io = pl.bf16 ? 2 : 4;
+    if (e == hipSuccess)
+      e = zero_bytes(a->dx_prev, (size_t)d->batch * d->nheads * d->rank_in * d->headdim * io, s);
+    if (e == hipSuccess)
+      e = zero_bytes(a->dB_prev, (size_t)d->batch * d->ngroups * d->rank_in * d->dstate * io, s);
     return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
   }
   const bool te = (d->flags & SSM_F_TWO_ENDPOINT) != 0;
@@ -467,8 +492,12 @@ int ssm_scan_bwd(const ssm_desc* d, const ssm_bwd_args* a, void* ws, size_t ws_b
   if (!te && (a->dbeta || a->dgamma)) return SSM_ERR_NULL;
   if (d->n_pairs == 0 && a->domega) return SSM_ERR_NULL;
   if (!hasD && a->dD) return SSM_ERR_NULL;
+  if ((a->x_prev != nullptr) != (a->B_prev != nullptr) || (a->x_prev && !te)) return SSM_ERR_NULL;
+  if ((a->dx_prev || a->dB_prev) && !a->x_prev) return SSM_ERR_NULL;
   for (const void* q : {a->x, a->B, a->C, a->dy, (const void*)a->dx, (const void*)a->dB,
-                        (const void*)a->dC, (const void*)a->saved, (const void*)ws})
+                        (const void*)a->dC, (const void*)a->saved, (const void*)ws, a->x_prev,
+                        a->B_prev, (const void*)a->dh_final, (const void*)a->dx_prev,
+                        (const void*)a->dB_prev})
     if (q && !aligned(q, 16)) return SSM_ERR_ALIGN;
   for (const void* q : {(const void*)a->dt, (const void*)a->A, (const void*)a->omega,
                         (const void*)a->beta, (const void*)a->gamma, (const void*)a->D,
@@ -484,6 +513,8 @@ int ssm_scan_bwd(const ssm_desc* d, const ssm_bwd_args* a, void* ws, size_t ws_b
   p.omega = a->omega; p.beta = a->beta; p.gamma = a->gamma; p.D = a->D; p.saved = a->saved;
   p.dx = a->dx; p.dB = a->dB; p.dC = a->dC; p.ddt = a->ddt; p.dbeta = a->dbeta;
   p.dgamma = a->dgamma; p.dA = a->dA; p.domega = a->domega; p.dD = a->dD; p.dh0 = a->dh0;
+  p.x_prev = a->x_prev; p.B_prev = a->B_prev; p.dh_final = a->dh_final;
+  p.dx_prev = a->dx_prev; p.dB_prev = a->dB_prev;
   p.gseg = ws;
   p.part = reinterpret_cast<float*>(static_cast<char*>(ws) +
                                     (bwd_gseg_bytes(d, pl) + 255) / 256 * 256);

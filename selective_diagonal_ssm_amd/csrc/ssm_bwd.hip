@@ -104,7 +104,9 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_adjoint(BwdParams p) {
 
   // carried adjoint: zero past the sequence end, else (full pass of a segment) the
   // adjoint flowing in from the segments on the right
-  const float* g_in = seg + 1 < p.nseg ? p.gin + ((size_t)slice * p.nseg + seg) * N * p.P + p0 : nullptr;
+  // (the last segment: dh_final, the adjoint after the last token, or zero)
+  const float* g_in = seg + 1 < p.nseg ? p.gin + ((size_t)slice * p.nseg + seg) * N * p.P + p0
+                      : (p.dh_final ? p.dh_final + (size_t)slice * N * p.P + p0 : nullptr);
   // adjoint tiles, transposed: st[k][i] = G[n = 16 tn + (lane & 15)][p = 16 tp + 4 (lane >> 4) + i]
   // (one state row per lane, so each lane stores a 4-column piece; a pair's two rows
   // sit in lanes l, l ^ 1)
@@ -125,6 +127,18 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_adjoint(BwdParams p) {
   for (int k = 0; k < S::ST_PER_WAVE; ++k) asm volatile("" : "+v"(st[k]));
 
   const int nch = p.nchunks;
+  if (seg == p.nseg - 1) {
+    // boundary slot nch: the adjoint after the last token, read by the last chunk's gradients
+#pragma unroll
+    for (int k = 0; k < S::ST_PER_WAVE; ++k) {
+      const int tile = wave + NW * k;
+      if (tile < S::ST_TILES) {
+        const int n = 16 * (tile / S::TP) + (lane & 15), pl = 16 * (tile % S::TP) + 4 * (lane >> 4);
+        const float v4[4] = {st[k][0], st[k][1], st[k][2], st[k][3]};
+        store4<BF16>(static_cast<T*>(p.gseg) + (((size_t)slice * (nch + 1) + nch) * N + n) * P + p0 + pl, v4);
+      }
+    }
+  }
   // register prefetch of one chunk's C rows, dy rows and steps
   uint4 pc[S::C_PER], py[S::Y_PER];
   float pdt = 0.f;
@@ -264,7 +278,7 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_adjoint(BwdParams p) {
         st[k] = acc;
         // the boundary adjoint in the io dtype (it enters the chunk products so)
         const int n = 16 * tnn + (lane & 15), pl = 16 * tp + 4 * (lane >> 4);
-        T* dst = static_cast<T*>(p.gseg) + ((size_t)slice * nch + c) * N * P;
+        T* dst = static_cast<T*>(p.gseg) + ((size_t)slice * (nch + 1) + c) * N * P;
         const float v4[4] = {acc[0], acc[1], acc[2], acc[3]};
         store4<BF16>(dst + (size_t)n * P + p0 + pl, v4);
       }
@@ -328,7 +342,12 @@ __global__ __launch_bounds__(256) void ssm_adj_combine(BwdParams p, int per_row)
     const bool pair = per_row && n >= nreal;
     const float om = pair ? p.omega[(size_t)h * p.n_pairs + ((n - nreal) >> 1)] : 0.f;
     const size_t sb = (size_t)slice * p.nseg, sl = (size_t)slice * (p.nseg - 1) * p.nsub;
+    // the adjoint after the last token: dh_final, or zero
     float a = 0.f, bv = 0.f;
+    if (p.dh_final) {
+      a = p.dh_final[((size_t)slice * N + n) * P + pp];
+      bv = p.dh_final[((size_t)slice * N + n + 1) * P + pp];
+    }
     for (int s = p.nseg - 1; s >= 1; --s) {
       // ranges (last first) in blocks of kCombineBlock: a block's reads are issued
       // together, then chained (one memory round trip per block instead of per range)
@@ -584,6 +603,8 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
         const int row = v / (N / VEC), n0 = (v % (N / VEC)) * VEC;
         const int t = t0 + row / R - S::TEH, r = row % R;
         if (t >= 0 && t < L && r < rin) raw = *reinterpret_cast<const uint4*>(Bg + ((((size_t)b * L + t) * G + g) * rin + r) * N + n0);
+        else if (t == -1 && r < rin && p.B_prev)  // the carried token before the sequence
+          raw = *reinterpret_cast<const uint4*>(static_cast<const T*>(p.B_prev) + (((size_t)b * G + g) * rin + r) * N + n0);
       }
       pfb[k] = raw;
     }
@@ -597,6 +618,8 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
         const int row = v / (P / VEC), p0 = (v % (P / VEC)) * VEC;
         const int t = t0 + row / R - S::TEH, r = row % R;
         if (t >= 0 && t < L && r < rin) raw = *reinterpret_cast<const uint4*>(xg + ((((size_t)b * L + t) * H + h) * rin + r) * P + p0);
+        else if (t == -1 && r < rin && p.x_prev)
+          raw = *reinterpret_cast<const uint4*>(static_cast<const T*>(p.x_prev) + (((size_t)b * H + h) * rin + r) * P + p0);
       }
       pfx[k] = raw;
     }
@@ -628,12 +651,14 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
       return;
     }
     if (part == 3) {
-      const T* Gg = static_cast<const T*>(p.gseg) + ((size_t)slice * nch + (c + 1)) * N * P;
+      // the boundary adjoint of the next chunk (after the last chunk: slot nch, dh_final or
+      // zero)
+      const T* Gg = static_cast<const T*>(p.gseg) + ((size_t)slice * (nch + 1) + (c + 1)) * N * P;
 #pragma unroll
       for (int k = 0; k < SP; ++k) {
         const int v = tid + S::NTH * k;
         Raw4 g0 = zr4, g1 = zr4;
-        if (v < SPV && has_next) {
+        if (v < SPV) {
           const int n = 2 * (v / PV), q0 = (v % PV) * 4;
           g0 = *reinterpret_cast<const Raw4*>(Gg + (size_t)n * P + q0);
           g1 = *reinterpret_cast<const Raw4*>(Gg + (size_t)(n + 1) * P + q0);
@@ -1713,6 +1738,54 @@ __global__ __launch_bounds__(256) void ssm_bwd_group_sum(BwdParams p, int R) {
   }
 }
 
+// ============================================================== carried token
+// Gradients of the token before the sequence, whose write beta_0 B_prev X_prev enters at
+// token 0:  dX_prev = beta_0 B_prev^T g_0  and  dB_prev = beta_0 g_0 X_prev^T, with g_0 the
+// boundary adjoint of chunk 0 (the adjoint at token 0).  One workgroup per (batch, group):
+// dB_prev is the sum over the group's heads, added in head order.
+constexpr int kPrevMaxNP = 128 * 64;  // N x P of the largest variant
+template <bool BF16>
+__global__ __launch_bounds__(256) void ssm_bwd_prev(BwdParams p) {
+  using T = typename Elem<BF16>::T;
+  __shared__ float sG[kPrevMaxNP];
+  const int N = p.n_real + 2 * p.n_pairs, P = p.P, R = p.rin, H = p.H, G = p.G, hpg = H / G;
+  const int b = blockIdx.x / G, g = blockIdx.x % G, tid = threadIdx.x;
+  const T* Bp = static_cast<const T*>(p.B_prev) + ((size_t)b * G + g) * R * N;
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};  // dB_prev entries tid + 256 j (R N <= 1024)
+  for (int k = 0; k < hpg; ++k) {
+    const int h = g * hpg + k, slice = b * H + h;
+    const T* g0 = static_cast<const T*>(p.gseg) + (size_t)slice * (p.nchunks + 1) * N * P;
+    const T* xp = static_cast<const T*>(p.x_prev) + (size_t)slice * R * P;
+    const float beta0 = p.beta[(size_t)b * p.L * H + h];
+    __syncthreads();
+    for (int i = tid; i < N * P; i += 256) sG[i] = to_f32(g0[i]);
+    __syncthreads();
+    if (p.dx_prev)
+      for (int i = tid; i < R * P; i += 256) {
+        const int r = i / P, q = i % P;
+        float v = 0.f;
+        for (int n = 0; n < N; ++n) v += to_f32(Bp[r * N + n]) * sG[n * P + q];
+        static_cast<T*>(p.dx_prev)[(size_t)slice * R * P + i] = from_f32<T>(beta0 * v);
+      }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int i = tid + 256 * j;
+      if (i < R * N) {
+        const int r = i / N, n = i % N;
+        float v = 0.f;
+        for (int q = 0; q < P; ++q) v += sG[n * P + q] * to_f32(xp[r * P + q]);
+        acc[j] += beta0 * v;
+      }
+    }
+  }
+  if (p.dB_prev)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int i = tid + 256 * j;
+      if (i < R * N) static_cast<T*>(p.dB_prev)[((size_t)b * G + g) * R * N + i] = from_f32<T>(acc[j]);
+    }
+}
+
 // ============================================================== parameter sums
 // One wave per output: lane l sums the partials j = l, l + 64, ... of the (batch,
 // chunk) items in order, then a fixed butterfly combines the lanes, so the result
@@ -1841,6 +1914,8 @@ hipError_t launch_bwd(const BwdKey& k, const BwdParams& p, hipStream_t stream,
     }                                                                                         \
     hipLaunchKernelGGL((ssm_bwd_adjoint<BF, NN, PB, RR, QTT, CO, ADJ_NT>), dim3(agrid),       \
                        dim3(ADJ_NT), 0, stream, p);                                           \
+    if (p.dx_prev || p.dB_prev)                                                               \
+      hipLaunchKernelGGL(ssm_bwd_prev<BF>, dim3(p.batch * p.G), dim3(256), 0, stream, p);     \
     mark(1);                                                                                  \
     {                                                                                         \
       static std::atomic<int> occ{0};                                                         \

@@ -142,6 +142,9 @@ __global__ __launch_bounds__(256) void ssm_fwd_exact(FwdParams p, int qtk) {
   const size_t tsB = (size_t)G * rin * N, tsC = (size_t)G * rout * N;
   const size_t tsX = (size_t)H * rin * P, tsY = (size_t)H * rout * P;
   const float* dtg = p.dt + (size_t)b * L * H + h;
+  // the carried token before the sequence, or null
+  const T* Bpv = p.B_prev ? static_cast<const T*>(p.B_prev) + ((size_t)b * G + g) * rin * N : nullptr;
+  const T* xpv = p.x_prev ? static_cast<const T*>(p.x_prev) + ((size_t)b * H + h) * rin * P : nullptr;
 
   // the state entering the segment: h0, the combined segment state, or zero
   const float* hin = seg == 0 ? (p.h0 ? p.h0 + (size_t)slice * N * P : nullptr)
@@ -173,11 +176,13 @@ __global__ __launch_bounds__(256) void ssm_fwd_exact(FwdParams p, int qtk) {
     __syncthreads();  // the previous block is done with the staged rows
     for (int i = tid; i < (nt + 1) * R * N; i += 256) {
       const int tau = i / (R * N) - 1, r = (i / N) % R, n = i % N, t = t0 + tau;
-      sB[i] = (t >= 0 && r < rin) ? to_f32(Bg[(size_t)t * tsB + r * N + n]) : 0.f;
+      sB[i] = (t >= 0 && r < rin) ? to_f32(Bg[(size_t)t * tsB + r * N + n])
+              : (t == -1 && r < rin && Bpv) ? to_f32(Bpv[r * N + n]) : 0.f;
     }
     for (int i = tid; i < (nt + 1) * R * PBX; i += 256) {
       const int tau = i / (R * PBX) - 1, r = (i / PBX) % R, c = i % PBX, t = t0 + tau;
-      sX[i] = (t >= 0 && r < rin) ? to_f32(xg[(size_t)t * tsX + r * P + px * PBX + c]) : 0.f;
+      sX[i] = (t >= 0 && r < rin) ? to_f32(xg[(size_t)t * tsX + r * P + px * PBX + c])
+              : (t == -1 && r < rin && xpv) ? to_f32(xpv[r * P + px * PBX + c]) : 0.f;
     }
     for (int i = tid; i < nt * R * N; i += 256) {
       const int tau = i / (R * N), o = (i / N) % R, n = i % N;
@@ -333,12 +338,16 @@ __global__ __launch_bounds__(256) void ssm_bwd_exact(BwdParams p) {
         const int tau = i / (R * N) - 1, r = (i / N) % R, n = i % N, t = t0 + tau;
         sB[i] = (t >= 0 && r < rin)
                     ? static_cast<const T*>(p.B)[((((size_t)b * L + t) * G + g) * rin + r) * N + n]
+                : (t == -1 && r < rin && p.B_prev)
+                    ? static_cast<const T*>(p.B_prev)[(((size_t)b * G + g) * rin + r) * N + n]
                     : from_f32<T>(0.f);
       }
       for (int i = tid; i < (nT + 1) * R * P; i += 256) {
         const int tau = i / (R * P) - 1, r = (i / P) % R, q = i % P, t = t0 + tau;
         sX[i] = (t >= 0 && r < rin)
                     ? static_cast<const T*>(p.x)[((((size_t)b * L + t) * H + h) * rin + r) * P + q]
+                : (t == -1 && r < rin && p.x_prev)
+                    ? static_cast<const T*>(p.x_prev)[(((size_t)b * H + h) * rin + r) * P + q]
                     : from_f32<T>(0.f);
       }
       for (int i = tid; i < nT * R * N; i += 256) {
@@ -351,10 +360,11 @@ __global__ __launch_bounds__(256) void ssm_bwd_exact(BwdParams p) {
         sDY[i] = o < rout ? static_cast<const T*>(p.dy)[((((size_t)b * L + t) * H + h) * rout + o) * P + q]
                           : from_f32<T>(0.f);
       }
-      // the adjoint at the next chunk's first token (zero past the sequence end)
+      // the adjoint at the next chunk's first token (after the last chunk: slot nch,
+      // dh_final or zero)
       {
-        const T* gn = static_cast<const T*>(p.gseg) + ((size_t)slice * nch + c + 1) * N * P;
-        for (int i = tid; i < N * P; i += 256) sG[i] = has_next ? to_f32(gn[i]) : 0.f;
+        const T* gn = static_cast<const T*>(p.gseg) + ((size_t)slice * (nch + 1) + c + 1) * N * P;
+        for (int i = tid; i < N * P; i += 256) sG[i] = to_f32(gn[i]);
       }
       __syncthreads();
       for (int i = tid; i < (nT + 1) * N; i += 256) {

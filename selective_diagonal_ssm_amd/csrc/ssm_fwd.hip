@@ -192,6 +192,9 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
   const float* gag = S::TE ? p.gamma + (size_t)b * L * H + h : nullptr;
   // per-token strides of B, C, x, y
   const int tsB = G * rin * N, tsC = G * rout * N, tsX = H * rin * P, tsY = H * rout * P;
+  // the carried token before the sequence (two-endpoint writes), or null
+  const T* Bprev = p.B_prev ? static_cast<const T*>(p.B_prev) + ((size_t)b * G + g) * rin * N : nullptr;
+  const T* xprev = p.x_prev ? static_cast<const T*>(p.x_prev) + ((size_t)b * H + h) * rin * P + p0 : nullptr;
 
   // shift identity: the state carried inside the kernel is h' = h - gamma B X of the
   // last token; a later segment's incoming state (h) loses gamma_{t0-1} B_{t0-1} X_{t0-1}
@@ -231,11 +234,15 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
         const int row = v / S::NVEC_N, nv = v % S::NVEC_N;
         const int t = t0 + row / R - S::TEH, r = row % R;
         if (t >= 0 && t < L && r < rin) val = *reinterpret_cast<const uint4*>(Bg + t * tsB + r * N + nv * VEC);
+        else if (t == -1 && r < rin && Bprev)  // the carried token before the sequence
+          val = *reinterpret_cast<const uint4*>(Bprev + r * N + nv * VEC);
       } else if (u >= S::X0 && u < S::ALL_VECS) {
         const int v = u - S::X0;
         const int row = v / S::NVEC_P, pv = v % S::NVEC_P;
         const int t = t0 + row / R - S::TEH, r = row % R;
         if (t >= 0 && t < L && r < rin) val = *reinterpret_cast<const uint4*>(xg + t * tsX + r * P + pv * VEC);
+        else if (t == -1 && r < rin && xprev)
+          val = *reinterpret_cast<const uint4*>(xprev + r * P + pv * VEC);
       }
       rr[k] = val;
     }
@@ -1015,7 +1022,8 @@ bool fwd_variant_exists(const FwdKey& k) {
 // the forward's local pass: B keys and x values over the ranges of segments 0 .. nseg-2
 static LocalParams local_params(const FwdParams& p) {
   LocalParams l{};
-  l.key = p.B; l.val = p.x; l.dt = p.dt; l.A = p.A; l.omega = p.omega; l.beta = p.beta;
+  l.key = p.B; l.val = p.x; l.key_prev = p.B_prev; l.val_prev = p.x_prev;
+  l.dt = p.dt; l.A = p.A; l.omega = p.omega; l.beta = p.beta;
   l.gamma = p.gamma; l.out = p.seg_local; l.delta = p.seg_delta; l.rk = p.rin;
   l.batch = p.batch; l.L = p.L; l.H = p.H; l.G = p.G; l.P = p.P; l.n_real = p.n_real;
   l.n_pairs = p.n_pairs; l.softplus = p.softplus; l.head_rates = p.head_rates;

@@ -20,6 +20,10 @@ struct FwdParams {
   void* saved;   // [batch][nheads][nchunks + 1][N][P] in the io dtype, or null
   const float* h0;  // [batch][nheads][N][P] fp32 state before token 0, or null
   float* h_final;   // [batch][nheads][N][P] fp32 state after the last token, or null
+  // the token before the sequence (two-endpoint carry), or null: x [batch][nheads][rin][P],
+  // B [batch][ngroups][rin][N]
+  const void* x_prev;
+  const void* B_prev;
   int batch, L, H, G, P, n_real, n_pairs, nchunks, npblk;
   // ranks of the write (B, x) and of the readout (C, y); the kernel's rank R is the
   // larger, rows past a side's own rank are zero on load and dropped on store
@@ -56,6 +60,9 @@ constexpr int kCombineBlock = 8;
 struct LocalParams {
   const void* key;  // B (forward) or C (adjoint): [batch][L][G][R][N], io dtype
   const void* val;  // x (forward) or dy (adjoint): [batch][L][H][R][P], io dtype
+  // forward: the token before the sequence (two-endpoint carry), or null
+  const void* key_prev;  // [batch][G][R][N]
+  const void* val_prev;  // [batch][H][R][P]
   const float* dt;
   const float* A;
   const float* omega;
@@ -80,6 +87,13 @@ struct BwdParams {
   const float* gamma;
   const float* D;
   const void* saved;  // forward's chunk-boundary states (io dtype)
+  // two-endpoint carry (or null): the token before the sequence, its gradients, and the
+  // upstream gradient of the final state
+  const void* x_prev;
+  const void* B_prev;
+  const float* dh_final;  // [batch][nheads][N][P] fp32
+  void* dx_prev;
+  void* dB_prev;
   void* dx;
   void* dB;
   void* dC;
@@ -87,7 +101,8 @@ struct BwdParams {
   float* dbeta;
   float* dgamma;
   float* part;     // per-(slice, segment) parameter-gradient partials (workspace)
-  void* gseg;      // chunk-boundary adjoint states, io dtype (workspace)
+  void* gseg;      // chunk-boundary adjoint states, [slice][nchunks + 1][N][P] io dtype
+                   // (workspace); slot nchunks holds dh_final (zero without it)
   float* dA;
   float* domega;
   float* dD;

@@ -140,6 +140,8 @@ __global__ __launch_bounds__(256) void ssm_local(LocalParams p) {
   const T* Kg = static_cast<const T*>(p.key) + ((size_t)b * L * G + g) * rk * N;
   const T* Vg = static_cast<const T*>(p.val) + ((size_t)b * L * H + h) * rk * P + p0;
   const int tsG = G * rk * N, tsH = H * rk * P;
+  const T* Kp = (!ADJ && p.key_prev) ? static_cast<const T*>(p.key_prev) + ((size_t)b * G + g) * rk * N : nullptr;
+  const T* Vp = (!ADJ && p.val_prev) ? static_cast<const T*>(p.val_prev) + ((size_t)b * H + h) * rk * P + p0 : nullptr;
   T* kw = reinterpret_cast<T*>(smem) + wave * 32 * KS;
   T* vw = reinterpret_cast<T*>(smem) + 4 * 32 * KS + wave * 32 * VS;
   const float ah = COORD ? 0.f : p.A[h] * kLog2e;
@@ -169,12 +171,15 @@ __global__ __launch_bounds__(256) void ssm_local(LocalParams p) {
       const int j = u / NV, v = u % NV;
       const int t = ta + i0 + j;
       const bool ok = u < S::BI && i0 + j < len && t >= 0;
+      // the carried token before the sequence (forward, two-endpoint writes)
+      const bool okp = !ADJ && u < S::BI && t == -1 && Kp != nullptr;
       const int tc = ok ? t : ta;
 #pragma unroll
       for (int r = 0; r < R; ++r) {
         const int rc = r < rk ? r : 0;
-        const uint4 val = *reinterpret_cast<const uint4*>(Kg + (size_t)tc * tsG + rc * N + v * VEC);
-        rb[q][r] = keep(ok && r < rk, val);
+        const uint4 val = *reinterpret_cast<const uint4*>(
+            (okp ? Kp : Kg + (size_t)tc * tsG) + rc * N + v * VEC);
+        rb[q][r] = keep((ok || okp) && r < rk, val);
       }
     }
 #pragma unroll
@@ -184,9 +189,10 @@ __global__ __launch_bounds__(256) void ssm_local(LocalParams p) {
       const int j = jr / R, r = jr % R;
       const int t = ta + i0 + j;
       const bool ok = u < S::XI && i0 + j < len && t >= 0 && r < rk;
-      const int tc = ok ? t : ta, rc = ok ? r : 0;
-      const uint4 val = *reinterpret_cast<const uint4*>(Vg + (size_t)tc * tsH + rc * P + pv * VEC);
-      rx[q] = keep(ok, val);
+      const bool okp = !ADJ && u < S::XI && t == -1 && r < rk && Vp != nullptr;
+      const int tc = ok ? t : ta, rc = (ok || okp) ? r : 0;
+      const uint4 val = *reinterpret_cast<const uint4*>((okp ? Vp : Vg + (size_t)tc * tsH) + rc * P + pv * VEC);
+      rx[q] = keep(ok || okp, val);
     }
   };
 

@@ -25,10 +25,11 @@ def _on(stream):
 
 def forward(desc_dict: dict, io_dtype: str, x, B, C, dt, A, omega=None, beta=None, gamma=None,
             D=None, save_for_backward: bool = False, chunk: int = 0, stream=None, h0=None,
-            return_final_state: bool = False):
+            return_final_state: bool = False, x_prev=None, B_prev=None):
     """Run the forward scan.  Returns (y, saved) where saved is None unless
     ``save_for_backward``; with ``return_final_state`` returns (y, saved, h_final).
-    ``h0``: optional fp32 [batch][nheads][N][P] state before token 0."""
+    ``h0``: optional fp32 [batch][nheads][N][P] state before token 0; ``x_prev`` /
+    ``B_prev``: the token before the sequence (two-endpoint carry)."""
     desc = _lib.make_desc(desc_dict, io_dtype, chunk)
     d = desc_dict
     with _on(stream):
@@ -45,7 +46,8 @@ def forward(desc_dict: dict, io_dtype: str, x, B, C, dt, A, omega=None, beta=Non
             h_final = torch.empty((d["batch"], d["nheads"], d["dstate"], d["headdim"]),
                                   dtype=torch.float32, device=x.device)
         _lib.scan_fwd(desc, x, B, C, dt, A, y, omega=omega, beta=beta, gamma=gamma, D=D,
-                      saved=saved, ws=ws, stream=stream, h0=h0, h_final=h_final)
+                      saved=saved, ws=ws, stream=stream, h0=h0, h_final=h_final, x_prev=x_prev,
+                      B_prev=B_prev)
     if return_final_state:
         return y, saved, h_final
     return y, saved
@@ -53,9 +55,11 @@ def forward(desc_dict: dict, io_dtype: str, x, B, C, dt, A, omega=None, beta=Non
 
 def backward(desc_dict: dict, io_dtype: str, x, B, C, dy, dt, A, saved, omega=None, beta=None,
              gamma=None, D=None, chunk: int = 0, stream=None, want=("dA", "domega", "dbeta",
-                                                                     "dgamma", "dD")):
+                                                                     "dgamma", "dD"),
+             x_prev=None, B_prev=None, dh_final=None):
     """Run the fused reverse pass.  Returns a dict of gradient tensors (``dh0`` too
-    when "dh0" is in ``want``)."""
+    when "dh0" is in ``want``; ``dx_prev`` and ``dB_prev`` when the carried token
+    ``x_prev`` / ``B_prev`` is given).  ``dh_final``: upstream gradient of the final state."""
     desc = _lib.make_desc(desc_dict, io_dtype, chunk)
     d = desc_dict
     dev = x.device
@@ -81,12 +85,17 @@ def backward(desc_dict: dict, io_dtype: str, x, B, C, dy, dt, A, saved, omega=No
         if "dh0" in want:
             g["dh0"] = torch.empty((d["batch"], d["nheads"], d["dstate"], d["headdim"]),
                                    dtype=f32, device=dev)
+        if x_prev is not None:
+            g["dx_prev"] = torch.empty_like(x_prev)
+            g["dB_prev"] = torch.empty_like(B_prev)
         wsb = _lib.workspace_bytes(desc, True)
         ws = torch.empty(wsb, dtype=torch.uint8, device=dev) if wsb else None
         _lib.scan_bwd(desc, x, B, C, dy, dt, A, saved, g["dx"], g["dB"], g["dC"], g["ddt"],
                       omega=omega, beta=beta, gamma=gamma, D=D, dA=g.get("dA"),
                       domega=g.get("domega"), dbeta=g.get("dbeta"), dgamma=g.get("dgamma"),
-                      dD=g.get("dD"), ws=ws, stream=stream, dh0=g.get("dh0"))
+                      dD=g.get("dD"), ws=ws, stream=stream, dh0=g.get("dh0"), x_prev=x_prev,
+                      B_prev=B_prev, dh_final=dh_final, dx_prev=g.get("dx_prev"),
+                      dB_prev=g.get("dB_prev"))
     return g
 
 

@@ -27,7 +27,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_abi_version_and_status_strings():
     lib = ssm.load()
-    assert lib.ssm_abi_version() == 4
+    assert lib.ssm_abi_version() == 5
     for s in range(0, -9, -1):
         assert lib.ssm_status_string(s)
 

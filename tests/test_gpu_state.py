@@ -258,3 +258,133 @@ def test_empty_problem_writes_nonempty_outputs(name, batch, seqlen):
     torch.cuda.synchronize()
     for k, v in g.items():
         assert torch.count_nonzero(v).item() == 0, k
+
+
+# ---------------------------------------------------------------- two-endpoint carry
+CARRY = {
+    "f32_hybrid": ("hybrid", dict(dtype="f32", dstate=32, n_real=16, n_pairs=8, headdim=16,
+                                  batch=2, nheads=2, ngroups=2, seqlen=77), 0),
+    "bf16_hybrid": ("hybrid", dict(batch=2, seqlen=150, nheads=2, ngroups=2), 0),
+    "bf16_hybrid_r1": ("hybrid_r1", dict(batch=2, seqlen=150, nheads=2, ngroups=2), 0),
+    "bf16_groups": ("hybrid", dict(batch=2, seqlen=90, nheads=4, ngroups=2), 0),
+    "f32_groups_segments": ("hybrid", dict(dtype="f32", dstate=32, n_real=16, n_pairs=8,
+                                           headdim=16, batch=1, nheads=3, ngroups=1,
+                                           seqlen=333), 3),
+    "bf16_segments": ("hybrid", dict(batch=1, seqlen=500, nheads=2, ngroups=2), 3),
+    "f32_steep": ("hybrid", dict(dtype="f32", dstate=32, n_real=16, n_pairs=8, headdim=16,
+                                 batch=2, nheads=2, ngroups=2, seqlen=77, dt_mean=2.0,
+                                 A_lo=16.0, A_hi=16.0), 0),
+}
+
+
+def _carry_inputs(prob, seed):
+    d = prob["desc"]
+    rng = np.random.default_rng(seed)
+    io = torch.bfloat16 if prob["dtype"] == "bf16" else torch.float32
+    sc = workloads.spec("hybrid")["xbc_scale"]
+    xp = (rng.standard_normal((d["batch"], d["nheads"], d["rank_in"], d["headdim"])) * sc
+          ).astype(np.float32)
+    bp = (rng.standard_normal((d["batch"], d["ngroups"], d["rank_in"], d["dstate"])) * sc
+          ).astype(np.float32)
+    if prob["dtype"] == "bf16":
+        xp, bp = workloads.round_bf16(xp), workloads.round_bf16(bp)
+    h0 = workloads.make_state(d, seed=seed + 1, scale=0.5)
+    dhf = workloads.make_state(d, seed=seed + 2)
+    t = {"x_prev": torch.from_numpy(xp).cuda().to(io), "B_prev": torch.from_numpy(bp).cuda().to(io),
+         "h0": torch.from_numpy(h0).cuda(), "dh_final": torch.from_numpy(dhf).cuda()}
+    return xp, bp, h0, dhf, t
+
+
+@pytest.mark.parametrize("case", sorted(CARRY))
+def test_carried_token_forward_and_backward_match_oracle(case, monkeypatch):
+    """The token before the sequence (x_prev, B_prev), h0 and an upstream gradient of the
+    final state: y, h_final and every gradient, including dx_prev, dB_prev and dh0,
+    against the oracle."""
+    name, kw, nseg = CARRY[case]
+    if nseg:
+        monkeypatch.setenv("SSM_NSEG", str(nseg))
+    prob = workloads.make_problem(workloads.spec(name, **kw), seed=31, with_dy=True)
+    xp, bp, h0, dhf, c = _carry_inputs(prob, 37)
+    print(f"[carry] case={case} desc={prob['desc']}", flush=True)
+    t = workloads.to_device(prob)
+    for save in (False, True):
+        y, saved, hf = ssm.forward(prob["desc"], prob["dtype"], t["x"], t["B"], t["C"], t["dt"],
+                                   t["A"], omega=t.get("omega"), beta=t.get("beta"),
+                                   gamma=t.get("gamma"), D=t.get("D"), save_for_backward=save,
+                                   h0=c["h0"], return_final_state=True, x_prev=c["x_prev"],
+                                   B_prev=c["B_prev"])
+        torch.cuda.synchronize()
+        yr, hr = oracle.fwd(prob, h0=h0.astype(np.float64), x_prev=xp, B_prev=bp)
+        ey, eh = rel_l2(_np(y), yr), rel_l2(_np(hf), hr)
+        print(f"[carry] case={case} save={save} y={ey:.2e} h_final={eh:.2e}", flush=True)
+        assert ey <= tol(prob) and eh <= tol(prob), (ey, eh)
+    g = ssm.backward(prob["desc"], prob["dtype"], t["x"], t["B"], t["C"], t["dy"], t["dt"],
+                     t["A"], saved, omega=t.get("omega"), beta=t.get("beta"),
+                     gamma=t.get("gamma"), D=t.get("D"),
+                     want=("dA", "domega", "dbeta", "dgamma", "dD", "dh0"),
+                     x_prev=c["x_prev"], B_prev=c["B_prev"], dh_final=c["dh_final"])
+    torch.cuda.synchronize()
+    ref = oracle.bwd(prob, prob["dy"], h0=h0.astype(np.float64), x_prev=xp, B_prev=bp,
+                     dh_final=dhf.astype(np.float64))
+    errs = {k: rel_l2(_np(g[k]), ref[k]) for k in GRADS + ["dx_prev", "dB_prev"]
+            if k in g and ref.get(k) is not None}
+    print(f"[carry] case={case} " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()), flush=True)
+    assert {"dh0", "dx_prev", "dB_prev", "dbeta"} <= set(errs)
+    bad = {k: v for k, v in errs.items() if not v <= tol(prob)}
+    assert not bad, bad
+
+
+@pytest.mark.parametrize("case", ["f32_hybrid", "bf16_hybrid", "bf16_hybrid_r1"])
+def test_two_endpoint_split_run_chains_through_the_carry(case):
+    """Two GPU calls over the halves of a two-endpoint sequence, the second continued with
+    the first one's h_final and last token, give one run's outputs; their backward passes
+    chained (the second's dh0 as the first's dh_final, its dx_prev / dB_prev added to the
+    first's last token) give one run's gradients."""
+    name, kw, _ = CARRY[case]
+    prob = workloads.make_problem(workloads.spec(name, **kw), seed=41, with_dy=True)
+    L = prob["desc"]["seqlen"]
+    L1 = L // 2 + 3
+    t = workloads.to_device(prob)
+    kw_p = dict(omega=t.get("omega"), D=t.get("D"))
+
+    def part(lo, hi):
+        return {k: (v[:, lo:hi].contiguous() if k in ("x", "B", "C", "dt", "beta", "gamma", "dy")
+                    else v) for k, v in t.items()}
+
+    def fwd(d, tq, **extra):
+        return ssm.forward(d, prob["dtype"], tq["x"], tq["B"], tq["C"], tq["dt"], tq["A"],
+                           beta=tq["beta"], gamma=tq["gamma"], save_for_backward=True,
+                           return_final_state=True, **kw_p, **extra)
+
+    def bwd(d, tq, saved, **extra):
+        return ssm.backward(d, prob["dtype"], tq["x"], tq["B"], tq["C"], tq["dy"], tq["dt"],
+                            tq["A"], saved, beta=tq["beta"], gamma=tq["gamma"],
+                            want=("dA", "domega", "dbeta", "dgamma", "dD", "dh0"), **kw_p, **extra)
+
+    d1, d2 = dict(prob["desc"], seqlen=L1), dict(prob["desc"], seqlen=L - L1)
+    t1, t2 = part(0, L1), part(L1, L)
+    y, sv, hf = fwd(prob["desc"], t)
+    g = bwd(prob["desc"], t, sv)
+    carry = dict(x_prev=t["x"][:, L1 - 1].contiguous(), B_prev=t["B"][:, L1 - 1].contiguous())
+    y1, s1, h1 = fwd(d1, t1)
+    y2, s2, h2 = fwd(d2, t2, h0=h1, **carry)
+    g2 = bwd(d2, t2, s2, **carry)
+    g1 = bwd(d1, t1, s1, dh_final=g2["dh0"])
+    torch.cuda.synchronize()
+    tl = tol(prob)
+    assert rel_l2(_np(torch.cat([y1, y2], 1)), _np(y)) <= tl
+    assert rel_l2(_np(h2), _np(hf)) <= tl
+    dx1, dB1 = g1["dx"].float().clone(), g1["dB"].float().clone()
+    dx1[:, L1 - 1] += g2["dx_prev"].float()
+    dB1[:, L1 - 1] += g2["dB_prev"].float()
+    errs = {"dx": rel_l2(_np(torch.cat([dx1, g2["dx"].float()], 1)), _np(g["dx"])),
+            "dB": rel_l2(_np(torch.cat([dB1, g2["dB"].float()], 1)), _np(g["dB"]))}
+    for k in ("dC", "ddt", "dbeta", "dgamma"):
+        errs[k] = rel_l2(_np(torch.cat([g1[k], g2[k]], 1)), _np(g[k]))
+    for k in ("dA", "domega", "dD"):
+        errs[k] = rel_l2(_np(g1[k] + g2[k]), _np(g[k]))
+    errs["dh0"] = rel_l2(_np(g1["dh0"]), _np(g["dh0"]))
+    print(f"[carry-chain] case={case} " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()),
+          flush=True)
+    bad = {k: v for k, v in errs.items() if not v <= tl}
+    assert not bad, bad
