@@ -54,7 +54,8 @@ def algorithmic_bytes(desc: dict, io_bytes: int, direction: str) -> int:
 
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
-    for f in ("ssm_fwd.hip", "ssm_bwd.hip", "ssm_device.hpp", "ssm_local.hpp", "ssm_kernels.hpp"):
+    for f in ("ssm_fwd.hip", "ssm_bwd.hip", "ssm_device.hpp", "ssm_local.hpp", "ssm_kernels.hpp",
+              "ssm_exact.hpp"):
         p = os.path.join(ROOT, "selective_diagonal_ssm_amd", "csrc", f)
         if os.path.exists(p):
             h.update(open(p, "rb").read())
