@@ -40,7 +40,7 @@ def build(force: bool = True) -> str:
 class _Desc(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int) for n in (
         "batch", "seqlen", "nheads", "ngroups", "headdim", "dstate", "rank_in", "rank_out",
-        "n_real", "n_pairs", "decay_mode", "dt_softplus", "two_endpoint", "has_D")]
+        "n_real", "n_pairs", "decay_mode", "dt_softplus", "two_endpoint", "has_D", "n_static")]
 
 
 @dataclass
@@ -59,16 +59,17 @@ class OracleDesc:
     dt_softplus: bool
     two_endpoint: bool
     has_D: bool
+    n_static: int = 0  # the first n_static real rows decay by exp(-A) per token
 
     def c(self) -> _Desc:
         return _Desc(self.batch, self.seqlen, self.nheads, self.ngroups, self.headdim,
                      self.dstate, self.rank_in, self.rank_out, self.n_real, self.n_pairs,
                      0 if self.decay_mode == "head" else 1, int(self.dt_softplus),
-                     int(self.two_endpoint), int(self.has_D))
+                     int(self.two_endpoint), int(self.has_D), int(self.n_static))
 
     @classmethod
     def from_dict(cls, d: dict) -> "OracleDesc":
-        return cls(**{k: d[k] for k in cls.__dataclass_fields__})
+        return cls(**{k: d[k] for k in cls.__dataclass_fields__ if k in d})
 
 
 def load():

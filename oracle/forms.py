@@ -28,7 +28,9 @@ def _t(a):
 
 
 def transition_matrices(desc: dict, dt, A, omega):
-    """Full N x N transition A_t for every (b, t, h): tensor [b, T, H, N, N]."""
+    """Full N x N transition A_t for every (b, t, h): tensor [b, T, H, N, N].
+    Real static rows (Part 08 section 3 of the same page: HybridMamba's real static,
+    real dynamic and complex dynamic rows) decay by exp(-A) per token, whatever Delta."""
     b, T, H, N = desc["batch"], desc["seqlen"], desc["nheads"], desc["dstate"]
     nr, npairs = desc["n_real"], desc["n_pairs"]
     delta = torch.nn.functional.softplus(dt) if desc["dt_softplus"] else dt
@@ -41,7 +43,9 @@ def transition_matrices(desc: dict, dt, A, omega):
             rates = [A[h, n] for n in range(nr)]
             prates = [A[h, nr + k] for k in range(npairs)]
         for n in range(nr):
-            Am[:, :, h, n, n] = torch.exp(-delta[:, :, h] * rates[n])
+            # a static row (the first n_static real rows) takes a unit step at every token
+            step = 1.0 if n < desc.get("n_static", 0) else delta[:, :, h]
+            Am[:, :, h, n, n] = torch.exp(-step * rates[n])
         for k in range(npairs):
             i, j = nr + 2 * k, nr + 2 * k + 1
             rho = torch.exp(-delta[:, :, h] * prates[k])
@@ -122,7 +126,8 @@ def complex_y(desc: dict, x, B, C, dt, A, omega, beta=None, gamma=None, D=None):
             prev = None
             for t in range(T):
                 d = delta[bb, t, h]
-                ar = np.exp(-d * A[h, :nr])
+                # static rows (the first n_static) take a unit step whatever Delta is
+                ar = np.exp(-np.where(np.arange(nr) < desc.get("n_static", 0), 1.0, d) * A[h, :nr])
                 lam = np.exp(-d * A[h, nr:nr + npairs] + 1j * d * omega[h, :npairs])
                 w = B[bb, t, g].T @ x[bb, t, h]  # N x P
                 gm = gamma[bb, t, h] if desc["two_endpoint"] else 1.0

@@ -4,10 +4,10 @@
  * tests/test_oracle_sanitize.py on the host; nothing else loads it).
  *
  * It calls oracle_fwd and oracle_bwd on small problems that reach every branch of the
- * oracle's indexing: head and per-row decay, rotating pairs, two-endpoint writes with
- * the carried previous token, an initial state and an upstream gradient of the final
- * state, head groups shared by several heads, different write and readout ranks, a
- * subset of the slices, length 1 and length 0.  The inputs are deterministic
+ * oracle's indexing: head and per-row decay, static real rows, rotating pairs,
+ * two-endpoint writes with the carried previous token, an initial state and an upstream
+ * gradient of the final state, head groups shared by several heads, different write and
+ * readout ranks, a subset of the slices, length 1 and length 0.  The inputs are deterministic
  * pseudo-random values from a small linear congruential generator: the sanitizers, not
  * the values, are what this run checks.  Exit status 0 when every call returned 0 and
  * every output is finite.
@@ -89,7 +89,7 @@ static int run_case(oracle_desc d, int carry, int half_slices) {
 
 int main(void) {
   /* batch, seqlen, nheads, ngroups, headdim, dstate, rank_in, rank_out, n_real, n_pairs,
-     decay_mode, dt_softplus, two_endpoint, has_D */
+     decay_mode, dt_softplus, two_endpoint, has_D, n_static */
   const oracle_desc cases[] = {
       {2, 70, 3, 3, 5, 4, 1, 1, 4, 0, ORACLE_DECAY_HEAD, 1, 0, 1},
       {1, 130, 4, 2, 3, 6, 2, 2, 2, 2, ORACLE_DECAY_COORD, 1, 1, 1},
@@ -97,6 +97,8 @@ int main(void) {
       {1, 1, 2, 2, 2, 4, 2, 1, 0, 2, ORACLE_DECAY_COORD, 1, 1, 0},
       {1, 0, 2, 2, 2, 4, 1, 1, 2, 1, ORACLE_DECAY_COORD, 1, 1, 1},
       {2, 9, 2, 2, 2, 6, 1, 3, 6, 0, ORACLE_DECAY_COORD, 1, 0, 0},
+      /* static real rows next to dynamic rows and pairs */
+      {1, 40, 2, 1, 3, 10, 2, 2, 4, 3, ORACLE_DECAY_COORD, 1, 1, 1, 2},
   };
   const int n = (int)(sizeof(cases) / sizeof(cases[0]));
   int failures = 0;

@@ -22,10 +22,17 @@
  *   - the same page, Parts 03/08.3 and the arXiv abstract (mlinfo.pages.dev):
  *     SSD-MIMO writes R values per step (B_t is N x R, X_t is R x P) and reads
  *     O rows (C_t is N x O); HybridMamba mixes real per-coordinate-decay rows with
- *     complex rotating pairs and two-endpoint writes (x_{t-1}, x_t).
+ *     complex rotating pairs and two-endpoint writes (x_{t-1}, x_t);
+ *   - the same page, Part 08 section 3: HybridMamba mixes real static, real dynamic
+ *     and complex dynamic rows.  Read here as: a static row's decay does not depend
+ *     on the input (its per-token factor is exp(-A_{h,n}) whatever Delta_t is), a
+ *     dynamic row's decay is exp(-Delta_t A_{h,n}); writes and readouts are the same
+ *     for every row.
  *
  * The transition A_t is block diagonal:
- *   real row n < n_real:   a_t[n]  = exp(-Delta_t * A_{h,n})
+ *   real row n < n_real:   a_t[n]  = exp(-Delta_t * A_{h,n})   (dynamic rows)
+ *   static row n < n_static (the first n_static real rows):
+ *                          a_t[n]  = exp(-A_{h,n}), the same at every token
  *   pair k (rows n_real+2k, n_real+2k+1):
  *                          rho_t   = exp(-Delta_t * Ac_{h,k}),
  *                          theta_t = Delta_t * omega_{h,k},
@@ -50,7 +57,7 @@ static double sigmoid(double v) { return 1.0 / (1.0 + exp(-v)); }
 
 /* One slice's inputs gathered into contiguous fp64 arrays. */
 typedef struct {
-  int T, N, P, R, O, n_real, n_pairs;
+  int T, N, P, R, O, n_real, n_pairs, n_static;
   int two_endpoint, has_D;
   double *x;     /* [T][R][P] */
   double *B;     /* [T][R][N] */
@@ -74,7 +81,7 @@ static void gather_slice(const oracle_desc *d, int b, int h, const float *x, con
   const int T = d->seqlen, H = d->nheads, G = d->ngroups, P = d->headdim, N = d->dstate;
   const int R = d->rank_in, O = d->rank_out, g = h / (H / G);
   s->T = T; s->N = N; s->P = P; s->R = R; s->O = O;
-  s->n_real = d->n_real; s->n_pairs = d->n_pairs;
+  s->n_real = d->n_real; s->n_pairs = d->n_pairs; s->n_static = d->n_static;
   s->two_endpoint = d->two_endpoint; s->has_D = d->has_D;
   for (int t = 0; t < T; ++t) {
     const size_t bt = (size_t)b * T + t;
@@ -155,12 +162,15 @@ static const double *prev_X(const slice_t *s, int t, int r) {
   return s->has_prev ? s->xprev + (size_t)r * s->P : NULL;
 }
 
+/* The step a real row's decay takes at token t: Delta_t, or 1 on a static row. */
+static double row_step(const slice_t *s, int t, int n) { return n < s->n_static ? 1.0 : s->delta[t]; }
+
 /* h <- A_t h  (block-diagonal transition of step t). */
 static void apply_transition(const slice_t *s, int t, double *h) {
   const int N = s->N, P = s->P, nr = s->n_real;
   const double dl = s->delta[t];
   for (int n = 0; n < nr; ++n) {
-    const double a = exp(-dl * s->rate[n]);
+    const double a = exp(-row_step(s, t, n) * s->rate[n]);
     for (int p = 0; p < P; ++p) h[(size_t)n * P + p] *= a;
   }
   for (int k = 0; k < s->n_pairs; ++k) {
@@ -182,7 +192,7 @@ static void apply_transition_T(const slice_t *s, int t, double *h) {
   const int P = s->P, nr = s->n_real;
   const double dl = s->delta[t];
   for (int n = 0; n < nr; ++n) {
-    const double a = exp(-dl * s->rate[n]);
+    const double a = exp(-row_step(s, t, n) * s->rate[n]);
     for (int p = 0; p < P; ++p) h[(size_t)n * P + p] *= a;
   }
   for (int k = 0; k < s->n_pairs; ++k) {
@@ -247,6 +257,8 @@ static int check_desc(const oracle_desc *d) {
     return -2;
   if (d->nheads % d->ngroups) return -2;
   if (d->decay_mode == ORACLE_DECAY_HEAD && (d->n_pairs != 0 || d->n_real != d->dstate)) return -2;
+  if (d->n_static < 0 || d->n_static > d->n_real) return -2;
+  if (d->decay_mode == ORACLE_DECAY_HEAD && d->n_static != 0) return -2;
   if (d->n_real + 2 * d->n_pairs != d->dstate) return -2;
   if (d->has_D && d->rank_in != d->rank_out) return -2;
   return 0;
@@ -393,11 +405,12 @@ int oracle_bwd(const oracle_desc *d, const float *x, const float *B, const float
         /* transition of step t: parameter grads use h_{t-1} */
         double dl = 0.0;
         for (int n = 0; n < nr; ++n) {
-          const double a = exp(-s.delta[t] * s.rate[n]);
+          const double st = row_step(&s, t, n);
+          const double a = exp(-st * s.rate[n]);
           double e = 0.0;
           for (int p = 0; p < P; ++p) e += gs[(size_t)n * P + p] * hp[(size_t)n * P + p];
-          dl += -s.rate[n] * a * e;
-          dA_loc[d->decay_mode == ORACLE_DECAY_HEAD ? 0 : n] += -s.delta[t] * a * e;
+          if (n >= s.n_static) dl += -s.rate[n] * a * e;  /* a static row ignores Delta */
+          dA_loc[d->decay_mode == ORACLE_DECAY_HEAD ? 0 : n] += -st * a * e;
         }
         for (int k = 0; k < np; ++k) {
           const int i = nr + 2 * k, j = i + 1;

@@ -9,7 +9,8 @@
  *   x     [b][t][h][r][p]     B  [b][t][g][r][n]     C  [b][t][g][o][n]
  *   dt, beta, gamma [b][t][h]
  *   A     head mode: [h]; coordinate mode: [h][n_real + n_pairs]
- *         (first n_real entries: real-row rates; then one rate per pair)
+ *         (first n_real entries: real-row rates, the first n_static of them static rows;
+ *         then one rate per pair)
  *   omega [h][n_pairs]        D [h]        h0, h_final, dh0, dh_final [b][h][n][p]
  *   x_prev, dx_prev [b][h][r][p], B_prev, dB_prev [b][g][r][n]: the token before the
  *         sequence (two-endpoint carry: its write beta_0 B_prev X_prev enters at token 0);
@@ -37,6 +38,8 @@ typedef struct {
   int batch, seqlen, nheads, ngroups, headdim, dstate, rank_in, rank_out;
   int n_real, n_pairs, decay_mode;
   int dt_softplus, two_endpoint, has_D;
+  int n_static; /* the first n_static real rows decay by exp(-A) per token, whatever
+                   Delta is (coordinate mode only; 0 = every real row is dynamic) */
 } oracle_desc;
 
 int oracle_fwd(const oracle_desc *d, const float *x, const float *B, const float *C,

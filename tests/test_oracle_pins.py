@@ -114,6 +114,9 @@ def test_p1_constant_decay_is_first_order_iir(oracle_lib):
     # the pairs of a head decaying at different rates ("different decay laws", arXiv abstract)
     ("hybrid", dict(batch=1, seqlen=8, nheads=2, ngroups=2, headdim=2, dstate=8, n_real=2,
                     n_pairs=3, rank_in=2, rank_out=2, pair_rate_per_pair=True)),
+    # real static, real dynamic and complex dynamic rows in one head (Part 08 section 3)
+    ("hybrid", dict(batch=2, seqlen=8, nheads=2, ngroups=2, headdim=2, dstate=10, n_real=4,
+                    n_static=2, n_pairs=3, rank_in=2, rank_out=2, pair_rate_per_pair=True)),
 ])
 def test_p2_recurrence_equals_quadratic_form(oracle_lib, name, kw):
     p = workloads.make_problem(small(name, **kw), seed=11)
@@ -353,6 +356,8 @@ GRAD_PAIRS = [("x", "dx"), ("B", "dB"), ("C", "dC"), ("dt", "ddt"), ("A", "dA"),
                     n_pairs=1, rank_in=1, rank_out=1)),
     ("hybrid", dict(batch=1, seqlen=7, nheads=2, ngroups=2, headdim=2, dstate=8, n_real=2,
                     n_pairs=3, rank_in=2, rank_out=2, pair_rate_per_pair=True)),
+    ("hybrid", dict(batch=1, seqlen=7, nheads=2, ngroups=2, headdim=2, dstate=10, n_real=4,
+                    n_static=2, n_pairs=3, rank_in=2, rank_out=2, A_static_hi=3.0)),
 ])
 def test_p8_adjoint_matches_autograd_of_quadratic_form(oracle_lib, name, kw):
     p = workloads.make_problem(small(name, **kw), seed=81, with_dy=True)
@@ -536,3 +541,84 @@ def test_p8_carry_gradients_match_autograd_of_quadratic_form(oracle_lib):
         ref = ins[k].grad.numpy()
         np.testing.assert_allclose(g[gk], ref, rtol=1e-9, atol=1e-12 * max(1, np.abs(ref).max()),
                                    err_msg=gk)
+
+
+# ---------------------------------------------------------------- P10 real static rows
+# Part 08 section 3 of "When a Diagonal State Is Not Enough": HybridMamba mixes real
+# static, real dynamic and complex dynamic rows.  A static row's decay exp(-A_n) per token
+# does not depend on the input, so a state of static rows only is a linear time-invariant
+# filter of the writes.
+
+def static_problem(T=40, N=4, P=3, seed=101, softplus=True):
+    s = small("hybrid", batch=1, seqlen=T, nheads=1, ngroups=1, headdim=P, dstate=N,
+              n_real=N, n_static=N, n_pairs=0, rank_in=1, rank_out=1, two_endpoint=False,
+              has_D=False, dt_softplus=softplus)
+    return workloads.make_problem(s, seed=seed, with_dy=True)
+
+
+def test_p10_static_rows_are_first_order_iir_per_row(oracle_lib):
+    # every row n is h_n <- exp(-A_n) h_n + B_n X: scipy's lfilter per row and column,
+    # read out by C_t
+    p = static_problem()
+    y, _ = oracle.fwd(p)
+    T, N, P = 40, 4, 3
+    A = p["A"][0].astype(np.float64)
+    Bw = p["B"][0, :, 0, 0, :].astype(np.float64)        # [T, N]
+    X = p["x"][0, :, 0, 0, :].astype(np.float64)         # [T, P]
+    Cr = p["C"][0, :, 0, 0, :].astype(np.float64)        # [T, N]
+    ref = np.zeros((T, P))
+    for n in range(N):
+        a = float(np.exp(-np.float64(np.float32(A[n]))))
+        hn = scipy.signal.lfilter([1.0], [1.0, -a], Bw[:, n:n + 1] * X, axis=0)  # [T, P]
+        ref += Cr[:, n:n + 1] * hn
+    np.testing.assert_allclose(y.reshape(T, P), ref, rtol=1e-11, atol=1e-13)
+
+
+def test_p10_static_rows_ignore_the_step(oracle_lib):
+    # outputs do not move with dt, and the step gradient is exactly zero
+    p = static_problem()
+    y, _ = oracle.fwd(p)
+    q = dict(p); q["dt"] = (p["dt"] * 3.0 + 1.0).astype(np.float32)
+    y2, _ = oracle.fwd(q)
+    np.testing.assert_array_equal(y, y2)
+    g = oracle.bwd(p, p["dy"])
+    assert np.all(g["ddt"] == 0.0)
+
+
+def test_p10_static_row_is_dynamic_row_at_unit_step(oracle_lib):
+    # with Delta = 1 at every token (no softplus, dt = 1) a static row and a dynamic row
+    # with the same rate are the same recurrence: outputs and every gradient but ddt agree
+    s = small("hybrid", batch=2, seqlen=20, nheads=2, ngroups=1, headdim=3, dstate=8,
+              n_real=4, n_pairs=2, rank_in=2, rank_out=2, dt_softplus=False)
+    p = workloads.make_problem(s, seed=103, with_dy=True)
+    p["dt"] = np.ones_like(p["dt"])
+    ps = dict(p); ps["desc"] = dict(p["desc"], n_static=4)
+    y0, h0 = oracle.fwd(p)
+    y1, h1 = oracle.fwd(ps)
+    np.testing.assert_allclose(y1, y0, rtol=1e-13, atol=1e-15)
+    g0, g1 = oracle.bwd(p, p["dy"]), oracle.bwd(ps, p["dy"])
+    for k in g0:
+        if k == "ddt":
+            continue
+        np.testing.assert_allclose(g1[k], g0[k], rtol=1e-12, atol=1e-14, err_msg=k)
+
+
+def test_p10_static_rows_finite_differences(oracle_lib):
+    # dA of static rows and ddt (which the static rows must not feed) by central differences
+    s = small("hybrid", batch=1, seqlen=9, nheads=1, ngroups=1, headdim=2, dstate=6,
+              n_real=4, n_static=2, n_pairs=1, rank_in=1, rank_out=1, A_static_hi=2.0)
+    p = workloads.make_problem(s, seed=105, with_dy=True)
+    g = oracle.bwd(p, p["dy"])
+    dy = p["dy"].astype(np.float64)
+
+    def loss(q):
+        y, _ = oracle.fwd(q)
+        return float((y * dy).sum())
+
+    for k, gk, idxs in [("A", "dA", [(0, 0), (0, 1), (0, 2)]), ("dt", "ddt", [(0, 3, 0), (0, 7, 0)])]:
+        for idx in idxs:
+            h = 1e-2 * max(1.0, abs(float(p[k][idx])))
+            qp = dict(p); qp[k] = p[k].copy(); qp[k][idx] += np.float32(h)
+            qm = dict(p); qm[k] = p[k].copy(); qm[k][idx] -= np.float32(h)
+            fd = (loss(qp) - loss(qm)) / (float(qp[k][idx]) - float(qm[k][idx]))
+            assert abs(fd - g[gk][idx]) <= 2e-4 * max(1.0, abs(fd)), (k, idx, fd, g[gk][idx])

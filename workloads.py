@@ -34,6 +34,10 @@ Optional spec keys (absent from the workloads above, so their draws are unchange
 
 ``pair_rate_per_pair``  draw the rotating pairs' decay rates per (head, pair) instead of
                         one per head (the pairs of a head then decay at different rates)
+``n_static``            the first n_static real rows are static (per-row decay only): their
+                        decay exp(-A) per token does not depend on the step; their rates are
+                        drawn ~ U[A_static_lo, A_static_hi] (default U[0.01, 1]) from a third
+                        generator, ``default_rng([seed, 2])``, so the other draws do not move
 ``dt_spike_prob``       probability (a float, or a list with one entry per head) that a
                         token's raw step is replaced by a spike ~ N(dt_spike_mean,
                         dt_spike_std): steps large enough to wipe a state row within a
@@ -144,7 +148,14 @@ def make_problem(spec_or_name, seed: int = 0, with_dy: bool | None = None) -> di
     if s["dtype"] == "bf16":
         x, B, C = round_bf16(x), round_bf16(B), round_bf16(C)
         dy = round_bf16(dy) if dy is not None else None
-    prob = dict(desc={k: s[k] for k in DESC_KEYS}, dtype=s["dtype"], chunk=s.get("chunk", 0),
+    ns = s.get("n_static", 0)
+    if ns:
+        r3 = np.random.default_rng([seed, 2])
+        A[:, :ns] = r3.uniform(s.get("A_static_lo", 0.01), s.get("A_static_hi", 1.0),
+                               size=(H, ns)).astype(f32)
+    desc = {k: s[k] for k in DESC_KEYS}
+    desc["n_static"] = ns
+    prob = dict(desc=desc, dtype=s["dtype"], chunk=s.get("chunk", 0),
                 x=x, B=B, C=C, dt=dt, A=A, omega=omega, beta=beta, gamma=gamma, D=D, dy=dy)
     return prob
 
