@@ -19,6 +19,9 @@
  *
  * Transition A_t (block diagonal, N = n_real + 2 n_pairs rows):
  *   real row n:  a_t[n] = exp(-Delta_t * A_{h,n})   (head mode: A_{h,n} = A_h)
+ *   static row n < n_static (coordinate mode): a_t[n] = exp(-A_{h,n}), whatever Delta_t
+ *                is -- the "real static" rows HybridMamba mixes with real dynamic and
+ *                complex dynamic rows (same page, Part 08 section 3)
  *   pair k (rows n_real+2k, n_real+2k+1):
  *                rho_t = exp(-Delta_t * A_{h, n_real+k}),  theta_t = Delta_t * omega_{h,k},
  *                block = rho_t [[cos theta, -sin theta], [sin theta, cos theta]]
@@ -86,7 +89,7 @@
 extern "C" {
 #endif
 
-#define SSM_ABI_VERSION 5
+#define SSM_ABI_VERSION 6
 
 typedef enum {
   SSM_OK = 0,
@@ -125,6 +128,9 @@ typedef struct {
   int32_t io_dtype;   /* ssm_dtype: storage of x, B, C, y, dy, dx, dB, dC */
   int32_t decay_mode; /* ssm_decay_mode */
   uint32_t flags;     /* SSM_F_* */
+  int32_t n_static;   /* coordinate mode: the first n_static real rows are static (decay
+                         exp(-A) per token, no dependence on the step); 0 <= n_static <=
+                         n_real, even; must be 0 in head mode */
 } ssm_desc;
 
 typedef struct {

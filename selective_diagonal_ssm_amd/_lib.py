@@ -32,7 +32,8 @@ class SsmDesc(ctypes.Structure):
                 ("rank_in", ctypes.c_int32), ("rank_out", ctypes.c_int32),
                 ("n_real", ctypes.c_int32), ("n_pairs", ctypes.c_int32),
                 ("chunk", ctypes.c_int32), ("io_dtype", ctypes.c_int32),
-                ("decay_mode", ctypes.c_int32), ("flags", ctypes.c_uint32)]
+                ("decay_mode", ctypes.c_int32), ("flags", ctypes.c_uint32),
+                ("n_static", ctypes.c_int32)]
 
 
 _vp = ctypes.c_void_p
@@ -100,7 +101,8 @@ def make_desc(d: dict, io_dtype: str, chunk: int = 0) -> SsmDesc:
     return SsmDesc(d["batch"], d["seqlen"], d["nheads"], d["ngroups"], d["headdim"], d["dstate"],
                    d["rank_in"], d["rank_out"], d["n_real"], d["n_pairs"], chunk,
                    SSM_BF16 if io_dtype == "bf16" else SSM_F32,
-                   SSM_DECAY_HEAD if d["decay_mode"] == "head" else SSM_DECAY_COORD, flags)
+                   SSM_DECAY_HEAD if d["decay_mode"] == "head" else SSM_DECAY_COORD, flags,
+                   d.get("n_static", 0))
 
 
 def _ptr(t):

@@ -81,6 +81,8 @@ int check_operation(const ssm_desc* d) {
   if (d->decay_mode == SSM_DECAY_HEAD && d->n_pairs != 0) return SSM_ERR_SHAPE;
   if (d->flags & ~(SSM_F_DT_SOFTPLUS | SSM_F_TWO_ENDPOINT | SSM_F_HAS_D)) return SSM_ERR_SHAPE;
   if ((d->flags & SSM_F_HAS_D) && d->rank_in != d->rank_out) return SSM_ERR_SHAPE;
+  if (d->n_static < 0 || d->n_static > d->n_real) return SSM_ERR_SHAPE;
+  if (d->decay_mode == SSM_DECAY_HEAD && d->n_static != 0) return SSM_ERR_SHAPE;
   return SSM_OK;
 }
 
@@ -89,6 +91,7 @@ int make_plan(const ssm_desc* d, Plan* pl) {
   if (rc) return rc;
   if (d->headdim % 16) return SSM_ERR_UNSUPPORTED;
   if (d->n_pairs > 0 && (d->n_real % 2)) return SSM_ERR_UNSUPPORTED;
+  if (d->n_static % 2) return SSM_ERR_UNSUPPORTED;  // the kernels take real rows in pairs
   // kernels index inside a tensor with 32-bit offsets
   const int rmax = std::max(d->rank_in, d->rank_out);
   const double elems = (double)d->batch * d->seqlen * d->nheads * rmax *
@@ -390,6 +393,7 @@ int scan_fwd_impl(const ssm_desc* d, const ssm_fwd_args* a, void* ws, size_t ws_
   p.h0 = a->h0; p.h_final = a->h_final; p.x_prev = a->x_prev; p.B_prev = a->B_prev;
   p.batch = d->batch; p.L = d->seqlen; p.H = d->nheads; p.G = d->ngroups; p.P = d->headdim;
   p.n_real = d->n_real; p.n_pairs = d->n_pairs; p.nchunks = pl.nchunks;
+  p.n_static = d->n_static;
   p.npblk = d->headdim / pb;
   p.rin = d->rank_in;
   p.rout = d->rank_out;
@@ -520,6 +524,7 @@ int ssm_scan_bwd(const ssm_desc* d, const ssm_bwd_args* a, void* ws, size_t ws_b
                                     (bwd_gseg_bytes(d, pl) + 255) / 256 * 256);
   p.batch = d->batch; p.L = d->seqlen; p.H = d->nheads; p.G = d->ngroups; p.P = d->headdim;
   p.n_real = d->n_real; p.n_pairs = d->n_pairs; p.nchunks = pl.nchunks;
+  p.n_static = d->n_static;
   p.rin = d->rank_in; p.rout = d->rank_out;
   const Segs sg = adj_segments(d, pl);
   p.nseg = sg.nseg;
@@ -561,7 +566,7 @@ int ssm_decode_step(const ssm_desc* d, const ssm_decode_args* a, void* stream) {
   if (!a) return SSM_ERR_NULL;
   if (d->seqlen != 1) return SSM_ERR_SHAPE;
   if (d->rank_in > ssm::kDecodeMaxRank || d->rank_out > ssm::kDecodeMaxRank ||
-      d->headdim % 4 || d->headdim > 1024 || (d->n_real % 2))
+      d->headdim % 4 || d->headdim > 1024 || (d->n_real % 2) || (d->n_static % 2))
     return SSM_ERR_UNSUPPORTED;
   if ((double)d->batch * d->nheads * d->dstate * d->headdim >= 2147483648.0)
     return SSM_ERR_UNSUPPORTED;
@@ -593,6 +598,7 @@ int ssm_decode_step(const ssm_desc* d, const ssm_decode_args* a, void* stream) {
   p.state = a->state; p.y = a->y;
   p.batch = d->batch; p.H = d->nheads; p.G = d->ngroups; p.P = d->headdim;
   p.R = d->rank_in; p.O = d->rank_out; p.n_real = d->n_real; p.n_pairs = d->n_pairs;
+  p.n_static = d->n_static;
   p.softplus = (d->flags & SSM_F_DT_SOFTPLUS) ? 1 : 0;
   p.head_rates = d->decay_mode == SSM_DECAY_HEAD ? 1 : 0;
   p.tps = tps;

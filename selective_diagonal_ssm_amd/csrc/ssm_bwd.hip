@@ -71,7 +71,9 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_adjoint(BwdParams p) {
   constexpr int NS = S::NS, VS = S::VS, VEC = S::VEC;
   __shared__ __align__(16) T sQ[S::QOC * NS];  // folded, decayed C rows
   __shared__ __align__(16) T sY[S::QOC * VS];  // dy rows (head mode: decayed)
-  __shared__ float sRate[N], sOmega[N / 2 + 1];
+  // per-row rates: a dynamic row's in sRate (exponent rate x summed step), a static row's
+  // in sRateS (exponent rate x token count)
+  __shared__ float sRate[N], sRateS[N], sOmega[N / 2 + 1];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   // the chunk-gradient kernel that follows sets this word when a chunk is too steep for
@@ -92,7 +94,9 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_adjoint(BwdParams p) {
       if (p.head_rates) r = p.A[h];
       else if (n < nreal) r = p.A[(size_t)h * na + n];
       else r = p.A[(size_t)h * na + nreal + ((n - nreal) >> 1)];
-      sRate[n] = r;
+      const bool st = n < p.n_static;
+      sRate[n] = st ? 0.f : r;
+      sRateS[n] = st ? r : 0.f;
     }
     for (int k = tid; k < p.n_pairs; k += S::NTH) sOmega[k] = p.omega[(size_t)h * p.n_pairs + k];
   }
@@ -188,6 +192,9 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_adjoint(BwdParams p) {
     const float cdx = cd - read_lane(dl, 0);               // sum over (t0, t]
     const float cdx_end = read_lane(cdx, QT - 1) + dnext;  // sum over (t0, t0']
     dnext = read_lane(dl, 0);
+    // static rows count the transitions instead: t - t0 over (t0, t], and over (t0, t0']
+    // the chunk's tokens after the first plus the next chunk's first token
+    const float cnx_end = static_cast<float>(min(QT, L - t0) - 1 + (t0 + QT < L ? 1 : 0));
 
     // operands: rows (t, o) of  e^{L'_t} R(-Theta'_t) C_t  and  dy_t
 #pragma unroll
@@ -195,6 +202,7 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_adjoint(BwdParams p) {
       const int v = tid + S::NTH * k;
       const int row = (v < S::C_VECS ? v : 0) / (N / VEC);
       const float cdr = __shfl(cdx, row / R, kWave);
+      const float cnr = static_cast<float>(row / R);
       if (v < S::C_VECS) {
         const int nv = v % (N / VEC), n0 = nv * VEC;
         uint4 raw = pc[k];
@@ -213,7 +221,7 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_adjoint(BwdParams p) {
             }
           }
 #pragma unroll
-          for (int i = 0; i < VEC; ++i) vals[i] *= __expf(-sRate[n0 + i] * cdr);
+          for (int i = 0; i < VEC; ++i) vals[i] *= __expf(-sRate[n0 + i] * cdr - sRateS[n0 + i] * cnr);
           raw = pack<BF16>(vals);
         }
         *reinterpret_cast<uint4*>(sQ + row * NS + n0) = raw;
@@ -245,7 +253,7 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_adjoint(BwdParams p) {
       const int tile = wave + NW * k;
       if (tile < S::ST_TILES) {
         const int n = 16 * (tile / S::TP) + (lane & 15);
-        const float dec = COORD ? __expf(-sRate[n] * cdx_end) : __expf(-Ah * cdx_end);
+        const float dec = COORD ? __expf(-sRate[n] * cdx_end - sRateS[n] * cnx_end) : __expf(-Ah * cdx_end);
 #pragma unroll
         for (int i = 0; i < 4; ++i) st[k][i] *= dec;
         if (COORD) {
@@ -294,7 +302,7 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_adjoint(BwdParams p) {
       const int tile = wave + NW * k;
       if (tile < S::ST_TILES) {
         const int n = 16 * (tile / S::TP) + (lane & 15), pl = 16 * (tile % S::TP) + 4 * (lane >> 4);
-        const float dec = COORD ? __expf(-sRate[n] * d0) : __expf(-Ah * d0);
+        const float dec = COORD ? __expf(-sRate[n] * d0 - sRateS[n]) : __expf(-Ah * d0);
         float v[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) v[i] = st[k][i] * dec;
@@ -339,6 +347,9 @@ __global__ __launch_bounds__(256) void ssm_adj_combine(BwdParams p, int per_row)
       return m < nreal ? p.A[(size_t)h * na + m] : p.A[(size_t)h * na + nreal + ((m - nreal) >> 1)];
     };
     const float ra = rate(n), rb = rate(n + 1);
+    // static rows (n_static is even, so both rows of the pair (n, n + 1) are of one kind)
+    // decay once per token: over a range, the number of transitions it spans
+    const bool stat = per_row && n < p.n_static;
     const bool pair = per_row && n >= nreal;
     const float om = pair ? p.omega[(size_t)h * p.n_pairs + ((n - nreal) >> 1)] : 0.f;
     const size_t sb = (size_t)slice * p.nseg, sl = (size_t)slice * (p.nseg - 1) * p.nsub;
@@ -365,7 +376,14 @@ __global__ __launch_bounds__(256) void ssm_adj_combine(BwdParams p, int per_row)
 #pragma unroll
         for (int k = 0; k < kCombineBlock; ++k) {
           if (k >= cnt) break;
-          const float dsum = ds[k];
+          float dsum = ds[k];
+          if (stat) {
+            // range u0 - k of segment s: the transitions of its tokens after the first and
+            // of the token after it (when inside the sequence)
+            const int ta = s * p.seg_tokens + (u0 - k) * p.lsub;
+            const int tb = min(min(ta + p.lsub, (s + 1) * p.seg_tokens), p.L) - 1;
+            dsum = tb >= ta ? static_cast<float>(tb - ta + (tb + 1 < p.L ? 1 : 0)) : 0.f;
+          }
           float a2 = a * expf(-ra * dsum), b2 = bv * expf(-rb * dsum);
           if (pair) {
             float sn, cs;
@@ -461,14 +479,16 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
 
   __shared__ __align__(16) T sQ[S::QOC * NS];   // q rows (t, o)
   __shared__ __align__(16) T sK[QK * NS];        // k rows j
-  __shared__ __align__(16) T sKe[COORD ? QK * NS : 8];
+  
   __shared__ __align__(16) T sV[QK * PS];        // value rows j
   __shared__ __align__(16) T sY[S::QOC * PS];   // dy rows (t, o)
   __shared__ __align__(16) T sSM[S::QOC * KS];  // (S o M) rows (t, o)
   __shared__ __align__(16) T sZM[S::QOC * KS];  // (Z o M) rows (t, o)
   __shared__ __align__(16) T sGh[S::NC * PS];   // folded adjoint G~ (io dtype)
   __shared__ __align__(16) T sSh[N * PS];        // incoming state (io dtype)
-  __shared__ float sRate[N], sOmega[N / 2 + 1];
+  // per-row rates: a dynamic row's in sRate (exponent rate x summed step), a static row's
+  // in sRateS (exponent rate x token count)
+  __shared__ float sRate[N], sRateS[N], sOmega[N / 2 + 1];
   __shared__ float sE2[2][N], sEth[N / 2 + 1];   // final-state terms per row (by item parity) / pair
   constexpr int WC = COORD ? NW : 1, WH = COORD ? 1 : NW, WT = S::TE ? NW : 1;
   constexpr int NCO = COORD ? N : 1, PCO = COORD ? N / 2 + 1 : 1;
@@ -483,7 +503,7 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
   __shared__ __align__(16) float sTailX[S::TE ? R * P : 4], sTailB[S::TE ? R * N : 4];
   // two-endpoint tail inputs: the next chunk's raw first adjoint g', B and X of the
   // chunk's last token
-  __shared__ __align__(16) float sGraw[S::TE ? N * P : 4];
+  __shared__ __align__(16) T sGraw[S::TE ? N * PS : 8];  // io dtype, rows of PS
   __shared__ __align__(16) T sBt1[S::TE ? R * N : 8], sXt1[S::TE ? R * P : 8];
   // two-endpoint: the item's raw B rows (token t0 - 1 + row / R), for the endpoint-weight
   // gradients
@@ -535,7 +555,6 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
     for (int i = tid; i < S::QOC * (S::NC - N); i += S::NTH) sQ[(i / (S::NC - N)) * NS + N + i % (S::NC - N)] = T(0);
     for (int i = tid; i < QK * (S::NC - N); i += S::NTH) {
       sK[(i / (S::NC - N)) * NS + N + i % (S::NC - N)] = T(0);
-      if (COORD) sKe[(i / (S::NC - N)) * NS + N + i % (S::NC - N)] = T(0);
     }
   }
   if (S::PC > P) {
@@ -754,7 +773,11 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
     if (!RELAXED) __syncthreads();  // the previous item is done with every shared buffer
     if (COORD) {
       // rates and pair frequencies arrived with the item's prefetched operands
-      if (tid < N) sRate[tid] = pf_rate;
+      if (tid < N) {
+        const bool st = tid < p.n_static;
+        sRate[tid] = st ? 0.f : pf_rate;
+        sRateS[tid] = st ? pf_rate : 0.f;
+      }
       else if (tid < N + npairs) sOmega[tid - N] = pf_rate;
     }
     if (!RELAXED) {
@@ -786,12 +809,18 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
     }
     const float cd_l = wave_prefix_sum(dl);
     const float cdend = read_lane(cd_l, QT - 1);
+    // static rows count tokens in place of the summed step: t + 1 at token t, the chunk's
+    // tokens inside the sequence at its end, one for the next chunk's first token
+    const float nvend = static_cast<float>(min(QT, L - t0));
     if constexpr (COORD) {
       // a chunk too steep for the midpoint fold is redone by the token-by-token reverse
-      // pass: the largest |rate| of the item's rows (lanes of wave 0 hold the rates)
+      // pass: the largest |rate| of the item's dynamic and static rows (lanes of wave 0
+      // hold the rates)
       if (wave == 0 && p.wild) {
-        const float amax = wave_max(lane < N ? fabsf(pf_rate) : 0.f);
-        const bool steep = amax * cdend > kFoldLimit;
+        const bool st = lane < p.n_static;
+        const float amax = wave_max(lane < N && !st ? fabsf(pf_rate) : 0.f);
+        const float smax = wave_max(lane < N && st ? fabsf(pf_rate) : 0.f);
+        const bool steep = amax * cdend + smax * nvend > kFoldLimit;
         if (lane == 0) {
           p.wild[item] = steep ? 1 : 0;
           if (steep) atomicOr(p.wild_any, 1);
@@ -814,7 +843,7 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
     }
     if constexpr (COORD) {
       // factor tables (one entry pair per thread; the shuffle runs on whole waves)
-      const float hc = 0.5f * cdend;
+      const float hc = 0.5f * cdend, hn = 0.5f * nvend;
       constexpr int TE_N = QT * (N / 2);
 #pragma unroll
       for (int i0 = 0; i0 < TE_N; i0 += S::NTH) {
@@ -831,7 +860,9 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
             q = make_float2(e * cs, e * sn);
             k = make_float2(ei * cs, ei * sn);
           } else {
-            const float x0 = sRate[n] * (cd - hc), x1 = sRate[n + 1] * (cd - hc);
+            const float cn = static_cast<float>(t + 1) - hn;
+            const float x0 = sRate[n] * (cd - hc) + sRateS[n] * cn;
+            const float x1 = sRate[n + 1] * (cd - hc) + sRateS[n + 1] * cn;
             q = make_float2(__expf(-x0), __expf(-x1));
             k = make_float2(__expf(x0), __expf(x1));
           }
@@ -840,8 +871,8 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
         }
       }
       for (int n = tid; n < N; n += S::NTH) {
-        sEr[n] = __expf(-sRate[n] * hc);
-        sFd[n] = __expf(-sRate[n] * dnext);
+        sEr[n] = __expf(-sRate[n] * hc - sRateS[n] * hn);
+        sFd[n] = __expf(-sRate[n] * dnext - (has_next ? sRateS[n] : 0.f));
         if (n >= nreal && ((n - nreal) & 1) == 0) {
           float sn, cs;
           fast_sincos(sOmega[(n - nreal) >> 1] * (cdend + dnext), &sn, &cs);
@@ -890,18 +921,14 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
         const int tau = sl + e;
         if (tau < 0 || tau >= QT || (e == 0 && sl < 0)) continue;
         const int j = tau * KR + (e ? R : 0) + r;
-        float u[VEC], kk[VEC], ke[VEC];
+        float u[VEC], kk[VEC];
   #pragma unroll
         for (int i = 0; i < VEC; ++i) u[i] = vals[i] * wv[e];
         if (COORD) {
           // k = R(-Theta_tau) u / E_tau,  ke = k e^{-A CD_end / 2}
           apply_tab(u, sTK + tau * N, n0);
   #pragma unroll
-          for (int i = 0; i < VEC; ++i) {
-            kk[i] = u[i];
-            ke[i] = u[i] * sEr[n0 + i];
-          }
-          *reinterpret_cast<uint4*>(sKe + j * NS + n0) = pack<BF16>(ke);
+          for (int i = 0; i < VEC; ++i) kk[i] = u[i];
         } else {
   #pragma unroll
           for (int i = 0; i < VEC; ++i) kk[i] = u[i];
@@ -929,6 +956,8 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
       *reinterpret_cast<uint4*>(sY + row * PS + p0) = pfy[k];
     }
     // incoming state S_in and folded adjoint G~ = e^{-A Dnext} R(-omega (cd_end + Dnext)) g'
+    // (per-row decay: also times e^{-A CD_end / 2}, the factor that turns the folded keys
+    // into the keys seen from the chunk end, so the keys need no second scaled copy)
     // (rounded to the io dtype as MFMA operands), final-state terms per row / pair
     {
       const float lend_h = COORD ? 0.f : __expf(-Ah * cdend);
@@ -945,13 +974,13 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
         raw4_f32(pfg[k][0], ga);
         raw4_f32(pfg[k][1], gb);
         if (S::TE) {
-          *reinterpret_cast<float4*>(sGraw + n * P + q0) = make_float4(ga[0], ga[1], ga[2], ga[3]);
-          *reinterpret_cast<float4*>(sGraw + (n + 1) * P + q0) = make_float4(gb[0], gb[1], gb[2], gb[3]);
+          store4<BF16>(sGraw + n * PS + q0, ga);
+          store4<BF16>(sGraw + (n + 1) * PS + q0, gb);
         }
         float fa, fb, lea, leb;
         if (COORD) {
-          fa = sFd[n]; fb = sFd[n + 1];
-          lea = sEr[n] * sEr[n]; leb = sEr[n + 1] * sEr[n + 1];
+          fa = sFd[n] * sEr[n]; fb = sFd[n + 1] * sEr[n + 1];
+          lea = sEr[n]; leb = sEr[n + 1];
         } else {
           fa = fb = gdec_h; lea = leb = lend_h;
         }
@@ -1002,26 +1031,24 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
     }
     // two-endpoint tails of the last token from the staged rows: beta_{t0'} B_{t1}^T g'
     // and g' X_{t1}^T (zero without a next chunk, where g' and beta_{t0'} are zero),
-    // as fp32 MFMA products with the R rows padded to 16:
+    // as MFMA products in the io dtype (g' rounded to it, as the folded G~ is) with the
+    // R rows padded to 16:
     //   tail X (R x P) = B_{t1} (R x N) g' (N x P),   tail B^T (N x R) = g' (N x P) X_{t1}^T (P x R),
     // one 16-column output tile per wave (P / 16 tiles of tail X, then N / 16 of tail B)
     if constexpr (S::TE && N % 32 == 0 && P % 32 == 0) {
       static_assert(R <= 16, "tail products with the rows padded to 16");
       // 8 consecutive elements of row m of a staged R-row buffer (zero for m >= R)
       auto rows8 = [&](const T* buf, int ld, int m, int k0) {
-        Frag<false> f;
+        Frag<BF16> f;
         if (m < R) {
-          if constexpr (BF16) {
-            float v[8];
-            unpack<true>(*reinterpret_cast<const uint4*>(buf + m * ld + k0), v);
-#pragma unroll
-            for (int i = 0; i < 8; ++i) f.v[i] = v[i];
-          } else {
-            f = load_frag<false>(reinterpret_cast<const float*>(buf) + m * ld + k0);
-          }
+          f = load_frag<BF16>(buf + m * ld + k0);
         } else {
+          if constexpr (BF16) {
+            f.v = bf16x8{};
+          } else {
 #pragma unroll
-          for (int i = 0; i < 8; ++i) f.v[i] = 0.f;
+            for (int i = 0; i < 8; ++i) f.v[i] = 0.f;
+          }
         }
         return f;
       };
@@ -1032,8 +1059,8 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
 #pragma unroll
           for (int kk = 0; kk < N / 32; ++kk) {
             const auto fa = rows8(sBt1, N, lane & 15, kk * 32 + 8 * (lane >> 4));
-            const auto fb = load_frag_tr<false>(sGraw + (kk * 32) * P + 16 * tp, P);
-            mma<false>(acc, fa, fb);
+            const auto fb = load_frag_tr<BF16>(sGraw + (kk * 32) * PS + 16 * tp, PS);
+            mma<BF16>(acc, fa, fb);
           }
           // lane l: rows r = 4 (l >> 4) + i, column p = 16 tp + (l & 15)
 #pragma unroll
@@ -1045,9 +1072,9 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
           const int tn = u - P / 16;
 #pragma unroll
           for (int kk = 0; kk < P / 32; ++kk) {
-            const auto fa = load_frag<false>(sGraw + (16 * tn + (lane & 15)) * P + kk * 32 + 8 * (lane >> 4));
+            const auto fa = load_frag<BF16>(sGraw + (16 * tn + (lane & 15)) * PS + kk * 32 + 8 * (lane >> 4));
             const auto fb = rows8(sXt1, P, lane & 15, kk * 32 + 8 * (lane >> 4));
-            mma<false>(acc, fa, fb);
+            mma<BF16>(acc, fa, fb);
           }
           // lane l: rows n = 16 tn + 4 (l >> 4) + i, column r = l & 15
           if ((lane & 15) < R) {
@@ -1070,12 +1097,12 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
           const int r = o / P, pp = o % P;
 #pragma unroll 2
           for (int n = part * (N / TT); n < (part + 1) * (N / TT); ++n)
-            acc += to_f32(sBt1[r * N + n]) * sGraw[n * P + pp];
+            acc += to_f32(sBt1[r * N + n]) * to_f32(sGraw[n * PS + pp]);
         } else if (o < OT) {
           const int r = (o - O1) / N, n = (o - O1) % N;
 #pragma unroll 2
           for (int pp = part * (P / TT); pp < (part + 1) * (P / TT); ++pp)
-            acc += sGraw[n * P + pp] * to_f32(sXt1[r * P + pp]);
+            acc += to_f32(sGraw[n * PS + pp]) * to_f32(sXt1[r * P + pp]);
         }
         acc = group_sum<TT>(acc);
         if (part == 0 && o < O1) sTailX[o] = bnext * acc;
@@ -1168,7 +1195,7 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
     __syncthreads();
 
     // ---------------------------------------------------------------- dV -> dX
-    // dV^T = dY^T (S o M) + G~^T Ke^T, computed transposed: lane l holds key
+    // dV^T = dY^T (S o M) + G~^T K^T, computed transposed: lane l holds key
     // 16 tj + (l & 15) and value columns 16 tp + 4 (l >> 4) + i.  When NW is a multiple
     // of the column tiles, a wave takes two tiles of one column block (tiles t and
     // t + NW), and their dY and G~ fragments are read once.
@@ -1223,7 +1250,7 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
             const auto fgh = load_frag_tr<BF16>(sGh + (kk * 32) * PS + 16 * tp, PS);
 #pragma unroll
             for (int x = 0; x < DVB; ++x) {
-              const auto fk = load_frag<BF16>((COORD ? sKe : sK) + (16 * tjs[x] + (lane & 15)) * NS + kk * 32 + 8 * (lane >> 4));
+              const auto fk = load_frag<BF16>(sK + (16 * tjs[x] + (lane & 15)) * NS + kk * 32 + 8 * (lane >> 4));
               mma<BF16>(ae[x], fgh, fk);
             }
           }
@@ -1257,14 +1284,13 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
         const int n = n0 + i;
         rpa[i] = 0.f; rek[i] = 0.f;
         if (COORD) {
-          const float er = sEr[n];  // e^{r_n}
-          const float ck = ai[i] + er * ae[i];
+          const float ck = ai[i] + ae[i];
           dk[i] = ck;  // scaled by e^{r - L_s} (with the pair's turn) below
           // source terms: -k o cK  (rows); the inter part also feeds the final-state term
           const float dr = -kv[i] * ck;
-          tokacc += -sRate[n] * dr;
-          rpa[i] = -cds * dr;
-          rek[i] = kv[i] * er * ae[i];
+          tokacc += -sRate[n] * dr;                          // zero on static rows
+          rpa[i] = -(n < p.n_static ? static_cast<float>(s + 1) : cds) * dr;
+          rek[i] = kv[i] * ae[i];
         } else {
           dk[i] = ai[i] + wj * ae[i];
           tokacc += kv[i] * wj * ae[i];  // K~ o dK~ (inter part)
@@ -1276,13 +1302,12 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
           const int n = n0 + i;
           if (n >= nreal) {
             const int kp = (n - nreal) >> 1;
-            const float er = sEr[n];
-            const float ca = ai[i] + er * ae[i], cb = ai[i + 1] + er * ae[i + 1];
+            const float ca = ai[i] + ae[i], cb = ai[i + 1] + ae[i + 1];
             // K~^T J dK~ in scaled form: -k_a cK_b + k_b cK_a
             const float dth = -kv[i] * cb + kv[i + 1] * ca;
             tokacc += sOmega[kp] * dth;
             rpw[i >> 1] = cds * dth;
-            rekt[i >> 1] = -(-kv[i] * er * ae[i + 1] + kv[i + 1] * er * ae[i]);
+            rekt[i >> 1] = -(-kv[i] * ae[i + 1] + kv[i + 1] * ae[i]);
           }
         }
         // dK~ = e^{r - L_s} cK, and unfold the key's rotation: u = R(+Theta_s) dK~
@@ -1465,8 +1490,8 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
           const float cc = ai[i] + er * ae[i];
           dc[i] = cc;  // scaled by E_t (with the pair's turn) below
           const float dr = qv[i] * cc;
-          tokacc += -sRate[n] * dr;
-          rpa[i] = -cdt * dr;
+          tokacc += -sRate[n] * dr;                          // zero on static rows
+          rpa[i] = -(n < p.n_static ? static_cast<float>(t + 1) : cdt) * dr;
         } else {
           dc[i] = ai[i] + elt * ae[i];
           tokacc += qv[i] * elt * ae[i];  // C~ o dC~ (inter part)
@@ -1676,7 +1701,7 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
         __syncthreads();
         for (int n = tid; n < N; n += S::NTH) {
           const float en = sE[n] + wsum<WC>(sEK, n);
-          sEK[0][n] = wsum<WC>(sPA, n) + (-cdend) * en;
+          sEK[0][n] = wsum<WC>(sPA, n) - (n < p.n_static ? nvend : cdend) * en;
         }
         __syncthreads();
         if (p.head_rates) {
@@ -1829,6 +1854,9 @@ __global__ __launch_bounds__(256) void ssm_bwd_params(BwdParams p, int nA) {
   X(true, 64, 64, 4, 4, 16, false, false)     \
   X(true, 64, 64, 1, 2, 16, true, false)      \
   X(true, 64, 64, 2, 4, 16, true, false)     \
+  /* per-row decay with plain writes */     \
+  X(true, 64, 64, 1, 1, 32, true, false)     \
+  X(true, 64, 64, 2, 2, 16, true, false)     \
   /* write and readout ranks that differ */ \
   X(false, 32, 16, 2, 2, 32, false, true)    \
   X(false, 32, 16, 2, 4, 16, true, true)     \
@@ -1887,6 +1915,7 @@ static LocalParams adj_local_params(const BwdParams& p) {
   l.key = p.C; l.val = p.dy; l.dt = p.dt; l.A = p.A; l.omega = p.omega;
   l.out = p.gloc; l.delta = p.gdel; l.rk = p.rout;
   l.batch = p.batch; l.L = p.L; l.H = p.H; l.G = p.G; l.P = p.P; l.n_real = p.n_real;
+  l.n_static = p.n_static;
   l.n_pairs = p.n_pairs; l.softplus = p.softplus; l.head_rates = p.head_rates;
   l.nseg = p.nseg; l.seg_tokens = p.seg_tokens; l.nsub = p.nsub; l.lsub = p.lsub;
   return l;

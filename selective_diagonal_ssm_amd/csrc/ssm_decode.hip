@@ -183,7 +183,9 @@ __global__ __launch_bounds__(256) void ssm_decode_kernel(DecodeParams p) {
     sC[2 * it + 1] = e.y;
   }
   if (live && tid < npair) {
-    const float d0 = __expf(-ra0 * dl), d1 = __expf(-ra1 * dl);
+    // a static row pair (n_static is even) takes a unit step whatever Delta is
+    const float dq = nq < p.n_static ? 1.f : dl;
+    const float d0 = __expf(-ra0 * dq), d1 = __expf(-ra1 * dq);
     if (qpair) {
       float sn, cs;
       fast_sincos(om * dl, &sn, &cs);
@@ -204,8 +206,9 @@ __global__ __launch_bounds__(256) void ssm_decode_kernel(DecodeParams p) {
       sTab[n] = d * cs;
       sTab[n + 1] = d * sn;
     } else {
-      sTab[n] = __expf(-p.A[p.head_rates ? h : h * na + n] * dl);
-      sTab[n + 1] = __expf(-p.A[p.head_rates ? h : h * na + n + 1] * dl);
+      const float dq = n < p.n_static ? 1.f : dl;
+      sTab[n] = __expf(-p.A[p.head_rates ? h : h * na + n] * dq);
+      sTab[n + 1] = __expf(-p.A[p.head_rates ? h : h * na + n + 1] * dq);
     }
   }
   lds_barrier();

@@ -6,8 +6,8 @@
 // so the intra-chunk product stays one MFMA contraction.  The folded factors reach
 // e^{A_n CD_end / 2}: when a chunk's summed step times the largest rate of its rows
 // passes kFoldLimit, those kernels flag the chunk and a kernel here redoes the work with
-// the recurrence itself, whose factors are the decays a_t = e^{-A_n Delta_t} <= 1 and the
-// pair rotations -- exact for any step:
+// the recurrence itself, whose factors are the decays a_t = e^{-A_n Delta_t} <= 1 (e^{-A_n}
+// on a static row) and the pair rotations -- exact for any step:
 //
 //   ssm_fwd_exact  one workgroup per (slice, sequence segment, value-column block) whose
 //                  segment holds a flagged chunk: h_t = A_t h_{t-1} + gamma_t B_t X_t +
@@ -50,12 +50,12 @@ __device__ __forceinline__ float row_rate(const float* A, int h, int n, int nrea
 }
 
 // Per-token transition table of one token: real row n -> a_t[n]; the rows (n0, n0 + 1) of
-// a pair -> (rho cos theta, rho sin theta).
+// a pair -> (rho cos theta, rho sin theta).  A static row (n < nstatic) takes a unit step.
 __device__ __forceinline__ void transition_entry(float* dst, int n, float delta,
                                                  const float* rate, const float* om,
-                                                 int nreal) {
+                                                 int nreal, int nstatic) {
   if (n < nreal) {
-    dst[n] = __expf(-rate[n] * delta);
+    dst[n] = __expf(-rate[n] * (n < nstatic ? 1.f : delta));
   } else if (((n - nreal) & 1) == 0) {
     const float rho = __expf(-rate[n] * delta);
     float sn, cs;
@@ -198,7 +198,7 @@ __global__ __launch_bounds__(256) void ssm_fwd_exact(FwdParams p, int qtk) {
       const int tau = i / N, n = i % N;
       const float raw = dtg[(size_t)(t0 + tau) * H];
       const float delta = p.softplus ? softplus_f32(raw) : raw;
-      transition_entry(sTr[tau], n, delta, sRate, sOm, nreal);
+      transition_entry(sTr[tau], n, delta, sRate, sOm, nreal, p.n_static);
     }
     __syncthreads();
     for (int tau = 0; tau < nt; ++tau) {
@@ -369,7 +369,8 @@ __global__ __launch_bounds__(256) void ssm_bwd_exact(BwdParams p) {
       __syncthreads();
       for (int i = tid; i < (nT + 1) * N; i += 256) {
         const int tau = i / N, n = i % N;
-        transition_entry(sTr[tau], n, sDl[tau], sRate, sOm, nreal);
+        // past the sequence end there is no transition (step 0, and no static rows either)
+        transition_entry(sTr[tau], n, sDl[tau], sRate, sOm, nreal, (tau < nT || has_next) ? p.n_static : 0);
       }
       // V_{t1+1} and W_{t1+1} from the next chunk's adjoint and token t1's X and B rows
       for (int i = tid; i < R * N; i += 256) {
@@ -519,9 +520,11 @@ __global__ __launch_bounds__(256) void ssm_bwd_exact(BwdParams p) {
         if (tid < N) {
           const int n = tid;
           if (n < nreal) {
+            // a static row takes a unit step whatever Delta is: no step gradient
             const float a = sTr[tau][n], e = sE[n][0];
-            ddl = -sRate[n] * a * e;
-            sPart[n] += -dl * a * e;
+            const bool st = n < p.n_static;
+            ddl = st ? 0.f : -sRate[n] * a * e;
+            sPart[n] += -(st ? 1.f : dl) * a * e;
           } else if (((n - nreal) & 1) == 0) {
             const int k2 = (n - nreal) >> 1;
             const float cr = sTr[tau][n], sr = sTr[tau][n + 1];  // rho cos, rho sin

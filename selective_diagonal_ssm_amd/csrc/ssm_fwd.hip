@@ -139,8 +139,11 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
   // beta / gamma of chunk c in slot c & 3 (a chunk's readout still reads its own after the
   // next-but-one chunk's are staged)
   __shared__ __align__(16) float sGa[4][S::TE ? 64 : 1], sBe[4][S::TE ? 64 : 1];
-  __shared__ float sMisc[4][2];                // CD_end, head: e^{-A CD_end}
-  __shared__ float sRate[COORD ? N : 1], sOmega[COORD ? N / 2 + 1 : 1];
+  __shared__ float sMisc[4][3];                // CD_end, head: e^{-A CD_end}, tokens in the chunk
+  // per-row decay: the exponent of row n over a stretch of tokens is
+  // sRate[n] (summed step) + sRateS[n] (token count): a dynamic row has its rate in
+  // sRate, a static row (decay e^{-A} per token, whatever the step) in sRateS
+  __shared__ float sRate[COORD ? N : 1], sRateS[COORD ? N : 1], sOmega[COORD ? N / 2 + 1 : 1];
   // per-row decay: factor tables of the next chunk to stage, [token][n] (see tables)
   __shared__ __align__(16) float sTC[COORD ? QT * N : 4], sTK0[COORD ? QT * N : 4];
   __shared__ __align__(16) float sTK1[COORD && S::TE && !S::SHIFT ? QT * N : 4];
@@ -165,12 +168,16 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
 
   // per-row rates (thread n < N) and pair frequencies (thread k < n_pairs): read first,
   // written to LDS once the prologue's other reads are in flight
-  float r_rate = 0.f, r_om = 0.f;
+  float r_rate = 0.f, r_rs = 0.f, r_om = 0.f;
   if (COORD) {
     const int na = p.n_real + p.n_pairs;
     if (tid < N)
       r_rate = p.head_rates ? p.A[h]  // one rate per head
                             : p.A[(size_t)h * na + (tid < nreal ? tid : nreal + ((tid - nreal) >> 1))];
+    if (tid < p.n_static) {  // a static row's rate goes with the token count
+      r_rs = r_rate;
+      r_rate = 0.f;
+    }
     if (tid < p.n_pairs) r_om = p.omega[(size_t)h * p.n_pairs + tid];
   }
   // the state entering the first chunk: h0 (rows < N, this P-block), the combined
@@ -265,13 +272,14 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
   // per-row decay: the largest |rate| of the head's rows (factor wave, from the rates its
   // lanes read) and whether a chunk of this range is too steep for the midpoint fold
   // (summed step times that rate above kFoldLimit)
-  float amax = 0.f;
+  float amax = 0.f, smax = 0.f;  // dynamic rows' and static rows' largest |rate|
   bool steep = false;
   auto factors = [&](int c, float dl) {
     const int bi = c & 3;
     const float cd = wave_prefix_sum(dl);
     const float cdend = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cd), QT - 1));
-    if (COORD) steep = steep || amax * cdend > kFoldLimit;
+    const int nv = min(QT, L - c * QT);  // tokens of the chunk inside the sequence
+    if (COORD) steep = steep || amax * cdend + smax * nv > kFoldLimit;
     if (lane < QT) {
       if (COORD) sCD[bi][lane] = cd;
       if (!COORD) {
@@ -281,6 +289,7 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
     if (lane == 0) {
       sMisc[bi][0] = cdend;
       sMisc[bi][1] = COORD ? 0.f : __builtin_amdgcn_exp2f(-Ah * kLog2e * cdend);
+      sMisc[bi][2] = static_cast<float>(nv);
     }
   };
 
@@ -293,10 +302,11 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
   //   q = R(-Theta_t) C_t E_t,  k = R(-Theta_s) (g B) / E_s.
   // With the shift identity the key table is TK0 = TK1[t] + TK0[t-1] (the key at t
   // carries B_{t-1}), where the entry at t = -1 is gamma of the token before the chunk
-  // (gprev) at CD = 0, Theta = 0.
+  // (gprev) at CD = 0, Theta = 0.  A static row counts tokens instead: CD_t is t + 1 and
+  // CD_end the chunk's token count.
   auto tables = [&](int c, float gprev) {
     const int sc = c & 3, sg = c & 3;
-    const float hc = 0.5f * sMisc[sc][0];
+    const float hc = 0.5f * sMisc[sc][0], hn = 0.5f * sMisc[sc][2];
     for (int i = tid; i < QT * (N / 2); i += S::NTH) {
       const int t = i / (N / 2), n = 2 * (i % (N / 2));
       const float cd = sCD[sc][t] - hc;
@@ -321,14 +331,16 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
           tk0 = make_float2(tk1.x + gm * eim * csm, tk1.y + gm * eim * snm);
         }
       } else {
-        const float x0 = sRate[n] * cd, x1 = sRate[n + 1] * cd;
+        // static rows: the token count t + 1 in place of the summed step
+        const float cn = static_cast<float>(t + 1) - hn, cnm = static_cast<float>(t) - hn;
+        const float x0 = sRate[n] * cd + sRateS[n] * cn, x1 = sRate[n + 1] * cd + sRateS[n + 1] * cn;
         const float ei0 = __expf(x0), ei1 = __expf(x1);
         tc = make_float2(__expf(-x0), __expf(-x1));
         tk0 = make_float2(g0 * ei0, g0 * ei1);
         tk1 = make_float2(g1 * ei0, g1 * ei1);
         if (SH)
-          tk0 = make_float2(tk1.x + gm * __expf(sRate[n] * (cdm - hc)),
-                            tk1.y + gm * __expf(sRate[n + 1] * (cdm - hc)));
+          tk0 = make_float2(tk1.x + gm * __expf(sRate[n] * (cdm - hc) + sRateS[n] * cnm),
+                            tk1.y + gm * __expf(sRate[n + 1] * (cdm - hc) + sRateS[n + 1] * cnm));
       }
       *reinterpret_cast<float2*>(sTC + t * N + n) = tc;
       *reinterpret_cast<float2*>(sTK0 + t * N + n) = tk0;
@@ -553,7 +565,10 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
 #pragma unroll
   for (int k = 0; k < S::ST_PER_WAVE; ++k) asm volatile("" : "+v"(st[k]));
   if (COORD) {
-    if (tid < N) sRate[tid] = r_rate;
+    if (tid < N) {
+      sRate[tid] = r_rate;
+      sRateS[tid] = r_rs;
+    }
     if (tid < p.n_pairs) sOmega[tid] = r_om;
   }
   if (saved && seg == 0) {
@@ -570,7 +585,10 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
       }
     }
   }
-  if (COORD && wave == PW) amax = wave_max(tid < N ? fabsf(r_rate) : 0.f);
+  if (COORD && wave == PW) {
+    amax = wave_max(tid < N ? fabsf(r_rate) : 0.f);
+    smax = wave_max(tid < N ? fabsf(r_rs) : 0.f);
+  }
   if (wave == PW) {
     factors(c0, (lane < QT && c0 * QT + lane < L) ? (p.softplus ? softplus_f32(dt0) : dt0) : 0.f);
     if (c0 + 1 < c1) factors(c0 + 1, (lane < QT && (c0 + 1) * QT + lane < L) ? (p.softplus ? softplus_f32(dt1) : dt1) : 0.f);
@@ -583,13 +601,13 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
   // buffer 0 of the readout copy: the incoming state from this wave's state tiles
   // (per-row decay: pre-scaled by e^{-A CD_end / 2} of the first chunk)
   {
-    const float hc0 = 0.5f * sMisc[c0 & 3][0];
+    const float hc0 = 0.5f * sMisc[c0 & 3][0], hn0 = 0.5f * sMisc[c0 & 3][2];
 #pragma unroll
     for (int k = 0; k < S::ST_PER_WAVE; ++k) {
       const int tile = wave * S::ST_PER_WAVE + k;
       if (tile < S::ST_TILES) {
         const int n = 16 * (tile / S::TP) + (lane & 15), pl = 16 * (tile % S::TP) + 4 * (lane >> 4);
-        const float sc0 = COORD ? __expf(-sRate[n] * hc0) : 1.f;
+        const float sc0 = COORD ? __expf(-sRate[n] * hc0 - sRateS[n] * hn0) : 1.f;
         const float v[4] = {sc0 * st[k][0], sc0 * st[k][1], sc0 * st[k][2], sc0 * st[k][3]};
         store4<BF16>(sST + n * VS + pl, v);
       }
@@ -675,8 +693,9 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
       // state tiles of this wave: wave * ST_PER_WAVE + k, so a wave's tiles share
       // their n-block whenever TP is a multiple of ST_PER_WAVE (one key fragment
       // then serves all of them)
-      const float cdend = sMisc[sc][0];
+      const float cdend = sMisc[sc][0], nvend = sMisc[sc][2];
       const float cdnext = c + 1 < c1 ? sMisc[(c + 1) & 3][0] : 0.f;
+      const float nvnext = c + 1 < c1 ? sMisc[(c + 1) & 3][2] : 0.f;
       constexpr bool SHARE = S::TP % S::ST_PER_WAVE == 0;
       f32x4 acc[S::ST_PER_WAVE];
       float hh[S::ST_PER_WAVE];
@@ -684,7 +703,8 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
       for (int k = 0; k < S::ST_PER_WAVE; ++k) {
         const int tile = wave * S::ST_PER_WAVE + k;
         const int n = 16 * (tile / S::TP) + (lane & 15);
-        hh[k] = COORD ? __expf(-0.5f * sRate[n < N ? n : 0] * cdend) : sMisc[sc][1];
+        const int nn = n < N ? n : 0;
+        hh[k] = COORD ? __expf(-0.5f * (sRate[nn] * cdend + sRateS[nn] * nvend)) : sMisc[sc][1];
 #pragma unroll
         for (int i = 0; i < 4; ++i) acc[k][i] = st[k][i] * hh[k];
       }
@@ -717,7 +737,7 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
           if (COORD) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) acc[k][i] *= hh[k];
-            sst = __expf(-0.5f * sRate[n] * cdnext);
+            sst = __expf(-0.5f * (sRate[n] * cdnext + sRateS[n] * nvnext));
             // chunk-total rotation of the pairs: rows (n, n+1) sit in lanes (l, l^1)
             const bool pair = n >= nreal;
             float sn = 0.f, cs = 1.f;
@@ -899,6 +919,9 @@ __global__ __launch_bounds__(256) void ssm_fwd_combine(FwdParams p, int per_row)
       return m < nreal ? p.A[(size_t)h * na + m] : p.A[(size_t)h * na + nreal + ((m - nreal) >> 1)];
     };
     const float ra = rate(n), rb = rate(n + 1);
+    // static rows (n_static is even, so both rows of the pair (n, n + 1) are of one kind)
+    // decay by their rate once per token: over a range, the range's token count
+    const bool stat = per_row && n < p.n_static;
     const bool pair = per_row && n >= nreal;
     const float om = pair ? p.omega[(size_t)h * p.n_pairs + ((n - nreal) >> 1)] : 0.f;
     const size_t sb = (size_t)slice * p.nseg, sl = (size_t)slice * (p.nseg - 1) * p.nsub;
@@ -924,7 +947,12 @@ __global__ __launch_bounds__(256) void ssm_fwd_combine(FwdParams p, int per_row)
 #pragma unroll
         for (int k = 0; k < kCombineBlock; ++k) {
           if (k >= cnt) break;
-          const float dsum = ds[k];
+          float dsum = ds[k];
+          if (stat) {  // tokens of range u0 + k of segment s (ranges past the sequence end are empty)
+            const int ta = s * p.seg_tokens + (u0 + k) * p.lsub;
+            const int tb = min(min(ta + p.lsub, (s + 1) * p.seg_tokens), p.L) - 1;
+            dsum = static_cast<float>(max(tb - ta + 1, 0));
+          }
           float a2 = a * expf(-ra * dsum), b2 = bv * expf(-rb * dsum);
           if (pair) {
             float sn, cs;
@@ -1026,6 +1054,7 @@ static LocalParams local_params(const FwdParams& p) {
   l.dt = p.dt; l.A = p.A; l.omega = p.omega; l.beta = p.beta;
   l.gamma = p.gamma; l.out = p.seg_local; l.delta = p.seg_delta; l.rk = p.rin;
   l.batch = p.batch; l.L = p.L; l.H = p.H; l.G = p.G; l.P = p.P; l.n_real = p.n_real;
+  l.n_static = p.n_static;
   l.n_pairs = p.n_pairs; l.softplus = p.softplus; l.head_rates = p.head_rates;
   l.nseg = p.nseg; l.seg_tokens = p.seg_tokens; l.nsub = p.nsub; l.lsub = p.lsub;
   return l;

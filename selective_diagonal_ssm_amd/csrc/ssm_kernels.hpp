@@ -25,6 +25,7 @@ struct FwdParams {
   const void* x_prev;
   const void* B_prev;
   int batch, L, H, G, P, n_real, n_pairs, nchunks, npblk;
+  int n_static;  // the first n_static real rows decay by e^{-A} per token, whatever the step
   // ranks of the write (B, x) and of the readout (C, y); the kernel's rank R is the
   // larger, rows past a side's own rank are zero on load and dropped on store
   int rin, rout;
@@ -72,6 +73,7 @@ struct LocalParams {
   float* delta;  // [slice][nseg - 1][nsub] range summed steps
   int rk;        // rows per token of key and value (rank_in forward, rank_out adjoint)
   int batch, L, H, G, P, n_real, n_pairs, softplus, head_rates;
+  int n_static;  // static real rows (decay e^{-A} per token)
   int nseg, seg_tokens, nsub, lsub;
 };
 
@@ -113,6 +115,7 @@ struct BwdParams {
   void* dBh;
   void* dCh;
   int batch, L, H, G, P, n_real, n_pairs, nchunks;
+  int n_static;  // static real rows (decay e^{-A} per token)
   // ranks of the write (B, x, dB, dx) and of the readout (C, dy, dC); the kernels' rank
   // R is the larger, rows past a side's own rank are zero on load and dropped on store
   int rin, rout;
@@ -151,6 +154,7 @@ struct DecodeParams {
   float* state;        // [batch][nheads][N][P] fp32, read and overwritten
   void* y;             // [batch][nheads][O][P]
   int batch, H, G, P, R, O, n_real, n_pairs;
+  int n_static;  // static real rows (decay e^{-A} per token)
   int softplus, head_rates;
   int tps;  // threads per slice (64, 128 or 256); 256 / tps slices per workgroup
 };

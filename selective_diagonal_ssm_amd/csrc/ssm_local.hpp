@@ -62,7 +62,9 @@ __global__ __launch_bounds__(256) void ssm_local(LocalParams p) {
   __shared__ float sD[LM];                                   // Delta, then d (or d')
   __shared__ float sGa[TE ? LM : 1], sBe[TE ? LM : 1];
   __shared__ float sBlk[LM / 64];
-  __shared__ float sRate[COORD ? N : 1], sOm[COORD ? N / 2 + 1 : 1];
+  // per-row rates (log2 e scaled): dynamic rows in sRate (exponent rate x summed step),
+  // static rows in sRateS (exponent rate x token count); each row has one of them nonzero
+  __shared__ float sRate[COORD ? N : 1], sRateS[COORD ? N : 1], sOm[COORD ? N / 2 + 1 : 1];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int nlp = p.P / PBL, nsegl = p.nseg - 1;
@@ -88,7 +90,9 @@ __global__ __launch_bounds__(256) void ssm_local(LocalParams p) {
       if (p.head_rates) r = p.A[h];
       else if (n < nreal) r = p.A[(size_t)h * na + n];
       else r = p.A[(size_t)h * na + nreal + ((n - nreal) >> 1)];
-      sRate[n] = r * kLog2e;
+      const bool st = n < p.n_static;
+      sRate[n] = st ? 0.f : r * kLog2e;
+      sRateS[n] = st ? r * kLog2e : 0.f;
     }
     for (int k = tid; k < p.n_pairs; k += 256) sOm[k] = p.omega[(size_t)h * p.n_pairs + k];
   }
@@ -209,6 +213,10 @@ __global__ __launch_bounds__(256) void ssm_local(LocalParams p) {
       const bool h0 = i >= 0 && i < len;
       const bool h1 = TE && i + 1 < len;
       const float d0 = h0 ? sD[i] : 0.f, d1 = h1 ? sD[i + 1] : 0.f;
+      // the token counts that go with d0, d1 (static rows): tokens after i in the range
+      // (forward), tokens in (ta, ta + i] (adjoint)
+      const float n0c = h0 ? static_cast<float>(ADJ ? i : len - 1 - i) : 0.f;
+      const float n1c = h1 ? static_cast<float>(ADJ ? i + 1 : len - 2 - i) : 0.f;
       const float g0 = h0 ? (TE ? sGa[i] : 1.f) : 0.f, g1 = h1 ? sBe[i + 1] : 0.f;
       float cf[VEC], sf[VEC];  // per-row factor; pairs: (cos-part, sin-part) on both rows
       if (!COORD) {
@@ -236,9 +244,9 @@ __global__ __launch_bounds__(256) void ssm_local(LocalParams p) {
           } else {
 #pragma unroll
             for (int f = 0; f < 2; ++f) {
-              const float a = sRate[n + f];
-              float c = g0 * __builtin_amdgcn_exp2f(-a * d0);
-              if (TE) c += g1 * __builtin_amdgcn_exp2f(-a * d1);
+              const float a = sRate[n + f], as = sRateS[n + f];
+              float c = g0 * __builtin_amdgcn_exp2f(-a * d0 - as * n0c);
+              if (TE) c += g1 * __builtin_amdgcn_exp2f(-a * d1 - as * n1c);
               cf[e + f] = c; sf[e + f] = 0.f;
             }
           }

@@ -27,7 +27,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_abi_version_and_status_strings():
     lib = ssm.load()
-    assert lib.ssm_abi_version() == 5
+    assert lib.ssm_abi_version() == 6
     for s in range(0, -9, -1):
         assert lib.ssm_status_string(s)
 
@@ -53,6 +53,13 @@ def base_desc(**kw):
     (dict(dstate=48, n_real=48), -5),
     (dict(decay_mode="coord", n_real=31, n_pairs=16, dstate=63), -5),
     (dict(seqlen=-1), -2),
+    # static real rows: per-row mode only, at most n_real, an even count
+    (dict(decay_mode="coord", n_real=32, n_pairs=16, n_static=8), 0),
+    (dict(decay_mode="coord", n_real=32, n_pairs=16, n_static=32), 0),
+    (dict(decay_mode="coord", n_real=32, n_pairs=16, n_static=34), -2),
+    (dict(decay_mode="coord", n_real=32, n_pairs=16, n_static=-2), -2),
+    (dict(decay_mode="coord", n_real=32, n_pairs=16, n_static=3), -5),
+    (dict(n_static=2), -2),                     # head decay has no static rows
 ])
 def test_descriptor_validation(kw, status):
     d = _lib.make_desc(base_desc(**kw), "bf16")

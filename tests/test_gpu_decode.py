@@ -46,6 +46,11 @@ CASES = {
     "f32_hybrid_no_softplus": ("hybrid", dict(dtype="f32", dstate=32, n_real=16, n_pairs=8,
                                               headdim=16, batch=2, nheads=2, ngroups=2,
                                               dt_softplus=False, dt_mean=0.1, dt_std=0.02)),
+    # real static rows (decay e^{-A} per token whatever the step) next to dynamic rows and pairs
+    "f32_hybrid_static": ("hybrid", dict(dtype="f32", dstate=32, n_real=16, n_static=8,
+                                         n_pairs=8, headdim=16, batch=2, nheads=2, ngroups=2)),
+    "bf16_hm75_static": ("hybrid", dict(batch=2, nheads=2, ngroups=2, n_real=16, n_static=8,
+                                        n_pairs=24)),
 }
 
 

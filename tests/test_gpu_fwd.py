@@ -130,6 +130,26 @@ SMALL_CASES = {
     "bf16_te_head_steep": ("ssd_siso", dict(batch=2, seqlen=150, nheads=2, ngroups=2, dstate=64,
                                             n_real=64, two_endpoint=True, dt_mean=2.0,
                                             A_lo=16.0, A_hi=16.0, chunk=0)),
+    # real static rows (decay e^{-A} per token whatever the step) next to dynamic rows and
+    # pairs; HM-75 (three quarters of the rows in rotating pairs); static rows only; static
+    # rates large enough that every chunk is redone token by token; static rates up to 6,
+    # which put some chunks past the fold limit and leave others on the chunked path
+    "f32_hybrid_static": ("hybrid", dict(dtype="f32", dstate=32, n_real=16, n_static=8,
+                                         n_pairs=8, headdim=16, batch=2, nheads=2, ngroups=2,
+                                         seqlen=77)),
+    "f32_coord_plain_static": ("hybrid", dict(dtype="f32", two_endpoint=False, dstate=32,
+                                              n_real=16, n_static=16, n_pairs=8, headdim=16,
+                                              batch=2, nheads=2, ngroups=2, seqlen=61)),
+    "f32_hybrid_static_steep": ("hybrid", dict(dtype="f32", dstate=32, n_real=16, n_static=8,
+                                               n_pairs=8, headdim=16, batch=2, nheads=2,
+                                               ngroups=2, seqlen=77, A_static_lo=16.0,
+                                               A_static_hi=16.0)),
+    "bf16_hm75_static": ("hybrid", dict(batch=2, seqlen=150, nheads=2, ngroups=2, n_real=16,
+                                        n_static=8, n_pairs=24)),
+    "bf16_static_only": ("hybrid", dict(batch=2, seqlen=150, nheads=2, ngroups=2, n_real=64,
+                                        n_static=64, n_pairs=0)),
+    "bf16_hybrid_r1_static": ("hybrid_r1", dict(batch=2, seqlen=150, nheads=2, ngroups=2,
+                                                n_static=16, A_static_hi=6.0)),
     # head decay needs no fallback (its masks and factors are exponents <= 0): a check
     "bf16_ssd_siso_steep": ("ssd_siso", dict(batch=2, seqlen=300, nheads=2, ngroups=2,
                                              dt_mean=2.0, A_lo=16.0, A_hi=16.0)),

@@ -34,6 +34,12 @@ CASES = {
                                              seqlen=77, pair_rate_per_pair=True)),
     "bf16_hybrid_pair_rates": ("hybrid", dict(batch=2, seqlen=90, nheads=2, ngroups=2,
                                               pair_rate_per_pair=True)),
+    # real static rows next to dynamic rows and pairs
+    "f32_hybrid_static": ("hybrid", dict(dtype="f32", dstate=32, n_real=16, n_static=8,
+                                         n_pairs=8, headdim=16, batch=2, nheads=2, ngroups=2,
+                                         seqlen=77)),
+    "bf16_hm75_static": ("hybrid", dict(batch=2, seqlen=90, nheads=2, ngroups=2, n_real=16,
+                                        n_static=8, n_pairs=24)),
     # steep per-row decay (every chunk redone token by token) and a spike mix
     "f32_hybrid_steep": ("hybrid", dict(dtype="f32", dstate=32, n_real=16, n_pairs=8,
                                         headdim=16, batch=2, nheads=2, ngroups=2, seqlen=77,
@@ -134,6 +140,13 @@ SEG_CASES = {
                                   batch=1, nheads=2, ngroups=2, seqlen=333)),
     "bf16_ssd_mimo": ("ssd_mimo", dict(batch=1, seqlen=700, nheads=2, ngroups=2)),
     "bf16_hybrid": ("hybrid", dict(batch=1, seqlen=500, nheads=2, ngroups=2)),
+    # static rows: the combines decay them by the ranges' token counts
+    "f32_hybrid_static": ("hybrid", dict(dtype="f32", dstate=32, n_real=16, n_static=8,
+                                         n_pairs=8, headdim=16, batch=1, nheads=2, ngroups=2,
+                                         seqlen=333, A_static_lo=0.001, A_static_hi=0.05)),
+    "bf16_coord_plain_static": ("hybrid", dict(batch=1, seqlen=500, nheads=2, ngroups=2,
+                                               two_endpoint=False, n_static=16,
+                                               A_static_lo=0.001, A_static_hi=0.05)),
     # spikes in a few places only: segments with a steep chunk are redone token by token
     # from their combined incoming state, the others stay on the chunked path
     "bf16_hybrid_spikes": ("hybrid", dict(batch=1, seqlen=500, nheads=2, ngroups=2,
@@ -185,6 +198,8 @@ DOUBLE_CASES = {
                                   batch=1, nheads=2, ngroups=2, seqlen=501)),
     "bf16_hybrid": ("hybrid", dict(batch=1, seqlen=501, nheads=2, ngroups=2)),
     "bf16_hybrid_r1": ("hybrid_r1", dict(batch=1, seqlen=250, nheads=2, ngroups=2)),
+    "bf16_hybrid_static": ("hybrid", dict(batch=1, seqlen=501, nheads=2, ngroups=2,
+                                          n_static=16, A_static_lo=0.001, A_static_hi=0.05)),
     "bf16_hybrid_spikes": ("hybrid", dict(batch=1, seqlen=501, nheads=2, ngroups=2,
                                           dt_spike_prob=[0.0, 0.02], dt_spike_mean=3.0)),
 }
@@ -271,6 +286,8 @@ CARRY = {
                                            headdim=16, batch=1, nheads=3, ngroups=1,
                                            seqlen=333), 3),
     "bf16_segments": ("hybrid", dict(batch=1, seqlen=500, nheads=2, ngroups=2), 3),
+    "bf16_static_segments": ("hybrid", dict(batch=1, seqlen=500, nheads=2, ngroups=2,
+                                            n_static=8, A_static_lo=0.001, A_static_hi=0.05), 3),
     "f32_steep": ("hybrid", dict(dtype="f32", dstate=32, n_real=16, n_pairs=8, headdim=16,
                                  batch=2, nheads=2, ngroups=2, seqlen=77, dt_mean=2.0,
                                  A_lo=16.0, A_hi=16.0), 0),
