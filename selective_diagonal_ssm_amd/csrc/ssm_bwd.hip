@@ -448,9 +448,12 @@ struct BwdShape {
     const int c = (((16 * ti + 15) / R) * KR) / 16 + 1;
     return c < TK ? c : TK;
   }
+  // two-endpoint writes: the last key tile too, for every query tile (its last key group
+  // holds the halo row, which enters at the chunk's first token)
+  static constexpr bool extra_tile(int ti) { return TE && row_tiles(ti) < TK; }
   static constexpr int score_tiles() {
     int n = 0;
-    for (int ti = 0; ti < TQ; ++ti) n += row_tiles(ti);
+    for (int ti = 0; ti < TQ; ++ti) n += row_tiles(ti) + (extra_tile(ti) ? 1 : 0);
     return n;
   }
   static constexpr int SC_TILES = score_tiles();
@@ -498,8 +501,6 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
   __shared__ float sTT[WH][64], sSrc[WH][64];     // head: target / source inter terms per token
   __shared__ float sRS[WH][64], sCS[WH][64];      // head: row / column sums of Z o S o M
   __shared__ float sDg[WT][64], sDb[WT][64];      // per-wave dgamma / dbeta sums
-  __shared__ __align__(16) float sDX[S::TE ? 2 * (QT + 1) * R * P : 4];  // two-endpoint dX assembly
-  __shared__ __align__(16) float sDB[S::TE ? 2 * (QT + 1) * R * N : 4];  // two-endpoint dB assembly
   __shared__ __align__(16) float sTailX[S::TE ? R * P : 4], sTailB[S::TE ? R * N : 4];
   // two-endpoint tail inputs: the next chunk's raw first adjoint g', B and X of the
   // chunk's last token
@@ -753,6 +754,24 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
     }
   };
 
+  // Key rows.  Without two-endpoint writes group u (KR = R rows) holds the keys of token u.
+  // With them, group u (KR = 2R rows) holds the two rows that carry source token u's B_u and
+  // X_u: the gamma row gamma_u B_u, entering at u (rows r < R), and the beta row
+  // beta_{u+1} B_u, entering at u + 1 (rows R + r), so the gradients of B_u and X_u add
+  // lanes r and R + r of one group.  The last source's beta row enters the next chunk and
+  // is not formed here; its place holds the halo row beta_0 B_{t0-1} (source -1, entering
+  // at the chunk's first token).
+  auto key_entry = [](int j) {
+    const int u = j / KR;
+    return (!S::TE || j % KR < R) ? u : (u == QT - 1 ? 0 : u + 1);
+  };
+  auto key_src = [](int j) {
+    const int u = j / KR;
+    return (!S::TE || j % KR < R) ? u : (u == QT - 1 ? -1 : u);
+  };
+  // value of v in lane l ^ R (the other row of the same source inside a key group)
+  auto partner = [](float v) { return R == 1 ? dpp_f32<0xB1>(v) : dpp_f32<0x4E>(v); };
+
   int prev = -1;
   int item = blockIdx.x;
   if (item < nitems)
@@ -901,7 +920,8 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
       }
       *reinterpret_cast<uint4*>(sQ + row * NS + n0) = raw;
     }
-    // keys j: gamma_s B_s at (s, r) and beta_s B_{s-1} at (s, R + r)
+    // keys: gamma_s B_s in group s, beta_{s+1} B_s in group s (row R + r), the halo's beta
+    // row in the last group
   #pragma unroll
     for (int k = 0; k < BP; ++k) {
       const int v = tid + S::NTH * k;
@@ -920,7 +940,7 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
         if (e == 1 && !S::TE) break;
         const int tau = sl + e;
         if (tau < 0 || tau >= QT || (e == 0 && sl < 0)) continue;
-        const int j = tau * KR + (e ? R : 0) + r;
+        const int j = e == 0 ? sl * KR + r : (sl < 0 ? QT - 1 : sl) * KR + R + r;
         float u[VEC], kk[VEC];
   #pragma unroll
         for (int i = 0; i < VEC; ++i) u[i] = vals[i] * wv[e];
@@ -946,7 +966,8 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
       const int sl = row / R - S::TEH, r = row % R;
       if (sl >= 0) *reinterpret_cast<uint4*>(sV + (sl * KR + r) * PS + p0) = pfx[k];
       if (S::TE && sl == QT - 1) *reinterpret_cast<uint4*>(sXt1 + r * P + p0) = pfx[k];
-      if (S::TE && sl + 1 < QT) *reinterpret_cast<uint4*>(sV + ((sl + 1) * KR + R + r) * PS + p0) = pfx[k];
+      if (S::TE && sl + 1 < QT)
+        *reinterpret_cast<uint4*>(sV + ((sl < 0 ? QT - 1 : sl) * KR + R + r) * PS + p0) = pfx[k];
     }
   #pragma unroll
     for (int k = 0; k < YP; ++k) {
@@ -1131,11 +1152,13 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
       int ti = 0, tj = tile;
 #pragma unroll
       for (int a = 0; a < S::TQ - 1; ++a) {
-        if (tj >= S::row_tiles(ti)) {
-          tj -= S::row_tiles(ti);
+        const int rt = S::row_tiles(ti) + (S::extra_tile(ti) ? 1 : 0);
+        if (tj >= rt) {
+          tj -= rt;
           ++ti;
         }
       }
+      if (tj == S::row_tiles(ti)) tj = S::TK - 1;  // the halo's tile
       f32x4 sc = {0.f, 0.f, 0.f, 0.f}, z = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kk = 0; kk < S::NC / 32; ++kk) {
@@ -1155,7 +1178,7 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
       float smv[4], zmv[4], wv[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int s = (j0 + i) / KR;
+        const int s = key_entry(j0 + i);
         // masked by selection: with per-row decay the folded product of a masked entry
         // (s > t) can overflow, and inf * 0 would be NaN
         const bool causal = s <= t;
@@ -1215,13 +1238,29 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
         }
         const int t = t0 + s;
         if (t < L && kr < rin) store4<BF16>(dxg + ((((size_t)b * L + t) * H + h) * rin + kr) * P + pl, dv);
-      } else if (kr < R) {
-        // gamma row -> X_s
-        *reinterpret_cast<float4*>(sDX + ((s + 1) * R + kr) * P + pl) = make_float4(dv[0], dv[1], dv[2], dv[3]);
-      } else if (s >= 1) {
-        // beta row -> X_{s-1}
-        *reinterpret_cast<float4*>(sDX + (QT + 1) * R * P + (s * R + kr - R) * P + pl) =
-            make_float4(dv[0], dv[1], dv[2], dv[3]);
+      } else {
+        // dX_s = (gamma row) + (beta row) of group s, lanes kr and kr + R; the last
+        // source's beta term comes from the next chunk's boundary adjoint (the tail), and
+        // the halo row in its place belongs to the chunk before
+        float o[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[i] = partner(dv[i]);
+        if (kr < R) {
+          if (s == QT - 1) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) o[i] = sTailX[kr * P + pl + i];
+          }
+#pragma unroll
+          for (int i = 0; i < 4; ++i) dv[i] += o[i];
+          if (p.has_D) {
+            float yv[4];
+            load4<BF16>(sY + (s * R + kr) * PS + pl, yv);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) dv[i] += Dh * yv[i];
+          }
+          const int t = t0 + s;
+          if (t < L && kr < rin) store4<BF16>(dxg + ((((size_t)b * L + t) * H + h) * rin + kr) * P + pl, dv);
+        }
       }
     };
     {
@@ -1269,13 +1308,14 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
     // and adds them to this wave's slots
     auto dk_tile = [&](const int tnn, const int tj, const f32x4& ai, const f32x4& ae, float* xpa,
                        float* xek, float* xpw, float* xekt) {
-      const int j = 16 * tj + (lane & 15), s = j / KR, kr = j % KR;
+      const int j = 16 * tj + (lane & 15), kr = j % KR;
+      const int s = key_entry(j), src = key_src(j);  // entry token, token of the B row carried
       const int n0 = 16 * tnn + 4 * (lane >> 4);
       const float cds = sTcd[s];
       const float wj = COORD ? 1.f : sTw[s];
       const bool brow = S::TE && kr >= R;
       const int rr = brow ? kr - R : kr;
-      const int tb = t0 + (brow ? s - 1 : s);  // token whose B row this key carries
+      const int tb = t0 + src;
       float tokacc = 0.f;
       float dk[4], kv[4], rpa[4], rek[4], rpw[2] = {0.f, 0.f}, rekt[2] = {0.f, 0.f};
       load4<BF16>(sK + j * NS + n0, kv);
@@ -1333,16 +1373,27 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
         {
           // the staged raw row (zero outside the sequence and for rows >= rank_in)
           float braw[4];
-          load4<BF16>(sBraw + (((brow ? s - 1 : s) + 1) * R + rr) * N + n0, braw);
+          load4<BF16>(sBraw + ((src + 1) * R + rr) * N + n0, braw);
 #pragma unroll
           for (int i = 0; i < 4; ++i) dgb += dk[i] * braw[i];
         }
+        // dB_u = gamma_u (gamma row's dK~) + beta_{u+1} (beta row's dK~), lanes kr and kr + R
+        // of group u (the last source's beta term: the tail)
+        float db[4], o[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          db[i] = wgt * dk[i];
+          o[i] = partner(db[i]);
+        }
         if (!brow) {
-          *reinterpret_cast<float4*>(sDB + ((s + 1) * R + rr) * N + n0) =
-              make_float4(wgt * dk[0], wgt * dk[1], wgt * dk[2], wgt * dk[3]);
-        } else if (s >= 1) {
-          *reinterpret_cast<float4*>(sDB + (QT + 1) * R * N + (s * R + rr) * N + n0) =
-              make_float4(wgt * dk[0], wgt * dk[1], wgt * dk[2], wgt * dk[3]);
+          const int u = j / KR;
+          if (u == QT - 1) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) o[i] = sTailB[rr * N + n0 + i];
+          }
+#pragma unroll
+          for (int i = 0; i < 4; ++i) db[i] += o[i];
+          if (t0 + u < L && rr < rin) store_bc(dBg, rin, b, t0 + u, part ? h : g, rr, n0, db);
         }
       } else if (tb < L && rr < rin) {
         store_bc(dBg, rin, b, tb, part ? h : g, rr, n0, dk);
@@ -1359,17 +1410,31 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
           xekt[q] += rekt[q];
         }
       }
-      // per-key sums over the 4 row groups, then over the keys of one token
+      // per-key sums over the 4 row groups, then over the keys of one entry token: a group's
+      // R gamma rows; with two-endpoint writes the beta rows of the group before (R lanes
+      // down) enter at the same token and are added there, except for the tile's last
+      // group, whose beta rows (entering at the next group's token, or the halo's at 0)
+      // are stored on their own
       tokacc = add_xor16(tokacc);
       tokacc = add_xor32(tokacc);
-      tokacc = group_sum<KR>(tokacc);
+      bool tok_store = false;
+      if constexpr (S::TE) {
+        tokacc = group_sum<R>(tokacc);
+        const float prevb = dpp_f32<0x110 + R>(tokacc);  // lane - R inside the row
+        const int l16 = lane & 15;
+        if (kr == 0 && l16 >= KR) tokacc += prevb;
+        tok_store = kr == 0 || (kr == R && l16 == 16 - R);
+      } else {
+        tokacc = group_sum<KR>(tokacc);
+        tok_store = (lane % KR) == 0;
+      }
       if (S::TE) {
         dgb = add_xor16(dgb);
         dgb = add_xor32(dgb);
         dgb = group_sum<R>(dgb);
       }
       if (lane < 16) {
-        if ((lane % KR) == 0) {
+        if (tok_store) {
           if (COORD) sTok[wave][s] += tokacc;  // weighted source contribution
           else sSrc[wave][s] += tokacc;        // K~ o dK~ (inter), unweighted
         }
@@ -1594,40 +1659,6 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
       }
     }
     __syncthreads();
-
-    // ---------------------------------------------------------------- two-endpoint assembly
-    // dX_s = B_s^T (gamma_s g_s) + B_s^T (beta_{s+1} g_{s+1}) (+ D dy_s), dB likewise;
-    // the second term of the last token comes from the next chunk's first state
-    if (S::TE) {
-      for (int i4 = tid; i4 < QT * R * P / 4; i4 += S::NTH) {
-        const int i = 4 * i4;
-        const int s = i / (R * P), rem = i % (R * P), r = rem / P, pp = rem % P;
-        const int t = t0 + s;
-        const float4 a = *reinterpret_cast<const float4*>(sDX + ((s + 1) * R + r) * P + pp);
-        const float4 e = (s + 1 < QT)
-            ? *reinterpret_cast<const float4*>(sDX + (QT + 1) * R * P + ((s + 1) * R + r) * P + pp)
-            : *reinterpret_cast<const float4*>(sTailX + r * P + pp);
-        float v[4] = {a.x + e.x, a.y + e.y, a.z + e.z, a.w + e.w};
-        if (p.has_D) {
-          float yv[4];
-          load4<BF16>(sY + (s * R + r) * PS + pp, yv);
-  #pragma unroll
-          for (int q = 0; q < 4; ++q) v[q] += Dh * yv[q];
-        }
-        if (t < L && r < rin) store4<BF16>(dxg + ((((size_t)b * L + t) * H + h) * rin + r) * P + pp, v);
-      }
-      for (int i4 = tid; i4 < QT * R * N / 4; i4 += S::NTH) {
-        const int i = 4 * i4;
-        const int s = i / (R * N), rem = i % (R * N), r = rem / N, n = rem % N;
-        const int t = t0 + s;
-        const float4 a = *reinterpret_cast<const float4*>(sDB + ((s + 1) * R + r) * N + n);
-        const float4 e = (s + 1 < QT)
-            ? *reinterpret_cast<const float4*>(sDB + (QT + 1) * R * N + ((s + 1) * R + r) * N + n)
-            : *reinterpret_cast<const float4*>(sTailB + r * N + n);
-        const float v[4] = {a.x + e.x, a.y + e.y, a.z + e.z, a.w + e.w};
-        if (t < L && r < rin) store_bc(dBg, rin, b, t, part ? h : g, r, n, v);
-      }
-    }
 
     // ---------------------------------------------------------------- step gradient
     // per-token d(loss)/d(L_t) contributions; the final-state term sits on the last
