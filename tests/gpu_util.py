@@ -32,6 +32,7 @@ def rel_l2_by_position(a, ref, period, axis=1):
 
 
 def run_fwd(prob, chunk=0, save=False):
+    chunk = chunk or prob.get("chunk", 0)  # the spec's chunk, else the library's choice
     t = workloads.to_device(prob)
     y, saved = ssm.forward(prob["desc"], prob["dtype"], t["x"], t["B"], t["C"], t["dt"], t["A"],
                            omega=t.get("omega"), beta=t.get("beta"), gamma=t.get("gamma"),
@@ -41,6 +42,7 @@ def run_fwd(prob, chunk=0, save=False):
 
 
 def run_bwd(prob, chunk=0):
+    chunk = chunk or prob.get("chunk", 0)
     y, saved, t = run_fwd(prob, chunk=chunk, save=True)
     g = ssm.backward(prob["desc"], prob["dtype"], t["x"], t["B"], t["C"], t["dy"], t["dt"],
                      t["A"], saved, omega=t.get("omega"), beta=t.get("beta"),

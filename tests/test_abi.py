@@ -85,6 +85,9 @@ def test_chunk_and_saved_bytes():
     dh = _lib.make_desc(base_desc(decay_mode="coord", n_real=32, n_pairs=16, rank_in=2,
                                   rank_out=2, two_endpoint=True), "bf16")
     assert ssm.chunk_tokens(dh) == 16
+    dh32 = _lib.make_desc(base_desc(decay_mode="coord", n_real=32, n_pairs=16, rank_in=2,
+                                    rank_out=2, two_endpoint=True), "bf16", 32)
+    assert ssm.chunk_tokens(dh32) == 32  # a chunk the caller asks for
 
 
 def test_null_pointers_rejected_before_launch():

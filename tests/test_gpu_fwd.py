@@ -231,6 +231,7 @@ def test_fwd_siso_recovery_cross_kernel():
     te["desc"] = dict(prob["desc"], two_endpoint=True)
     te["beta"] = np.zeros_like(prob["dt"])
     te["gamma"] = np.ones_like(prob["dt"])
+    te["chunk"] = 0  # the per-row kernel's own chunk
     y_coord, _, _ = run_fwd(te)
     ref, _ = oracle.fwd(prob)
     assert rel_l2(y_head, ref) <= 1e-2 and rel_l2(y_coord, ref) <= 1e-2

@@ -53,7 +53,7 @@ def _fwd(prob, t, h0=None, save=False):
     y, saved, hf = ssm.forward(prob["desc"], prob["dtype"], t["x"], t["B"], t["C"], t["dt"],
                                t["A"], omega=t.get("omega"), beta=t.get("beta"),
                                gamma=t.get("gamma"), D=t.get("D"), save_for_backward=save,
-                               h0=h0, return_final_state=True)
+                               h0=h0, return_final_state=True, chunk=prob.get("chunk", 0))
     return y, saved, hf
 
 
@@ -192,16 +192,18 @@ def test_sequence_segments_match_oracle(case, nseg, monkeypatch):
 
 
 # two-endpoint forwards without saved states walk two chunks per step; segment
-# boundaries at an even number of chunks (16 tokens each) keep that path
+# boundaries at an even number of chunks (16 tokens each, asked for) keep that path
 DOUBLE_CASES = {
     "f32_hybrid": ("hybrid", dict(dtype="f32", dstate=32, n_real=16, n_pairs=8, headdim=16,
-                                  batch=1, nheads=2, ngroups=2, seqlen=501)),
-    "bf16_hybrid": ("hybrid", dict(batch=1, seqlen=501, nheads=2, ngroups=2)),
-    "bf16_hybrid_r1": ("hybrid_r1", dict(batch=1, seqlen=250, nheads=2, ngroups=2)),
+                                  batch=1, nheads=2, ngroups=2, seqlen=501, chunk=16)),
+    "bf16_hybrid": ("hybrid", dict(batch=1, seqlen=501, nheads=2, ngroups=2, chunk=16)),
+    "bf16_hybrid_r1": ("hybrid_r1", dict(batch=1, seqlen=250, nheads=2, ngroups=2, chunk=16)),
     "bf16_hybrid_static": ("hybrid", dict(batch=1, seqlen=501, nheads=2, ngroups=2,
-                                          n_static=16, A_static_lo=0.001, A_static_hi=0.05)),
+                                          n_static=16, A_static_lo=0.001, A_static_hi=0.05,
+                                          chunk=16)),
     "bf16_hybrid_spikes": ("hybrid", dict(batch=1, seqlen=501, nheads=2, ngroups=2,
-                                          dt_spike_prob=[0.0, 0.02], dt_spike_mean=3.0)),
+                                          dt_spike_prob=[0.0, 0.02], dt_spike_mean=3.0,
+                                          chunk=16)),
 }
 
 
