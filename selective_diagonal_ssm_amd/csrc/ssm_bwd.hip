@@ -1724,35 +1724,42 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
         if (lane == 0) sPartOut[0] = v;
       }
     }
-    // parameter partials of this chunk (per-row mode)
+    // parameter partials of this chunk: with per-row decay on wave 1, beside wave 0's step
+    // gradient (both read only the per-wave sums that the dC~ barrier published, and the
+    // next item's first barrier waits for both)
     if (p.part) {
       float* dst = sPartOut;
       const int na = (COORD && !p.head_rates) ? nreal + npairs : 1;
       if (COORD) {
-        __syncthreads();
-        for (int n = tid; n < N; n += S::NTH) {
-          const float en = sE[n] + wsum<WC>(sEK, n);
-          sEK[0][n] = wsum<WC>(sPA, n) - (n < p.n_static ? nvend : cdend) * en;
-        }
-        __syncthreads();
-        if (p.head_rates) {
-          if (wave == 0) {
+        if (wave == 1) {
+          // row n = n0 + lane; a pair's two rows sit in lanes (l, l ^ 1) (n_real is even)
+          float hsum = 0.f;
+          for (int n0 = 0; n0 < N; n0 += kWave) {
+            const int n = n0 + lane;
             float v = 0.f;
-            for (int n = lane; n < N; n += kWave) v += sEK[0][n];
-            v = wave_sum(v);
-            if (lane == 0) dst[0] = v;
+            if (n < N) {
+              const float en = sE[n] + wsum<WC>(sEK, n);
+              v = wsum<WC>(sPA, n) - (n < p.n_static ? nvend : cdend) * en;
+            }
+            const float other = swap_adjacent_lanes(v);
+            if (p.head_rates) hsum += v;
+            else if (n < nreal) dst[n] = v;
+            else if (n < N && ((n - nreal) & 1) == 0) dst[nreal + ((n - nreal) >> 1)] = v + other;
           }
-        } else {
-          for (int n = tid; n < nreal; n += S::NTH) dst[n] = sEK[0][n];
-          for (int k = tid; k < npairs; k += S::NTH) {
-            const int n = nreal + 2 * k;
-            dst[nreal + k] = sEK[0][n] + sEK[0][n + 1];
-            const float et = sEth[k] + wsum<WC>(sEKth, k);
-            dst[na + k] = wsum<WC>(sPW, k) + cdend * et;
+          if (p.head_rates) {
+            hsum = wave_sum(hsum);
+            if (lane == 0) dst[0] = hsum;
+          } else {
+            for (int k = lane; k < npairs; k += kWave) {
+              const float et = sEth[k] + wsum<WC>(sEKth, k);
+              dst[na + k] = wsum<WC>(sPW, k) + cdend * et;
+            }
           }
+          if (lane == 0) dst[na + npairs] = wsum1<NW>(sMisc);
         }
+      } else if (tid == 0) {
+        dst[na + npairs] = wsum1<NW>(sMisc);
       }
-      if (tid == 0) dst[na + npairs] = wsum1<NW>(sMisc);
     }
     prev = item;
   }  // items
