@@ -441,19 +441,28 @@ def run_decode(args):
         step()
     torch.cuda.synchronize()
     mk = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
-    ev = [[mk(), mk()] for _ in range(args.steps)]
-    start, end = mk(), mk()
+    # a state of a few hundred MB fits the 256 MB Infinity Cache partly: unless --no-flush,
+    # 1 GiB of scratch is written between steps, outside their events
+    scratch = (None if args.no_flush else
+               torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device=state.device))
+
+    def timed(n, flush):
+        ev = [[mk(), mk()] for _ in range(n)]
+        for k in range(n):
+            if flush and scratch is not None:
+                scratch.fill_(float(k))
+            ev[k][0].record(stream)
+            step()
+            ev[k][1].record(stream)
+        torch.cuda.synchronize()
+        return [a.elapsed_time(b) for a, b in ev]
+
+    warm = timed(min(args.steps, 10), False)
     wall0 = time.perf_counter()
-    start.record(stream)
-    for k in range(args.steps):
-        ev[k][0].record(stream)
-        step()
-        ev[k][1].record(stream)
-    end.record(stream)
-    torch.cuda.synchronize()
+    per_step = timed(args.steps, True)
     wall = time.perf_counter() - wall0
-    ms_per_step = start.elapsed_time(end) / args.steps
-    kms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    ms_per_step = float(np.median(per_step))
+    kms = ms_per_step
     io_bytes = 2 if io == "bf16" else 4
     abytes = decode_bytes(dd, io_bytes)
     achieved = abytes / (kms * 1e-3) / 1e9
@@ -475,6 +484,12 @@ def run_decode(args):
                    "rank": d["rank_in"], "decay": d["decay_mode"], "n_pairs": d["n_pairs"],
                    "two_endpoint": te, "step": "one token per (batch, head) slice"},
         "roofline": roofline, "cpu_baseline": cpu, "breakdown": {"wall_s": round(wall, 3)},
+        "timing": {"statistic": "median over the timed steps",
+                   "flush_bytes_between_steps": 0 if args.no_flush else FLUSH_BYTES,
+                   "step_ms_p10": round(float(np.percentile(per_step, 10)), 5),
+                   "step_ms_p90": round(float(np.percentile(per_step, 90)), 5),
+                   "warm_cache_step_ms_median": round(float(np.median(warm)), 5),
+                   "state_bytes": int(state.numel() * 4)},
     }
     print(json.dumps(out), flush=True)
 

@@ -728,7 +728,8 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
         if (p.dbeta) p.dbeta[idx] = o_db;
       }
     }
-    if (p.part)
+    // (per-row decay: wave 1 stores the partials itself at the end of the item)
+    if (p.part && !COORD)
       for (int k = tid; k < p.npart; k += S::NTH) p.part[((size_t)slice * nch + c) * p.npart + k] = sPartOut[k];
   };
 
@@ -798,15 +799,6 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
         sRateS[tid] = st ? pf_rate : 0.f;
       }
       else if (tid < N + npairs) sOmega[tid - N] = pf_rate;
-    }
-    if (!RELAXED) {
-      for (int i = tid; i < WC * 64; i += S::NTH) (&sTok[0][0])[i] = 0.f;
-      for (int i = tid; i < WH * 64; i += S::NTH) {
-        (&sTT[0][0])[i] = 0.f; (&sSrc[0][0])[i] = 0.f; (&sRS[0][0])[i] = 0.f; (&sCS[0][0])[i] = 0.f;
-      }
-      for (int i = tid; i < WT * 64; i += S::NTH) { (&sDg[0][0])[i] = 0.f; (&sDb[0][0])[i] = 0.f; }
-      for (int i = tid; i < WC * NCO; i += S::NTH) { (&sEK[0][0])[i] = 0.f; (&sPA[0][0])[i] = 0.f; }
-      for (int i = tid; i < WC * PCO; i += S::NTH) { (&sEKth[0][0])[i] = 0.f; (&sPW[0][0])[i] = 0.f; }
     }
     if (COORD) __syncthreads();  // rates and pair frequencies before the staging reads them
     const float Ah = COORD ? 0.f : p.A[h];
@@ -1046,9 +1038,16 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
       for (int part = 0; part < 4; ++part) prefetch(nxt, part);
     if (prev >= 0) flush_scalars(prev);
     __syncthreads();
+    // this wave's own slots of the per-wave sums (only it accumulates into them; the previous
+    // item's tail, which reads every wave's, ended before the staging barrier)
     if (RELAXED) {
-      // this wave's own per-token sums (only it accumulates into them)
       sTT[wave][lane] = 0.f; sSrc[wave][lane] = 0.f; sRS[wave][lane] = 0.f; sCS[wave][lane] = 0.f;
+    }
+    if (COORD) {
+      sTok[wave][lane] = 0.f;
+      for (int n = lane; n < NCO; n += kWave) { sEK[wave][n] = 0.f; sPA[wave][n] = 0.f; }
+      for (int k = lane; k < PCO; k += kWave) { sEKth[wave][k] = 0.f; sPW[wave][k] = 0.f; }
+      if (S::TE) { sDg[wave][lane] = 0.f; sDb[wave][lane] = 0.f; }
     }
     // two-endpoint tails of the last token from the staged rows: beta_{t0'} B_{t1}^T g'
     // and g' X_{t1}^T (zero without a next chunk, where g' and beta_{t0'} are zero),
@@ -1726,11 +1725,11 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
     }
     // parameter partials of this chunk: with per-row decay on wave 1, beside wave 0's step
     // gradient (both read only the per-wave sums that the dC~ barrier published, and the
-    // next item's first barrier waits for both)
+    // next item's first barrier waits for both), stored straight to the workspace
     if (p.part) {
-      float* dst = sPartOut;
       const int na = (COORD && !p.head_rates) ? nreal + npairs : 1;
       if (COORD) {
+        float* dst = p.part + ((size_t)slice * nch + c) * p.npart;
         if (wave == 1) {
           // row n = n0 + lane; a pair's two rows sit in lanes (l, l ^ 1) (n_real is even)
           float hsum = 0.f;
@@ -1758,7 +1757,7 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
           if (lane == 0) dst[na + npairs] = wsum1<NW>(sMisc);
         }
       } else if (tid == 0) {
-        dst[na + npairs] = wsum1<NW>(sMisc);
+        sPartOut[na + npairs] = wsum1<NW>(sMisc);
       }
     }
     prev = item;
