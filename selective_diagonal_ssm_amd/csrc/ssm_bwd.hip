@@ -598,7 +598,7 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
   };
   Raw4 zr4;
   if constexpr (BF16) zr4 = make_uint2(0, 0); else zr4 = make_float4(0.f, 0.f, 0.f, 0.f);
-  float pf_dt = 0.f, pf_be = 0.f, pf_ga = 0.f, pf_dtn = 0.f, pf_bn = 0.f;
+  float pf_dt = 0.f, pf_be = 0.f, pf_ga = 0.f, pf_dtn = 0.f, pf_bn = 0.f, pf_D = 0.f;
   // per-row decay: the item's rate of row tid (tid < N) or frequency of pair tid - N
   float pf_rate = 0.f;
   const uint4 zero4 = make_uint4(0, 0, 0, 0);
@@ -701,6 +701,10 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
       pf_dt = p.dt[idx];
       if (S::TE) { pf_be = p.beta[idx]; pf_ga = p.gamma[idx]; }
     }
+    // the head's skip weight travels with the item's operands: a global value read later,
+    // once the next item's loads and this item's stores are in flight, would wait for all
+    // of them (one counter covers vector-memory reads and writes)
+    pf_D = p.has_D ? p.D[h] : 0.f;
     pf_dtn = pf_bn = 0.f;
     if (has_next) {
       const size_t idx = ((size_t)b * L + tn) * H + h;
@@ -809,7 +813,7 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
     }
     if (COORD) __syncthreads();  // rates and pair frequencies before the staging reads them
     const float Ah = COORD ? 0.f : p.A[h];
-    const float Dh = p.has_D ? p.D[h] : 0.f;
+    const float Dh = pf_D;
 
     // ---------------------------------------------------------------- scalars
     float raw_l = 0.f, dl = 0.f, be_l = 0.f, ga_l = 1.f;
@@ -830,20 +834,16 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
     // static rows count tokens in place of the summed step: t + 1 at token t, the chunk's
     // tokens inside the sequence at its end, one for the next chunk's first token
     const float nvend = static_cast<float>(min(QT, L - t0));
-    if constexpr (COORD) {
-      // a chunk too steep for the midpoint fold is redone by the token-by-token reverse
-      // pass: the largest |rate| of the item's dynamic and static rows (lanes of wave 0
-      // hold the rates)
-      if (wave == 0 && p.wild) {
-        const bool st = lane < p.n_static;
-        const float amax = wave_max(lane < N && !st ? fabsf(pf_rate) : 0.f);
-        const float smax = wave_max(lane < N && st ? fabsf(pf_rate) : 0.f);
-        const bool steep = amax * cdend + smax * nvend > kFoldLimit;
-        if (lane == 0) {
-          p.wild[item] = steep ? 1 : 0;
-          if (steep) atomicOr(p.wild_any, 1);
-        }
-      }
+    // a chunk too steep for the midpoint fold is redone by the token-by-token reverse pass:
+    // the largest |rate| of the item's dynamic and static rows (lanes of wave 0 hold the
+    // rates).  The flag is stored after the next item's loads are issued, so that no wait
+    // for this item's operands includes it.
+    bool steep = false;
+    if (COORD && wave == 0 && p.wild) {
+      const bool st = lane < p.n_static;
+      const float amax = wave_max(lane < N && !st ? fabsf(pf_rate) : 0.f);
+      const float smax = wave_max(lane < N && st ? fabsf(pf_rate) : 0.f);
+      steep = amax * cdend + smax * nvend > kFoldLimit;
     }
     const float w_l = COORD ? 0.f : __expf(-Ah * (cdend - cd_l));   // e^{L_end - L_t}
     const float el_l = COORD ? 0.f : __expf(-Ah * cd_l);            // e^{L_t}
@@ -1044,6 +1044,10 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
     if (nxt < nitems)
       for (int part = 0; part < 4; ++part) prefetch(nxt, part);
     if (prev >= 0) flush_scalars(prev);
+    if (COORD && wave == 0 && lane == 0 && p.wild) {
+      p.wild[item] = steep ? 1 : 0;
+      if (steep) atomicOr(p.wild_any, 1);
+    }
     __syncthreads();
     // this wave's own slots of the per-wave sums (only it accumulates into them; the previous
     // item's tail, which reads every wave's, ended before the staging barrier)
