@@ -496,9 +496,10 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
   __shared__ __align__(16) T sZM[S::QOC * KS];  // (Z o M) rows (t, o)
   __shared__ __align__(16) T sGh[S::NC * PS];   // folded adjoint G~ (io dtype)
   __shared__ __align__(16) T sSh[N * PS];        // incoming state (io dtype)
-  // per-row rates: a dynamic row's in sRate (exponent rate x summed step), a static row's
-  // in sRateS (exponent rate x token count)
-  __shared__ float sRate[N], sRateS[N], sOmega[N / 2 + 1];
+  // per-row decay: the rates that multiply the summed step (zero on static rows) and the
+  // pair frequencies, by item parity (an item's step gradient reads them while the waves
+  // past the first two build the next item's)
+  __shared__ float sRate2[COORD ? 2 : 1][COORD ? N : 1], sOmega2[COORD ? 2 : 1][N / 2 + 1];
   __shared__ float sE2[2][N], sEth[N / 2 + 1];   // final-state terms per row (by item parity) / pair
   constexpr int WC = COORD ? NW : 1, WH = COORD ? 1 : NW, WT = S::TE ? NW : 1;
   constexpr int NCO = COORD ? N : 1, PCO = COORD ? N / 2 + 1 : 1;
@@ -521,6 +522,7 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
   __shared__ float sTw[64], sTel[64], sTlc[64];    // head: e^{L_end - L_t}, e^{L_t}, -A CD log2(e)
   __shared__ float sTga[S::TE ? 64 : 1], sTbe[S::TE ? 64 : 1];
   __shared__ float sMisc[NW];
+  __shared__ float sDh;  // the head's skip weight (written with the staging)
   __shared__ float sPartOut[N + N / 2 + 2];  // parameter partials of the item (stored a step later)
   // per-row decay: factor tables of the item (token t, row n), E_t = e^{-A_n (CD_t - CD_end/2)},
   // Theta_t = omega CD_t:  TQ[t] = E_t on real rows, (E_t cos, E_t sin)(Theta_t) on the rows of
@@ -599,8 +601,12 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
   Raw4 zr4;
   if constexpr (BF16) zr4 = make_uint2(0, 0); else zr4 = make_float4(0.f, 0.f, 0.f, 0.f);
   float pf_dt = 0.f, pf_be = 0.f, pf_ga = 0.f, pf_dtn = 0.f, pf_bn = 0.f, pf_D = 0.f;
-  // per-row decay: the item's rate of row tid (tid < N) or frequency of pair tid - N
-  float pf_rate = 0.f;
+  // per-row decay: the threads past the first two waves build the factor tables, each for
+  // one row pair (n, n + 1) = 2 ((tid - TT0) mod N / 2); they hold the item's rates of its
+  // two rows (a complex pair: its rate and its frequency)
+  constexpr int TT0 = 128, TTN = S::NTH - TT0;
+  static_assert(!COORD || (NW >= 4 && TTN % (N / 2) == 0), "table threads cover whole row pairs");
+  float pf_ra = 0.f, pf_rb = 0.f;
   const uint4 zero4 = make_uint4(0, 0, 0, 0);
 
   // The loads of an item, in four parts (C / B rows, X / dy rows and the per-token
@@ -711,14 +717,97 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
       pf_dtn = p.dt[idx];
       if (S::TE) pf_bn = p.beta[idx];
     }
-    if (COORD) {
-      const int na = nreal + npairs;
-      pf_rate = 0.f;
-      if (tid < N)
-        pf_rate = p.head_rates ? p.A[h]
-                  : p.A[(size_t)h * na + (tid < nreal ? tid : nreal + ((tid - nreal) >> 1))];
-      else if (tid < N + npairs)
-        pf_rate = p.omega[(size_t)h * npairs + tid - N];
+    if (COORD && tid >= TT0) {
+      // (the row index is formed per item: hoisted out of the item loop, the addresses
+      // derived from it would hold registers the item's phases need)
+      int n = 2 * ((tid - TT0) % (N / 2));
+      asm volatile("" : "+v"(n));
+      const bool pr = n >= nreal;
+      const int k = (n - nreal) >> 1;
+      const float* ah = p.A + (p.head_rates ? (size_t)h : (size_t)h * (nreal + npairs));
+      const int ia = p.head_rates ? 0 : (pr ? nreal + k : n);
+      const int ib = p.head_rates ? 0 : n + 1;
+      pf_ra = ah[ia];
+      pf_rb = pr ? p.omega[(size_t)h * npairs + k] : ah[ib];
+    }
+  };
+
+  // Per-row decay: the factor tables of item `it` and its rates into buffer `pw`, from its
+  // prefetched operands, on the threads tid >= TT0 (whole waves).  The tables have no readers
+  // left once an item's dC~ barrier is passed, so the next item's are built during the
+  // current item's tail (step gradient and parameter partials on waves 0 and 1).  The item's
+  // steep-chunk flag is stored here as well.
+  auto make_tables = [&](int it, int pw) {
+    const int ct = it % nch, t0t = ct * QT, tnt = t0t + QT;
+    float dlt = 0.f;
+    if (lane < QT && t0t + lane < L) dlt = p.softplus ? softplus_f32(pf_dt) : pf_dt;
+    const float cdt = wave_prefix_sum(dlt);
+    const float cde = read_lane(cdt, QT - 1);
+    const float nve = static_cast<float>(min(QT, L - t0t));
+    const float dnx = tnt < L ? (p.softplus ? softplus_f32(pf_dtn) : pf_dtn) : 0.f;
+    const int j = tid - TT0, n = 2 * (j % (N / 2));
+    const bool pair = n >= nreal, st0 = n < p.n_static, st1 = n + 1 < p.n_static;
+    // exponent rates of rows n, n + 1 per summed step (r) and per token (rs)
+    const float r0 = st0 ? 0.f : pf_ra, r0s = st0 ? pf_ra : 0.f;
+    const float r1 = pair ? pf_ra : (st1 ? 0.f : pf_rb), r1s = (pair || !st1) ? 0.f : pf_rb;
+    const float om = pair ? pf_rb : 0.f;
+    const float hc = 0.5f * cde, hn = 0.5f * nve;
+    // TQ[t] = E_t (times the pair's turn), TK[t] = 1 / E_t likewise, with
+    // E_t = e^{-A_n (CD_t - CD_end / 2)} (static rows: token counts for the summed steps)
+    constexpr int TE_N = QT * (N / 2);
+#pragma unroll
+    for (int i0 = 0; i0 < TE_N; i0 += TTN) {
+      const int i = i0 + j;
+      const int t = (i < TE_N ? i : 0) / (N / 2);
+      const float cd = __shfl(cdt, t, kWave);  // (the shuffle runs on whole waves)
+      if (i < TE_N) {
+        float2 q, k;
+        if (pair) {
+          const float x = r0 * (cd - hc);
+          const float e = __expf(-x), ei = __expf(x);
+          float sn, cs;
+          fast_sincos(om * cd, &sn, &cs);
+          q = make_float2(e * cs, e * sn);
+          k = make_float2(ei * cs, ei * sn);
+        } else {
+          const float cn = static_cast<float>(t + 1) - hn;
+          const float x0 = r0 * (cd - hc) + r0s * cn;
+          const float x1 = r1 * (cd - hc) + r1s * cn;
+          q = make_float2(__expf(-x0), __expf(-x1));
+          k = make_float2(__expf(x0), __expf(x1));
+        }
+        *reinterpret_cast<float2*>(sTQ + t * N + n) = q;
+        *reinterpret_cast<float2*>(sTK + t * N + n) = k;
+      }
+    }
+    // per row: Er = e^{-A_n CD_end / 2}, Fd = e^{-A_n Dnext}; per pair the turn
+    // (cos, sin)(omega (CD_end + Dnext)); the rates of the item
+    if (j < N / 2) {
+      const float nx = tnt < L ? 1.f : 0.f;
+      sEr[n] = __expf(-r0 * hc - r0s * hn);
+      sEr[n + 1] = __expf(-r1 * hc - r1s * hn);
+      sFd[n] = __expf(-r0 * dnx - r0s * nx);
+      sFd[n + 1] = __expf(-r1 * dnx - r1s * nx);
+      sRate2[pw][n] = r0;
+      sRate2[pw][n + 1] = r1;
+      if (pair) {
+        float sn, cs;
+        fast_sincos(om * (cde + dnx), &sn, &cs);
+        sTurn[(n - nreal) >> 1] = make_float2(cs, sn);
+        sOmega2[pw][(n - nreal) >> 1] = om;
+      }
+    }
+    // a chunk too steep for the midpoint fold is redone by the token-by-token reverse pass:
+    // the largest |rate| of its dynamic and of its static rows
+    if (p.wild && j < kWave) {
+      const bool own = j < N / 2;
+      const float amax = wave_max(own ? fmaxf(fabsf(r0), fabsf(r1)) : 0.f);
+      const float smax = wave_max(own ? fmaxf(fabsf(r0s), fabsf(r1s)) : 0.f);
+      const bool steep = amax * cde + smax * nve > kFoldLimit;
+      if (j == 0) {
+        p.wild[it] = steep ? 1 : 0;
+        if (steep) atomicOr(p.wild_any, 1);
+      }
     }
   };
 
@@ -786,8 +875,11 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
 
   int prev = -1;
   int item = blockIdx.x;
-  if (item < nitems)
+  if (item < nitems) {
+#pragma unroll
     for (int part = 0; part < 4; ++part) prefetch(item, part);
+    if (COORD && tid >= TT0) make_tables(item, 0);
+  }
   // Plain head decay: wave 0's step-gradient tail of an item reads only per-wave sums
   // (zeroed by their own wave after the staging barrier) and the final-state terms
   // (double-buffered by item parity), so the other waves go on with the next item's
@@ -801,19 +893,12 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
     const bool has_next = tn < L;
     float* sE = sE2[par];
 
-    if (!RELAXED) __syncthreads();  // the previous item is done with every shared buffer
-    if (COORD) {
-      // rates and pair frequencies arrived with the item's prefetched operands
-      if (tid < N) {
-        const bool st = tid < p.n_static;
-        sRate[tid] = st ? 0.f : pf_rate;
-        sRateS[tid] = st ? pf_rate : 0.f;
-      }
-      else if (tid < N + npairs) sOmega[tid - N] = pf_rate;
-    }
-    if (COORD) __syncthreads();  // rates and pair frequencies before the staging reads them
+    // the previous item is done with every shared buffer (and, per-row decay, its tail has
+    // built this item's factor tables and rates)
+    if (!RELAXED) __syncthreads();
+    const float* sRate = sRate2[COORD ? par : 0];
+    const float* sOmega = sOmega2[COORD ? par : 0];
     const float Ah = COORD ? 0.f : p.A[h];
-    const float Dh = pf_D;
 
     // ---------------------------------------------------------------- scalars
     float raw_l = 0.f, dl = 0.f, be_l = 0.f, ga_l = 1.f;
@@ -829,22 +914,15 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
       dnext = p.softplus ? softplus_f32(pf_dtn) : pf_dtn;
       if (S::TE) bnext = pf_bn;
     }
+    // scalars read again after the next item's loads are issued are materialised here: left
+    // to the compiler, they are copied out of the prefetch registers at the end of the item,
+    // and that copy waits for every load and store in flight
+    asm volatile("" : "+v"(raw_l), "+v"(dl), "+v"(bnext));
     const float cd_l = wave_prefix_sum(dl);
     const float cdend = read_lane(cd_l, QT - 1);
     // static rows count tokens in place of the summed step: t + 1 at token t, the chunk's
     // tokens inside the sequence at its end, one for the next chunk's first token
     const float nvend = static_cast<float>(min(QT, L - t0));
-    // a chunk too steep for the midpoint fold is redone by the token-by-token reverse pass:
-    // the largest |rate| of the item's dynamic and static rows (lanes of wave 0 hold the
-    // rates).  The flag is stored after the next item's loads are issued, so that no wait
-    // for this item's operands includes it.
-    bool steep = false;
-    if (COORD && wave == 0 && p.wild) {
-      const bool st = lane < p.n_static;
-      const float amax = wave_max(lane < N && !st ? fabsf(pf_rate) : 0.f);
-      const float smax = wave_max(lane < N && st ? fabsf(pf_rate) : 0.f);
-      steep = amax * cdend + smax * nvend > kFoldLimit;
-    }
     const float w_l = COORD ? 0.f : __expf(-Ah * (cdend - cd_l));   // e^{L_end - L_t}
     const float el_l = COORD ? 0.f : __expf(-Ah * cd_l);            // e^{L_t}
     if (wave == 0 && lane < QT) {
@@ -859,47 +937,6 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
         sTbe[lane] = be_l;
       }
     }
-    if constexpr (COORD) {
-      // factor tables (one entry pair per thread; the shuffle runs on whole waves)
-      const float hc = 0.5f * cdend, hn = 0.5f * nvend;
-      constexpr int TE_N = QT * (N / 2);
-#pragma unroll
-      for (int i0 = 0; i0 < TE_N; i0 += S::NTH) {
-        const int i = i0 + tid;
-        const int t = (i < TE_N ? i : 0) / (N / 2), n = 2 * (i % (N / 2));
-        const float cd = __shfl(cd_l, t, kWave);
-        if (i < TE_N) {
-          float2 q, k;
-          if (n >= nreal) {
-            const float x = sRate[n] * (cd - hc);
-            const float e = __expf(-x), ei = __expf(x);
-            float sn, cs;
-            fast_sincos(sOmega[(n - nreal) >> 1] * cd, &sn, &cs);
-            q = make_float2(e * cs, e * sn);
-            k = make_float2(ei * cs, ei * sn);
-          } else {
-            const float cn = static_cast<float>(t + 1) - hn;
-            const float x0 = sRate[n] * (cd - hc) + sRateS[n] * cn;
-            const float x1 = sRate[n + 1] * (cd - hc) + sRateS[n + 1] * cn;
-            q = make_float2(__expf(-x0), __expf(-x1));
-            k = make_float2(__expf(x0), __expf(x1));
-          }
-          *reinterpret_cast<float2*>(sTQ + t * N + n) = q;
-          *reinterpret_cast<float2*>(sTK + t * N + n) = k;
-        }
-      }
-      for (int n = tid; n < N; n += S::NTH) {
-        sEr[n] = __expf(-sRate[n] * hc - sRateS[n] * hn);
-        sFd[n] = __expf(-sRate[n] * dnext - (has_next ? sRateS[n] : 0.f));
-        if (n >= nreal && ((n - nreal) & 1) == 0) {
-          float sn, cs;
-          fast_sincos(sOmega[(n - nreal) >> 1] * (cdend + dnext), &sn, &cs);
-          sTurn[(n - nreal) >> 1] = make_float2(cs, sn);
-        }
-      }
-      __syncthreads();
-    }
-
     // ---------------------------------------------------------------- staging
     // queries (t, o)
   #pragma unroll
@@ -955,7 +992,9 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
         *reinterpret_cast<uint4*>(sK + j * NS + n0) = pack<BF16>(kk);
       }
     }
-    // values j and dy rows
+    // values j and dy rows (and the head's skip weight, from the prefetched operands: kept in
+    // a register across the item, its copy would wait for the next item's loads)
+    if (tid == 0) sDh = pf_D;
     float dDp = 0.f;
   #pragma unroll
     for (int k = 0; k < XP; ++k) {
@@ -1042,12 +1081,9 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
     // the next item's loads go out now and land while this one computes
     const int nxt = item + static_cast<int>(gridDim.x);
     if (nxt < nitems)
+#pragma unroll
       for (int part = 0; part < 4; ++part) prefetch(nxt, part);
     if (prev >= 0) flush_scalars(prev);
-    if (COORD && wave == 0 && lane == 0 && p.wild) {
-      p.wild[item] = steep ? 1 : 0;
-      if (steep) atomicOr(p.wild_any, 1);
-    }
     __syncthreads();
     // this wave's own slots of the per-wave sums (only it accumulates into them; the previous
     // item's tail, which reads every wave's, ended before the staging barrier)
@@ -1244,7 +1280,7 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
           float yv[4];
           load4<BF16>(sY + (s * R + kr) * PS + pl, yv);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) dv[i] += Dh * yv[i];
+          for (int i = 0; i < 4; ++i) dv[i] += sDh * yv[i];
         }
         const int t = t0 + s;
         if (t < L && kr < rin) store4<BF16>(dxg + ((((size_t)b * L + t) * H + h) * rin + kr) * P + pl, dv);
@@ -1266,7 +1302,7 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
             float yv[4];
             load4<BF16>(sY + (s * R + kr) * PS + pl, yv);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) dv[i] += Dh * yv[i];
+            for (int i = 0; i < 4; ++i) dv[i] += sDh * yv[i];
           }
           const int t = t0 + s;
           if (t < L && kr < rin) store4<BF16>(dxg + ((((size_t)b * L + t) * H + h) * rin + kr) * P + pl, dv);
@@ -1752,9 +1788,13 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
               v = wsum<WC>(sPA, n) - (n < p.n_static ? nvend : cdend) * en;
             }
             const float other = swap_adjacent_lanes(v);
+            // slot of row n (a pair's first row: the pair's); formed here each item (hoisted
+            // out of the item loop, the compiler keeps it in a spilled register)
+            int slot = n < nreal ? n : nreal + ((n - nreal) >> 1);
+            asm volatile("" : "+v"(slot));
             if (p.head_rates) hsum += v;
-            else if (n < nreal) dst[n] = v;
-            else if (n < N && ((n - nreal) & 1) == 0) dst[nreal + ((n - nreal) >> 1)] = v + other;
+            else if (n < nreal) dst[slot] = v;
+            else if (n < N && ((n - nreal) & 1) == 0) dst[slot] = v + other;
           }
           if (p.head_rates) {
             hsum = wave_sum(hsum);
@@ -1771,6 +1811,7 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
         sPartOut[na + npairs] = wsum1<NW>(sMisc);
       }
     }
+    if (COORD && tid >= TT0 && nxt < nitems) make_tables(nxt, par ^ 1);
     prev = item;
   }  // items
   __syncthreads();
