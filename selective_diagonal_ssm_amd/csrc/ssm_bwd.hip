@@ -1536,6 +1536,9 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
       if (COORD) zero_rows();
       for (int blk = wave; blk < NBN * NBJ; blk += NW) {
         const int tn0 = (COORD ? blk % NBN : blk / NBJ) * BN, tj0 = (COORD ? blk / NBN : blk % NBJ) * BJ;
+        // key tiles of the block: per-row decay takes tiles NBJ apart, so that a wave holds
+        // an early and a late key tile (the late ones carry the tails: more work)
+        auto ktile = [&](int y) { return COORD ? blk / NBN + y * NBJ : tj0 + y; };
         f32x4 ai[BN][BJ], ae[BN][BJ];
 #pragma unroll
         for (int x = 0; x < BN; ++x)
@@ -1547,7 +1550,7 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
 #pragma unroll
           for (int x = 0; x < BN; ++x) a[x] = load_frag_tr<BF16>(sQ + (kk * 32) * NS + 16 * (tn0 + x), NS);
 #pragma unroll
-          for (int y = 0; y < BJ; ++y) bz[y] = load_frag_tr<BF16>(sZM + (kk * 32) * KS + 16 * (tj0 + y), KS);
+          for (int y = 0; y < BJ; ++y) bz[y] = load_frag_tr<BF16>(sZM + (kk * 32) * KS + 16 * ktile(y), KS);
 #pragma unroll
           for (int x = 0; x < BN; ++x)
 #pragma unroll
@@ -1558,7 +1561,7 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
           Frag<BF16> bv[BJ], ah[BN];
 #pragma unroll
           for (int y = 0; y < BJ; ++y)
-            bv[y] = load_frag<BF16>(sV + (16 * (tj0 + y) + (lane & 15)) * PS + kk * 32 + 8 * (lane >> 4));
+            bv[y] = load_frag<BF16>(sV + (16 * ktile(y) + (lane & 15)) * PS + kk * 32 + 8 * (lane >> 4));
 #pragma unroll
           for (int x = 0; x < BN; ++x) {
             ah[x] = load_frag<BF16>(sGh + (16 * (tn0 + x) + (lane & 15)) * PS + kk * 32 + 8 * (lane >> 4));
@@ -1573,7 +1576,7 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
 #pragma unroll
         for (int x = 0; x < BN; ++x)
 #pragma unroll
-          for (int y = 0; y < BJ; ++y) dk_tile(tn0 + x, tj0 + y, ai[x][y], ae[x][y], apa[x], aek[x], apw[x], aekt[x]);
+          for (int y = 0; y < BJ; ++y) dk_tile(tn0 + x, ktile(y), ai[x][y], ae[x][y], apa[x], aek[x], apw[x], aekt[x]);
         if (COORD && !SHARE_N) {
           flush_rows(tn0);
           zero_rows();
@@ -1662,7 +1665,13 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
     {
       constexpr int BN = S::CBLK ? 2 : 1, BQ = (S::CBLK || S::CPAIR) ? 2 : 1, NBQ = S::TQ / BQ;
       for (int blk = wave; blk < (S::TN / BN) * NBQ; blk += NW) {
-        const int tn0 = (blk / NBQ) * BN, tq0 = (blk % NBQ) * BQ;
+        // per-row decay: n-blocks interleaved from the middle (pair rows, usually the upper
+        // ones, cost more), so that the waves whose dK~ block holds real rows take pair rows
+        // here and the other way round
+        constexpr int NBC = S::TN / BN;
+        const int ib = blk / NBQ;
+        const int tn0 = (COORD && NBC % 2 == 0 ? (ib % 2 == 0 ? NBC / 2 + ib / 2 : ib / 2) : ib) * BN;
+        const int tq0 = (blk % NBQ) * BQ;
         f32x4 ai[BN][BQ], ae[BN][BQ];
 #pragma unroll
         for (int x = 0; x < BN; ++x)
