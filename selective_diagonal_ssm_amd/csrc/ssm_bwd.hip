@@ -479,8 +479,10 @@ struct BwdShape {
 
 // SPLIT: write and readout ranks differ (taken from the parameters; R is the larger);
 // otherwise both are R, known at compile time
+// (at least two waves per SIMD: 256-thread workgroups must fit two to a compute unit, so the
+// kernel keeps within 256 registers per lane)
 template <bool BF16, int N, int P, int R, int KR, int QT, bool COORD, int NTHREADS, bool SPLIT>
-__global__ __launch_bounds__(NTHREADS) void ssm_bwd_chunk(BwdParams p) {
+__global__ __launch_bounds__(NTHREADS, 2) void ssm_bwd_chunk(BwdParams p) {
   using S = BwdShape<BF16, N, P, R, KR, QT, COORD, NTHREADS>;
   constexpr int NW = S::NW;
   using T = typename S::T;
