@@ -552,9 +552,17 @@ __global__ __launch_bounds__(NTHREADS, 2) void ssm_bwd_chunk(BwdParams p) {
   const int GO = part ? H : G;  // rows per token of those buffers
   // rows per token: the side's own rank in the outputs, R in the partials
   const int rin = SPLIT ? p.rin : R, rout = SPLIT ? p.rout : R;
-  auto store_bc = [&](T* out, int rows, int bb, int t, int go, int r, int n, const float* v) {
+  // dB / dC row r of token t0 + tl of batch bb.  Head decay: a 64-bit base at the item's
+  // first token and a 32-bit offset from it (|tl| <= QT); per-row decay forms the whole
+  // 64-bit index (held across the item, the bases cost that kernel registers it lacks)
+  auto store_bc = [&](T* out, int rows, int bb, int t0_, int tl, int go, int r, int n, const float* v) {
     const int rs = part ? R : rows;
-    store4<BF16>(out + ((((size_t)bb * L + t) * GO + go) * rs + r) * N + n, v);
+    if constexpr (COORD) {
+      store4<BF16>(out + ((((size_t)bb * L + t0_ + tl) * GO + go) * rs + r) * N + n, v);
+    } else {
+      T* const base = out + (((size_t)bb * L + t0_) * GO + go) * rs * N;
+      store4<BF16>(base + ((tl * GO * rs + r) * N + n), v);
+    }
   };
 
   // zero padding rows / columns (the staging never writes them)
@@ -618,6 +626,12 @@ __global__ __launch_bounds__(NTHREADS, 2) void ssm_bwd_chunk(BwdParams p) {
     const int b = slice / H, h = slice % H, g = h / (H / G);
     const int t0 = c * QT, tn = t0 + QT;
     const bool has_next = tn < L;
+    // Rows (token t0 + tl, rank r) of the [batch][L][heads][rank][width] operands, as in
+    // store_bc: head decay adds a 32-bit offset to a 64-bit base at the item's first token
+    auto row_at = [&](const T* base, int heads, int hh, int rank, int width, int tl, int r, int col) {
+      if constexpr (COORD) return base + ((((size_t)b * L + t0 + tl) * heads + hh) * rank + r) * width + col;
+      else return base + (((size_t)b * L + t0) * heads + hh) * rank * width + ((tl * heads * rank + r) * width + col);
+    };
     if (part == 0) {
 #pragma unroll
     for (int k = 0; k < CP; ++k) {
@@ -626,7 +640,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void ssm_bwd_chunk(BwdParams p) {
       if (v < S::C_VECS) {
         const int row = v / (N / VEC), n0 = (v % (N / VEC)) * VEC;
         const int t = t0 + row / R, o = row % R;
-        if (t < L && o < rout) raw = *reinterpret_cast<const uint4*>(Cg + ((((size_t)b * L + t) * G + g) * rout + o) * N + n0);
+        if (t < L && o < rout) raw = *reinterpret_cast<const uint4*>(row_at(Cg, G, g, rout, N, row / R, o, n0));
       }
       pfc[k] = raw;
     }
@@ -637,7 +651,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void ssm_bwd_chunk(BwdParams p) {
       if (v < S::B_VECS) {
         const int row = v / (N / VEC), n0 = (v % (N / VEC)) * VEC;
         const int t = t0 + row / R - S::TEH, r = row % R;
-        if (t >= 0 && t < L && r < rin) raw = *reinterpret_cast<const uint4*>(Bg + ((((size_t)b * L + t) * G + g) * rin + r) * N + n0);
+        if (t >= 0 && t < L && r < rin) raw = *reinterpret_cast<const uint4*>(row_at(Bg, G, g, rin, N, row / R - S::TEH, r, n0));
         else if (t == -1 && r < rin && p.B_prev)  // the carried token before the sequence
           raw = *reinterpret_cast<const uint4*>(static_cast<const T*>(p.B_prev) + (((size_t)b * G + g) * rin + r) * N + n0);
       }
@@ -652,7 +666,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void ssm_bwd_chunk(BwdParams p) {
       if (v < S::X_VECS) {
         const int row = v / (P / VEC), p0 = (v % (P / VEC)) * VEC;
         const int t = t0 + row / R - S::TEH, r = row % R;
-        if (t >= 0 && t < L && r < rin) raw = *reinterpret_cast<const uint4*>(xg + ((((size_t)b * L + t) * H + h) * rin + r) * P + p0);
+        if (t >= 0 && t < L && r < rin) raw = *reinterpret_cast<const uint4*>(row_at(xg, H, h, rin, P, row / R - S::TEH, r, p0));
         else if (t == -1 && r < rin && p.x_prev)
           raw = *reinterpret_cast<const uint4*>(static_cast<const T*>(p.x_prev) + (((size_t)b * H + h) * rin + r) * P + p0);
       }
@@ -665,7 +679,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void ssm_bwd_chunk(BwdParams p) {
       if (v < S::Y_VECS) {
         const int row = v / (P / VEC), p0 = (v % (P / VEC)) * VEC;
         const int t = t0 + row / R, o = row % R;
-        if (t < L && o < rout) raw = *reinterpret_cast<const uint4*>(dyg + ((((size_t)b * L + t) * H + h) * rout + o) * P + p0);
+        if (t < L && o < rout) raw = *reinterpret_cast<const uint4*>(row_at(dyg, H, h, rout, P, row / R, o, p0));
       }
       pfy[k] = raw;
     }
@@ -705,7 +719,9 @@ __global__ __launch_bounds__(NTHREADS, 2) void ssm_bwd_chunk(BwdParams p) {
     if (part != 1) return;
     pf_dt = pf_be = pf_ga = 0.f;
     if (lane < QT && t0 + lane < L) {
-      const size_t idx = ((size_t)b * L + t0 + lane) * H + h;
+      // token t0 + lane of the head (head decay: a 64-bit base and a 32-bit offset)
+      const size_t idx = COORD ? ((size_t)b * L + t0 + lane) * H + h
+                               : ((size_t)b * L + t0) * H + h + lane * H;
       pf_dt = p.dt[idx];
       if (S::TE) { pf_be = p.beta[idx]; pf_ga = p.gamma[idx]; }
     }
@@ -823,7 +839,8 @@ __global__ __launch_bounds__(NTHREADS, 2) void ssm_bwd_chunk(BwdParams p) {
     const int b = slice / H, h = slice % H;
     const int t0 = c * QT;
     if (wave == 0 && lane < QT && t0 + lane < L) {
-      const size_t idx = ((size_t)b * L + t0 + lane) * H + h;
+      const size_t idx = COORD ? ((size_t)b * L + t0 + lane) * H + h
+                               : ((size_t)b * L + t0) * H + h + lane * H;
       p.ddt[idx] = o_ddt;
       if (S::TE) {
         if (p.dgamma) p.dgamma[idx] = o_dg;
@@ -894,6 +911,11 @@ __global__ __launch_bounds__(NTHREADS, 2) void ssm_bwd_chunk(BwdParams p) {
     const int t0 = c * QT, tn = t0 + QT;
     const bool has_next = tn < L;
     float* sE = sE2[par];
+    // row (token t0 + s, rank kr) of dx, addressed like the dB / dC rows (store_bc)
+    auto dx_row = [&](int s, int kr, int col) {
+      if constexpr (COORD) return dxg + ((((size_t)b * L + t0 + s) * H + h) * rin + kr) * P + col;
+      else return dxg + (((size_t)b * L + t0) * H + h) * rin * P + ((s * H * rin + kr) * P + col);
+    };
 
     // the previous item is done with every shared buffer (and, per-row decay, its tail has
     // built this item's factor tables and rates)
@@ -1285,7 +1307,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void ssm_bwd_chunk(BwdParams p) {
           for (int i = 0; i < 4; ++i) dv[i] += sDh * yv[i];
         }
         const int t = t0 + s;
-        if (t < L && kr < rin) store4<BF16>(dxg + ((((size_t)b * L + t) * H + h) * rin + kr) * P + pl, dv);
+        if (t < L && kr < rin) store4<BF16>(dx_row(s, kr, pl), dv);
       } else {
         // dX_s = (gamma row) + (beta row) of group s, lanes kr and kr + R; the last
         // source's beta term comes from the next chunk's boundary adjoint (the tail), and
@@ -1307,7 +1329,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void ssm_bwd_chunk(BwdParams p) {
             for (int i = 0; i < 4; ++i) dv[i] += sDh * yv[i];
           }
           const int t = t0 + s;
-          if (t < L && kr < rin) store4<BF16>(dxg + ((((size_t)b * L + t) * H + h) * rin + kr) * P + pl, dv);
+          if (t < L && kr < rin) store4<BF16>(dx_row(s, kr, pl), dv);
         }
       }
     };
@@ -1441,10 +1463,10 @@ __global__ __launch_bounds__(NTHREADS, 2) void ssm_bwd_chunk(BwdParams p) {
           }
 #pragma unroll
           for (int i = 0; i < 4; ++i) db[i] += o[i];
-          if (t0 + u < L && rr < rin) store_bc(dBg, rin, b, t0 + u, part ? h : g, rr, n0, db);
+          if (t0 + u < L && rr < rin) store_bc(dBg, rin, b, t0, u, part ? h : g, rr, n0, db);
         }
       } else if (tb < L && rr < rin) {
-        store_bc(dBg, rin, b, tb, part ? h : g, rr, n0, dk);
+        store_bc(dBg, rin, b, t0, src, part ? h : g, rr, n0, dk);
       }
       if (COORD) {
 #pragma unroll
@@ -1641,7 +1663,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void ssm_bwd_chunk(BwdParams p) {
           }
         }
       }
-      if (tg < L && o < rout) store_bc(dCg, rout, b, tg, part ? h : g, o, n0, dc);
+      if (tg < L && o < rout) store_bc(dCg, rout, b, t0, t, part ? h : g, o, n0, dc);
       if (COORD) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) rpa[i] = group_sum<16>(rpa[i]);
