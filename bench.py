@@ -80,6 +80,28 @@ def measured_traffic(kernel: str, workload: str, mode: str):
     return int(v) if v else None
 
 
+def decode_source_hash() -> str:
+    p = os.path.join(ROOT, "selective_diagonal_ssm_amd", "csrc", "ssm_decode.hip")
+    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16] if os.path.exists(p) else ""
+
+
+def measured_decode_traffic(workload: str):
+    """HBM bytes per recurrent step from the committed rocprofv3 summary of that workload,
+    only if it was taken on the current recurrent-step source; else None."""
+    path = os.path.join(ROOT, "profiles", f"kernels_{workload}_decode.md")
+    if not os.path.exists(path):
+        return None
+    rec = {}
+    for line in open(path):
+        if ":" in line and line.startswith(("decode_kernel_hash", "traffic_bytes_per_launch")):
+            k, v = line.split(":", 1)
+            rec[k.strip()] = v.strip()
+    if rec.get("decode_kernel_hash") != decode_source_hash():
+        return None
+    v = rec.get("traffic_bytes_per_launch ssm_decode_kernel")
+    return int(v) if v else None
+
+
 def decode_bytes(desc: dict, io_bytes: int) -> int:
     """Compulsory HBM bytes of one recurrent step over all slices: the fp32 state
     read and written once, plus x, x_prev, y, B, B_prev, C and the per-slice scalars."""
@@ -468,7 +490,8 @@ def run_decode(args):
     achieved = abytes / (kms * 1e-3) / 1e9
     value = d["batch"] / (ms_per_step * 1e-3) / 1e6
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": measured_decode_traffic(args.workload),
                 "kernel": "ssm_decode_kernel", "algorithmic_bytes_per_launch": abytes,
                 "avg_launch_ms": round(kms, 4)}
     cpu = None
