@@ -81,6 +81,10 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_adjoint(BwdParams p) {
   // per-row rates: a dynamic row's in sRate (exponent rate x summed step), a static row's
   // in sRateS (exponent rate x token count)
   __shared__ float sRate[N], sRateS[N], sOmega[N / 2 + 1];
+  // per-token scalars of chunk c in slot c & 1, formed by the last wave a chunk ahead: the
+  // summed step over (t0, t] of each token, and over (t0, t0'] (to the next chunk's first
+  // token) with the static rows' transition count
+  __shared__ float sCdx[2][64], sCend[2][2];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   // the chunk-gradient kernel that follows sets this word when a chunk is too steep for
@@ -150,9 +154,8 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_adjoint(BwdParams p) {
       }
     }
   }
-  // register prefetch of one chunk's C rows, dy rows and steps
+  // register prefetch of one chunk's C rows and dy rows
   uint4 pc[S::C_PER], py[S::Y_PER];
-  float pdt = 0.f;
   auto prefetch = [&](int c) {
     const int t0 = c * QT;
 #pragma unroll
@@ -179,36 +182,59 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_adjoint(BwdParams p) {
       }
       py[k] = raw;
     }
-    pdt = 0.f;
-    if (lane < QT && t0 + lane < L) pdt = p.dt[((size_t)b * L + t0 + lane) * H + h];
   };
 
-  float dnext = 0.f;  // step of the first token of the chunk after the current one
-  if (c1 < nch) {
-    const float raw = p.dt[((size_t)b * L + c1 * QT) * H + h];
-    dnext = p.softplus ? softplus_f32(raw) : raw;
-  }
-  prefetch(c1 - 1);
-  for (int c = c1 - 1; c >= c0; --c) {
+  // The per-token scalars are formed once, by the last wave (SW), a chunk ahead: for chunk c
+  // during chunk c + 1's staging, from steps read a chunk before that (held in sdt).  The
+  // other waves only read them (the staging waves need them at once, and every wave used to
+  // form them itself, all at the same moment).
+  constexpr int SW = NW - 1;
+  float dnext = 0.f;  // wave SW: step of the first token of the chunk after the one it forms
+  auto load_dt = [&](int c) {
+    float r = 0.f;
+    if (c >= c0 && lane < QT && c * QT + lane < L) r = p.dt[((size_t)b * L + c * QT + lane) * H + h];
+    return r;
+  };
+  auto form_scalars = [&](int c, float raw) {
     const int t0 = c * QT;
-    __syncthreads();  // the previous chunk's products are done with sQ / sY
-    // step of this chunk's tokens (lane = token)
-    float dl = 0.f;
-    if (lane < QT && t0 + lane < L) dl = p.softplus ? softplus_f32(pdt) : pdt;
+    float dl = 0.f;  // step of this chunk's tokens (lane = token)
+    if (lane < QT && t0 + lane < L) dl = p.softplus ? softplus_f32(raw) : raw;
     const float cd = wave_prefix_sum(dl);
     const float cdx = cd - read_lane(dl, 0);               // sum over (t0, t]
     const float cdx_end = read_lane(cdx, QT - 1) + dnext;  // sum over (t0, t0']
     dnext = read_lane(dl, 0);
-    // static rows count the transitions instead: t - t0 over (t0, t], and over (t0, t0']
-    // the chunk's tokens after the first plus the next chunk's first token
-    const float cnx_end = static_cast<float>(min(QT, L - t0) - 1 + (t0 + QT < L ? 1 : 0));
+    if (lane < QT) sCdx[c & 1][lane] = cdx;
+    if (lane == 0) {
+      sCend[c & 1][0] = cdx_end;
+      // static rows count the transitions instead: t - t0 over (t0, t], and over (t0, t0']
+      // the chunk's tokens after the first plus the next chunk's first token
+      sCend[c & 1][1] = static_cast<float>(min(QT, L - t0) - 1 + (t0 + QT < L ? 1 : 0));
+    }
+  };
+  float sdt = 0.f;  // wave SW: raw steps of the chunk it forms next
+  if (wave == SW) {
+    if (c1 < nch) {
+      const float raw = p.dt[((size_t)b * L + c1 * QT) * H + h];
+      dnext = p.softplus ? softplus_f32(raw) : raw;
+    }
+    form_scalars(c1 - 1, load_dt(c1 - 1));
+    sdt = load_dt(c1 - 2);
+  }
+  prefetch(c1 - 1);
+  for (int c = c1 - 1; c >= c0; --c) {
+    const int t0 = c * QT;
+    __syncthreads();  // the previous chunk's products are done with sQ / sY (and this chunk's
+                      // scalars are formed)
+    if (wave == SW && c > c0) form_scalars(c - 1, sdt);
+    const float* cdxs = sCdx[c & 1];
+    const float cdx_end = sCend[c & 1][0], cnx_end = sCend[c & 1][1];
 
     // operands: rows (t, o) of  e^{L'_t} R(-Theta'_t) C_t  and  dy_t
 #pragma unroll
     for (int k = 0; k < S::C_PER; ++k) {
       const int v = tid + S::NTH * k;
       const int row = (v < S::C_VECS ? v : 0) / (N / VEC);
-      const float cdr = __shfl(cdx, row / R, kWave);
+      const float cdr = cdxs[row / R];
       const float cnr = static_cast<float>(row / R);
       if (v < S::C_VECS) {
         const int nv = v % (N / VEC), n0 = nv * VEC;
@@ -238,7 +264,7 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_adjoint(BwdParams p) {
     for (int k = 0; k < S::Y_PER; ++k) {
       const int v = (tid + S::NTH - S::Y_T0) % S::NTH + S::NTH * k;
       const int row = (v < S::Y_VECS ? v : 0) / (PB / VEC);
-      const float wr = COORD ? 1.f : __expf(-Ah * __shfl(cdx, row / R, kWave));
+      const float wr = COORD ? 1.f : __expf(-Ah * cdxs[row / R]);
       if (v < S::Y_VECS) {
         const int pv = v % (PB / VEC);
         uint4 raw = py[k];
@@ -253,6 +279,7 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_adjoint(BwdParams p) {
       }
     }
     if (c > c0) prefetch(c - 1);  // in flight during this chunk's products
+    if (wave == SW && c > c0) sdt = load_dt(c - 2);
 
     // carried adjoint: Gpre[c+1] -> Phi_{t0',t0}^T Gpre[c+1]
 #pragma unroll
