@@ -222,7 +222,6 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_adjoint(BwdParams p) {
   }
   prefetch(c1 - 1);
   for (int c = c1 - 1; c >= c0; --c) {
-    const int t0 = c * QT;
     __syncthreads();  // the previous chunk's products are done with sQ / sY (and this chunk's
                       // scalars are formed)
     if (wave == SW && c > c0) form_scalars(c - 1, sdt);
@@ -560,6 +559,10 @@ __global__ __launch_bounds__(NTHREADS, 2) void ssm_bwd_chunk(BwdParams p) {
   __shared__ __align__(16) float sTQ[COORD ? QT * N : 4], sTK[COORD ? QT * N : 4];
   __shared__ float sEr[COORD ? N : 1], sFd[COORD ? N : 1];
   __shared__ float2 sTurn[COORD ? N / 2 + 1 : 1];
+  // per-row decay: the item's per-token scalars, formed with its tables in the previous item's
+  // tail: the raw steps (wave 0's step gradient reads them at the item's end) and (CD_end,
+  // token count) (wave 1's partials), by item parity; beta of the next chunk's first token
+  __shared__ float sRaw2[COORD ? 2 : 1][COORD ? 64 : 1], sCn2[COORD ? 2 : 1][2], sBn;
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int nch = p.nchunks;
@@ -744,8 +747,10 @@ __global__ __launch_bounds__(NTHREADS, 2) void ssm_bwd_chunk(BwdParams p) {
       return;
     }
     if (part != 1) return;
+    // per-row decay: only the table waves (tid >= TT0) use the per-token scalars
+    const bool scal = !COORD || tid >= TT0;
     pf_dt = pf_be = pf_ga = 0.f;
-    if (lane < QT && t0 + lane < L) {
+    if (scal && lane < QT && t0 + lane < L) {
       // token t0 + lane of the head (head decay: a 64-bit base and a 32-bit offset)
       const size_t idx = COORD ? ((size_t)b * L + t0 + lane) * H + h
                                : ((size_t)b * L + t0) * H + h + lane * H;
@@ -757,7 +762,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void ssm_bwd_chunk(BwdParams p) {
     // of them (one counter covers vector-memory reads and writes)
     pf_D = p.has_D ? p.D[h] : 0.f;
     pf_dtn = pf_bn = 0.f;
-    if (has_next) {
+    if (scal && has_next) {
       const size_t idx = ((size_t)b * L + tn) * H + h;
       pf_dtn = p.dt[idx];
       if (S::TE) pf_bn = p.beta[idx];
@@ -791,6 +796,23 @@ __global__ __launch_bounds__(NTHREADS, 2) void ssm_bwd_chunk(BwdParams p) {
     const float nve = static_cast<float>(min(QT, L - t0t));
     const float dnx = tnt < L ? (p.softplus ? softplus_f32(pf_dtn) : pf_dtn) : 0.f;
     const int j = tid - TT0, n = 2 * (j % (N / 2));
+    if (j < kWave) {
+      // the per-token scalars of the item (its first table wave)
+      if (lane < QT) {
+        sTcd[lane] = cdt;
+        sRaw2[pw][lane] = (t0t + lane < L) ? pf_dt : 0.f;
+        if (S::TE) {
+          const bool in = t0t + lane < L;
+          sTga[lane] = in ? pf_ga : 0.f;
+          sTbe[lane] = in ? pf_be : 0.f;
+        }
+      }
+      if (lane == 0) {
+        sCn2[pw][0] = cde;
+        sCn2[pw][1] = nve;
+        if (S::TE) sBn = tnt < L ? pf_bn : 0.f;
+      }
+    }
     const bool pair = n >= nreal, st0 = n < p.n_static, st1 = n + 1 < p.n_static;
     // exponent rates of rows n, n + 1 per summed step (r) and per token (rs)
     const float r0 = st0 ? 0.f : pf_ra, r0s = st0 ? pf_ra : 0.f;
@@ -952,40 +974,30 @@ __global__ __launch_bounds__(NTHREADS, 2) void ssm_bwd_chunk(BwdParams p) {
     const float Ah = COORD ? 0.f : p.A[h];
 
     // ---------------------------------------------------------------- scalars
-    float raw_l = 0.f, dl = 0.f, be_l = 0.f, ga_l = 1.f;
-    if (lane < QT && t0 + lane < L) {
-      raw_l = pf_dt;
-      dl = p.softplus ? softplus_f32(raw_l) : raw_l;
-      if (S::TE) { be_l = pf_be; ga_l = pf_ga; }
-    } else if (S::TE) {
-      ga_l = 0.f;
-    }
-    float dnext = 0.f, bnext = 0.f;
-    if (has_next) {
-      dnext = p.softplus ? softplus_f32(pf_dtn) : pf_dtn;
-      if (S::TE) bnext = pf_bn;
-    }
-    // scalars read again after the next item's loads are issued are materialised here: left
-    // to the compiler, they are copied out of the prefetch registers at the end of the item,
-    // and that copy waits for every load and store in flight
-    asm volatile("" : "+v"(raw_l), "+v"(dl), "+v"(bnext));
-    const float cd_l = wave_prefix_sum(dl);
-    const float cdend = read_lane(cd_l, QT - 1);
-    // static rows count tokens in place of the summed step: t + 1 at token t, the chunk's
-    // tokens inside the sequence at its end, one for the next chunk's first token
-    const float nvend = static_cast<float>(min(QT, L - t0));
-    const float w_l = COORD ? 0.f : __expf(-Ah * (cdend - cd_l));   // e^{L_end - L_t}
-    const float el_l = COORD ? 0.f : __expf(-Ah * cd_l);            // e^{L_t}
-    if (wave == 0 && lane < QT) {
-      sTcd[lane] = cd_l;
-      if (!COORD) {
+    // per-row decay: formed with the tables in the previous item's tail (sTcd, sTga, sTbe,
+    // sRaw2, sCn2, sBn); head decay: formed here by every wave
+    float raw_l = 0.f, dl = 0.f;
+    float dnext = 0.f;
+    float cdend = 0.f;
+    if constexpr (!COORD) {
+      if (lane < QT && t0 + lane < L) {
+        raw_l = pf_dt;
+        dl = p.softplus ? softplus_f32(raw_l) : raw_l;
+      }
+      if (has_next) dnext = p.softplus ? softplus_f32(pf_dtn) : pf_dtn;
+      // scalars read again after the next item's loads are issued are materialised here:
+      // left to the compiler, they are copied out of the prefetch registers at the end of
+      // the item, and that copy waits for every load and store in flight
+      asm volatile("" : "+v"(raw_l), "+v"(dl));
+      const float cd_l = wave_prefix_sum(dl);
+      cdend = read_lane(cd_l, QT - 1);
+      const float w_l = __expf(-Ah * (cdend - cd_l));   // e^{L_end - L_t}
+      const float el_l = __expf(-Ah * cd_l);            // e^{L_t}
+      if (wave == 0 && lane < QT) {
+        sTcd[lane] = cd_l;
         sTw[lane] = w_l;
         sTel[lane] = el_l;
         sTlc[lane] = -Ah * 1.4426950408889634f * cd_l;
-      }
-      if (S::TE) {
-        sTga[lane] = ga_l;
-        sTbe[lane] = be_l;
       }
     }
     // ---------------------------------------------------------------- staging
@@ -1016,7 +1028,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void ssm_bwd_chunk(BwdParams p) {
       const int row = vv / (N / VEC), n0 = (vv % (N / VEC)) * VEC;
       const int sl = row / R - S::TEH, r = row % R;
       const int ta = sl < 0 ? 0 : sl, tb = sl + 1 < QT ? sl + 1 : QT - 1;
-      const float wv[2] = {S::TE ? __shfl(ga_l, ta, kWave) : 1.f, S::TE ? __shfl(be_l, tb, kWave) : 0.f};
+      const float wv[2] = {S::TE ? sTga[ta] : 1.f, S::TE ? sTbe[tb] : 0.f};
       if (v >= S::B_VECS) continue;
       if (S::TE && sl == QT - 1) *reinterpret_cast<uint4*>(sBt1 + r * N + n0) = pfb[k];
       if (S::TE) *reinterpret_cast<uint4*>(sBraw + row * N + n0) = pfb[k];
@@ -1184,7 +1196,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void ssm_bwd_chunk(BwdParams p) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int r = 4 * (lane >> 4) + i;
-            if (r < R) sTailX[r * P + 16 * tp + (lane & 15)] = bnext * acc[i];
+            if (r < R) sTailX[r * P + 16 * tp + (lane & 15)] = sBn * acc[i];
           }
         } else {
           const int tn = u - P / 16;
@@ -1197,7 +1209,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void ssm_bwd_chunk(BwdParams p) {
           // lane l: rows n = 16 tn + 4 (l >> 4) + i, column r = l & 15
           if ((lane & 15) < R) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) sTailB[(lane & 15) * N + 16 * tn + 4 * (lane >> 4) + i] = bnext * acc[i];
+            for (int i = 0; i < 4; ++i) sTailB[(lane & 15) * N + 16 * tn + 4 * (lane >> 4) + i] = sBn * acc[i];
           }
         }
       }
@@ -1223,8 +1235,8 @@ __global__ __launch_bounds__(NTHREADS, 2) void ssm_bwd_chunk(BwdParams p) {
             acc += to_f32(sGraw[n * PS + pp]) * to_f32(sXt1[r * P + pp]);
         }
         acc = group_sum<TT>(acc);
-        if (part == 0 && o < O1) sTailX[o] = bnext * acc;
-        else if (part == 0 && o < OT) sTailB[o - O1] = bnext * acc;
+        if (part == 0 && o < O1) sTailX[o] = sBn * acc;
+        else if (part == 0 && o < OT) sTailB[o - O1] = sBn * acc;
       }
     }
     if (p.has_D) {
@@ -1818,7 +1830,8 @@ __global__ __launch_bounds__(NTHREADS, 2) void ssm_bwd_chunk(BwdParams p) {
       }
       const int t = t0 + lane;
       if (lane < QT && t < L) {
-        o_ddt = p.softplus ? rev * sigmoid_f32(raw_l) : rev;
+        const float raw = COORD ? sRaw2[COORD ? par : 0][lane] : raw_l;
+        o_ddt = p.softplus ? rev * sigmoid_f32(raw) : rev;
         if (S::TE) {
           o_dg = wsum<WT>(sDg, lane);
           o_db = wsum<WT>(sDb, lane);
@@ -1845,7 +1858,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void ssm_bwd_chunk(BwdParams p) {
             float v = 0.f;
             if (n < N) {
               const float en = sE[n] + wsum<WC>(sEK, n);
-              v = wsum<WC>(sPA, n) - (n < p.n_static ? nvend : cdend) * en;
+              v = wsum<WC>(sPA, n) - (n < p.n_static ? sCn2[par][1] : sCn2[par][0]) * en;
             }
             const float other = swap_adjacent_lanes(v);
             // slot of row n (a pair's first row: the pair's); formed here each item (hoisted
@@ -1862,7 +1875,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void ssm_bwd_chunk(BwdParams p) {
           } else {
             for (int k = lane; k < npairs; k += kWave) {
               const float et = sEth[k] + wsum<WC>(sEKth, k);
-              dst[na + k] = wsum<WC>(sPW, k) + cdend * et;
+              dst[na + k] = wsum<WC>(sPW, k) + sCn2[par][0] * et;
             }
           }
           if (lane == 0) dst[na + npairs] = wsum1<NW>(sMisc);
