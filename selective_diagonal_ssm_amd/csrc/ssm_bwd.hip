@@ -824,10 +824,15 @@ __global__ __launch_bounds__(NTHREADS, 2) void ssm_bwd_chunk(BwdParams p) {
     constexpr int TE_N = QT * (N / 2);
 #pragma unroll
     for (int i0 = 0; i0 < TE_N; i0 += TTN) {
-      const int i = i0 + j;
-      const int t = (i < TE_N ? i : 0) / (N / 2);
+      // a partial last round goes to the last table threads (the first table wave also forms
+      // the per-token scalars and the per-row terms); entries stay TTN apart, so a thread's
+      // row pair is the same in every round
+      const int cnt = TE_N - i0 < TTN ? TE_N - i0 : TTN;
+      const bool ok = j >= TTN - cnt;
+      const int i = i0 + j - (TTN - cnt);
+      const int t = (ok ? i : 0) / (N / 2);
       const float cd = __shfl(cdt, t, kWave);  // (the shuffle runs on whole waves)
-      if (i < TE_N) {
+      if (ok) {
         float2 q, k;
         if (pair) {
           const float x = r0 * (cd - hc);
