@@ -85,6 +85,10 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_adjoint(BwdParams p) {
   // summed step over (t0, t] of each token, and over (t0, t0'] (to the next chunk's first
   // token) with the static rows' transition count
   __shared__ float sCdx[2][64], sCend[2][2];
+  // per-row decay: the fold of chunk c's C rows, [token][n]: e^{-A_n d'_t} on real rows,
+  // e^{-A d'_t} (cos, sin)(omega d'_t) on the rows of a pair; built by the upper half of
+  // the workgroup during chunk c + 1's products
+  __shared__ __align__(16) float sTC[COORD ? QT * N : 4];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   // the chunk-gradient kernel that follows sets this word when a chunk is too steep for
@@ -211,6 +215,24 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_adjoint(BwdParams p) {
       sCend[c & 1][1] = static_cast<float>(min(QT, L - t0) - 1 + (t0 + QT < L ? 1 : 0));
     }
   };
+  constexpr int TB0 = NTHREADS / 2;  // first thread of the fold-table builders
+  auto build_table = [&](int c) {
+    const float* cdxs = sCdx[c & 1];
+    for (int i = tid - TB0; i < QT * (N / 2); i += NTHREADS - TB0) {
+      const int t = i / (N / 2), n = 2 * (i % (N / 2));
+      const float cdr = cdxs[t], cnr = static_cast<float>(t);
+      float2 f;
+      if (n >= nreal) {
+        float sn, cs;
+        fast_sincos(sOmega[(n - nreal) >> 1] * cdr, &sn, &cs);
+        const float e = __expf(-sRate[n] * cdr);
+        f = make_float2(e * cs, e * sn);
+      } else {
+        f = make_float2(__expf(-sRate[n] * cdr - sRateS[n] * cnr), __expf(-sRate[n + 1] * cdr - sRateS[n + 1] * cnr));
+      }
+      *reinterpret_cast<float2*>(sTC + t * N + n) = f;
+    }
+  };
   float sdt = 0.f;  // wave SW: raw steps of the chunk it forms next
   if (wave == SW) {
     if (c1 < nch) {
@@ -219,6 +241,10 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_adjoint(BwdParams p) {
     }
     form_scalars(c1 - 1, load_dt(c1 - 1));
     sdt = load_dt(c1 - 2);
+  }
+  if (COORD) {
+    __syncthreads();  // the first chunk's scalars (and the rates) before its fold table
+    if (tid >= TB0) build_table(c1 - 1);
   }
   prefetch(c1 - 1);
   for (int c = c1 - 1; c >= c0; --c) {
@@ -233,27 +259,31 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_adjoint(BwdParams p) {
     for (int k = 0; k < S::C_PER; ++k) {
       const int v = tid + S::NTH * k;
       const int row = (v < S::C_VECS ? v : 0) / (N / VEC);
-      const float cdr = cdxs[row / R];
-      const float cnr = static_cast<float>(row / R);
       if (v < S::C_VECS) {
         const int nv = v % (N / VEC), n0 = nv * VEC;
         uint4 raw = pc[k];
         if (COORD) {
-          float vals[VEC];
+          // times the fold table: per-row factors, or on a pair (a, b) the product
+          // (a u0 + b u1, -b u0 + a u1)
+          float vals[VEC], f[VEC];
           unpack<BF16>(raw, vals);
+          const float* tab = sTC + (row / R) * N + n0;
 #pragma unroll
-          for (int i = 0; i < VEC; i += 2) {
-            const int n = n0 + i;
-            if (n >= nreal) {
-              float sn, cs;
-              fast_sincos(sOmega[(n - nreal) >> 1] * cdr, &sn, &cs);
-              const float a = vals[i], bb = vals[i + 1];
-              vals[i] = cs * a + sn * bb;
-              vals[i + 1] = -sn * a + cs * bb;
-            }
+          for (int i = 0; i < VEC; i += 4) {
+            const float4 w = *reinterpret_cast<const float4*>(tab + i);
+            f[i] = w.x; f[i + 1] = w.y; f[i + 2] = w.z; f[i + 3] = w.w;
           }
 #pragma unroll
-          for (int i = 0; i < VEC; ++i) vals[i] *= __expf(-sRate[n0 + i] * cdr - sRateS[n0 + i] * cnr);
+          for (int i = 0; i < VEC; i += 2) {
+            const float a = vals[i], bb = vals[i + 1];
+            if (n0 + i >= nreal) {
+              vals[i] = f[i] * a + f[i + 1] * bb;
+              vals[i + 1] = -f[i + 1] * a + f[i] * bb;
+            } else {
+              vals[i] = f[i] * a;
+              vals[i + 1] = f[i + 1] * bb;
+            }
+          }
           raw = pack<BF16>(vals);
         }
         *reinterpret_cast<uint4*>(sQ + row * NS + n0) = raw;
@@ -324,6 +354,8 @@ __global__ __launch_bounds__(NTHREADS) void ssm_bwd_adjoint(BwdParams p) {
         store4<BF16>(dst + (size_t)n * P + p0 + pl, v4);
       }
     }
+    // the next chunk's fold table (its scalars were formed during this chunk's staging)
+    if (COORD && c > c0 && tid >= TB0) build_table(c - 1);
   }
   // dLoss/dh0 = A_0^T g_0, with g_0 (the adjoint at token 0) now in st
   if (p.dh0 && seg == 0) {
