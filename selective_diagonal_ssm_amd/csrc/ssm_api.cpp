@@ -394,6 +394,8 @@ int scan_fwd_impl(const ssm_desc* d, const ssm_fwd_args* a, void* ws, size_t ws_
   p.batch = d->batch; p.L = d->seqlen; p.H = d->nheads; p.G = d->ngroups; p.P = d->headdim;
   p.n_real = d->n_real; p.n_pairs = d->n_pairs; p.nchunks = pl.nchunks;
   p.n_static = d->n_static;
+  p.save_chunk = pl.QT;
+  p.save_nchunks = pl.nchunks;
   p.npblk = d->headdim / pb;
   p.rin = d->rank_in;
   p.rout = d->rank_out;
@@ -403,12 +405,14 @@ int scan_fwd_impl(const ssm_desc* d, const ssm_fwd_args* a, void* ws, size_t ws_
   const Segs sg = segments((long)d->batch * d->nheads * p.npblk, pl.nchunks);
   p.nseg = sg.nseg;
   p.cps = sg.cps;
-  // A forward that keeps no boundary states may walk two chunks per step (the saved
-  // states, when asked for, follow the plan's chunk).  Two-endpoint writes only, where
-  // the shift identity keeps a double chunk's keys within the plan chunk's tiles;
-  // segment boundaries stay where they are (an even number of chunks per segment).
-  if (!a->saved && (d->flags & SSM_F_TWO_ENDPOINT) && (sg.nseg == 1 || sg.cps % 2 == 0) &&
-      env_int("SSM_FWD_SINGLE", 0) == 0) {
+  // A two-endpoint forward may walk two chunks per step: the shift identity keeps a double
+  // chunk's keys within the plan chunk's tiles; segment boundaries stay where they are (an
+  // even number of chunks per segment).  Saved states still follow the plan's chunk: with
+  // per-row decay and an even rank, the double-chunk kernel also saves the state after each
+  // double chunk's first half; otherwise a forward that saves states keeps the plan's chunk.
+  const bool half_save = pl.coord_kernel && (pl.QT * pl.R) % 32 == 0;
+  if ((!a->saved || half_save) && (d->flags & SSM_F_TWO_ENDPOINT) &&
+      (sg.nseg == 1 || sg.cps % 2 == 0) && env_int("SSM_FWD_SINGLE", 0) == 0) {
     FwdKey k2 = key;
     k2.QT = 2 * pl.QT;
     if (ssm::fwd_variant_exists(k2)) {

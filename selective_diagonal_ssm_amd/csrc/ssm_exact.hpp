@@ -157,7 +157,7 @@ __global__ __launch_bounds__(256) void ssm_fwd_exact(FwdParams p, int qtk) {
     hs[j][1] = (hin && n0 < N) ? hin[(size_t)(n0 + 1) * P + col] : 0.f;
   }
   T* saved = static_cast<T*>(p.saved);
-  const size_t sl_saved = (size_t)slice * (p.nchunks + 1);
+  const size_t sl_saved = (size_t)slice * (p.save_nchunks + 1);
   auto save_state = [&](int slot) {
 #pragma unroll
     for (int j = 0; j < MAXQ; ++j) {
@@ -237,7 +237,7 @@ __global__ __launch_bounds__(256) void ssm_fwd_exact(FwdParams p, int qtk) {
         if (q0 == 0) sY[(tau * R + o) * PBX + pl] = part + Dh * sX[((tau + 1) * R + o) * PBX + pl];
       }
       const int t = t0 + tau;
-      if (saved && ((t + 1) % qtk == 0 || t == L - 1)) save_state(t / qtk + 1);
+      if (saved && ((t + 1) % p.save_chunk == 0 || t == L - 1)) save_state(t / p.save_chunk + 1);
     }
     __syncthreads();
     for (int i = tid; i < nt * rout * PBX; i += 256) {

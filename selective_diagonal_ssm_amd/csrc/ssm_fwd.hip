@@ -57,6 +57,12 @@ struct FwdShape {
   // keys [gamma_s B_s | beta_s B_{s-1}] with values [X_s ; X_{s-1}] measured faster.
   static constexpr bool SHIFT = TE && QT >= 32 && (QT * R) % 32 == 0;
   static constexpr int KEYS = SHIFT ? R : KR;  // key rows per token
+  // Per-row decay in shifted form can also save the state after the first QT / 2 tokens of
+  // each chunk (the boundary states of half-size chunks, which the chunk gradients consume):
+  // those tokens' keys are the first (QT / 2) KEYS key rows, a whole number of 32-row MFMA
+  // steps of the state update.
+  static constexpr bool CAN_HALF = SHIFT && COORD && QT % 2 == 0 && ((QT / 2) * KEYS) % 32 == 0;
+  static constexpr int KK_HALF = CAN_HALF ? (QT / 2) * KEYS / 32 : 0;
   static constexpr int QK = QT * KEYS;
   static constexpr int NS = NC + PAD;  // row stride of n-contiguous buffers
   static constexpr int KS = QK + PAD;  // row stride of key-contiguous buffers (scores)
@@ -499,8 +505,11 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
   };
 
   const int nch = p.nchunks;
-  const size_t sl_saved = (size_t)slice * (nch + 1);
-  T* saved = static_cast<T*>(p.saved);  // chunk-boundary states, stored in the io dtype
+  // chunk-boundary states, stored in the io dtype, for chunks of save_chunk tokens: QT, or
+  // QT / 2 (the state after each chunk's first half is saved too)
+  const size_t sl_saved = (size_t)slice * (p.save_nchunks + 1);
+  T* saved = static_cast<T*>(p.saved);
+  const bool save_half = S::CAN_HALF && saved && 2 * p.save_chunk == QT;
 
   // prologue.  The global reads come first -- the factor wave's steps of the first two
   // chunks and beta / gamma of the first, the first chunk's operands, the incoming
@@ -698,6 +707,7 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
       const float nvnext = c + 1 < c1 ? sMisc[(c + 1) & 3][2] : 0.f;
       constexpr bool SHARE = S::TP % S::ST_PER_WAVE == 0;
       f32x4 acc[S::ST_PER_WAVE];
+      f32x4 acch[S::CAN_HALF ? S::ST_PER_WAVE : 1];  // after the first half's keys
       float hh[S::ST_PER_WAVE];
 #pragma unroll
       for (int k = 0; k < S::ST_PER_WAVE; ++k) {
@@ -710,6 +720,12 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
       }
 #pragma unroll
       for (int kk = 0; kk < S::QK / 32; ++kk) {
+        if constexpr (S::CAN_HALF) {
+          if (kk == S::KK_HALF) {
+#pragma unroll
+            for (int k = 0; k < S::ST_PER_WAVE; ++k) acch[k] = acc[k];
+          }
+        }
         Frag<BF16> fk;
         if (SHARE) {
           const int tn = (wave * S::ST_PER_WAVE) / S::TP;
@@ -757,7 +773,43 @@ __global__ __launch_bounds__(NTHREADS) void ssm_fwd_kernel(FwdParams p) {
           store4<BF16>(sST + (bi ^ 1) * S::NC * VS + n * VS + pl, COORD ? r4 : v4);
           if (saved) {
             if (SH) add_last_write(v4, c, bi, n, pl);  // saved states are h, not h'
-            store4<BF16>(saved + ((sl_saved + c + 1) * N + n) * P + p0 + pl, v4);
+            const int slot = save_half ? min(2 * c + 2, p.save_nchunks) : c + 1;
+            store4<BF16>(saved + ((sl_saved + slot) * N + n) * P + p0 + pl, v4);
+          }
+          if constexpr (S::CAN_HALF) {
+            // the state after the first half (when the chunk holds more tokens than that):
+            // e^{L_m - L_end/2} times the accumulator after the first half's keys
+            // (= e^{L_m} S + sum_{s <= m} e^{L_m - L_s} K~_s V_s), turned by the pairs'
+            // rotation up to token m, plus the gamma write of token m (whose key, at m + 1,
+            // belongs to the second half)
+            constexpr int TM = QT / 2 - 1;
+            if (save_half && c * QT + TM + 1 < L) {
+              const float cdm = sCD[sc][TM];
+              const float fm = __expf(-(sRate[n] * (cdm - 0.5f * cdend) +
+                                        sRateS[n] * (static_cast<float>(TM + 1) - 0.5f * nvend)));
+              float m4[4];
+#pragma unroll
+              for (int i = 0; i < 4; ++i) m4[i] = acch[k][i] * fm;
+              const bool pair = n >= nreal;
+              float sn = 0.f, cs = 1.f;
+              if (pair) fast_sincos(sOmega[(n - nreal) >> 1] * cdm, &sn, &cs);
+              const float sg = (lane & 1) ? sn : -sn;
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                const float other = swap_adjacent_lanes(m4[i]);
+                m4[i] = pair ? cs * m4[i] + sg * other : m4[i];
+              }
+              const float gm = sGa[c & 3][TM];
+#pragma unroll
+              for (int r = 0; r < R; ++r) {
+                float xv[4];  // X_m: the value row of the key at m + 1
+                load4<BF16>(sV + bi * VSZ + ((TM + 1) * R + r) * VS + pl, xv);
+                const float bw = gm * to_f32(sBraw[(TM * R + r) * NS + n]);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) m4[i] += bw * xv[i];
+              }
+              store4<BF16>(saved + ((sl_saved + 2 * c + 1) * N + n) * P + p0 + pl, m4);
+            }
           }
         }
       }

@@ -17,7 +17,7 @@ struct FwdParams {
   const float* gamma;
   const float* D;
   void* y;
-  void* saved;   // [batch][nheads][nchunks + 1][N][P] in the io dtype, or null
+  void* saved;   // [batch][nheads][save_nchunks + 1][N][P] in the io dtype, or null
   const float* h0;  // [batch][nheads][N][P] fp32 state before token 0, or null
   float* h_final;   // [batch][nheads][N][P] fp32 state after the last token, or null
   // the token before the sequence (two-endpoint carry), or null: x [batch][nheads][rin][P],
@@ -25,6 +25,9 @@ struct FwdParams {
   const void* x_prev;
   const void* B_prev;
   int batch, L, H, G, P, n_real, n_pairs, nchunks, npblk;
+  // the saved states are those of chunks of save_chunk tokens (the kernel's chunk, or half of
+  // it), save_nchunks of them
+  int save_chunk, save_nchunks;
   int n_static;  // the first n_static real rows decay by e^{-A} per token, whatever the step
   // ranks of the write (B, x) and of the readout (C, y); the kernel's rank R is the
   // larger, rows past a side's own rank are zero on load and dropped on store

@@ -407,3 +407,61 @@ def test_two_endpoint_split_run_chains_through_the_carry(case):
           flush=True)
     bad = {k: v for k, v in errs.items() if not v <= tl}
     assert not bad, bad
+
+
+def _prefix(prob, n):
+    """The problem cut to its first n tokens."""
+    out = dict(prob)
+    out["desc"] = dict(prob["desc"], seqlen=n)
+    for k in ("x", "B", "C", "dt", "beta", "gamma", "dy"):
+        if prob.get(k) is not None:
+            out[k] = np.ascontiguousarray(prob[k][:, :n])
+    return out
+
+
+def _saved_states(prob, saved, q):
+    """The saved chunk-boundary states as [batch][nheads][slots][N][P] float64."""
+    d = prob["desc"]
+    slots = (d["seqlen"] + q - 1) // q + 1
+    shape = (d["batch"], d["nheads"], slots, d["dstate"], d["headdim"])
+    flat = saved.view(torch.bfloat16) if prob["dtype"] == "bf16" else saved
+    return _np(flat[: int(np.prod(shape))].reshape(shape))
+
+
+@pytest.mark.parametrize("nseg", [1, 4])
+@pytest.mark.parametrize("case", sorted(DOUBLE_CASES))
+def test_saved_states_match_oracle(case, nseg, monkeypatch):
+    """Every slot of the saved chunk-boundary states (two-endpoint per-row decay at an even
+    rank walks double chunks and also saves the state after each one's first half) is the
+    oracle's state after that many tokens, and agrees with the one-chunk walk; y and the
+    final state match the oracle."""
+    monkeypatch.setenv("SSM_NSEG", str(nseg))
+    name, kw = DOUBLE_CASES[case]
+    prob = workloads.make_problem(workloads.spec(name, **kw), seed=31)
+    h0 = workloads.make_state(prob["desc"], seed=37)
+    q = prob["chunk"]
+    L = prob["desc"]["seqlen"]
+    print(f"[saved] case={case} nseg={nseg} desc={prob['desc']}", flush=True)
+    t = workloads.to_device(prob)
+    h0t = torch.from_numpy(h0).cuda()
+    y, saved, hf = _fwd(prob, t, h0=h0t, save=True)
+    monkeypatch.setenv("SSM_FWD_SINGLE", "1")
+    y1, saved1, hf1 = _fwd(prob, t, h0=h0t, save=True)
+    torch.cuda.synchronize()
+    yr, hr = oracle.fwd(prob, h0=h0.astype(np.float64))
+    ey, eh = rel_l2(_np(y), yr), rel_l2(_np(hf), hr)
+    S, S1 = _saved_states(prob, saved, q), _saved_states(prob, saved1, q)
+    nslots = S.shape[2]
+    e1 = rel_l2(S, S1)
+    # slot k holds the state after min(k q, L) tokens: the first few (a double chunk's
+    # half and end), one in the middle and the last two (a ragged end)
+    errs = {}
+    for k in sorted({0, 1, 2, 3, nslots // 2 | 1, nslots - 2, nslots - 1}):
+        n = min(k * q, L)
+        ref = h0.astype(np.float64) if n == 0 else oracle.fwd(_prefix(prob, n), h0=h0.astype(np.float64))[1]
+        errs[k] = rel_l2(S[:, :, k], ref)
+    print(f"[saved] case={case} nseg={nseg} y={ey:.2e} h_final={eh:.2e} slots vs one-chunk "
+          f"{e1:.2e} vs oracle " + " ".join(f"{k}:{v:.2e}" for k, v in errs.items()), flush=True)
+    assert ey <= tol(prob) and eh <= tol(prob), (ey, eh)
+    assert e1 <= tol(prob), e1
+    assert all(v <= tol(prob) for v in errs.values()), errs
