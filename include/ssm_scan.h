@@ -204,7 +204,10 @@ int ssm_scan_fwd(const ssm_desc *desc, const ssm_fwd_args *args, void *ws, size_
 
 /* Fused reverse-mode pass: dx, dB, dC, ddt and the requested parameter
    gradients (dA, domega, dbeta, dgamma, dD), given dy and the forward's
-   `saved` states.  When groups are shared by several heads (ngroups < nheads),
+   `saved` states.  It is the adjoint of the recurrence above (g_t = C_t dy_t +
+   A_{t+1}^T g_{t+1}); "When a Diagonal State Is Not Enough", Part 04, checks the
+   method by outputs, input gradients and parameter gradients alike, and the arXiv
+   abstract times the kernels forward + backward.  When groups are shared by several heads (ngroups < nheads),
    dB and dC of a group are the sums over its heads, taken in a fixed head order
    from per-head partials in the workspace, so every call gives the same bits. */
 int ssm_scan_bwd(const ssm_desc *desc, const ssm_bwd_args *args, void *ws, size_t ws_bytes,
