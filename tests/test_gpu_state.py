@@ -428,15 +428,30 @@ def _saved_states(prob, saved, q):
     return _np(flat[: int(np.prod(shape))].reshape(shape))
 
 
+# ragged ends of the double-chunk walk: a last 32-token chunk of exactly 16 tokens (no middle
+# state of its own: its end is the last 16-token slot), of 17, and of one token
+RAGGED_SAVE = {
+    f"{dt}_hybrid_L{L}": ("hybrid", dict(DOUBLE_CASES[f"{dt}_hybrid"][1], seqlen=L))
+    for dt in ("bf16", "f32") for L in (496, 497, 481)
+}
+# steep per-row decay (every double chunk flagged and redone token by token, which stores the
+# same 16-token slots), with a ragged end of 9 tokens
+RAGGED_SAVE.update({
+    f"{dt}_hybrid_steep_L201": ("hybrid", dict(DOUBLE_CASES[f"{dt}_hybrid"][1], seqlen=201,
+                                               dt_mean=2.0, A_lo=16.0, A_hi=16.0))
+    for dt in ("bf16", "f32")
+})
+
+
 @pytest.mark.parametrize("nseg", [1, 4])
-@pytest.mark.parametrize("case", sorted(DOUBLE_CASES))
+@pytest.mark.parametrize("case", sorted(DOUBLE_CASES) + sorted(RAGGED_SAVE))
 def test_saved_states_match_oracle(case, nseg, monkeypatch):
     """Every slot of the saved chunk-boundary states (two-endpoint per-row decay at an even
     rank walks double chunks and also saves the state after each one's first half) is the
     oracle's state after that many tokens, and agrees with the one-chunk walk; y and the
     final state match the oracle."""
     monkeypatch.setenv("SSM_NSEG", str(nseg))
-    name, kw = DOUBLE_CASES[case]
+    name, kw = DOUBLE_CASES[case] if case in DOUBLE_CASES else RAGGED_SAVE[case]
     prob = workloads.make_problem(workloads.spec(name, **kw), seed=31)
     h0 = workloads.make_state(prob["desc"], seed=37)
     q = prob["chunk"]
