@@ -52,9 +52,9 @@ struct FwdShape {
   //   h'_t = A_t h'_{t-1} + B^_{t-1} X_{t-1},  B^_{t-1} = (gamma_{t-1} A_t + beta_t) B_{t-1},
   //   y_t  = C_t^T h'_t + gamma_t (C_t . B_t) X_t + D X_t,
   // one key row per (token, rank) instead of two, plus a same-token term.  Used for
-  // 32-token chunks (the two-chunk walk of a forward without saved states), where it
-  // keeps the keys within the tiles of a 16-token chunk; at 16 tokens the two-endpoint
-  // keys [gamma_s B_s | beta_s B_{s-1}] with values [X_s ; X_{s-1}] measured faster.
+  // 32-token chunks (the two-chunk walk of the 16-token plan), where it keeps the keys
+  // within the tiles of a 16-token chunk; at 16 tokens the two-endpoint keys
+  // [gamma_s B_s | beta_s B_{s-1}] with values [X_s ; X_{s-1}] measured faster.
   static constexpr bool SHIFT = TE && QT >= 32 && (QT * R) % 32 == 0;
   static constexpr int KEYS = SHIFT ? R : KR;  // key rows per token
   // Per-row decay in shifted form can also save the state after the first QT / 2 tokens of
