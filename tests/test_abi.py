@@ -88,6 +88,13 @@ def test_chunk_and_saved_bytes():
     dh32 = _lib.make_desc(base_desc(decay_mode="coord", n_real=32, n_pairs=16, rank_in=2,
                                     rank_out=2, two_endpoint=True), "bf16", 32)
     assert ssm.chunk_tokens(dh32) == 32  # a chunk the caller asks for
+    # the HybridMamba training step: the forward walks 32-token chunks, but the saved
+    # states stay those of the 16-token plan chunks the reverse pass consumes
+    dt = _lib.make_desc(dict(base_desc(decay_mode="coord", n_real=32, n_pairs=16, rank_in=2,
+                                       rank_out=2, two_endpoint=True), batch=2, seqlen=16384,
+                             nheads=32, ngroups=32), "bf16")
+    assert ssm.chunk_tokens(dt) == 16
+    assert ssm.saved_bytes(dt) == 2 * 32 * (16384 // 16 + 1) * 64 * 64 * 2
 
 
 def test_null_pointers_rejected_before_launch():
